@@ -1,0 +1,62 @@
+"""Small Command specs used by the tests (inputs only: no arithmetic here).
+
+Same format as the workload specs in ``workloads.py``; the hand-worked pins in
+``tests/golden/hand_worked.txt`` and the invariant tests name these.
+"""
+import workloads as W
+
+
+def unary(op, dt_in, dt_out=None):
+    if op == "cvt":
+        return [("x", ("load", dt_in, 1)), ("r", ("cvt", "x", dt_out)), ("o", ("store", "r", 1))]
+    return [("x", ("load", dt_in, 1)), ("r", (op, "x")), ("o", ("store", "r", 1))]
+
+
+def binary(op, dt):
+    return [("x", ("load", dt, 1)), ("y", ("load", dt, 1)), ("r", (op, "x", "y")),
+            ("o", ("store", "r", 1))]
+
+
+SPECS = {
+    "add_f32": W.ADD_F32,
+    "int_fused": W.INT_FUSED,
+    "axpby_f32": W.AXPBY_F32,
+    "mixed_two_out": W.MIXED_TWO_OUT,
+    "transposed_2d": W.TRANSPOSED_2D,
+    "copy_f32": W.COPY_F32,
+    "sub_f32": binary("sub", "f32"),
+    "mul_f32": binary("mul", "f32"),
+    "add_i32": binary("add", "i32"),
+    "sub_i32": binary("sub", "i32"),
+    "mul_i32": binary("mul", "i32"),
+    "neg_f32": unary("neg", "f32"),
+    "neg_i32": unary("neg", "i32"),
+    "neg_f16": unary("neg", "f16"),
+}
+for a in ("f16", "f32", "i32"):
+    for b in ("f16", "f32", "i32"):
+        SPECS["cvt_%s_%s" % (a, b)] = unary("cvt", a, b)
+
+DT = {"f16": "f16", "f32": "f32", "i32": "i32"}
+
+
+def arg_dtypes(spec):
+    """dtype of each input argument and of each output, in declaration order."""
+    dt = {}
+    ins, outs = [], []
+    for name, st in spec:
+        k = st[0]
+        if k in ("load", "scalar"):
+            dt[name] = st[1]
+            ins.append(st[1])
+        elif k in ("add", "sub", "mul", "neg"):
+            dt[name] = dt[st[1]]
+        elif k == "cvt":
+            dt[name] = st[2]
+        elif k == "store":
+            outs.append(dt[st[1]])
+    return ins, outs
+
+
+def input_kinds(spec):
+    return [st[0] for _, st in spec if st[0] in ("load", "scalar")]

@@ -1,0 +1,99 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies the oracle's C core, plants one plausible mistake (a wrong
+sign, a swapped operand, truncation instead of rounding, a flushed subnormal,
+a transposed index ...), builds it with the same flags, swaps it in, and checks
+that the pin suite's fast checks fail.  CPU only.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+from specs import SPECS
+import test_oracle_pins as P
+
+MUTANTS = {
+    "sub_operands_swapped": ("if (op == OR_SUB) return a - b;", "if (op == OR_SUB) return b - a;"),
+    "f32_sub_as_add": ("else if (op == OR_SUB) z = x - y;", "else if (op == OR_SUB) z = x + y;"),
+    "i32_add_through_float": ("if (op == OR_ADD) return a + b;",
+                              "if (op == OR_ADD) return (uint32_t)(int32_t)((float)(int32_t)a + (float)(int32_t)b);"),
+    "neg_as_zero_minus": ("if (dst_dtype == OR_F32) return a ^ 0x80000000u;",
+                          "if (dst_dtype == OR_F32) return bits_from_f32(0.0f - f32_from_bits(a));"),
+    "f16_round_truncates": ("double q = nearbyint(ldexp(a, -spacing_exp));",
+                            "double q = trunc(ldexp(a, -spacing_exp));"),
+    "f16_round_half_up": ("double q = nearbyint(ldexp(a, -spacing_exp));",
+                          "double q = floor(ldexp(a, -spacing_exp) + 0.5);"),
+    "f16_out_subnormal_flushed": ("return sign | (uint16_t)q;", "return sign;"),
+    "f16_in_subnormal_flushed": ("mag = ldexp((double)m, -24);", "mag = 0.0;"),
+    "f16_exponent_bias_off": ("mag = ldexp((double)(1024 + m), (int)e - 25);",
+                              "mag = ldexp((double)(1024 + m), (int)e - 24);"),
+    "view_index_transposed": ("int64_t off = r * g->stride[0] + c * g->stride[1];\n    if (g->dtype == OR_F16) {\n        uint16_t h;",
+                              "int64_t off = r * g->stride[1] + c * g->stride[0];\n    if (g->dtype == OR_F16) {\n        uint16_t h;"),
+    "scalar_ignored": ("val[t] = J->args[n->arg].bits;", "val[t] = 0u;"),
+    "f32_to_i32_rounds": ("return (int32_t)truncf(f);", "return (int32_t)nearbyintf(f);"),
+    "second_operand_is_first": ("n->b >= 0 ? val[n->b] : 0u", "n->b >= 0 ? val[n->a] : 0u"),
+    "mul_high_dropped": ("return a * b;                        /* low 32 bits of the product */",
+                         "return (a & 0xffffu) * (b & 0xffffu);"),
+}
+
+
+def _fast_pins(oracle_mod):
+    """Run the quick pins; return the number that fail."""
+    failures = 0
+    checks = [lambda c=c: P.test_hand_worked(oracle_mod, c) for c in P.GOLDEN_CASES]
+    checks += [
+        lambda: P.test_add_f32_vs_numpy(oracle_mod),
+        lambda: P.test_int_fused_vs_numpy(oracle_mod, True),
+        lambda: P.test_axpby_vs_numpy_and_binary64(oracle_mod),
+        lambda: P.test_mixed_vs_numpy(oracle_mod),
+        lambda: P.test_int32_invariants(oracle_mod),
+        lambda: P.test_f32_invariants(oracle_mod),
+        lambda: P.test_f16_to_f32_all_patterns(oracle_mod),
+        lambda: P.test_f32_to_f16_every_tie_and_neighbour(oracle_mod),
+        lambda: P.test_transposed_brute_force(oracle_mod, (17, 33), 1, 3),
+        lambda: P.test_i32_conversions_vs_numpy(oracle_mod),
+    ]
+    for chk in checks:
+        try:
+            chk()
+        except AssertionError:
+            failures += 1
+    return failures
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+def test_unmutated_copy_passes(oracle_mod, mutant_dir):
+    src = open(oracle_mod.SRC).read()
+    path = str(mutant_dir / "clean.c")
+    open(path, "w").write(src)
+    so = path[:-2] + ".so"
+    subprocess.run(["gcc", *oracle_mod.GCC_FLAGS, "-o", so, path, "-lm"], check=True)
+    prev = oracle_mod.use_library(so)
+    try:
+        assert _fast_pins(oracle_mod) == 0
+    finally:
+        oracle_mod.use_library(prev)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(oracle_mod, mutant_dir, name):
+    old, new = MUTANTS[name]
+    src = open(oracle_mod.SRC).read()
+    assert src.count(old) == 1, "mutation anchor for %s not found exactly once" % name
+    path = str(mutant_dir / (name + ".c"))
+    open(path, "w").write(src.replace(old, new))
+    so = path[:-2] + ".so"
+    subprocess.run(["gcc", *oracle_mod.GCC_FLAGS, "-Wno-unused-function", "-o", so, path, "-lm"],
+                   check=True)
+    prev = oracle_mod.use_library(so)
+    try:
+        assert _fast_pins(oracle_mod) > 0, "planted mistake %s went unnoticed" % name
+    finally:
+        oracle_mod.use_library(prev)

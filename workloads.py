@@ -1,0 +1,196 @@
+"""Seeded synthetic workloads for elementwise tensor Commands.
+
+This module holds *inputs only*: the declarative shape of each Command (which
+loads, scalars, E_ operations and stores, in declaration order) and seeded
+NumPy generators for its tensors and scalars.  It holds none of the arithmetic:
+the oracle and the GPU library each turn a spec into their own Command with
+their own code.
+
+Spec format: a list of ``(name, step)`` pairs.  ``step`` is one of
+``("load", dtype, rank)``, ``("scalar", dtype)``, ``("add"|"sub"|"mul", a, b)``,
+``("neg", a)``, ``("cvt", a, dtype)`` or ``("store", value, rank)``, where ``a``,
+``b`` and ``value`` name earlier steps.  CommandArguments are the loads,
+scalars and stores in the order they appear.
+
+Generators follow one recipe: ``np.random.default_rng(seed)`` (PCG64), with
+``seed = 1000 + k`` for workload k, drawing the tensors in declaration order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# The five Commands.
+
+ADD_F32 = [
+    ("x", ("load", "f32", 1)),
+    ("y", ("load", "f32", 1)),
+    ("z", ("add", "x", "y")),
+    ("out", ("store", "z", 1)),
+]
+
+INT_FUSED = [
+    ("x", ("load", "i32", 1)),
+    ("y", ("load", "i32", 1)),
+    ("w", ("load", "i32", 1)),
+    ("s", ("scalar", "i32")),
+    ("a", ("add", "x", "y")),
+    ("m", ("mul", "a", "w")),
+    ("z", ("sub", "m", "s")),
+    ("out", ("store", "z", 1)),
+]
+
+AXPBY_F32 = [
+    ("x", ("load", "f32", 1)),
+    ("y", ("load", "f32", 1)),
+    ("alpha", ("scalar", "f32")),
+    ("beta", ("scalar", "f32")),
+    ("ax", ("mul", "alpha", "x")),
+    ("by", ("mul", "beta", "y")),
+    ("r", ("add", "ax", "by")),
+    ("out", ("store", "r", 1)),
+]
+
+MIXED_TWO_OUT = [
+    ("x", ("load", "f16", 1)),
+    ("y", ("load", "f16", 1)),
+    ("z", ("load", "f16", 1)),
+    ("s", ("scalar", "f32")),
+    ("xf", ("cvt", "x", "f32")),
+    ("yf", ("cvt", "y", "f32")),
+    ("zf", ("cvt", "z", "f32")),
+    ("t", ("mul", "xf", "yf")),
+    ("u", ("add", "t", "zf")),
+    ("v", ("sub", "t", "zf")),
+    ("uv", ("mul", "u", "v")),
+    ("o0", ("cvt", "uv", "f16")),
+    ("o1", ("add", "u", "s")),
+    ("out0", ("store", "o0", 1)),
+    ("out1", ("store", "o1", 1)),
+]
+
+TRANSPOSED_2D = [
+    ("X", ("load", "f32", 2)),
+    ("Yt", ("load", "f32", 2)),
+    ("alpha", ("scalar", "f32")),
+    ("ay", ("mul", "alpha", "Yt")),
+    ("o", ("add", "X", "ay")),
+    ("out", ("store", "o", 2)),
+]
+
+COPY_F32 = [
+    ("x", ("load", "f32", 1)),
+    ("out", ("store", "x", 1)),
+]
+
+WORKLOADS = {
+    "add_f32": dict(index=0, spec=ADD_F32, n=65536,
+                    label="z = x + y, fp32, n=65536 contiguous"),
+    "int_fused": dict(index=1, spec=INT_FUSED, n=1 << 24,
+                      label="z = (x + y) * w - s, int32, n=2^24, s=12345"),
+    "axpby_f32": dict(index=2, spec=AXPBY_F32, n=1 << 28,
+                      label="out = alpha*x + beta*y, fp32, n=2^28, alpha=1.5, beta=-0.25"),
+    "mixed_two_out": dict(index=3, spec=MIXED_TWO_OUT, n=1 << 27,
+                          label="fp16 x,y,z -> out0=fp16(u*v), out1=u+s, t=x*y shared, n=2^27"),
+    "transposed_2d": dict(index=4, spec=TRANSPOSED_2D, n=16384,
+                          label="out[i,j] = X[i,j] + alpha*Y[j,i], fp32 16384x16384, X row stride 16448"),
+}
+
+SCALARS = {
+    "int_fused": {"s": np.int32(12345)},
+    "axpby_f32": {"alpha": np.float32(1.5), "beta": np.float32(-0.25)},
+    "mixed_two_out": {"s": np.float32(0.5)},
+    "transposed_2d": {"alpha": np.float32(2.0)},
+}
+
+
+def seed_of(workload: str) -> int:
+    return 1000 + WORKLOADS[workload]["index"]
+
+
+def arg_names(spec, outputs: bool = False):
+    """Names of the input (or output) CommandArguments in declaration order."""
+    if outputs:
+        return [name for name, st in spec if st[0] == "store"]
+    return [name for name, st in spec if st[0] in ("load", "scalar")]
+
+
+def _uniform_pm1_f32(rng, shape):
+    # rng.random(float32) is k * 2^-24 on [0, 1); *2 - 1 is exact in binary32.
+    return rng.random(shape, dtype=np.float32) * np.float32(2) - np.float32(1)
+
+
+def _uniform_pm4_f16(rng, n):
+    a = (rng.random(n, dtype=np.float32) * np.float32(8) - np.float32(4)).astype(np.float16)
+    bits = a.view(np.uint16)
+    bits[bits == 0x4400] = 0x43FF        # +4.0 after rounding -> largest fp16 below 4
+    return a
+
+
+def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
+                row_pad: int = 64):
+    """Host inputs for one workload, in declaration order.
+
+    Returns ``(values, extra)``: ``values`` is the list of input argument values
+    (numpy arrays for loads, numpy scalars for scalars); for the 2-D workload,
+    ``values[0]`` is the X *view* (a slice of a padded row-major storage whose
+    padding is NaN) and ``values[1]`` is the transposed view ``Y.T`` of a
+    contiguous Y; ``extra`` holds the backing storages.  ``n`` overrides the
+    length (the 2-D side length for the 2-D workload).
+    """
+    w = WORKLOADS[workload]
+    n = w["n"] if n is None else n
+    rng = np.random.default_rng(seed_of(workload) if seed is None else seed)
+    sc = SCALARS.get(workload, {})
+    extra = {}
+    if workload == "add_f32":
+        vals = [_uniform_pm1_f32(rng, n), _uniform_pm1_f32(rng, n)]
+    elif workload == "int_fused":
+        vals = [rng.integers(-32768, 32768, n, dtype=np.int32) for _ in range(3)]
+        vals.append(sc["s"])
+    elif workload == "axpby_f32":
+        vals = [rng.standard_normal(n, dtype=np.float32), rng.standard_normal(n, dtype=np.float32)]
+        vals += [sc["alpha"], sc["beta"]]
+    elif workload == "mixed_two_out":
+        vals = [_uniform_pm4_f16(rng, n) for _ in range(3)]
+        vals.append(sc["s"])
+    elif workload == "transposed_2d":
+        rows = cols = n
+        xs = np.full((rows, cols + row_pad), np.nan, dtype=np.float32)
+        xs[:, :cols] = _uniform_pm1_f32(rng, (rows, cols))
+        y = _uniform_pm1_f32(rng, (cols, rows))
+        extra = {"X_storage": xs, "Y": y}
+        vals = [xs[:, :cols], y.T, sc["alpha"]]
+    else:
+        raise KeyError(workload)
+    return vals, extra
+
+
+def algorithmic_bytes(workload: str, n: int | None = None) -> int:
+    """Logical elements x (sum of input element sizes + sum of output element
+    sizes); row padding and scalars are not counted."""
+    w = WORKLOADS[workload]
+    n = w["n"] if n is None else n
+    elems = n * n if workload == "transposed_2d" else n
+    size = {"f16": 2, "f32": 4, "i32": 4}
+    dt = {}
+    per = 0
+    for name, st in w["spec"]:
+        if st[0] == "load":
+            dt[name] = st[1]
+            per += size[st[1]]
+        elif st[0] == "scalar":
+            dt[name] = st[1]
+        elif st[0] in ("add", "sub", "mul", "neg"):
+            dt[name] = dt[st[1]]
+        elif st[0] == "cvt":
+            dt[name] = st[2]
+        elif st[0] == "store":
+            per += size[dt[st[1]]]
+    return elems * per
+
+
+def elements(workload: str, n: int | None = None) -> int:
+    w = WORKLOADS[workload]
+    n = w["n"] if n is None else n
+    return n * n if workload == "transposed_2d" else n
