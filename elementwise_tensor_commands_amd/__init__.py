@@ -1,0 +1,260 @@
+"""Python binding for libecmd.so: elementwise tensor Commands on MI355X.
+
+A thin ctypes layer over the C ABI declared in ``include/ecmd.h``; it only
+marshals arguments (tensor pointers, sizes and strides, scalar bit patterns,
+the current HIP stream).  Every step of the evaluation runs in the library's
+gfx950 kernels.  There is no fallback: if the library has not been built, the
+import fails.
+
+    import elementwise_tensor_commands_amd as ecmd
+    c = ecmd.Command()
+    x = c.load("f32"); y = c.load("f32")
+    c.store(c.add(x, y))
+    c.launch(x_t, y_t, out_t)          # torch tensors on the GPU, declaration order
+
+The Command model is rocRoller's (rocRoller "Design Overview", sections
+"Command Class", "Operations", "CommandArgument", "Command Kernel").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import struct
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libecmd.so")
+
+F16, F32, I32 = 1, 2, 3
+E_ADD, E_SUB, E_MUL, E_NEG, E_CVT = 1, 2, 3, 4, 5
+ARG_TENSOR, ARG_SCALAR = 1, 2
+PATH_NONE, PATH_LINEAR, PATH_TILED, PATH_GATHER = 0, 1, 2, 3
+PATH_NAMES = {0: "none", 1: "linear", 2: "tiled", 3: "gather"}
+STATUS = {
+    0: "CMD_OK", -1: "CMD_E_ARG", -2: "CMD_E_TAG", -3: "CMD_E_DTYPE", -4: "CMD_E_SHAPE",
+    -5: "CMD_E_STRIDE", -6: "CMD_E_ALIAS", -7: "CMD_E_LIMIT", -8: "CMD_E_NOSTORE",
+    -9: "CMD_E_STATE", -10: "CMD_E_LAUNCH", -11: "CMD_E_NOMEM",
+}
+DTYPES = {"f16": F16, "f32": F32, "i32": I32}
+DTYPE_NAMES = {F16: "f16", F32: "f32", I32: "i32"}
+
+
+class Error(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(code, "?"), code, msg))
+        self.code = code
+        self.name = STATUS.get(code, "?")
+
+
+class cmd_arg(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ptr", ctypes.c_void_p),
+                ("size", ctypes.c_int64 * 2), ("stride", ctypes.c_int64 * 2),
+                ("bits", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class cmd_plan_info(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("specialised", ctypes.c_int32), ("vector", ctypes.c_int32),
+                ("elems_per_thread", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("kernel", ctypes.c_char * 64)]
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libecmd.so is not built (%s); build it with "
+            "`python -m elementwise_tensor_commands_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "cmd_create": (ctypes.c_int, [ctypes.POINTER(vp)]),
+        "cmd_destroy": (ctypes.c_int, [vp]),
+        "cmd_load": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, i32p, i32p]),
+        "cmd_scalar": (ctypes.c_int, [vp, ctypes.c_int32, i32p, i32p]),
+        "cmd_op": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p]),
+        "cmd_store": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, i32p]),
+        "cmd_launch": (ctypes.c_int, [vp, ctypes.POINTER(cmd_arg), ctypes.c_int32, vp]),
+        "cmd_plan": (ctypes.c_int, [vp, ctypes.POINTER(cmd_arg), ctypes.c_int32, ctypes.POINTER(cmd_plan_info)]),
+        "cmd_dump": (ctypes.c_int64, [vp, ctypes.c_char_p, ctypes.c_int64]),
+        "cmd_last_error": (ctypes.c_char_p, [vp]),
+        "cmd_version": (ctypes.c_int32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load_library()
+
+# Raw C entry points under their C names (argument marshalling is the caller's).
+cmd_create = lib.cmd_create
+cmd_destroy = lib.cmd_destroy
+cmd_load = lib.cmd_load
+cmd_scalar = lib.cmd_scalar
+cmd_op = lib.cmd_op
+cmd_store = lib.cmd_store
+cmd_launch = lib.cmd_launch
+cmd_plan = lib.cmd_plan
+cmd_dump = lib.cmd_dump
+cmd_last_error = lib.cmd_last_error
+cmd_version = lib.cmd_version
+
+
+def _dt(d) -> int:
+    return DTYPES[d] if isinstance(d, str) else int(d)
+
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    return {torch.float16: F16, torch.float32: F32, torch.int32: I32}.get(t.dtype, 0)
+
+
+def scalar_bits(value, dtype: int) -> int:
+    """Bit pattern of a scalar CommandArgument value of the declared dtype."""
+    if dtype == F32:
+        return struct.unpack("<I", struct.pack("<f", float(value)))[0]
+    if dtype == I32:
+        return int(value) & 0xFFFFFFFF
+    return struct.unpack("<H", struct.pack("<e", float(value)))[0]
+
+
+class Command:
+    """One Command.  Tags are ints; CommandArguments are numbered in the order
+    load / scalar / store are called."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        rc = lib.cmd_create(ctypes.byref(h))
+        if rc:
+            raise Error(rc, lib.cmd_last_error(None).decode())
+        self._h = h
+        self.arg_kinds: list[tuple[int, int, int]] = []   # (kind, dtype, rank) per argument
+        self._dtypes: list[int] = []                      # dtype per tag
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and lib is not None:
+            lib.cmd_destroy(h)
+            self._h = None
+
+    def _check(self, rc: int):
+        if rc:
+            raise Error(rc, lib.cmd_last_error(self._h).decode())
+
+    def load(self, dtype, rank: int = 1) -> int:
+        tag, arg = ctypes.c_int32(), ctypes.c_int32()
+        self._check(lib.cmd_load(self._h, _dt(dtype), rank, ctypes.byref(tag), ctypes.byref(arg)))
+        self.arg_kinds.append((ARG_TENSOR, _dt(dtype), rank))
+        self._dtypes.append(_dt(dtype))
+        return tag.value
+
+    def scalar(self, dtype) -> int:
+        tag, arg = ctypes.c_int32(), ctypes.c_int32()
+        self._check(lib.cmd_scalar(self._h, _dt(dtype), ctypes.byref(tag), ctypes.byref(arg)))
+        self.arg_kinds.append((ARG_SCALAR, _dt(dtype), 0))
+        self._dtypes.append(_dt(dtype))
+        return tag.value
+
+    def op(self, opcode: int, a: int, b: int = -1, dtype=None) -> int:
+        if dtype is None:
+            dtype = self._dtypes[a] if 0 <= a < len(self._dtypes) else F32
+        tag = ctypes.c_int32()
+        self._check(lib.cmd_op(self._h, opcode, _dt(dtype), a, b, ctypes.byref(tag)))
+        self._dtypes.append(_dt(dtype))
+        return tag.value
+
+    def add(self, a, b): return self.op(E_ADD, a, b)
+    def sub(self, a, b): return self.op(E_SUB, a, b)
+    def mul(self, a, b): return self.op(E_MUL, a, b)
+    def neg(self, a): return self.op(E_NEG, a)
+    def cvt(self, a, dtype): return self.op(E_CVT, a, -1, dtype)
+
+    def store(self, tag: int, rank: int = 1) -> int:
+        arg = ctypes.c_int32()
+        self._check(lib.cmd_store(self._h, tag, rank, ctypes.byref(arg)))
+        dt = self._dtypes[tag] if 0 <= tag < len(self._dtypes) else 0
+        self.arg_kinds.append((ARG_TENSOR, dt, rank))
+        return arg.value
+
+    # -- argument marshalling --------------------------------------------------
+    def _args(self, values):
+        n = len(values)
+        arr = (cmd_arg * max(1, n))()
+        for i, v in enumerate(values):
+            kind, dt, rank = self.arg_kinds[i] if i < len(self.arg_kinds) else (ARG_TENSOR, 0, 1)
+            a = arr[i]
+            if kind == ARG_SCALAR:
+                a.kind, a.dtype, a.bits = ARG_SCALAR, dt, scalar_bits(v, dt)
+                continue
+            a.kind = ARG_TENSOR
+            a.dtype = _torch_dtype_code(v)
+            a.ptr = v.data_ptr() if v.numel() > 0 else (v.data_ptr() or None)
+            shape, strides = tuple(v.shape), tuple(v.stride())
+            for d in range(min(2, len(shape))):
+                a.size[d] = shape[d]
+                a.stride[d] = strides[d]
+            if len(shape) != rank:
+                # the C side checks shapes per declared rank; a rank mismatch is an argument error
+                a.size[0] = a.size[1] = -1
+        return arr, n
+
+    def launch(self, *values, stream=None):
+        """Enqueue the Command on ``stream`` (default: torch's current stream)
+        with one value per CommandArgument in declaration order: GPU tensors
+        for loads and stores, numbers for scalars."""
+        arr, n = self._args(values)
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream()
+        handle = stream if isinstance(stream, int) else getattr(stream, "cuda_stream", stream)
+        self._check(lib.cmd_launch(self._h, arr, n, ctypes.c_void_p(handle)))
+
+    def plan(self, *values) -> dict:
+        """What launch would do with these values (host only, no GPU needed)."""
+        arr, n = self._args(values)
+        info = cmd_plan_info()
+        self._check(lib.cmd_plan(self._h, arr, n, ctypes.byref(info)))
+        return {"path": PATH_NAMES[info.path], "specialised": bool(info.specialised),
+                "vector": bool(info.vector), "elems_per_thread": info.elems_per_thread,
+                "grid": info.grid, "block": info.block, "lds_bytes": info.lds_bytes,
+                "rows": info.rows, "cols": info.cols, "kernel": info.kernel.decode()}
+
+    def dump(self) -> str:
+        n = lib.cmd_dump(self._h, None, 0)
+        if n < 0:
+            self._check(int(n))
+        buf = ctypes.create_string_buffer(int(n) + 1)
+        lib.cmd_dump(self._h, buf, n + 1)
+        return buf.value.decode()
+
+
+def from_spec(spec) -> Command:
+    """Build a Command from a declarative list of ``(name, step)`` pairs, steps
+    being ("load", dtype, rank), ("scalar", dtype), ("add"|"sub"|"mul", a, b),
+    ("neg", a), ("cvt", a, dtype) or ("store", value, rank)."""
+    c = Command()
+    tags = {}
+    for name, st in spec:
+        k = st[0]
+        if k == "load":
+            tags[name] = c.load(st[1], st[2] if len(st) > 2 else 1)
+        elif k == "scalar":
+            tags[name] = c.scalar(st[1])
+        elif k == "add":
+            tags[name] = c.add(tags[st[1]], tags[st[2]])
+        elif k == "sub":
+            tags[name] = c.sub(tags[st[1]], tags[st[2]])
+        elif k == "mul":
+            tags[name] = c.mul(tags[st[1]], tags[st[2]])
+        elif k == "neg":
+            tags[name] = c.neg(tags[st[1]])
+        elif k == "cvt":
+            tags[name] = c.cvt(tags[st[1]], st[2])
+        elif k == "store":
+            c.store(tags[st[1]], st[2] if len(st) > 2 else 1)
+        else:
+            raise ValueError("unknown step %r" % (k,))
+    return c

@@ -1,0 +1,354 @@
+// ecmd_eval.h -- per-element evaluation of a lowered Program on gfx950.
+//
+// Values are 32-bit containers: binary32 bits, int32, or binary16 bits in the
+// low half.  Each work-item evaluates E consecutive elements at once.
+//
+// Two evaluators share the operation semantics below:
+//   * RtEval interprets the Program held in the kernel argument block.  Every
+//     branch depends only on Program bytes, which are the same for all lanes,
+//     so the wavefront never diverges.  Operands are picked by switch
+//     statements over compile-time register names: the register file stays in
+//     VGPRs (a runtime-indexed private array would live in scratch memory).
+//   * CtEval<P> evaluates a compile-time Program: the operation list is
+//     unrolled by template recursion and every reference is a constant, so the
+//     code is what one would write by hand for that Command.
+//
+// This file must be compiled with -ffp-contract=off: each binary32 operation
+// rounds on its own, as the E_ operations are separate operations of the
+// Command (rocRoller "Design Overview", section "Operations").
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ecmd_tape.h"
+
+namespace ecmd {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// binary16 -> binary32 (exact; v_cvt_f32_f16 keeps subnormals in FP16 denorm mode 3).
+__device__ __forceinline__ uint32_t h2f(uint32_t h)
+{
+    _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)h);
+    return as_u((float)x);
+}
+
+// binary32 -> binary16, round to nearest even (v_cvt_f16_f32 under the default
+// round mode), overflow to infinity, gradual underflow.  The empty asm pins the
+// binary32 operand in a VGPR: without it the backend folds a preceding binary32
+// multiply into the conversion (v_fma_mix* with a +0 addend), which rounds the
+// exact product once instead of twice and turns a -0 product into +0.
+__device__ __forceinline__ uint32_t f2h(uint32_t f)
+{
+    float v = as_f(f);
+    asm("" : "+v"(v));
+    _Float16 x = (_Float16)v;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x);
+}
+
+// binary32 -> int32: truncate toward zero, saturate, NaN -> 0.  Written out so
+// that no out-of-range conversion (undefined in C++) is ever performed.
+__device__ __forceinline__ uint32_t f2i_sat(float f)
+{
+    if (!(f == f)) return 0u;
+    if (f >= 2147483648.0f) return 0x7fffffffu;
+    if (f < -2147483648.0f) return 0x80000000u;
+    return (uint32_t)(int32_t)f;
+}
+
+template <int C>
+__device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b)
+{
+    if constexpr (C == C_MOV) return a;
+    else if constexpr (C == C_ADD_F32) return as_u(as_f(a) + as_f(b));
+    else if constexpr (C == C_SUB_F32) return as_u(as_f(a) - as_f(b));
+    else if constexpr (C == C_MUL_F32) return as_u(as_f(a) * as_f(b));
+    else if constexpr (C == C_ADD_I32) return a + b;
+    else if constexpr (C == C_SUB_I32) return a - b;
+    else if constexpr (C == C_MUL_I32) return a * b;
+    else if constexpr (C == C_NEG_F32) return a ^ 0x80000000u;
+    else if constexpr (C == C_NEG_I32) return 0u - a;
+    else if constexpr (C == C_NEG_F16) return (a ^ 0x8000u) & 0xffffu;
+    else if constexpr (C == C_CVT_F16_F32) return h2f(a);
+    else if constexpr (C == C_CVT_F32_F16) return f2h(a);
+    else if constexpr (C == C_CVT_I32_F32) return as_u((float)(int32_t)a);
+    else if constexpr (C == C_CVT_F32_I32) return f2i_sat(as_f(a));
+    // int32 -> binary16 through binary32: exact below 2^24, and at or above
+    // 2^24 both this and a direct rounding give infinity, so one rounding.
+    else if constexpr (C == C_CVT_I32_F16) return f2h(as_u((float)(int32_t)a));
+    else if constexpr (C == C_CVT_F16_I32) return f2i_sat(as_f(h2f(a)));
+    else return 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Generic interpreter.
+
+template <int E>
+struct Regs {
+    uint32_t in[kMaxIn][E];
+    uint32_t s[kMaxSlot][E];
+};
+
+template <int E>
+__device__ __forceinline__ void rt_fetch(uint8_t ref, const Regs<E> &R, const uint32_t *uni,
+                                         uint32_t (&o)[E])
+{
+    switch (ref) {
+#define ECMD_FETCH_IN(k)                                  \
+    case kRefIn + k:                                      \
+        _Pragma("unroll") for (int e = 0; e < E; ++e) o[e] = R.in[k][e]; \
+        break;
+#define ECMD_FETCH_S(k)                                   \
+    case kRefSlot + k:                                    \
+        _Pragma("unroll") for (int e = 0; e < E; ++e) o[e] = R.s[k][e]; \
+        break;
+#define ECMD_FETCH_U(k)                                   \
+    case kRefUni + k: {                                   \
+        const uint32_t u = uni[k];                        \
+        _Pragma("unroll") for (int e = 0; e < E; ++e) o[e] = u; \
+        break;                                            \
+    }
+        ECMD_FETCH_IN(0) ECMD_FETCH_IN(1) ECMD_FETCH_IN(2) ECMD_FETCH_IN(3)
+        ECMD_FETCH_IN(4) ECMD_FETCH_IN(5) ECMD_FETCH_IN(6) ECMD_FETCH_IN(7)
+        ECMD_FETCH_S(0) ECMD_FETCH_S(1) ECMD_FETCH_S(2) ECMD_FETCH_S(3)
+        ECMD_FETCH_S(4) ECMD_FETCH_S(5) ECMD_FETCH_S(6) ECMD_FETCH_S(7)
+        ECMD_FETCH_U(0) ECMD_FETCH_U(1) ECMD_FETCH_U(2) ECMD_FETCH_U(3)
+        ECMD_FETCH_U(4) ECMD_FETCH_U(5) ECMD_FETCH_U(6) ECMD_FETCH_U(7)
+#undef ECMD_FETCH_IN
+#undef ECMD_FETCH_S
+#undef ECMD_FETCH_U
+    default:
+        _Pragma("unroll") for (int e = 0; e < E; ++e) o[e] = 0u;
+        break;
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void rt_put(uint8_t dst, Regs<E> &R, const uint32_t (&v)[E])
+{
+    switch (dst) {
+#define ECMD_PUT_S(k)                                     \
+    case kRefSlot + k:                                    \
+        _Pragma("unroll") for (int e = 0; e < E; ++e) R.s[k][e] = v[e]; \
+        break;
+        ECMD_PUT_S(0) ECMD_PUT_S(1) ECMD_PUT_S(2) ECMD_PUT_S(3)
+        ECMD_PUT_S(4) ECMD_PUT_S(5) ECMD_PUT_S(6) ECMD_PUT_S(7)
+#undef ECMD_PUT_S
+    default:
+        break;
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void rt_apply(uint8_t code, const uint32_t (&a)[E], const uint32_t (&b)[E],
+                                         uint32_t (&r)[E])
+{
+    switch (code) {
+#define ECMD_APPLY(c)                                     \
+    case c:                                               \
+        _Pragma("unroll") for (int e = 0; e < E; ++e) r[e] = apply<c>(a[e], b[e]); \
+        break;
+        ECMD_APPLY(C_MOV) ECMD_APPLY(C_ADD_F32) ECMD_APPLY(C_SUB_F32) ECMD_APPLY(C_MUL_F32)
+        ECMD_APPLY(C_ADD_I32) ECMD_APPLY(C_SUB_I32) ECMD_APPLY(C_MUL_I32)
+        ECMD_APPLY(C_NEG_F32) ECMD_APPLY(C_NEG_I32) ECMD_APPLY(C_NEG_F16)
+        ECMD_APPLY(C_CVT_F16_F32) ECMD_APPLY(C_CVT_F32_F16) ECMD_APPLY(C_CVT_I32_F32)
+        ECMD_APPLY(C_CVT_F32_I32) ECMD_APPLY(C_CVT_I32_F16) ECMD_APPLY(C_CVT_F16_I32)
+#undef ECMD_APPLY
+    default:
+        _Pragma("unroll") for (int e = 0; e < E; ++e) r[e] = 0u;
+        break;
+    }
+}
+
+struct RtEval {
+    static constexpr bool kSpecialised = false;
+    __device__ static int n_in(const Program &P) { return P.n_in; }
+    __device__ static int n_out(const Program &P) { return P.n_out; }
+    __device__ static uint8_t in_ty(const Program &P, int k) { return P.in_ty[k]; }
+    __device__ static uint8_t out_ty(const Program &P, int k) { return P.out_ty[k]; }
+
+    template <int E>
+    __device__ static __forceinline__ void run(const Program &P, const uint32_t *uni, Regs<E> &R,
+                                               uint32_t (&out)[kMaxOut][E])
+    {
+        const int n_ops = P.n_ops;
+        for (int i = 0; i < n_ops; ++i) {
+            const TapeOp op = P.ops[i];
+            uint32_t a[E], b[E], r[E];
+            rt_fetch<E>(op.a, R, uni, a);
+            rt_fetch<E>(op.b, R, uni, b);
+            rt_apply<E>(op.code, a, b, r);
+            rt_put<E>(op.dst, R, r);
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxOut; ++k)
+            if (k < P.n_out) rt_fetch<E>(P.out_ref[k], R, uni, out[k]);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Compile-time evaluator.
+
+template <const Program &P>
+struct CtEval {
+    static constexpr bool kSpecialised = true;
+    __device__ static constexpr int n_in(const Program &) { return P.n_in; }
+    __device__ static constexpr int n_out(const Program &) { return P.n_out; }
+    __device__ static constexpr uint8_t in_ty(const Program &, int k) { return P.in_ty[k]; }
+    __device__ static constexpr uint8_t out_ty(const Program &, int k) { return P.out_ty[k]; }
+
+    template <uint8_t ref, int E>
+    __device__ static __forceinline__ uint32_t get(const Regs<E> &R, const uint32_t *uni, int e)
+    {
+        if constexpr (ref == kRefNone) return 0u;
+        else if constexpr (ref < kRefSlot) return R.in[ref - kRefIn][e];
+        else if constexpr (ref < kRefUni) return R.s[ref - kRefSlot][e];
+        else return uni[ref - kRefUni];
+    }
+
+    template <int I, int E>
+    __device__ static __forceinline__ void step(const uint32_t *uni, Regs<E> &R)
+    {
+        if constexpr (I < P.n_ops) {
+            constexpr TapeOp op = P.ops[I];
+            uint32_t r[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                r[e] = apply<op.code>(get<op.a, E>(R, uni, e), get<op.b, E>(R, uni, e));
+#pragma unroll
+            for (int e = 0; e < E; ++e) R.s[op.dst - kRefSlot][e] = r[e];
+            step<I + 1, E>(uni, R);
+        }
+    }
+
+    template <int K, int E>
+    __device__ static __forceinline__ void outs(const uint32_t *uni, const Regs<E> &R,
+                                                uint32_t (&out)[kMaxOut][E])
+    {
+        if constexpr (K < P.n_out) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) out[K][e] = get<P.out_ref[K], E>(R, uni, e);
+            outs<K + 1, E>(uni, R, out);
+        }
+    }
+
+    template <int E>
+    __device__ static __forceinline__ void run(const Program &, const uint32_t *uni, Regs<E> &R,
+                                               uint32_t (&out)[kMaxOut][E])
+    {
+        step<0, E>(uni, R);
+        outs<0, E>(uni, R, out);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Global memory access for E consecutive elements of one operand.
+
+template <int E, bool VEC>
+__device__ __forceinline__ void load_elems(const void *p, uint8_t ty, int64_t i, int count,
+                                           uint32_t (&v)[E])
+{
+    if (ty == TY_F16) {
+        const uint16_t *q = static_cast<const uint16_t *>(p) + i;
+        if constexpr (VEC) {
+            static_assert(E % 8 == 0 || E == 4, "binary16 vectors are 8 or 4 wide");
+            if constexpr (E % 8 == 0) {
+#pragma unroll
+                for (int w = 0; w < E / 8; ++w) {
+                    const u32x4 d = reinterpret_cast<const u32x4 *>(q)[w];
+                    const uint32_t x[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[8 * w + 2 * j] = x[j] & 0xffffu;
+                        v[8 * w + 2 * j + 1] = x[j] >> 16;
+                    }
+                }
+            } else {
+                const u32x2 d = *reinterpret_cast<const u32x2 *>(q);
+                v[0] = d.x & 0xffffu;
+                v[1] = d.x >> 16;
+                v[2] = d.y & 0xffffu;
+                v[3] = d.y >> 16;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = e < count ? (uint32_t)q[e] : 0u;
+        }
+    } else {
+        const uint32_t *q = static_cast<const uint32_t *>(p) + i;
+        if constexpr (VEC) {
+            static_assert(E % 4 == 0, "32-bit vectors are 4 wide");
+#pragma unroll
+            for (int w = 0; w < E / 4; ++w) {
+                const u32x4 d = reinterpret_cast<const u32x4 *>(q)[w];
+                v[4 * w + 0] = d.x;
+                v[4 * w + 1] = d.y;
+                v[4 * w + 2] = d.z;
+                v[4 * w + 3] = d.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = e < count ? q[e] : 0u;
+        }
+    }
+}
+
+template <int E, bool VEC, bool NT>
+__device__ __forceinline__ void store_elems(void *p, uint8_t ty, int64_t i, int count,
+                                            const uint32_t (&v)[E])
+{
+    if (ty == TY_F16) {
+        uint16_t *q = static_cast<uint16_t *>(p) + i;
+        if constexpr (VEC) {
+            if constexpr (E % 8 == 0) {
+#pragma unroll
+                for (int w = 0; w < E / 8; ++w) {
+                    u32x4 d;
+                    d.x = (v[8 * w + 0] & 0xffffu) | (v[8 * w + 1] << 16);
+                    d.y = (v[8 * w + 2] & 0xffffu) | (v[8 * w + 3] << 16);
+                    d.z = (v[8 * w + 4] & 0xffffu) | (v[8 * w + 5] << 16);
+                    d.w = (v[8 * w + 6] & 0xffffu) | (v[8 * w + 7] << 16);
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(q) + w;
+                    if constexpr (NT) __builtin_nontemporal_store(d, dst);
+                    else *dst = d;
+                }
+            } else {
+                u32x2 d;
+                d.x = (v[0] & 0xffffu) | (v[1] << 16);
+                d.y = (v[2] & 0xffffu) | (v[3] << 16);
+                u32x2 *dst = reinterpret_cast<u32x2 *>(q);
+                if constexpr (NT) __builtin_nontemporal_store(d, dst);
+                else *dst = d;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (e < count) q[e] = (uint16_t)v[e];
+        }
+    } else {
+        uint32_t *q = static_cast<uint32_t *>(p) + i;
+        if constexpr (VEC) {
+#pragma unroll
+            for (int w = 0; w < E / 4; ++w) {
+                u32x4 d;
+                d.x = v[4 * w + 0];
+                d.y = v[4 * w + 1];
+                d.z = v[4 * w + 2];
+                d.w = v[4 * w + 3];
+                u32x4 *dst = reinterpret_cast<u32x4 *>(q) + w;
+                if constexpr (NT) __builtin_nontemporal_store(d, dst);
+                else *dst = d;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (e < count) q[e] = v[e];
+        }
+    }
+}
+
+}  // namespace ecmd

@@ -1,0 +1,754 @@
+// ecmd_host.cpp -- the C ABI: Command building, validation, lowering, path
+// selection and launch.
+//
+// Command model (rocRoller "Design Overview", sections "Command Class",
+// "Operations", "CommandArgument", "Command Kernel"): operations are appended
+// in order and named by tags; loads, scalars and stores allocate
+// CommandArguments whose values arrive at launch in declaration order.  The
+// first launch freezes the Command and lowers it (once) to a Program (see
+// ecmd_tape.h); each launch then checks the argument values, picks a kernel
+// and a launch geometry, packs one argument block and enqueues one kernel.
+//
+// Error rule (Silk "AMDGPU Backend", section "AQL Dispatch Packets": validate
+// everything before the runtime queue sees work): every check runs before the
+// first HIP call of a launch, so a failing launch submits nothing.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/ecmd.h"
+#include "ecmd_tape.h"
+
+using namespace ecmd;
+
+namespace {
+
+enum NodeKind { N_LOAD = 1, N_SCALAR = 2, N_OP = 3 };
+
+struct Node {
+    int kind, dtype, op, a, b, arg;
+};
+
+struct ArgDecl {
+    int kind;       // CMD_ARG_TENSOR or CMD_ARG_SCALAR
+    int dtype;
+    int rank;       // tensors
+    bool output;
+    int tag;        // value produced (load/scalar) or stored (store)
+};
+
+struct View {
+    char *ptr;
+    int64_t s0, s1;
+    int dtype;
+};
+
+struct Bound {
+    int64_t rows = 0, cols = 0;
+    View in[kMaxIn];
+    View out[kMaxOut];
+    uint32_t uni[kMaxUni];
+};
+
+struct Selection {
+    int path = CMD_PATH_NONE;
+    int variant = -1;
+    bool vec = false;
+    bool nt = false;
+    int n_staged = 0;
+    uint8_t staged[kMaxIn] = {};
+    int64_t grid = 0;
+    int block = 0;
+    int lds = 0;
+    int e = 0;
+    const char *name = "";
+};
+
+}  // namespace
+
+struct ecmd_command {
+    std::vector<Node> nodes;
+    std::vector<ArgDecl> args;
+    std::vector<std::pair<int, int>> stores;  // (tag, arg)
+    bool frozen = false;
+    int lower_status = 1;                     // 1 = not lowered yet
+    Program prog{};
+    int in_arg[kMaxIn];                       // CommandArgument index of input k
+    int uni_arg[kMaxUni];
+    int out_arg[kMaxOut];
+    std::string err;
+};
+
+namespace {
+
+thread_local std::string g_create_err;
+
+int fail(cmd_t h, int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (h) h->err = buf;
+    else g_create_err = buf;
+    return code;
+}
+
+bool valid_dtype(int d) { return d == CMD_F16 || d == CMD_F32 || d == CMD_I32; }
+int esize(int d) { return d == CMD_F16 ? 2 : 4; }
+const char *dtype_name(int d) { return d == CMD_F16 ? "f16" : d == CMD_F32 ? "f32" : d == CMD_I32 ? "i32" : "?"; }
+
+int opcode_for(int op, int src, int dst)
+{
+    switch (op) {
+    case E_ADD: return dst == CMD_F32 ? C_ADD_F32 : C_ADD_I32;
+    case E_SUB: return dst == CMD_F32 ? C_SUB_F32 : C_SUB_I32;
+    case E_MUL: return dst == CMD_F32 ? C_MUL_F32 : C_MUL_I32;
+    case E_NEG: return dst == CMD_F32 ? C_NEG_F32 : dst == CMD_I32 ? C_NEG_I32 : C_NEG_F16;
+    case E_CVT:
+        if (src == dst) return C_MOV;
+        if (src == CMD_F16 && dst == CMD_F32) return C_CVT_F16_F32;
+        if (src == CMD_F32 && dst == CMD_F16) return C_CVT_F32_F16;
+        if (src == CMD_I32 && dst == CMD_F32) return C_CVT_I32_F32;
+        if (src == CMD_F32 && dst == CMD_I32) return C_CVT_F32_I32;
+        if (src == CMD_I32 && dst == CMD_F16) return C_CVT_I32_F16;
+        return C_CVT_F16_I32;
+    }
+    return C_MOV;
+}
+
+const char *code_name(int c)
+{
+    static const char *names[] = {"mov", "add.f32", "sub.f32", "mul.f32", "add.i32", "sub.i32",
+                                  "mul.i32", "neg.f32", "neg.i32", "neg.f16", "cvt.f16.f32",
+                                  "cvt.f32.f16", "cvt.i32.f32", "cvt.f32.i32", "cvt.i32.f16",
+                                  "cvt.f16.i32"};
+    return c >= 0 && c < C_COUNT ? names[c] : "?";
+}
+
+// ---------------------------------------------------------------------------
+// Lowering: live values, input / uniform numbering, register slots.
+
+int lower(cmd_t h)
+{
+    if (h->lower_status != 1) return h->lower_status;
+    const int n = (int)h->nodes.size();
+    if (h->stores.empty())
+        return h->lower_status = fail(h, CMD_E_NOSTORE, "the Command has no store");
+    if ((int)h->stores.size() > kMaxOut)
+        return h->lower_status = fail(h, CMD_E_LIMIT, "%d stores exceed the limit of %d",
+                                      (int)h->stores.size(), kMaxOut);
+    // 1. Live values: everything a store depends on (later operations that no
+    //    store reaches are dropped).
+    std::vector<char> live(n, 0);
+    for (auto &s : h->stores) live[s.first] = 1;
+    for (int t = n - 1; t >= 0; --t) {
+        if (!live[t] || h->nodes[t].kind != N_OP) continue;
+        live[h->nodes[t].a] = 1;
+        if (h->nodes[t].b >= 0) live[h->nodes[t].b] = 1;
+    }
+    // 2. A conversion to the same dtype is the value itself.
+    std::vector<int> alias(n), code(n, -1);
+    for (int t = 0; t < n; ++t) {
+        alias[t] = t;
+        const Node &nd = h->nodes[t];
+        if (nd.kind != N_OP) continue;
+        code[t] = opcode_for(nd.op, h->nodes[nd.a].dtype, nd.dtype);
+        if (code[t] == C_MOV) alias[t] = alias[nd.a];
+    }
+    // 3. Inputs and uniform values in insertion order; operation count; last uses.
+    Program P{};
+    std::vector<int> ref(n, -1), last_use(n, -1);
+    int n_ops = 0;
+    for (int t = 0; t < n; ++t) {
+        if (!live[t]) continue;
+        const Node &nd = h->nodes[t];
+        if (nd.kind == N_LOAD) {
+            if (P.n_in >= kMaxIn)
+                return h->lower_status = fail(h, CMD_E_LIMIT, "more than %d live tensor loads", kMaxIn);
+            h->in_arg[P.n_in] = nd.arg;
+            P.in_ty[P.n_in] = (uint8_t)nd.dtype;
+            ref[t] = kRefIn + P.n_in++;
+        } else if (nd.kind == N_SCALAR) {
+            if (P.n_uni >= kMaxUni)
+                return h->lower_status = fail(h, CMD_E_LIMIT, "more than %d live scalars", kMaxUni);
+            h->uni_arg[P.n_uni] = nd.arg;
+            ref[t] = kRefUni + P.n_uni++;
+        } else if (code[t] != C_MOV) {
+            last_use[alias[nd.a]] = n_ops;
+            if (nd.b >= 0) last_use[alias[nd.b]] = n_ops;
+            ++n_ops;
+        }
+    }
+    if (n_ops > kMaxOps)
+        return h->lower_status = fail(h, CMD_E_LIMIT, "%d operations exceed the limit of %d", n_ops, kMaxOps);
+    for (auto &s : h->stores) last_use[alias[s.first]] = n_ops;   // stored values live to the end
+    // 4. Slots in insertion order; an operand's slot is free again after its
+    //    last use, so the result may take it.
+    bool busy[kMaxSlot] = {};
+    int i = 0;
+    for (int t = 0; t < n; ++t) {
+        if (!live[t] || h->nodes[t].kind != N_OP || code[t] == C_MOV) continue;
+        const Node &nd = h->nodes[t];
+        const int a = alias[nd.a], b = nd.b >= 0 ? alias[nd.b] : -1;
+        int ra = ref[a], rb = b >= 0 ? ref[b] : kRefNone;
+        for (int v : {a, b})
+            if (v >= 0 && ref[v] >= kRefSlot && ref[v] < kRefUni && last_use[v] <= i)
+                busy[ref[v] - kRefSlot] = false;
+        int slot = -1;
+        for (int s = 0; s < kMaxSlot; ++s)
+            if (!busy[s]) { slot = s; break; }
+        if (slot < 0)
+            return h->lower_status = fail(h, CMD_E_LIMIT, "more than %d temporaries alive at once", kMaxSlot);
+        busy[slot] = true;
+        ref[t] = kRefSlot + slot;
+        // Commutative operations list the smaller reference first so that one
+        // Command written either way lowers to the same Program (x+y and y+x,
+        // x*y and y*x are equal bit for bit in IEEE and two's-complement
+        // arithmetic; only NaN payloads, which carry no meaning here, may differ).
+        const int c = code[t];
+        if ((c == C_ADD_F32 || c == C_MUL_F32 || c == C_ADD_I32 || c == C_MUL_I32) && rb < ra)
+            std::swap(ra, rb);
+        P.ops[i].code = (uint8_t)c;
+        P.ops[i].dst = (uint8_t)ref[t];
+        P.ops[i].a = (uint8_t)ra;
+        P.ops[i].b = (uint8_t)rb;
+        ++i;
+    }
+    P.n_ops = (uint8_t)i;
+    for (size_t k = 0; k < h->stores.size(); ++k) {
+        P.out_ref[k] = (uint8_t)ref[alias[h->stores[k].first]];
+        P.out_ty[k] = (uint8_t)h->nodes[h->stores[k].first].dtype;
+        h->out_arg[k] = h->stores[k].second;
+    }
+    P.n_out = (uint8_t)h->stores.size();
+    h->prog = P;
+    return h->lower_status = CMD_OK;
+}
+
+int program_match_linear(const Program &P)
+{
+    int k = 0;
+#define ECMD_MATCH(name, prog) \
+    if (std::memcmp(&P, &prog, sizeof(Program)) == 0) return k; \
+    ++k;
+    ECMD_LINEAR_SPECIALISED(ECMD_MATCH)
+#undef ECMD_MATCH
+    return -1;
+}
+
+const char *linear_name(int variant)
+{
+    int k = 0;
+#define ECMD_NAME(name, prog) \
+    if (variant == k) return "linear_" #name; \
+    ++k;
+    ECMD_LINEAR_SPECIALISED(ECMD_NAME)
+#undef ECMD_NAME
+    return "linear_generic";
+}
+
+// ---------------------------------------------------------------------------
+// Argument binding and validation.
+
+bool env_flag(const char *name)
+{
+    const char *v = std::getenv(name);
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+int64_t env_int(const char *name, int64_t dflt)
+{
+    const char *v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::strtoll(v, nullptr, 10);
+}
+
+// Highest element offset a view reaches (views have non-negative strides).
+__int128 max_offset(int64_t rows, int64_t cols, int64_t s0, int64_t s1)
+{
+    return (__int128)(rows - 1) * s0 + (__int128)(cols - 1) * s1;
+}
+
+// A store view must be one-to-one.  Accepted: after dropping size-1
+// dimensions, the inner (smaller-stride) dimension has stride >= 1 and the
+// outer stride is at least the inner extent.  (Sufficient, not necessary.)
+bool injective(int64_t rows, int64_t cols, int64_t s0, int64_t s1)
+{
+    if (rows <= 1 && cols <= 1) return true;
+    if (rows <= 1) return s1 >= 1;
+    if (cols <= 1) return s0 >= 1;
+    if (s0 >= s1) return s1 >= 1 && (__int128)s0 >= (__int128)cols * s1;
+    return s0 >= 1 && (__int128)s1 >= (__int128)rows * s0;
+}
+
+int bind(cmd_t h, const cmd_arg *args, int nargs, Bound &B)
+{
+    if (nargs != (int)h->args.size())
+        return fail(h, CMD_E_ARG, "expected %d argument values, got %d", (int)h->args.size(), nargs);
+    if (nargs > 0 && !args) return fail(h, CMD_E_ARG, "args is NULL");
+    bool have_shape = false;
+    for (int i = 0; i < nargs; ++i) {
+        const cmd_arg &a = args[i];
+        const ArgDecl &d = h->args[i];
+        if (a.kind != d.kind)
+            return fail(h, CMD_E_ARG, "argument %d: kind %d, declared %d", i, a.kind, d.kind);
+        if (a.dtype != d.dtype)
+            return fail(h, CMD_E_DTYPE, "argument %d: dtype %s, declared %s", i, dtype_name(a.dtype),
+                        dtype_name(d.dtype));
+        if (a.reserved != 0) return fail(h, CMD_E_ARG, "argument %d: reserved field is not 0", i);
+        if (d.kind != CMD_ARG_TENSOR) {
+            if (d.dtype == CMD_F16 && (a.bits >> 16) != 0)
+                return fail(h, CMD_E_ARG, "argument %d: binary16 scalar has bits above bit 15", i);
+            continue;
+        }
+        const int64_t rows = d.rank == 1 ? 1 : a.size[0];
+        const int64_t cols = d.rank == 1 ? a.size[0] : a.size[1];
+        if (rows < 0 || cols < 0) return fail(h, CMD_E_SHAPE, "argument %d: negative size", i);
+        if (a.stride[0] < 0 || (d.rank == 2 && a.stride[1] < 0))
+            return fail(h, CMD_E_STRIDE, "argument %d: negative stride", i);
+        if (!have_shape) {
+            B.rows = rows;
+            B.cols = cols;
+            have_shape = true;
+        } else if (rows != B.rows || cols != B.cols) {
+            return fail(h, CMD_E_SHAPE, "argument %d: shape %lldx%lld differs from %lldx%lld", i,
+                        (long long)rows, (long long)cols, (long long)B.rows, (long long)B.cols);
+        }
+    }
+    if (!have_shape) return fail(h, CMD_E_SHAPE, "no tensor argument gives the shape");
+    if (B.rows > INT32_MAX || B.cols > ((int64_t)1 << 40) || (__int128)B.rows * B.cols > ((__int128)1 << 40))
+        return fail(h, CMD_E_LIMIT, "shape %lldx%lld exceeds 2^40 elements", (long long)B.rows,
+                    (long long)B.cols);
+    const bool empty = B.rows == 0 || B.cols == 0;
+    auto view_of = [&](int i, View &v) -> int {
+        const cmd_arg &a = args[i];
+        const ArgDecl &d = h->args[i];
+        v.ptr = static_cast<char *>(a.ptr);
+        v.dtype = d.dtype;
+        if (d.rank == 1) {
+            v.s0 = 0;
+            v.s1 = a.stride[0];
+        } else {
+            v.s0 = a.stride[0];
+            v.s1 = a.stride[1];
+        }
+        if (!empty) {
+            if (!v.ptr) return fail(h, CMD_E_ARG, "argument %d: NULL pointer", i);
+            if (max_offset(B.rows, B.cols, v.s0, v.s1) >= ((__int128)1 << 48))
+                return fail(h, CMD_E_LIMIT, "argument %d: view spans more than 2^48 elements", i);
+            if ((reinterpret_cast<uintptr_t>(v.ptr) % (uintptr_t)esize(d.dtype)) != 0)
+                return fail(h, CMD_E_ARG, "argument %d: pointer not aligned to its element size", i);
+        }
+        return CMD_OK;
+    };
+    for (int k = 0; k < h->prog.n_in; ++k) {
+        int rc = view_of(h->in_arg[k], B.in[k]);
+        if (rc) return rc;
+    }
+    for (int k = 0; k < h->prog.n_out; ++k) {
+        const int i = h->out_arg[k];
+        int rc = view_of(i, B.out[k]);
+        if (rc) return rc;
+        if (!empty && !injective(B.rows, B.cols, B.out[k].s0, B.out[k].s1))
+            return fail(h, CMD_E_STRIDE, "argument %d: store view maps two indexes to one element", i);
+    }
+    for (int k = 0; k < h->prog.n_uni; ++k) B.uni[k] = args[h->uni_arg[k]].bits;
+    if (empty) return CMD_OK;
+    // Overlap: outputs pairwise disjoint; an output meets an input only as the identical view.
+    auto range = [&](const View &v, uintptr_t &lo, uintptr_t &hi) {
+        lo = reinterpret_cast<uintptr_t>(v.ptr);
+        hi = lo + (uintptr_t)((max_offset(B.rows, B.cols, v.s0, v.s1) + 1) * esize(v.dtype));
+    };
+    for (int k = 0; k < h->prog.n_out; ++k) {
+        uintptr_t lo, hi;
+        range(B.out[k], lo, hi);
+        for (int j = 0; j < k; ++j) {
+            uintptr_t lo2, hi2;
+            range(B.out[j], lo2, hi2);
+            if (lo < hi2 && lo2 < hi)
+                return fail(h, CMD_E_ALIAS, "outputs %d and %d overlap", h->out_arg[j], h->out_arg[k]);
+        }
+        for (int j = 0; j < h->prog.n_in; ++j) {
+            uintptr_t lo2, hi2;
+            range(B.in[j], lo2, hi2);
+            if (!(lo < hi2 && lo2 < hi)) continue;
+            const View &o = B.out[k], &in = B.in[j];
+            const bool same = o.ptr == in.ptr && o.dtype == in.dtype &&
+                              (B.rows == 1 || o.s0 == in.s0) && (B.cols == 1 || o.s1 == in.s1);
+            if (!same)
+                return fail(h, CMD_E_ALIAS, "output argument %d overlaps input argument %d other than as the identical view",
+                            h->out_arg[k], h->in_arg[j]);
+        }
+    }
+    return CMD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Path and geometry.
+
+int g_cu_count[64];   // per device ordinal, 0 = not queried yet
+
+int cu_count_cached(int dev) { return dev >= 0 && dev < 64 && g_cu_count[dev] > 0 ? g_cu_count[dev] : 256; }
+
+bool flat(const Bound &B, const View &v)
+{
+    return (B.cols == 1 || v.s1 == 1) && (B.rows == 1 || v.s0 == B.cols);
+}
+
+bool aligned(const void *p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes == 0; }
+
+void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
+{
+    const Program &P = h->prog;
+    const int64_t numel = B.rows * B.cols;
+    if (numel == 0) {
+        S.path = CMD_PATH_NONE;
+        S.name = "none";
+        return;
+    }
+    const bool force_generic = env_flag("ECMD_FORCE_GENERIC");
+    bool all_flat = true;
+    for (int k = 0; k < P.n_in; ++k) all_flat = all_flat && flat(B, B.in[k]);
+    for (int k = 0; k < P.n_out; ++k) all_flat = all_flat && flat(B, B.out[k]);
+    if (all_flat) {
+        S.path = CMD_PATH_LINEAR;
+        S.vec = true;
+        for (int k = 0; k < P.n_in; ++k) S.vec = S.vec && aligned(B.in[k].ptr, 16);
+        for (int k = 0; k < P.n_out; ++k) S.vec = S.vec && aligned(B.out[k].ptr, 16);
+        S.variant = (S.vec && !force_generic) ? program_match_linear(P) : -1;
+        S.nt = env_flag("ECMD_NT_STORE");
+        S.e = kLinearE;
+        S.block = kLinearBlock;
+        const int64_t chunks = numel / kLinearE;
+        int64_t need = (chunks + kLinearBlock - 1) / kLinearBlock;
+        if (need < 1) need = 1;
+        const int64_t per_cu = env_int("ECMD_BLOCKS_PER_CU", 8);
+        const int64_t cap = std::max<int64_t>(1, per_cu * cu_count);
+        S.grid = std::min(need, cap);
+        S.name = S.vec ? linear_name(S.variant) : "linear_generic_unaligned";
+        return;
+    }
+    // Tiled: rank 2 with every output and every input either inner-contiguous
+    // (direct) or outer-contiguous (staged through LDS), with vector-aligned rows.
+    bool tiled = B.rows >= 2 && B.cols >= 2;
+    int n_staged = 0, mask = 0;
+    for (int k = 0; k < P.n_out && tiled; ++k) {
+        const View &v = B.out[k];
+        const int64_t vb = 4 * esize(v.dtype);
+        tiled = v.s1 == 1 && aligned(v.ptr, vb) && (v.s0 * esize(v.dtype)) % vb == 0;
+    }
+    for (int k = 0; k < P.n_in && tiled; ++k) {
+        const View &v = B.in[k];
+        const int64_t vb = 4 * esize(v.dtype);
+        if (v.s1 == 1) {
+            tiled = aligned(v.ptr, vb) && (v.s0 * esize(v.dtype)) % vb == 0;
+        } else if (v.s0 == 1) {
+            tiled = aligned(v.ptr, vb) && (v.s1 * esize(v.dtype)) % vb == 0;
+            S.staged[k] = (uint8_t)(++n_staged);
+            mask |= 1 << k;
+        } else {
+            tiled = false;
+        }
+    }
+    if (tiled && n_staged <= 3) {
+        S.path = CMD_PATH_TILED;
+        S.n_staged = n_staged;
+        S.variant = (!force_generic && std::memcmp(&P, &kProgAddScaledF32, sizeof(Program)) == 0 && mask == 0x2) ? 0 : -1;
+        S.e = 4;
+        S.block = kTileBlock;
+        S.grid = ((B.rows + kTileRows - 1) / kTileRows) * ((B.cols + kTileCols - 1) / kTileCols);
+        S.lds = n_staged * kTileCols * (kTileRows + 1) * 4;
+        S.name = S.variant == 0 ? "tiled_add_scaled_f32" : "tiled_generic";
+        return;
+    }
+    std::memset(S.staged, 0, sizeof S.staged);
+    S.n_staged = 0;
+    S.path = CMD_PATH_GATHER;
+    S.variant = -1;
+    S.e = kGatherE;
+    S.block = kGatherBlock;
+    const int64_t total = B.rows * ((B.cols + kGatherE - 1) / kGatherE);
+    S.grid = std::max<int64_t>(1, std::min<int64_t>((total + kGatherBlock - 1) / kGatherBlock, 8LL * cu_count));
+    S.name = "gather_generic";
+}
+
+int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int cu_count)
+{
+    h->frozen = true;
+    int rc = lower(h);
+    if (rc) return rc;
+    rc = bind(h, args, nargs, B);
+    if (rc) return rc;
+    select_path(h, B, cu_count, S);
+    return CMD_OK;
+}
+
+void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
+{
+    std::memset(&A, 0, sizeof A);
+    for (int k = 0; k < h->prog.n_in; ++k) {
+        A.in[k] = B.in[k].ptr;
+        A.in_s0[k] = B.in[k].s0;
+        A.in_s1[k] = B.in[k].s1;
+        A.in_staged[k] = S.staged[k];
+    }
+    for (int k = 0; k < h->prog.n_out; ++k) {
+        A.out[k] = B.out[k].ptr;
+        A.out_s0[k] = B.out[k].s0;
+        A.out_s1[k] = B.out[k].s1;
+    }
+    A.rows = B.rows;
+    A.cols = B.cols;
+    A.tiles_c = (B.cols + kTileCols - 1) / kTileCols;
+    std::memcpy(A.uni, B.uni, sizeof A.uni);
+    A.prog = h->prog;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The C ABI.
+
+extern "C" {
+
+int32_t cmd_version(void) { return 100; }
+
+int cmd_create(cmd_t *out)
+{
+    if (!out) return fail(nullptr, CMD_E_ARG, "out is NULL");
+    cmd_t h = new (std::nothrow) ecmd_command();
+    if (!h) return fail(nullptr, CMD_E_NOMEM, "out of host memory");
+    *out = h;
+    return CMD_OK;
+}
+
+int cmd_destroy(cmd_t h)
+{
+    delete h;
+    return CMD_OK;
+}
+
+static int add_node(cmd_t h, const Node &n, cmd_tag *tag)
+{
+    if ((int)h->nodes.size() >= CMD_MAX_NODES)
+        return fail(h, CMD_E_LIMIT, "more than %d operations in one Command", CMD_MAX_NODES);
+    h->nodes.push_back(n);
+    if (tag) *tag = (cmd_tag)h->nodes.size() - 1;
+    return CMD_OK;
+}
+
+int cmd_load(cmd_t h, int32_t dtype, int32_t rank, cmd_tag *tag, int32_t *arg_index)
+{
+    if (!h) return CMD_E_ARG;
+    if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
+    if (!valid_dtype(dtype)) return fail(h, CMD_E_DTYPE, "unknown dtype %d", dtype);
+    if (rank != 1 && rank != 2) return fail(h, CMD_E_LIMIT, "rank %d is not 1 or 2", rank);
+    if ((int)h->args.size() >= CMD_MAX_ARGS)
+        return fail(h, CMD_E_LIMIT, "more than %d CommandArguments", CMD_MAX_ARGS);
+    const int arg = (int)h->args.size();
+    int rc = add_node(h, Node{N_LOAD, dtype, 0, -1, -1, arg}, tag);
+    if (rc) return rc;
+    h->args.push_back(ArgDecl{CMD_ARG_TENSOR, dtype, rank, false, (int)h->nodes.size() - 1});
+    if (arg_index) *arg_index = arg;
+    return CMD_OK;
+}
+
+int cmd_scalar(cmd_t h, int32_t dtype, cmd_tag *tag, int32_t *arg_index)
+{
+    if (!h) return CMD_E_ARG;
+    if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
+    if (!valid_dtype(dtype)) return fail(h, CMD_E_DTYPE, "unknown dtype %d", dtype);
+    if ((int)h->args.size() >= CMD_MAX_ARGS)
+        return fail(h, CMD_E_LIMIT, "more than %d CommandArguments", CMD_MAX_ARGS);
+    const int arg = (int)h->args.size();
+    int rc = add_node(h, Node{N_SCALAR, dtype, 0, -1, -1, arg}, tag);
+    if (rc) return rc;
+    h->args.push_back(ArgDecl{CMD_ARG_SCALAR, dtype, 0, false, (int)h->nodes.size() - 1});
+    if (arg_index) *arg_index = arg;
+    return CMD_OK;
+}
+
+int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, cmd_tag *tag)
+{
+    if (!h) return CMD_E_ARG;
+    if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
+    const int n = (int)h->nodes.size();
+    if (opcode < E_ADD || opcode > E_CVT) return fail(h, CMD_E_ARG, "unknown opcode %d", opcode);
+    if (!valid_dtype(result_dtype)) return fail(h, CMD_E_DTYPE, "unknown dtype %d", result_dtype);
+    if (a < 0 || a >= n) return fail(h, CMD_E_TAG, "tag %d does not name an earlier value", a);
+    const int da = h->nodes[a].dtype;
+    if (opcode == E_NEG || opcode == E_CVT) {
+        if (b != -1) return fail(h, CMD_E_ARG, "unary operation takes b = -1");
+        if (opcode == E_NEG && result_dtype != da)
+            return fail(h, CMD_E_DTYPE, "neg of %s cannot give %s", dtype_name(da), dtype_name(result_dtype));
+    } else {
+        if (b < 0 || b >= n) return fail(h, CMD_E_TAG, "tag %d does not name an earlier value", b);
+        const int db = h->nodes[b].dtype;
+        if (da != db)
+            return fail(h, CMD_E_DTYPE, "operands are %s and %s", dtype_name(da), dtype_name(db));
+        if (da == CMD_F16)
+            return fail(h, CMD_E_DTYPE, "binary16 is a storage type: convert to f32 first");
+        if (result_dtype != da)
+            return fail(h, CMD_E_DTYPE, "result %s differs from operands %s", dtype_name(result_dtype),
+                        dtype_name(da));
+    }
+    return add_node(h, Node{N_OP, result_dtype, opcode, a, b, -1}, tag);
+}
+
+int cmd_store(cmd_t h, cmd_tag value, int32_t rank, int32_t *arg_index)
+{
+    if (!h) return CMD_E_ARG;
+    if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
+    if (value < 0 || value >= (int)h->nodes.size())
+        return fail(h, CMD_E_TAG, "tag %d does not name an earlier value", value);
+    if (rank != 1 && rank != 2) return fail(h, CMD_E_LIMIT, "rank %d is not 1 or 2", rank);
+    if ((int)h->args.size() >= CMD_MAX_ARGS)
+        return fail(h, CMD_E_LIMIT, "more than %d CommandArguments", CMD_MAX_ARGS);
+    if ((int)h->stores.size() >= CMD_MAX_STORES)
+        return fail(h, CMD_E_LIMIT, "more than %d stores", CMD_MAX_STORES);
+    const int arg = (int)h->args.size();
+    h->args.push_back(ArgDecl{CMD_ARG_TENSOR, h->nodes[value].dtype, rank, true, value});
+    h->stores.emplace_back(value, arg);
+    if (arg_index) *arg_index = arg;
+    return CMD_OK;
+}
+
+int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info)
+{
+    if (!h) return CMD_E_ARG;
+    if (!info) return fail(h, CMD_E_ARG, "info is NULL");
+    Bound B;
+    Selection S;
+    int dev = 0;
+    int rc = prepare(h, args, nargs, B, S, cu_count_cached(dev));
+    if (rc) return rc;
+    std::memset(info, 0, sizeof *info);
+    info->path = S.path;
+    info->specialised = S.variant >= 0;
+    info->vector = S.path == CMD_PATH_TILED ? 1 : S.vec;
+    info->elems_per_thread = S.e;
+    info->grid = S.grid;
+    info->block = S.block;
+    info->lds_bytes = S.lds;
+    info->rows = B.rows;
+    info->cols = B.cols;
+    std::snprintf(info->kernel, sizeof info->kernel, "%s", S.name);
+    h->err.clear();
+    return CMD_OK;
+}
+
+int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
+{
+    if (!h) return CMD_E_ARG;
+    h->frozen = true;
+    int rc = lower(h);
+    if (rc) return rc;
+    Bound B;
+    rc = bind(h, args, nargs, B);
+    if (rc) return rc;
+    if (B.rows * B.cols == 0) return CMD_OK;
+    // All checks passed; from here on HIP is called.
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(h, CMD_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64 && g_cu_count[dev] == 0) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail(h, CMD_E_LAUNCH, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+        g_cu_count[dev] = cus > 0 ? cus : 256;
+    }
+    Selection S;
+    select_path(h, B, cu_count_cached(dev), S);
+    if (env_flag("ECMD_DUMP_TAPE")) {
+        char buf[4096];
+        cmd_dump(h, buf, sizeof buf);
+        std::fprintf(stderr, "[ecmd] %s grid=%lld block=%d\n%s", S.name, (long long)S.grid, S.block, buf);
+    }
+    const LaunchGeometry g{S.grid, S.block};
+    int herr = 0;
+    if (S.path == CMD_PATH_LINEAR) {
+        LinearArgs A;
+        std::memset(&A, 0, sizeof A);
+        for (int k = 0; k < h->prog.n_in; ++k) A.in[k] = B.in[k].ptr;
+        for (int k = 0; k < h->prog.n_out; ++k) A.out[k] = B.out[k].ptr;
+        A.n = B.rows * B.cols;
+        std::memcpy(A.uni, B.uni, sizeof A.uni);
+        A.prog = h->prog;
+        herr = launch_linear(S.variant, S.vec, S.nt, A, g, hip_stream);
+    } else {
+        StridedArgs A;
+        fill_strided(h, B, S, A);
+        herr = S.path == CMD_PATH_TILED ? launch_tiled(S.variant, A, g, hip_stream)
+                                        : launch_gather(A, g, hip_stream);
+    }
+    if (herr != 0)
+        return fail(h, CMD_E_LAUNCH, "%s launch failed: %s", S.name, hipGetErrorString((hipError_t)herr));
+    h->err.clear();
+    return CMD_OK;
+}
+
+int64_t cmd_dump(cmd_t h, char *buf, int64_t cap)
+{
+    if (!h) return CMD_E_ARG;
+    h->frozen = true;
+    int rc = lower(h);
+    if (rc) return rc;
+    const Program &P = h->prog;
+    std::string s;
+    char line[160];
+    auto refname = [&](int r) -> std::string {
+        char b[16];
+        if (r == kRefNone) return "-";
+        if (r < kRefSlot) std::snprintf(b, sizeof b, "in%d", r - kRefIn);
+        else if (r < kRefUni) std::snprintf(b, sizeof b, "s%d", r - kRefSlot);
+        else std::snprintf(b, sizeof b, "u%d", r - kRefUni);
+        return b;
+    };
+    for (int k = 0; k < P.n_in; ++k) {
+        std::snprintf(line, sizeof line, "in%d = load.%s arg%d\n", k, dtype_name(P.in_ty[k]), h->in_arg[k]);
+        s += line;
+    }
+    for (int k = 0; k < P.n_uni; ++k) {
+        std::snprintf(line, sizeof line, "u%d = scalar.%s arg%d\n", k, dtype_name(h->args[h->uni_arg[k]].dtype),
+                      h->uni_arg[k]);
+        s += line;
+    }
+    for (int i = 0; i < P.n_ops; ++i) {
+        const TapeOp &o = P.ops[i];
+        if (o.b == kRefNone)
+            std::snprintf(line, sizeof line, "%s = %s %s\n", refname(o.dst).c_str(), code_name(o.code),
+                          refname(o.a).c_str());
+        else
+            std::snprintf(line, sizeof line, "%s = %s %s, %s\n", refname(o.dst).c_str(), code_name(o.code),
+                          refname(o.a).c_str(), refname(o.b).c_str());
+        s += line;
+    }
+    for (int k = 0; k < P.n_out; ++k) {
+        std::snprintf(line, sizeof line, "store.%s arg%d <- %s\n", dtype_name(P.out_ty[k]), h->out_arg[k],
+                      refname(P.out_ref[k]).c_str());
+        s += line;
+    }
+    if (buf && cap > 0) {
+        const int64_t n = std::min<int64_t>(cap - 1, (int64_t)s.size());
+        std::memcpy(buf, s.data(), (size_t)n);
+        buf[n] = 0;
+    }
+    return (int64_t)s.size();
+}
+
+const char *cmd_last_error(cmd_t h)
+{
+    if (!h) return g_create_err.c_str();
+    return h->err.c_str();
+}
+
+}  // extern "C"

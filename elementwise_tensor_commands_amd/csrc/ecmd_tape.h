@@ -1,0 +1,211 @@
+// ecmd_tape.h -- the lowered form of a Command, shared by the host lowerer and
+// the gfx950 kernels.
+//
+// A Command (rocRoller "Design Overview", sections "Command Class" and
+// "Operations") is lowered once into a Program: a straight-line list of
+// per-element operations in insertion order, each reading operand references
+// and writing a register slot.  The Program travels to the GPU inside the
+// kernel argument block, so every wavefront reads the same bytes through the
+// scalar unit and branches on them uniformly (rocRoller "Design Overview",
+// section "Loading Arguments": arguments are loaded into registers once).
+//
+// Operand references (one byte):
+//   kRefIn  + k  (0..7)   input k: the k-th live tensor load, held in registers
+//   kRefSlot + k (8..15)  temporary slot k
+//   kRefUni + k  (16..23) uniform value k: the k-th live scalar argument
+//   kRefNone     (255)    no operand (unary operations)
+#pragma once
+#include <stdint.h>
+
+namespace ecmd {
+
+constexpr int kMaxIn = 8;
+constexpr int kMaxOut = 4;
+constexpr int kMaxUni = 8;
+constexpr int kMaxSlot = 8;
+constexpr int kMaxOps = 32;
+
+constexpr uint8_t kRefIn = 0;
+constexpr uint8_t kRefSlot = 8;
+constexpr uint8_t kRefUni = 16;
+constexpr uint8_t kRefNone = 255;
+
+// Element types; the numbers equal the public CMD_F16 / CMD_F32 / CMD_I32.
+enum Ty : uint8_t { TY_F16 = 1, TY_F32 = 2, TY_I32 = 3 };
+
+// One opcode per (E_ operation, type) pair, so that the evaluator dispatches
+// on a single byte.
+enum Code : uint8_t {
+    C_MOV = 0,
+    C_ADD_F32,
+    C_SUB_F32,
+    C_MUL_F32,
+    C_ADD_I32,
+    C_SUB_I32,
+    C_MUL_I32,
+    C_NEG_F32,
+    C_NEG_I32,
+    C_NEG_F16,
+    C_CVT_F16_F32,
+    C_CVT_F32_F16,
+    C_CVT_I32_F32,
+    C_CVT_F32_I32,
+    C_CVT_I32_F16,
+    C_CVT_F16_I32,
+    C_COUNT
+};
+
+constexpr bool code_is_binary(uint8_t c)
+{
+    return c == C_ADD_F32 || c == C_SUB_F32 || c == C_MUL_F32 || c == C_ADD_I32 ||
+           c == C_SUB_I32 || c == C_MUL_I32;
+}
+
+struct TapeOp {
+    uint8_t code, dst, a, b;
+};
+
+// The lowered Command.  Unused entries are zero so that two Programs can be
+// compared byte for byte.
+struct Program {
+    uint8_t n_in, n_uni, n_ops, n_out;
+    uint8_t in_ty[kMaxIn];
+    uint8_t out_ty[kMaxOut];
+    uint8_t out_ref[kMaxOut];
+    TapeOp ops[kMaxOps];
+};
+
+constexpr int ty_size(uint8_t t) { return t == TY_F16 ? 2 : 4; }
+
+// ---------------------------------------------------------------------------
+// Kernel argument blocks.  Each kernel takes one of these by value; the whole
+// block sits in the kernarg segment (explicit arguments first, as in the Code
+// Object V6 layout described in Silk "AMDGPU Backend", section "Code Object
+// Format").
+
+// Every view is flat contiguous: element i of every operand is at base + i.
+struct LinearArgs {
+    const void *in[kMaxIn];
+    void *out[kMaxOut];
+    int64_t n;
+    uint32_t uni[kMaxUni];
+    Program prog;
+};
+
+// Rank-2 shape (rows x cols) with per-operand element strides.
+struct StridedArgs {
+    const void *in[kMaxIn];
+    void *out[kMaxOut];
+    int64_t in_s0[kMaxIn], in_s1[kMaxIn];
+    int64_t out_s0[kMaxOut], out_s1[kMaxOut];
+    int64_t rows, cols;
+    int64_t tiles_c;          // tiled path: number of column tiles
+    uint32_t uni[kMaxUni];
+    uint8_t in_staged[kMaxIn];  // tiled path: 1 = read through an LDS tile (column-contiguous view)
+    Program prog;
+};
+
+// ---------------------------------------------------------------------------
+// Compile-time-specialised Programs.  A lowered Command that equals one of
+// these byte for byte runs a kernel instantiated for it, in which every
+// operand reference is a compile-time constant; otherwise the generic
+// interpreter runs the same Program from the argument block.
+
+#define ECMD_R_IN(k) uint8_t(kRefIn + (k))
+#define ECMD_R_S(k) uint8_t(kRefSlot + (k))
+#define ECMD_R_U(k) uint8_t(kRefUni + (k))
+
+// z = x + y  (binary32)
+constexpr Program kProgAddF32 = {
+    2, 0, 1, 1, {TY_F32, TY_F32}, {TY_F32}, {ECMD_R_S(0)},
+    {{C_ADD_F32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_IN(1)}}};
+
+// z = (x + y) * w - s  (int32)
+constexpr Program kProgIntFused = {
+    3, 1, 3, 1, {TY_I32, TY_I32, TY_I32}, {TY_I32}, {ECMD_R_S(0)},
+    {{C_ADD_I32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_IN(1)},
+     {C_MUL_I32, ECMD_R_S(0), ECMD_R_IN(2), ECMD_R_S(0)},
+     {C_SUB_I32, ECMD_R_S(0), ECMD_R_S(0), ECMD_R_U(0)}}};
+
+// out = alpha * x + beta * y  (binary32)
+constexpr Program kProgAxpbyF32 = {
+    2, 2, 3, 1, {TY_F32, TY_F32}, {TY_F32}, {ECMD_R_S(0)},
+    {{C_MUL_F32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_U(0)},
+     {C_MUL_F32, ECMD_R_S(1), ECMD_R_IN(1), ECMD_R_U(1)},
+     {C_ADD_F32, ECMD_R_S(0), ECMD_R_S(0), ECMD_R_S(1)}}};
+
+// binary16 x, y, z; t = x*y; u = t + z; v = t - z; out0 = f16(u*v); out1 = u + s
+constexpr Program kProgMixedTwoOut = {
+    3, 1, 9, 2, {TY_F16, TY_F16, TY_F16}, {TY_F16, TY_F32}, {ECMD_R_S(0), ECMD_R_S(1)},
+    {{C_CVT_F16_F32, ECMD_R_S(0), ECMD_R_IN(0), kRefNone},
+     {C_CVT_F16_F32, ECMD_R_S(1), ECMD_R_IN(1), kRefNone},
+     {C_CVT_F16_F32, ECMD_R_S(2), ECMD_R_IN(2), kRefNone},
+     {C_MUL_F32, ECMD_R_S(0), ECMD_R_S(0), ECMD_R_S(1)},
+     {C_ADD_F32, ECMD_R_S(1), ECMD_R_S(0), ECMD_R_S(2)},
+     {C_SUB_F32, ECMD_R_S(0), ECMD_R_S(0), ECMD_R_S(2)},
+     {C_MUL_F32, ECMD_R_S(0), ECMD_R_S(0), ECMD_R_S(1)},
+     {C_CVT_F32_F16, ECMD_R_S(0), ECMD_R_S(0), kRefNone},
+     {C_ADD_F32, ECMD_R_S(1), ECMD_R_S(1), ECMD_R_U(0)}}};
+
+// out = X + alpha * Yt  (binary32; Yt is the transposed view on the tiled path)
+constexpr Program kProgAddScaledF32 = {
+    2, 1, 2, 1, {TY_F32, TY_F32}, {TY_F32}, {ECMD_R_S(0)},
+    {{C_MUL_F32, ECMD_R_S(0), ECMD_R_IN(1), ECMD_R_U(0)},
+     {C_ADD_F32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_S(0)}}};
+
+// out = x  (binary32 copy; also the bandwidth reference)
+constexpr Program kProgCopyF32 = {1, 0, 0, 1, {TY_F32}, {TY_F32}, {ECMD_R_IN(0)}, {}};
+
+// out = x * s  (binary32)
+constexpr Program kProgScaleF32 = {
+    1, 1, 1, 1, {TY_F32}, {TY_F32}, {ECMD_R_S(0)},
+    {{C_MUL_F32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_U(0)}}};
+
+// out = f16(x), out = f32(x)
+constexpr Program kProgCvtF32F16 = {
+    1, 0, 1, 1, {TY_F32}, {TY_F16}, {ECMD_R_S(0)},
+    {{C_CVT_F32_F16, ECMD_R_S(0), ECMD_R_IN(0), kRefNone}}};
+constexpr Program kProgCvtF16F32 = {
+    1, 0, 1, 1, {TY_F16}, {TY_F32}, {ECMD_R_S(0)},
+    {{C_CVT_F16_F32, ECMD_R_S(0), ECMD_R_IN(0), kRefNone}}};
+
+}  // namespace ecmd
+
+namespace ecmd {
+
+// Specialised Programs per path: X(name, program).  The host lowerer matches a
+// lowered Command against these lists; the kernel files instantiate one kernel
+// per entry, in the same order.
+#define ECMD_LINEAR_SPECIALISED(X)        \
+    X(add_f32, kProgAddF32)               \
+    X(int_fused, kProgIntFused)           \
+    X(axpby_f32, kProgAxpbyF32)           \
+    X(mixed_two_out, kProgMixedTwoOut)    \
+    X(copy_f32, kProgCopyF32)             \
+    X(scale_f32, kProgScaleF32)           \
+    X(cvt_f32_f16, kProgCvtF32F16)        \
+    X(cvt_f16_f32, kProgCvtF16F32)
+
+#define ECMD_TILED_SPECIALISED(X)         \
+    X(add_scaled_f32, kProgAddScaledF32)
+
+// Launch entry points implemented by the kernel files (host code).  variant:
+// -1 = generic interpreter, k >= 0 = k-th specialised Program of the path's
+// list.  Each returns a hipError_t as int.
+struct LaunchGeometry {
+    int64_t grid;
+    int32_t block;
+};
+int launch_linear(int variant, bool vec, bool nt, const LinearArgs &A, LaunchGeometry g, void *stream);
+int launch_tiled(int variant, const StridedArgs &A, LaunchGeometry g, void *stream);
+int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
+
+constexpr int kLinearE = 8;        // elements per work-item per step on the linear path
+constexpr int kLinearBlock = 256;
+constexpr int kTileRows = 64;      // tiled path: output tile is kTileRows x kTileCols
+constexpr int kTileCols = 64;
+constexpr int kTileBlock = 256;
+constexpr int kGatherE = 4;
+constexpr int kGatherBlock = 256;
+
+}  // namespace ecmd

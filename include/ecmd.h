@@ -1,0 +1,207 @@
+/*
+ * ecmd.h -- C ABI for evaluating elementwise tensor Commands on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The model is rocRoller's Command (rocRoller "Design Overview", sections
+ * "Command Class", "Operations", "CommandArgument", "Command Kernel"):
+ *
+ *   - A Command is built by appending operations.  Every operation that yields
+ *     a value returns a tag; later operations name earlier values by tag, so
+ *     the operations always form a DAG.
+ *   - Loads (tensors) and scalars bring values in; stores write values out.
+ *     Each of them allocates one CommandArgument.  CommandArguments are
+ *     numbered in declaration order (arg_index) and their values -- device
+ *     pointers with sizes and strides, or scalar bit patterns -- are supplied
+ *     at launch, all together and in that order.
+ *   - The T_Execute part is a set of E_ operations applied element by element:
+ *     E_ADD, E_SUB, E_MUL (binary, both operands of the result dtype), E_NEG
+ *     (unary, same dtype) and E_CVT (unary, to the given dtype).
+ *
+ * Arithmetic (the same rules the test oracle implements):
+ *   CMD_I32  two's-complement, every operation modulo 2^32; E_NEG(INT_MIN) = INT_MIN.
+ *   CMD_F32  IEEE binary32, round to nearest even, every operation rounded on its
+ *            own (no fused multiply-add), subnormals kept (the default FP32 denorm
+ *            mode 3 of the AMDHSA kernel descriptor, Silk "AMDGPU Backend",
+ *            section "Code Object Format").  E_NEG flips the sign bit.
+ *   CMD_F16  storage type: load, store, E_NEG (sign flip) and E_CVT only.
+ *   E_CVT    f16->f32 exact; f32->f16 and i32->f16 round to nearest even with
+ *            overflow to infinity and gradual underflow; i32->f32 rounds to
+ *            nearest even; f32->i32 and f16->i32 truncate toward zero, saturate,
+ *            and map NaN to 0.  A conversion to the same dtype is a copy.
+ *   Scalars broadcast to every element.
+ *
+ * Shapes and views: every tensor argument of one launch has the same logical
+ * shape -- rank 1 (n) or rank 2 (rows, cols); a rank-1 view counts as (1, n).
+ * A view maps index (r, c) to element offset r*stride[0] + c*stride[1] from its
+ * base pointer (rank 1: i*stride[0]), following the coordinate-transform model
+ * of rocRoller "Design Overview", section "Kernel Graph" (a dimension has a size
+ * and a stride; Flatten is the row-major contiguous index).  Strides are in
+ * elements and must be >= 0.  A load may use stride 0 (broadcast).  A store view
+ * must not map two indexes to one element.  Outputs must not overlap each other,
+ * and an output may overlap an input only as the identical view (same pointer,
+ * strides and dtype: in place).
+ *
+ * Errors follow one rule (Silk "AMDGPU Backend", section "AQL Dispatch
+ * Packets": everything is validated before any runtime queue sees work): every
+ * status except CMD_E_LAUNCH is returned before any HIP call is made, and no GPU
+ * work is submitted after a failed check.  Launch is asynchronous; a fault that
+ * happens while the kernel runs is reported by the caller's next synchronisation
+ * of the stream, separately from the launch status.
+ *
+ * Ownership: the caller owns the cmd_t handle (cmd_create / cmd_destroy), every
+ * device buffer and the stream.  The library never allocates device memory and
+ * keeps no argument pointer after cmd_launch returns.  A handle is not
+ * thread-safe; separate handles are independent.
+ */
+#ifndef ECMD_H
+#define ECMD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ecmd_command *cmd_t;
+typedef int32_t cmd_tag;
+
+/* Element types. */
+#define CMD_F16 1
+#define CMD_F32 2
+#define CMD_I32 3
+
+/* E_ operations. */
+#define E_ADD 1
+#define E_SUB 2
+#define E_MUL 3
+#define E_NEG 4
+#define E_CVT 5
+
+/* CommandArgument kinds. */
+#define CMD_ARG_TENSOR 1
+#define CMD_ARG_SCALAR 2
+
+/* Status codes: 0 is success, every error is negative. */
+#define CMD_OK 0
+#define CMD_E_ARG (-1)     /* null or malformed argument, wrong argument kind or count  */
+#define CMD_E_TAG (-2)     /* tag does not name an earlier value                         */
+#define CMD_E_DTYPE (-3)   /* dtype not allowed for the operation, or argument dtype      */
+#define CMD_E_SHAPE (-4)   /* tensor arguments of one launch disagree on the shape       */
+#define CMD_E_STRIDE (-5)  /* negative stride, or a store view that is not one-to-one    */
+#define CMD_E_ALIAS (-6)   /* outputs overlap, or an output overlaps an input otherwise   */
+                           /* than as the identical view                                 */
+#define CMD_E_LIMIT (-7)   /* a fixed capacity is exceeded (see the CMD_MAX_* values)     */
+#define CMD_E_NOSTORE (-8) /* the Command has no store                                    */
+#define CMD_E_STATE (-9)   /* the Command is frozen (it has been launched or planned)     */
+#define CMD_E_LAUNCH (-10) /* the HIP runtime refused the launch; see cmd_last_error       */
+#define CMD_E_NOMEM (-11)  /* host allocation failed                                       */
+
+/* Capacities of one Command. */
+#define CMD_MAX_ARGS 16    /* CommandArguments (loads + scalars + stores)                 */
+#define CMD_MAX_LOADS 8    /* tensor loads that a store depends on                         */
+#define CMD_MAX_SCALARS 8  /* scalar arguments that a store depends on                     */
+#define CMD_MAX_STORES 4
+#define CMD_MAX_OPS 32     /* E_ operations that a store depends on                        */
+#define CMD_MAX_LIVE 8     /* per-element temporaries alive at once after lowering         */
+#define CMD_MAX_NODES 256  /* everything appended to one Command                           */
+
+/* One CommandArgument value, bound at launch.
+ *   kind   CMD_ARG_TENSOR or CMD_ARG_SCALAR; must match the declaration.
+ *   dtype  must equal the declared dtype.
+ *   ptr    tensor: device pointer to element (0, 0) of the view (HIP device
+ *          memory of the current device).  May be NULL only if the shape has
+ *          no elements.
+ *   size   tensor: logical sizes; rank 1 uses size[0] only.
+ *   stride tensor: element strides, >= 0; rank 1 uses stride[0] only.
+ *   bits   scalar: the value's bit pattern -- binary32 bits, int32 two's
+ *          complement, or binary16 bits in the low 16 bits.
+ */
+typedef struct {
+    int32_t kind;
+    int32_t dtype;
+    void *ptr;
+    int64_t size[2];
+    int64_t stride[2];
+    uint32_t bits;
+    uint32_t reserved;   /* must be 0 */
+} cmd_arg;
+
+/* Create an empty Command.  Host only, no HIP call.  *out receives the handle. */
+int cmd_create(cmd_t *out);
+
+/* Destroy a handle.  NULL is a no-op.  The caller must not use the handle again. */
+int cmd_destroy(cmd_t h);
+
+/* Append a tensor load of element type dtype and rank 1 or 2 (rocRoller "Design
+ * Overview", section "Operations": loads allocate the CommandArguments that
+ * describe the data).  *tag receives the loaded value's tag and *arg_index the
+ * CommandArgument's index.  Either output pointer may be NULL. */
+int cmd_load(cmd_t h, int32_t dtype, int32_t rank, cmd_tag *tag, int32_t *arg_index);
+
+/* Append a scalar CommandArgument of element type dtype (rocRoller "Design
+ * Overview", section "CommandArgument": an argument may be a scalar value).
+ * Its value broadcasts to every element. */
+int cmd_scalar(cmd_t h, int32_t dtype, cmd_tag *tag, int32_t *arg_index);
+
+/* Append an E_ operation (rocRoller "Design Overview", section "Operations":
+ * T_Execute holds E_ operations on vectors or scalars).  a and b are earlier
+ * tags; b must be -1 for E_NEG and E_CVT.  result_dtype must equal the
+ * operands' dtype except for E_CVT, where it is the target dtype.  E_ADD, E_SUB
+ * and E_MUL accept CMD_F32 and CMD_I32 operands of one dtype. */
+int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, cmd_tag *tag);
+
+/* Append a store of value's tag to an output tensor of rank 1 or 2; the
+ * output's dtype is the value's dtype (rocRoller "Design Overview", section
+ * "Operations": stores allocate CommandArguments too). */
+int cmd_store(cmd_t h, cmd_tag value, int32_t rank, int32_t *arg_index);
+
+/* Evaluate the Command on the GPU (rocRoller "Design Overview", section
+ * "Command Kernel": one built kernel, launched with per-call argument values
+ * given in declaration order).  args[nargs] holds one value per
+ * CommandArgument.  The first call freezes and lowers the Command.  The work
+ * is enqueued on hip_stream (a hipStream_t; NULL means the null stream) of the
+ * current HIP device and the call returns without waiting.  A shape with no
+ * elements succeeds without launching anything. */
+int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream);
+
+/* Description of what cmd_launch would do with these arguments. */
+typedef struct {
+    int32_t path;          /* CMD_PATH_* below                                           */
+    int32_t specialised;   /* 1 if a compile-time-specialised kernel matches the Command  */
+    int32_t vector;        /* 1 if 128-bit global accesses are used (alignment allows)     */
+    int32_t elems_per_thread;
+    int64_t grid;          /* work-groups                                                  */
+    int32_t block;         /* work-items per work-group                                    */
+    int32_t lds_bytes;     /* static LDS per work-group                                    */
+    int64_t rows, cols;    /* logical shape                                                */
+    char kernel[64];       /* kernel name                                                  */
+} cmd_plan_info;
+
+#define CMD_PATH_NONE 0    /* no elements: nothing would be launched   */
+#define CMD_PATH_LINEAR 1  /* every view is flat contiguous            */
+#define CMD_PATH_TILED 2   /* rank 2, inner-contiguous and transposed views, LDS staged */
+#define CMD_PATH_GATHER 3  /* any other strides                        */
+
+/* Validate args exactly as cmd_launch does and describe the launch without
+ * making it.  Host only: no HIP call.  Freezes the Command like cmd_launch. */
+int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info);
+
+/* Write a text listing of the lowered program (inputs, per-element operations
+ * with their register slots, stores) into buf[cap], NUL-terminated.  Freezes
+ * and lowers the Command.  Returns the full length of the listing (which may
+ * exceed cap - 1) or a negative status. */
+int64_t cmd_dump(cmd_t h, char *buf, int64_t cap);
+
+/* Message describing the last failure on this handle ("" if none).  Never
+ * NULL; valid until the next call on the handle.  For a NULL handle it
+ * describes the last failure of cmd_create on this thread. */
+const char *cmd_last_error(cmd_t h);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t cmd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ECMD_H */

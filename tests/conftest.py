@@ -21,3 +21,11 @@ def oracle_mod():
     from oracle import oracle
     oracle.build()
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stdout before it touches the GPU."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print("\n[gpu-case] %s" % request.node.nodeid, flush=True)
+    yield

@@ -1,0 +1,342 @@
+"""The C ABI on the host: symbols, validation, lowering and path selection.
+CPU only -- cmd_plan and cmd_dump make no HIP call, and every cmd_launch here
+fails a check before its first HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import elementwise_tensor_commands_amd as E
+import workloads as W
+from specs import SPECS, arg_dtypes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ecmd.h")
+
+
+def test_library_exports_every_declared_function():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:int|int32_t|int64_t|const char \*)\s*(cmd_\w+)\s*\(", text, re.M))
+    assert declared >= {"cmd_create", "cmd_destroy", "cmd_load", "cmd_scalar", "cmd_op", "cmd_store",
+                        "cmd_launch", "cmd_plan", "cmd_dump", "cmd_last_error", "cmd_version"}
+    lib = ctypes.CDLL(E.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.cmd_version() == 100
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(E.cmd_arg) == 56
+    assert E.cmd_arg.ptr.offset == 8 and E.cmd_arg.size.offset == 16 and E.cmd_arg.bits.offset == 48
+    assert ctypes.sizeof(E.cmd_plan_info) == 112
+
+
+def _t(*shape, dtype=torch.float32):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _err(fn, name):
+    with pytest.raises(E.Error) as e:
+        fn()
+    assert e.value.name == name, str(e.value)
+    return e.value
+
+
+# ---------------------------------------------------------------------------
+# Building.
+
+def test_build_errors():
+    c = E.Command()
+    x = c.load("f32")
+    i = c.load("i32")
+    h = c.load("f16")
+    _err(lambda: c.add(x, i), "CMD_E_DTYPE")
+    _err(lambda: c.add(x, 17), "CMD_E_TAG")
+    _err(lambda: c.add(h, h), "CMD_E_DTYPE")
+    _err(lambda: c.op(E.E_NEG, x, -1, "i32"), "CMD_E_DTYPE")
+    _err(lambda: c.op(E.E_NEG, x, x), "CMD_E_ARG")
+    _err(lambda: c.op(9, x, x), "CMD_E_ARG")
+    _err(lambda: c.load(7), "CMD_E_DTYPE")
+    _err(lambda: c.load("f32", 3), "CMD_E_LIMIT")
+    _err(lambda: c.store(99), "CMD_E_TAG")
+    assert c.neg(h) >= 0 and c.cvt(h, "i32") >= 0
+
+
+def test_nostore_and_frozen():
+    c = E.Command()
+    x = c.load("f32")
+    _err(lambda: c.plan(_t(4)), "CMD_E_NOSTORE")
+    _err(lambda: c.store(x), "CMD_E_STATE")      # the first plan froze it
+    c2 = E.from_spec(W.ADD_F32)
+    c2.plan(_t(4), _t(4), _t(4))
+    _err(lambda: c2.load("f32"), "CMD_E_STATE")
+
+
+def test_argument_limits():
+    c = E.Command()
+    for _ in range(16):
+        c.load("f32")
+    _err(lambda: c.load("f32"), "CMD_E_LIMIT")
+    c = E.Command()
+    xs = [c.load("f32") for _ in range(9)]
+    acc = xs[0]
+    for v in xs[1:]:
+        acc = c.add(acc, v)
+    c.store(acc)
+    _err(lambda: c.plan(*[_t(8)] * 10), "CMD_E_LIMIT")    # nine live loads
+
+
+def test_too_many_live_temporaries():
+    c = E.Command()
+    x = c.load("f32")
+    ts = [c.neg(x)]
+    for _ in range(8):
+        ts.append(c.neg(ts[-1]))
+    acc = ts[0]
+    for t in ts[1:]:
+        acc = c.add(acc, t)          # all nine negations alive until summed
+    c.store(acc)
+    _err(lambda: c.plan(_t(8), _t(8)), "CMD_E_LIMIT")
+
+
+# ---------------------------------------------------------------------------
+# Binding values.
+
+def test_binding_errors():
+    c = E.from_spec(W.ADD_F32)
+    _err(lambda: c.plan(_t(4), _t(4)), "CMD_E_ARG")                       # count
+    _err(lambda: c.plan(_t(4), _t(5), _t(4)), "CMD_E_SHAPE")
+    _err(lambda: c.plan(_t(4), _t(4, dtype=torch.int32), _t(4)), "CMD_E_DTYPE")
+    _err(lambda: c.plan(_t(4), _t(2, 2), _t(4)), "CMD_E_SHAPE")           # rank 2 for a rank-1 load
+    b = _t(16)
+    _err(lambda: c.plan(b[:8], b[4:12], b[6:14]), "CMD_E_ALIAS")          # output overlaps an input
+    o = _t(8)
+    c.plan(o, b[:8], o)                                                   # identical view: in place
+    two = E.from_spec(W.MIXED_TWO_OUT)
+    h = _t(8, dtype=torch.float16)
+    buf = _t(8)
+    _err(lambda: two.plan(h, h, h, 0.5, buf.view(torch.float16)[:8], buf), "CMD_E_ALIAS")   # outputs overlap
+
+
+def _raw_args(c, views):
+    arr = (E.cmd_arg * len(views))()
+    for i, v in enumerate(views):
+        for k, val in v.items():
+            if k in ("size", "stride"):
+                for d, x in enumerate(val):
+                    getattr(arr[i], k)[d] = x
+            else:
+                setattr(arr[i], k, val)
+    return arr
+
+
+def test_raw_stride_and_null_errors():
+    c = E.from_spec(W.ADD_F32)
+    x = _t(64)
+    good = dict(kind=E.ARG_TENSOR, dtype=E.F32, ptr=x.data_ptr(), size=(8, 0), stride=(1, 0))
+    info = E.cmd_plan_info()
+    args = _raw_args(c, [good, dict(good, stride=(-1, 0)), good])
+    assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == -5
+    args = _raw_args(c, [good, good, dict(good, ptr=None)])
+    assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == -1
+    out = _t(64)
+    args = _raw_args(c, [good, good, dict(good, ptr=out.data_ptr(), stride=(0, 0))])
+    assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == -5         # non-injective store
+    args = _raw_args(c, [good, dict(good, stride=(0, 0)), dict(good, ptr=out.data_ptr())])
+    assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == 0          # broadcast load is fine
+    assert info.path == E.PATH_GATHER
+    args = _raw_args(c, [good, good, dict(good, ptr=out.data_ptr(), reserved=1)])
+    assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == -1
+    args = _raw_args(c, [good, good, dict(good, ptr=out.data_ptr() + 1)])
+    assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == -1         # not element aligned
+    assert b"aligned" in E.lib.cmd_last_error(c._h)
+
+
+def test_launch_checks_precede_any_hip_call():
+    """On this GPU-less host, a launch that fails a check returns that check's
+    code (not CMD_E_LAUNCH): nothing reached the HIP runtime."""
+    c = E.from_spec(W.ADD_F32)
+    for bad, name in (((_t(4), _t(5), _t(4)), "CMD_E_SHAPE"),
+                      ((_t(4), _t(4, dtype=torch.int32), _t(4)), "CMD_E_DTYPE"),
+                      ((_t(4), _t(4)), "CMD_E_ARG")):
+        with pytest.raises(E.Error) as e:
+            c.launch(*bad, stream=0)
+        assert e.value.name == name
+    b = _t(16)
+    with pytest.raises(E.Error) as e:
+        c.launch(b[:8], b[:8], b[1:9], stream=0)
+    assert e.value.name == "CMD_E_ALIAS"
+
+
+def test_empty_launch_succeeds_without_gpu():
+    c = E.from_spec(W.ADD_F32)
+    c.launch(_t(0), _t(0), _t(0), stream=0)
+    assert c.plan(_t(0), _t(0), _t(0))["path"] == "none"
+
+
+# ---------------------------------------------------------------------------
+# Lowering.
+
+def test_shared_subexpression_evaluated_once():
+    c = E.from_spec(W.MIXED_TWO_OUT)
+    d = c.dump()
+    ops = [l for l in d.splitlines() if re.match(r"s\d+ = ", l)]
+    assert sum(1 for l in ops if "mul.f32" in l) == 2            # t = x*y once, and u*v
+    assert sum(1 for l in ops if "cvt.f16.f32" in l) == 3
+    assert len(ops) == 9
+
+
+def test_dead_code_is_dropped():
+    c = E.Command()
+    x = c.load("f32")
+    y = c.load("f32")
+    c.mul(x, y)                      # never stored
+    c.store(c.neg(x))
+    d = c.dump()
+    assert "mul" not in d and "in1" not in d
+    plan = c.plan(_t(8), _t(8), _t(8))
+    assert plan["path"] == "linear"
+
+
+def test_same_type_cvt_is_an_alias():
+    c = E.Command()
+    x = c.load("f32")
+    a = c.cvt(x, "f32")
+    c.store(c.add(a, x))
+    assert c.dump().count("add.f32 in0, in0") == 1
+
+
+def test_commutative_operands_canonical():
+    specs = [W.AXPBY_F32, [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)),
+                           ("alpha", ("scalar", "f32")), ("beta", ("scalar", "f32")),
+                           ("ax", ("mul", "x", "alpha")), ("by", ("mul", "y", "beta")),
+                           ("r", ("add", "by", "ax")), ("out", ("store", "r", 1))]]
+    dumps = [E.from_spec(s).dump() for s in specs]
+    assert dumps[0] == dumps[1]
+
+
+@pytest.mark.parametrize("wl,kernel", [("add_f32", "linear_add_f32"), ("int_fused", "linear_int_fused"),
+                                       ("axpby_f32", "linear_axpby_f32"),
+                                       ("mixed_two_out", "linear_mixed_two_out"),
+                                       ("transposed_2d", "tiled_add_scaled_f32")])
+def test_workloads_select_specialised_kernels(wl, kernel):
+    spec = W.WORKLOADS[wl]["spec"]
+    n = 1 << 12 if wl != "transposed_2d" else 256
+    vals, extra = W.make_inputs(wl, n)
+    tv = [torch.from_numpy(v) if isinstance(v, np.ndarray) else v for v in vals]
+    if wl == "transposed_2d":
+        tv[0] = torch.from_numpy(extra["X_storage"])[:, :n]
+        tv[1] = torch.from_numpy(extra["Y"]).t()
+    _, outs = arg_dtypes(spec)
+    shape = (n, n) if wl == "transposed_2d" else (n,)
+    o = [torch.empty(shape, dtype={"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}[d]) for d in outs]
+    plan = E.from_spec(spec).plan(*tv, *o)
+    assert plan["kernel"] == kernel and plan["specialised"] and plan["vector"]
+
+
+def test_geometry_rules():
+    """Work-group and grid obey the dispatch rules: grid >= 1, work-group size
+    nonzero and at most 1024, LDS within 64 KiB."""
+    c = E.from_spec(W.ADD_F32)
+    for n in (1, 7, 8, 2048, 1 << 20, 1 << 26):
+        p = c.plan(_t(n), _t(n), _t(n))
+        assert p["grid"] >= 1 and 0 < p["block"] <= 1024 and p["lds_bytes"] <= 65536
+    c2 = E.from_spec(W.TRANSPOSED_2D)
+    for R, C in ((2, 2), (65, 129), (1000, 3)):
+        X = _t(R, C)
+        Y = _t(C, R)
+        p = c2.plan(X, Y.t(), 2.0, _t(R, C))
+        assert p["grid"] >= 1 and p["block"] == 256
+
+
+def test_unaligned_views_pick_slower_variants():
+    c = E.from_spec(W.ADD_F32)
+    b = _t(40)
+    assert not c.plan(b[1:33], b[:32], _t(32))["vector"]
+    c2 = E.from_spec(W.TRANSPOSED_2D)
+    Xs = _t(64, 67)
+    Y = _t(64, 64)
+    assert c2.plan(Xs[:, :64], Y.t(), 2.0, _t(64, 64))["path"] == "gather"     # row stride 67: not 16B
+    Xs = _t(64, 68)
+    assert c2.plan(Xs[:, :64], Y.t(), 2.0, _t(64, 64))["path"] == "tiled"
+
+
+# ---------------------------------------------------------------------------
+# A test-only executor of the lowered listing (numpy arithmetic, no FMA) run
+# against the oracle: it catches lowering mistakes (slot reuse, operand order,
+# aliasing) without a GPU.
+
+def _emulate(listing, ins, uni, n):
+    regs = {}
+    outs = []
+    f16 = np.float16
+
+    def f2i(a):
+        a = a.astype(np.float64)
+        r = np.where(np.isnan(a), 0, np.clip(np.trunc(np.nan_to_num(a)), -2**31, 2**31 - 1))
+        return r.astype(np.int64).astype(np.int32)
+    for k, v in enumerate(ins):
+        regs["in%d" % k] = v
+    for k, v in enumerate(uni):
+        regs["u%d" % k] = np.full(n, v)
+    for line in listing.splitlines():
+        m = re.match(r"(s\d+) = (\S+) (\S+?)(?:, (\S+))?$", line)
+        if m:
+            dst, op, a, b = m.groups()
+            A = regs[a]
+            B = regs[b] if b else None
+            with np.errstate(all="ignore"):
+                if op in ("add.f32", "add.i32"): r = A + B
+                elif op in ("sub.f32", "sub.i32"): r = A - B
+                elif op in ("mul.f32", "mul.i32"): r = A * B
+                elif op.startswith("neg"): r = (A.view(np.uint32 if A.itemsize == 4 else np.uint16) ^ (0x80000000 if A.itemsize == 4 else 0x8000)).view(A.dtype) if op != "neg.i32" else (np.int32(0) - A)
+                elif op == "cvt.f16.f32": r = A.astype(np.float32)
+                elif op == "cvt.f32.f16": r = A.astype(f16)
+                elif op == "cvt.i32.f32": r = A.astype(np.float32)
+                elif op == "cvt.f32.i32": r = f2i(A)
+                elif op == "cvt.i32.f16": r = A.astype(np.float64).astype(f16)
+                elif op == "cvt.f16.i32": r = f2i(A.astype(np.float32))
+                else: raise AssertionError(op)
+            regs[dst] = r
+            continue
+        m = re.match(r"store\.\S+ arg\d+ <- (\S+)", line)
+        if m:
+            outs.append(regs[m.group(1)])
+    return outs
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_lowered_listing_matches_oracle(oracle_mod, seed):
+    import random_commands as G
+    rng = np.random.default_rng(1000 + seed)
+    spec = G._random_spec(rng, int(rng.integers(1, 5)), int(rng.integers(1, 14)), 1)
+    n = 257
+    vals = G._random_inputs(rng, spec, (n,))
+    try:
+        ref = oracle_mod.from_spec(spec).run(*vals)
+    except oracle_mod.OracleError:
+        pytest.skip("invalid random Command")
+    c = E.from_spec(spec)
+    try:
+        listing = c.dump()
+    except E.Error as e:
+        assert e.name == "CMD_E_LIMIT"
+        pytest.skip(str(e))
+    # inputs / uniforms in the listing's numbering: live loads and scalars in order
+    in_args = [int(a) for a in re.findall(r"in\d+ = load\.\S+ arg(\d+)", listing)]
+    u_args = [int(a) for a in re.findall(r"u\d+ = scalar\.\S+ arg(\d+)", listing)]
+    ins = [vals[a] for a in in_args]
+    uni = [vals[a] for a in u_args]
+    got = _emulate(listing, ins, uni, n)
+    for k, (g, r) in enumerate(zip(got, ref)):
+        g = np.asarray(g).astype(r.dtype) if np.asarray(g).dtype != r.dtype else g
+        gb = g.view(np.uint16 if r.itemsize == 2 else np.uint32)
+        rb = r.view(np.uint16 if r.itemsize == 2 else np.uint32)
+        if r.dtype.kind == "f":
+            ok = (gb == rb) | (np.isnan(g) & np.isnan(r))
+        else:
+            ok = gb == rb
+        assert ok.all(), "seed %d out%d\n%s" % (seed, k, listing)
