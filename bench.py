@@ -82,7 +82,10 @@ def time_steps(cmd, args, steps, warmup, cold=False):
     launch on the launch stream.  Returns (total_ms, per-launch ms list)."""
     import torch
     stream = torch.cuda.current_stream()
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0") if cold else None
+    # Cold runs: read 1 GiB of unrelated data before each timed launch (outside
+    # the events) so that none of the Command's data is left in the 256 MB
+    # last-level cache; reading, not writing, leaves no dirty lines behind.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0") if cold else None
     for _ in range(warmup):
         cmd.launch(*args, stream=stream)
     torch.cuda.synchronize()
@@ -91,7 +94,7 @@ def time_steps(cmd, args, steps, warmup, cold=False):
     t0 = time.perf_counter()
     for i in range(steps):
         if cold:
-            flush.zero_()         # 1 GiB written: evicts the last-level cache (outside the events)
+            flush.sum()
         starts[i].record(stream)
         cmd.launch(*args, stream=stream)
         ends[i].record(stream)
@@ -184,6 +187,8 @@ def main():
     ap.add_argument("--workload", default="int_fused")
     ap.add_argument("--all", action="store_true", help="also measure every other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold (cache-flushed) launches, e.g. under a kernel-trace profiler")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -194,7 +199,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     khash = kernel_source_hash()
     log("workload %s: %s" % (a.workload, W.WORKLOADS[a.workload]["label"]))
-    head = measure(a.workload, a.steps, a.warmup)
+    head = measure(a.workload, a.steps, a.warmup, cold_too=not a.no_cold)
     log("headline %s: %.1f GB/s whole-job, kernel avg %.2f us" % (head["kernel"], head["whole_job_gbps"], head["kernel_avg_us"]))
     traffic = traffic_from_profiles(a.workload, khash)
     line = {
@@ -215,7 +220,8 @@ def main():
                    "grid": head["grid"], "block": head["block"]},
         "pct_of_peak": round(100 * head["whole_job_gbps"] / PEAK_GBPS, 2),
         "gelem_per_s": round(head["elements"] * a.steps / (head["total_ms"] * 1e-3) / 1e9, 3),
-        "cold": {"median_us": round(head["cold_median_us"], 3), "gbps": round(head["cold_gbps"], 2)},
+        "cold": ({"median_us": round(head["cold_median_us"], 3), "gbps": round(head["cold_gbps"], 2)}
+                 if "cold_median_us" in head else None),
         "roofline": {
             "bound": "hbm", "achieved": round(head["kernel_gbps"], 2), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(head["kernel_gbps"] / PEAK_GBPS, 4),

@@ -351,4 +351,97 @@ __device__ __forceinline__ void store_elems(void *p, uint8_t ty, int64_t i, int 
     }
 }
 
+// One vector access of G consecutive elements (G = 4 or 8) at element index i:
+// 32-bit types move 16 bytes per 4 elements, binary16 8 bytes per 4.  With
+// VEC false (unaligned views) the elements are accessed one by one, and only
+// the first count of them.
+template <bool NT, class T>
+__device__ __forceinline__ T ld(const T *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+// NTL: nontemporal loads ("nt" cache policy: the data is streamed, not kept).
+template <int G, bool VEC, bool NTL = false>
+__device__ __forceinline__ void load_group(const void *p, uint8_t ty, int64_t i, int count, uint32_t (&v)[G])
+{
+    static_assert(G == 4 || G == 8, "group of 4 or 8");
+    if constexpr (VEC) {
+        if (ty == TY_F16) {
+            const uint16_t *q = static_cast<const uint16_t *>(p) + i;
+            if constexpr (G == 8) {
+                const u32x4 d = ld<NTL>(reinterpret_cast<const u32x4 *>(q));
+                const uint32_t x[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[2 * j] = x[j] & 0xffffu;
+                    v[2 * j + 1] = x[j] >> 16;
+                }
+            } else {
+                const u32x2 d = ld<NTL>(reinterpret_cast<const u32x2 *>(q));
+                v[0] = d.x & 0xffffu;
+                v[1] = d.x >> 16;
+                v[2] = d.y & 0xffffu;
+                v[3] = d.y >> 16;
+            }
+        } else {
+            const uint32_t *q = static_cast<const uint32_t *>(p) + i;
+#pragma unroll
+            for (int w = 0; w < G / 4; ++w) {
+                const u32x4 d = ld<NTL>(reinterpret_cast<const u32x4 *>(q) + w);
+                v[4 * w + 0] = d.x;
+                v[4 * w + 1] = d.y;
+                v[4 * w + 2] = d.z;
+                v[4 * w + 3] = d.w;
+            }
+        }
+    } else {
+        load_elems<G, false>(p, ty, i, count, v);
+    }
+}
+
+template <int G, bool VEC, bool NT>
+__device__ __forceinline__ void store_group(void *p, uint8_t ty, int64_t i, int count, const uint32_t (&v)[G])
+{
+    static_assert(G == 4 || G == 8, "group of 4 or 8");
+    if constexpr (VEC) {
+        if (ty == TY_F16) {
+            uint16_t *q = static_cast<uint16_t *>(p) + i;
+            if constexpr (G == 8) {
+                u32x4 d;
+                d.x = (v[0] & 0xffffu) | (v[1] << 16);
+                d.y = (v[2] & 0xffffu) | (v[3] << 16);
+                d.z = (v[4] & 0xffffu) | (v[5] << 16);
+                d.w = (v[6] & 0xffffu) | (v[7] << 16);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(q);
+                if constexpr (NT) __builtin_nontemporal_store(d, dst);
+                else *dst = d;
+            } else {
+                u32x2 d;
+                d.x = (v[0] & 0xffffu) | (v[1] << 16);
+                d.y = (v[2] & 0xffffu) | (v[3] << 16);
+                u32x2 *dst = reinterpret_cast<u32x2 *>(q);
+                if constexpr (NT) __builtin_nontemporal_store(d, dst);
+                else *dst = d;
+            }
+        } else {
+            uint32_t *q = static_cast<uint32_t *>(p) + i;
+#pragma unroll
+            for (int w = 0; w < G / 4; ++w) {
+                u32x4 d;
+                d.x = v[4 * w + 0];
+                d.y = v[4 * w + 1];
+                d.z = v[4 * w + 2];
+                d.w = v[4 * w + 3];
+                u32x4 *dst = reinterpret_cast<u32x4 *>(q) + w;
+                if constexpr (NT) __builtin_nontemporal_store(d, dst);
+                else *dst = d;
+            }
+        }
+    } else {
+        store_elems<G, false, false>(p, ty, i, count, v);
+    }
+}
+
 }  // namespace ecmd

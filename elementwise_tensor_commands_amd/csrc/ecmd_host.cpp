@@ -61,7 +61,8 @@ struct Selection {
     int path = CMD_PATH_NONE;
     int variant = -1;
     bool vec = false;
-    bool nt = false;
+    LinearShape shape{4, 4, false, true};
+    bool xcd_remap = false;
     int n_staged = 0;
     uint8_t staged[kMaxIn] = {};
     int64_t grid = 0;
@@ -272,6 +273,32 @@ int64_t env_int(const char *name, int64_t dflt)
     return std::strtoll(v, nullptr, 10);
 }
 
+// Linear kernel shape and cache policy.
+//   Shape: ECMD_LINEAR_SHAPE = "ExG", E elements per work-item in groups of G:
+//   "4x4" (default: one 16-byte vector per 32-bit operand per work-item, the
+//   fastest on MI355X), "8x4" or "8x8".
+//   Stores are nontemporal by default (ECMD_NT_STORE=0 turns it off): with G = 4
+//   every store instruction covers whole cache lines, and streaming them past
+//   the caches raised every workload's rate.
+//   Loads are nontemporal when the launch moves more than kMallBytes (the
+//   256 MB last-level Infinity Cache): such data cannot stay cached between
+//   launches anyway.  Smaller working sets use ordinary loads so that repeated
+//   launches can hit in that cache.  ECMD_NT_LOAD=0/1 overrides.
+constexpr int64_t kMallBytes = (int64_t)256 << 20;
+
+LinearShape linear_shape(int64_t bytes)
+{
+    LinearShape s{4, 4, bytes > kMallBytes, true};
+    const char *v = std::getenv("ECMD_LINEAR_SHAPE");
+    if (v && std::strcmp(v, "8x8") == 0) s.e = 8, s.g = 8;
+    if (v && std::strcmp(v, "8x4") == 0) s.e = 8, s.g = 4;
+    const char *l = std::getenv("ECMD_NT_LOAD");
+    if (l && *l) s.nt_load = std::strcmp(l, "0") != 0;
+    const char *st = std::getenv("ECMD_NT_STORE");
+    if (st && *st) s.nt_store = std::strcmp(st, "0") != 0;
+    return s;
+}
+
 // Highest element offset a view reaches (views have non-negative strides).
 __int128 max_offset(int64_t rows, int64_t cols, int64_t s0, int64_t s1)
 {
@@ -425,15 +452,22 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         for (int k = 0; k < P.n_in; ++k) S.vec = S.vec && aligned(B.in[k].ptr, 16);
         for (int k = 0; k < P.n_out; ++k) S.vec = S.vec && aligned(B.out[k].ptr, 16);
         S.variant = (S.vec && !force_generic) ? program_match_linear(P) : -1;
-        S.nt = env_flag("ECMD_NT_STORE");
-        S.e = kLinearE;
+        int64_t bytes = 0;
+        for (int k = 0; k < P.n_in; ++k) bytes += numel * esize(B.in[k].dtype);
+        for (int k = 0; k < P.n_out; ++k) bytes += numel * esize(B.out[k].dtype);
+        S.shape = linear_shape(bytes);
+        if (S.variant < 0) S.shape.e = 4, S.shape.g = 4;   // the interpreter has one shape
+        S.e = S.shape.e;
         S.block = kLinearBlock;
-        const int64_t chunks = numel / kLinearE;
-        int64_t need = (chunks + kLinearBlock - 1) / kLinearBlock;
+        // One wavefront per chunk of 64 * E elements (no grid-stride loop)
+        // unless ECMD_BLOCKS_PER_CU caps the grid.
+        const int64_t chunks = numel / (64 * S.e);
+        const int64_t waves = kLinearBlock / 64;
+        int64_t need = (chunks + waves - 1) / waves;
         if (need < 1) need = 1;
-        const int64_t per_cu = env_int("ECMD_BLOCKS_PER_CU", 8);
-        const int64_t cap = std::max<int64_t>(1, per_cu * cu_count);
-        S.grid = std::min(need, cap);
+        const int64_t per_cu = env_int("ECMD_BLOCKS_PER_CU", 0);
+        S.grid = per_cu > 0 ? std::min(need, std::max<int64_t>(1, per_cu * cu_count)) : need;
+        S.xcd_remap = env_flag("ECMD_XCD_REMAP") && S.grid % 8 == 0;
         S.name = S.vec ? linear_name(S.variant) : "linear_generic_unaligned";
         return;
     }
@@ -682,12 +716,15 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         for (int k = 0; k < h->prog.n_out; ++k) A.out[k] = B.out[k].ptr;
         A.n = B.rows * B.cols;
         std::memcpy(A.uni, B.uni, sizeof A.uni);
+        A.flags = S.xcd_remap ? kLinearXcdRemap : 0u;
         A.prog = h->prog;
-        herr = launch_linear(S.variant, S.vec, S.nt, A, g, hip_stream);
+        herr = launch_linear(S.variant, S.vec, S.shape, A, g, hip_stream);
     } else {
         StridedArgs A;
         fill_strided(h, B, S, A);
-        herr = S.path == CMD_PATH_TILED ? launch_tiled(S.variant, A, g, hip_stream)
+        const char *ntv = std::getenv("ECMD_TILED_NT");
+        const bool nt = !(ntv && std::strcmp(ntv, "0") == 0);
+        herr = S.path == CMD_PATH_TILED ? launch_tiled(S.variant, nt, A, g, hip_stream)
                                         : launch_gather(A, g, hip_stream);
     }
     if (herr != 0)

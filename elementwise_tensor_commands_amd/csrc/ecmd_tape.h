@@ -89,8 +89,10 @@ struct LinearArgs {
     void *out[kMaxOut];
     int64_t n;
     uint32_t uni[kMaxUni];
+    uint32_t flags;           // kLinearXcdRemap
     Program prog;
 };
+constexpr uint32_t kLinearXcdRemap = 1;   // give each XCD one contiguous run of blocks
 
 // Rank-2 shape (rows x cols) with per-operand element strides.
 struct StridedArgs {
@@ -196,11 +198,17 @@ struct LaunchGeometry {
     int64_t grid;
     int32_t block;
 };
-int launch_linear(int variant, bool vec, bool nt, const LinearArgs &A, LaunchGeometry g, void *stream);
-int launch_tiled(int variant, const StridedArgs &A, LaunchGeometry g, void *stream);
+// Linear kernel shapes: E elements per work-item per step, moved in groups of
+// G consecutive elements per vector access.
+struct LinearShape {
+    int e, g;
+    bool nt_load, nt_store;   // nontemporal ("nt") cache policy on loads / stores
+};
+int launch_linear(int variant, bool vec, LinearShape shape, const LinearArgs &A, LaunchGeometry g,
+                  void *stream);
+int launch_tiled(int variant, bool nt, const StridedArgs &A, LaunchGeometry g, void *stream);
 int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
 
-constexpr int kLinearE = 8;        // elements per work-item per step on the linear path
 constexpr int kLinearBlock = 256;
 constexpr int kTileRows = 64;      // tiled path: output tile is kTileRows x kTileCols
 constexpr int kTileCols = 64;

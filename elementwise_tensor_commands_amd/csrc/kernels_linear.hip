@@ -2,68 +2,124 @@
 //
 // Every view is flat contiguous, so element i of every operand sits at
 // base + i (the Flatten coordinate transform of rocRoller "Design Overview",
-// section "Kernel Graph").  Work-item t of the grid handles E = 8 consecutive
-// elements, then strides by the whole grid: each step issues 128-bit loads for
-// every input (two per 32-bit input, one per binary16 input), evaluates the
-// Program in registers and issues 128-bit stores.  A wavefront therefore moves
-// 64 x 16 B = 1 KiB per load instruction, fully coalesced.  The n mod 8 tail
-// is done by one work-item with per-element accesses.  Views whose base is not
-// 16-byte aligned take the per-element variant of the same kernel.
+// section "Kernel Graph").
+//
+// Work is cut into wavefront chunks of 64 * E elements.  Inside a chunk, lane l
+// owns the groups g = w * 64 + l (w = 0 .. E/G - 1) of G consecutive elements,
+// so each vector access instruction of the wavefront covers 64 * G consecutive
+// elements: with G = 4, one fully used 1 KiB run per 32-bit operand and
+// 512 bytes per binary16 operand -- whole cache lines, which nontemporal
+// stores need to stream at full rate.  A work-item issues every load of its
+// step before any arithmetic, evaluates the Program in registers and then
+// stores.  The default shape is E = G = 4 (one 16-byte vector per 32-bit
+// operand per work-item) with one wavefront per chunk and no grid-stride loop:
+// the most wavefronts in flight, which measured fastest on MI355X.  The fewer
+// than 64 * E elements after the last full chunk are done one element per
+// work-item by the last work-group.
 #include <hip/hip_runtime.h>
 
 #include "ecmd_eval.h"
 
 namespace ecmd {
 
-template <class EV, int E, bool VEC, bool NT>
-__device__ __forceinline__ void linear_step(const LinearArgs &A, int64_t i, int count)
+template <class EV, int E>
+__device__ __forceinline__ void linear_tail(const LinearArgs &A, int64_t first)
 {
-    Regs<E> R;
+    for (int64_t i = first + threadIdx.x; i < A.n; i += blockDim.x) {
+        Regs<1> R;
 #pragma unroll
-    for (int k = 0; k < kMaxIn; ++k)
-        if (k < EV::n_in(A.prog)) load_elems<E, VEC>(A.in[k], EV::in_ty(A.prog, k), i, count, R.in[k]);
-    uint32_t out[kMaxOut][E];
-    EV::template run<E>(A.prog, A.uni, R, out);
+        for (int k = 0; k < kMaxIn; ++k)
+            if (k < EV::n_in(A.prog)) load_elems<1, false>(A.in[k], EV::in_ty(A.prog, k), i, 1, R.in[k]);
+        uint32_t out[kMaxOut][1];
+        EV::template run<1>(A.prog, A.uni, R, out);
 #pragma unroll
-    for (int k = 0; k < kMaxOut; ++k)
-        if (k < EV::n_out(A.prog))
-            store_elems<E, VEC, NT>(A.out[k], EV::out_ty(A.prog, k), i, count, out[k]);
+        for (int k = 0; k < kMaxOut; ++k)
+            if (k < EV::n_out(A.prog)) store_elems<1, false, false>(A.out[k], EV::out_ty(A.prog, k), i, 1, out[k]);
+    }
 }
 
-template <class EV, bool VEC, bool NT>
+template <class EV, int E, int G, bool VEC, bool NTL, bool NTS>
 __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
 {
-    constexpr int E = kLinearE;
-    const int64_t n = A.n;
-    const int64_t nfull = n / E;
-    const int64_t step = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nfull; c += step)
-        linear_step<EV, E, VEC, NT>(A, c * E, E);
-    const int rem = (int)(n - nfull * E);
-    if (rem != 0 && blockIdx.x == 0 && threadIdx.x == 0)
-        linear_step<EV, E, false, false>(A, nfull * E, rem);
+    constexpr int kChunk = 64 * E;
+    constexpr int kWaves = kLinearBlock / 64;
+    const int lane = threadIdx.x & 63;
+    uint32_t bid = blockIdx.x;
+    if (A.flags & kLinearXcdRemap) {
+        // Work-groups are handed to the 8 XCDs in turn; renumber them so that
+        // XCD x works through the x-th eighth of the array in order.
+        const uint32_t per = gridDim.x >> 3;
+        bid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    }
+    const int64_t nchunks = A.n / kChunk;
+    const int64_t stride = (int64_t)gridDim.x * kWaves;
+    for (int64_t c = (int64_t)bid * kWaves + (threadIdx.x >> 6); c < nchunks; c += stride) {
+        const int64_t base = c * kChunk;
+        Regs<E> R;
+#pragma unroll
+        for (int k = 0; k < kMaxIn; ++k) {
+            if (k < EV::n_in(A.prog)) {
+#pragma unroll
+                for (int w = 0; w < E / G; ++w) {
+                    uint32_t v[G];
+                    load_group<G, VEC, NTL>(A.in[k], EV::in_ty(A.prog, k), base + (int64_t)(w * 64 + lane) * G, G, v);
+#pragma unroll
+                    for (int j = 0; j < G; ++j) R.in[k][w * G + j] = v[j];
+                }
+            }
+        }
+        uint32_t out[kMaxOut][E];
+        EV::template run<E>(A.prog, A.uni, R, out);
+#pragma unroll
+        for (int k = 0; k < kMaxOut; ++k) {
+            if (k < EV::n_out(A.prog)) {
+#pragma unroll
+                for (int w = 0; w < E / G; ++w) {
+                    uint32_t v[G];
+#pragma unroll
+                    for (int j = 0; j < G; ++j) v[j] = out[k][w * G + j];
+                    store_group<G, VEC, NTS>(A.out[k], EV::out_ty(A.prog, k), base + (int64_t)(w * 64 + lane) * G, G, v);
+                }
+            }
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1) linear_tail<EV, E>(A, nchunks * kChunk);
 }
 
-template <class EV, bool VEC, bool NT>
+template <class EV, int E, int G, bool VEC, bool NTL, bool NTS>
 static int launch_one(const LinearArgs &A, LaunchGeometry g, void *stream)
 {
-    hipLaunchKernelGGL((k_linear<EV, VEC, NT>), dim3((unsigned)g.grid), dim3(g.block), 0,
+    hipLaunchKernelGGL((k_linear<EV, E, G, VEC, NTL, NTS>), dim3((unsigned)g.grid), dim3(g.block), 0,
                        (hipStream_t)stream, A);
     return (int)hipGetLastError();
 }
 
-int launch_linear(int variant, bool vec, bool nt, const LinearArgs &A, LaunchGeometry g, void *stream)
+template <class EV, int E, int G>
+static int launch_policy(LinearShape s, const LinearArgs &A, LaunchGeometry g, void *stream)
 {
-    if (!vec) return launch_one<RtEval, false, false>(A, g, stream);
+    if (s.nt_load) return s.nt_store ? launch_one<EV, E, G, true, true, true>(A, g, stream)
+                                     : launch_one<EV, E, G, true, true, false>(A, g, stream);
+    return s.nt_store ? launch_one<EV, E, G, true, false, true>(A, g, stream)
+                      : launch_one<EV, E, G, true, false, false>(A, g, stream);
+}
+
+template <class EV>
+static int launch_shape(LinearShape s, const LinearArgs &A, LaunchGeometry g, void *stream)
+{
+    if (s.e == 4) return launch_policy<EV, 4, 4>(s, A, g, stream);
+    return s.g == 8 ? launch_policy<EV, 8, 8>(s, A, g, stream) : launch_policy<EV, 8, 4>(s, A, g, stream);
+}
+
+int launch_linear(int variant, bool vec, LinearShape shape, const LinearArgs &A, LaunchGeometry g, void *stream)
+{
+    if (!vec) return launch_one<RtEval, 4, 4, false, false, false>(A, g, stream);
     int k = 0;
-#define ECMD_DISPATCH(name, prog)                                                        \
-    if (variant == k)                                                                    \
-        return nt ? launch_one<CtEval<prog>, true, true>(A, g, stream)                   \
-                  : launch_one<CtEval<prog>, true, false>(A, g, stream);                 \
+#define ECMD_DISPATCH(name, prog)                                          \
+    if (variant == k) return launch_shape<CtEval<prog>>(shape, A, g, stream); \
     ++k;
     ECMD_LINEAR_SPECIALISED(ECMD_DISPATCH)
 #undef ECMD_DISPATCH
-    return nt ? launch_one<RtEval, true, true>(A, g, stream) : launch_one<RtEval, true, false>(A, g, stream);
+    return launch_policy<RtEval, 4, 4>(shape, A, g, stream);
 }
 
 }  // namespace ecmd

@@ -20,6 +20,8 @@
 //      elements of one row: direct inputs are read with 16-byte vector loads,
 //      staged inputs from LDS, and outputs are written with 16-byte stores,
 //      so every global access is a contiguous run of 256 bytes per row.
+// Global accesses of full tiles use the nontemporal cache policy by default
+// (each instruction covers whole cache lines).
 // Edge tiles (rows or cols not a multiple of 64) use per-element masked
 // accesses.  Staging is a prior-art idea the Silk backend also assumes (its
 // tiled kernels default to a 16 KiB LDS segment, Silk "AMDGPU Backend",
@@ -56,6 +58,7 @@ __device__ __forceinline__ int stage_pos(const StridedArgs &A, int k)
 
 // Copy the tile's columns c0..c0+TN-1, rows r0..r0+TM-1 of a column-contiguous
 // view into LDS: dst[cl * kPitch + rl].
+template <bool NTL>
 __device__ __forceinline__ void stage_tile(const void *base, uint8_t ty, int64_t s1, int64_t r0,
                                            int64_t c0, int64_t rows, int64_t cols, bool full,
                                            uint32_t *dst)
@@ -70,7 +73,7 @@ __device__ __forceinline__ void stage_tile(const void *base, uint8_t ty, int64_t
         const int64_t off = (c0 + cl) * s1 + (r0 + rl);
         uint32_t v[4];
         if (full) {
-            load_elems<4, true>(base, ty, off, 4, v);
+            load_group<4, true, NTL>(base, ty, off, 4, v);
         } else {
             int count = 0;
             if (c0 + cl < cols) {
@@ -85,21 +88,23 @@ __device__ __forceinline__ void stage_tile(const void *base, uint8_t ty, int64_t
     }
 }
 
-template <class EV, int MASK>
+template <class EV, int MASK, bool NT>
 __global__ __launch_bounds__(kTileBlock) void k_tiled(const StridedArgs A)
 {
     extern __shared__ uint32_t lds[];
-    const int64_t tile = blockIdx.x;
-    const int64_t tr = tile / A.tiles_c;
-    const int64_t tc = tile - tr * A.tiles_c;
-    const int64_t r0 = tr * TM, c0 = tc * TN;
+    // Tile counts fit in 32 bits (the grid is one dimension of < 2^31 groups).
+    const uint32_t tile = blockIdx.x;
+    const uint32_t tiles_c = (uint32_t)A.tiles_c;
+    const uint32_t tr = tile / tiles_c;
+    const uint32_t tc = tile - tr * tiles_c;
+    const int64_t r0 = (int64_t)tr * TM, c0 = (int64_t)tc * TN;
     const bool full = (r0 + TM <= A.rows) && (c0 + TN <= A.cols);
     const int t = threadIdx.x;
 
 #pragma unroll
     for (int k = 0; k < kMaxIn; ++k)
         if (k < EV::n_in(A.prog) && staged<MASK>(A, k))
-            stage_tile(A.in[k], EV::in_ty(A.prog, k), A.in_s1[k], r0, c0, A.rows, A.cols, full,
+            stage_tile<NT>(A.in[k], EV::in_ty(A.prog, k), A.in_s1[k], r0, c0, A.rows, A.cols, full,
                        lds + stage_pos<MASK>(A, k) * kTileWords);
     __syncthreads();
 
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tiled(const StridedArgs A)
                     for (int j = 0; j < 4; ++j) R.in[k][j] = src[(cl + j) * kPitch + rl];
                 } else {
                     const int64_t off = r * A.in_s0[k] + c;
-                    if (full) load_elems<4, true>(A.in[k], EV::in_ty(A.prog, k), off, 4, R.in[k]);
+                    if (full) load_group<4, true, NT>(A.in[k], EV::in_ty(A.prog, k), off, 4, R.in[k]);
                     else load_elems<4, false>(A.in[k], EV::in_ty(A.prog, k), off, count, R.in[k]);
                 }
             }
@@ -135,32 +140,35 @@ __global__ __launch_bounds__(kTileBlock) void k_tiled(const StridedArgs A)
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < EV::n_out(A.prog)) {
                 const int64_t off = r * A.out_s0[k] + c;
-                if (full) store_elems<4, true, false>(A.out[k], EV::out_ty(A.prog, k), off, 4, out[k]);
+                if (full) store_group<4, true, NT>(A.out[k], EV::out_ty(A.prog, k), off, 4, out[k]);
                 else store_elems<4, false, false>(A.out[k], EV::out_ty(A.prog, k), off, count, out[k]);
             }
         }
     }
 }
 
-template <class EV, int MASK>
+template <class EV, int MASK, bool NT>
 static int launch_one(const StridedArgs &A, LaunchGeometry g, void *stream, int lds_bytes)
 {
-    hipLaunchKernelGGL((k_tiled<EV, MASK>), dim3((unsigned)g.grid), dim3(g.block),
+    hipLaunchKernelGGL((k_tiled<EV, MASK, NT>), dim3((unsigned)g.grid), dim3(g.block),
                        (unsigned)lds_bytes, (hipStream_t)stream, A);
     return (int)hipGetLastError();
 }
 
 int tiled_lds_bytes(int n_staged) { return n_staged * kTileWords * 4; }
 
-int launch_tiled(int variant, const StridedArgs &A, LaunchGeometry g, void *stream)
+int launch_tiled(int variant, bool nt, const StridedArgs &A, LaunchGeometry g, void *stream)
 {
     int n_staged = 0;
     for (int k = 0; k < A.prog.n_in; ++k) n_staged += A.in_staged[k] != 0;
     const int lds = tiled_lds_bytes(n_staged);
     // The specialised kernel for out = X + alpha * Yt is instantiated with Yt
     // (input 1) staged; the host only picks it for that staging mask.
-    if (variant == 0) return launch_one<CtEval<kProgAddScaledF32>, 0x2>(A, g, stream, lds);
-    return launch_one<RtEval, kMaskRuntime>(A, g, stream, lds);
+    if (variant == 0)
+        return nt ? launch_one<CtEval<kProgAddScaledF32>, 0x2, true>(A, g, stream, lds)
+                  : launch_one<CtEval<kProgAddScaledF32>, 0x2, false>(A, g, stream, lds);
+    return nt ? launch_one<RtEval, kMaskRuntime, true>(A, g, stream, lds)
+              : launch_one<RtEval, kMaskRuntime, false>(A, g, stream, lds);
 }
 
 }  // namespace ecmd

@@ -92,6 +92,33 @@ def test_linear_small(wl, n):
     assert plan["path"] == "linear" and plan["specialised"]
 
 
+@pytest.mark.parametrize("wl", LINEAR)
+@pytest.mark.parametrize("shape", ["8x4", "8x8", "4x4", "8x4/ld0", "8x4/st0", "8x8/ld0st0", "4x4/ld0st0",
+                                   "8x4/xcd", "8x4/cap"])
+def test_linear_shapes(wl, shape):
+    """Every linear kernel instantiation (group size, nontemporal loads and
+    stores on or off, XCD renumbering, capped grid with a grid-stride loop)
+    against the oracle, at a size with several chunks and a ragged tail."""
+    g, _, opt = shape.partition("/")
+    env = {"ECMD_LINEAR_SHAPE": g, "ECMD_NT_LOAD": "0" if "ld0" in opt else "1",
+           "ECMD_NT_STORE": "0" if "st0" in opt else "1"}
+    if opt == "xcd":
+        env["ECMD_XCD_REMAP"] = "1"
+    if opt == "cap":
+        env["ECMD_BLOCKS_PER_CU"] = "1"
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        n = 256 * 8 * 16 * 9 + 77 if opt == "xcd" else (1 << 19) + 333
+        _check_workload(wl, n)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 @pytest.mark.parametrize("wl", LINEAR + ["transposed_2d"])
 def test_generic_interpreter(wl):
     n = 257 if wl == "transposed_2d" else (1 << 18) + 5
@@ -102,7 +129,24 @@ def test_generic_interpreter(wl):
 @pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 200, 1000])
 def test_transposed_small(n):
     plan = _check_workload("transposed_2d", n)
-    assert plan["path"] == ("tiled" if n >= 2 else "gather")
+    # 1x1 is flat; the tiled path needs 16-byte rows: X's row stride n + 64 and
+    # Y's n must be multiples of 4 elements, else the gather kernel runs.
+    assert plan["path"] == ("linear" if n == 1 else "tiled" if n % 4 == 0 else "gather")
+
+
+@pytest.mark.parametrize("n", [64, 200, 1000])
+def test_transposed_cached_policy(n):
+    """The tiled kernels with ordinary (not nontemporal) global accesses."""
+    old = os.environ.get("ECMD_TILED_NT")
+    os.environ["ECMD_TILED_NT"] = "0"
+    try:
+        _check_workload("transposed_2d", n)
+        _check_workload("transposed_2d", n + 4, generic=True)
+    finally:
+        if old is None:
+            os.environ.pop("ECMD_TILED_NT", None)
+        else:
+            os.environ["ECMD_TILED_NT"] = old
 
 
 @pytest.mark.parametrize("wl", ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"])
