@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0        # MI355X HBM3E peak, 8 TB/s
 METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, per Command"
 DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two_out": "f16/f32",
-            "transposed_2d": "f32"}
+            "transposed_2d": "f32", "copy_f32": "f32"}
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(msg):
@@ -77,32 +78,48 @@ def setup(wl, n=None):
     return cmd, args, plan, vals
 
 
-def time_steps(cmd, args, steps, warmup, cold=False):
-    """Launch the Command steps times back to back; HIP events around every
-    launch on the launch stream.  Returns (total_ms, per-launch ms list)."""
+def time_steps(cmd, args, steps, warmup):
+    """Launch the Command steps times back to back on the current stream, with
+    HIP events at both ends of the timed region.  Returns (total_ms, wall_ms)."""
     import torch
     stream = torch.cuda.current_stream()
-    # Cold runs: read 1 GiB of unrelated data before each timed launch (outside
-    # the events) so that none of the Command's data is left in the 256 MB
-    # last-level cache; reading, not writing, leaves no dirty lines behind.
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0") if cold else None
+    bound = cmd.bind(*args, stream=stream)
     for _ in range(warmup):
-        cmd.launch(*args, stream=stream)
+        bound.launch()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        if cold:
-            flush.sum()
-        starts[i].record(stream)
-        cmd.launch(*args, stream=stream)
-        ends[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
+        bound.launch()
+    end.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    total = starts[0].elapsed_time(ends[-1])
-    return total, per, wall_ms
+    return start.elapsed_time(end), wall_ms
+
+
+def time_each(cmd, args, reps, cold=False):
+    """Per-launch HIP event pairs, optionally reading 1 GiB of unrelated data
+    before each launch (outside the events) so that none of the Command's data
+    is left in the 256 MB last-level cache; reading leaves no dirty lines."""
+    import torch
+    stream = torch.cuda.current_stream()
+    bound = cmd.bind(*args, stream=stream)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0") if cold else None
+    bound.launch()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        if cold:
+            flush.sum()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        bound.launch()
+        e.record(stream)
+        e.synchronize()
+        per.append(s.elapsed_time(e))
+    return per
 
 
 def cpu_baseline(wl, budget_s=20.0):
@@ -157,26 +174,138 @@ def traffic_from_profiles(wl, kernel_hash):
 
 
 def measure(wl, steps, warmup, cold_too=True):
+    """Timed region: steps back-to-back launches between two HIP events on the
+    launch stream.  The kernel's average duration is that time / steps (the
+    host queues launches faster than they run, so the GPU never waits).
+    Separately, per-launch event pairs give median / p10 / p90 and, with a
+    cache flush before each launch, the cold rate."""
     import workloads as W
     cmd, args, plan, _ = setup(wl)
     byts = W.algorithmic_bytes(wl)
     elems = W.elements(wl)
-    total_ms, per, wall_ms = time_steps(cmd, args, steps, warmup)
-    avg_ms = statistics.mean(per)
+    total_ms, wall_ms = time_steps(cmd, args, steps, warmup)
+    avg_ms = total_ms / steps
+    per = sorted(time_each(cmd, args, min(steps, 50)))
     r = {
         "kernel": plan["kernel"], "grid": plan["grid"], "block": plan["block"],
         "algorithmic_bytes": byts, "elements": elems,
         "whole_job_gbps": byts * steps / (total_ms * 1e-3) / 1e9,
         "kernel_avg_us": avg_ms * 1e3, "kernel_median_us": statistics.median(per) * 1e3,
-        "kernel_p10_us": sorted(per)[len(per) // 10] * 1e3, "kernel_p90_us": sorted(per)[(9 * len(per)) // 10] * 1e3,
+        "kernel_p10_us": per[len(per) // 10] * 1e3, "kernel_p90_us": per[(9 * len(per)) // 10] * 1e3,
         "total_ms": total_ms, "wall_ms": wall_ms,
     }
     r["kernel_gbps"] = byts / (avg_ms * 1e-3) / 1e9
     if cold_too:
-        _, per_c, _ = time_steps(cmd, args, min(steps, 20), 1, cold=True)
+        per_c = time_each(cmd, args, 20, cold=True)
         r["cold_median_us"] = statistics.median(per_c) * 1e3
         r["cold_gbps"] = byts / (statistics.median(per_c) * 1e-3) / 1e9
     return r
+
+
+def read_write_bytes(wl):
+    """Algorithmic bytes read and written by one launch of the workload."""
+    import workloads as W
+    size = {"f16": 2, "f32": 4, "i32": 4}
+    dt, rd, wr = {}, 0, 0
+    for name, st in W.WORKLOADS[wl]["spec"]:
+        if st[0] == "load":
+            dt[name] = st[1]
+            rd += size[st[1]]
+        elif st[0] == "scalar":
+            dt[name] = st[1]
+        elif st[0] == "cvt":
+            dt[name] = st[2]
+        elif st[0] in ("add", "sub", "mul", "neg"):
+            dt[name] = dt[st[1]]
+        elif st[0] == "store":
+            wr += size[dt[st[1]]]
+    e = W.elements(wl)
+    return e * rd, e * wr
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def summarize_counters(root, command):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (root/fetch_<wl>,
+    root/write_<wl>, one per workload plus copy_f32) into profiles/.  Each
+    counter is scaled by what it reads for the plain copy of known size (1 GiB
+    read + 1 GiB written)."""
+    import workloads as W
+
+    def per_dispatch(kind, wl):
+        rows = [r for r in _csv_rows(os.path.join(root, "%s_%s" % (kind, wl)), "counter_collection.csv")
+                if "ecmd::k_" in r["Kernel_Name"]]
+        assert rows, "no ecmd kernel rows for %s %s" % (kind, wl)
+        names = sorted({r["Kernel_Name"] for r in rows})
+        assert len(names) == 1, names
+        vals = [float(r["Counter_Value"]) for r in rows]
+        return names[0], statistics.mean(vals), len(vals)
+
+    khash = kernel_source_hash()
+    cr, cw = read_write_bytes("copy_f32")
+    _, f_copy, _ = per_dispatch("fetch", "copy_f32")
+    _, w_copy, _ = per_dispatch("write", "copy_f32")
+    cal_f, cal_w = cr / (f_copy * 1024), cw / (w_copy * 1024)
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Command (one counter per run, one run per workload):", "", "    " + command, "",
+             "Calibration: the plain copy `copy_f32` (2^28 fp32: 1 GiB read, 1 GiB written) reads "
+             "FETCH_SIZE = %.0f KiB and WRITE_SIZE = %.0f KiB per dispatch, so FETCH_SIZE is scaled by "
+             "%.4f and WRITE_SIZE by %.4f." % (f_copy, w_copy, cal_f, cal_w), "",
+             "kernel source hash: %s" % khash, "",
+             "| workload | kernel | dispatches | FETCH KiB | WRITE KiB | read B (scaled) | algorithmic read B | "
+             "ratio | written B (scaled) | algorithmic write B | ratio |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for wl in W.CONFIGS + ["copy_f32"]:
+        name, f, nf = per_dispatch("fetch", wl)
+        _, w, _ = per_dispatch("write", wl)
+        rd, wr = read_write_bytes(wl)
+        fb, wb = f * 1024 * cal_f, w * 1024 * cal_w
+        rec = {"workload": wl, "kernel": name, "dispatches": nf, "fetch_kib_per_dispatch": f,
+               "write_kib_per_dispatch": w, "fetch_scale": cal_f, "write_scale": cal_w,
+               "read_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+               "hbm_bytes_per_launch": fb + wb, "algorithmic_read_bytes": rd,
+               "algorithmic_write_bytes": wr, "read_ratio": fb / rd, "write_ratio": wb / wr,
+               "kernel_source_hash": khash, "command": command}
+        with open(os.path.join(PROFILES, "counters_%s.json" % wl), "w") as out:
+            json.dump(rec, out, indent=1)
+        lines.append("| %s | `%s` | %d | %.0f | %.0f | %.0f | %d | %.4f | %.0f | %d | %.4f |" % (
+            wl, name[:70], nf, f, w, fb, rd, fb / rd, wb, wr, wb / wr))
+    with open(os.path.join(PROFILES, "counters_summary.md"), "w") as out:
+        out.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_trace(directory, wl, bench_json, command):
+    """profiles/kernel_trace_<wl>.txt from a rocprofv3 --kernel-trace --stats
+    run of bench.py and the JSON line that same run printed."""
+    rows = [r for r in _csv_rows(directory, "kernel_stats.csv") if "ecmd::k_" in r["Name"]]
+    assert len(rows) == 1, [r["Name"] for r in rows]
+    r = rows[0]
+    with open(bench_json) as f:
+        line = json.loads([l for l in f.read().splitlines() if l.startswith("{")][-1])
+    prof_us = float(r["AverageNs"]) / 1e3
+    bench_us = line["roofline"]["kernel_avg_us"]
+    text = ["kernel trace: %s" % wl, "", "command:", "    " + command, "",
+            "rocprofv3 kernel stats (ecmd kernel row):"]
+    text += ["    %s: %s" % (k, v) for k, v in r.items()]
+    text += ["", "bench.py HIP-event average over the same run's timed launches: %.3f us" % bench_us,
+             "rocprofv3 average over all dispatches (warm-up + timed): %.3f us" % prof_us,
+             "difference: %.2f %%" % (100 * (prof_us - bench_us) / bench_us),
+             "bench value: %s %s; roofline achieved %s GB/s = %.1f %% of %s GB/s" % (
+                 line["value"], line["unit"], line["roofline"]["achieved"], 100 * line["roofline"]["frac"],
+                 line["roofline"]["peak"]),
+             "kernel source hash: %s" % kernel_source_hash()]
+    with open(os.path.join(PROFILES, "kernel_trace_%s.txt" % wl), "w") as out:
+        out.write("\n".join(text) + "\n")
+    print("\n".join(text))
 
 
 def main():
@@ -189,7 +318,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold (cache-flushed) launches, e.g. under a kernel-trace profiler")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write profiles/ counter summaries from rocprofv3 --pmc output in DIR and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "BENCH_JSON"),
+                    help="write profiles/kernel_trace_<workload>.txt from a kernel-trace run and exit")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     a = ap.parse_args()
+    if a.summarize_counters:
+        summarize_counters(a.summarize_counters, a.command)
+        return
+    if a.summarize_trace:
+        summarize_trace(a.summarize_trace[0], a.workload, a.summarize_trace[1], a.command)
+        return
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
@@ -232,7 +372,7 @@ def main():
     }
     if a.all:
         line["commands"] = {}
-        for wl in W.WORKLOADS:
+        for wl in W.CONFIGS + ["copy_f32"]:
             if wl == a.workload:
                 r = head
             else:
@@ -241,10 +381,11 @@ def main():
             line["commands"][wl] = {
                 "kernel": r["kernel"], "gbps": round(r["kernel_gbps"], 1),
                 "pct_of_peak": round(100 * r["kernel_gbps"] / PEAK_GBPS, 2),
+                "avg_us": round(r["kernel_avg_us"], 3),
                 "median_us": round(r["kernel_median_us"], 3), "p10_us": round(r["kernel_p10_us"], 3),
                 "p90_us": round(r["kernel_p90_us"], 3), "cold_median_us": round(r["cold_median_us"], 3),
                 "cold_gbps": round(r["cold_gbps"], 1), "whole_job_gbps": round(r["whole_job_gbps"], 1),
-                "gelem_per_s": round(r["elements"] / (r["kernel_median_us"] * 1e-6) / 1e9, 2),
+                "gelem_per_s": round(r["elements"] / (r["kernel_avg_us"] * 1e-6) / 1e9, 2),
             }
             log("%s: %s" % (wl, json.dumps(line["commands"][wl])))
     if not a.no_cpu_baseline:

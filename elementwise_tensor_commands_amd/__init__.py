@@ -212,6 +212,11 @@ class Command:
         handle = stream if isinstance(stream, int) else getattr(stream, "cuda_stream", stream)
         self._check(lib.cmd_launch(self._h, arr, n, ctypes.c_void_p(handle)))
 
+    def bind(self, *values, stream=None) -> "BoundLaunch":
+        """Marshal the argument values once; the returned object launches the
+        Command with them in a single C call (for repeated launches)."""
+        return BoundLaunch(self, values, stream)
+
     def plan(self, *values) -> dict:
         """What launch would do with these values (host only, no GPU needed)."""
         arr, n = self._args(values)
@@ -229,6 +234,27 @@ class Command:
         buf = ctypes.create_string_buffer(int(n) + 1)
         lib.cmd_dump(self._h, buf, n + 1)
         return buf.value.decode()
+
+
+class BoundLaunch:
+    """A Command with its argument values marshalled (rocRoller "Design
+    Overview", section "Command Kernel": a kernel launched with a prepared
+    block of runtime arguments)."""
+
+    def __init__(self, cmd: Command, values, stream=None):
+        self.cmd = cmd
+        self.values = values                   # keeps the tensors alive
+        self.arr, self.n = cmd._args(values)
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream()
+        handle = stream if isinstance(stream, int) else getattr(stream, "cuda_stream", stream)
+        self.stream = ctypes.c_void_p(handle)
+
+    def launch(self):
+        rc = lib.cmd_launch(self.cmd._h, self.arr, self.n, self.stream)
+        if rc:
+            self.cmd._check(rc)
 
 
 def from_spec(spec) -> Command:

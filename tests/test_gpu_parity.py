@@ -229,6 +229,22 @@ def test_non_default_stream():
     compare(out.cpu().numpy(), ref, 0, "side stream")
 
 
+def test_bound_launch_repeated():
+    """The marshal-once launcher, launched repeatedly on one stream."""
+    n = (1 << 20) + 9
+    vals, _ = W.make_inputs("mixed_two_out", n)
+    ref = run_oracle(W.MIXED_TWO_OUT, vals)
+    import elementwise_tensor_commands_amd as ecmd
+    gv = [to_dev(v) if isinstance(v, np.ndarray) else v for v in vals]
+    outs = [torch.empty(n, dtype=torch.float16, device=dev()), torch.empty(n, dtype=torch.float32, device=dev())]
+    bound = ecmd.from_spec(W.MIXED_TWO_OUT).bind(*gv, *outs)
+    for _ in range(5):
+        bound.launch()
+    torch.cuda.synchronize()
+    compare(outs[0].cpu().numpy(), ref[0], 2, "bound out0")
+    compare(outs[1].cpu().numpy(), ref[1], 2, "bound out1")
+
+
 def test_rejected_launch_leaves_output():
     """Failed checks submit nothing: the output keeps its contents."""
     import elementwise_tensor_commands_amd as ecmd

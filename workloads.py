@@ -94,7 +94,12 @@ WORKLOADS = {
                           label="fp16 x,y,z -> out0=fp16(u*v), out1=u+s, t=x*y shared, n=2^27"),
     "transposed_2d": dict(index=4, spec=TRANSPOSED_2D, n=16384,
                           label="out[i,j] = X[i,j] + alpha*Y[j,i], fp32 16384x16384, X row stride 16448"),
+    # Not one of the five configurations: a plain copy of known size, the
+    # bandwidth reference and the calibration kernel for the HBM counters.
+    "copy_f32": dict(index=5, spec=COPY_F32, n=1 << 28,
+                     label="out = x, fp32, n=2^28 (plain copy reference)"),
 }
+CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
 SCALARS = {
     "int_fused": {"s": np.int32(12345)},
@@ -154,6 +159,8 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
     elif workload == "mixed_two_out":
         vals = [_uniform_pm4_f16(rng, n) for _ in range(3)]
         vals.append(sc["s"])
+    elif workload == "copy_f32":
+        vals = [_uniform_pm1_f32(rng, n)]
     elif workload == "transposed_2d":
         rows = cols = n
         xs = np.full((rows, cols + row_pad), np.nan, dtype=np.float32)
