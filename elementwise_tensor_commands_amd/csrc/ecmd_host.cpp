@@ -63,6 +63,9 @@ struct Selection {
     bool vec = false;
     LinearShape shape{4, 4, false, true};
     bool xcd_remap = false;
+    TileShape tile{64, 64, 256};
+    int walk = 1;
+    int64_t tiles_r = 0, tiles_c = 0;
     int n_staged = 0;
     uint8_t staged[kMaxIn] = {};
     int64_t grid = 0;
@@ -285,6 +288,7 @@ int64_t env_int(const char *name, int64_t dflt)
 //   launches anyway.  Smaller working sets use ordinary loads so that repeated
 //   launches can hit in that cache.  ECMD_NT_LOAD=0/1 overrides.
 constexpr int64_t kMallBytes = (int64_t)256 << 20;
+constexpr int kDefaultTileM = 32, kDefaultTileN = 256, kDefaultTileBlock = 512, kDefaultTileWalk = 1;
 
 LinearShape linear_shape(int64_t bytes)
 {
@@ -297,6 +301,24 @@ LinearShape linear_shape(int64_t bytes)
     const char *st = std::getenv("ECMD_NT_STORE");
     if (st && *st) s.nt_store = std::strcmp(st, "0") != 0;
     return s;
+}
+
+// Tiled kernel: ECMD_TILE = "TMxTN" or "TMxTNxTB" picks the specialised
+// kernel's tile and work-group size (see launch_tiled for the instantiated
+// set); ECMD_TILE_WALK = tile rows walked before moving right.
+TileShape tile_shape()
+{
+    TileShape t{kDefaultTileM, kDefaultTileN, kDefaultTileBlock};
+    const char *v = std::getenv("ECMD_TILE");
+    int a = 0, b = 0, c = 256;
+    if (v && std::sscanf(v, "%dx%dx%d", &a, &b, &c) >= 2) {
+        const int key = (a * 1000 + b) * 10 + (c == 512 ? 1 : 0);
+        static const int ok[] = {640640, 1281280, 1281281, 1280640, 641280, 641281, 642560,
+                                 642561, 321280, 322560, 322561, 325121};
+        for (int k : ok)
+            if (k == key) t = {a, b, c == 512 ? 512 : 256};
+    }
+    return t;
 }
 
 // Highest element offset a view reaches (views have non-negative strides).
@@ -497,10 +519,14 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         S.path = CMD_PATH_TILED;
         S.n_staged = n_staged;
         S.variant = (!force_generic && std::memcmp(&P, &kProgAddScaledF32, sizeof(Program)) == 0 && mask == 0x2) ? 0 : -1;
+        S.tile = S.variant == 0 ? tile_shape() : TileShape{64, 64, 256};   // the interpreter has one shape
+        S.walk = (int)env_int("ECMD_TILE_WALK", kDefaultTileWalk);
         S.e = 4;
-        S.block = kTileBlock;
-        S.grid = ((B.rows + kTileRows - 1) / kTileRows) * ((B.cols + kTileCols - 1) / kTileCols);
-        S.lds = n_staged * kTileCols * (kTileRows + 1) * 4;
+        S.block = S.tile.block;
+        S.tiles_r = (B.rows + S.tile.tm - 1) / S.tile.tm;
+        S.tiles_c = (B.cols + S.tile.tn - 1) / S.tile.tn;
+        S.grid = S.tiles_r * S.tiles_c;
+        S.lds = n_staged * S.tile.tn * (S.tile.tm + 1) * 4;
         S.name = S.variant == 0 ? "tiled_add_scaled_f32" : "tiled_generic";
         return;
     }
@@ -542,7 +568,9 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
     }
     A.rows = B.rows;
     A.cols = B.cols;
-    A.tiles_c = (B.cols + kTileCols - 1) / kTileCols;
+    A.tiles_r = S.tiles_r;
+    A.tiles_c = S.tiles_c;
+    A.tile_walk = S.walk;
     std::memcpy(A.uni, B.uni, sizeof A.uni);
     A.prog = h->prog;
 }
@@ -724,7 +752,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         fill_strided(h, B, S, A);
         const char *ntv = std::getenv("ECMD_TILED_NT");
         const bool nt = !(ntv && std::strcmp(ntv, "0") == 0);
-        herr = S.path == CMD_PATH_TILED ? launch_tiled(S.variant, nt, A, g, hip_stream)
+        herr = S.path == CMD_PATH_TILED ? launch_tiled(S.variant, nt, S.tile, A, g, hip_stream)
                                         : launch_gather(A, g, hip_stream);
     }
     if (herr != 0)

@@ -101,7 +101,8 @@ struct StridedArgs {
     int64_t in_s0[kMaxIn], in_s1[kMaxIn];
     int64_t out_s0[kMaxOut], out_s1[kMaxOut];
     int64_t rows, cols;
-    int64_t tiles_c;          // tiled path: number of column tiles
+    int64_t tiles_r, tiles_c; // tiled path: number of row and column tiles
+    int32_t tile_walk;        // tiled path: tile rows walked before moving right (<= 1: row by row)
     uint32_t uni[kMaxUni];
     uint8_t in_staged[kMaxIn];  // tiled path: 1 = read through an LDS tile (column-contiguous view)
     Program prog;
@@ -206,12 +207,15 @@ struct LinearShape {
 };
 int launch_linear(int variant, bool vec, LinearShape shape, const LinearArgs &A, LaunchGeometry g,
                   void *stream);
-int launch_tiled(int variant, bool nt, const StridedArgs &A, LaunchGeometry g, void *stream);
+// Tiled path: output tile of tm x tn elements (64 or 128 each).
+struct TileShape {
+    int tm, tn;
+    int block;   // work-items per work-group: 256 or 512
+};
+int launch_tiled(int variant, bool nt, TileShape shape, const StridedArgs &A, LaunchGeometry g, void *stream);
 int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
 
 constexpr int kLinearBlock = 256;
-constexpr int kTileRows = 64;      // tiled path: output tile is kTileRows x kTileCols
-constexpr int kTileCols = 64;
 constexpr int kTileBlock = 256;
 constexpr int kGatherE = 4;
 constexpr int kGatherBlock = 256;

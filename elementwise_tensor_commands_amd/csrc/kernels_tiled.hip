@@ -4,38 +4,40 @@
 // Logical shape rows x cols.  An operand view maps (r, c) to r*s0 + c*s1
 // (rocRoller "Design Overview", section "Kernel Graph": each dimension has a
 // size and a stride).  Outputs and "direct" inputs are inner-contiguous
-// (s1 == 1): a row of the tile is one contiguous run.  "Staged" inputs are
+// (s1 == 1): a row of a tile is one contiguous run.  "Staged" inputs are
 // column-contiguous (s0 == 1, e.g. the transpose of a row-major matrix): a
-// column of the tile is one contiguous run, so reading them along rows would
-// touch one element per 64-element stretch of memory.
+// column of a tile is one contiguous run, so reading them along rows would
+// touch one element per run.
 //
-// One work-group (256 work-items, 4 wavefronts) owns a 64 x 64 output tile:
-//   1. For every staged input it reads the 64 tile columns as 64 contiguous
-//      runs of 64 elements (16-byte vectors, 16 work-items per run) and writes
+// One work-group (TB = 256 or 512 work-items) owns a TM x TN output tile:
+//   1. For every staged input it reads the TN tile columns as contiguous runs
+//      of TM elements (16-byte vectors, TM/4 work-items per run) and writes
 //      them into an LDS tile stored column by column with one padding word per
-//      column (65-word pitch).  With the pitch odd, the 16 work-items of a run
-//      and the 4 runs of a wavefront land in 64 distinct banks for every word
-//      they write, and the transposed read in step 2 does too.
-//   2. After a barrier each work-item evaluates 4 steps of 4 consecutive
-//      elements of one row: direct inputs are read with 16-byte vector loads,
-//      staged inputs from LDS, and outputs are written with 16-byte stores,
-//      so every global access is a contiguous run of 256 bytes per row.
-// Global accesses of full tiles use the nontemporal cache policy by default
-// (each instruction covers whole cache lines).
-// Edge tiles (rows or cols not a multiple of 64) use per-element masked
-// accesses.  Staging is a prior-art idea the Silk backend also assumes (its
-// tiled kernels default to a 16 KiB LDS segment, Silk "AMDGPU Backend",
-// section "Code Object Format"): a 64 x 65 binary32 tile is 16,640 bytes.
+//      column (pitch TM + 1, odd).  With an odd pitch the transposed read in
+//      step 2 hits 64 distinct banks for a 64 x 64 tile.
+//   2. After one barrier each work-item evaluates TM*TN/(4*TB) chunks of 4
+//      consecutive elements of one row: direct inputs are read with 16-byte
+//      vector loads, staged ones from LDS, and outputs are written with 16-byte
+//      stores, so every global access is a contiguous run of TN elements.
+// In the specialised kernels the direct inputs' loads are issued before the
+// barrier, together with the staging loads, so that a tile waits for one
+// round trip to memory instead of two.  Full tiles use the nontemporal cache
+// policy (every instruction covers whole cache lines); edge tiles (rows or
+// cols not a multiple of the tile) use per-element masked accesses.
+//
+// Tile order: tile t of the grid is (t / tiles_c, t % tiles_c) when walk <= 1;
+// otherwise tiles go down a band of `walk` tile rows before moving right, so
+// that tiles running at the same time read neighbouring stretches of the
+// staged input's rows (the same DRAM pages) as well as of the direct inputs'.
+//
+// Staging is a prior-art idea the Silk backend also assumes (its tiled kernels
+// default to a 16 KiB LDS segment, Silk "AMDGPU Backend", section "Code Object
+// Format"): a 64 x 65 binary32 tile is 16,640 bytes.
 #include <hip/hip_runtime.h>
 
 #include "ecmd_eval.h"
 
 namespace ecmd {
-
-constexpr int TM = kTileRows;
-constexpr int TN = kTileCols;
-constexpr int kPitch = TM + 1;          // LDS words per staged tile column
-constexpr int kTileWords = TN * kPitch;
 
 // Staged-input mask: bit k set = input k goes through LDS.  kMaskRuntime reads
 // the mask from the argument block.
@@ -56,119 +58,177 @@ __device__ __forceinline__ int stage_pos(const StridedArgs &A, int k)
     else return __builtin_popcount(MASK & ((1 << k) - 1));
 }
 
-// Copy the tile's columns c0..c0+TN-1, rows r0..r0+TM-1 of a column-contiguous
-// view into LDS: dst[cl * kPitch + rl].
-template <bool NTL>
-__device__ __forceinline__ void stage_tile(const void *base, uint8_t ty, int64_t s1, int64_t r0,
-                                           int64_t c0, int64_t rows, int64_t cols, bool full,
-                                           uint32_t *dst)
-{
-    const int t = threadIdx.x;
-    const int q = t & 15;            // 4-row chunk of the column
-    const int lane_line = t >> 4;    // 0..15
-#pragma unroll
-    for (int pass = 0; pass < TN / 16; ++pass) {
-        const int cl = lane_line + 16 * pass;
-        const int rl = 4 * q;
-        const int64_t off = (c0 + cl) * s1 + (r0 + rl);
-        uint32_t v[4];
-        if (full) {
-            load_group<4, true, NTL>(base, ty, off, 4, v);
-        } else {
-            int count = 0;
-            if (c0 + cl < cols) {
-                const int64_t left = rows - (r0 + rl);
-                count = left <= 0 ? 0 : (left >= 4 ? 4 : (int)left);
-            }
-            if (count > 0) load_elems<4, false>(base, ty, off, count, v);
-            else v[0] = v[1] = v[2] = v[3] = 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[cl * kPitch + rl + j] = v[j];
-    }
-}
+__device__ __forceinline__ int clamp4(int64_t left) { return left <= 0 ? 0 : (left >= 4 ? 4 : (int)left); }
 
-template <class EV, int MASK, bool NT>
-__global__ __launch_bounds__(kTileBlock) void k_tiled(const StridedArgs A)
+template <class EV, int MASK, bool NT, int TM, int TN, int TB>
+__global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
 {
+    constexpr int kPitch = TM + 1;
+    constexpr int kWords = TN * kPitch;
+    constexpr int kRunVec = TM / 4;                     // 4-element vectors per staged column run
+    constexpr int kSV = TN * TM / 4 / TB;               // staging vectors per work-item per staged input
+    constexpr int kRowVec = TN / 4;                     // 4-element chunks per output row
+    constexpr int kP = TM * TN / 4 / TB;                // chunks per work-item
+    constexpr bool kPrefetch = MASK != kMaskRuntime;
+    static_assert(kSV >= 1 && kP >= 1, "tile too small for the work-group");
     extern __shared__ uint32_t lds[];
-    // Tile counts fit in 32 bits (the grid is one dimension of < 2^31 groups).
-    const uint32_t tile = blockIdx.x;
-    const uint32_t tiles_c = (uint32_t)A.tiles_c;
-    const uint32_t tr = tile / tiles_c;
-    const uint32_t tc = tile - tr * tiles_c;
+
+    // Tile coordinates (all counts fit in 32 bits: the grid is one dimension).
+    const uint32_t id = blockIdx.x;
+    const uint32_t tiles_c = (uint32_t)A.tiles_c, tiles_r = (uint32_t)A.tiles_r;
+    const uint32_t walk = (uint32_t)A.tile_walk;
+    uint32_t tr, tc;
+    if (walk <= 1) {
+        tr = id / tiles_c;
+        tc = id - tr * tiles_c;
+    } else {
+        const uint32_t band = walk * tiles_c;
+        const uint32_t b = id / band, rem = id - b * band;
+        const uint32_t left = tiles_r - b * walk;
+        const uint32_t h = left < walk ? left : walk;
+        tc = rem / h;
+        tr = b * walk + (rem - tc * h);
+    }
     const int64_t r0 = (int64_t)tr * TM, c0 = (int64_t)tc * TN;
     const bool full = (r0 + TM <= A.rows) && (c0 + TN <= A.cols);
     const int t = threadIdx.x;
 
+    // Direct inputs of every chunk, loaded up front in the specialised kernels.
+    Regs<4> R[kP];
+    int count[kP];
 #pragma unroll
-    for (int k = 0; k < kMaxIn; ++k)
-        if (k < EV::n_in(A.prog) && staged<MASK>(A, k))
-            stage_tile<NT>(A.in[k], EV::in_ty(A.prog, k), A.in_s1[k], r0, c0, A.rows, A.cols, full,
-                       lds + stage_pos<MASK>(A, k) * kTileWords);
-    __syncthreads();
-
-    const int cl = (t & 15) * 4;
-#pragma unroll
-    for (int p = 0; p < TM / 16; ++p) {
-        const int rl = (t >> 4) + 16 * p;
-        const int64_t r = r0 + rl, c = c0 + cl;
-        int count = 4;
-        if (!full) {
-            const int64_t left = A.cols - c;
-            count = (r >= A.rows || left <= 0) ? 0 : (left >= 4 ? 4 : (int)left);
-            if (count == 0) continue;
-        }
-        Regs<4> R;
+    for (int p = 0; p < kP; ++p) {
+        const int v = t + TB * p;
+        const int rl = v / kRowVec, cl = 4 * (v % kRowVec);
+        count[p] = full ? 4 : (r0 + rl < A.rows ? clamp4(A.cols - (c0 + cl)) : 0);
+    }
+    auto load_direct = [&](int p) {
+        const int v = t + TB * p;
+        const int64_t r = r0 + v / kRowVec, c = c0 + 4 * (v % kRowVec);
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
-            if (k < EV::n_in(A.prog)) {
-                if (staged<MASK>(A, k)) {
-                    const uint32_t *src = lds + stage_pos<MASK>(A, k) * kTileWords;
+            if (k < EV::n_in(A.prog) && !staged<MASK>(A, k)) {
+                const int64_t off = r * A.in_s0[k] + c;
+                if (full) load_group<4, true, NT>(A.in[k], EV::in_ty(A.prog, k), off, 4, R[p].in[k]);
+                else if (count[p] > 0) load_elems<4, false>(A.in[k], EV::in_ty(A.prog, k), off, count[p], R[p].in[k]);
+            }
+        }
+    };
+    if constexpr (kPrefetch) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) R.in[k][j] = src[(cl + j) * kPitch + rl];
+        for (int p = 0; p < kP; ++p) load_direct(p);
+    }
+
+    // Stage the column-contiguous inputs: LDS word (cl, rl) at cl * kPitch + rl.
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) {
+        if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
+            const uint8_t ty = EV::in_ty(A.prog, k);
+            uint32_t *dst = lds + stage_pos<MASK>(A, k) * kWords;
+            uint32_t sv[kSV][4];
+#pragma unroll
+            for (int j = 0; j < kSV; ++j) {
+                const int v = t + TB * j;
+                const int cl = v / kRunVec, rl = 4 * (v % kRunVec);
+                const int64_t off = (c0 + cl) * A.in_s1[k] + (r0 + rl);
+                if (full) {
+                    load_group<4, true, NT>(A.in[k], ty, off, 4, sv[j]);
                 } else {
-                    const int64_t off = r * A.in_s0[k] + c;
-                    if (full) load_group<4, true, NT>(A.in[k], EV::in_ty(A.prog, k), off, 4, R.in[k]);
-                    else load_elems<4, false>(A.in[k], EV::in_ty(A.prog, k), off, count, R.in[k]);
+                    const int cnt = c0 + cl < A.cols ? clamp4(A.rows - (r0 + rl)) : 0;
+                    if (cnt > 0) load_elems<4, false>(A.in[k], ty, off, cnt, sv[j]);
+                    else sv[j][0] = sv[j][1] = sv[j][2] = sv[j][3] = 0u;
                 }
+            }
+#pragma unroll
+            for (int j = 0; j < kSV; ++j) {
+                const int v = t + TB * j;
+                const int cl = v / kRunVec, rl = 4 * (v % kRunVec);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[cl * kPitch + rl + e] = sv[j][e];
+            }
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+        if (count[p] == 0) continue;
+        const int v = t + TB * p;
+        const int rl = v / kRowVec, cl = 4 * (v % kRowVec);
+        const int64_t r = r0 + rl, c = c0 + cl;
+        if constexpr (!kPrefetch) load_direct(p);
+#pragma unroll
+        for (int k = 0; k < kMaxIn; ++k) {
+            if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
+                const uint32_t *src = lds + stage_pos<MASK>(A, k) * kWords;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) R[p].in[k][e] = src[(cl + e) * kPitch + rl];
             }
         }
         uint32_t out[kMaxOut][4];
-        EV::template run<4>(A.prog, A.uni, R, out);
+        EV::template run<4>(A.prog, A.uni, R[p], out);
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < EV::n_out(A.prog)) {
                 const int64_t off = r * A.out_s0[k] + c;
                 if (full) store_group<4, true, NT>(A.out[k], EV::out_ty(A.prog, k), off, 4, out[k]);
-                else store_elems<4, false, false>(A.out[k], EV::out_ty(A.prog, k), off, count, out[k]);
+                else store_elems<4, false, false>(A.out[k], EV::out_ty(A.prog, k), off, count[p], out[k]);
             }
         }
     }
 }
 
-template <class EV, int MASK, bool NT>
+template <class EV, int MASK, bool NT, int TM, int TN, int TB>
 static int launch_one(const StridedArgs &A, LaunchGeometry g, void *stream, int lds_bytes)
 {
-    hipLaunchKernelGGL((k_tiled<EV, MASK, NT>), dim3((unsigned)g.grid), dim3(g.block),
-                       (unsigned)lds_bytes, (hipStream_t)stream, A);
+    auto kern = k_tiled<EV, MASK, NT, TM, TN, TB>;
+    // Above 64 KiB of dynamic LDS the kernel must be allowed more, once per
+    // process (the largest instantiated tile needs 128 * 129 * 4 bytes per
+    // staged input, within gfx950's 160 KiB).
+    static int lds_allowed = 65536;
+    if (lds_bytes > lds_allowed) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (e != hipSuccess) return (int)e;
+        lds_allowed = lds_bytes;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)g.grid), dim3(TB), (unsigned)lds_bytes, (hipStream_t)stream, A);
     return (int)hipGetLastError();
 }
 
-int tiled_lds_bytes(int n_staged) { return n_staged * kTileWords * 4; }
+template <class EV, int MASK, int TM, int TN, int TB>
+static int launch_nt(bool nt, const StridedArgs &A, LaunchGeometry g, void *stream, int lds)
+{
+    return nt ? launch_one<EV, MASK, true, TM, TN, TB>(A, g, stream, lds)
+              : launch_one<EV, MASK, false, TM, TN, TB>(A, g, stream, lds);
+}
 
-int launch_tiled(int variant, bool nt, const StridedArgs &A, LaunchGeometry g, void *stream)
+int launch_tiled(int variant, bool nt, TileShape shape, const StridedArgs &A, LaunchGeometry g, void *stream)
 {
     int n_staged = 0;
     for (int k = 0; k < A.prog.n_in; ++k) n_staged += A.in_staged[k] != 0;
-    const int lds = tiled_lds_bytes(n_staged);
-    // The specialised kernel for out = X + alpha * Yt is instantiated with Yt
-    // (input 1) staged; the host only picks it for that staging mask.
-    if (variant == 0)
-        return nt ? launch_one<CtEval<kProgAddScaledF32>, 0x2, true>(A, g, stream, lds)
-                  : launch_one<CtEval<kProgAddScaledF32>, 0x2, false>(A, g, stream, lds);
-    return nt ? launch_one<RtEval, kMaskRuntime, true>(A, g, stream, lds)
-              : launch_one<RtEval, kMaskRuntime, false>(A, g, stream, lds);
+    const int lds = n_staged * shape.tn * (shape.tm + 1) * 4;
+    if (variant == 0) {
+        // out = X + alpha * Yt with Yt (input 1) staged; the host picks it only
+        // for that staging mask.
+        using EV = CtEval<kProgAddScaledF32>;
+        const int key = (shape.tm * 1000 + shape.tn) * 10 + (shape.block == 512 ? 1 : 0);
+        switch (key) {
+        case 1281280: return launch_nt<EV, 0x2, 128, 128, 256>(nt, A, g, stream, lds);
+        case 1281281: return launch_nt<EV, 0x2, 128, 128, 512>(nt, A, g, stream, lds);
+        case 1280640: return launch_nt<EV, 0x2, 128, 64, 256>(nt, A, g, stream, lds);
+        case 641280: return launch_nt<EV, 0x2, 64, 128, 256>(nt, A, g, stream, lds);
+        case 641281: return launch_nt<EV, 0x2, 64, 128, 512>(nt, A, g, stream, lds);
+        case 642560: return launch_nt<EV, 0x2, 64, 256, 256>(nt, A, g, stream, lds);
+        case 642561: return launch_nt<EV, 0x2, 64, 256, 512>(nt, A, g, stream, lds);
+        case 321280: return launch_nt<EV, 0x2, 32, 128, 256>(nt, A, g, stream, lds);
+        case 322560: return launch_nt<EV, 0x2, 32, 256, 256>(nt, A, g, stream, lds);
+        case 322561: return launch_nt<EV, 0x2, 32, 256, 512>(nt, A, g, stream, lds);
+        case 325121: return launch_nt<EV, 0x2, 32, 512, 512>(nt, A, g, stream, lds);
+        default: return launch_nt<EV, 0x2, 64, 64, 256>(nt, A, g, stream, lds);
+        }
+    }
+    return launch_nt<RtEval, kMaskRuntime, 64, 64, 256>(nt, A, g, stream, lds);
 }
 
 }  // namespace ecmd

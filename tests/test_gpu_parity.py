@@ -134,6 +134,28 @@ def test_transposed_small(n):
     assert plan["path"] == ("linear" if n == 1 else "tiled" if n % 4 == 0 else "gather")
 
 
+@pytest.mark.parametrize("tile", ["64x64", "128x64", "64x128", "128x128", "32x128", "32x256", "64x256",
+                                  "128x128x512", "64x128x512", "64x256x512", "32x256x512", "32x512x512"])
+@pytest.mark.parametrize("walk", ["1", "3", "8"])
+def test_tiled_shapes(tile, walk):
+    """Every specialised tiled instantiation and tile order against the oracle,
+    on a square that is not a multiple of any tile (edge tiles in both
+    directions) and on one that is."""
+    env = {"ECMD_TILE": tile, "ECMD_TILE_WALK": walk}
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        for n in (1000, 512):
+            plan = _check_workload("transposed_2d", n)
+            assert plan["kernel"] == "tiled_add_scaled_f32"
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 @pytest.mark.parametrize("n", [64, 200, 1000])
 def test_transposed_cached_policy(n):
     """The tiled kernels with ordinary (not nontemporal) global accesses."""
