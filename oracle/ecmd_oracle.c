@@ -28,6 +28,11 @@
  *           kept (Silk "AMDGPU Backend", section "Code Object Format": the
  *           default execution mode keeps FP32/FP16 denormals, mode 3).
  *   Neg   : IEEE negate, i.e. flip the sign bit (int32: 0 - a mod 2^32).
+ *   Abs   : clear the sign bit (int32: |INT_MIN| wraps to INT_MIN).
+ *   Compare (EQ NE LT LE GT GE; LTU LEU GTU GEU on int32 as unsigned) gives
+ *           int32 1 or 0; binary32 comparisons are IEEE (false with a NaN,
+ *           except NE).  Min / Max: signed int32; binary32 ignores a NaN
+ *           operand and orders -0 below +0.  Select(c, x, y) = c != 0 ? x : y.
  *   f16->f32 exact; f32->f16 and i32->f16 round to nearest even from the exact
  *   value, overflow to infinity, gradual underflow; i32->f32 round to nearest
  *   even; f32->i32 and f16->i32 truncate toward zero, saturate, NaN -> 0.
@@ -55,12 +60,27 @@
 #define OR_MUL 3
 #define OR_NEG 4
 #define OR_CVT 5
+/* comparisons give int32 1 (true) or 0 (false); *_U compare int32 bit patterns as unsigned */
+#define OR_CMP_EQ 6
+#define OR_CMP_NE 7
+#define OR_CMP_LT 8
+#define OR_CMP_LE 9
+#define OR_CMP_GT 10
+#define OR_CMP_GE 11
+#define OR_CMP_LTU 12
+#define OR_CMP_LEU 13
+#define OR_CMP_GTU 14
+#define OR_CMP_GEU 15
+#define OR_MIN 16
+#define OR_MAX 17
+#define OR_ABS 18
+#define OR_SELECT 19   /* a != 0 ? b : c */
 
-/* One tag of the Command.  kind = load / scalar / op.  For an op, a and b are
- * earlier tags (b = -1 for the unary Neg and Cvt).  For a load or scalar, arg is
- * the CommandArgument index it reads. */
+/* One tag of the Command.  kind = load / scalar / op.  For an op, a, b and c
+ * are earlier tags (-1 when the operation has fewer operands; only Select has
+ * three).  For a load or scalar, arg is the CommandArgument index it reads. */
 typedef struct {
-    int32_t kind, dtype, op, a, b, arg;
+    int32_t kind, dtype, op, a, b, c, arg;
 } oracle_node;
 
 /* One store: write tag's value through the view of argument arg. */
@@ -182,8 +202,74 @@ int oracle_check_fpenv(void)
 /* ------------------------------------------------------------------------ */
 /* One E_ operation on bit patterns.                                         */
 
-static uint32_t apply_op(int op, int dst_dtype, int src_dtype, uint32_t a, uint32_t b)
+/* binary32 minimum / maximum: a NaN operand is ignored unless both are NaN,
+ * and -0 counts as smaller than +0 (IEEE 754-2019 minimumNumber and
+ * maximumNumber). */
+static float min_number(float x, float y)
 {
+    if (isnan(x)) return y;
+    if (isnan(y)) return x;
+    if (x < y) return x;
+    if (y < x) return y;
+    return signbit(x) ? x : y;          /* equal: pick -0 over +0 */
+}
+
+static float max_number(float x, float y)
+{
+    if (isnan(x)) return y;
+    if (isnan(y)) return x;
+    if (x > y) return x;
+    if (y > x) return y;
+    return signbit(x) ? y : x;          /* equal: pick +0 over -0 */
+}
+
+static uint32_t compare(int op, int src_dtype, uint32_t a, uint32_t b)
+{
+    int r;
+    if (op >= OR_CMP_LTU) {                     /* unsigned int32 */
+        if (op == OR_CMP_LTU) r = a < b;
+        else if (op == OR_CMP_LEU) r = a <= b;
+        else if (op == OR_CMP_GTU) r = a > b;
+        else r = a >= b;
+    } else if (src_dtype == OR_I32) {           /* signed int32 */
+        int32_t x = (int32_t)a, y = (int32_t)b;
+        if (op == OR_CMP_EQ) r = x == y;
+        else if (op == OR_CMP_NE) r = x != y;
+        else if (op == OR_CMP_LT) r = x < y;
+        else if (op == OR_CMP_LE) r = x <= y;
+        else if (op == OR_CMP_GT) r = x > y;
+        else r = x >= y;
+    } else {                                    /* binary32: C's IEEE comparisons */
+        float x = f32_from_bits(a), y = f32_from_bits(b);
+        if (op == OR_CMP_EQ) r = x == y;
+        else if (op == OR_CMP_NE) r = x != y;  /* true when either is NaN */
+        else if (op == OR_CMP_LT) r = x < y;
+        else if (op == OR_CMP_LE) r = x <= y;
+        else if (op == OR_CMP_GT) r = x > y;
+        else r = x >= y;
+    }
+    return r ? 1u : 0u;
+}
+
+static uint32_t apply_op(int op, int dst_dtype, int src_dtype, uint32_t a, uint32_t b, uint32_t c)
+{
+    if (op >= OR_CMP_EQ && op <= OR_CMP_GEU)
+        return compare(op, src_dtype, a, b);
+    if (op == OR_SELECT)
+        return a != 0u ? b : c;
+    if (op == OR_ABS) {
+        if (dst_dtype == OR_I32) return (a & 0x80000000u) ? 0u - a : a;   /* |INT_MIN| wraps to INT_MIN */
+        if (dst_dtype == OR_F32) return a & 0x7fffffffu;
+        return a & 0x7fffu;
+    }
+    if (op == OR_MIN || op == OR_MAX) {
+        if (dst_dtype == OR_I32) {
+            int32_t x = (int32_t)a, y = (int32_t)b;
+            return (uint32_t)(op == OR_MIN ? (x < y ? x : y) : (x > y ? x : y));
+        }
+        float x = f32_from_bits(a), y = f32_from_bits(b);
+        return bits_from_f32(op == OR_MIN ? min_number(x, y) : max_number(x, y));
+    }
     if (op == OR_CVT) {
         if (src_dtype == dst_dtype)
             return a;
@@ -270,7 +356,7 @@ static void *run_range(void *vp)
                 val[t] = J->args[n->arg].bits;
             else
                 val[t] = apply_op(n->op, n->dtype, J->nodes[n->a].dtype, val[n->a],
-                                  n->b >= 0 ? val[n->b] : 0u);
+                                  n->b >= 0 ? val[n->b] : 0u, n->c >= 0 ? val[n->c] : 0u);
         }
         for (int s = 0; s < J->n_stores; ++s)
             write_elem(&J->args[J->stores[s].arg], r, c, val[J->stores[s].tag]);

@@ -34,7 +34,10 @@ NP_BITS = {F16: np.uint16, F32: np.uint32, I32: np.uint32}
 
 LOAD, SCALAR, OP = 1, 2, 3
 ADD, SUB, MUL, NEG, CVT = 1, 2, 3, 4, 5
-OP_CODE = {"add": ADD, "sub": SUB, "mul": MUL, "neg": NEG, "cvt": CVT}
+CMP = {"eq": 6, "ne": 7, "lt": 8, "le": 9, "gt": 10, "ge": 11, "ltu": 12, "leu": 13, "gtu": 14, "geu": 15}
+MIN, MAX, ABS, SELECT = 16, 17, 18, 19
+OP_CODE = {"add": ADD, "sub": SUB, "mul": MUL, "neg": NEG, "cvt": CVT, "min": MIN, "max": MAX,
+           "abs": ABS, "select": SELECT, **CMP}
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread",
              "-Wall", "-Wextra", "-std=c11"]
@@ -52,7 +55,8 @@ def build(force: bool = False) -> str:
 
 class _Node(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("dtype", ctypes.c_int32), ("op", ctypes.c_int32),
-                ("a", ctypes.c_int32), ("b", ctypes.c_int32), ("arg", ctypes.c_int32)]
+                ("a", ctypes.c_int32), ("b", ctypes.c_int32), ("c", ctypes.c_int32),
+                ("arg", ctypes.c_int32)]
 
 
 class _Store(ctypes.Structure):
@@ -120,7 +124,7 @@ class OracleCommand:
     indexes count loads, scalars and stores in declaration order."""
 
     def __init__(self):
-        self.nodes: list[tuple] = []      # (kind, dtype, op, a, b, arg)
+        self.nodes: list[tuple] = []      # (kind, dtype, op, a, b, c, arg)
         self.stores: list[tuple] = []     # (tag, arg)
         self.args: list[tuple] = []       # ("tensor"|"scalar", dtype, rank, is_output)
 
@@ -130,24 +134,24 @@ class OracleCommand:
         if rank not in (1, 2):
             raise OracleError("rank must be 1 or 2")
         self.args.append(("tensor", dt, rank, False))
-        self.nodes.append((LOAD, dt, 0, -1, -1, len(self.args) - 1))
+        self.nodes.append((LOAD, dt, 0, -1, -1, -1, len(self.args) - 1))
         return len(self.nodes) - 1
 
     def scalar(self, dtype) -> int:
         dt = _dt(dtype)
         self.args.append(("scalar", dt, 0, False))
-        self.nodes.append((SCALAR, dt, 0, -1, -1, len(self.args) - 1))
+        self.nodes.append((SCALAR, dt, 0, -1, -1, -1, len(self.args) - 1))
         return len(self.nodes) - 1
 
     def _check_tag(self, t):
         if not (0 <= t < len(self.nodes)):
             raise OracleError("tag %r does not name an earlier result" % (t,))
 
-    def op(self, name: str, a: int, b: int | None = None, dtype=None) -> int:
+    def op(self, name: str, a: int, b: int | None = None, dtype=None, c: int | None = None) -> int:
         code = OP_CODE[name]
         self._check_tag(a)
         da = self.nodes[a][1]
-        if code in (ADD, SUB, MUL):
+        if code in (ADD, SUB, MUL, MIN, MAX) or code in CMP.values():
             if b is None:
                 raise OracleError("binary op needs two operands")
             self._check_tag(b)
@@ -156,10 +160,22 @@ class OracleCommand:
                 raise OracleError("operand dtypes differ")
             if da == F16:
                 raise OracleError("binary16 arithmetic is not part of the op set")
-            res = da
-        elif code == NEG:
+            if code in (CMP["ltu"], CMP["leu"], CMP["gtu"], CMP["geu"]) and da != I32:
+                raise OracleError("unsigned comparison needs int32 operands")
+            res = I32 if code in CMP.values() else da
+        elif code == SELECT:
+            if b is None or c is None:
+                raise OracleError("select takes a condition and two values")
+            self._check_tag(b)
+            self._check_tag(c)
+            if da != I32:
+                raise OracleError("select condition must be int32")
+            if self.nodes[b][1] != self.nodes[c][1]:
+                raise OracleError("select values differ in dtype")
+            res = self.nodes[b][1]
+        elif code in (NEG, ABS):
             if b is not None:
-                raise OracleError("neg is unary")
+                raise OracleError("neg / abs are unary")
             res = da
         else:
             if b is not None or dtype is None:
@@ -167,14 +183,16 @@ class OracleCommand:
             res = _dt(dtype)
         if dtype is not None and _dt(dtype) != res:
             raise OracleError("result dtype mismatch")
-        self.nodes.append((OP, res, code, a, -1 if b is None else b, -1))
+        self.nodes.append((OP, res, code, a, -1 if b is None else b, -1 if c is None else c, -1))
         return len(self.nodes) - 1
 
     def add(self, a, b): return self.op("add", a, b)
     def sub(self, a, b): return self.op("sub", a, b)
     def mul(self, a, b): return self.op("mul", a, b)
     def neg(self, a): return self.op("neg", a)
+    def abs(self, a): return self.op("abs", a)
     def cvt(self, a, dtype): return self.op("cvt", a, None, dtype)
+    def select(self, cond, x, y): return self.op("select", cond, x, None, y)
 
     def store(self, tag: int, rank: int = 1) -> int:
         self._check_tag(tag)
@@ -277,10 +295,11 @@ def f16_to_f32_all() -> np.ndarray:
 
 
 def from_spec(spec) -> OracleCommand:
-    """Build an OracleCommand from a declarative workload spec (a list of steps
-    such as ("load", "f32", 1), ("scalar", "f32"), ("add", a, b), ("neg", a),
-    ("cvt", a, "f16"), ("store", t, 1)); step i's result is tag i for value
-    steps.  Returns the command; tags follow the spec's own numbering."""
+    """Build an OracleCommand from a declarative workload spec: a list of
+    (name, step) pairs with steps ("load", dtype, rank), ("scalar", dtype),
+    (binary op, a, b) for add sub mul min max and the comparisons, ("neg", a),
+    ("abs", a), ("cvt", a, dtype), ("select", cond, x, y), ("store", value,
+    rank)."""
     cmd = OracleCommand()
     tags = {}
     for name, step in spec:
@@ -289,10 +308,12 @@ def from_spec(spec) -> OracleCommand:
             tags[name] = cmd.load(step[1], step[2] if len(step) > 2 else 1)
         elif kind == "scalar":
             tags[name] = cmd.scalar(step[1])
-        elif kind in ("add", "sub", "mul"):
+        elif kind in ("add", "sub", "mul", "min", "max") or kind in CMP:
             tags[name] = cmd.op(kind, tags[step[1]], tags[step[2]])
-        elif kind == "neg":
-            tags[name] = cmd.neg(tags[step[1]])
+        elif kind in ("neg", "abs"):
+            tags[name] = cmd.op(kind, tags[step[1]])
+        elif kind == "select":
+            tags[name] = cmd.select(tags[step[1]], tags[step[2]], tags[step[3]])
         elif kind == "cvt":
             tags[name] = cmd.cvt(tags[step[1]], step[2])
         elif kind == "store":

@@ -17,6 +17,20 @@ def binary(op, dt):
             ("o", ("store", "r", 1))]
 
 
+def select(dt):
+    return [("c", ("load", "i32", 1)), ("x", ("load", dt, 1)), ("y", ("load", dt, 1)),
+            ("r", ("select", "c", "x", "y")), ("o", ("store", "r", 1))]
+
+
+COMPARES = ["eq", "ne", "lt", "le", "gt", "ge"]
+UNSIGNED = ["ltu", "leu", "gtu", "geu"]
+
+# The threshold classifier of the Silk AMDGPU page's example kernels: an
+# unsigned comparison of every element against a scalar threshold.
+CLASSIFY_U32 = [("x", ("load", "i32", 1)), ("t", ("scalar", "i32")), ("r", ("gtu", "x", "t")),
+                ("o", ("store", "r", 1))]
+
+
 SPECS = {
     "add_f32": W.ADD_F32,
     "int_fused": W.INT_FUSED,
@@ -36,6 +50,18 @@ SPECS = {
 for a in ("f16", "f32", "i32"):
     for b in ("f16", "f32", "i32"):
         SPECS["cvt_%s_%s" % (a, b)] = unary("cvt", a, b)
+for c in COMPARES:
+    SPECS["cmp_%s_f32" % c] = binary(c, "f32")
+    SPECS["cmp_%s_i32" % c] = binary(c, "i32")
+for c in UNSIGNED:
+    SPECS["cmp_%s_i32" % c] = binary(c, "i32")
+for dt in ("f32", "i32"):
+    SPECS["min_" + dt] = binary("min", dt)
+    SPECS["max_" + dt] = binary("max", dt)
+for dt in ("f16", "f32", "i32"):
+    SPECS["abs_" + dt] = unary("abs", dt)
+    SPECS["select_" + dt] = select(dt)
+SPECS["classify_u32"] = CLASSIFY_U32
 
 DT = {"f16": "f16", "f32": "f32", "i32": "i32"}
 
@@ -49,8 +75,12 @@ def arg_dtypes(spec):
         if k in ("load", "scalar"):
             dt[name] = st[1]
             ins.append(st[1])
-        elif k in ("add", "sub", "mul", "neg"):
+        elif k in ("add", "sub", "mul", "neg", "abs", "min", "max"):
             dt[name] = dt[st[1]]
+        elif k in COMPARES or k in UNSIGNED:
+            dt[name] = "i32"
+        elif k == "select":
+            dt[name] = dt[st[2]]
         elif k == "cvt":
             dt[name] = st[2]
         elif k == "store":

@@ -35,6 +35,16 @@ MUTANTS = {
     "scalar_ignored": ("val[t] = J->args[n->arg].bits;", "val[t] = 0u;"),
     "f32_to_i32_rounds": ("return (int32_t)truncf(f);", "return (int32_t)nearbyintf(f);"),
     "second_operand_is_first": ("n->b >= 0 ? val[n->b] : 0u", "n->b >= 0 ? val[n->a] : 0u"),
+    "select_swapped": ("return a != 0u ? b : c;", "return a != 0u ? c : b;"),
+    "unsigned_compare_signed": ("if (op == OR_CMP_LTU) r = a < b;",
+                                "if (op == OR_CMP_LTU) r = (int32_t)a < (int32_t)b;"),
+    "float_ne_ordered": ("else if (op == OR_CMP_NE) r = x != y;  /* true when either is NaN */",
+                         "else if (op == OR_CMP_NE) r = (x < y) || (x > y);"),
+    "min_keeps_nan": ("static float min_number(float x, float y)\n{\n    if (isnan(x)) return y;\n    if (isnan(y)) return x;\n",
+                      "static float min_number(float x, float y)\n{\n"),
+    "min_zero_sign": ("return signbit(x) ? x : y;          /* equal: pick -0 over +0 */", "return x;"),
+    "abs_int_saturates": ("return (a & 0x80000000u) ? 0u - a : a;",
+                          "return (a & 0x80000000u) ? (a == 0x80000000u ? 0x7fffffffu : 0u - a) : a;"),
     "mul_high_dropped": ("return a * b;                        /* low 32 bits of the product */",
                          "return (a & 0xffffu) * (b & 0xffffu);"),
 }

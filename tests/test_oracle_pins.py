@@ -460,3 +460,64 @@ def test_front_end_rejects(oracle_mod):
         c2.run(np.zeros(4, np.float32), np.zeros(5, np.float32))
     with pytest.raises(O.OracleError):
         c2.run(np.zeros(4, np.float32), np.zeros(4, np.int32))
+
+
+# ---------------------------------------------------------------------------
+# Comparisons, select, min / max, abs against NumPy on special-value-rich data.
+
+def _special_f32(rng, n):
+    x = rng.standard_normal(n).astype(np.float32)
+    sp = np.float32([0.0, -0.0, np.inf, -np.inf, np.nan, 1.0, -1.0, 1e-45, -1e-45, 3.4e38])
+    idx = rng.integers(0, n, n // 4)
+    x[idx] = rng.choice(sp, idx.size)
+    return x
+
+
+def test_new_ops_vs_numpy(oracle_mod):
+    from specs import COMPARES, UNSIGNED
+    rng = np.random.default_rng(21)
+    n = 1 << 14
+    x, y = _special_f32(rng, n), _special_f32(rng, n)
+    y[: n // 8] = x[: n // 8]                                  # many equal pairs
+    npcmp = {"eq": np.equal, "ne": np.not_equal, "lt": np.less, "le": np.less_equal,
+             "gt": np.greater, "ge": np.greater_equal}
+    with np.errstate(invalid="ignore"):
+        for c in COMPARES:
+            (r,) = oracle_mod.from_spec(SPECS["cmp_%s_f32" % c]).run(x, y)
+            assert np.array_equal(r, npcmp[c](x, y).astype(np.int32)), c
+    xi = rng.integers(-2**31, 2**31, n, dtype=np.int64).astype(np.int32)
+    yi = rng.integers(-2**31, 2**31, n, dtype=np.int64).astype(np.int32)
+    yi[: n // 8] = xi[: n // 8]
+    for c in COMPARES:
+        (r,) = oracle_mod.from_spec(SPECS["cmp_%s_i32" % c]).run(xi, yi)
+        assert np.array_equal(r, npcmp[c](xi, yi).astype(np.int32)), c
+    for c in UNSIGNED:
+        (r,) = oracle_mod.from_spec(SPECS["cmp_%s_i32" % c]).run(xi, yi)
+        assert np.array_equal(r, npcmp[c[:2]](xi.view(np.uint32), yi.view(np.uint32)).astype(np.int32)), c
+    # min / max: NumPy's fmin / fmax ignore a NaN; tied zeros of opposite sign are
+    # pinned by the hand-worked cases instead (C's fmin may return either)
+    tie = (x == y) & (x == 0)
+    for name, fn in (("min", np.fmin), ("max", np.fmax)):
+        (r,) = oracle_mod.from_spec(SPECS[name + "_f32"]).run(x, y)
+        ref = fn(x, y)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(r), nan)
+        ok = ~nan & ~tie
+        assert np.array_equal(r.view(np.uint32)[ok], ref.view(np.uint32)[ok]), name
+        (ri,) = oracle_mod.from_spec(SPECS[name + "_i32"]).run(xi, yi)
+        assert np.array_equal(ri, (np.minimum if name == "min" else np.maximum)(xi, yi))
+    (r,) = oracle_mod.from_spec(SPECS["abs_f32"]).run(x)
+    assert np.array_equal(r.view(np.uint32), x.view(np.uint32) & np.uint32(0x7FFFFFFF))
+    (r,) = oracle_mod.from_spec(SPECS["abs_i32"]).run(xi)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(r, np.abs(xi))                  # NumPy's abs wraps at INT_MIN too
+    cond = rng.integers(-2, 3, n).astype(np.int32)
+    (r,) = oracle_mod.from_spec(SPECS["select_f32"]).run(cond, x, y)
+    assert np.array_equal(r.view(np.uint32), np.where(cond != 0, x, y).view(np.uint32))
+
+
+def test_fill_is_a_scalar_store(oracle_mod):
+    spec = [("s", ("scalar", "f32")), ("o", ("store", "s", 1))]
+    out = np.zeros(37, np.float32)
+    oracle_mod.from_spec(spec).run(np.float32(-0.0), outputs=[out])
+    assert np.all(out.view(np.uint32) == 0x80000000)
