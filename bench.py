@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0        # MI355X HBM3E peak, 8 TB/s
 METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, per Command"
 DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two_out": "f16/f32",
-            "transposed_2d": "f32", "copy_f32": "f32"}
+            "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -67,8 +67,12 @@ def setup(wl, n=None):
             dts[name] = st[1]
         elif st[0] == "cvt":
             dts[name] = st[2]
-        elif st[0] in ("add", "sub", "mul", "neg"):
+        elif st[0] in ("add", "sub", "mul", "neg", "abs", "min", "max"):
             dts[name] = dts[st[1]]
+        elif st[0] == "select":
+            dts[name] = dts[st[2]]
+        elif st[0] in ("eq", "ne", "lt", "le", "gt", "ge", "ltu", "leu", "gtu", "geu"):
+            dts[name] = "i32"
         elif st[0] == "store":
             out_dt.append(dts[st[1]])
     outs = [torch.empty(shape, dtype=td[d], device=dev) for d in out_dt]
@@ -215,8 +219,12 @@ def read_write_bytes(wl):
             dt[name] = st[1]
         elif st[0] == "cvt":
             dt[name] = st[2]
-        elif st[0] in ("add", "sub", "mul", "neg"):
+        elif st[0] in ("add", "sub", "mul", "neg", "abs", "min", "max"):
             dt[name] = dt[st[1]]
+        elif st[0] == "select":
+            dt[name] = dt[st[2]]
+        elif st[0] in ("eq", "ne", "lt", "le", "gt", "ge", "ltu", "leu", "gtu", "geu"):
+            dt[name] = "i32"
         elif st[0] == "store":
             wr += size[dt[st[1]]]
     e = W.elements(wl)
@@ -263,7 +271,9 @@ def summarize_counters(root, command):
              "| workload | kernel | dispatches | FETCH KiB | WRITE KiB | read B (scaled) | algorithmic read B | "
              "ratio | written B (scaled) | algorithmic write B | ratio |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
-    for wl in W.CONFIGS + ["copy_f32"]:
+    for wl in W.CONFIGS + ["copy_f32", "classify_u32", "fill_f32"]:
+        if not os.path.isdir(os.path.join(root, "fetch_" + wl)):
+            continue
         name, f, nf = per_dispatch("fetch", wl)
         _, w, _ = per_dispatch("write", wl)
         rd, wr = read_write_bytes(wl)
@@ -272,12 +282,13 @@ def summarize_counters(root, command):
                "write_kib_per_dispatch": w, "fetch_scale": cal_f, "write_scale": cal_w,
                "read_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                "hbm_bytes_per_launch": fb + wb, "algorithmic_read_bytes": rd,
-               "algorithmic_write_bytes": wr, "read_ratio": fb / rd, "write_ratio": wb / wr,
+               "algorithmic_write_bytes": wr, "read_ratio": fb / rd if rd else None,
+               "write_ratio": wb / wr,
                "kernel_source_hash": khash, "command": command}
         with open(os.path.join(PROFILES, "counters_%s.json" % wl), "w") as out:
             json.dump(rec, out, indent=1)
-        lines.append("| %s | `%s` | %d | %.0f | %.0f | %.0f | %d | %.4f | %.0f | %d | %.4f |" % (
-            wl, name[:70], nf, f, w, fb, rd, fb / rd, wb, wr, wb / wr))
+        lines.append("| %s | `%s` | %d | %.0f | %.0f | %.0f | %d | %s | %.0f | %d | %.4f |" % (
+            wl, name[:70], nf, f, w, fb, rd, "%.4f" % (fb / rd) if rd else "-", wb, wr, wb / wr))
     with open(os.path.join(PROFILES, "counters_summary.md"), "w") as out:
         out.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -372,7 +383,7 @@ def main():
     }
     if a.all:
         line["commands"] = {}
-        for wl in W.CONFIGS + ["copy_f32"]:
+        for wl in W.CONFIGS + ["copy_f32", "classify_u32", "fill_f32"]:
             if wl == a.workload:
                 r = head
             else:

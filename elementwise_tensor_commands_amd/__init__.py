@@ -26,6 +26,8 @@ LIB_PATH = os.path.join(PKG, "libecmd.so")
 
 F16, F32, I32 = 1, 2, 3
 E_ADD, E_SUB, E_MUL, E_NEG, E_CVT = 1, 2, 3, 4, 5
+E_CMP = {"eq": 6, "ne": 7, "lt": 8, "le": 9, "gt": 10, "ge": 11, "ltu": 12, "leu": 13, "gtu": 14, "geu": 15}
+E_MIN, E_MAX, E_ABS, E_SELECT = 16, 17, 18, 19
 ARG_TENSOR, ARG_SCALAR = 1, 2
 PATH_NONE, PATH_LINEAR, PATH_TILED, PATH_GATHER = 0, 1, 2, 3
 PATH_NAMES = {0: "none", 1: "linear", 2: "tiled", 3: "gather"}
@@ -64,7 +66,7 @@ def _load_library():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             "libecmd.so is not built (%s); build it with "
-            "`python -m elementwise_tensor_commands_amd.build`" % LIB_PATH)
+            "`python elementwise_tensor_commands_amd/build.py`" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
     sig = {
@@ -74,6 +76,7 @@ def _load_library():
         "cmd_scalar": (ctypes.c_int, [vp, ctypes.c_int32, i32p, i32p]),
         "cmd_op": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p]),
         "cmd_store": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, i32p]),
+        "cmd_select": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p]),
         "cmd_launch": (ctypes.c_int, [vp, ctypes.POINTER(cmd_arg), ctypes.c_int32, vp]),
         "cmd_plan": (ctypes.c_int, [vp, ctypes.POINTER(cmd_arg), ctypes.c_int32, ctypes.POINTER(cmd_plan_info)]),
         "cmd_dump": (ctypes.c_int64, [vp, ctypes.c_char_p, ctypes.c_int64]),
@@ -96,6 +99,7 @@ cmd_load = lib.cmd_load
 cmd_scalar = lib.cmd_scalar
 cmd_op = lib.cmd_op
 cmd_store = lib.cmd_store
+cmd_select = lib.cmd_select
 cmd_launch = lib.cmd_launch
 cmd_plan = lib.cmd_plan
 cmd_dump = lib.cmd_dump
@@ -169,8 +173,22 @@ class Command:
     def add(self, a, b): return self.op(E_ADD, a, b)
     def sub(self, a, b): return self.op(E_SUB, a, b)
     def mul(self, a, b): return self.op(E_MUL, a, b)
+    def min(self, a, b): return self.op(E_MIN, a, b)
+    def max(self, a, b): return self.op(E_MAX, a, b)
     def neg(self, a): return self.op(E_NEG, a)
+    def abs(self, a): return self.op(E_ABS, a)
     def cvt(self, a, dtype): return self.op(E_CVT, a, -1, dtype)
+
+    def cmp(self, how: str, a, b):
+        """Comparison how in eq ne lt le gt ge (signed / IEEE) or ltu leu gtu geu
+        (int32 as unsigned): an int32 value, 1 or 0."""
+        return self.op(E_CMP[how], a, b, I32)
+
+    def select(self, cond, x, y) -> int:
+        tag = ctypes.c_int32()
+        self._check(lib.cmd_select(self._h, cond, x, y, ctypes.byref(tag)))
+        self._dtypes.append(self._dtypes[x] if 0 <= x < len(self._dtypes) else 0)
+        return tag.value
 
     def store(self, tag: int, rank: int = 1) -> int:
         arg = ctypes.c_int32()
@@ -259,8 +277,9 @@ class BoundLaunch:
 
 def from_spec(spec) -> Command:
     """Build a Command from a declarative list of ``(name, step)`` pairs, steps
-    being ("load", dtype, rank), ("scalar", dtype), ("add"|"sub"|"mul", a, b),
-    ("neg", a), ("cvt", a, dtype) or ("store", value, rank)."""
+    being ("load", dtype, rank), ("scalar", dtype), (op, a, b) for add sub mul
+    min max and the comparisons, ("neg", a), ("abs", a), ("cvt", a, dtype),
+    ("select", cond, x, y) or ("store", value, rank)."""
     c = Command()
     tags = {}
     for name, st in spec:
@@ -275,8 +294,18 @@ def from_spec(spec) -> Command:
             tags[name] = c.sub(tags[st[1]], tags[st[2]])
         elif k == "mul":
             tags[name] = c.mul(tags[st[1]], tags[st[2]])
+        elif k == "min":
+            tags[name] = c.min(tags[st[1]], tags[st[2]])
+        elif k == "max":
+            tags[name] = c.max(tags[st[1]], tags[st[2]])
+        elif k in E_CMP:
+            tags[name] = c.cmp(k, tags[st[1]], tags[st[2]])
         elif k == "neg":
             tags[name] = c.neg(tags[st[1]])
+        elif k == "abs":
+            tags[name] = c.abs(tags[st[1]])
+        elif k == "select":
+            tags[name] = c.select(tags[st[1]], tags[st[2]], tags[st[3]])
         elif k == "cvt":
             tags[name] = c.cvt(tags[st[1]], st[2])
         elif k == "store":

@@ -1,6 +1,8 @@
 """Build libecmd.so (the C ABI and its gfx950 kernels) in-tree with hipcc.
 
-    python -m elementwise_tensor_commands_amd.build [-v]
+    python elementwise_tensor_commands_amd/build.py [-v]
+
+(run it as a script: importing the package would load the library first).
 
 Every source is compiled for gfx950 only, non-relocatable device code (each
 kernel's device code lives in its own translation unit, as clang's HIP support

@@ -60,8 +60,31 @@ __device__ __forceinline__ uint32_t f2i_sat(float f)
     return (uint32_t)(int32_t)f;
 }
 
+// binary32 minimum / maximum: a NaN operand is ignored unless both are NaN;
+// -0 is below +0.  Written with comparisons and selects, not v_min/v_max, so
+// that the result does not depend on the hardware's NaN and signed-zero rules.
+__device__ __forceinline__ uint32_t fmin_bits(uint32_t a, uint32_t b)
+{
+    const float x = as_f(a), y = as_f(b);
+    if (!(x == x)) return b;
+    if (!(y == y)) return a;
+    if (x < y) return a;
+    if (y < x) return b;
+    return (a & 0x80000000u) ? a : b;
+}
+
+__device__ __forceinline__ uint32_t fmax_bits(uint32_t a, uint32_t b)
+{
+    const float x = as_f(a), y = as_f(b);
+    if (!(x == x)) return b;
+    if (!(y == y)) return a;
+    if (x > y) return a;
+    if (y > x) return b;
+    return (a & 0x80000000u) ? b : a;
+}
+
 template <int C>
-__device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b)
+__device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b, uint32_t c = 0u)
 {
     if constexpr (C == C_MOV) return a;
     else if constexpr (C == C_ADD_F32) return as_u(as_f(a) + as_f(b));
@@ -81,6 +104,30 @@ __device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b)
     // 2^24 both this and a direct rounding give infinity, so one rounding.
     else if constexpr (C == C_CVT_I32_F16) return f2h(as_u((float)(int32_t)a));
     else if constexpr (C == C_CVT_F16_I32) return f2i_sat(as_f(h2f(a)));
+    else if constexpr (C == C_EQ_F32) return as_f(a) == as_f(b) ? 1u : 0u;
+    else if constexpr (C == C_NE_F32) return as_f(a) != as_f(b) ? 1u : 0u;
+    else if constexpr (C == C_LT_F32) return as_f(a) < as_f(b) ? 1u : 0u;
+    else if constexpr (C == C_LE_F32) return as_f(a) <= as_f(b) ? 1u : 0u;
+    else if constexpr (C == C_GT_F32) return as_f(a) > as_f(b) ? 1u : 0u;
+    else if constexpr (C == C_GE_F32) return as_f(a) >= as_f(b) ? 1u : 0u;
+    else if constexpr (C == C_EQ_I32) return a == b ? 1u : 0u;
+    else if constexpr (C == C_NE_I32) return a != b ? 1u : 0u;
+    else if constexpr (C == C_LT_I32) return (int32_t)a < (int32_t)b ? 1u : 0u;
+    else if constexpr (C == C_LE_I32) return (int32_t)a <= (int32_t)b ? 1u : 0u;
+    else if constexpr (C == C_GT_I32) return (int32_t)a > (int32_t)b ? 1u : 0u;
+    else if constexpr (C == C_GE_I32) return (int32_t)a >= (int32_t)b ? 1u : 0u;
+    else if constexpr (C == C_LT_U32) return a < b ? 1u : 0u;
+    else if constexpr (C == C_LE_U32) return a <= b ? 1u : 0u;
+    else if constexpr (C == C_GT_U32) return a > b ? 1u : 0u;
+    else if constexpr (C == C_GE_U32) return a >= b ? 1u : 0u;
+    else if constexpr (C == C_MIN_F32) return fmin_bits(a, b);
+    else if constexpr (C == C_MAX_F32) return fmax_bits(a, b);
+    else if constexpr (C == C_MIN_I32) return (int32_t)a < (int32_t)b ? a : b;
+    else if constexpr (C == C_MAX_I32) return (int32_t)a > (int32_t)b ? a : b;
+    else if constexpr (C == C_ABS_F32) return a & 0x7fffffffu;
+    else if constexpr (C == C_ABS_I32) return (a & 0x80000000u) ? 0u - a : a;
+    else if constexpr (C == C_ABS_F16) return a & 0x7fffu;
+    else if constexpr (C == C_SELECT) return a != 0u ? b : c;
     else return 0u;
 }
 
@@ -145,18 +192,24 @@ __device__ __forceinline__ void rt_put(uint8_t dst, Regs<E> &R, const uint32_t (
 
 template <int E>
 __device__ __forceinline__ void rt_apply(uint8_t code, const uint32_t (&a)[E], const uint32_t (&b)[E],
-                                         uint32_t (&r)[E])
+                                         const uint32_t (&c)[E], uint32_t (&r)[E])
 {
     switch (code) {
-#define ECMD_APPLY(c)                                     \
-    case c:                                               \
-        _Pragma("unroll") for (int e = 0; e < E; ++e) r[e] = apply<c>(a[e], b[e]); \
+#define ECMD_APPLY(k)                                     \
+    case k:                                               \
+        _Pragma("unroll") for (int e = 0; e < E; ++e) r[e] = apply<k>(a[e], b[e], c[e]); \
         break;
         ECMD_APPLY(C_MOV) ECMD_APPLY(C_ADD_F32) ECMD_APPLY(C_SUB_F32) ECMD_APPLY(C_MUL_F32)
         ECMD_APPLY(C_ADD_I32) ECMD_APPLY(C_SUB_I32) ECMD_APPLY(C_MUL_I32)
         ECMD_APPLY(C_NEG_F32) ECMD_APPLY(C_NEG_I32) ECMD_APPLY(C_NEG_F16)
         ECMD_APPLY(C_CVT_F16_F32) ECMD_APPLY(C_CVT_F32_F16) ECMD_APPLY(C_CVT_I32_F32)
         ECMD_APPLY(C_CVT_F32_I32) ECMD_APPLY(C_CVT_I32_F16) ECMD_APPLY(C_CVT_F16_I32)
+        ECMD_APPLY(C_EQ_F32) ECMD_APPLY(C_NE_F32) ECMD_APPLY(C_LT_F32) ECMD_APPLY(C_LE_F32)
+        ECMD_APPLY(C_GT_F32) ECMD_APPLY(C_GE_F32) ECMD_APPLY(C_EQ_I32) ECMD_APPLY(C_NE_I32)
+        ECMD_APPLY(C_LT_I32) ECMD_APPLY(C_LE_I32) ECMD_APPLY(C_GT_I32) ECMD_APPLY(C_GE_I32)
+        ECMD_APPLY(C_LT_U32) ECMD_APPLY(C_LE_U32) ECMD_APPLY(C_GT_U32) ECMD_APPLY(C_GE_U32)
+        ECMD_APPLY(C_MIN_F32) ECMD_APPLY(C_MAX_F32) ECMD_APPLY(C_MIN_I32) ECMD_APPLY(C_MAX_I32)
+        ECMD_APPLY(C_ABS_F32) ECMD_APPLY(C_ABS_I32) ECMD_APPLY(C_ABS_F16) ECMD_APPLY(C_SELECT)
 #undef ECMD_APPLY
     default:
         _Pragma("unroll") for (int e = 0; e < E; ++e) r[e] = 0u;
@@ -178,10 +231,11 @@ struct RtEval {
         const int n_ops = P.n_ops;
         for (int i = 0; i < n_ops; ++i) {
             const TapeOp op = P.ops[i];
-            uint32_t a[E], b[E], r[E];
+            uint32_t a[E], b[E], c[E], r[E];
             rt_fetch<E>(op.a, R, uni, a);
             rt_fetch<E>(op.b, R, uni, b);
-            rt_apply<E>(op.code, a, b, r);
+            rt_fetch<E>(op.c, R, uni, c);
+            rt_apply<E>(op.code, a, b, c, r);
             rt_put<E>(op.dst, R, r);
         }
 #pragma unroll
@@ -218,7 +272,7 @@ struct CtEval {
             uint32_t r[E];
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                r[e] = apply<op.code>(get<op.a, E>(R, uni, e), get<op.b, E>(R, uni, e));
+                r[e] = apply<op.code>(get<op.a, E>(R, uni, e), get<op.b, E>(R, uni, e), get<op.c, E>(R, uni, e));
 #pragma unroll
             for (int e = 0; e < E; ++e) R.s[op.dst - kRefSlot][e] = r[e];
             step<I + 1, E>(uni, R);

@@ -33,7 +33,7 @@ namespace {
 enum NodeKind { N_LOAD = 1, N_SCALAR = 2, N_OP = 3 };
 
 struct Node {
-    int kind, dtype, op, a, b, arg;
+    int kind, dtype, op, a, b, c, arg;
 };
 
 struct ArgDecl {
@@ -112,7 +112,19 @@ const char *dtype_name(int d) { return d == CMD_F16 ? "f16" : d == CMD_F32 ? "f3
 
 int opcode_for(int op, int src, int dst)
 {
+    if (op >= E_CMP_EQ && op <= E_CMP_GE) {
+        const int k = op - E_CMP_EQ;
+        return (src == CMD_F32 ? C_EQ_F32 : C_EQ_I32) + k;
+    }
     switch (op) {
+    case E_CMP_LTU: return C_LT_U32;
+    case E_CMP_LEU: return C_LE_U32;
+    case E_CMP_GTU: return C_GT_U32;
+    case E_CMP_GEU: return C_GE_U32;
+    case E_MIN: return dst == CMD_F32 ? C_MIN_F32 : C_MIN_I32;
+    case E_MAX: return dst == CMD_F32 ? C_MAX_F32 : C_MAX_I32;
+    case E_ABS: return dst == CMD_F32 ? C_ABS_F32 : dst == CMD_I32 ? C_ABS_I32 : C_ABS_F16;
+    case E_SELECT: return C_SELECT;
     case E_ADD: return dst == CMD_F32 ? C_ADD_F32 : C_ADD_I32;
     case E_SUB: return dst == CMD_F32 ? C_SUB_F32 : C_SUB_I32;
     case E_MUL: return dst == CMD_F32 ? C_MUL_F32 : C_MUL_I32;
@@ -134,7 +146,12 @@ const char *code_name(int c)
     static const char *names[] = {"mov", "add.f32", "sub.f32", "mul.f32", "add.i32", "sub.i32",
                                   "mul.i32", "neg.f32", "neg.i32", "neg.f16", "cvt.f16.f32",
                                   "cvt.f32.f16", "cvt.i32.f32", "cvt.f32.i32", "cvt.i32.f16",
-                                  "cvt.f16.i32"};
+                                  "cvt.f16.i32", "eq.f32", "ne.f32", "lt.f32", "le.f32", "gt.f32",
+                                  "ge.f32", "eq.i32", "ne.i32", "lt.i32", "le.i32", "gt.i32",
+                                  "ge.i32", "lt.u32", "le.u32", "gt.u32", "ge.u32", "min.f32",
+                                  "max.f32", "min.i32", "max.i32", "abs.f32", "abs.i32", "abs.f16",
+                                  "select"};
+    static_assert(sizeof(names) / sizeof(names[0]) == C_COUNT, "one name per code");
     return c >= 0 && c < C_COUNT ? names[c] : "?";
 }
 
@@ -158,6 +175,7 @@ int lower(cmd_t h)
         if (!live[t] || h->nodes[t].kind != N_OP) continue;
         live[h->nodes[t].a] = 1;
         if (h->nodes[t].b >= 0) live[h->nodes[t].b] = 1;
+        if (h->nodes[t].c >= 0) live[h->nodes[t].c] = 1;
     }
     // 2. A conversion to the same dtype is the value itself.
     std::vector<int> alias(n), code(n, -1);
@@ -189,6 +207,7 @@ int lower(cmd_t h)
         } else if (code[t] != C_MOV) {
             last_use[alias[nd.a]] = n_ops;
             if (nd.b >= 0) last_use[alias[nd.b]] = n_ops;
+            if (nd.c >= 0) last_use[alias[nd.c]] = n_ops;
             ++n_ops;
         }
     }
@@ -202,9 +221,10 @@ int lower(cmd_t h)
     for (int t = 0; t < n; ++t) {
         if (!live[t] || h->nodes[t].kind != N_OP || code[t] == C_MOV) continue;
         const Node &nd = h->nodes[t];
-        const int a = alias[nd.a], b = nd.b >= 0 ? alias[nd.b] : -1;
+        const int a = alias[nd.a], b = nd.b >= 0 ? alias[nd.b] : -1, cc = nd.c >= 0 ? alias[nd.c] : -1;
         int ra = ref[a], rb = b >= 0 ? ref[b] : kRefNone;
-        for (int v : {a, b})
+        const int rc = cc >= 0 ? ref[cc] : kRefNone;
+        for (int v : {a, b, cc})
             if (v >= 0 && ref[v] >= kRefSlot && ref[v] < kRefUni && last_use[v] <= i)
                 busy[ref[v] - kRefSlot] = false;
         int slot = -1;
@@ -216,15 +236,19 @@ int lower(cmd_t h)
         ref[t] = kRefSlot + slot;
         // Commutative operations list the smaller reference first so that one
         // Command written either way lowers to the same Program (x+y and y+x,
-        // x*y and y*x are equal bit for bit in IEEE and two's-complement
-        // arithmetic; only NaN payloads, which carry no meaning here, may differ).
+        // x*y and y*x, min, max, == and != are equal bit for bit both ways in
+        // IEEE and two's-complement arithmetic; only NaN payloads, which carry
+        // no meaning here, may differ).
         const int c = code[t];
-        if ((c == C_ADD_F32 || c == C_MUL_F32 || c == C_ADD_I32 || c == C_MUL_I32) && rb < ra)
-            std::swap(ra, rb);
+        const bool commutes = c == C_ADD_F32 || c == C_MUL_F32 || c == C_ADD_I32 || c == C_MUL_I32 ||
+                              c == C_EQ_F32 || c == C_NE_F32 || c == C_EQ_I32 || c == C_NE_I32 ||
+                              c == C_MIN_F32 || c == C_MAX_F32 || c == C_MIN_I32 || c == C_MAX_I32;
+        if (commutes && rb < ra) std::swap(ra, rb);
         P.ops[i].code = (uint8_t)c;
         P.ops[i].dst = (uint8_t)ref[t];
         P.ops[i].a = (uint8_t)ra;
         P.ops[i].b = (uint8_t)rb;
+        P.ops[i].c = (uint8_t)rc;
         ++i;
     }
     P.n_ops = (uint8_t)i;
@@ -617,7 +641,7 @@ int cmd_load(cmd_t h, int32_t dtype, int32_t rank, cmd_tag *tag, int32_t *arg_in
     if ((int)h->args.size() >= CMD_MAX_ARGS)
         return fail(h, CMD_E_LIMIT, "more than %d CommandArguments", CMD_MAX_ARGS);
     const int arg = (int)h->args.size();
-    int rc = add_node(h, Node{N_LOAD, dtype, 0, -1, -1, arg}, tag);
+    int rc = add_node(h, Node{N_LOAD, dtype, 0, -1, -1, -1, arg}, tag);
     if (rc) return rc;
     h->args.push_back(ArgDecl{CMD_ARG_TENSOR, dtype, rank, false, (int)h->nodes.size() - 1});
     if (arg_index) *arg_index = arg;
@@ -632,7 +656,7 @@ int cmd_scalar(cmd_t h, int32_t dtype, cmd_tag *tag, int32_t *arg_index)
     if ((int)h->args.size() >= CMD_MAX_ARGS)
         return fail(h, CMD_E_LIMIT, "more than %d CommandArguments", CMD_MAX_ARGS);
     const int arg = (int)h->args.size();
-    int rc = add_node(h, Node{N_SCALAR, dtype, 0, -1, -1, arg}, tag);
+    int rc = add_node(h, Node{N_SCALAR, dtype, 0, -1, -1, -1, arg}, tag);
     if (rc) return rc;
     h->args.push_back(ArgDecl{CMD_ARG_SCALAR, dtype, 0, false, (int)h->nodes.size() - 1});
     if (arg_index) *arg_index = arg;
@@ -644,14 +668,15 @@ int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, 
     if (!h) return CMD_E_ARG;
     if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
     const int n = (int)h->nodes.size();
-    if (opcode < E_ADD || opcode > E_CVT) return fail(h, CMD_E_ARG, "unknown opcode %d", opcode);
+    if (opcode < E_ADD || opcode > E_ABS) return fail(h, CMD_E_ARG, "unknown opcode %d (select: cmd_select)", opcode);
     if (!valid_dtype(result_dtype)) return fail(h, CMD_E_DTYPE, "unknown dtype %d", result_dtype);
     if (a < 0 || a >= n) return fail(h, CMD_E_TAG, "tag %d does not name an earlier value", a);
     const int da = h->nodes[a].dtype;
-    if (opcode == E_NEG || opcode == E_CVT) {
+    if (opcode == E_NEG || opcode == E_ABS || opcode == E_CVT) {
         if (b != -1) return fail(h, CMD_E_ARG, "unary operation takes b = -1");
-        if (opcode == E_NEG && result_dtype != da)
-            return fail(h, CMD_E_DTYPE, "neg of %s cannot give %s", dtype_name(da), dtype_name(result_dtype));
+        if (opcode != E_CVT && result_dtype != da)
+            return fail(h, CMD_E_DTYPE, "%s of %s cannot give %s", opcode == E_NEG ? "neg" : "abs", dtype_name(da),
+                        dtype_name(result_dtype));
     } else {
         if (b < 0 || b >= n) return fail(h, CMD_E_TAG, "tag %d does not name an earlier value", b);
         const int db = h->nodes[b].dtype;
@@ -659,11 +684,29 @@ int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, 
             return fail(h, CMD_E_DTYPE, "operands are %s and %s", dtype_name(da), dtype_name(db));
         if (da == CMD_F16)
             return fail(h, CMD_E_DTYPE, "binary16 is a storage type: convert to f32 first");
-        if (result_dtype != da)
-            return fail(h, CMD_E_DTYPE, "result %s differs from operands %s", dtype_name(result_dtype),
-                        dtype_name(da));
+        const bool cmp = opcode >= E_CMP_EQ && opcode <= E_CMP_GEU;
+        if (opcode >= E_CMP_LTU && opcode <= E_CMP_GEU && da != CMD_I32)
+            return fail(h, CMD_E_DTYPE, "unsigned comparisons take int32 operands");
+        const int want = cmp ? CMD_I32 : da;
+        if (result_dtype != want)
+            return fail(h, CMD_E_DTYPE, "result %s, expected %s", dtype_name(result_dtype), dtype_name(want));
     }
-    return add_node(h, Node{N_OP, result_dtype, opcode, a, b, -1}, tag);
+    return add_node(h, Node{N_OP, result_dtype, opcode, a, b, -1, -1}, tag);
+}
+
+int cmd_select(cmd_t h, cmd_tag cond, cmd_tag x, cmd_tag y, cmd_tag *tag)
+{
+    if (!h) return CMD_E_ARG;
+    if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
+    const int n = (int)h->nodes.size();
+    for (cmd_tag t : {cond, x, y})
+        if (t < 0 || t >= n) return fail(h, CMD_E_TAG, "tag %d does not name an earlier value", t);
+    if (h->nodes[cond].dtype != CMD_I32)
+        return fail(h, CMD_E_DTYPE, "select condition is %s, not i32", dtype_name(h->nodes[cond].dtype));
+    if (h->nodes[x].dtype != h->nodes[y].dtype)
+        return fail(h, CMD_E_DTYPE, "select values are %s and %s", dtype_name(h->nodes[x].dtype),
+                    dtype_name(h->nodes[y].dtype));
+    return add_node(h, Node{N_OP, h->nodes[x].dtype, E_SELECT, cond, x, y, -1}, tag);
 }
 
 int cmd_store(cmd_t h, cmd_tag value, int32_t rank, int32_t *arg_index)
@@ -792,9 +835,12 @@ int64_t cmd_dump(cmd_t h, char *buf, int64_t cap)
         if (o.b == kRefNone)
             std::snprintf(line, sizeof line, "%s = %s %s\n", refname(o.dst).c_str(), code_name(o.code),
                           refname(o.a).c_str());
-        else
+        else if (o.c == kRefNone)
             std::snprintf(line, sizeof line, "%s = %s %s, %s\n", refname(o.dst).c_str(), code_name(o.code),
                           refname(o.a).c_str(), refname(o.b).c_str());
+        else
+            std::snprintf(line, sizeof line, "%s = %s %s, %s, %s\n", refname(o.dst).c_str(), code_name(o.code),
+                          refname(o.a).c_str(), refname(o.b).c_str(), refname(o.c).c_str());
         s += line;
     }
     for (int k = 0; k < P.n_out; ++k) {

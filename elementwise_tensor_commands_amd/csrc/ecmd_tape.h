@@ -9,7 +9,7 @@
 // scalar unit and branches on them uniformly (rocRoller "Design Overview",
 // section "Loading Arguments": arguments are loaded into registers once).
 //
-// Operand references (one byte):
+// Operand references (one byte; an operation has up to three, a b c):
 //   kRefIn  + k  (0..7)   input k: the k-th live tensor load, held in registers
 //   kRefSlot + k (8..15)  temporary slot k
 //   kRefUni + k  (16..23) uniform value k: the k-th live scalar argument
@@ -52,17 +52,38 @@ enum Code : uint8_t {
     C_CVT_F32_I32,
     C_CVT_I32_F16,
     C_CVT_F16_I32,
+    C_EQ_F32,      // comparisons: int32 1 / 0
+    C_NE_F32,
+    C_LT_F32,
+    C_LE_F32,
+    C_GT_F32,
+    C_GE_F32,
+    C_EQ_I32,
+    C_NE_I32,
+    C_LT_I32,
+    C_LE_I32,
+    C_GT_I32,
+    C_GE_I32,
+    C_LT_U32,
+    C_LE_U32,
+    C_GT_U32,
+    C_GE_U32,
+    C_MIN_F32,
+    C_MAX_F32,
+    C_MIN_I32,
+    C_MAX_I32,
+    C_ABS_F32,
+    C_ABS_I32,
+    C_ABS_F16,
+    C_SELECT,      // a != 0 ? b : c
     C_COUNT
 };
 
-constexpr bool code_is_binary(uint8_t c)
-{
-    return c == C_ADD_F32 || c == C_SUB_F32 || c == C_MUL_F32 || c == C_ADD_I32 ||
-           c == C_SUB_I32 || c == C_MUL_I32;
-}
-
+// Operands a, b, c: b is kRefNone for unary operations and c for every
+// operation except C_SELECT.
 struct TapeOp {
     uint8_t code, dst, a, b;
+    uint8_t c = kRefNone;
 };
 
 // The lowered Command.  Unused entries are zero so that two Programs can be
@@ -164,6 +185,14 @@ constexpr Program kProgScaleF32 = {
     1, 1, 1, 1, {TY_F32}, {TY_F32}, {ECMD_R_S(0)},
     {{C_MUL_F32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_U(0)}}};
 
+// out = (x >u t) ? 1 : 0  (int32 compared as unsigned against a scalar threshold)
+constexpr Program kProgClassifyU32 = {
+    1, 1, 1, 1, {TY_I32}, {TY_I32}, {ECMD_R_S(0)},
+    {{C_GT_U32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_U(0)}}};
+
+// out = s  (fill with a scalar; binary32 or int32 bits alike)
+constexpr Program kProgFillF32 = {0, 1, 0, 1, {}, {TY_F32}, {ECMD_R_U(0)}, {}};
+
 // out = f16(x), out = f32(x)
 constexpr Program kProgCvtF32F16 = {
     1, 0, 1, 1, {TY_F32}, {TY_F16}, {ECMD_R_S(0)},
@@ -187,7 +216,9 @@ namespace ecmd {
     X(copy_f32, kProgCopyF32)             \
     X(scale_f32, kProgScaleF32)           \
     X(cvt_f32_f16, kProgCvtF32F16)        \
-    X(cvt_f16_f32, kProgCvtF16F32)
+    X(cvt_f16_f32, kProgCvtF16F32)        \
+    X(classify_u32, kProgClassifyU32)     \
+    X(fill_f32, kProgFillF32)
 
 #define ECMD_TILED_SPECIALISED(X)         \
     X(add_scaled_f32, kProgAddScaledF32)

@@ -93,8 +93,10 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
     const bool full = (r0 + TM <= A.rows) && (c0 + TN <= A.cols);
     const int t = threadIdx.x;
 
-    // Direct inputs of every chunk, loaded up front in the specialised kernels.
-    Regs<4> R[kP];
+    // Direct inputs of every chunk, loaded up front in the specialised kernels
+    // (the interpreter keeps one chunk's registers at a time).
+    constexpr int kRegSets = kPrefetch ? kP : 1;
+    Regs<4> R[kRegSets];
     int count[kP];
 #pragma unroll
     for (int p = 0; p < kP; ++p) {
@@ -105,12 +107,13 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
     auto load_direct = [&](int p) {
         const int v = t + TB * p;
         const int64_t r = r0 + v / kRowVec, c = c0 + 4 * (v % kRowVec);
+        Regs<4> &Rp = R[kPrefetch ? p : 0];
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
             if (k < EV::n_in(A.prog) && !staged<MASK>(A, k)) {
                 const int64_t off = r * A.in_s0[k] + c;
-                if (full) load_group<4, true, NT>(A.in[k], EV::in_ty(A.prog, k), off, 4, R[p].in[k]);
-                else if (count[p] > 0) load_elems<4, false>(A.in[k], EV::in_ty(A.prog, k), off, count[p], R[p].in[k]);
+                if (full) load_group<4, true, NT>(A.in[k], EV::in_ty(A.prog, k), off, 4, Rp.in[k]);
+                else if (count[p] > 0) load_elems<4, false>(A.in[k], EV::in_ty(A.prog, k), off, count[p], Rp.in[k]);
             }
         }
     };
@@ -157,16 +160,17 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
         const int rl = v / kRowVec, cl = 4 * (v % kRowVec);
         const int64_t r = r0 + rl, c = c0 + cl;
         if constexpr (!kPrefetch) load_direct(p);
+        Regs<4> &Rp = R[kPrefetch ? p : 0];
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
             if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
                 const uint32_t *src = lds + stage_pos<MASK>(A, k) * kWords;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) R[p].in[k][e] = src[(cl + e) * kPitch + rl];
+                for (int e = 0; e < 4; ++e) Rp.in[k][e] = src[(cl + e) * kPitch + rl];
             }
         }
         uint32_t out[kMaxOut][4];
-        EV::template run<4>(A.prog, A.uni, R[p], out);
+        EV::template run<4>(A.prog, A.uni, Rp, out);
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < EV::n_out(A.prog)) {

@@ -14,8 +14,10 @@
  *     pointers with sizes and strides, or scalar bit patterns -- are supplied
  *     at launch, all together and in that order.
  *   - The T_Execute part is a set of E_ operations applied element by element:
- *     E_ADD, E_SUB, E_MUL (binary, both operands of the result dtype), E_NEG
- *     (unary, same dtype) and E_CVT (unary, to the given dtype).
+ *     E_ADD, E_SUB, E_MUL, E_MIN, E_MAX (binary, both operands of the result
+ *     dtype), the comparisons E_CMP_* (binary, int32 result), E_NEG and E_ABS
+ *     (unary, same dtype), E_CVT (unary, to the given dtype) and the ternary
+ *     select.
  *
  * Arithmetic (the same rules the test oracle implements):
  *   CMD_I32  two's-complement, every operation modulo 2^32; E_NEG(INT_MIN) = INT_MIN.
@@ -23,12 +25,19 @@
  *            own (no fused multiply-add), subnormals kept (the default FP32 denorm
  *            mode 3 of the AMDHSA kernel descriptor, Silk "AMDGPU Backend",
  *            section "Code Object Format").  E_NEG flips the sign bit.
- *   CMD_F16  storage type: load, store, E_NEG (sign flip) and E_CVT only.
+ *   CMD_F16  storage type: load, store, E_NEG, E_ABS, select and E_CVT only.
  *   E_CVT    f16->f32 exact; f32->f16 and i32->f16 round to nearest even with
  *            overflow to infinity and gradual underflow; i32->f32 rounds to
  *            nearest even; f32->i32 and f16->i32 truncate toward zero, saturate,
  *            and map NaN to 0.  A conversion to the same dtype is a copy.
- *   Scalars broadcast to every element.
+ *   E_CMP_*  CMD_F32 or CMD_I32 operands of one dtype (the unsigned forms: CMD_I32),
+ *            CMD_I32 result 1 or 0; binary32 comparisons are false when an
+ *            operand is NaN, except E_CMP_NE, and -0 equals +0.
+ *   E_MIN / E_MAX  CMD_I32 signed; CMD_F32 ignores a NaN operand unless both are
+ *            NaN and orders -0 below +0 (IEEE 754-2019 minimumNumber/maximumNumber).
+ *   E_ABS    clears the sign bit (any dtype); for CMD_I32 |INT_MIN| = INT_MIN.
+ *   Select   cond != 0 ? x : y, cond CMD_I32, x and y of one dtype (cmd_select).
+ *   Scalars broadcast to every element; a store of a scalar fills the output.
  *
  * Shapes and views: every tensor argument of one launch has the same logical
  * shape -- rank 1 (n) or rank 2 (rows, cols); a rank-1 view counts as (1, n).
@@ -76,6 +85,23 @@ typedef int32_t cmd_tag;
 #define E_MUL 3
 #define E_NEG 4
 #define E_CVT 5
+/* Comparisons: int32 result 1 (true) or 0 (false).  EQ..GE compare int32 as
+ * signed and binary32 as IEEE values; LTU..GEU compare int32 bit patterns as
+ * unsigned. */
+#define E_CMP_EQ 6
+#define E_CMP_NE 7
+#define E_CMP_LT 8
+#define E_CMP_LE 9
+#define E_CMP_GT 10
+#define E_CMP_GE 11
+#define E_CMP_LTU 12
+#define E_CMP_LEU 13
+#define E_CMP_GTU 14
+#define E_CMP_GEU 15
+#define E_MIN 16
+#define E_MAX 17
+#define E_ABS 18
+#define E_SELECT 19   /* ternary: only through cmd_select */
 
 /* CommandArgument kinds. */
 #define CMD_ARG_TENSOR 1
@@ -145,10 +171,17 @@ int cmd_scalar(cmd_t h, int32_t dtype, cmd_tag *tag, int32_t *arg_index);
 
 /* Append an E_ operation (rocRoller "Design Overview", section "Operations":
  * T_Execute holds E_ operations on vectors or scalars).  a and b are earlier
- * tags; b must be -1 for E_NEG and E_CVT.  result_dtype must equal the
- * operands' dtype except for E_CVT, where it is the target dtype.  E_ADD, E_SUB
- * and E_MUL accept CMD_F32 and CMD_I32 operands of one dtype. */
+ * tags; b must be -1 for E_NEG, E_ABS and E_CVT.  result_dtype must equal the
+ * operands' dtype except for E_CVT (the target dtype) and the comparisons
+ * (CMD_I32).  E_ADD, E_SUB, E_MUL, E_MIN, E_MAX and E_CMP_EQ..GE accept CMD_F32
+ * and CMD_I32 operands of one dtype; E_CMP_LTU..GEU CMD_I32 only.  E_SELECT
+ * is refused here (it has three operands: use cmd_select). */
 int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, cmd_tag *tag);
+
+/* Append a select: cond != 0 ? x : y, per element (a ternary E_ operation of
+ * the same T_Execute family).  cond must be CMD_I32; x and y must share a dtype,
+ * which is the result's. */
+int cmd_select(cmd_t h, cmd_tag cond, cmd_tag x, cmd_tag y, cmd_tag *tag);
 
 /* Append a store of value's tag to an output tensor of rank 1 or 2; the
  * output's dtype is the value's dtype (rocRoller "Design Overview", section

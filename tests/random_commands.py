@@ -16,9 +16,37 @@ def _random_spec(rng, n_in, n_ops, rank):
         names.append("s%d" % i)
     for i in range(n_ops):
         a = names[rng.integers(len(names))]
-        kind = rng.choice(["add", "sub", "mul", "neg", "cvt", "cvt"])
+        kind = rng.choice(["add", "sub", "mul", "neg", "cvt", "cvt", "min", "max", "abs", "cmp", "select"])
         nm = "t%d" % i
-        if kind in ("add", "sub", "mul"):
+        if kind == "cmp":
+            if dts[a] == "f16":
+                kind = "cvt"
+            else:
+                same = [x for x in names if dts[x] == dts[a]]
+                b = same[rng.integers(len(same))]
+                how = rng.choice(["eq", "ne", "lt", "le", "gt", "ge"] + (["ltu", "leu", "gtu", "geu"] if dts[a] == "i32" else []))
+                spec.append((nm, (how, a, b)))
+                dts[nm] = "i32"
+                names.append(nm)
+                continue
+        if kind == "select":
+            conds = [x for x in names if dts[x] == "i32"]
+            if conds:
+                cnd = conds[rng.integers(len(conds))]
+                same = [x for x in names if dts[x] == dts[a]]
+                b = same[rng.integers(len(same))]
+                spec.append((nm, ("select", cnd, a, b)))
+                dts[nm] = dts[a]
+                names.append(nm)
+                continue
+            kind = "neg"
+        if kind == "abs":
+            kind = "neg" if rng.random() < 0.3 else "abs"
+            spec.append((nm, (kind, a)))
+            dts[nm] = dts[a]
+            names.append(nm)
+            continue
+        if kind in ("add", "sub", "mul", "min", "max"):
             if dts[a] == "f16":
                 spec.append((nm, ("cvt", a, "f32")))
                 dts[nm] = "f32"

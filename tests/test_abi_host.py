@@ -58,7 +58,16 @@ def test_build_errors():
     _err(lambda: c.add(h, h), "CMD_E_DTYPE")
     _err(lambda: c.op(E.E_NEG, x, -1, "i32"), "CMD_E_DTYPE")
     _err(lambda: c.op(E.E_NEG, x, x), "CMD_E_ARG")
-    _err(lambda: c.op(9, x, x), "CMD_E_ARG")
+    _err(lambda: c.op(99, x, x), "CMD_E_ARG")
+    _err(lambda: c.op(E.E_SELECT, x, x), "CMD_E_ARG")                # ternary: cmd_select only
+    _err(lambda: c.op(E.E_CMP["lt"], x, x, "f32"), "CMD_E_DTYPE")    # comparisons give int32
+    _err(lambda: c.cmp("ltu", x, x), "CMD_E_DTYPE")                  # unsigned needs int32
+    _err(lambda: c.cmp("lt", h, h), "CMD_E_DTYPE")                   # no binary16 comparisons
+    _err(lambda: c.min(x, i), "CMD_E_DTYPE")
+    _err(lambda: c.select(x, x, x), "CMD_E_DTYPE")                   # condition must be int32
+    _err(lambda: c.select(i, x, h), "CMD_E_DTYPE")                   # values of one dtype
+    _err(lambda: c.select(i, x, 77), "CMD_E_TAG")
+    assert c.cmp("gtu", i, i) >= 0 and c.select(i, h, h) >= 0 and c.abs(h) >= 0 and c.max(x, x) >= 0
     _err(lambda: c.load(7), "CMD_E_DTYPE")
     _err(lambda: c.load("f32", 3), "CMD_E_LIMIT")
     _err(lambda: c.store(99), "CMD_E_TAG")
@@ -189,6 +198,31 @@ def test_shared_subexpression_evaluated_once():
     assert len(ops) == 9
 
 
+def test_select_and_compare_lowering():
+    """A select's three operands stay alive until it runs; comparisons and
+    min/max list the smaller reference first when they commute."""
+    c = E.Command()
+    x = c.load("f32")
+    y = c.load("f32")
+    lt = c.cmp("lt", y, x)
+    eq = c.cmp("eq", y, x)
+    m = c.min(y, x)
+    s = c.select(lt, m, c.neg(x))
+    c.store(s)
+    c.store(eq)
+    d = c.dump()
+    assert "lt.f32 in1, in0" in d and "eq.f32 in0, in1" in d and "min.f32 in0, in1" in d
+    assert re.search(r"s\d = select s\d, s\d, s\d", d), d
+
+
+def test_fill_plan():
+    c = E.Command()
+    v = c.scalar("f32")
+    c.store(v)
+    p = c.plan(2.5, _t(1000))
+    assert p["path"] == "linear" and p["kernel"] == "linear_fill_f32"
+
+
 def test_dead_code_is_dropped():
     c = E.Command()
     x = c.load("f32")
@@ -283,11 +317,12 @@ def _emulate(listing, ins, uni, n):
     for k, v in enumerate(uni):
         regs["u%d" % k] = np.full(n, v)
     for line in listing.splitlines():
-        m = re.match(r"(s\d+) = (\S+) (\S+?)(?:, (\S+))?$", line)
+        m = re.match(r"(s\d+) = (\S+) (\S+?)(?:, (\S+?))?(?:, (\S+))?$", line)
         if m:
-            dst, op, a, b = m.groups()
+            dst, op, a, b, c = m.groups()
             A = regs[a]
             B = regs[b] if b else None
+            C = regs[c] if c else None
             with np.errstate(all="ignore"):
                 if op in ("add.f32", "add.i32"): r = A + B
                 elif op in ("sub.f32", "sub.i32"): r = A - B
@@ -299,6 +334,20 @@ def _emulate(listing, ins, uni, n):
                 elif op == "cvt.f32.i32": r = f2i(A)
                 elif op == "cvt.i32.f16": r = A.astype(np.float64).astype(f16)
                 elif op == "cvt.f16.i32": r = f2i(A.astype(np.float32))
+                elif op.split(".")[0] in ("eq", "ne", "lt", "le", "gt", "ge"):
+                    X, Y = (A.view(np.uint32), B.view(np.uint32)) if op.endswith(".u32") else (A, B)
+                    r = getattr(np, {"eq": "equal", "ne": "not_equal", "lt": "less", "le": "less_equal",
+                                     "gt": "greater", "ge": "greater_equal"}[op.split(".")[0]])(X, Y).astype(np.int32)
+                elif op in ("min.i32", "max.i32"): r = (np.minimum if op == "min.i32" else np.maximum)(A, B)
+                elif op in ("min.f32", "max.f32"):
+                    r = (np.fmin if op == "min.f32" else np.fmax)(A, B)
+                    z = (A == 0) & (B == 0)                      # order -0 below +0 on ties
+                    neg = np.signbit(A) | np.signbit(B) if op == "min.f32" else np.signbit(A) & np.signbit(B)
+                    r = np.where(z, np.where(neg, np.float32(-0.0), np.float32(0.0)), r)
+                elif op.startswith("abs"):
+                    r = (A.view(np.uint32) & 0x7FFFFFFF).view(A.dtype) if op == "abs.f32" else \
+                        ((A.view(np.uint16) & 0x7FFF).view(A.dtype) if op == "abs.f16" else np.abs(A))
+                elif op == "select": r = np.where(A != 0, B, C)
                 else: raise AssertionError(op)
             regs[dst] = r
             continue

@@ -36,10 +36,13 @@ def _gpu_values(wl, vals, extra, n):
 def _check_workload(wl, n, generic=False):
     spec = W.WORKLOADS[wl]["spec"]
     vals, extra = W.make_inputs(wl, n)
-    ref = run_oracle(spec, vals)
-    gv = _gpu_values(wl, vals, extra, n)
     _, outs = arg_dtypes(spec)
     shape = (n, n) if wl == "transposed_2d" else (n,)
+    if any(isinstance(v, np.ndarray) for v in vals):
+        ref = run_oracle(spec, vals)
+    else:                                  # no tensor input: the outputs give the shape
+        ref = run_oracle(spec, vals, outputs=[np.zeros(shape, NPD[d]) for d in outs])
+    gv = _gpu_values(wl, vals, extra, n)
     old = os.environ.get("ECMD_FORCE_GENERIC")
     if generic:
         os.environ["ECMD_FORCE_GENERIC"] = "1"
@@ -179,6 +182,34 @@ def test_full_size(wl):
     print("  full size %s n=%d" % (wl, n), flush=True)
     plan = _check_workload(wl, n)
     assert plan["specialised"]
+
+
+@pytest.mark.parametrize("wl", ["classify_u32", "fill_f32"])
+@pytest.mark.parametrize("n", [1, 1027, (1 << 20) + 5, 1 << 28])
+def test_widened_workloads(wl, n):
+    """The compare and fill Commands, from a few elements to full size."""
+    if n == 1 << 28:
+        print("  full size %s" % wl, flush=True)
+    plan = _check_workload(wl, n)
+    assert plan["specialised"]
+
+
+@pytest.mark.parametrize("dt", ["f32", "i32", "f16"])
+def test_fill_generic_and_2d(dt):
+    """Fills that the specialised kernel does not cover: int32 and binary16
+    values (interpreter), and a rank-2 strided output (gather)."""
+    import elementwise_tensor_commands_amd as ecmd
+    val = {"f32": -0.0, "i32": -7, "f16": 65504.0}[dt]
+    c = ecmd.Command()
+    s_ = c.scalar(dt)
+    c.store(s_, 2)
+    out = torch.zeros((33, 70), dtype=TD[dt], device=dev())
+    view = out[:, 3:67]
+    c.launch(val, view)
+    torch.cuda.synchronize()
+    ref = np.zeros((33, 70), NPD[dt])
+    ref[:, 3:67] = np.array(val, dtype=NPD[dt])
+    compare(out.cpu().numpy(), ref, 0, "fill %s" % dt)
 
 
 # ---------------------------------------------------------------------------
@@ -373,7 +404,7 @@ def test_gather_views():
 # ---------------------------------------------------------------------------
 # Random Commands (generic interpreter coverage).
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_commands(seed):
     rng = np.random.default_rng(seed)
     rank = 2 if seed % 3 == 0 else 1

@@ -83,6 +83,21 @@ COPY_F32 = [
     ("out", ("store", "x", 1)),
 ]
 
+# The threshold classifier of the Silk AMDGPU page's example kernels: an
+# unsigned comparison of every element against a scalar threshold.
+CLASSIFY_U32 = [
+    ("x", ("load", "i32", 1)),
+    ("t", ("scalar", "i32")),
+    ("r", ("gtu", "x", "t")),
+    ("out", ("store", "r", 1)),
+]
+
+# A fill: one scalar stored to every element.
+FILL_F32 = [
+    ("s", ("scalar", "f32")),
+    ("out", ("store", "s", 1)),
+]
+
 WORKLOADS = {
     "add_f32": dict(index=0, spec=ADD_F32, n=65536,
                     label="z = x + y, fp32, n=65536 contiguous"),
@@ -98,6 +113,10 @@ WORKLOADS = {
     # bandwidth reference and the calibration kernel for the HBM counters.
     "copy_f32": dict(index=5, spec=COPY_F32, n=1 << 28,
                      label="out = x, fp32, n=2^28 (plain copy reference)"),
+    # Further Commands of the widened op set (compare/select, fill).
+    "classify_u32": dict(index=6, spec=CLASSIFY_U32, n=1 << 28,
+                         label="out = (x >u t) ? 1 : 0, int32 x uniform over all 2^32 patterns, t = 2^31, n=2^28"),
+    "fill_f32": dict(index=7, spec=FILL_F32, n=1 << 28, label="out = s, fp32, s = 1.25, n=2^28"),
 }
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
@@ -106,6 +125,8 @@ SCALARS = {
     "axpby_f32": {"alpha": np.float32(1.5), "beta": np.float32(-0.25)},
     "mixed_two_out": {"s": np.float32(0.5)},
     "transposed_2d": {"alpha": np.float32(2.0)},
+    "classify_u32": {"t": np.int32(-2**31)},          # 0x80000000 as unsigned
+    "fill_f32": {"s": np.float32(1.25)},
 }
 
 
@@ -161,6 +182,10 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
         vals.append(sc["s"])
     elif workload == "copy_f32":
         vals = [_uniform_pm1_f32(rng, n)]
+    elif workload == "classify_u32":
+        vals = [rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32).view(np.int32), sc["t"]]
+    elif workload == "fill_f32":
+        vals = [sc["s"]]
     elif workload == "transposed_2d":
         rows = cols = n
         xs = np.full((rows, cols + row_pad), np.nan, dtype=np.float32)
@@ -188,8 +213,12 @@ def algorithmic_bytes(workload: str, n: int | None = None) -> int:
             per += size[st[1]]
         elif st[0] == "scalar":
             dt[name] = st[1]
-        elif st[0] in ("add", "sub", "mul", "neg"):
+        elif st[0] in ("add", "sub", "mul", "neg", "abs", "min", "max"):
             dt[name] = dt[st[1]]
+        elif st[0] in ("eq", "ne", "lt", "le", "gt", "ge", "ltu", "leu", "gtu", "geu"):
+            dt[name] = "i32"
+        elif st[0] == "select":
+            dt[name] = dt[st[2]]
         elif st[0] == "cvt":
             dt[name] = st[2]
         elif st[0] == "store":
