@@ -14,12 +14,13 @@
  * combine earlier tags, and stores write a tag's value to an output tensor.
  * Argument values (pointers, strides, scalar bits) arrive at execution time.
  *
- * For every logical index p = (r, c) of the common shape, in row-major order,
- * the oracle walks the operations in insertion order, keeps one value per tag
- * (so a shared subexpression is computed once per element), and then performs
- * every store.  A tensor view maps (r, c) to element offset r*s0 + c*s1
- * (rocRoller "Design Overview", section "Kernel Graph": a dimension has a size
- * and a stride; Flatten gives the row-major contiguous index).
+ * For every logical index p = (i0, i1, i2, i3) of the common shape, in
+ * row-major order, the oracle walks the operations in insertion order, keeps
+ * one value per tag (so a shared subexpression is computed once per element),
+ * and then performs every store.  A tensor view maps p to element offset
+ * i0*s0 + i1*s1 + i2*s2 + i3*s3 (rocRoller "Design Overview", section "Kernel
+ * Graph": a dimension has a size and a stride; Flatten gives the row-major
+ * contiguous index).
  *
  * Arithmetic rules (readings written out in the design notes):
  *   int32 : two's-complement, every op modulo 2^32 (done in uint32_t).
@@ -88,11 +89,13 @@ typedef struct {
     int32_t tag, arg;
 } oracle_store;
 
-/* One CommandArgument value.  Tensors: base pointer and element strides of the
- * 2-D view (a 1-D view is rows = 1 with stride[0] unused).  Scalars: bits. */
+/* One CommandArgument value.  Tensors: base pointer and element strides of
+ * the view over the 4-D logical shape (a view of rank k < 4 has its sizes
+ * right-aligned: strides of the missing leading dimensions are 0).
+ * Scalars: bits. */
 typedef struct {
     void *ptr;
-    int64_t stride[2];
+    int64_t stride[4];
     uint32_t bits;
     int32_t dtype;
 } oracle_arg;
@@ -308,9 +311,14 @@ static uint32_t apply_op(int op, int dst_dtype, int src_dtype, uint32_t a, uint3
 /* ------------------------------------------------------------------------ */
 /* Element loop.                                                             */
 
-static uint32_t read_elem(const oracle_arg *g, int64_t r, int64_t c)
+static int64_t offset_of(const oracle_arg *g, const int64_t idx[4])
 {
-    int64_t off = r * g->stride[0] + c * g->stride[1];
+    return idx[0] * g->stride[0] + idx[1] * g->stride[1] + idx[2] * g->stride[2] + idx[3] * g->stride[3];
+}
+
+static uint32_t read_elem(const oracle_arg *g, const int64_t idx[4])
+{
+    int64_t off = offset_of(g, idx);
     if (g->dtype == OR_F16) {
         uint16_t h;
         memcpy(&h, (const char *)g->ptr + off * 2, 2);
@@ -321,9 +329,9 @@ static uint32_t read_elem(const oracle_arg *g, int64_t r, int64_t c)
     return u;
 }
 
-static void write_elem(const oracle_arg *g, int64_t r, int64_t c, uint32_t v)
+static void write_elem(const oracle_arg *g, const int64_t idx[4], uint32_t v)
 {
-    int64_t off = r * g->stride[0] + c * g->stride[1];
+    int64_t off = offset_of(g, idx);
     if (g->dtype == OR_F16) {
         uint16_t h = (uint16_t)v;
         memcpy((char *)g->ptr + off * 2, &h, 2);
@@ -338,7 +346,7 @@ typedef struct {
     const oracle_store *stores;
     int n_stores;
     const oracle_arg *args;
-    int64_t cols;
+    int64_t shape[4];
     int64_t first, last;     /* flat index range [first, last) */
 } oracle_job;
 
@@ -347,11 +355,15 @@ static void *run_range(void *vp)
     const oracle_job *J = (const oracle_job *)vp;
     uint32_t *val = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(J->n_nodes > 0 ? J->n_nodes : 1));
     for (int64_t p = J->first; p < J->last; ++p) {
-        int64_t r = p / J->cols, c = p % J->cols;
+        int64_t idx[4], q = p;                 /* row-major: the last index varies fastest */
+        for (int d = 3; d >= 0; --d) {
+            idx[d] = q % J->shape[d];
+            q /= J->shape[d];
+        }
         for (int t = 0; t < J->n_nodes; ++t) {
             const oracle_node *n = &J->nodes[t];
             if (n->kind == OR_LOAD)
-                val[t] = read_elem(&J->args[n->arg], r, c);
+                val[t] = read_elem(&J->args[n->arg], idx);
             else if (n->kind == OR_SCALAR)
                 val[t] = J->args[n->arg].bits;
             else
@@ -359,23 +371,23 @@ static void *run_range(void *vp)
                                   n->b >= 0 ? val[n->b] : 0u, n->c >= 0 ? val[n->c] : 0u);
         }
         for (int s = 0; s < J->n_stores; ++s)
-            write_elem(&J->args[J->stores[s].arg], r, c, val[J->stores[s].tag]);
+            write_elem(&J->args[J->stores[s].arg], idx, val[J->stores[s].tag]);
     }
     free(val);
     return NULL;
 }
 
-/* Evaluate the Command over the logical shape rows x cols.  The caller (the
- * oracle's Python front end) has already checked tags, dtypes and shapes.
- * nthreads > 1 splits the flat index range into contiguous pieces; the result
- * does not depend on it.  Returns 0, or a nonzero code if the floating-point
- * environment is not IEEE default. */
+/* Evaluate the Command over the 4-D logical shape.  The caller (the oracle's
+ * Python front end) has already checked tags, dtypes and shapes.  nthreads > 1
+ * splits the flat index range into contiguous pieces; the result does not
+ * depend on it.  Returns 0, or a nonzero code if the floating-point environment
+ * is not IEEE default. */
 int oracle_eval(const oracle_node *nodes, int n_nodes, const oracle_store *stores, int n_stores,
-                const oracle_arg *args, int64_t rows, int64_t cols, int nthreads)
+                const oracle_arg *args, const int64_t shape[4], int nthreads)
 {
     if (oracle_check_fpenv() != 0)
         return -1;
-    int64_t total = rows * cols;
+    int64_t total = shape[0] * shape[1] * shape[2] * shape[3];
     if (total <= 0)
         return 0;
     if (nthreads < 1) nthreads = 1;
@@ -389,7 +401,7 @@ int oracle_eval(const oracle_node *nodes, int n_nodes, const oracle_store *store
         jobs[k].stores = stores;
         jobs[k].n_stores = n_stores;
         jobs[k].args = args;
-        jobs[k].cols = cols;
+        for (int d = 0; d < 4; ++d) jobs[k].shape[d] = shape[d];
         jobs[k].first = total * k / nthreads;
         jobs[k].last = total * (k + 1) / nthreads;
     }

@@ -64,7 +64,7 @@ class _Store(ctypes.Structure):
 
 
 class _Arg(ctypes.Structure):
-    _fields_ = [("ptr", ctypes.c_void_p), ("stride", ctypes.c_int64 * 2),
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride", ctypes.c_int64 * 4),
                 ("bits", ctypes.c_uint32), ("dtype", ctypes.c_int32)]
 
 
@@ -91,8 +91,8 @@ def _load(path):
     L = ctypes.CDLL(path)
     L.oracle_eval.restype = ctypes.c_int
     L.oracle_eval.argtypes = [ctypes.POINTER(_Node), ctypes.c_int, ctypes.POINTER(_Store),
-                              ctypes.c_int, ctypes.POINTER(_Arg), ctypes.c_int64,
-                              ctypes.c_int64, ctypes.c_int]
+                              ctypes.c_int, ctypes.POINTER(_Arg), ctypes.POINTER(ctypes.c_int64),
+                              ctypes.c_int]
     L.oracle_f16_to_f32.restype = ctypes.c_uint32
     L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
     L.oracle_f32_to_f16.restype = ctypes.c_uint16
@@ -131,8 +131,8 @@ class OracleCommand:
     # -- building ------------------------------------------------------------
     def load(self, dtype, rank: int = 1) -> int:
         dt = _dt(dtype)
-        if rank not in (1, 2):
-            raise OracleError("rank must be 1 or 2")
+        if rank not in (1, 2, 3, 4):
+            raise OracleError("rank must be 1 to 4")
         self.args.append(("tensor", dt, rank, False))
         self.nodes.append((LOAD, dt, 0, -1, -1, -1, len(self.args) - 1))
         return len(self.nodes) - 1
@@ -196,8 +196,8 @@ class OracleCommand:
 
     def store(self, tag: int, rank: int = 1) -> int:
         self._check_tag(tag)
-        if rank not in (1, 2):
-            raise OracleError("rank must be 1 or 2")
+        if rank not in (1, 2, 3, 4):
+            raise OracleError("rank must be 1 to 4")
         self.args.append(("tensor", self.nodes[tag][1], rank, True))
         self.stores.append((tag, len(self.args) - 1))
         return len(self.args) - 1
@@ -229,15 +229,16 @@ class OracleCommand:
                 raise OracleError("argument %d: dtype %s, declared %s" % (k, arr.dtype, NP_DTYPE[dt]))
             if arr.ndim != rank:
                 raise OracleError("argument %d: rank %d, declared %d" % (k, arr.ndim, rank))
-            shp = (1, arr.shape[0]) if rank == 1 else tuple(arr.shape)
+            shp = (1,) * (4 - rank) + tuple(arr.shape)          # right-aligned 4-D shape
             if shape is None:
                 shape = shp
             elif shape != shp:
                 raise OracleError("argument %d: shape %s differs from %s" % (k, shp, shape))
             isz = arr.itemsize
-            st = [0, arr.strides[0] // isz] if rank == 1 else [s // isz for s in arr.strides]
+            st = [0] * (4 - rank) + [s_ // isz for s_ in arr.strides]
             cargs[k].ptr = arr.__array_interface__["data"][0]
-            cargs[k].stride[0], cargs[k].stride[1] = st
+            for d in range(4):
+                cargs[k].stride[d] = st[d]
             cargs[k].dtype = dt
             keep.append(arr)
 
@@ -257,18 +258,18 @@ class OracleCommand:
             outputs = []
             for k in out_idx:
                 rank, dt = self.args[k][2], self.args[k][1]
-                shp = (shape[1],) if rank == 1 else shape
-                if rank == 1 and shape[0] != 1:
-                    raise OracleError("rank-1 output for a 2-D shape")
-                outputs.append(np.zeros(shp, dtype=NP_DTYPE[dt]))
+                if any(d != 1 for d in shape[: 4 - rank]):
+                    raise OracleError("rank-%d output for the shape %s" % (rank, shape))
+                outputs.append(np.zeros(shape[4 - rank:], dtype=NP_DTYPE[dt]))
         if len(outputs) != len(out_idx):
             raise OracleError("expected %d outputs" % len(out_idx))
         for k, o in zip(out_idx, outputs):
             view_of(k, o)
         nodes = (_Node * max(1, len(self.nodes)))(*[_Node(*n) for n in self.nodes])
         stores = (_Store * max(1, len(self.stores)))(*[_Store(*s) for s in self.stores])
-        rc = lib().oracle_eval(nodes, len(self.nodes), stores, len(self.stores), cargs,
-                               shape[0], shape[1], int(nthreads))
+        cshape = (ctypes.c_int64 * 4)(*shape)
+        rc = lib().oracle_eval(nodes, len(self.nodes), stores, len(self.stores), cargs, cshape,
+                               int(nthreads))
         if rc != 0:
             raise OracleError("host floating-point environment is not IEEE default (code %d)" % rc)
         return list(outputs)

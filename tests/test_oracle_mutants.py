@@ -7,6 +7,7 @@ that the pin suite's fast checks fail.  CPU only.
 """
 import os
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -30,8 +31,10 @@ MUTANTS = {
     "f16_in_subnormal_flushed": ("mag = ldexp((double)m, -24);", "mag = 0.0;"),
     "f16_exponent_bias_off": ("mag = ldexp((double)(1024 + m), (int)e - 25);",
                               "mag = ldexp((double)(1024 + m), (int)e - 24);"),
-    "view_index_transposed": ("int64_t off = r * g->stride[0] + c * g->stride[1];\n    if (g->dtype == OR_F16) {\n        uint16_t h;",
-                              "int64_t off = r * g->stride[1] + c * g->stride[0];\n    if (g->dtype == OR_F16) {\n        uint16_t h;"),
+    "view_index_transposed": ("return idx[0] * g->stride[0] + idx[1] * g->stride[1] + idx[2] * g->stride[2] + idx[3] * g->stride[3];",
+                              "return idx[0] * g->stride[0] + idx[1] * g->stride[1] + idx[3] * g->stride[2] + idx[2] * g->stride[3];"),
+    "leading_dim_dropped": ("return idx[0] * g->stride[0] + idx[1] * g->stride[1] + idx[2] * g->stride[2] + idx[3] * g->stride[3];",
+                            "return idx[1] * g->stride[1] + idx[2] * g->stride[2] + idx[3] * g->stride[3];"),
     "scalar_ignored": ("val[t] = J->args[n->arg].bits;", "val[t] = 0u;"),
     "f32_to_i32_rounds": ("return (int32_t)truncf(f);", "return (int32_t)nearbyintf(f);"),
     "second_operand_is_first": ("n->b >= 0 ? val[n->b] : 0u", "n->b >= 0 ? val[n->a] : 0u"),
@@ -65,6 +68,8 @@ def _fast_pins(oracle_mod):
         lambda: P.test_f32_to_f16_every_tie_and_neighbour(oracle_mod),
         lambda: P.test_transposed_brute_force(oracle_mod, (17, 33), 1, 3),
         lambda: P.test_i32_conversions_vs_numpy(oracle_mod),
+        lambda: P.test_rank_n_views_brute_force(oracle_mod, 3),
+        lambda: P.test_new_ops_vs_numpy(oracle_mod),
     ]
     for chk in checks:
         try:
@@ -92,6 +97,23 @@ def test_unmutated_copy_passes(oracle_mod, mutant_dir):
         oracle_mod.use_library(prev)
 
 
+def _run_pins_in_child(so):
+    """Run the fast pins against the library at so in a child process: a
+    planted mistake may read out of bounds and abort, which also counts as
+    caught.  Returns (failures or None if the child crashed, output)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = ("import sys; sys.path[:0] = [%r, %r]\n"
+            "from oracle import oracle\n"
+            "import test_oracle_mutants as M\n"
+            "oracle.use_library(%r)\n"
+            "print('FAILURES', M._fast_pins(oracle))\n") % (os.path.dirname(here), here, so)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    for line in r.stdout.splitlines():
+        if line.startswith("FAILURES"):
+            return int(line.split()[1]), r.stdout + r.stderr
+    return None, r.stdout + r.stderr
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(oracle_mod, mutant_dir, name):
     old, new = MUTANTS[name]
@@ -102,8 +124,5 @@ def test_mutant_is_caught(oracle_mod, mutant_dir, name):
     so = path[:-2] + ".so"
     subprocess.run(["gcc", *oracle_mod.GCC_FLAGS, "-Wno-unused-function", "-o", so, path, "-lm"],
                    check=True)
-    prev = oracle_mod.use_library(so)
-    try:
-        assert _fast_pins(oracle_mod) > 0, "planted mistake %s went unnoticed" % name
-    finally:
-        oracle_mod.use_library(prev)
+    failures, out = _run_pins_in_child(so)
+    assert failures is None or failures > 0, "planted mistake %s went unnoticed" % name

@@ -454,7 +454,7 @@ def test_front_end_rejects(oracle_mod):
     with pytest.raises(O.OracleError):
         c.add(h, h)                    # no binary16 arithmetic
     with pytest.raises(O.OracleError):
-        c.load("f32", 3)
+        c.load("f32", 5)
     c2 = O.from_spec(W.ADD_F32)
     with pytest.raises(O.OracleError):
         c2.run(np.zeros(4, np.float32), np.zeros(5, np.float32))
@@ -521,3 +521,51 @@ def test_fill_is_a_scalar_store(oracle_mod):
     out = np.zeros(37, np.float32)
     oracle_mod.from_spec(spec).run(np.float32(-0.0), outputs=[out])
     assert np.all(out.view(np.uint32) == 0x80000000)
+
+
+# ---------------------------------------------------------------------------
+# Rank-3 and rank-4 views: permuted, broadcast (stride 0), strided; brute force.
+
+def _brute(expr, shape, *arrs):
+    """Element-by-element reference: expr applied to the i-th elements."""
+    out = np.empty(shape, np.float32)
+    for idx in np.ndindex(*shape):
+        out[idx] = expr(*(a[idx] for a in arrs))
+    return out
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_rank_n_views_brute_force(oracle_mod, case):
+    rng = np.random.default_rng(300 + case)
+    shape = [(2, 3, 4), (3, 1, 5, 2), (4, 5, 6), (2, 3, 4, 5), (1, 7, 1, 3), (5, 4, 3, 2)][case]
+    r = len(shape)
+    base = rng.random(shape, dtype=np.float32)
+    perm = rng.permutation(r)
+    # X: the transpose of a contiguous array, viewed back in the logical order
+    xs = np.ascontiguousarray(np.transpose(base, perm))
+    X = np.transpose(xs, np.argsort(perm))
+    # Y: broadcast along a random dimension (stride 0) of a smaller array
+    bd = int(rng.integers(r))
+    small = rng.random(tuple(1 if d == bd else s for d, s in enumerate(shape)), dtype=np.float32)
+    Y = np.broadcast_to(small, shape)
+    # out: every other element of a wider buffer along the last dimension
+    wide = np.zeros(shape[:-1] + (2 * shape[-1],), np.float32)
+    out = wide[..., ::2]
+    spec = [("x", ("load", "f32", r)), ("y", ("load", "f32", r)), ("a", ("scalar", "f32")),
+            ("ay", ("mul", "a", "y")), ("o", ("sub", "x", "ay")), ("out", ("store", "o", r))]
+    oracle_mod.from_spec(spec).run(X, Y, np.float32(1.5), outputs=[out])
+    ref = _brute(lambda x, y: np.float32(x - np.float32(1.5) * y), shape, X, Y)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    assert np.all(wide[..., 1::2] == 0)
+
+
+def test_rank_mixing_right_aligned(oracle_mod):
+    """A rank-1 view of n matches a rank-3 view of shape (1, 1, n)."""
+    x = np.arange(7, dtype=np.float32)
+    y = np.arange(7, dtype=np.float32).reshape(1, 1, 7) * 2
+    spec = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 3)), ("r", ("add", "x", "y")),
+            ("o", ("store", "r", 3))]
+    (o,) = oracle_mod.from_spec(spec).run(x, y)
+    assert o.shape == (1, 1, 7) and np.array_equal(o.ravel(), x * 3)
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.from_spec(spec).run(x, np.zeros((1, 2, 7), np.float32))
