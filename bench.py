@@ -26,7 +26,11 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0        # MI355X HBM3E peak, 8 TB/s
 METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, per Command"
 DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two_out": "f16/f32",
-            "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32"}
+            "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32",
+            "batched_transpose": "f32", "bias_nchw": "f32"}
+# Measured besides the five configurations: the plain copy (the bandwidth and
+# counter reference), the widened op set and the rank-3/4 views.
+EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -53,12 +57,8 @@ def setup(wl, n=None):
     spec = W.WORKLOADS[wl]["spec"]
     vals, extra = W.make_inputs(wl, n)
     dev = torch.device("cuda:0")
-    gv = [torch.from_numpy(np.ascontiguousarray(v)).to(dev) if isinstance(v, np.ndarray) else v for v in vals]
-    side = W.WORKLOADS[wl]["n"] if n is None else n
-    if wl == "transposed_2d":
-        gv[0] = torch.from_numpy(extra["X_storage"]).to(dev)[:, :side]
-        gv[1] = torch.from_numpy(extra["Y"]).to(dev).t()
-    shape = (side, side) if wl == "transposed_2d" else (side,)
+    gv = W.to_torch(vals, extra, dev)
+    shape = W.shape_of(wl, n)
     td = {"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}
     out_dt = []
     dts = {}
@@ -135,11 +135,12 @@ def cpu_baseline(wl, budget_s=20.0):
     from oracle import oracle
     spec = W.WORKLOADS[wl]["spec"]
     threads = max(1, min(16, os.cpu_count() or 1))
-    full = W.WORKLOADS[wl]["n"]
+    full = W.WORKLOADS[wl].get("n")
     n = full if wl != "transposed_2d" else 2048
     if wl in ("axpby_f32", "mixed_two_out"):
         n = 1 << 24
-    vals, extra = W.make_inputs(wl, n)
+    shape = {"batched_transpose": (4, 2048, 2048), "bias_nchw": (2, 256, 128, 256)}.get(wl)
+    vals, extra = W.make_inputs(wl, n, shape=shape)
     cmd = oracle.from_spec(spec)
     res = {}
     for t in (1, threads):
@@ -151,8 +152,8 @@ def cpu_baseline(wl, budget_s=20.0):
             if sum(runs) > budget_s:
                 break
         res[t] = statistics.median(runs)
-    elems = W.elements(wl, n)
-    byts = W.algorithmic_bytes(wl, n)
+    elems = W.elements(wl, n, shape)
+    byts = W.algorithmic_bytes(wl, n, shape)
     best_t = threads
     return {
         "value": round(byts / res[best_t] / 1e9, 3), "unit": "GB/s", "cores": best_t, "kind": "oracle",
@@ -209,26 +210,7 @@ def measure(wl, steps, warmup, cold_too=True):
 def read_write_bytes(wl):
     """Algorithmic bytes read and written by one launch of the workload."""
     import workloads as W
-    size = {"f16": 2, "f32": 4, "i32": 4}
-    dt, rd, wr = {}, 0, 0
-    for name, st in W.WORKLOADS[wl]["spec"]:
-        if st[0] == "load":
-            dt[name] = st[1]
-            rd += size[st[1]]
-        elif st[0] == "scalar":
-            dt[name] = st[1]
-        elif st[0] == "cvt":
-            dt[name] = st[2]
-        elif st[0] in ("add", "sub", "mul", "neg", "abs", "min", "max"):
-            dt[name] = dt[st[1]]
-        elif st[0] == "select":
-            dt[name] = dt[st[2]]
-        elif st[0] in ("eq", "ne", "lt", "le", "gt", "ge", "ltu", "leu", "gtu", "geu"):
-            dt[name] = "i32"
-        elif st[0] == "store":
-            wr += size[dt[st[1]]]
-    e = W.elements(wl)
-    return e * rd, e * wr
+    return W.algorithmic_read_write(wl)
 
 
 def _csv_rows(directory, suffix):
@@ -271,7 +253,7 @@ def summarize_counters(root, command):
              "| workload | kernel | dispatches | FETCH KiB | WRITE KiB | read B (scaled) | algorithmic read B | "
              "ratio | written B (scaled) | algorithmic write B | ratio |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
-    for wl in W.CONFIGS + ["copy_f32", "classify_u32", "fill_f32"]:
+    for wl in W.CONFIGS + EXTRA:
         if not os.path.isdir(os.path.join(root, "fetch_" + wl)):
             continue
         name, f, nf = per_dispatch("fetch", wl)
@@ -383,7 +365,7 @@ def main():
     }
     if a.all:
         line["commands"] = {}
-        for wl in W.CONFIGS + ["copy_f32", "classify_u32", "fill_f32"]:
+        for wl in W.CONFIGS + EXTRA:
             if wl == a.workload:
                 r = head
             else:

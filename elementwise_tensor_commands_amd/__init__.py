@@ -51,15 +51,15 @@ class Error(RuntimeError):
 
 class cmd_arg(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ptr", ctypes.c_void_p),
-                ("size", ctypes.c_int64 * 2), ("stride", ctypes.c_int64 * 2),
+                ("size", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4),
                 ("bits", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class cmd_plan_info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("specialised", ctypes.c_int32), ("vector", ctypes.c_int32),
                 ("elems_per_thread", ctypes.c_int32), ("grid", ctypes.c_int64),
-                ("block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("rows", ctypes.c_int64),
-                ("cols", ctypes.c_int64), ("kernel", ctypes.c_char * 64)]
+                ("block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("dims", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("size", ctypes.c_int64 * 4), ("kernel", ctypes.c_char * 64)]
 
 
 def _load_library():
@@ -211,12 +211,13 @@ class Command:
             a.dtype = _torch_dtype_code(v)
             a.ptr = v.data_ptr() if v.numel() > 0 else (v.data_ptr() or None)
             shape, strides = tuple(v.shape), tuple(v.stride())
-            for d in range(min(2, len(shape))):
+            for d in range(min(4, len(shape))):
                 a.size[d] = shape[d]
                 a.stride[d] = strides[d]
             if len(shape) != rank:
                 # the C side checks shapes per declared rank; a rank mismatch is an argument error
-                a.size[0] = a.size[1] = -1
+                for d in range(4):
+                    a.size[d] = -1
         return arr, n
 
     def launch(self, *values, stream=None):
@@ -243,7 +244,7 @@ class Command:
         return {"path": PATH_NAMES[info.path], "specialised": bool(info.specialised),
                 "vector": bool(info.vector), "elems_per_thread": info.elems_per_thread,
                 "grid": info.grid, "block": info.block, "lds_bytes": info.lds_bytes,
-                "rows": info.rows, "cols": info.cols, "kernel": info.kernel.decode()}
+                "dims": info.dims, "size": tuple(info.size), "kernel": info.kernel.decode()}
 
     def dump(self) -> str:
         n = lib.cmd_dump(self._h, None, 0)

@@ -44,17 +44,29 @@ struct ArgDecl {
     int tag;        // value produced (load/scalar) or stored (store)
 };
 
+// A bound view over the right-aligned 4-D shape.
 struct View {
     char *ptr;
-    int64_t s0, s1;
+    int64_t s[4];
     int dtype;
 };
 
 struct Bound {
-    int64_t rows = 0, cols = 0;
+    int64_t shape[4] = {1, 1, 1, 1};
+    int64_t numel = 0;
     View in[kMaxIn];
     View out[kMaxOut];
     uint32_t uni[kMaxUni];
+};
+
+// Canonical form: size-1 dimensions dropped, dimensions ordered by the first
+// output's strides (largest first) and contiguous neighbours merged, then
+// padded on the left to 4 dimensions.
+struct Canon {
+    int dims = 1;
+    int64_t n[4] = {1, 1, 1, 1};
+    int64_t in_s[kMaxIn][4] = {};
+    int64_t out_s[kMaxOut][4] = {};
 };
 
 struct Selection {
@@ -66,6 +78,8 @@ struct Selection {
     TileShape tile{64, 64, 256};
     int walk = 1;
     int64_t tiles_r = 0, tiles_c = 0;
+    uint8_t rowconst[kMaxIn] = {};
+    Canon cn;
     int n_staged = 0;
     uint8_t staged[kMaxIn] = {};
     int64_t grid = 0;
@@ -346,21 +360,30 @@ TileShape tile_shape()
 }
 
 // Highest element offset a view reaches (views have non-negative strides).
-__int128 max_offset(int64_t rows, int64_t cols, int64_t s0, int64_t s1)
+__int128 max_offset(const int64_t shape[4], const int64_t s[4])
 {
-    return (__int128)(rows - 1) * s0 + (__int128)(cols - 1) * s1;
+    __int128 m = 0;
+    for (int d = 0; d < 4; ++d) m += (__int128)(shape[d] - 1) * s[d];
+    return m;
 }
 
-// A store view must be one-to-one.  Accepted: after dropping size-1
-// dimensions, the inner (smaller-stride) dimension has stride >= 1 and the
-// outer stride is at least the inner extent.  (Sufficient, not necessary.)
-bool injective(int64_t rows, int64_t cols, int64_t s0, int64_t s1)
+// A store view must be one-to-one.  Accepted (sufficient, not necessary): the
+// dimensions of size > 1, taken in increasing stride order, each have a stride
+// larger than the highest offset the smaller ones reach.
+bool injective(const int64_t shape[4], const int64_t s[4])
 {
-    if (rows <= 1 && cols <= 1) return true;
-    if (rows <= 1) return s1 >= 1;
-    if (cols <= 1) return s0 >= 1;
-    if (s0 >= s1) return s1 >= 1 && (__int128)s0 >= (__int128)cols * s1;
-    return s0 >= 1 && (__int128)s1 >= (__int128)rows * s0;
+    int64_t st[4], sz[4];
+    int k = 0;
+    for (int d = 0; d < 4; ++d)
+        if (shape[d] > 1) st[k] = s[d], sz[k] = shape[d], ++k;
+    for (int i = 1; i < k; ++i)                 // insertion sort by stride
+        for (int j = i; j > 0 && st[j] < st[j - 1]; --j) std::swap(st[j], st[j - 1]), std::swap(sz[j], sz[j - 1]);
+    __int128 reach = 0;
+    for (int i = 0; i < k; ++i) {
+        if ((__int128)st[i] <= reach) return false;
+        reach += (__int128)st[i] * (sz[i] - 1);
+    }
+    return true;
 }
 
 int bind(cmd_t h, const cmd_arg *args, int nargs, Bound &B)
@@ -383,40 +406,40 @@ int bind(cmd_t h, const cmd_arg *args, int nargs, Bound &B)
                 return fail(h, CMD_E_ARG, "argument %d: binary16 scalar has bits above bit 15", i);
             continue;
         }
-        const int64_t rows = d.rank == 1 ? 1 : a.size[0];
-        const int64_t cols = d.rank == 1 ? a.size[0] : a.size[1];
-        if (rows < 0 || cols < 0) return fail(h, CMD_E_SHAPE, "argument %d: negative size", i);
-        if (a.stride[0] < 0 || (d.rank == 2 && a.stride[1] < 0))
-            return fail(h, CMD_E_STRIDE, "argument %d: negative stride", i);
+        int64_t shp[4] = {1, 1, 1, 1};
+        for (int k = 0; k < d.rank; ++k) {
+            if (a.size[k] < 0) return fail(h, CMD_E_SHAPE, "argument %d: negative size", i);
+            if (a.stride[k] < 0) return fail(h, CMD_E_STRIDE, "argument %d: negative stride", i);
+            shp[4 - d.rank + k] = a.size[k];
+        }
         if (!have_shape) {
-            B.rows = rows;
-            B.cols = cols;
+            std::memcpy(B.shape, shp, sizeof shp);
             have_shape = true;
-        } else if (rows != B.rows || cols != B.cols) {
-            return fail(h, CMD_E_SHAPE, "argument %d: shape %lldx%lld differs from %lldx%lld", i,
-                        (long long)rows, (long long)cols, (long long)B.rows, (long long)B.cols);
+        } else if (std::memcmp(B.shape, shp, sizeof shp) != 0) {
+            return fail(h, CMD_E_SHAPE, "argument %d: shape (%lld,%lld,%lld,%lld) differs from (%lld,%lld,%lld,%lld)",
+                        i, (long long)shp[0], (long long)shp[1], (long long)shp[2], (long long)shp[3],
+                        (long long)B.shape[0], (long long)B.shape[1], (long long)B.shape[2], (long long)B.shape[3]);
         }
     }
     if (!have_shape) return fail(h, CMD_E_SHAPE, "no tensor argument gives the shape");
-    if (B.rows > INT32_MAX || B.cols > ((int64_t)1 << 40) || (__int128)B.rows * B.cols > ((__int128)1 << 40))
-        return fail(h, CMD_E_LIMIT, "shape %lldx%lld exceeds 2^40 elements", (long long)B.rows,
-                    (long long)B.cols);
-    const bool empty = B.rows == 0 || B.cols == 0;
+    __int128 numel = 1;
+    for (int d = 0; d < 4; ++d) {
+        if (B.shape[d] > ((int64_t)1 << 40)) return fail(h, CMD_E_LIMIT, "a size exceeds 2^40");
+        numel *= B.shape[d];
+    }
+    if (numel > ((__int128)1 << 40)) return fail(h, CMD_E_LIMIT, "the shape has more than 2^40 elements");
+    B.numel = (int64_t)numel;
+    const bool empty = B.numel == 0;
     auto view_of = [&](int i, View &v) -> int {
         const cmd_arg &a = args[i];
         const ArgDecl &d = h->args[i];
         v.ptr = static_cast<char *>(a.ptr);
         v.dtype = d.dtype;
-        if (d.rank == 1) {
-            v.s0 = 0;
-            v.s1 = a.stride[0];
-        } else {
-            v.s0 = a.stride[0];
-            v.s1 = a.stride[1];
-        }
+        for (int k = 0; k < 4; ++k) v.s[k] = 0;
+        for (int k = 0; k < d.rank; ++k) v.s[4 - d.rank + k] = a.stride[k];
         if (!empty) {
             if (!v.ptr) return fail(h, CMD_E_ARG, "argument %d: NULL pointer", i);
-            if (max_offset(B.rows, B.cols, v.s0, v.s1) >= ((__int128)1 << 48))
+            if (max_offset(B.shape, v.s) >= ((__int128)1 << 48))
                 return fail(h, CMD_E_LIMIT, "argument %d: view spans more than 2^48 elements", i);
             if ((reinterpret_cast<uintptr_t>(v.ptr) % (uintptr_t)esize(d.dtype)) != 0)
                 return fail(h, CMD_E_ARG, "argument %d: pointer not aligned to its element size", i);
@@ -431,7 +454,7 @@ int bind(cmd_t h, const cmd_arg *args, int nargs, Bound &B)
         const int i = h->out_arg[k];
         int rc = view_of(i, B.out[k]);
         if (rc) return rc;
-        if (!empty && !injective(B.rows, B.cols, B.out[k].s0, B.out[k].s1))
+        if (!empty && !injective(B.shape, B.out[k].s))
             return fail(h, CMD_E_STRIDE, "argument %d: store view maps two indexes to one element", i);
     }
     for (int k = 0; k < h->prog.n_uni; ++k) B.uni[k] = args[h->uni_arg[k]].bits;
@@ -439,7 +462,7 @@ int bind(cmd_t h, const cmd_arg *args, int nargs, Bound &B)
     // Overlap: outputs pairwise disjoint; an output meets an input only as the identical view.
     auto range = [&](const View &v, uintptr_t &lo, uintptr_t &hi) {
         lo = reinterpret_cast<uintptr_t>(v.ptr);
-        hi = lo + (uintptr_t)((max_offset(B.rows, B.cols, v.s0, v.s1) + 1) * esize(v.dtype));
+        hi = lo + (uintptr_t)((max_offset(B.shape, v.s) + 1) * esize(v.dtype));
     };
     for (int k = 0; k < h->prog.n_out; ++k) {
         uintptr_t lo, hi;
@@ -455,14 +478,62 @@ int bind(cmd_t h, const cmd_arg *args, int nargs, Bound &B)
             range(B.in[j], lo2, hi2);
             if (!(lo < hi2 && lo2 < hi)) continue;
             const View &o = B.out[k], &in = B.in[j];
-            const bool same = o.ptr == in.ptr && o.dtype == in.dtype &&
-                              (B.rows == 1 || o.s0 == in.s0) && (B.cols == 1 || o.s1 == in.s1);
+            bool same = o.ptr == in.ptr && o.dtype == in.dtype;
+            for (int d = 0; d < 4; ++d) same = same && (B.shape[d] == 1 || o.s[d] == in.s[d]);
             if (!same)
                 return fail(h, CMD_E_ALIAS, "output argument %d overlaps input argument %d other than as the identical view",
                             h->out_arg[k], h->in_arg[j]);
         }
     }
     return CMD_OK;
+}
+
+// The canonical form of the bound views (see Canon).  Elementwise evaluation
+// visits every index once, so any common reordering of the dimensions gives the
+// same result; ordering by the first output's strides makes that output
+// row-major, and merging contiguous neighbours turns jointly contiguous views
+// into one flat dimension.
+Canon canonicalize(const Program &P, const Bound &B)
+{
+    int dims[4], nd = 0;
+    for (int d = 0; d < 4; ++d)
+        if (B.shape[d] > 1) dims[nd++] = d;
+    for (int i = 1; i < nd; ++i)     // stable: largest first output stride first
+        for (int j = i; j > 0 && B.out[0].s[dims[j]] > B.out[0].s[dims[j - 1]]; --j) std::swap(dims[j], dims[j - 1]);
+    // operand strides along the ordered dimensions, merged
+    int64_t n[4], is[kMaxIn][4], os[kMaxOut][4];
+    int m = 0;
+    for (int i = 0; i < nd; ++i) {
+        const int d = dims[i];
+        bool merge = m > 0;
+        for (int k = 0; k < P.n_in && merge; ++k) merge = is[k][m - 1] == B.in[k].s[d] * B.shape[d];
+        for (int k = 0; k < P.n_out && merge; ++k) merge = os[k][m - 1] == B.out[k].s[d] * B.shape[d];
+        if (merge) {
+            n[m - 1] *= B.shape[d];
+            for (int k = 0; k < P.n_in; ++k) is[k][m - 1] = B.in[k].s[d];
+            for (int k = 0; k < P.n_out; ++k) os[k][m - 1] = B.out[k].s[d];
+        } else {
+            n[m] = B.shape[d];
+            for (int k = 0; k < P.n_in; ++k) is[k][m] = B.in[k].s[d];
+            for (int k = 0; k < P.n_out; ++k) os[k][m] = B.out[k].s[d];
+            ++m;
+        }
+    }
+    Canon c;
+    if (m == 0) {                   // a single element
+        m = 1;
+        n[0] = 1;
+        for (int k = 0; k < P.n_in; ++k) is[k][0] = 1;
+        for (int k = 0; k < P.n_out; ++k) os[k][0] = 1;
+    }
+    c.dims = m;
+    const int pad = 4 - m;
+    for (int i = 0; i < m; ++i) {
+        c.n[pad + i] = n[i];
+        for (int k = 0; k < P.n_in; ++k) c.in_s[k][pad + i] = is[k][i];
+        for (int k = 0; k < P.n_out; ++k) c.out_s[k][pad + i] = os[k][i];
+    }
+    return c;
 }
 
 // ---------------------------------------------------------------------------
@@ -472,26 +543,26 @@ int g_cu_count[64];   // per device ordinal, 0 = not queried yet
 
 int cu_count_cached(int dev) { return dev >= 0 && dev < 64 && g_cu_count[dev] > 0 ? g_cu_count[dev] : 256; }
 
-bool flat(const Bound &B, const View &v)
-{
-    return (B.cols == 1 || v.s1 == 1) && (B.rows == 1 || v.s0 == B.cols);
-}
+// Work-items of one dispatch: its grid size is a 32-bit count.
+constexpr int64_t kMaxGridItems = (int64_t)1 << 31;
 
 bool aligned(const void *p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes == 0; }
 
 void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
 {
     const Program &P = h->prog;
-    const int64_t numel = B.rows * B.cols;
+    const int64_t numel = B.numel;
     if (numel == 0) {
         S.path = CMD_PATH_NONE;
         S.name = "none";
         return;
     }
     const bool force_generic = env_flag("ECMD_FORCE_GENERIC");
-    bool all_flat = true;
-    for (int k = 0; k < P.n_in; ++k) all_flat = all_flat && flat(B, B.in[k]);
-    for (int k = 0; k < P.n_out; ++k) all_flat = all_flat && flat(B, B.out[k]);
+    S.cn = canonicalize(P, B);
+    const Canon &C = S.cn;
+    bool all_flat = C.dims == 1;
+    for (int k = 0; k < P.n_in && all_flat; ++k) all_flat = C.in_s[k][3] == 1;
+    for (int k = 0; k < P.n_out && all_flat; ++k) all_flat = C.out_s[k][3] == 1;
     if (all_flat) {
         S.path = CMD_PATH_LINEAR;
         S.vec = true;
@@ -513,54 +584,97 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         if (need < 1) need = 1;
         const int64_t per_cu = env_int("ECMD_BLOCKS_PER_CU", 0);
         S.grid = per_cu > 0 ? std::min(need, std::max<int64_t>(1, per_cu * cu_count)) : need;
+        S.grid = std::min<int64_t>(S.grid, kMaxGridItems / kLinearBlock);   // the kernel loops over the rest
         S.xcd_remap = env_flag("ECMD_XCD_REMAP") && S.grid % 8 == 0;
         S.name = S.vec ? linear_name(S.variant) : "linear_generic_unaligned";
         return;
     }
-    // Tiled: rank 2 with every output and every input either inner-contiguous
-    // (direct) or outer-contiguous (staged through LDS), with vector-aligned rows.
-    bool tiled = B.rows >= 2 && B.cols >= 2;
-    int n_staged = 0, mask = 0;
-    for (int k = 0; k < P.n_out && tiled; ++k) {
-        const View &v = B.out[k];
-        const int64_t vb = 4 * esize(v.dtype);
-        tiled = v.s1 == 1 && aligned(v.ptr, vb) && (v.s0 * esize(v.dtype)) % vb == 0;
-    }
+    // Tiled: planes of dimensions (2, 3) after moving the staged inputs' unit
+    // stride dimension to position 2.  Every output is unit-stride along
+    // dimension 3; every input is direct (unit stride along 3), row-constant
+    // (stride 0 along 3) or staged (unit stride along one other dimension, the
+    // same for all staged inputs).  Vector accesses need 16-byte rows (8-byte
+    // for binary16) in every plane.
+    bool tiled = C.dims >= 2;
+    int r_dim = -1, n_staged = 0, mask = 0;
+    for (int k = 0; k < P.n_out && tiled; ++k) tiled = C.out_s[k][3] == 1;
     for (int k = 0; k < P.n_in && tiled; ++k) {
-        const View &v = B.in[k];
-        const int64_t vb = 4 * esize(v.dtype);
-        if (v.s1 == 1) {
-            tiled = aligned(v.ptr, vb) && (v.s0 * esize(v.dtype)) % vb == 0;
-        } else if (v.s0 == 1) {
-            tiled = aligned(v.ptr, vb) && (v.s1 * esize(v.dtype)) % vb == 0;
-            S.staged[k] = (uint8_t)(++n_staged);
-            mask |= 1 << k;
+        if (C.in_s[k][3] == 1 || C.in_s[k][3] == 0) continue;
+        int r = -1;
+        for (int d = 0; d < 3; ++d)
+            if (C.n[d] > 1 && C.in_s[k][d] == 1) r = d;
+        if (r < 0 || (r_dim >= 0 && r != r_dim)) tiled = false;
+        r_dim = r;
+    }
+    Canon T = C;
+    if (tiled && r_dim >= 0 && r_dim != 2) {     // move r_dim to position 2, keep the others' order
+        auto move = [&](int64_t (&v)[4]) {
+            const int64_t x = v[r_dim];
+            for (int d = r_dim; d < 2; ++d) v[d] = v[d + 1];
+            v[2] = x;
+        };
+        move(T.n);
+        for (int k = 0; k < P.n_in; ++k) move(T.in_s[k]);
+        for (int k = 0; k < P.n_out; ++k) move(T.out_s[k]);
+    }
+    // Full tiles access 4-element vectors that start at a multiple of 4 along
+    // the view's unit-stride dimension `unit`: the base and every other stride
+    // must keep them 4-element aligned.
+    auto plane_aligned = [&](const View &v, const int64_t (&st)[4], int unit) {
+        bool ok = aligned(v.ptr, 4 * esize(v.dtype));
+        for (int d = 0; d < 4 && ok; ++d)
+            if (d != unit && T.n[d] > 1) ok = st[d] % 4 == 0;
+        return ok;
+    };
+    uint8_t staged[kMaxIn] = {}, rowconst[kMaxIn] = {};
+    for (int k = 0; k < P.n_out && tiled; ++k) tiled = plane_aligned(B.out[k], T.out_s[k], 3);
+    for (int k = 0; k < P.n_in && tiled; ++k) {
+        if (T.in_s[k][3] == 0) {
+            rowconst[k] = 1;
+        } else if (T.in_s[k][3] == 1) {
+            tiled = plane_aligned(B.in[k], T.in_s[k], 3);
         } else {
-            tiled = false;
+            tiled = plane_aligned(B.in[k], T.in_s[k], 2);
+            staged[k] = (uint8_t)(++n_staged);
+            mask |= 1 << k;
         }
+    }
+    // One work-group per tile and no loop: the grid must stay within the
+    // dispatch's 32-bit work-item count.
+    if (tiled && n_staged <= 3) {
+        const TileShape ts = tile_shape();
+        const int64_t tiles = ((T.n[2] + 63) / 64) * ((T.n[3] + 63) / 64) * T.n[0] * T.n[1];
+        tiled = tiles * 256 < kMaxGridItems &&
+                ((T.n[2] + ts.tm - 1) / ts.tm) * ((T.n[3] + ts.tn - 1) / ts.tn) * T.n[0] * T.n[1] * ts.block <
+                    kMaxGridItems;
     }
     if (tiled && n_staged <= 3) {
         S.path = CMD_PATH_TILED;
+        S.cn = T;
         S.n_staged = n_staged;
-        S.variant = (!force_generic && std::memcmp(&P, &kProgAddScaledF32, sizeof(Program)) == 0 && mask == 0x2) ? 0 : -1;
+        std::memcpy(S.staged, staged, sizeof staged);
+        std::memcpy(S.rowconst, rowconst, sizeof rowconst);
+        bool any_rowconst = false;
+        for (int k = 0; k < P.n_in; ++k) any_rowconst = any_rowconst || rowconst[k];
+        S.variant = (!force_generic && !any_rowconst && std::memcmp(&P, &kProgAddScaledF32, sizeof(Program)) == 0 &&
+                     mask == 0x2) ? 0 : -1;
         S.tile = S.variant == 0 ? tile_shape() : TileShape{64, 64, 256};   // the interpreter has one shape
         S.walk = (int)env_int("ECMD_TILE_WALK", kDefaultTileWalk);
         S.e = 4;
         S.block = S.tile.block;
-        S.tiles_r = (B.rows + S.tile.tm - 1) / S.tile.tm;
-        S.tiles_c = (B.cols + S.tile.tn - 1) / S.tile.tn;
-        S.grid = S.tiles_r * S.tiles_c;
+        S.tiles_r = (T.n[2] + S.tile.tm - 1) / S.tile.tm;
+        S.tiles_c = (T.n[3] + S.tile.tn - 1) / S.tile.tn;
+        S.grid = S.tiles_r * S.tiles_c * T.n[0] * T.n[1];
         S.lds = n_staged * S.tile.tn * (S.tile.tm + 1) * 4;
         S.name = S.variant == 0 ? "tiled_add_scaled_f32" : "tiled_generic";
         return;
     }
-    std::memset(S.staged, 0, sizeof S.staged);
     S.n_staged = 0;
     S.path = CMD_PATH_GATHER;
     S.variant = -1;
     S.e = kGatherE;
     S.block = kGatherBlock;
-    const int64_t total = B.rows * ((B.cols + kGatherE - 1) / kGatherE);
+    const int64_t total = C.n[0] * C.n[1] * C.n[2] * ((C.n[3] + kGatherE - 1) / kGatherE);
     S.grid = std::max<int64_t>(1, std::min<int64_t>((total + kGatherBlock - 1) / kGatherBlock, 8LL * cu_count));
     S.name = "gather_generic";
 }
@@ -579,19 +693,18 @@ int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int
 void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
 {
     std::memset(&A, 0, sizeof A);
+    const Canon &C = S.cn;
     for (int k = 0; k < h->prog.n_in; ++k) {
         A.in[k] = B.in[k].ptr;
-        A.in_s0[k] = B.in[k].s0;
-        A.in_s1[k] = B.in[k].s1;
+        std::memcpy(A.in_s[k], C.in_s[k], sizeof A.in_s[k]);
         A.in_staged[k] = S.staged[k];
+        A.in_rowconst[k] = S.rowconst[k];
     }
     for (int k = 0; k < h->prog.n_out; ++k) {
         A.out[k] = B.out[k].ptr;
-        A.out_s0[k] = B.out[k].s0;
-        A.out_s1[k] = B.out[k].s1;
+        std::memcpy(A.out_s[k], C.out_s[k], sizeof A.out_s[k]);
     }
-    A.rows = B.rows;
-    A.cols = B.cols;
+    std::memcpy(A.n, C.n, sizeof A.n);
     A.tiles_r = S.tiles_r;
     A.tiles_c = S.tiles_c;
     A.tile_walk = S.walk;
@@ -637,7 +750,7 @@ int cmd_load(cmd_t h, int32_t dtype, int32_t rank, cmd_tag *tag, int32_t *arg_in
     if (!h) return CMD_E_ARG;
     if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
     if (!valid_dtype(dtype)) return fail(h, CMD_E_DTYPE, "unknown dtype %d", dtype);
-    if (rank != 1 && rank != 2) return fail(h, CMD_E_LIMIT, "rank %d is not 1 or 2", rank);
+    if (rank < 1 || rank > CMD_MAX_RANK) return fail(h, CMD_E_LIMIT, "rank %d is not 1 to 4", rank);
     if ((int)h->args.size() >= CMD_MAX_ARGS)
         return fail(h, CMD_E_LIMIT, "more than %d CommandArguments", CMD_MAX_ARGS);
     const int arg = (int)h->args.size();
@@ -715,7 +828,7 @@ int cmd_store(cmd_t h, cmd_tag value, int32_t rank, int32_t *arg_index)
     if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
     if (value < 0 || value >= (int)h->nodes.size())
         return fail(h, CMD_E_TAG, "tag %d does not name an earlier value", value);
-    if (rank != 1 && rank != 2) return fail(h, CMD_E_LIMIT, "rank %d is not 1 or 2", rank);
+    if (rank < 1 || rank > CMD_MAX_RANK) return fail(h, CMD_E_LIMIT, "rank %d is not 1 to 4", rank);
     if ((int)h->args.size() >= CMD_MAX_ARGS)
         return fail(h, CMD_E_LIMIT, "more than %d CommandArguments", CMD_MAX_ARGS);
     if ((int)h->stores.size() >= CMD_MAX_STORES)
@@ -744,8 +857,8 @@ int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info)
     info->grid = S.grid;
     info->block = S.block;
     info->lds_bytes = S.lds;
-    info->rows = B.rows;
-    info->cols = B.cols;
+    info->dims = S.cn.dims;
+    for (int d = 0; d < 4; ++d) info->size[d] = S.cn.n[d];
     std::snprintf(info->kernel, sizeof info->kernel, "%s", S.name);
     h->err.clear();
     return CMD_OK;
@@ -760,7 +873,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
     Bound B;
     rc = bind(h, args, nargs, B);
     if (rc) return rc;
-    if (B.rows * B.cols == 0) return CMD_OK;
+    if (B.numel == 0) return CMD_OK;
     // All checks passed; from here on HIP is called.
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -785,7 +898,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         std::memset(&A, 0, sizeof A);
         for (int k = 0; k < h->prog.n_in; ++k) A.in[k] = B.in[k].ptr;
         for (int k = 0; k < h->prog.n_out; ++k) A.out[k] = B.out[k].ptr;
-        A.n = B.rows * B.cols;
+        A.n = B.numel;
         std::memcpy(A.uni, B.uni, sizeof A.uni);
         A.flags = S.xcd_remap ? kLinearXcdRemap : 0u;
         A.prog = h->prog;

@@ -115,17 +115,22 @@ struct LinearArgs {
 };
 constexpr uint32_t kLinearXcdRemap = 1;   // give each XCD one contiguous run of blocks
 
-// Rank-2 shape (rows x cols) with per-operand element strides.
+// Canonical 4-D views (the host drops size-1 dimensions, orders dimensions by
+// the first output's strides and merges contiguous ones, then pads on the
+// left with size-1 dimensions): sizes n[0..3], element strides per operand.
+// On the tiled path dimensions 0 and 1 are batch dimensions, 2 the rows and 3
+// the columns of the tiled plane.
 struct StridedArgs {
     const void *in[kMaxIn];
     void *out[kMaxOut];
-    int64_t in_s0[kMaxIn], in_s1[kMaxIn];
-    int64_t out_s0[kMaxOut], out_s1[kMaxOut];
-    int64_t rows, cols;
-    int64_t tiles_r, tiles_c; // tiled path: number of row and column tiles
-    int32_t tile_walk;        // tiled path: tile rows walked before moving right (<= 1: row by row)
+    int64_t n[4];
+    int64_t in_s[kMaxIn][4];
+    int64_t out_s[kMaxOut][4];
+    int64_t tiles_r, tiles_c;   // tiled path: tiles per plane in each direction
+    int32_t tile_walk;          // tiled path: tile rows walked before moving right (<= 1: row by row)
     uint32_t uni[kMaxUni];
-    uint8_t in_staged[kMaxIn];  // tiled path: 1 = read through an LDS tile (column-contiguous view)
+    uint8_t in_staged[kMaxIn];  // tiled path: p + 1 = read through LDS tile p (column-contiguous view)
+    uint8_t in_rowconst[kMaxIn];// tiled path: 1 = stride 0 along the columns (one value per row)
     Program prog;
 };
 

@@ -1,11 +1,12 @@
-// kernels_gather.hip -- rank-2 evaluation for views no faster path accepts
-// (inner stride other than 1 on an output, both strides other than 1, stride 0
-// on the inner dimension, or bases too misaligned for vector access).
+// kernels_gather.hip -- evaluation for views no faster path accepts (after
+// canonicalization: an output with no unit-stride dimension, inputs strided in
+// every dimension, broadcasts the tiled path does not take, or bases too
+// misaligned for vector access).
 //
-// Each work-item takes 4 consecutive columns of one row, computes every
-// operand's element offset r*s0 + c*s1 (rocRoller "Design Overview", section
-// "Kernel Graph": a view is sizes plus strides) and accesses elements one by
-// one.  It is correct for every accepted view and makes no attempt at
+// Each work-item takes 4 consecutive elements along the last canonical
+// dimension, computes every operand's element offset i0*s0 + i1*s1 + i2*s2 +
+// i3*s3 (rocRoller "Design Overview", section "Kernel Graph": a view is sizes
+// plus strides) and accesses elements one by one.  It is correct for every accepted view and makes no attempt at
 // coalescing.
 #include <hip/hip_runtime.h>
 
@@ -16,23 +17,29 @@ namespace ecmd {
 __global__ __launch_bounds__(kGatherBlock) void k_gather(const StridedArgs A)
 {
     constexpr int E = kGatherE;
-    const int64_t cchunks = (A.cols + E - 1) / E;
-    const int64_t total = A.rows * cchunks;
+    const int64_t cchunks = (A.n[3] + E - 1) / E;
+    const int64_t total = A.n[0] * A.n[1] * A.n[2] * cchunks;
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < total; id += step) {
-        const int64_t r = id / cchunks;
-        const int64_t c = (id - r * cchunks) * E;
-        const int64_t left = A.cols - c;
+        // id -> (i0, i1, i2, chunk of 4 along dimension 3), row-major
+        int64_t q = id / cchunks;
+        const int64_t c = (id - q * cchunks) * E;
+        const int64_t i2 = q % A.n[2];
+        q /= A.n[2];
+        const int64_t i1 = q % A.n[1];
+        const int64_t i0 = q / A.n[1];
+        const int64_t left = A.n[3] - c;
         const int count = left >= E ? E : (int)left;
         Regs<E> R;
         for (int k = 0; k < kMaxIn; ++k) {
             if (k >= A.prog.n_in) break;
             const uint8_t ty = A.prog.in_ty[k];
+            const int64_t base = i0 * A.in_s[k][0] + i1 * A.in_s[k][1] + i2 * A.in_s[k][2];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 uint32_t v = 0u;
                 if (e < count) {
-                    const int64_t off = r * A.in_s0[k] + (c + e) * A.in_s1[k];
+                    const int64_t off = base + (c + e) * A.in_s[k][3];
                     v = ty == TY_F16 ? (uint32_t) static_cast<const uint16_t *>(A.in[k])[off]
                                      : static_cast<const uint32_t *>(A.in[k])[off];
                 }
@@ -54,10 +61,11 @@ __global__ __launch_bounds__(kGatherBlock) void k_gather(const StridedArgs A)
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < A.prog.n_out) {
                 const uint8_t ty = A.prog.out_ty[k];
+                const int64_t base = i0 * A.out_s[k][0] + i1 * A.out_s[k][1] + i2 * A.out_s[k][2];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     if (e < count) {
-                        const int64_t off = r * A.out_s0[k] + (c + e) * A.out_s1[k];
+                        const int64_t off = base + (c + e) * A.out_s[k][3];
                         if (ty == TY_F16) static_cast<uint16_t *>(A.out[k])[off] = (uint16_t)out[k][e];
                         else static_cast<uint32_t *>(A.out[k])[off] = out[k][e];
                     }

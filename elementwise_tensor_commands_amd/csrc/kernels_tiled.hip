@@ -1,13 +1,17 @@
 // kernels_tiled.hip -- rank-2 evaluation with transposed operands staged
 // through LDS.
 //
-// Logical shape rows x cols.  An operand view maps (r, c) to r*s0 + c*s1
+// Canonical 4-D views (see StridedArgs): dimensions 0 and 1 are batch
+// dimensions, each batch index selects a rows x cols plane (dimensions 2 and
+// 3).  An operand view maps (b0, b1, r, c) to b0*s0 + b1*s1 + r*s2 + c*s3
 // (rocRoller "Design Overview", section "Kernel Graph": each dimension has a
 // size and a stride).  Outputs and "direct" inputs are inner-contiguous
-// (s1 == 1): a row of a tile is one contiguous run.  "Staged" inputs are
-// column-contiguous (s0 == 1, e.g. the transpose of a row-major matrix): a
-// column of a tile is one contiguous run, so reading them along rows would
-// touch one element per run.
+// (s3 == 1): a row of a tile is one contiguous run.  "Staged" inputs are
+// row-contiguous along the plane's rows instead (s2 == 1, e.g. the transpose
+// of a row-major matrix): a column of a tile is one contiguous run, so reading
+// them along rows would touch one element per run.  "Row-constant" inputs have
+// s3 == 0 (broadcast along the columns, e.g. a per-channel bias): one value
+// per row.
 //
 // One work-group (TB = 256 or 512 work-items) owns a TM x TN output tile:
 //   1. For every staged input it reads the TN tile columns as contiguous runs
@@ -73,9 +77,14 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
     static_assert(kSV >= 1 && kP >= 1, "tile too small for the work-group");
     extern __shared__ uint32_t lds[];
 
-    // Tile coordinates (all counts fit in 32 bits: the grid is one dimension).
-    const uint32_t id = blockIdx.x;
+    // Plane and tile coordinates (all counts fit in 32 bits: the grid is one
+    // dimension).  Each plane (batch index) has tiles_r x tiles_c tiles.
     const uint32_t tiles_c = (uint32_t)A.tiles_c, tiles_r = (uint32_t)A.tiles_r;
+    const uint32_t per_plane = tiles_r * tiles_c;
+    const uint32_t plane = blockIdx.x / per_plane;
+    const uint32_t id = blockIdx.x - plane * per_plane;
+    const uint32_t n1 = (uint32_t)A.n[1];
+    const uint32_t b0 = plane / n1, b1 = plane - b0 * n1;
     const uint32_t walk = (uint32_t)A.tile_walk;
     uint32_t tr, tc;
     if (walk <= 1) {
@@ -89,9 +98,13 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
         tc = rem / h;
         tr = b * walk + (rem - tc * h);
     }
+    const int64_t rows = A.n[2], cols = A.n[3];
     const int64_t r0 = (int64_t)tr * TM, c0 = (int64_t)tc * TN;
-    const bool full = (r0 + TM <= A.rows) && (c0 + TN <= A.cols);
+    const bool full = (r0 + TM <= rows) && (c0 + TN <= cols);
     const int t = threadIdx.x;
+    // Element offset of this plane in each operand.
+    auto in_base = [&](int k) { return (int64_t)b0 * A.in_s[k][0] + (int64_t)b1 * A.in_s[k][1]; };
+    auto out_base = [&](int k) { return (int64_t)b0 * A.out_s[k][0] + (int64_t)b1 * A.out_s[k][1]; };
 
     // Direct inputs of every chunk, loaded up front in the specialised kernels
     // (the interpreter keeps one chunk's registers at a time).
@@ -102,7 +115,7 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
     for (int p = 0; p < kP; ++p) {
         const int v = t + TB * p;
         const int rl = v / kRowVec, cl = 4 * (v % kRowVec);
-        count[p] = full ? 4 : (r0 + rl < A.rows ? clamp4(A.cols - (c0 + cl)) : 0);
+        count[p] = full ? 4 : (r0 + rl < rows ? clamp4(cols - (c0 + cl)) : 0);
     }
     auto load_direct = [&](int p) {
         const int v = t + TB * p;
@@ -111,9 +124,20 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
             if (k < EV::n_in(A.prog) && !staged<MASK>(A, k)) {
-                const int64_t off = r * A.in_s0[k] + c;
-                if (full) load_group<4, true, NT>(A.in[k], EV::in_ty(A.prog, k), off, 4, Rp.in[k]);
-                else if (count[p] > 0) load_elems<4, false>(A.in[k], EV::in_ty(A.prog, k), off, count[p], Rp.in[k]);
+                const uint8_t ty = EV::in_ty(A.prog, k);
+                if (MASK == kMaskRuntime && A.in_rowconst[k]) {
+                    // one value per row, the same for the 4 columns
+                    if (count[p] > 0) {
+                        uint32_t one[1];
+                        load_elems<1, false>(A.in[k], ty, in_base(k) + r * A.in_s[k][2], 1, one);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Rp.in[k][e] = one[0];
+                    }
+                    continue;
+                }
+                const int64_t off = in_base(k) + r * A.in_s[k][2] + c;
+                if (full) load_group<4, true, NT>(A.in[k], ty, off, 4, Rp.in[k]);
+                else if (count[p] > 0) load_elems<4, false>(A.in[k], ty, off, count[p], Rp.in[k]);
             }
         }
     };
@@ -133,11 +157,11 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
             for (int j = 0; j < kSV; ++j) {
                 const int v = t + TB * j;
                 const int cl = v / kRunVec, rl = 4 * (v % kRunVec);
-                const int64_t off = (c0 + cl) * A.in_s1[k] + (r0 + rl);
+                const int64_t off = in_base(k) + (c0 + cl) * A.in_s[k][3] + (r0 + rl);
                 if (full) {
                     load_group<4, true, NT>(A.in[k], ty, off, 4, sv[j]);
                 } else {
-                    const int cnt = c0 + cl < A.cols ? clamp4(A.rows - (r0 + rl)) : 0;
+                    const int cnt = c0 + cl < cols ? clamp4(rows - (r0 + rl)) : 0;
                     if (cnt > 0) load_elems<4, false>(A.in[k], ty, off, cnt, sv[j]);
                     else sv[j][0] = sv[j][1] = sv[j][2] = sv[j][3] = 0u;
                 }
@@ -174,7 +198,7 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < EV::n_out(A.prog)) {
-                const int64_t off = r * A.out_s0[k] + c;
+                const int64_t off = out_base(k) + r * A.out_s[k][2] + c;
                 if (full) store_group<4, true, NT>(A.out[k], EV::out_ty(A.prog, k), off, 4, out[k]);
                 else store_elems<4, false, false>(A.out[k], EV::out_ty(A.prog, k), off, count[p], out[k]);
             }

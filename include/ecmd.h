@@ -39,16 +39,19 @@
  *   Select   cond != 0 ? x : y, cond CMD_I32, x and y of one dtype (cmd_select).
  *   Scalars broadcast to every element; a store of a scalar fills the output.
  *
- * Shapes and views: every tensor argument of one launch has the same logical
- * shape -- rank 1 (n) or rank 2 (rows, cols); a rank-1 view counts as (1, n).
- * A view maps index (r, c) to element offset r*stride[0] + c*stride[1] from its
- * base pointer (rank 1: i*stride[0]), following the coordinate-transform model
- * of rocRoller "Design Overview", section "Kernel Graph" (a dimension has a size
- * and a stride; Flatten is the row-major contiguous index).  Strides are in
- * elements and must be >= 0.  A load may use stride 0 (broadcast).  A store view
- * must not map two indexes to one element.  Outputs must not overlap each other,
- * and an output may overlap an input only as the identical view (same pointer,
- * strides and dtype: in place).
+ * Shapes and views: tensor arguments have rank 1 to 4, and every tensor
+ * argument of one launch has the same logical shape once shapes are
+ * right-aligned (a rank-k shape is padded on the left with size-1
+ * dimensions: (n) matches (1, n) and (1, 1, n)).  A view maps index
+ * (i0, ..., i{k-1}) to element offset sum(i_d * stride[d]) from its base
+ * pointer, following the coordinate-transform model of rocRoller "Design
+ * Overview", section "Kernel Graph" (a dimension has a size and a stride;
+ * Flatten is the row-major contiguous index).  Strides are in elements and
+ * must be >= 0.  A load may use stride 0 on any dimension (broadcast).  A store
+ * view must not map two indexes to one element.  Outputs must not overlap each
+ * other, and an output may overlap an input only as the identical view (same
+ * pointer, strides and dtype: in place).  The element order in which the
+ * library visits the shape is its own choice: results do not depend on it.
  *
  * Errors follow one rule (Silk "AMDGPU Backend", section "AQL Dispatch
  * Packets": everything is validated before any runtime queue sees work): every
@@ -130,6 +133,7 @@ typedef int32_t cmd_tag;
 #define CMD_MAX_OPS 32     /* E_ operations that a store depends on                        */
 #define CMD_MAX_LIVE 8     /* per-element temporaries alive at once after lowering         */
 #define CMD_MAX_NODES 256  /* everything appended to one Command                           */
+#define CMD_MAX_RANK 4     /* dimensions of one view                                      */
 
 /* One CommandArgument value, bound at launch.
  *   kind   CMD_ARG_TENSOR or CMD_ARG_SCALAR; must match the declaration.
@@ -137,8 +141,8 @@ typedef int32_t cmd_tag;
  *   ptr    tensor: device pointer to element (0, 0) of the view (HIP device
  *          memory of the current device).  May be NULL only if the shape has
  *          no elements.
- *   size   tensor: logical sizes; rank 1 uses size[0] only.
- *   stride tensor: element strides, >= 0; rank 1 uses stride[0] only.
+ *   size   tensor: logical sizes of the view's rank k dimensions, size[0..k-1].
+ *   stride tensor: element strides, >= 0, stride[0..k-1].
  *   bits   scalar: the value's bit pattern -- binary32 bits, int32 two's
  *          complement, or binary16 bits in the low 16 bits.
  */
@@ -146,8 +150,8 @@ typedef struct {
     int32_t kind;
     int32_t dtype;
     void *ptr;
-    int64_t size[2];
-    int64_t stride[2];
+    int64_t size[4];
+    int64_t stride[4];
     uint32_t bits;
     uint32_t reserved;   /* must be 0 */
 } cmd_arg;
@@ -158,7 +162,7 @@ int cmd_create(cmd_t *out);
 /* Destroy a handle.  NULL is a no-op.  The caller must not use the handle again. */
 int cmd_destroy(cmd_t h);
 
-/* Append a tensor load of element type dtype and rank 1 or 2 (rocRoller "Design
+/* Append a tensor load of element type dtype and rank 1 to 4 (rocRoller "Design
  * Overview", section "Operations": loads allocate the CommandArguments that
  * describe the data).  *tag receives the loaded value's tag and *arg_index the
  * CommandArgument's index.  Either output pointer may be NULL. */
@@ -183,7 +187,7 @@ int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, 
  * which is the result's. */
 int cmd_select(cmd_t h, cmd_tag cond, cmd_tag x, cmd_tag y, cmd_tag *tag);
 
-/* Append a store of value's tag to an output tensor of rank 1 or 2; the
+/* Append a store of value's tag to an output tensor of rank 1 to 4; the
  * output's dtype is the value's dtype (rocRoller "Design Overview", section
  * "Operations": stores allocate CommandArguments too). */
 int cmd_store(cmd_t h, cmd_tag value, int32_t rank, int32_t *arg_index);
@@ -205,15 +209,19 @@ typedef struct {
     int32_t elems_per_thread;
     int64_t grid;          /* work-groups                                                  */
     int32_t block;         /* work-items per work-group                                    */
-    int32_t lds_bytes;     /* static LDS per work-group                                    */
-    int64_t rows, cols;    /* logical shape                                                */
+    int32_t lds_bytes;     /* LDS per work-group                                           */
+    int32_t dims;          /* dimensions left after dropping size-1 dimensions and merging */
+                           /* the contiguous ones (1..4)                                   */
+    int32_t reserved;
+    int64_t size[4];       /* those dimensions' sizes, padded on the left with 1s          */
     char kernel[64];       /* kernel name                                                  */
 } cmd_plan_info;
 
 #define CMD_PATH_NONE 0    /* no elements: nothing would be launched   */
-#define CMD_PATH_LINEAR 1  /* every view is flat contiguous            */
-#define CMD_PATH_TILED 2   /* rank 2, inner-contiguous and transposed views, LDS staged */
-#define CMD_PATH_GATHER 3  /* any other strides                        */
+#define CMD_PATH_LINEAR 1  /* every view is flat contiguous (in the library's element order) */
+#define CMD_PATH_TILED 2   /* planes of inner-contiguous, transposed (LDS-staged) and        */
+                           /* row-broadcast views, with up to two batch dimensions           */
+#define CMD_PATH_GATHER 3  /* any other strides                                              */
 
 /* Validate args exactly as cmd_launch does and describe the launch without
  * making it.  Host only: no HIP call.  Freezes the Command like cmd_launch. */

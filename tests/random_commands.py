@@ -84,3 +84,84 @@ def _random_inputs(rng, spec, shape):
         elif st[0] == "scalar":
             out.append(np.float32(rng.standard_normal()) if st[1] == "f32" else np.int32(rng.integers(-1000, 1000)))
     return out
+
+
+def random_view(rng, storage_fill, shape, dtype, broadcast=False, align=False):
+    """A random view of logical ``shape`` cut from a fresh contiguous storage:
+    the storage holds the dimensions in a random order, each padded and
+    started at a random offset; broadcast views also get stride 0 along a
+    random subset of dimensions.  ``align`` keeps paddings and offsets at
+    multiples of 4 elements.  Returns (view, storage); ``storage_fill(shape)``
+    makes the storage's contents."""
+    from numpy.lib.stride_tricks import as_strided
+    r = len(shape)
+    perm = rng.permutation(r)                  # storage dimension i holds logical dimension perm[i]
+    step = 4 if align else 1
+    starts = [int(rng.choice([0, 0, 1])) * step for _ in range(r)]
+    pads = [int(rng.choice([0, 0, 1, 3])) * step for _ in range(r)]
+    st_shape = tuple(shape[p] + starts[i] + pads[i] for i, p in enumerate(perm))
+    storage = np.ascontiguousarray(storage_fill(st_shape).astype(dtype))
+    v = storage[tuple(slice(starts[i], starts[i] + shape[p]) for i, p in enumerate(perm))]
+    v = v.transpose(np.argsort(perm))
+    if broadcast:
+        zero = rng.random(r) < 0.35
+        strides = tuple(0 if z else s for z, s in zip(zero, v.strides))
+        v = as_strided(v, shape=v.shape, strides=strides, writeable=False)
+    return v, storage
+
+
+_NPD = {"f16": np.float16, "f32": np.float32, "i32": np.int32}
+
+
+def _arg_dtypes(spec):
+    """Input argument dtypes (loads and scalars) and output dtypes, in order."""
+    dts, ins, outs = {}, [], []
+    for name, st in spec:
+        if st[0] in ("load", "scalar"):
+            dts[name] = st[1]
+            ins.append(st[1])
+        elif st[0] == "cvt":
+            dts[name] = st[2]
+        elif st[0] == "select":
+            dts[name] = dts[st[2]]
+        elif st[0] in ("eq", "ne", "lt", "le", "gt", "ge", "ltu", "leu", "gtu", "geu"):
+            dts[name] = "i32"
+        elif st[0] == "store":
+            outs.append(dts[st[1]])
+        else:
+            dts[name] = dts[st[1]]
+    return ins, outs
+
+
+def _fill_for(rng, dt):
+    if dt == "i32":
+        return lambda sh: rng.integers(-2**31, 2**31, sh, dtype=np.int64).astype(np.int32)
+
+    def f(sh):
+        b = rng.integers(0, 2**32, sh, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        return np.where(rng.random(sh) < 0.5, rng.standard_normal(sh).astype(np.float32) * 100, b)
+    return f
+
+
+SIZES = [1, 2, 3, 4, 5, 8, 12, 16, 33, 64, 68, 100, 132, 260]
+
+
+def random_view_case(seed):
+    """A random Command of random rank over random views (inputs only)."""
+    rng = np.random.default_rng(5000 + seed)
+    r = int(rng.integers(1, 5))
+    while True:
+        shape = tuple(int(rng.choice(SIZES)) for _ in range(r))
+        if np.prod(shape) <= 300_000:
+            break
+    spec = _random_spec(rng, int(rng.integers(1, 4)), int(rng.integers(1, 7)), r)
+    in_dt, out_dt = _arg_dtypes(spec)
+    align = rng.random() < 0.6
+    ins = []
+    for (_, st), dt in zip([s for s in spec if s[1][0] in ("load", "scalar")], in_dt):
+        if st[0] == "scalar":
+            ins.append(np.float32(rng.standard_normal()) if dt == "f32" else np.int32(rng.integers(-1000, 1000)))
+        else:
+            ins.append(random_view(rng, _fill_for(rng, dt), shape, _NPD[dt], broadcast=True, align=align))
+    outs = [random_view(rng, _fill_for(rng, dt), shape, _NPD[dt], align=align) for dt in out_dt]
+    return spec, ins, outs

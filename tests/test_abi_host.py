@@ -29,9 +29,10 @@ def test_library_exports_every_declared_function():
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(E.cmd_arg) == 56
-    assert E.cmd_arg.ptr.offset == 8 and E.cmd_arg.size.offset == 16 and E.cmd_arg.bits.offset == 48
-    assert ctypes.sizeof(E.cmd_plan_info) == 112
+    assert ctypes.sizeof(E.cmd_arg) == 88
+    assert E.cmd_arg.ptr.offset == 8 and E.cmd_arg.size.offset == 16 and E.cmd_arg.bits.offset == 80
+    assert ctypes.sizeof(E.cmd_plan_info) == 136
+    assert E.cmd_plan_info.size.offset == 40 and E.cmd_plan_info.kernel.offset == 72
 
 
 def _t(*shape, dtype=torch.float32):
@@ -69,7 +70,9 @@ def test_build_errors():
     _err(lambda: c.select(i, x, 77), "CMD_E_TAG")
     assert c.cmp("gtu", i, i) >= 0 and c.select(i, h, h) >= 0 and c.abs(h) >= 0 and c.max(x, x) >= 0
     _err(lambda: c.load(7), "CMD_E_DTYPE")
-    _err(lambda: c.load("f32", 3), "CMD_E_LIMIT")
+    _err(lambda: c.load("f32", 5), "CMD_E_LIMIT")
+    _err(lambda: c.load("f32", 0), "CMD_E_LIMIT")
+    assert c.load("f32", 3) >= 0 and c.load("f32", 4) >= 0
     _err(lambda: c.store(99), "CMD_E_TAG")
     assert c.neg(h) >= 0 and c.cvt(h, "i32") >= 0
 
@@ -255,20 +258,21 @@ def test_commutative_operands_canonical():
 @pytest.mark.parametrize("wl,kernel", [("add_f32", "linear_add_f32"), ("int_fused", "linear_int_fused"),
                                        ("axpby_f32", "linear_axpby_f32"),
                                        ("mixed_two_out", "linear_mixed_two_out"),
-                                       ("transposed_2d", "tiled_add_scaled_f32")])
-def test_workloads_select_specialised_kernels(wl, kernel):
+                                       ("transposed_2d", "tiled_add_scaled_f32"),
+                                       ("batched_transpose", "tiled_add_scaled_f32"),
+                                       ("bias_nchw", "tiled_generic")])
+def test_workloads_select_their_kernels(wl, kernel):
     spec = W.WORKLOADS[wl]["spec"]
     n = 1 << 12 if wl != "transposed_2d" else 256
-    vals, extra = W.make_inputs(wl, n)
-    tv = [torch.from_numpy(v) if isinstance(v, np.ndarray) else v for v in vals]
-    if wl == "transposed_2d":
-        tv[0] = torch.from_numpy(extra["X_storage"])[:, :n]
-        tv[1] = torch.from_numpy(extra["Y"]).t()
+    small = {"batched_transpose": (3, 64, 96), "bias_nchw": (2, 8, 4, 16)}
+    vals, extra = W.make_inputs(wl, n, shape=small.get(wl))
+    n = None if wl in small else n
+    tv = W.to_torch(vals, extra, "cpu")
     _, outs = arg_dtypes(spec)
-    shape = (n, n) if wl == "transposed_2d" else (n,)
+    shape = W.shape_of(wl, n, small.get(wl))
     o = [torch.empty(shape, dtype={"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}[d]) for d in outs]
     plan = E.from_spec(spec).plan(*tv, *o)
-    assert plan["kernel"] == kernel and plan["specialised"] and plan["vector"]
+    assert plan["kernel"] == kernel and plan["specialised"] == (wl != "bias_nchw") and plan["vector"]
 
 
 def test_geometry_rules():

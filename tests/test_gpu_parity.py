@@ -24,20 +24,14 @@ ULP = {"mixed_two_out": 2}
 
 
 def _gpu_values(wl, vals, extra, n):
-    out = []
-    for v in vals:
-        out.append(to_dev(v) if isinstance(v, np.ndarray) else v)
-    if wl == "transposed_2d":
-        out[0] = to_dev(extra["X_storage"])[:, :n]
-        out[1] = to_dev(extra["Y"]).t()
-    return out
+    return W.to_torch(vals, extra, dev())
 
 
 def _check_workload(wl, n, generic=False):
     spec = W.WORKLOADS[wl]["spec"]
     vals, extra = W.make_inputs(wl, n)
     _, outs = arg_dtypes(spec)
-    shape = (n, n) if wl == "transposed_2d" else (n,)
+    shape = W.shape_of(wl, n)
     if any(isinstance(v, np.ndarray) for v in vals):
         ref = run_oracle(spec, vals)
     else:                                  # no tensor input: the outputs give the shape

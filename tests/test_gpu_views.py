@@ -1,0 +1,164 @@
+"""Rank-1 to rank-4 views on the GPU, compared with the oracle.
+
+Every case cuts its views from contiguous storages (permuted, padded, offset
+and, for loads, broadcast with stride 0), runs the Command on the GPU over
+device copies of the storages and in the oracle over host copies, and compares
+the whole output storages bit for bit: the elements a store view covers must
+match and every other element must be left as it was."""
+import os
+
+import numpy as np
+import pytest
+import torch
+from numpy.lib.stride_tricks import as_strided
+
+import workloads as W
+from gpu_util import NPD, compare, dev, run_oracle
+from random_commands import random_view_case
+from specs import arg_dtypes
+
+pytestmark = pytest.mark.gpu
+
+
+def _recut(view, storage, copy):
+    """The view of ``storage`` rebuilt over ``copy`` (same offset and strides)."""
+    off, strides = W.layout(view, storage)
+    isz = copy.itemsize
+    return as_strided(copy.reshape(-1)[off:], shape=view.shape, strides=tuple(s * isz for s in strides))
+
+
+def _device(view, storage):
+    off, strides = W.layout(view, storage)
+    flat = torch.from_numpy(np.ascontiguousarray(storage).reshape(-1)).to(dev())
+    return flat, flat.as_strided(view.shape, strides, off)
+
+
+def run_views(spec, inputs, outputs, generic=False, what=""):
+    """inputs: (view, storage) pairs for loads, plain values for scalars, in
+    declaration order; outputs: (view, storage) pairs in store order.
+    Returns the plan the GPU launch used."""
+    import elementwise_tensor_commands_amd as ecmd
+    host_out = [st.copy() for _, st in outputs]
+    ref_views = [_recut(v, st, c) for (v, st), c in zip(outputs, host_out)]
+    vals = [x[0] if isinstance(x, tuple) else x for x in inputs]
+    run_oracle(spec, vals, outputs=ref_views)
+    gin = [(_device(*x)[1] if isinstance(x, tuple) else x) for x in inputs]
+    gflat, gout = [], []
+    for v, st in outputs:
+        f, g = _device(v, st)
+        gflat.append(f)
+        gout.append(g)
+    cmd = ecmd.from_spec(spec)
+    old = os.environ.get("ECMD_FORCE_GENERIC")
+    if generic:
+        os.environ["ECMD_FORCE_GENERIC"] = "1"
+    try:
+        plan = cmd.plan(*gin, *gout)
+        print("    %s: %s dims=%d size=%s" % (what, plan["kernel"], plan["dims"], plan["size"]), flush=True)
+        cmd.launch(*gin, *gout)
+        torch.cuda.synchronize()
+    finally:
+        if generic:
+            if old is None:
+                del os.environ["ECMD_FORCE_GENERIC"]
+            else:
+                os.environ["ECMD_FORCE_GENERIC"] = old
+    for k, (f, ref) in enumerate(zip(gflat, host_out)):
+        compare(f.cpu().numpy(), ref.reshape(-1), 0, "%s out%d (%s)" % (what, k, plan["kernel"]))
+    return plan
+
+
+def _workload_case(wl, shape):
+    spec = W.WORKLOADS[wl]["spec"]
+    vals, extra = W.make_inputs(wl, shape=shape)
+    ins = [(v, st) if st is not None else v for v, st in zip(vals, extra["storage"])]
+    _, outs = arg_dtypes(spec)
+    rng = np.random.default_rng(7)
+    out_pairs = []
+    for d in outs:
+        st = rng.integers(0, 2**32, shape, dtype=np.uint64).astype(np.uint32).view(np.float32).astype(NPD[d])
+        out_pairs.append((st, st))
+    return spec, ins, out_pairs
+
+
+@pytest.mark.parametrize("generic", [False, True])
+@pytest.mark.parametrize("wl,shape", [
+    ("batched_transpose", (3, 200, 300)), ("batched_transpose", (2, 64, 64)), ("batched_transpose", (5, 33, 517)),
+    ("batched_transpose", (1, 1, 1)), ("batched_transpose", (4, 1, 260)), ("batched_transpose", (7, 260, 4)),
+    ("bias_nchw", (3, 37, 5, 67)), ("bias_nchw", (2, 8, 1, 1)), ("bias_nchw", (1, 1, 1, 1)),
+    ("bias_nchw", (2, 3, 16, 16)), ("bias_nchw", (2, 70, 9, 12))])
+def test_workload_shapes(wl, shape, generic):
+    spec, ins, outs = _workload_case(wl, shape)
+    plan = run_views(spec, ins, outs, generic, "%s %s" % (wl, shape))
+    if generic:
+        assert not plan["specialised"]
+
+
+@pytest.mark.parametrize("tile", ["64x64", "32x256x512", "128x128", "64x128x512"])
+def test_batched_transpose_tiles(tile):
+    """Every instantiated tile of the specialised kernel over several planes
+    with ragged edges."""
+    old = os.environ.get("ECMD_TILE")
+    os.environ["ECMD_TILE"] = tile
+    try:
+        spec, ins, outs = _workload_case("batched_transpose", (3, 196, 516))
+        plan = run_views(spec, ins, outs, False, "tile %s" % tile)
+    finally:
+        if old is None:
+            del os.environ["ECMD_TILE"]
+        else:
+            os.environ["ECMD_TILE"] = old
+    assert plan["specialised"] and plan["path"] == "tiled"
+
+
+@pytest.mark.parametrize("wl", ["batched_transpose", "bias_nchw"])
+def test_full_size_views(wl):
+    """The full shapes the benchmark times, in its launch configuration,
+    compared with the oracle on every element."""
+    shape = W.WORKLOADS[wl]["shape"]
+    print("  full size %s %s" % (wl, shape), flush=True)
+    spec = W.WORKLOADS[wl]["spec"]
+    vals, extra = W.make_inputs(wl)
+    ref = run_oracle(spec, vals)
+    gin = W.to_torch(vals, extra, dev())
+    import elementwise_tensor_commands_amd as ecmd
+    cmd = ecmd.from_spec(spec)
+    out = torch.empty(shape, dtype=torch.float32, device=dev())
+    plan = cmd.plan(*gin, out)
+    cmd.launch(*gin, out)
+    torch.cuda.synchronize()
+    compare(out.cpu().numpy(), ref[0], 0, "%s full (%s)" % (wl, plan["kernel"]))
+    assert plan["path"] == "tiled"
+
+
+def test_staged_direct_and_row_constant_together():
+    """One Command with a direct binary16 input, a staged (transposed) fp32
+    input and a row-constant int32 input over a batch of planes."""
+    B, R, C = 3, 132, 260
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((B, R, C)).astype(np.float16)
+    y = rng.standard_normal((B, C, R)).astype(np.float32) * 100
+    k = rng.integers(-50, 50, (B, R), dtype=np.int32)
+    kv = as_strided(k, shape=(B, R, C), strides=(k.strides[0], k.strides[1], 0), writeable=False)
+    spec = [("x", ("load", "f16", 3)), ("y", ("load", "f32", 3)), ("k", ("load", "i32", 3)),
+            ("xf", ("cvt", "x", "f32")), ("kf", ("cvt", "k", "f32")), ("p", ("mul", "xf", "y")),
+            ("q", ("add", "p", "kf")), ("h", ("cvt", "q", "f16")), ("kk", ("mul", "k", "k")),
+            ("o0", ("store", "h", 3)), ("o1", ("store", "kk", 3))]
+    o0 = np.zeros((B, R, C), np.float16)
+    o1 = np.zeros((B, R, C), np.int32)
+    plan = run_views(spec, [(x, x), (y.transpose(0, 2, 1), y), (kv, k)], [(o0, o0), (o1, o1)], False, "mixed")
+    assert plan["path"] == "tiled" and plan["lds_bytes"] > 0
+
+
+def test_empty_rank4_leaves_outputs_alone():
+    spec, ins, outs = _workload_case("bias_nchw", (3, 0, 5, 7))
+    run_views(spec, ins, outs, False, "empty")
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_views(seed):
+    spec, ins, outs = random_view_case(seed)
+    run_views(spec, ins, outs, False, "seed %d" % seed)
+    if seed % 4 == 0:
+        spec, ins, outs = random_view_case(seed)
+        run_views(spec, ins, outs, True, "seed %d generic" % seed)

@@ -569,3 +569,26 @@ def test_rank_mixing_right_aligned(oracle_mod):
     assert o.shape == (1, 1, 7) and np.array_equal(o.ravel(), x * 3)
     with pytest.raises(oracle_mod.OracleError):
         oracle_mod.from_spec(spec).run(x, np.zeros((1, 2, 7), np.float32))
+
+
+@pytest.mark.parametrize("shape", [(3, 20, 36), (1, 1, 1), (2, 7, 130)])
+def test_batched_transpose_workload_matches_numpy(oracle_mod, shape):
+    """out[b] = X[b] + 2 * Y[b]^T: numpy's float32 operations round each
+    product and sum once, and 2*y is exact."""
+    vals, extra = W.make_inputs("batched_transpose", shape=shape)
+    (o,) = oracle_mod.from_spec(W.BATCHED_TRANSPOSE).run(*vals)
+    Y = extra["storage"][1]
+    ref = vals[0] + np.float32(2) * np.transpose(Y, (0, 2, 1))
+    assert np.array_equal(o.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(2, 5, 3, 7), (1, 1, 1, 1), (3, 16, 1, 9)])
+def test_bias_nchw_workload_matches_numpy(oracle_mod, shape):
+    """out = x * scale[c] + bias[c] through stride-0 views, against numpy's
+    own broadcasting of the per-channel arrays."""
+    vals, extra = W.make_inputs("bias_nchw", shape=shape)
+    assert vals[1].strides[0] == 0 and vals[1].strides[2:] == (0, 0)
+    (o,) = oracle_mod.from_spec(W.BIAS_NCHW).run(*vals)
+    _, scale, bias = extra["storage"]
+    ref = vals[0] * scale.reshape(1, -1, 1, 1) + bias.reshape(1, -1, 1, 1)
+    assert np.array_equal(o.view(np.uint32), ref.view(np.uint32))

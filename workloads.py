@@ -7,9 +7,11 @@ the oracle and the GPU library each turn a spec into their own Command with
 their own code.
 
 Spec format: a list of ``(name, step)`` pairs.  ``step`` is one of
-``("load", dtype, rank)``, ``("scalar", dtype)``, ``("add"|"sub"|"mul", a, b)``,
-``("neg", a)``, ``("cvt", a, dtype)`` or ``("store", value, rank)``, where ``a``,
-``b`` and ``value`` name earlier steps.  CommandArguments are the loads,
+``("load", dtype, rank)``, ``("scalar", dtype)``, a binary operation
+``(op, a, b)`` (add sub mul min max and the comparisons eq ne lt le gt ge ltu
+leu gtu geu), ``("neg"|"abs", a)``, ``("cvt", a, dtype)``,
+``("select", cond, a, b)`` or ``("store", value, rank)``, where ``a``, ``b``,
+``cond`` and ``value`` name earlier steps.  CommandArguments are the loads,
 scalars and stores in the order they appear.
 
 Generators follow one recipe: ``np.random.default_rng(seed)`` (PCG64), with
@@ -20,7 +22,7 @@ from __future__ import annotations
 import numpy as np
 
 # ---------------------------------------------------------------------------
-# The five Commands.
+# The Commands.
 
 ADD_F32 = [
     ("x", ("load", "f32", 1)),
@@ -98,6 +100,27 @@ FILL_F32 = [
     ("out", ("store", "s", 1)),
 ]
 
+# Views of rank 3 and 4.  A batch of transposed planes: out[b] = X[b] + alpha * Y[b]^T.
+BATCHED_TRANSPOSE = [
+    ("X", ("load", "f32", 3)),
+    ("Yt", ("load", "f32", 3)),
+    ("alpha", ("scalar", "f32")),
+    ("ay", ("mul", "alpha", "Yt")),
+    ("o", ("add", "X", "ay")),
+    ("out", ("store", "o", 3)),
+]
+
+# A per-channel affine map over an NCHW activation: scale and bias hold one
+# value per channel and are read through stride-0 (broadcast) views.
+BIAS_NCHW = [
+    ("x", ("load", "f32", 4)),
+    ("scale", ("load", "f32", 4)),
+    ("bias", ("load", "f32", 4)),
+    ("xs", ("mul", "x", "scale")),
+    ("o", ("add", "xs", "bias")),
+    ("out", ("store", "o", 4)),
+]
+
 WORKLOADS = {
     "add_f32": dict(index=0, spec=ADD_F32, n=65536,
                     label="z = x + y, fp32, n=65536 contiguous"),
@@ -117,6 +140,12 @@ WORKLOADS = {
     "classify_u32": dict(index=6, spec=CLASSIFY_U32, n=1 << 28,
                          label="out = (x >u t) ? 1 : 0, int32 x uniform over all 2^32 patterns, t = 2^31, n=2^28"),
     "fill_f32": dict(index=7, spec=FILL_F32, n=1 << 28, label="out = s, fp32, s = 1.25, n=2^28"),
+    # Rank-3 and rank-4 views.  ``shape`` is the logical shape; ``varies``
+    # lists, for each broadcast load, the dimensions its storage spans.
+    "batched_transpose": dict(index=8, spec=BATCHED_TRANSPOSE, shape=(64, 2048, 2048),
+                              label="out[b,i,j] = X[b,i,j] + alpha*Y[b,j,i], fp32, 64 x 2048 x 2048, alpha=2"),
+    "bias_nchw": dict(index=9, spec=BIAS_NCHW, shape=(32, 256, 128, 256), varies={"scale": (1,), "bias": (1,)},
+                      label="out = x*scale[c] + bias[c], fp32 NCHW 32 x 256 x 128 x 256, per-channel broadcast"),
 }
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
@@ -127,7 +156,32 @@ SCALARS = {
     "transposed_2d": {"alpha": np.float32(2.0)},
     "classify_u32": {"t": np.int32(-2**31)},          # 0x80000000 as unsigned
     "fill_f32": {"s": np.float32(1.25)},
+    "batched_transpose": {"alpha": np.float32(2.0)},
 }
+
+
+def shape_of(workload: str, n: int | None = None, shape=None) -> tuple:
+    """Logical shape: ``shape`` (or the workload's) for the rank-3/4 workloads,
+    (n, n) for the 2-D one, (n,) otherwise."""
+    w = WORKLOADS[workload]
+    if "shape" in w:
+        return tuple(w["shape"] if shape is None else shape)
+    n = w["n"] if n is None else n
+    return (n, n) if workload == "transposed_2d" else (n,)
+
+
+def layout(view: np.ndarray, storage: np.ndarray):
+    """(element offset, element strides) of ``view`` inside the contiguous
+    ``storage`` it was cut from, for rebuilding the same view over a device
+    copy of the storage."""
+    isz = storage.itemsize
+    off = view.__array_interface__["data"][0] - storage.__array_interface__["data"][0]
+    assert storage.flags.c_contiguous and off % isz == 0 and off >= 0
+    strides = tuple(st // isz for st in view.strides)
+    assert all(st * isz == b for st, b in zip(strides, view.strides))
+    span = off // isz + sum((sz - 1) * st for sz, st in zip(view.shape, strides)) if view.size else 0
+    assert span < storage.size or view.size == 0
+    return off // isz, strides
 
 
 def seed_of(workload: str) -> int:
@@ -154,7 +208,7 @@ def _uniform_pm4_f16(rng, n):
 
 
 def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
-                row_pad: int = 64):
+                row_pad: int = 64, shape=None):
     """Host inputs for one workload, in declaration order.
 
     Returns ``(values, extra)``: ``values`` is the list of input argument values
@@ -162,10 +216,13 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
     ``values[0]`` is the X *view* (a slice of a padded row-major storage whose
     padding is NaN) and ``values[1]`` is the transposed view ``Y.T`` of a
     contiguous Y; ``extra`` holds the backing storages.  ``n`` overrides the
-    length (the 2-D side length for the 2-D workload).
+    length (the 2-D side length for the 2-D workload) and ``shape`` the shape
+    of the rank-3/4 workloads.  ``extra["storage"]`` lists, per input value,
+    the contiguous array a view was cut from (the value itself when it is
+    contiguous, None for scalars); ``layout`` gives the view inside it.
     """
     w = WORKLOADS[workload]
-    n = w["n"] if n is None else n
+    n = w.get("n") if n is None else n
     rng = np.random.default_rng(seed_of(workload) if seed is None else seed)
     sc = SCALARS.get(workload, {})
     extra = {}
@@ -191,26 +248,48 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
         xs = np.full((rows, cols + row_pad), np.nan, dtype=np.float32)
         xs[:, :cols] = _uniform_pm1_f32(rng, (rows, cols))
         y = _uniform_pm1_f32(rng, (cols, rows))
-        extra = {"X_storage": xs, "Y": y}
+        extra = {"X_storage": xs, "Y": y, "storage": [xs, y, None]}
         vals = [xs[:, :cols], y.T, sc["alpha"]]
+        return vals, extra
+    elif workload == "batched_transpose":
+        b, r, c = shape_of(workload, shape=shape)
+        x = _uniform_pm1_f32(rng, (b, r, c))
+        y = _uniform_pm1_f32(rng, (b, c, r))
+        extra = {"storage": [x, y, None]}
+        return [x, y.transpose(0, 2, 1), sc["alpha"]], extra
+    elif workload == "bias_nchw":
+        shp = shape_of(workload, shape=shape)
+        x = _uniform_pm1_f32(rng, shp)
+        scale = rng.standard_normal(shp[1], dtype=np.float32)
+        bias = rng.standard_normal(shp[1], dtype=np.float32)
+        per_channel = lambda v: np.broadcast_to(v.reshape(1, -1, 1, 1), shp)
+        extra = {"storage": [x, scale, bias]}
+        return [x, per_channel(scale), per_channel(bias)], extra
     else:
         raise KeyError(workload)
+    extra["storage"] = [v if isinstance(v, np.ndarray) else None for v in vals]
     return vals, extra
 
 
-def algorithmic_bytes(workload: str, n: int | None = None) -> int:
-    """Logical elements x (sum of input element sizes + sum of output element
-    sizes); row padding and scalars are not counted."""
+def algorithmic_read_write(workload: str, n: int | None = None, shape=None):
+    """(bytes read, bytes written) by one launch: every tensor's distinct
+    elements x its element size, summed over the loads and over the stores --
+    logical elements for ordinary views, the stored elements for broadcast
+    loads; row padding and scalars are not counted."""
     w = WORKLOADS[workload]
-    n = w["n"] if n is None else n
-    elems = n * n if workload == "transposed_2d" else n
+    shp = shape_of(workload, n, shape)
+    elems = int(np.prod(shp, dtype=np.int64))
+    varies = w.get("varies", {})
     size = {"f16": 2, "f32": 4, "i32": 4}
     dt = {}
-    per = 0
+    rd = wr = 0
     for name, st in w["spec"]:
         if st[0] == "load":
             dt[name] = st[1]
-            per += size[st[1]]
+            if name in varies:
+                rd += size[st[1]] * int(np.prod([shp[d] for d in varies[name]], dtype=np.int64))
+            else:
+                rd += size[st[1]] * elems
         elif st[0] == "scalar":
             dt[name] = st[1]
         elif st[0] in ("add", "sub", "mul", "neg", "abs", "min", "max"):
@@ -222,11 +301,30 @@ def algorithmic_bytes(workload: str, n: int | None = None) -> int:
         elif st[0] == "cvt":
             dt[name] = st[2]
         elif st[0] == "store":
-            per += size[dt[st[1]]]
-    return elems * per
+            wr += size[dt[st[1]]] * elems
+    return rd, wr
 
 
-def elements(workload: str, n: int | None = None) -> int:
-    w = WORKLOADS[workload]
-    n = w["n"] if n is None else n
-    return n * n if workload == "transposed_2d" else n
+def algorithmic_bytes(workload: str, n: int | None = None, shape=None) -> int:
+    """Bytes read + bytes written by one launch (see algorithmic_read_write)."""
+    return sum(algorithmic_read_write(workload, n, shape))
+
+
+def elements(workload: str, n: int | None = None, shape=None) -> int:
+    return int(np.prod(shape_of(workload, n, shape), dtype=np.int64))
+
+
+def to_torch(vals, extra, device):
+    """The input values as torch tensors on ``device``: each storage is copied
+    once and every view is rebuilt over the copy with the same offset and
+    strides (broadcast views keep their stride 0).  Scalars pass through."""
+    import torch
+    out = []
+    for v, st in zip(vals, extra["storage"]):
+        if st is None:
+            out.append(v)
+            continue
+        off, strides = layout(v, st)
+        flat = torch.from_numpy(np.ascontiguousarray(st).reshape(-1)).to(device)
+        out.append(flat.as_strided(v.shape, strides, off))
+    return out
