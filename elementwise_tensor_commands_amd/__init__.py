@@ -29,8 +29,8 @@ E_ADD, E_SUB, E_MUL, E_NEG, E_CVT = 1, 2, 3, 4, 5
 E_CMP = {"eq": 6, "ne": 7, "lt": 8, "le": 9, "gt": 10, "ge": 11, "ltu": 12, "leu": 13, "gtu": 14, "geu": 15}
 E_MIN, E_MAX, E_ABS, E_SELECT = 16, 17, 18, 19
 ARG_TENSOR, ARG_SCALAR = 1, 2
-PATH_NONE, PATH_LINEAR, PATH_TILED, PATH_GATHER = 0, 1, 2, 3
-PATH_NAMES = {0: "none", 1: "linear", 2: "tiled", 3: "gather"}
+PATH_NONE, PATH_LINEAR, PATH_TILED, PATH_GATHER, PATH_ROWS = 0, 1, 2, 3, 4
+PATH_NAMES = {0: "none", 1: "linear", 2: "tiled", 3: "gather", 4: "rows"}
 STATUS = {
     0: "CMD_OK", -1: "CMD_E_ARG", -2: "CMD_E_TAG", -3: "CMD_E_DTYPE", -4: "CMD_E_SHAPE",
     -5: "CMD_E_STRIDE", -6: "CMD_E_ALIAS", -7: "CMD_E_LIMIT", -8: "CMD_E_NOSTORE",

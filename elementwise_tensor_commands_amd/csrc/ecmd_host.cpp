@@ -79,6 +79,7 @@ struct Selection {
     int walk = 1;
     int64_t tiles_r = 0, tiles_c = 0;
     uint8_t rowconst[kMaxIn] = {};
+    int64_t n_vec = 0;
     Canon cn;
     int n_staged = 0;
     uint8_t staged[kMaxIn] = {};
@@ -296,6 +297,17 @@ const char *linear_name(int variant)
     ECMD_LINEAR_SPECIALISED(ECMD_NAME)
 #undef ECMD_NAME
     return "linear_generic";
+}
+
+const char *rows_name(int variant)
+{
+    int k = 0;
+#define ECMD_NAME(name, prog) \
+    if (variant == k) return "rows_" #name; \
+    ++k;
+    ECMD_LINEAR_SPECIALISED(ECMD_NAME)
+#undef ECMD_NAME
+    return "rows_generic";
 }
 
 // ---------------------------------------------------------------------------
@@ -589,6 +601,53 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         S.name = S.vec ? linear_name(S.variant) : "linear_generic_unaligned";
         return;
     }
+    // Rows: outputs unit-stride along dimension 3, inputs unit-stride or
+    // constant along it, vectors aligned in every row.
+    {
+        auto row_aligned = [&](const View &v, const int64_t (&st)[4]) {
+            bool ok = aligned(v.ptr, 4 * esize(v.dtype));
+            for (int d = 0; d < 3 && ok; ++d)
+                if (C.n[d] > 1) ok = st[d] % 4 == 0;
+            return ok;
+        };
+        bool rows = true;
+        uint8_t rowconst[kMaxIn] = {};
+        for (int k = 0; k < P.n_out && rows; ++k) rows = C.out_s[k][3] == 1 && row_aligned(B.out[k], C.out_s[k]);
+        for (int k = 0; k < P.n_in && rows; ++k) {
+            if (C.in_s[k][3] == 0) rowconst[k] = 1;
+            else rows = C.in_s[k][3] == 1 && row_aligned(B.in[k], C.in_s[k]);
+        }
+        const int64_t per_row = (C.n[3] + 3) / 4;
+        const int64_t n_vec = C.n[0] * C.n[1] * C.n[2] * per_row;
+        if (rows && n_vec < kMaxGridItems && per_row < kMaxGridItems) {
+            S.path = CMD_PATH_ROWS;
+            std::memcpy(S.rowconst, rowconst, sizeof rowconst);
+            S.variant = force_generic ? -1 : program_match_linear(P);
+            S.vec = true;
+            S.e = 4;
+            S.block = kRowsBlock;
+            S.grid = (n_vec + kRowsBlock - 1) / kRowsBlock;
+            S.n_vec = n_vec;
+            // Nontemporal loads once the data outgrows the last-level cache (as
+            // on the linear path); nontemporal stores only where every store
+            // instruction covers whole 128-byte lines (rows of whole lines).
+            int64_t bytes = 0;
+            bool lines = true;
+            for (int k = 0; k < P.n_in; ++k)
+                if (!rowconst[k]) bytes += numel * esize(B.in[k].dtype);
+            for (int k = 0; k < P.n_out; ++k) {
+                const int64_t es = esize(B.out[k].dtype);
+                bytes += numel * es;
+                lines = lines && aligned(B.out[k].ptr, 128) && (C.n[3] * es) % 128 == 0;
+                for (int d = 0; d < 3; ++d)
+                    if (C.n[d] > 1) lines = lines && (C.out_s[k][d] * es) % 128 == 0;
+            }
+            S.shape = linear_shape(bytes);
+            S.shape.nt_store = S.shape.nt_store && lines;
+            S.name = rows_name(S.variant);
+            return;
+        }
+    }
     // Tiled: planes of dimensions (2, 3) after moving the staged inputs' unit
     // stride dimension to position 2.  Every output is unit-stride along
     // dimension 3; every input is direct (unit stride along 3), row-constant
@@ -690,6 +749,20 @@ int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int
     return CMD_OK;
 }
 
+// Multiplier and shifts for dividing 32-bit values by d (1 <= d < 2^31), the
+// method of Granlund and Montgomery (see FastDiv).
+FastDiv make_fast_div(uint32_t d)
+{
+    uint32_t l = 0;
+    while (l < 32 && ((uint64_t)1 << l) < d) ++l;
+    FastDiv f;
+    f.d = d;
+    f.mul = (uint32_t)(((((uint64_t)1 << l) - d) << 32) / d + 1);
+    f.s1 = l < 1 ? l : 1;
+    f.s2 = l > 1 ? l - 1 : 0;
+    return f;
+}
+
 void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
 {
     std::memset(&A, 0, sizeof A);
@@ -705,6 +778,13 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
         std::memcpy(A.out_s[k], C.out_s[k], sizeof A.out_s[k]);
     }
     std::memcpy(A.n, C.n, sizeof A.n);
+    if (S.path == CMD_PATH_ROWS) {
+        A.n_vec = S.n_vec;
+        A.div_vec = make_fast_div((uint32_t)((C.n[3] + 3) / 4));
+        A.wave_in_row = ((C.n[3] + 3) / 4) % 64 == 0 ? 1u : 0u;
+        A.div_n2 = make_fast_div((uint32_t)C.n[2]);
+        A.div_n1 = make_fast_div((uint32_t)C.n[1]);
+    }
     A.tiles_r = S.tiles_r;
     A.tiles_c = S.tiles_c;
     A.tile_walk = S.walk;
@@ -852,7 +932,7 @@ int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info)
     std::memset(info, 0, sizeof *info);
     info->path = S.path;
     info->specialised = S.variant >= 0;
-    info->vector = S.path == CMD_PATH_TILED ? 1 : S.vec;
+    info->vector = S.path == CMD_PATH_TILED || S.path == CMD_PATH_ROWS ? 1 : S.vec;
     info->elems_per_thread = S.e;
     info->grid = S.grid;
     info->block = S.block;
@@ -908,8 +988,9 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         fill_strided(h, B, S, A);
         const char *ntv = std::getenv("ECMD_TILED_NT");
         const bool nt = !(ntv && std::strcmp(ntv, "0") == 0);
-        herr = S.path == CMD_PATH_TILED ? launch_tiled(S.variant, nt, S.tile, A, g, hip_stream)
-                                        : launch_gather(A, g, hip_stream);
+        herr = S.path == CMD_PATH_TILED  ? launch_tiled(S.variant, nt, S.tile, A, g, hip_stream)
+               : S.path == CMD_PATH_ROWS ? launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream)
+                                         : launch_gather(A, g, hip_stream);
     }
     if (herr != 0)
         return fail(h, CMD_E_LAUNCH, "%s launch failed: %s", S.name, hipGetErrorString((hipError_t)herr));

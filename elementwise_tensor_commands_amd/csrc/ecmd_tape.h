@@ -115,11 +115,22 @@ struct LinearArgs {
 };
 constexpr uint32_t kLinearXcdRemap = 1;   // give each XCD one contiguous run of blocks
 
+// Unsigned 32-bit division by a divisor d fixed at launch, as a multiply-high,
+// a subtraction and two shifts (Granlund and Montgomery, "Division by
+// Invariant Integers using Multiplication", 1994, section 4): with
+// l = ceil(log2 d), mul = floor(2^32 (2^l - d) / d) + 1, s1 = min(l, 1) and
+// s2 = max(l - 1, 0), n / d = (t + ((n - t) >> s1)) >> s2 with t the high
+// word of mul * n, for every 32-bit n.
+struct FastDiv {
+    uint32_t mul, d, s1, s2;
+};
+
 // Canonical 4-D views (the host drops size-1 dimensions, orders dimensions by
 // the first output's strides and merges contiguous ones, then pads on the
 // left with size-1 dimensions): sizes n[0..3], element strides per operand.
 // On the tiled path dimensions 0 and 1 are batch dimensions, 2 the rows and 3
-// the columns of the tiled plane.
+// the columns of the tiled plane.  On the rows path the rows (b0, b1, r) are
+// numbered in order and cut into 4-element vectors along dimension 3.
 struct StridedArgs {
     const void *in[kMaxIn];
     void *out[kMaxOut];
@@ -130,7 +141,10 @@ struct StridedArgs {
     int32_t tile_walk;          // tiled path: tile rows walked before moving right (<= 1: row by row)
     uint32_t uni[kMaxUni];
     uint8_t in_staged[kMaxIn];  // tiled path: p + 1 = read through LDS tile p (column-contiguous view)
-    uint8_t in_rowconst[kMaxIn];// tiled path: 1 = stride 0 along the columns (one value per row)
+    uint8_t in_rowconst[kMaxIn];// tiled and rows paths: 1 = stride 0 along dimension 3 (one value per row)
+    int64_t n_vec;              // rows path: vectors in all, ceil(n[3] / 4) per row
+    uint32_t wave_in_row;       // rows path: 1 = a multiple of 64 vectors per row (no wavefront spans two rows)
+    FastDiv div_vec, div_n2, div_n1;   // rows path: by vectors per row, by n[2], by n[1]
     Program prog;
 };
 
@@ -198,6 +212,13 @@ constexpr Program kProgClassifyU32 = {
 // out = s  (fill with a scalar; binary32 or int32 bits alike)
 constexpr Program kProgFillF32 = {0, 1, 0, 1, {}, {TY_F32}, {ECMD_R_U(0)}, {}};
 
+// out = x * a + b, three fp32 loads (a per-channel affine map when a and b
+// are broadcast views)
+constexpr Program kProgAffineF32 = {
+    3, 0, 2, 1, {TY_F32, TY_F32, TY_F32}, {TY_F32}, {ECMD_R_S(0)},
+    {{C_MUL_F32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_IN(1)},
+     {C_ADD_F32, ECMD_R_S(0), ECMD_R_IN(2), ECMD_R_S(0)}}};
+
 // out = f16(x), out = f32(x)
 constexpr Program kProgCvtF32F16 = {
     1, 0, 1, 1, {TY_F32}, {TY_F16}, {ECMD_R_S(0)},
@@ -223,7 +244,8 @@ namespace ecmd {
     X(cvt_f32_f16, kProgCvtF32F16)        \
     X(cvt_f16_f32, kProgCvtF16F32)        \
     X(classify_u32, kProgClassifyU32)     \
-    X(fill_f32, kProgFillF32)
+    X(fill_f32, kProgFillF32)             \
+    X(affine_f32, kProgAffineF32)
 
 #define ECMD_TILED_SPECIALISED(X)         \
     X(add_scaled_f32, kProgAddScaledF32)
@@ -250,10 +272,14 @@ struct TileShape {
 };
 int launch_tiled(int variant, bool nt, TileShape shape, const StridedArgs &A, LaunchGeometry g, void *stream);
 int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
+// Rows path: the linear path's specialised Programs (variant indexes the same
+// list); nontemporal loads / stores as the host chooses.
+int launch_rows(int variant, bool nt_load, bool nt_store, const StridedArgs &A, LaunchGeometry g, void *stream);
 
 constexpr int kLinearBlock = 256;
 constexpr int kTileBlock = 256;
 constexpr int kGatherE = 4;
 constexpr int kGatherBlock = 256;
+constexpr int kRowsBlock = 256;
 
 }  // namespace ecmd

@@ -222,6 +222,8 @@ typedef struct {
 #define CMD_PATH_TILED 2   /* planes of inner-contiguous, transposed (LDS-staged) and        */
                            /* row-broadcast views, with up to two batch dimensions           */
 #define CMD_PATH_GATHER 3  /* any other strides                                              */
+#define CMD_PATH_ROWS 4    /* rows: every view contiguous or constant along its last          */
+                           /* dimension (padded rows, batch strides, broadcasts), no transpose */
 
 /* Validate args exactly as cmd_launch does and describe the launch without
  * making it.  Host only: no HIP call.  Freezes the Command like cmd_launch. */

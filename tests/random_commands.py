@@ -86,19 +86,21 @@ def _random_inputs(rng, spec, shape):
     return out
 
 
-def random_view(rng, storage_fill, shape, dtype, broadcast=False, align=False):
+def random_view(rng, storage_fill, shape, dtype, broadcast=False, align=False, permute=True):
     """A random view of logical ``shape`` cut from a fresh contiguous storage:
     the storage holds the dimensions in a random order, each padded and
     started at a random offset; broadcast views also get stride 0 along a
-    random subset of dimensions.  ``align`` keeps paddings and offsets at
-    multiples of 4 elements.  Returns (view, storage); ``storage_fill(shape)``
+    random subset of dimensions.  ``align`` keeps offsets at multiples of 4
+    elements and pads every storage dimension to a multiple of 4.  Returns (view, storage); ``storage_fill(shape)``
     makes the storage's contents."""
     from numpy.lib.stride_tricks import as_strided
     r = len(shape)
-    perm = rng.permutation(r)                  # storage dimension i holds logical dimension perm[i]
+    perm = rng.permutation(r) if permute else np.arange(r)   # storage dimension i holds logical dimension perm[i]
     step = 4 if align else 1
     starts = [int(rng.choice([0, 0, 1])) * step for _ in range(r)]
     pads = [int(rng.choice([0, 0, 1, 3])) * step for _ in range(r)]
+    if align:                                  # padded storage dimensions of whole vectors
+        pads = [(-(shape[p] + starts[i])) % 4 + p_ for i, (p, p_) in enumerate(zip(perm, pads))]
     st_shape = tuple(shape[p] + starts[i] + pads[i] for i, p in enumerate(perm))
     storage = np.ascontiguousarray(storage_fill(st_shape).astype(dtype))
     v = storage[tuple(slice(starts[i], starts[i] + shape[p]) for i, p in enumerate(perm))]
@@ -146,22 +148,25 @@ def _fill_for(rng, dt):
 SIZES = [1, 2, 3, 4, 5, 8, 12, 16, 33, 64, 68, 100, 132, 260]
 
 
-def random_view_case(seed):
-    """A random Command of random rank over random views (inputs only)."""
-    rng = np.random.default_rng(5000 + seed)
-    r = int(rng.integers(1, 5))
+def random_view_case(seed, staged=False):
+    """A random Command of random rank over random views (inputs only).
+    ``staged``: rank 2 to 4, aligned, no broadcasts and outputs in logical
+    order, so that inputs stored in another order need a transpose."""
+    rng = np.random.default_rng((9000 if staged else 5000) + seed)
+    r = int(rng.integers(2 if staged else 1, 5))
     while True:
         shape = tuple(int(rng.choice(SIZES)) for _ in range(r))
         if np.prod(shape) <= 300_000:
             break
     spec = _random_spec(rng, int(rng.integers(1, 4)), int(rng.integers(1, 7)), r)
     in_dt, out_dt = _arg_dtypes(spec)
-    align = rng.random() < 0.6
+    align = staged or rng.random() < 0.6
     ins = []
     for (_, st), dt in zip([s for s in spec if s[1][0] in ("load", "scalar")], in_dt):
         if st[0] == "scalar":
             ins.append(np.float32(rng.standard_normal()) if dt == "f32" else np.int32(rng.integers(-1000, 1000)))
         else:
-            ins.append(random_view(rng, _fill_for(rng, dt), shape, _NPD[dt], broadcast=True, align=align))
-    outs = [random_view(rng, _fill_for(rng, dt), shape, _NPD[dt], align=align) for dt in out_dt]
+            ins.append(random_view(rng, _fill_for(rng, dt), shape, _NPD[dt], broadcast=not staged, align=align))
+    outs = [random_view(rng, _fill_for(rng, dt), shape, _NPD[dt], align=align, permute=not staged)
+            for dt in out_dt]
     return spec, ins, outs

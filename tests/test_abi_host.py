@@ -159,7 +159,7 @@ def test_raw_stride_and_null_errors():
     assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == -5         # non-injective store
     args = _raw_args(c, [good, dict(good, stride=(0, 0)), dict(good, ptr=out.data_ptr())])
     assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == 0          # broadcast load is fine
-    assert info.path == E.PATH_GATHER
+    assert info.path == E.PATH_ROWS                                        # one row with a broadcast value
     args = _raw_args(c, [good, good, dict(good, ptr=out.data_ptr(), reserved=1)])
     assert E.lib.cmd_plan(c._h, args, 3, ctypes.byref(info)) == -1
     args = _raw_args(c, [good, good, dict(good, ptr=out.data_ptr() + 1)])
@@ -260,7 +260,7 @@ def test_commutative_operands_canonical():
                                        ("mixed_two_out", "linear_mixed_two_out"),
                                        ("transposed_2d", "tiled_add_scaled_f32"),
                                        ("batched_transpose", "tiled_add_scaled_f32"),
-                                       ("bias_nchw", "tiled_generic")])
+                                       ("bias_nchw", "rows_affine_f32")])
 def test_workloads_select_their_kernels(wl, kernel):
     spec = W.WORKLOADS[wl]["spec"]
     n = 1 << 12 if wl != "transposed_2d" else 256
@@ -272,7 +272,7 @@ def test_workloads_select_their_kernels(wl, kernel):
     shape = W.shape_of(wl, n, small.get(wl))
     o = [torch.empty(shape, dtype={"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}[d]) for d in outs]
     plan = E.from_spec(spec).plan(*tv, *o)
-    assert plan["kernel"] == kernel and plan["specialised"] == (wl != "bias_nchw") and plan["vector"]
+    assert plan["kernel"] == kernel and plan["specialised"] and plan["vector"]
 
 
 def test_geometry_rules():

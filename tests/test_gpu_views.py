@@ -128,7 +128,7 @@ def test_full_size_views(wl):
     cmd.launch(*gin, out)
     torch.cuda.synchronize()
     compare(out.cpu().numpy(), ref[0], 0, "%s full (%s)" % (wl, plan["kernel"]))
-    assert plan["path"] == "tiled"
+    assert plan["path"] == {"batched_transpose": "tiled", "bias_nchw": "rows"}[wl]
 
 
 def test_staged_direct_and_row_constant_together():
@@ -162,3 +162,43 @@ def test_random_views(seed):
     if seed % 4 == 0:
         spec, ins, outs = random_view_case(seed)
         run_views(spec, ins, outs, True, "seed %d generic" % seed)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_transposed_views(seed):
+    """Random Commands whose inputs are stored in other dimension orders than
+    the outputs (mostly the tiled path's staged inputs)."""
+    spec, ins, outs = random_view_case(seed, staged=True)
+    run_views(spec, ins, outs, False, "staged seed %d" % seed)
+
+
+@pytest.mark.parametrize("shape", [(3, 5, 1), (3, 5, 2), (3, 5, 3), (3, 5, 5), (2, 3, 7, 63), (2, 3, 7, 64),
+                                   (2, 3, 7, 65), (4, 129), (1, 70001, 8), (3, 1, (1 << 20) + 3), (7, 1, 9, 4),
+                                   (5, 3, 1, 260), (1,), (6,), (1 << 20,)])
+def test_rows_path_shapes(shape):
+    """The rows path: padded rows, a per-row broadcast and a broadcast along
+    the rows, for row lengths with and without a partial last vector and row
+    counts that exercise the constant divisions."""
+    rng = np.random.default_rng(sum(shape) + len(shape))
+    spec = [("x", ("load", "f32", len(shape))), ("s", ("load", "f32", len(shape))),
+            ("b", ("load", "f32", len(shape))), ("xs", ("mul", "x", "s")), ("o", ("add", "b", "xs")),
+            ("out", ("store", "o", len(shape)))]
+    last = shape[-1]
+    pitch = last + (-last) % 4 + 4
+    lead = shape[:-1]
+
+    def padded():
+        st = rng.standard_normal(lead + (pitch,)).astype(np.float32)
+        return st[..., :last], st
+
+    x, xs = padded()
+    srow = rng.standard_normal(lead if lead else (1,)).astype(np.float32)
+    s = as_strided(srow, shape=shape, strides=(srow.strides if lead else ()) + (0,), writeable=False)
+    bcol = rng.standard_normal(last).astype(np.float32)
+    b = as_strided(bcol, shape=shape, strides=(0,) * len(lead) + (4,), writeable=False)
+    o, os_ = padded()
+    plan = run_views(spec, [(x, xs), (s, srow), (b, bcol)], [(o, os_)], False, "rows %s" % (shape,))
+    if np.prod(shape) == 1:
+        assert plan["path"] == "linear", plan
+    elif last > 1:                     # rows of one element are a strided vector: gathered
+        assert plan["path"] == "rows", plan

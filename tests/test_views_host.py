@@ -91,8 +91,8 @@ def test_contiguous_dimensions_merge_despite_row_padding_elsewhere():
     shape = (4, 64, 64)
     pad = (64 * 80, 80, 1)
     p = E.from_spec(add_spec(3)).plan(T(shape, pad), T(shape, pad), T(shape, pad))
-    assert p["path"] == "tiled" and p["dims"] == 2 and p["size"] == (1, 1, 256, 64), p
-    assert not p["specialised"] and p["lds_bytes"] == 0
+    assert p["path"] == "rows" and p["dims"] == 2 and p["size"] == (1, 1, 256, 64), p
+    assert p["specialised"] and p["kernel"] == "rows_add_f32" and p["lds_bytes"] == 0
 
 
 def test_batched_transpose_is_tiled_and_specialised():
@@ -134,21 +134,32 @@ def test_per_channel_broadcast_nchw_is_row_constant():
     N, C, H, W = 2, 8, 4, 16
     bias = T((N, C, H, W), (0, 1, 0, 0))
     p = E.from_spec(add_spec(4)).plan(T((N, C, H, W)), bias, T((N, C, H, W)))
-    assert p["path"] == "tiled" and not p["specialised"], p
+    assert p["path"] == "rows" and p["specialised"], p
     assert p["dims"] == 3 and p["size"] == (1, N, C, H * W)
     assert p["lds_bytes"] == 0
+    # with a transposed input as well, the tiled path reads the bias once per row
+    yt = T((N, C, H, W), (C * H * W, H * W, 1, H))
+    p = E.from_spec(add_spec(4)).plan(yt, bias, T((N, C, H, W)))
+    assert p["path"] == "tiled" and not p["specialised"], p
 
 
 def test_per_channel_broadcast_nhwc_is_direct():
     N, H, W, C = 2, 4, 16, 8
     scale = T((N, H, W, C), (0, 0, 0, 1))
     p = E.from_spec(add_spec(4)).plan(T((N, H, W, C)), scale, T((N, H, W, C)))
-    assert p["path"] == "tiled" and p["dims"] == 2 and p["size"] == (1, 1, N * H * W, C), p
+    assert p["path"] == "rows" and p["dims"] == 2 and p["size"] == (1, 1, N * H * W, C), p
 
 
-def test_broadcast_along_every_dimension_gathers():
-    shape = (4, 8, 16)
+def test_broadcast_along_every_dimension_is_one_row():
+    shape = (4, 8, 17)
     p = E.from_spec(add_spec(3)).plan(T(shape), T(shape, (0, 0, 0)), T(shape))
+    assert p["path"] == "rows" and p["size"] == (1, 1, 1, 4 * 8 * 17), p
+    assert p["grid"] == (4 * 8 * 17 // 4 + 1 + 255) // 256
+
+
+def test_no_vector_alignment_gathers():
+    shape = (4, 8, 16)
+    p = E.from_spec(add_spec(3)).plan(T(shape), T(shape, (0, 0, 0), base=1), T(shape, (8 * 17, 17, 1)))
     assert p["path"] == "gather", p
 
 
@@ -158,7 +169,7 @@ def test_misaligned_batch_stride_gathers():
     p = E.from_spec(add_spec(3)).plan(T(shape), T(shape), out)
     assert p["path"] == "gather", p
     ok = T(shape, (8 * 16 + 4, 16, 1))
-    assert E.from_spec(add_spec(3)).plan(T(shape), T(shape), ok)["path"] == "tiled"
+    assert E.from_spec(add_spec(3)).plan(T(shape), T(shape), ok)["path"] == "rows"
 
 
 def test_misaligned_base_of_a_staged_input_gathers():
@@ -252,13 +263,13 @@ def test_negative_strides_and_sizes_are_rejected():
 
 def test_random_view_cases_reach_every_path():
     """The random view cases that the GPU parity tests run cover the linear,
-    tiled and gather paths (planned here with the device's alignment: every
+    rows, tiled and gather paths (planned here with the device's alignment: every
     storage at a fresh 4 KiB-aligned address)."""
     import workloads as W
     from random_commands import random_view_case
     seen = {}
-    for seed in range(60):
-        spec, ins, outs = random_view_case(seed)
+    for seed, staged in [(s, False) for s in range(60)] + [(s, True) for s in range(30)]:
+        spec, ins, outs = random_view_case(seed, staged)
         vals = []
         for x in list(ins) + list(outs):
             if isinstance(x, tuple):
@@ -271,4 +282,4 @@ def test_random_view_cases_reach_every_path():
                 vals.append(x)
         p = E.from_spec(spec).plan(*vals)
         seen[p["path"]] = seen.get(p["path"], 0) + 1
-    assert all(seen.get(k, 0) >= 5 for k in ("linear", "tiled", "gather")), seen
+    assert all(seen.get(k, 0) >= 8 for k in ("linear", "rows", "tiled", "gather")), seen
