@@ -37,6 +37,16 @@
  *   f16->f32 exact; f32->f16 and i32->f16 round to nearest even from the exact
  *   value, overflow to infinity, gradual underflow; i32->f32 round to nearest
  *   even; f32->i32 and f16->i32 truncate toward zero, saturate, NaN -> 0.
+ *   f16 and bf16 (bfloat16: binary32's sign and 8-bit exponent with a 7-bit
+ *   fraction) are compute types too: Add, Sub and Mul give the exact result
+ *   rounded once to the operands' format (nearest even, overflow to infinity,
+ *   gradual underflow).  The oracle forms the binary64 result and rounds that;
+ *   binary64 carries at least 2p + 2 bits for p = 11 and p = 8, so rounding
+ *   twice gives the same value as rounding the exact result once (Figueroa,
+ *   "When is double rounding innocuous?", 1995).  Conversions to f16 or bf16
+ *   round the exact source value once; bf16->f32 and f16->bf16's source values
+ *   are exact in binary64.  Compare, Min, Max, Abs, Neg and Select follow the
+ *   binary32 rules on the values.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared -pthread
  */
@@ -51,6 +61,7 @@
 #define OR_F16 1
 #define OR_F32 2
 #define OR_I32 3
+#define OR_BF16 4
 
 #define OR_LOAD 1
 #define OR_SCALAR 2
@@ -164,6 +175,62 @@ uint16_t oracle_f32_to_f16(uint32_t bits)
     return f16_round_from_exact((double)f32_from_bits(bits));  /* float -> double is exact */
 }
 
+/* bfloat16 -> value, from the format's definition: sign bit, 8-bit exponent
+ * field with bias 127, 7-bit fraction.  Field 0 is a subnormal m * 2^-133,
+ * field 255 is inf/NaN, otherwise (128 + m) * 2^(e - 134).  Every bfloat16
+ * value is exactly a binary64 value. */
+static double bf16_value(uint16_t h)
+{
+    int neg = (h >> 15) & 1;
+    uint32_t e = (uint32_t)((h >> 7) & 0xff);
+    uint32_t m = (uint32_t)(h & 0x7f);
+    double mag;
+    if (e == 255)
+        mag = m == 0 ? INFINITY : NAN;
+    else if (e == 0)
+        mag = ldexp((double)m, -133);
+    else
+        mag = ldexp((double)(128 + m), (int)e - 134);
+    return neg ? -mag : mag;
+}
+
+/* Exact real value (held in a double that represents it exactly, or is the
+ * binary64 rounding of it, see the header) -> bfloat16, round to nearest,
+ * ties to even.  The grid has spacing 2^-133 below 2^-126 and 2^(k-7) in the
+ * binade [2^k, 2^(k+1)); a magnitude that rounds to 2^128 or above is
+ * infinity.  NaN gives the quiet NaN of the same sign. */
+static uint16_t bf16_round_from_exact(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v))
+        return sign | 0x7fc0u;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7f80u;
+    if (a == 0.0)
+        return sign;
+    int k;
+    frexp(a, &k);
+    int binade = k - 1;                   /* a in [2^binade, 2^(binade+1)) */
+    int unit_exp = binade < -126 ? -133 : binade - 7;   /* grid spacing 2^unit_exp */
+    double units = nearbyint(ldexp(a, -unit_exp));     /* a in grid units, to nearest even */
+    double rounded = ldexp(units, unit_exp);
+    if (rounded >= ldexp(1.0, 128))
+        return sign | 0x7f80u;
+    if (rounded < ldexp(1.0, -126))       /* subnormal (or zero): field = units of 2^-133 */
+        return sign | (uint16_t)units;
+    frexp(rounded, &k);
+    int e = k - 1;                        /* the rounding may carry into the next binade */
+    uint32_t fraction = (uint32_t)(ldexp(rounded, 7 - e)) - 128u;
+    return sign | (uint16_t)(((uint32_t)(e + 127) << 7) | fraction);
+}
+
+/* binary16 -> value as a double (exact). */
+static double f16_value(uint16_t h)
+{
+    return (double)f32_from_bits(oracle_f16_to_f32(h));
+}
+
 /* float -> int32: truncate toward zero, saturate at the int32 range, NaN -> 0. */
 static int32_t i32_from_f32_sat(float f)
 {
@@ -176,6 +243,23 @@ static int32_t i32_from_f32_sat(float f)
     return (int32_t)truncf(f);
 }
 
+/* Value of a binary16 / bfloat16 / binary32 bit pattern as a double (exact). */
+static double float_value(int dtype, uint32_t bits)
+{
+    if (dtype == OR_F16) return f16_value((uint16_t)bits);
+    if (dtype == OR_BF16) return bf16_value((uint16_t)bits);
+    return (double)f32_from_bits(bits);
+}
+
+/* Round an exact value to binary16 / bfloat16. */
+static uint32_t round16(int dtype, double v)
+{
+    return dtype == OR_F16 ? f16_round_from_exact(v) : bf16_round_from_exact(v);
+}
+
+uint16_t oracle_f32_to_bf16(uint32_t bits) { return bf16_round_from_exact((double)f32_from_bits(bits)); }
+uint32_t oracle_bf16_to_f32(uint16_t h) { return bits_from_f32((float)bf16_value(h)); }
+
 /* Bulk helpers so the exhaustive conversion tests do not pay a call per value. */
 void oracle_f32_to_f16_range(uint32_t first, uint64_t count, uint16_t *out)
 {
@@ -187,6 +271,12 @@ void oracle_f16_to_f32_all(uint32_t *out)
 {
     for (uint32_t h = 0; h < 65536; ++h)
         out[h] = oracle_f16_to_f32((uint16_t)h);
+}
+
+void oracle_f32_to_bf16_range(uint32_t first, uint64_t count, uint16_t *out)
+{
+    for (uint64_t k = 0; k < count; ++k)
+        out[k] = oracle_f32_to_bf16((uint32_t)(first + k));
 }
 
 /* Floating-point environment: returns 0 when MXCSR has FTZ and DAZ clear and
@@ -208,7 +298,7 @@ int oracle_check_fpenv(void)
 /* binary32 minimum / maximum: a NaN operand is ignored unless both are NaN,
  * and -0 counts as smaller than +0 (IEEE 754-2019 minimumNumber and
  * maximumNumber). */
-static float min_number(float x, float y)
+static double min_number(double x, double y)
 {
     if (isnan(x)) return y;
     if (isnan(y)) return x;
@@ -217,7 +307,7 @@ static float min_number(float x, float y)
     return signbit(x) ? x : y;          /* equal: pick -0 over +0 */
 }
 
-static float max_number(float x, float y)
+static double max_number(double x, double y)
 {
     if (isnan(x)) return y;
     if (isnan(y)) return x;
@@ -242,8 +332,8 @@ static uint32_t compare(int op, int src_dtype, uint32_t a, uint32_t b)
         else if (op == OR_CMP_LE) r = x <= y;
         else if (op == OR_CMP_GT) r = x > y;
         else r = x >= y;
-    } else {                                    /* binary32: C's IEEE comparisons */
-        float x = f32_from_bits(a), y = f32_from_bits(b);
+    } else {                                    /* floats: C's IEEE comparisons on the exact values */
+        double x = float_value(src_dtype, a), y = float_value(src_dtype, b);
         if (op == OR_CMP_EQ) r = x == y;
         else if (op == OR_CMP_NE) r = x != y;  /* true when either is NaN */
         else if (op == OR_CMP_LT) r = x < y;
@@ -263,15 +353,19 @@ static uint32_t apply_op(int op, int dst_dtype, int src_dtype, uint32_t a, uint3
     if (op == OR_ABS) {
         if (dst_dtype == OR_I32) return (a & 0x80000000u) ? 0u - a : a;   /* |INT_MIN| wraps to INT_MIN */
         if (dst_dtype == OR_F32) return a & 0x7fffffffu;
-        return a & 0x7fffu;
+        return a & 0x7fffu;                      /* binary16, bfloat16 */
     }
     if (op == OR_MIN || op == OR_MAX) {
         if (dst_dtype == OR_I32) {
             int32_t x = (int32_t)a, y = (int32_t)b;
             return (uint32_t)(op == OR_MIN ? (x < y ? x : y) : (x > y ? x : y));
         }
-        float x = f32_from_bits(a), y = f32_from_bits(b);
-        return bits_from_f32(op == OR_MIN ? min_number(x, y) : max_number(x, y));
+        /* the result is one of the operands, bits and all */
+        double x = float_value(dst_dtype, a), y = float_value(dst_dtype, b);
+        double m = op == OR_MIN ? min_number(x, y) : max_number(x, y);
+        if (isnan(m)) return b;                  /* both NaN */
+        if (m == x && m == y) return signbit(m) == signbit(x) ? a : b;
+        return m == x ? a : b;
     }
     if (op == OR_CVT) {
         if (src_dtype == dst_dtype)
@@ -288,17 +382,35 @@ static uint32_t apply_op(int op, int dst_dtype, int src_dtype, uint32_t a, uint3
             return (uint32_t)i32_from_f32_sat(f32_from_bits(a));
         if (src_dtype == OR_F16 && dst_dtype == OR_I32)
             return (uint32_t)i32_from_f32_sat(f32_from_bits(oracle_f16_to_f32((uint16_t)a)));
+        /* bfloat16: every source value is exact in binary64; round it once */
+        if (dst_dtype == OR_BF16)
+            return src_dtype == OR_I32 ? bf16_round_from_exact((double)(int32_t)a)
+                                       : bf16_round_from_exact(float_value(src_dtype, a));
+        if (src_dtype == OR_BF16 && dst_dtype == OR_F16)
+            return f16_round_from_exact(bf16_value((uint16_t)a));
+        if (src_dtype == OR_BF16 && dst_dtype == OR_F32)
+            return bits_from_f32((float)bf16_value((uint16_t)a));   /* exact */
+        if (src_dtype == OR_BF16 && dst_dtype == OR_I32)
+            return (uint32_t)i32_from_f32_sat((float)bf16_value((uint16_t)a));
         return 0;
     }
     if (op == OR_NEG) {
         if (dst_dtype == OR_I32) return 0u - a;
         if (dst_dtype == OR_F32) return a ^ 0x80000000u;
-        return (a ^ 0x8000u) & 0xffffu;
+        return (a ^ 0x8000u) & 0xffffu;          /* binary16, bfloat16 */
     }
     if (dst_dtype == OR_I32) {
         if (op == OR_ADD) return a + b;
         if (op == OR_SUB) return a - b;
         return a * b;                        /* low 32 bits of the product */
+    }
+    if (dst_dtype == OR_F16 || dst_dtype == OR_BF16) {
+        /* binary64 result of the exact operands, rounded once to the format */
+        double x = float_value(dst_dtype, a), y = float_value(dst_dtype, b), z;
+        if (op == OR_ADD) z = x + y;
+        else if (op == OR_SUB) z = x - y;
+        else z = x * y;
+        return round16(dst_dtype, z);
     }
     /* dst_dtype == OR_F32 */
     float x = f32_from_bits(a), y = f32_from_bits(b), z;
@@ -319,7 +431,7 @@ static int64_t offset_of(const oracle_arg *g, const int64_t idx[4])
 static uint32_t read_elem(const oracle_arg *g, const int64_t idx[4])
 {
     int64_t off = offset_of(g, idx);
-    if (g->dtype == OR_F16) {
+    if (g->dtype == OR_F16 || g->dtype == OR_BF16) {
         uint16_t h;
         memcpy(&h, (const char *)g->ptr + off * 2, 2);
         return h;
@@ -332,7 +444,7 @@ static uint32_t read_elem(const oracle_arg *g, const int64_t idx[4])
 static void write_elem(const oracle_arg *g, const int64_t idx[4], uint32_t v)
 {
     int64_t off = offset_of(g, idx);
-    if (g->dtype == OR_F16) {
+    if (g->dtype == OR_F16 || g->dtype == OR_BF16) {
         uint16_t h = (uint16_t)v;
         memcpy((char *)g->ptr + off * 2, &h, 2);
     } else {

@@ -27,10 +27,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "ecmd_oracle.c")
 LIB = os.path.join(HERE, "libecmd_oracle.so")
 
-F16, F32, I32 = 1, 2, 3
-DTYPE_CODE = {"f16": F16, "f32": F32, "i32": I32}
-NP_DTYPE = {F16: np.float16, F32: np.float32, I32: np.int32}
-NP_BITS = {F16: np.uint16, F32: np.uint32, I32: np.uint32}
+F16, F32, I32, BF16 = 1, 2, 3, 4
+DTYPE_CODE = {"f16": F16, "f32": F32, "i32": I32, "bf16": BF16}
+# NumPy has no bfloat16: bfloat16 tensors are uint16 arrays of bit patterns,
+# bfloat16 scalars uint16 bit patterns.
+NP_DTYPE = {F16: np.float16, F32: np.float32, I32: np.int32, BF16: np.uint16}
+NP_BITS = {F16: np.uint16, F32: np.uint32, I32: np.uint32, BF16: np.uint16}
 
 LOAD, SCALAR, OP = 1, 2, 3
 ADD, SUB, MUL, NEG, CVT = 1, 2, 3, 4, 5
@@ -101,6 +103,12 @@ def _load(path):
     L.oracle_f32_to_f16_range.argtypes = [ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p]
     L.oracle_f16_to_f32_all.restype = None
     L.oracle_f16_to_f32_all.argtypes = [ctypes.c_void_p]
+    L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    L.oracle_f32_to_bf16.argtypes = [ctypes.c_uint32]
+    L.oracle_bf16_to_f32.restype = ctypes.c_uint32
+    L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    L.oracle_f32_to_bf16_range.restype = None
+    L.oracle_f32_to_bf16_range.argtypes = [ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p]
     L.oracle_check_fpenv.restype = ctypes.c_int
     for name, cls in (("node", _Node), ("store", _Store), ("arg", _Arg)):
         fn = getattr(L, "oracle_sizeof_" + name)
@@ -158,8 +166,6 @@ class OracleCommand:
             db = self.nodes[b][1]
             if da != db:
                 raise OracleError("operand dtypes differ")
-            if da == F16:
-                raise OracleError("binary16 arithmetic is not part of the op set")
             if code in (CMP["ltu"], CMP["leu"], CMP["gtu"], CMP["geu"]) and da != I32:
                 raise OracleError("unsigned comparison needs int32 operands")
             res = I32 if code in CMP.values() else da
@@ -245,6 +251,8 @@ class OracleCommand:
         for k, v in zip(in_idx, values):
             kind, dt = self.args[k][0], self.args[k][1]
             if kind == "scalar":
+                if dt == BF16 and np.asarray(v).dtype != np.uint16:
+                    raise OracleError("scalar argument %d: bfloat16 scalars are uint16 bit patterns" % k)
                 s = np.asarray(v).astype(NP_DTYPE[dt]) if not isinstance(v, np.ndarray) else v
                 if s.dtype != np.dtype(NP_DTYPE[dt]):
                     raise OracleError("scalar argument %d: dtype %s" % (k, s.dtype))

@@ -47,23 +47,30 @@ SPECS = {
     "neg_i32": unary("neg", "i32"),
     "neg_f16": unary("neg", "f16"),
 }
-for a in ("f16", "f32", "i32"):
-    for b in ("f16", "f32", "i32"):
+DTYPES = ("f16", "bf16", "f32", "i32")
+for a in DTYPES:
+    for b in DTYPES:
         SPECS["cvt_%s_%s" % (a, b)] = unary("cvt", a, b)
 for c in COMPARES:
-    SPECS["cmp_%s_f32" % c] = binary(c, "f32")
-    SPECS["cmp_%s_i32" % c] = binary(c, "i32")
+    for dt in DTYPES:
+        SPECS["cmp_%s_%s" % (c, dt)] = binary(c, dt)
 for c in UNSIGNED:
     SPECS["cmp_%s_i32" % c] = binary(c, "i32")
-for dt in ("f32", "i32"):
+for dt in DTYPES:
     SPECS["min_" + dt] = binary("min", dt)
     SPECS["max_" + dt] = binary("max", dt)
-for dt in ("f16", "f32", "i32"):
     SPECS["abs_" + dt] = unary("abs", dt)
     SPECS["select_" + dt] = select(dt)
+# binary16 and bfloat16 arithmetic (native compute types)
+for dt in ("f16", "bf16"):
+    for op in ("add", "sub", "mul"):
+        SPECS["%s_%s" % (op, dt)] = binary(op, dt)
+SPECS["neg_bf16"] = unary("neg", "bf16")
+SPECS["axpby_f16"] = W.AXPBY_F16
+SPECS["axpby_bf16"] = W.AXPBY_BF16
 SPECS["classify_u32"] = CLASSIFY_U32
 
-DT = {"f16": "f16", "f32": "f32", "i32": "i32"}
+DT = {"f16": "f16", "bf16": "bf16", "f32": "f32", "i32": "i32"}
 
 
 def arg_dtypes(spec):

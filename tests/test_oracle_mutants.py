@@ -18,7 +18,8 @@ import test_oracle_pins as P
 
 MUTANTS = {
     "sub_operands_swapped": ("if (op == OR_SUB) return a - b;", "if (op == OR_SUB) return b - a;"),
-    "f32_sub_as_add": ("else if (op == OR_SUB) z = x - y;", "else if (op == OR_SUB) z = x + y;"),
+    "f32_sub_as_add": ("\n    else if (op == OR_SUB) z = x - y;", "\n    else if (op == OR_SUB) z = x + y;"),
+    "f16_sub_as_add": ("\n        else if (op == OR_SUB) z = x - y;", "\n        else if (op == OR_SUB) z = x + y;"),
     "i32_add_through_float": ("if (op == OR_ADD) return a + b;",
                               "if (op == OR_ADD) return (uint32_t)(int32_t)((float)(int32_t)a + (float)(int32_t)b);"),
     "neg_as_zero_minus": ("if (dst_dtype == OR_F32) return a ^ 0x80000000u;",
@@ -43,11 +44,27 @@ MUTANTS = {
                                 "if (op == OR_CMP_LTU) r = (int32_t)a < (int32_t)b;"),
     "float_ne_ordered": ("else if (op == OR_CMP_NE) r = x != y;  /* true when either is NaN */",
                          "else if (op == OR_CMP_NE) r = (x < y) || (x > y);"),
-    "min_keeps_nan": ("static float min_number(float x, float y)\n{\n    if (isnan(x)) return y;\n    if (isnan(y)) return x;\n",
-                      "static float min_number(float x, float y)\n{\n"),
+    "min_keeps_nan": ("static double min_number(double x, double y)\n{\n    if (isnan(x)) return y;\n    if (isnan(y)) return x;\n",
+                      "static double min_number(double x, double y)\n{\n"),
     "min_zero_sign": ("return signbit(x) ? x : y;          /* equal: pick -0 over +0 */", "return x;"),
     "abs_int_saturates": ("return (a & 0x80000000u) ? 0u - a : a;",
                           "return (a & 0x80000000u) ? (a == 0x80000000u ? 0x7fffffffu : 0u - a) : a;"),
+    # binary16 / bfloat16 arithmetic and bfloat16 conversions
+    "bf16_round_truncates": ("double units = nearbyint(ldexp(a, -unit_exp));",
+                             "double units = trunc(ldexp(a, -unit_exp));"),
+    "bf16_subnormal_flushed": ("return sign | (uint16_t)units;", "return sign;"),
+    "bf16_exponent_bias_off": ("mag = ldexp((double)(128 + m), (int)e - 134);",
+                               "mag = ldexp((double)(128 + m), (int)e - 133);"),
+    "bf16_overflow_one_binade_early": ("if (rounded >= ldexp(1.0, 128))", "if (rounded >= ldexp(1.0, 127))"),
+    "i32_bf16_through_f32": ("return src_dtype == OR_I32 ? bf16_round_from_exact((double)(int32_t)a)",
+                             "return src_dtype == OR_I32 ? bf16_round_from_exact((double)(float)(int32_t)a)"),
+    "f16_arith_rounded_to_bf16": ("return dtype == OR_F16 ? f16_round_from_exact(v) : bf16_round_from_exact(v);",
+                                  "return bf16_round_from_exact(v);"),
+    "f16_operands_read_as_f32": ("double x = float_value(dst_dtype, a), y = float_value(dst_dtype, b), z;",
+                                 "double x = float_value(OR_F32, a), y = float_value(OR_F32, b), z;"),
+    "bf16_round_half_away": ("double units = nearbyint(ldexp(a, -unit_exp));",
+                             "double units = floor(ldexp(a, -unit_exp) + 0.5);"),
+    "min16_returns_first": ("        return m == x ? a : b;", "        return a;"),
     "mul_high_dropped": ("return a * b;                        /* low 32 bits of the product */",
                          "return (a & 0xffffu) * (b & 0xffffu);"),
 }
@@ -55,6 +72,7 @@ MUTANTS = {
 
 def _fast_pins(oracle_mod):
     """Run the quick pins; return the number that fail."""
+    P.PAIRS_RANDOM, P.PAIRS_SPECIAL_BF16 = 1 << 16, 400
     failures = 0
     checks = [lambda c=c: P.test_hand_worked(oracle_mod, c) for c in P.GOLDEN_CASES]
     checks += [
@@ -70,6 +88,11 @@ def _fast_pins(oracle_mod):
         lambda: P.test_i32_conversions_vs_numpy(oracle_mod),
         lambda: P.test_rank_n_views_brute_force(oracle_mod, 3),
         lambda: P.test_new_ops_vs_numpy(oracle_mod),
+        lambda: P.test_16bit_arith_vs_libraries(oracle_mod, "add", "bf16"),
+        lambda: P.test_16bit_arith_vs_libraries(oracle_mod, "mul", "bf16"),
+        lambda: P.test_16bit_arith_vs_libraries(oracle_mod, "mul", "f16"),
+        lambda: P.test_bf16_conversions_vs_torch(oracle_mod),
+        lambda: P.test_16bit_min_max_compare_vs_libraries(oracle_mod, "bf16"),
     ]
     for chk in checks:
         try:

@@ -17,13 +17,14 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import workloads as W
 from specs import SPECS, arg_dtypes, input_kinds
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.txt")
-NPD = {"f16": np.float16, "f32": np.float32, "i32": np.int32}
-NPU = {"f16": np.uint16, "f32": np.uint32, "i32": np.uint32}
+NPD = {"f16": np.float16, "bf16": np.uint16, "f32": np.float32, "i32": np.int32}
+NPU = {"f16": np.uint16, "bf16": np.uint16, "f32": np.uint32, "i32": np.uint32}
 
 
 def load_golden():
@@ -42,6 +43,8 @@ def load_golden():
 def is_nan_bits(bits, dt):
     if dt == "f16":
         return (bits & 0x7C00) == 0x7C00 and (bits & 0x3FF) != 0
+    if dt == "bf16":
+        return (bits & 0x7F80) == 0x7F80 and (bits & 0x7F) != 0
     if dt == "f32":
         return (bits & 0x7F800000) == 0x7F800000 and (bits & 0x7FFFFF) != 0
     return False
@@ -451,10 +454,16 @@ def test_front_end_rejects(oracle_mod):
         c.add(x, i)                    # dtypes differ
     with pytest.raises(O.OracleError):
         c.add(x, 99)                   # unknown tag
+    b = c.load("bf16")
     with pytest.raises(O.OracleError):
-        c.add(h, h)                    # no binary16 arithmetic
+        c.add(h, b)                    # binary16 and bfloat16 do not mix
+    with pytest.raises(O.OracleError):
+        c.op("ltu", h, h)              # unsigned comparison needs int32
     with pytest.raises(O.OracleError):
         c.load("f32", 5)
+    c3 = O.from_spec([("s", ("scalar", "bf16")), ("o", ("store", "s", 1))])
+    with pytest.raises(O.OracleError):
+        c3.run(1.5, outputs=[np.zeros(3, np.uint16)])   # bfloat16 scalars are bit patterns
     c2 = O.from_spec(W.ADD_F32)
     with pytest.raises(O.OracleError):
         c2.run(np.zeros(4, np.float32), np.zeros(5, np.float32))
@@ -592,3 +601,207 @@ def test_bias_nchw_workload_matches_numpy(oracle_mod, shape):
     _, scale, bias = extra["storage"]
     ref = vals[0] * scale.reshape(1, -1, 1, 1) + bias.reshape(1, -1, 1, 1)
     assert np.array_equal(o.view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# Native binary16 / bfloat16 arithmetic and bfloat16 conversions.
+#
+# Library special cases: NumPy's float16 operations and torch's CPU bfloat16
+# operations compute in binary32 and round the result to the 16-bit format
+# (nearest even).  binary32 has 24 >= 2p + 2 bits for p = 11 and p = 8, so that
+# double rounding equals rounding the exact result once (Figueroa 1995) -- the
+# definition the oracle implements by a different route (binary64, then its
+# own rounding).  torch keeps subnormals on the CPU unless told otherwise.
+
+def _tbf(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def _nbf(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _nan16(bits, dt):
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dt == "bf16":
+        return ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
+    return ((bits & 0x7C00) == 0x7C00) & ((bits & 0x3FF) != 0)
+
+
+def _same16(got, ref, dt, what):
+    got, ref = np.asarray(got, dtype=np.uint16), np.asarray(ref, dtype=np.uint16)
+    ng, nr = _nan16(got, dt), _nan16(ref, dt)
+    bad = (ng != nr) | (~ng & (got != ref))
+    idx = np.flatnonzero(bad)
+    assert idx.size == 0, "%s: %d differ, first %s" % (what, idx.size, [(int(i), hex(got[i]), hex(ref[i])) for i in idx[:5]])
+
+
+def _special16(dt):
+    """Every sign and exponent field with fractions at the edges: zeros,
+    subnormals, the largest finite values, infinities, NaN."""
+    fb = 10 if dt == "f16" else 7
+    eb = 5 if dt == "f16" else 8
+    fr = [0, 1, 2, 3, (1 << (fb - 1)) - 1, 1 << (fb - 1), (1 << (fb - 1)) + 1, (1 << fb) - 2, (1 << fb) - 1]
+    out = [(s << 15) | (e << fb) | f for s in (0, 1) for e in range(1 << eb) for f in fr]
+    return np.array(sorted(set(out)), dtype=np.uint16)
+
+
+# Sizes of the 16-bit pair sweeps; the planted-mistake harness lowers them.
+PAIRS_RANDOM = 1 << 20
+PAIRS_SPECIAL_BF16 = 1000
+
+
+def _pairs16(dt, n_random=None, seed=77):
+    n_random = PAIRS_RANDOM if n_random is None else min(n_random, PAIRS_RANDOM)
+    sp = _special16(dt)
+    if dt == "bf16":                       # 4,600 specials: keep the pairs at ~1M
+        rng0 = np.random.default_rng(seed + 1)
+        sp = np.sort(rng0.choice(sp, PAIRS_SPECIAL_BF16, replace=False))
+    a = np.repeat(sp, sp.size)
+    b = np.tile(sp, sp.size)
+    rng = np.random.default_rng(seed)
+    ra = rng.integers(0, 1 << 16, n_random, dtype=np.uint32).astype(np.uint16)
+    rb = rng.integers(0, 1 << 16, n_random, dtype=np.uint32).astype(np.uint16)
+    return np.concatenate([a, ra]), np.concatenate([b, rb])
+
+
+def _oracle16(oracle_mod, spec_name, dt, *ins):
+    vals = [x.view(np.float16) if dt == "f16" else x for x in ins]
+    (o,) = oracle_mod.from_spec(SPECS[spec_name]).run(*vals, nthreads=8)
+    return o.view(np.uint16) if o.dtype != np.int32 else o
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("op", ["add", "sub", "mul"])
+def test_16bit_arith_vs_libraries(oracle_mod, op, dt):
+    a, b = _pairs16(dt)
+    got = _oracle16(oracle_mod, "%s_%s" % (op, dt), dt, a, b)
+    if dt == "f16":
+        x, y = a.view(np.float16), b.view(np.float16)
+        with np.errstate(all="ignore"):
+            ref = {"add": x + y, "sub": x - y, "mul": x * y}[op].view(np.uint16)
+    else:
+        x, y = _tbf(a), _tbf(b)
+        ref = _nbf({"add": x + y, "sub": x - y, "mul": x * y}[op])
+    _same16(got, ref, dt, "%s %s" % (op, dt))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_16bit_min_max_compare_vs_libraries(oracle_mod, dt):
+    """Min / max (NaN ignored: torch.fmin / fmax and NumPy fmin / fmax) and
+    the six comparisons; equal zeros of opposite signs are checked by hand in
+    the golden file, since the libraries do not fix which zero fmin returns."""
+    a, b = _pairs16(dt, n_random=1 << 18)
+    if dt == "f16":
+        x, y = a.view(np.float16), b.view(np.float16)
+    else:
+        x, y = _tbf(a).float().numpy(), _tbf(b).float().numpy()   # exact
+    zeros = ((a & 0x7FFF) == 0) & ((b & 0x7FFF) == 0)
+    with np.errstate(all="ignore"):
+        for op, fn in (("min", np.fmin), ("max", np.fmax)):
+            got = _oracle16(oracle_mod, "%s_%s" % (op, dt), dt, a, b)
+            ref = fn(x, y)
+            ref = ref.view(np.uint16) if dt == "f16" else _nbf(torch.from_numpy(ref).to(torch.bfloat16))
+            _same16(got[~zeros], ref[~zeros], dt, "%s %s" % (op, dt))
+        for c, fn in (("eq", np.equal), ("ne", np.not_equal), ("lt", np.less), ("le", np.less_equal),
+                      ("gt", np.greater), ("ge", np.greater_equal)):
+            got = _oracle16(oracle_mod, "cmp_%s_%s" % (c, dt), dt, a, b)
+            assert np.array_equal(got, fn(x, y).astype(np.int32)), (c, dt)
+
+
+def test_bf16_conversions_vs_torch(oracle_mod):
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    # bfloat16 -> binary32: every pattern (exact)
+    got = oracle_mod.from_spec(SPECS["cvt_bf16_f32"]).run(allb)[0].view(np.uint32)
+    ref = _tbf(allb).float().numpy().view(np.uint32)
+    nan = ((allb & 0x7F80) == 0x7F80) & ((allb & 0x7F) != 0)
+    assert np.array_equal(got[~nan], ref[~nan]) and np.isnan(got[nan].view(np.float32)).all()
+    # binary32 -> bfloat16: every bfloat16 value, each midpoint to the next one and the midpoint's
+    # neighbours, plus random patterns
+    v = allb.astype(np.uint32) << 16
+    f = np.concatenate([v, v + 0x8000, v + 0x7FFF, v + 0x8001,
+                        np.random.default_rng(5).integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)])
+    got = oracle_mod.from_spec(SPECS["cvt_f32_bf16"]).run(f.view(np.float32))[0]
+    ref = _nbf(torch.from_numpy(f.view(np.float32)).to(torch.bfloat16))
+    _same16(got, ref, "bf16", "f32 -> bf16")
+    # binary16 <-> bfloat16: every pattern (through the exact binary32 value in torch)
+    got = oracle_mod.from_spec(SPECS["cvt_f16_bf16"]).run(allb.view(np.float16))[0]
+    ref = _nbf(torch.from_numpy(allb.view(np.float16).astype(np.float32)).to(torch.bfloat16))
+    _same16(got, ref, "bf16", "f16 -> bf16")
+    got = oracle_mod.from_spec(SPECS["cvt_bf16_f16"]).run(allb)[0].view(np.uint16)
+    ref = _tbf(allb).float().numpy().astype(np.float16).view(np.uint16)
+    _same16(got, ref, "f16", "bf16 -> f16")
+    # bfloat16 -> int32 equals the (pinned) binary32 -> int32 of the exact value
+    got = oracle_mod.from_spec(SPECS["cvt_bf16_i32"]).run(allb)[0]
+    ref = oracle_mod.from_spec(SPECS["cvt_f32_i32"]).run(_tbf(allb).float().numpy())[0]
+    assert np.array_equal(got, ref)
+
+
+def test_i32_to_bf16(oracle_mod):
+    """Below 2^24 an int32 is exact in binary32, so torch's int -> binary32 ->
+    bfloat16 is a single rounding; above it, each result is checked to be a
+    nearest bfloat16 with an even fraction on ties, by exact integer
+    arithmetic on its two neighbours (brute force per element)."""
+    rng = np.random.default_rng(6)
+    small = np.concatenate([np.arange(-70000, 70000, dtype=np.int32),
+                            rng.integers(-(1 << 24), 1 << 24, 1 << 20, dtype=np.int64).astype(np.int32)])
+    got = oracle_mod.from_spec(SPECS["cvt_i32_bf16"]).run(small)[0]
+    ref = _nbf(torch.from_numpy(small.astype(np.float32)).to(torch.bfloat16))
+    _same16(got, ref, "bf16", "small int32 -> bf16")
+    big = rng.integers(-(1 << 31), 1 << 31, 20000, dtype=np.int64)
+    big = big[np.abs(big) >= (1 << 24)]
+    ties = np.array([(1 << 24) + (k << 16) for k in range(8)] + [(1 << 30) + (3 << 22), -(1 << 26) - (1 << 18)],
+                    dtype=np.int64)
+    big = np.concatenate([big, ties, ties + 1, ties - 1]).astype(np.int32)
+    got = oracle_mod.from_spec(SPECS["cvt_i32_bf16"]).run(big)[0]
+    vals = _tbf(got).double().numpy()
+    for i, g, r in zip(big.tolist(), got.tolist(), vals.tolist()):
+        m = abs(i)
+        ulp = 1 << (m.bit_length() - 8)          # bfloat16 spacing in m's binade
+        lo = (m // ulp) * ulp
+        hi = lo + ulp
+        if 2 * (m - lo) < ulp or (2 * (m - lo) == ulp and (lo // ulp) % 2 == 0):
+            want = lo
+        else:
+            want = hi
+        assert int(r) == (want if i > 0 else -want), (i, hex(g))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_16bit_invariants(oracle_mod, dt):
+    """x*1 = x, x+(+0) = x (x != -0), x+y = y+x, x*y = y*x, x-y = x+Neg(y),
+    Neg(Neg(x)) = x, x-x = +0 for finite x: bit for bit on every pattern
+    (the second operands at random)."""
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    one = np.full_like(allb, 0x3C00 if dt == "f16" else 0x3F80)
+    zero = np.zeros_like(allb)
+    nan = _nan16(allb, dt)
+    run = lambda name, *xs: _oracle16(oracle_mod, "%s_%s" % (name, dt), dt, *xs)
+    _same16(run("mul", allb, one), allb, dt, "x*1")
+    keep = allb != 0x8000
+    _same16(run("add", allb, zero)[keep], allb[keep], dt, "x+0")
+    y = np.random.default_rng(8).permutation(allb)
+    _same16(run("add", allb, y), run("add", y, allb), dt, "x+y")
+    _same16(run("mul", allb, y), run("mul", y, allb), dt, "x*y")
+    neg_y = (y ^ 0x8000).astype(np.uint16)
+    _same16(run("sub", allb, y), run("add", allb, neg_y), dt, "x-y")
+    (nn,) = oracle_mod.from_spec([("x", ("load", dt, 1)), ("a", ("neg", "x")), ("b", ("neg", "a")),
+                                   ("o", ("store", "b", 1))]).run(allb.view(np.float16) if dt == "f16" else allb)
+    assert np.array_equal(nn.view(np.uint16), allb)
+    inf = (allb & (0x7C00 if dt == "f16" else 0x7F80)) == (0x7C00 if dt == "f16" else 0x7F80)
+    d = run("sub", allb, allb)
+    assert np.all(d[~inf] == 0) and np.all(_nan16(d[inf], dt))
+
+
+@pytest.mark.parametrize("wl", ["axpby_f16", "axpby_bf16"])
+def test_16bit_axpby_workloads_vs_libraries(oracle_mod, wl):
+    vals, _ = W.make_inputs(wl, 1 << 18)
+    (o,) = oracle_mod.from_spec(W.WORKLOADS[wl]["spec"]).run(*vals, nthreads=8)
+    if wl == "axpby_f16":
+        x, y, al, be = vals
+        ref = (al * x + be * y).view(np.uint16)
+        _same16(o.view(np.uint16), ref, "f16", wl)
+    else:
+        x, y = _tbf(vals[0]), _tbf(vals[1])
+        al, be = _tbf(np.array([vals[2]])), _tbf(np.array([vals[3]]))
+        _same16(o, _nbf(al * x + be * y), "bf16", wl)

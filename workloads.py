@@ -100,6 +100,20 @@ FILL_F32 = [
     ("out", ("store", "s", 1)),
 ]
 
+# Native binary16 / bfloat16 arithmetic: out = alpha*x + beta*y computed in
+# the 16-bit format itself (each operation rounded once to it).
+AXPBY_F16 = [
+    ("x", ("load", "f16", 1)),
+    ("y", ("load", "f16", 1)),
+    ("alpha", ("scalar", "f16")),
+    ("beta", ("scalar", "f16")),
+    ("ax", ("mul", "alpha", "x")),
+    ("by", ("mul", "beta", "y")),
+    ("r", ("add", "ax", "by")),
+    ("out", ("store", "r", 1)),
+]
+AXPBY_BF16 = [(n, (st[0], "bf16") + st[2:]) if st[0] in ("load", "scalar") else (n, st) for n, st in AXPBY_F16]
+
 # Views of rank 3 and 4.  A batch of transposed planes: out[b] = X[b] + alpha * Y[b]^T.
 BATCHED_TRANSPOSE = [
     ("X", ("load", "f32", 3)),
@@ -146,6 +160,11 @@ WORKLOADS = {
                               label="out[b,i,j] = X[b,i,j] + alpha*Y[b,j,i], fp32, 64 x 2048 x 2048, alpha=2"),
     "bias_nchw": dict(index=9, spec=BIAS_NCHW, shape=(32, 256, 128, 256), varies={"scale": (1,), "bias": (1,)},
                       label="out = x*scale[c] + bias[c], fp32 NCHW 32 x 256 x 128 x 256, per-channel broadcast"),
+    # Native 16-bit arithmetic.
+    "axpby_f16": dict(index=10, spec=AXPBY_F16, n=1 << 28,
+                      label="out = alpha*x + beta*y in binary16, n=2^28, alpha=1.5, beta=-0.25"),
+    "axpby_bf16": dict(index=11, spec=AXPBY_BF16, n=1 << 28,
+                       label="out = alpha*x + beta*y in bfloat16, n=2^28, alpha=1.5, beta=-0.25"),
 }
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
@@ -157,6 +176,9 @@ SCALARS = {
     "classify_u32": {"t": np.int32(-2**31)},          # 0x80000000 as unsigned
     "fill_f32": {"s": np.float32(1.25)},
     "batched_transpose": {"alpha": np.float32(2.0)},
+    "axpby_f16": {"alpha": np.float16(1.5), "beta": np.float16(-0.25)},
+    # bfloat16 values are uint16 bit patterns: 1.5 = 0x3fc0, -0.25 = 0xbe80
+    "axpby_bf16": {"alpha": np.uint16(0x3FC0), "beta": np.uint16(0xBE80)},
 }
 
 
@@ -237,6 +259,14 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
     elif workload == "mixed_two_out":
         vals = [_uniform_pm4_f16(rng, n) for _ in range(3)]
         vals.append(sc["s"])
+    elif workload == "axpby_f16":
+        vals = [rng.standard_normal(n, dtype=np.float32).astype(np.float16) for _ in range(2)]
+        vals += [sc["alpha"], sc["beta"]]
+    elif workload == "axpby_bf16":
+        # bfloat16 bit patterns: the upper half of binary32 normal draws
+        vals = [(rng.standard_normal(n, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+                for _ in range(2)]
+        vals += [sc["alpha"], sc["beta"]]
     elif workload == "copy_f32":
         vals = [_uniform_pm1_f32(rng, n)]
     elif workload == "classify_u32":
@@ -280,7 +310,7 @@ def algorithmic_read_write(workload: str, n: int | None = None, shape=None):
     shp = shape_of(workload, n, shape)
     elems = int(np.prod(shp, dtype=np.int64))
     varies = w.get("varies", {})
-    size = {"f16": 2, "f32": 4, "i32": 4}
+    size = {"f16": 2, "bf16": 2, "f32": 4, "i32": 4}
     dt = {}
     rd = wr = 0
     for name, st in w["spec"]:
