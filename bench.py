@@ -27,10 +27,11 @@ PEAK_GBPS = 8000.0        # MI355X HBM3E peak, 8 TB/s
 METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, per Command"
 DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two_out": "f16/f32",
             "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32",
-            "batched_transpose": "f32", "bias_nchw": "f32"}
+            "batched_transpose": "f32", "bias_nchw": "f32", "axpby_f16": "f16", "axpby_bf16": "bf16"}
 # Measured besides the five configurations: the plain copy (the bandwidth and
-# counter reference), the widened op set and the rank-3/4 views.
-EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw"]
+# counter reference), the widened op set, the rank-3/4 views and native 16-bit
+# arithmetic.
+EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "axpby_f16", "axpby_bf16"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -59,7 +60,7 @@ def setup(wl, n=None):
     dev = torch.device("cuda:0")
     gv = W.to_torch(vals, extra, dev)
     shape = W.shape_of(wl, n)
-    td = {"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}
+    td = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32}
     out_dt = []
     dts = {}
     for name, st in spec:
@@ -137,7 +138,7 @@ def cpu_baseline(wl, budget_s=20.0):
     threads = max(1, min(16, os.cpu_count() or 1))
     full = W.WORKLOADS[wl].get("n")
     n = full if wl != "transposed_2d" else 2048
-    if wl in ("axpby_f32", "mixed_two_out"):
+    if wl in ("axpby_f32", "mixed_two_out", "axpby_f16", "axpby_bf16"):
         n = 1 << 24
     shape = {"batched_transpose": (4, 2048, 2048), "bias_nchw": (2, 256, 128, 256)}.get(wl)
     vals, extra = W.make_inputs(wl, n, shape=shape)

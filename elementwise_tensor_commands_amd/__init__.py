@@ -24,7 +24,7 @@ import struct
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libecmd.so")
 
-F16, F32, I32 = 1, 2, 3
+F16, F32, I32, BF16 = 1, 2, 3, 4
 E_ADD, E_SUB, E_MUL, E_NEG, E_CVT = 1, 2, 3, 4, 5
 E_CMP = {"eq": 6, "ne": 7, "lt": 8, "le": 9, "gt": 10, "ge": 11, "ltu": 12, "leu": 13, "gtu": 14, "geu": 15}
 E_MIN, E_MAX, E_ABS, E_SELECT = 16, 17, 18, 19
@@ -36,8 +36,8 @@ STATUS = {
     -5: "CMD_E_STRIDE", -6: "CMD_E_ALIAS", -7: "CMD_E_LIMIT", -8: "CMD_E_NOSTORE",
     -9: "CMD_E_STATE", -10: "CMD_E_LAUNCH", -11: "CMD_E_NOMEM",
 }
-DTYPES = {"f16": F16, "f32": F32, "i32": I32}
-DTYPE_NAMES = {F16: "f16", F32: "f32", I32: "i32"}
+DTYPES = {"f16": F16, "f32": F32, "i32": I32, "bf16": BF16}
+DTYPE_NAMES = {F16: "f16", F32: "f32", I32: "i32", BF16: "bf16"}
 
 
 class Error(RuntimeError):
@@ -113,7 +113,7 @@ def _dt(d) -> int:
 
 def _torch_dtype_code(t) -> int:
     import torch
-    return {torch.float16: F16, torch.float32: F32, torch.int32: I32}.get(t.dtype, 0)
+    return {torch.float16: F16, torch.float32: F32, torch.int32: I32, torch.bfloat16: BF16}.get(t.dtype, 0)
 
 
 def scalar_bits(value, dtype: int) -> int:
@@ -122,6 +122,16 @@ def scalar_bits(value, dtype: int) -> int:
         return struct.unpack("<I", struct.pack("<f", float(value)))[0]
     if dtype == I32:
         return int(value) & 0xFFFFFFFF
+    if dtype == BF16:
+        # a bfloat16 value is given as its bit pattern (numpy.uint16) or as a
+        # 0-d torch.bfloat16 tensor; a Python float is rejected rather than
+        # rounded here
+        if hasattr(value, "dtype") and str(value.dtype) == "uint16":
+            return int(value)
+        import torch
+        if isinstance(value, torch.Tensor) and value.dtype == torch.bfloat16 and value.numel() == 1:
+            return int(value.reshape(()).view(torch.int16).item()) & 0xFFFF
+        raise TypeError("bfloat16 scalars are numpy.uint16 bit patterns or 0-d torch.bfloat16 tensors")
     return struct.unpack("<H", struct.pack("<e", float(value)))[0]
 
 

@@ -50,6 +50,66 @@ __device__ __forceinline__ uint32_t f2h(uint32_t f)
     return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
+// bfloat16 -> binary32: the 16 bits are binary32's upper half (exact).
+__device__ __forceinline__ uint32_t bf2f(uint32_t h) { return h << 16; }
+
+// binary32 -> bfloat16: gfx950 converts in one instruction (v_cvt_pk_bf16_f32,
+// two values per instruction), rounding to nearest even under the default
+// round mode, with binary32 subnormals kept (FP32 denorm mode 3) and NaN kept
+// NaN.  The GPU tests compare it with the oracle on all 2^32 patterns.
+__device__ __forceinline__ uint32_t f2bf(uint32_t f)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)as_f(f));
+}
+
+// int32 -> bfloat16, rounded once from the exact integer (through binary32
+// would round twice: 2^24 + 2^16 + 1 would land on a midpoint).  |a| is
+// shifted to an 8-bit significand; the dropped bits decide the rounding.
+__device__ __forceinline__ uint32_t i2bf(uint32_t a)
+{
+    const uint32_t sign = (a >> 16) & 0x8000u;
+    const uint32_t m = (a & 0x80000000u) ? 0u - a : a;      // |INT_MIN| = 2^31 as unsigned
+    if (m == 0u) return 0u;
+    uint32_t e = 31u - (uint32_t)__builtin_clz(m);           // leading bit position
+    uint32_t q;
+    if (e <= 7u) {
+        q = m << (7u - e);
+    } else {
+        const uint32_t sh = e - 7u;
+        q = m >> sh;
+        const uint32_t rem = m & ((1u << sh) - 1u), half = 1u << (sh - 1u);
+        if (rem > half || (rem == half && (q & 1u))) ++q;
+        if (q == 256u) {                                     // carried into the next binade
+            q = 128u;
+            ++e;
+        }
+    }
+    return sign | ((e + 127u) << 7) | (q & 0x7fu);
+}
+
+// Value of a binary16 / bfloat16 pattern as binary32 bits (exact).
+template <bool BF>
+__device__ __forceinline__ uint32_t h16f(uint32_t h) { return BF ? bf2f(h) : h2f(h); }
+
+// binary16 / bfloat16 minimum and maximum on the exact values; the result is
+// one operand's 16-bit pattern (NaN operand ignored unless both are, -0 below +0).
+template <bool BF, bool MAX>
+__device__ __forceinline__ uint32_t minmax16(uint32_t a, uint32_t b)
+{
+    const float x = as_f(h16f<BF>(a)), y = as_f(h16f<BF>(b));
+    if (!(x == x)) return b;
+    if (!(y == y)) return a;
+    if (MAX ? x > y : x < y) return a;
+    if (MAX ? y > x : y < x) return b;
+    const bool a_neg = (a & 0x8000u) != 0u;
+    return (MAX ? !a_neg : a_neg) ? a : b;
+}
+
+// binary16 arithmetic in the format itself (v_add_f16 and friends: one IEEE
+// rounding, binary16 subnormals kept in FP16 denorm mode 3).
+__device__ __forceinline__ _Float16 as_h(uint32_t u) { return __builtin_bit_cast(_Float16, (uint16_t)u); }
+__device__ __forceinline__ uint32_t h_bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
+
 // binary32 -> int32: truncate toward zero, saturate, NaN -> 0.  Written out so
 // that no out-of-range conversion (undefined in C++) is ever performed.
 __device__ __forceinline__ uint32_t f2i_sat(float f)
@@ -128,6 +188,39 @@ __device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b, uint32_t c = 0
     else if constexpr (C == C_ABS_I32) return (a & 0x80000000u) ? 0u - a : a;
     else if constexpr (C == C_ABS_F16) return a & 0x7fffu;
     else if constexpr (C == C_SELECT) return a != 0u ? b : c;
+    else if constexpr (C == C_ADD_F16) return h_bits(as_h(a) + as_h(b));
+    else if constexpr (C == C_SUB_F16) return h_bits(as_h(a) - as_h(b));
+    else if constexpr (C == C_MUL_F16) return h_bits(as_h(a) * as_h(b));
+    // bfloat16 arithmetic through binary32: the binary32 result of two
+    // bfloat16 operands, rounded to bfloat16, equals the exact result rounded
+    // once (24 >= 2*8 + 2 bits; Figueroa 1995).
+    else if constexpr (C == C_ADD_BF16) return f2bf(as_u(as_f(bf2f(a)) + as_f(bf2f(b))));
+    else if constexpr (C == C_SUB_BF16) return f2bf(as_u(as_f(bf2f(a)) - as_f(bf2f(b))));
+    else if constexpr (C == C_MUL_BF16) return f2bf(as_u(as_f(bf2f(a)) * as_f(bf2f(b))));
+    else if constexpr (C == C_NEG_BF16) return (a ^ 0x8000u) & 0xffffu;
+    else if constexpr (C == C_ABS_BF16) return a & 0x7fffu;
+    else if constexpr (C == C_CVT_F16_BF16) return f2bf(h2f(a));
+    else if constexpr (C == C_CVT_BF16_F16) return f2h(bf2f(a));
+    else if constexpr (C == C_CVT_BF16_F32) return bf2f(a);
+    else if constexpr (C == C_CVT_F32_BF16) return f2bf(a);
+    else if constexpr (C == C_CVT_BF16_I32) return f2i_sat(as_f(bf2f(a)));
+    else if constexpr (C == C_CVT_I32_BF16) return i2bf(a);
+    else if constexpr (C == C_EQ_F16) return as_f(h2f(a)) == as_f(h2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_NE_F16) return as_f(h2f(a)) != as_f(h2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_LT_F16) return as_f(h2f(a)) < as_f(h2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_LE_F16) return as_f(h2f(a)) <= as_f(h2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_GT_F16) return as_f(h2f(a)) > as_f(h2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_GE_F16) return as_f(h2f(a)) >= as_f(h2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_EQ_BF16) return as_f(bf2f(a)) == as_f(bf2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_NE_BF16) return as_f(bf2f(a)) != as_f(bf2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_LT_BF16) return as_f(bf2f(a)) < as_f(bf2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_LE_BF16) return as_f(bf2f(a)) <= as_f(bf2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_GT_BF16) return as_f(bf2f(a)) > as_f(bf2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_GE_BF16) return as_f(bf2f(a)) >= as_f(bf2f(b)) ? 1u : 0u;
+    else if constexpr (C == C_MIN_F16) return minmax16<false, false>(a, b);
+    else if constexpr (C == C_MAX_F16) return minmax16<false, true>(a, b);
+    else if constexpr (C == C_MIN_BF16) return minmax16<true, false>(a, b);
+    else if constexpr (C == C_MAX_BF16) return minmax16<true, true>(a, b);
     else return 0u;
 }
 
@@ -210,6 +303,16 @@ __device__ __forceinline__ void rt_apply(uint8_t code, const uint32_t (&a)[E], c
         ECMD_APPLY(C_LT_U32) ECMD_APPLY(C_LE_U32) ECMD_APPLY(C_GT_U32) ECMD_APPLY(C_GE_U32)
         ECMD_APPLY(C_MIN_F32) ECMD_APPLY(C_MAX_F32) ECMD_APPLY(C_MIN_I32) ECMD_APPLY(C_MAX_I32)
         ECMD_APPLY(C_ABS_F32) ECMD_APPLY(C_ABS_I32) ECMD_APPLY(C_ABS_F16) ECMD_APPLY(C_SELECT)
+        ECMD_APPLY(C_ADD_F16) ECMD_APPLY(C_SUB_F16) ECMD_APPLY(C_MUL_F16)
+        ECMD_APPLY(C_ADD_BF16) ECMD_APPLY(C_SUB_BF16) ECMD_APPLY(C_MUL_BF16)
+        ECMD_APPLY(C_NEG_BF16) ECMD_APPLY(C_ABS_BF16)
+        ECMD_APPLY(C_CVT_F16_BF16) ECMD_APPLY(C_CVT_BF16_F16) ECMD_APPLY(C_CVT_BF16_F32)
+        ECMD_APPLY(C_CVT_F32_BF16) ECMD_APPLY(C_CVT_BF16_I32) ECMD_APPLY(C_CVT_I32_BF16)
+        ECMD_APPLY(C_EQ_F16) ECMD_APPLY(C_NE_F16) ECMD_APPLY(C_LT_F16) ECMD_APPLY(C_LE_F16)
+        ECMD_APPLY(C_GT_F16) ECMD_APPLY(C_GE_F16)
+        ECMD_APPLY(C_EQ_BF16) ECMD_APPLY(C_NE_BF16) ECMD_APPLY(C_LT_BF16) ECMD_APPLY(C_LE_BF16)
+        ECMD_APPLY(C_GT_BF16) ECMD_APPLY(C_GE_BF16)
+        ECMD_APPLY(C_MIN_F16) ECMD_APPLY(C_MAX_F16) ECMD_APPLY(C_MIN_BF16) ECMD_APPLY(C_MAX_BF16)
 #undef ECMD_APPLY
     default:
         _Pragma("unroll") for (int e = 0; e < E; ++e) r[e] = 0u;
@@ -306,7 +409,7 @@ template <int E, bool VEC>
 __device__ __forceinline__ void load_elems(const void *p, uint8_t ty, int64_t i, int count,
                                            uint32_t (&v)[E])
 {
-    if (ty == TY_F16) {
+    if (is16(ty)) {
         const uint16_t *q = static_cast<const uint16_t *>(p) + i;
         if constexpr (VEC) {
             static_assert(E % 8 == 0 || E == 4, "binary16 vectors are 8 or 4 wide");
@@ -355,7 +458,7 @@ template <int E, bool VEC, bool NT>
 __device__ __forceinline__ void store_elems(void *p, uint8_t ty, int64_t i, int count,
                                             const uint32_t (&v)[E])
 {
-    if (ty == TY_F16) {
+    if (is16(ty)) {
         uint16_t *q = static_cast<uint16_t *>(p) + i;
         if constexpr (VEC) {
             if constexpr (E % 8 == 0) {
@@ -422,7 +525,7 @@ __device__ __forceinline__ void load_group(const void *p, uint8_t ty, int64_t i,
 {
     static_assert(G == 4 || G == 8, "group of 4 or 8");
     if constexpr (VEC) {
-        if (ty == TY_F16) {
+        if (is16(ty)) {
             const uint16_t *q = static_cast<const uint16_t *>(p) + i;
             if constexpr (G == 8) {
                 const u32x4 d = ld<NTL>(reinterpret_cast<const u32x4 *>(q));
@@ -460,7 +563,7 @@ __device__ __forceinline__ void store_group(void *p, uint8_t ty, int64_t i, int 
 {
     static_assert(G == 4 || G == 8, "group of 4 or 8");
     if constexpr (VEC) {
-        if (ty == TY_F16) {
+        if (is16(ty)) {
             uint16_t *q = static_cast<uint16_t *>(p) + i;
             if constexpr (G == 8) {
                 u32x4 d;

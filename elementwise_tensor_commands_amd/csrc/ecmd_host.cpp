@@ -121,37 +121,52 @@ int fail(cmd_t h, int code, const char *fmt, ...)
     return code;
 }
 
-bool valid_dtype(int d) { return d == CMD_F16 || d == CMD_F32 || d == CMD_I32; }
-int esize(int d) { return d == CMD_F16 ? 2 : 4; }
-const char *dtype_name(int d) { return d == CMD_F16 ? "f16" : d == CMD_F32 ? "f32" : d == CMD_I32 ? "i32" : "?"; }
+bool valid_dtype(int d) { return d == CMD_F16 || d == CMD_F32 || d == CMD_I32 || d == CMD_BF16; }
+int esize(int d) { return d == CMD_F16 || d == CMD_BF16 ? 2 : 4; }
+const char *dtype_name(int d)
+{
+    return d == CMD_F16 ? "f16" : d == CMD_F32 ? "f32" : d == CMD_I32 ? "i32" : d == CMD_BF16 ? "bf16" : "?";
+}
+
+// One code per (operation, type); pick(d, f32, i32, f16, bf16).
+int pick(int d, int f32, int i32, int f16, int bf16)
+{
+    return d == CMD_F32 ? f32 : d == CMD_I32 ? i32 : d == CMD_F16 ? f16 : bf16;
+}
 
 int opcode_for(int op, int src, int dst)
 {
-    if (op >= E_CMP_EQ && op <= E_CMP_GE) {
-        const int k = op - E_CMP_EQ;
-        return (src == CMD_F32 ? C_EQ_F32 : C_EQ_I32) + k;
-    }
+    if (op >= E_CMP_EQ && op <= E_CMP_GE)
+        return pick(src, C_EQ_F32, C_EQ_I32, C_EQ_F16, C_EQ_BF16) + (op - E_CMP_EQ);
     switch (op) {
     case E_CMP_LTU: return C_LT_U32;
     case E_CMP_LEU: return C_LE_U32;
     case E_CMP_GTU: return C_GT_U32;
     case E_CMP_GEU: return C_GE_U32;
-    case E_MIN: return dst == CMD_F32 ? C_MIN_F32 : C_MIN_I32;
-    case E_MAX: return dst == CMD_F32 ? C_MAX_F32 : C_MAX_I32;
-    case E_ABS: return dst == CMD_F32 ? C_ABS_F32 : dst == CMD_I32 ? C_ABS_I32 : C_ABS_F16;
+    case E_MIN: return pick(dst, C_MIN_F32, C_MIN_I32, C_MIN_F16, C_MIN_BF16);
+    case E_MAX: return pick(dst, C_MAX_F32, C_MAX_I32, C_MAX_F16, C_MAX_BF16);
+    case E_ABS: return pick(dst, C_ABS_F32, C_ABS_I32, C_ABS_F16, C_ABS_BF16);
     case E_SELECT: return C_SELECT;
-    case E_ADD: return dst == CMD_F32 ? C_ADD_F32 : C_ADD_I32;
-    case E_SUB: return dst == CMD_F32 ? C_SUB_F32 : C_SUB_I32;
-    case E_MUL: return dst == CMD_F32 ? C_MUL_F32 : C_MUL_I32;
-    case E_NEG: return dst == CMD_F32 ? C_NEG_F32 : dst == CMD_I32 ? C_NEG_I32 : C_NEG_F16;
+    case E_ADD: return pick(dst, C_ADD_F32, C_ADD_I32, C_ADD_F16, C_ADD_BF16);
+    case E_SUB: return pick(dst, C_SUB_F32, C_SUB_I32, C_SUB_F16, C_SUB_BF16);
+    case E_MUL: return pick(dst, C_MUL_F32, C_MUL_I32, C_MUL_F16, C_MUL_BF16);
+    case E_NEG: return pick(dst, C_NEG_F32, C_NEG_I32, C_NEG_F16, C_NEG_BF16);
     case E_CVT:
         if (src == dst) return C_MOV;
-        if (src == CMD_F16 && dst == CMD_F32) return C_CVT_F16_F32;
-        if (src == CMD_F32 && dst == CMD_F16) return C_CVT_F32_F16;
-        if (src == CMD_I32 && dst == CMD_F32) return C_CVT_I32_F32;
-        if (src == CMD_F32 && dst == CMD_I32) return C_CVT_F32_I32;
-        if (src == CMD_I32 && dst == CMD_F16) return C_CVT_I32_F16;
-        return C_CVT_F16_I32;
+        switch (src * 10 + dst) {
+        case CMD_F16 * 10 + CMD_F32: return C_CVT_F16_F32;
+        case CMD_F32 * 10 + CMD_F16: return C_CVT_F32_F16;
+        case CMD_I32 * 10 + CMD_F32: return C_CVT_I32_F32;
+        case CMD_F32 * 10 + CMD_I32: return C_CVT_F32_I32;
+        case CMD_I32 * 10 + CMD_F16: return C_CVT_I32_F16;
+        case CMD_F16 * 10 + CMD_I32: return C_CVT_F16_I32;
+        case CMD_F16 * 10 + CMD_BF16: return C_CVT_F16_BF16;
+        case CMD_BF16 * 10 + CMD_F16: return C_CVT_BF16_F16;
+        case CMD_BF16 * 10 + CMD_F32: return C_CVT_BF16_F32;
+        case CMD_F32 * 10 + CMD_BF16: return C_CVT_F32_BF16;
+        case CMD_BF16 * 10 + CMD_I32: return C_CVT_BF16_I32;
+        default: return C_CVT_I32_BF16;
+        }
     }
     return C_MOV;
 }
@@ -165,7 +180,12 @@ const char *code_name(int c)
                                   "ge.f32", "eq.i32", "ne.i32", "lt.i32", "le.i32", "gt.i32",
                                   "ge.i32", "lt.u32", "le.u32", "gt.u32", "ge.u32", "min.f32",
                                   "max.f32", "min.i32", "max.i32", "abs.f32", "abs.i32", "abs.f16",
-                                  "select"};
+                                  "select", "add.f16", "sub.f16", "mul.f16", "add.bf16", "sub.bf16",
+                                  "mul.bf16", "neg.bf16", "abs.bf16", "cvt.f16.bf16", "cvt.bf16.f16",
+                                  "cvt.bf16.f32", "cvt.f32.bf16", "cvt.bf16.i32", "cvt.i32.bf16",
+                                  "eq.f16", "ne.f16", "lt.f16", "le.f16", "gt.f16", "ge.f16",
+                                  "eq.bf16", "ne.bf16", "lt.bf16", "le.bf16", "gt.bf16", "ge.bf16",
+                                  "min.f16", "max.f16", "min.bf16", "max.bf16"};
     static_assert(sizeof(names) / sizeof(names[0]) == C_COUNT, "one name per code");
     return c >= 0 && c < C_COUNT ? names[c] : "?";
 }
@@ -257,7 +277,10 @@ int lower(cmd_t h)
         const int c = code[t];
         const bool commutes = c == C_ADD_F32 || c == C_MUL_F32 || c == C_ADD_I32 || c == C_MUL_I32 ||
                               c == C_EQ_F32 || c == C_NE_F32 || c == C_EQ_I32 || c == C_NE_I32 ||
-                              c == C_MIN_F32 || c == C_MAX_F32 || c == C_MIN_I32 || c == C_MAX_I32;
+                              c == C_MIN_F32 || c == C_MAX_F32 || c == C_MIN_I32 || c == C_MAX_I32 ||
+                              c == C_ADD_F16 || c == C_MUL_F16 || c == C_ADD_BF16 || c == C_MUL_BF16 ||
+                              c == C_EQ_F16 || c == C_NE_F16 || c == C_EQ_BF16 || c == C_NE_BF16 ||
+                              c == C_MIN_F16 || c == C_MAX_F16 || c == C_MIN_BF16 || c == C_MAX_BF16;
         if (commutes && rb < ra) std::swap(ra, rb);
         P.ops[i].code = (uint8_t)c;
         P.ops[i].dst = (uint8_t)ref[t];
@@ -340,9 +363,13 @@ int64_t env_int(const char *name, int64_t dflt)
 constexpr int64_t kMallBytes = (int64_t)256 << 20;
 constexpr int kDefaultTileM = 32, kDefaultTileN = 256, kDefaultTileBlock = 512, kDefaultTileWalk = 1;
 
-LinearShape linear_shape(int64_t bytes)
+// Linear kernel shape: one 16-byte vector per operand per work-item -- 4
+// elements when any operand is 32-bit (E = 4 measured fastest there), 8 when
+// every operand is binary16 / bfloat16 (4 elements would be 8-byte accesses:
+// 5.1 against 6.5 TB/s for the 16-bit axpby).
+LinearShape linear_shape(int64_t bytes, bool all16 = false)
 {
-    LinearShape s{4, 4, bytes > kMallBytes, true};
+    LinearShape s{all16 ? 8 : 4, all16 ? 8 : 4, bytes > kMallBytes, true};
     const char *v = std::getenv("ECMD_LINEAR_SHAPE");
     if (v && std::strcmp(v, "8x8") == 0) s.e = 8, s.g = 8;
     if (v && std::strcmp(v, "8x4") == 0) s.e = 8, s.g = 4;
@@ -414,8 +441,8 @@ int bind(cmd_t h, const cmd_arg *args, int nargs, Bound &B)
                         dtype_name(d.dtype));
         if (a.reserved != 0) return fail(h, CMD_E_ARG, "argument %d: reserved field is not 0", i);
         if (d.kind != CMD_ARG_TENSOR) {
-            if (d.dtype == CMD_F16 && (a.bits >> 16) != 0)
-                return fail(h, CMD_E_ARG, "argument %d: binary16 scalar has bits above bit 15", i);
+            if (esize(d.dtype) == 2 && (a.bits >> 16) != 0)
+                return fail(h, CMD_E_ARG, "argument %d: 16-bit scalar has bits above bit 15", i);
             continue;
         }
         int64_t shp[4] = {1, 1, 1, 1};
@@ -582,9 +609,10 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         for (int k = 0; k < P.n_out; ++k) S.vec = S.vec && aligned(B.out[k].ptr, 16);
         S.variant = (S.vec && !force_generic) ? program_match_linear(P) : -1;
         int64_t bytes = 0;
-        for (int k = 0; k < P.n_in; ++k) bytes += numel * esize(B.in[k].dtype);
-        for (int k = 0; k < P.n_out; ++k) bytes += numel * esize(B.out[k].dtype);
-        S.shape = linear_shape(bytes);
+        bool all16 = true;
+        for (int k = 0; k < P.n_in; ++k) bytes += numel * esize(B.in[k].dtype), all16 = all16 && esize(B.in[k].dtype) == 2;
+        for (int k = 0; k < P.n_out; ++k) bytes += numel * esize(B.out[k].dtype), all16 = all16 && esize(B.out[k].dtype) == 2;
+        S.shape = linear_shape(bytes, all16);
         if (S.variant < 0) S.shape.e = 4, S.shape.g = 4;   // the interpreter has one shape
         S.e = S.shape.e;
         S.block = kLinearBlock;
@@ -875,8 +903,6 @@ int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, 
         const int db = h->nodes[b].dtype;
         if (da != db)
             return fail(h, CMD_E_DTYPE, "operands are %s and %s", dtype_name(da), dtype_name(db));
-        if (da == CMD_F16)
-            return fail(h, CMD_E_DTYPE, "binary16 is a storage type: convert to f32 first");
         const bool cmp = opcode >= E_CMP_EQ && opcode <= E_CMP_GEU;
         if (opcode >= E_CMP_LTU && opcode <= E_CMP_GEU && da != CMD_I32)
             return fail(h, CMD_E_DTYPE, "unsigned comparisons take int32 operands");

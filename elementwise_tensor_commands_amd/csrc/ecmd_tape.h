@@ -30,8 +30,10 @@ constexpr uint8_t kRefSlot = 8;
 constexpr uint8_t kRefUni = 16;
 constexpr uint8_t kRefNone = 255;
 
-// Element types; the numbers equal the public CMD_F16 / CMD_F32 / CMD_I32.
-enum Ty : uint8_t { TY_F16 = 1, TY_F32 = 2, TY_I32 = 3 };
+// Element types; the numbers equal the public CMD_F16 / CMD_F32 / CMD_I32 /
+// CMD_BF16.  binary16 and bfloat16 are 16-bit containers in memory.
+enum Ty : uint8_t { TY_F16 = 1, TY_F32 = 2, TY_I32 = 3, TY_BF16 = 4 };
+constexpr bool is16(uint8_t t) { return t == TY_F16 || t == TY_BF16; }
 
 // One opcode per (E_ operation, type) pair, so that the evaluator dispatches
 // on a single byte.
@@ -76,6 +78,36 @@ enum Code : uint8_t {
     C_ABS_I32,
     C_ABS_F16,
     C_SELECT,      // a != 0 ? b : c
+    C_ADD_F16,     // binary16 / bfloat16 arithmetic: exact result rounded once
+    C_SUB_F16,
+    C_MUL_F16,
+    C_ADD_BF16,
+    C_SUB_BF16,
+    C_MUL_BF16,
+    C_NEG_BF16,
+    C_ABS_BF16,
+    C_CVT_F16_BF16,
+    C_CVT_BF16_F16,
+    C_CVT_BF16_F32,
+    C_CVT_F32_BF16,
+    C_CVT_BF16_I32,
+    C_CVT_I32_BF16,
+    C_EQ_F16,
+    C_NE_F16,
+    C_LT_F16,
+    C_LE_F16,
+    C_GT_F16,
+    C_GE_F16,
+    C_EQ_BF16,
+    C_NE_BF16,
+    C_LT_BF16,
+    C_LE_BF16,
+    C_GT_BF16,
+    C_GE_BF16,
+    C_MIN_F16,
+    C_MAX_F16,
+    C_MIN_BF16,
+    C_MAX_BF16,
     C_COUNT
 };
 
@@ -96,7 +128,7 @@ struct Program {
     TapeOp ops[kMaxOps];
 };
 
-constexpr int ty_size(uint8_t t) { return t == TY_F16 ? 2 : 4; }
+constexpr int ty_size(uint8_t t) { return is16(t) ? 2 : 4; }
 
 // ---------------------------------------------------------------------------
 // Kernel argument blocks.  Each kernel takes one of these by value; the whole
@@ -219,6 +251,18 @@ constexpr Program kProgAffineF32 = {
     {{C_MUL_F32, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_IN(1)},
      {C_ADD_F32, ECMD_R_S(0), ECMD_R_IN(2), ECMD_R_S(0)}}};
 
+// out = alpha*x + beta*y computed in binary16 / bfloat16 (scalars of the same type)
+constexpr Program kProgAxpbyF16 = {
+    2, 2, 3, 1, {TY_F16, TY_F16}, {TY_F16}, {ECMD_R_S(0)},
+    {{C_MUL_F16, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_U(0)},
+     {C_MUL_F16, ECMD_R_S(1), ECMD_R_IN(1), ECMD_R_U(1)},
+     {C_ADD_F16, ECMD_R_S(0), ECMD_R_S(0), ECMD_R_S(1)}}};
+constexpr Program kProgAxpbyBF16 = {
+    2, 2, 3, 1, {TY_BF16, TY_BF16}, {TY_BF16}, {ECMD_R_S(0)},
+    {{C_MUL_BF16, ECMD_R_S(0), ECMD_R_IN(0), ECMD_R_U(0)},
+     {C_MUL_BF16, ECMD_R_S(1), ECMD_R_IN(1), ECMD_R_U(1)},
+     {C_ADD_BF16, ECMD_R_S(0), ECMD_R_S(0), ECMD_R_S(1)}}};
+
 // out = f16(x), out = f32(x)
 constexpr Program kProgCvtF32F16 = {
     1, 0, 1, 1, {TY_F32}, {TY_F16}, {ECMD_R_S(0)},
@@ -245,7 +289,9 @@ namespace ecmd {
     X(cvt_f16_f32, kProgCvtF16F32)        \
     X(classify_u32, kProgClassifyU32)     \
     X(fill_f32, kProgFillF32)             \
-    X(affine_f32, kProgAffineF32)
+    X(affine_f32, kProgAffineF32)         \
+    X(axpby_f16, kProgAxpbyF16)           \
+    X(axpby_bf16, kProgAxpbyBF16)
 
 #define ECMD_TILED_SPECIALISED(X)         \
     X(add_scaled_f32, kProgAddScaledF32)

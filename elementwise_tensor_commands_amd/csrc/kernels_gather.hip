@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kGatherBlock) void k_gather(const StridedArgs A)
                 uint32_t v = 0u;
                 if (e < count) {
                     const int64_t off = base + (c + e) * A.in_s[k][3];
-                    v = ty == TY_F16 ? (uint32_t) static_cast<const uint16_t *>(A.in[k])[off]
+                    v = is16(ty) ? (uint32_t) static_cast<const uint16_t *>(A.in[k])[off]
                                      : static_cast<const uint32_t *>(A.in[k])[off];
                 }
                 switch (k) {   // compile-time register names, see RtEval
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kGatherBlock) void k_gather(const StridedArgs A)
                 for (int e = 0; e < E; ++e) {
                     if (e < count) {
                         const int64_t off = base + (c + e) * A.out_s[k][3];
-                        if (ty == TY_F16) static_cast<uint16_t *>(A.out[k])[off] = (uint16_t)out[k][e];
+                        if (is16(ty)) static_cast<uint16_t *>(A.out[k])[off] = (uint16_t)out[k][e];
                         else static_cast<uint32_t *>(A.out[k])[off] = out[k][e];
                     }
                 }

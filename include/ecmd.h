@@ -25,16 +25,21 @@
  *            own (no fused multiply-add), subnormals kept (the default FP32 denorm
  *            mode 3 of the AMDHSA kernel descriptor, Silk "AMDGPU Backend",
  *            section "Code Object Format").  E_NEG flips the sign bit.
- *   CMD_F16  storage type: load, store, E_NEG, E_ABS, select and E_CVT only.
- *   E_CVT    f16->f32 exact; f32->f16 and i32->f16 round to nearest even with
- *            overflow to infinity and gradual underflow; i32->f32 rounds to
- *            nearest even; f32->i32 and f16->i32 truncate toward zero, saturate,
- *            and map NaN to 0.  A conversion to the same dtype is a copy.
- *   E_CMP_*  CMD_F32 or CMD_I32 operands of one dtype (the unsigned forms: CMD_I32),
- *            CMD_I32 result 1 or 0; binary32 comparisons are false when an
- *            operand is NaN, except E_CMP_NE, and -0 equals +0.
- *   E_MIN / E_MAX  CMD_I32 signed; CMD_F32 ignores a NaN operand unless both are
- *            NaN and orders -0 below +0 (IEEE 754-2019 minimumNumber/maximumNumber).
+ *   CMD_F16  IEEE binary16 and CMD_BF16 bfloat16 (binary32's sign and 8-bit
+ *            exponent with a 7-bit fraction) are compute types too: E_ADD, E_SUB
+ *            and E_MUL give the exact result rounded once to the operands'
+ *            format (nearest even, overflow to infinity, subnormals kept).
+ *   E_CVT    between any two of the four types: to a floating type, the exact
+ *            source value rounded once to nearest even, with overflow to
+ *            infinity and gradual underflow (f16->f32, bf16->f32 and f16->bf16
+ *            of small values are exact); to int32, truncate toward zero,
+ *            saturate and map NaN to 0.  A conversion to the same dtype is a copy.
+ *   E_CMP_*  operands of one dtype (the unsigned forms: CMD_I32), CMD_I32 result
+ *            1 or 0; floating comparisons are false when an operand is NaN,
+ *            except E_CMP_NE, and -0 equals +0.
+ *   E_MIN / E_MAX  CMD_I32 signed; floating types ignore a NaN operand unless
+ *            both are NaN and order -0 below +0 (IEEE 754-2019
+ *            minimumNumber/maximumNumber); the result is one operand's bits.
  *   E_ABS    clears the sign bit (any dtype); for CMD_I32 |INT_MIN| = INT_MIN.
  *   Select   cond != 0 ? x : y, cond CMD_I32, x and y of one dtype (cmd_select).
  *   Scalars broadcast to every element; a store of a scalar fills the output.
@@ -81,6 +86,7 @@ typedef int32_t cmd_tag;
 #define CMD_F16 1
 #define CMD_F32 2
 #define CMD_I32 3
+#define CMD_BF16 4
 
 /* E_ operations. */
 #define E_ADD 1

@@ -297,6 +297,12 @@ def f32_to_f16_range(first: int, count: int) -> np.ndarray:
     return out
 
 
+def f32_to_bf16_range(first: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.uint16)
+    lib().oracle_f32_to_bf16_range(first, count, out.ctypes.data)
+    return out
+
+
 def f16_to_f32_all() -> np.ndarray:
     out = np.empty(65536, dtype=np.uint32)
     lib().oracle_f16_to_f32_all(out.ctypes.data)

@@ -5,8 +5,10 @@ import os
 import numpy as np
 import torch
 
-TD = {"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}
-NPD = {"f16": np.float16, "f32": np.float32, "i32": np.int32}
+# bfloat16 has no NumPy type: on the host it is a uint16 array of bit patterns
+# (every uint16 array in these tests is one), on the device torch.bfloat16.
+TD = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32}
+NPD = {"f16": np.float16, "bf16": np.uint16, "f32": np.float32, "i32": np.int32}
 BITS = {2: np.uint16, 4: np.uint32}
 ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 
@@ -17,7 +19,23 @@ def dev():
 
 
 def to_dev(a):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev()).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev())
+
+
+def host(t):
+    """A device tensor as a NumPy array (bfloat16: uint16 bit patterns)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def _nan_mask(a):
+    if a.dtype == np.uint16:                 # bfloat16 bit patterns
+        return ((a & 0x7F80) == 0x7F80) & ((a & 0x7F) != 0)
+    return np.isnan(a)
 
 
 def bits(a):
@@ -36,8 +54,8 @@ def compare(got, ref, max_ulp=0, what=""):
     got, ref = np.asarray(got), np.asarray(ref)
     assert got.shape == ref.shape and got.dtype == ref.dtype, (got.shape, ref.shape, got.dtype, ref.dtype)
     gb, rb = bits(got).ravel(), bits(ref).ravel()
-    if got.dtype.kind == "f":
-        nan_g, nan_r = np.isnan(got).ravel(), np.isnan(ref).ravel()
+    if got.dtype.kind == "f" or got.dtype == np.uint16:
+        nan_g, nan_r = _nan_mask(got).ravel(), _nan_mask(ref).ravel()
         assert np.array_equal(nan_g, nan_r), "%s: NaN positions differ" % what
         gb, rb = gb[~nan_g], rb[~nan_r]
         if max_ulp:

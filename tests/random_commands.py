@@ -5,12 +5,12 @@ import numpy as np
 def _random_spec(rng, n_in, n_ops, rank):
     spec, dts, names = [], {}, []
     for i in range(n_in):
-        dt = rng.choice(["f16", "f32", "i32"])
+        dt = rng.choice(["f16", "bf16", "f32", "i32"])
         spec.append(("in%d" % i, ("load", dt, rank)))
         dts["in%d" % i] = dt
         names.append("in%d" % i)
     for i in range(rng.integers(0, 3)):
-        dt = rng.choice(["f32", "i32"])
+        dt = rng.choice(["f32", "i32", "f16", "bf16"])
         spec.append(("s%d" % i, ("scalar", dt)))
         dts["s%d" % i] = dt
         names.append("s%d" % i)
@@ -19,16 +19,13 @@ def _random_spec(rng, n_in, n_ops, rank):
         kind = rng.choice(["add", "sub", "mul", "neg", "cvt", "cvt", "min", "max", "abs", "cmp", "select"])
         nm = "t%d" % i
         if kind == "cmp":
-            if dts[a] == "f16":
-                kind = "cvt"
-            else:
-                same = [x for x in names if dts[x] == dts[a]]
-                b = same[rng.integers(len(same))]
-                how = rng.choice(["eq", "ne", "lt", "le", "gt", "ge"] + (["ltu", "leu", "gtu", "geu"] if dts[a] == "i32" else []))
-                spec.append((nm, (how, a, b)))
-                dts[nm] = "i32"
-                names.append(nm)
-                continue
+            same = [x for x in names if dts[x] == dts[a]]
+            b = same[rng.integers(len(same))]
+            how = rng.choice(["eq", "ne", "lt", "le", "gt", "ge"] + (["ltu", "leu", "gtu", "geu"] if dts[a] == "i32" else []))
+            spec.append((nm, (how, a, b)))
+            dts[nm] = "i32"
+            names.append(nm)
+            continue
         if kind == "select":
             conds = [x for x in names if dts[x] == "i32"]
             if conds:
@@ -47,19 +44,15 @@ def _random_spec(rng, n_in, n_ops, rank):
             names.append(nm)
             continue
         if kind in ("add", "sub", "mul", "min", "max"):
-            if dts[a] == "f16":
-                spec.append((nm, ("cvt", a, "f32")))
-                dts[nm] = "f32"
-            else:
-                same = [x for x in names if dts[x] == dts[a]]
-                b = same[rng.integers(len(same))]
-                spec.append((nm, (kind, a, b)))
-                dts[nm] = dts[a]
+            same = [x for x in names if dts[x] == dts[a]]
+            b = same[rng.integers(len(same))]
+            spec.append((nm, (kind, a, b)))
+            dts[nm] = dts[a]
         elif kind == "neg":
             spec.append((nm, ("neg", a)))
             dts[nm] = dts[a]
         else:
-            to = rng.choice(["f16", "f32", "i32"])
+            to = rng.choice(["f16", "bf16", "f32", "i32"])
             spec.append((nm, ("cvt", a, to)))
             dts[nm] = to
         names.append(nm)
@@ -80,10 +73,25 @@ def _random_inputs(rng, spec, shape):
                 b = rng.integers(0, 2**32, shape, dtype=np.uint64).astype(np.uint32)
                 f = b.view(np.float32)
                 f = np.where(rng.random(shape) < 0.5, rng.standard_normal(shape).astype(np.float32) * 100, f)
-                out.append(f.astype(np.float16) if st[1] == "f16" else f.astype(np.float32))
+                if st[1] == "bf16":          # bfloat16 bit patterns: the upper halves of the draws
+                    out.append((f.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+                else:
+                    out.append(f.astype(np.float16) if st[1] == "f16" else f.astype(np.float32))
         elif st[0] == "scalar":
-            out.append(np.float32(rng.standard_normal()) if st[1] == "f32" else np.int32(rng.integers(-1000, 1000)))
+            out.append(random_scalar(rng, st[1]))
     return out
+
+
+def random_scalar(rng, dt):
+    """A scalar CommandArgument value (bfloat16: a numpy.uint16 bit pattern)."""
+    if dt == "i32":
+        return np.int32(rng.integers(-1000, 1000))
+    f = np.float32(rng.standard_normal() * 4)
+    if dt == "f16":
+        return np.float16(f)
+    if dt == "bf16":
+        return np.uint16(int(np.array(f).view(np.uint32)) >> 16)
+    return f
 
 
 def random_view(rng, storage_fill, shape, dtype, broadcast=False, align=False, permute=True):
@@ -112,7 +120,7 @@ def random_view(rng, storage_fill, shape, dtype, broadcast=False, align=False, p
     return v, storage
 
 
-_NPD = {"f16": np.float16, "f32": np.float32, "i32": np.int32}
+_NPD = {"f16": np.float16, "bf16": np.uint16, "f32": np.float32, "i32": np.int32}
 
 
 def _arg_dtypes(spec):
@@ -141,7 +149,10 @@ def _fill_for(rng, dt):
 
     def f(sh):
         b = rng.integers(0, 2**32, sh, dtype=np.uint64).astype(np.uint32).view(np.float32)
-        return np.where(rng.random(sh) < 0.5, rng.standard_normal(sh).astype(np.float32) * 100, b)
+        v = np.where(rng.random(sh) < 0.5, rng.standard_normal(sh).astype(np.float32) * 100, b)
+        if dt == "bf16":            # bfloat16 bit patterns: the upper halves
+            return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        return v
     return f
 
 
@@ -164,7 +175,7 @@ def random_view_case(seed, staged=False):
     ins = []
     for (_, st), dt in zip([s for s in spec if s[1][0] in ("load", "scalar")], in_dt):
         if st[0] == "scalar":
-            ins.append(np.float32(rng.standard_normal()) if dt == "f32" else np.int32(rng.integers(-1000, 1000)))
+            ins.append(random_scalar(rng, dt))
         else:
             ins.append(random_view(rng, _fill_for(rng, dt), shape, _NPD[dt], broadcast=not staged, align=align))
     outs = [random_view(rng, _fill_for(rng, dt), shape, _NPD[dt], align=align, permute=not staged)

@@ -56,14 +56,16 @@ def test_build_errors():
     h = c.load("f16")
     _err(lambda: c.add(x, i), "CMD_E_DTYPE")
     _err(lambda: c.add(x, 17), "CMD_E_TAG")
-    _err(lambda: c.add(h, h), "CMD_E_DTYPE")
+    bh = c.load("bf16")
+    _err(lambda: c.add(h, bh), "CMD_E_DTYPE")                       # binary16 and bfloat16 do not mix
     _err(lambda: c.op(E.E_NEG, x, -1, "i32"), "CMD_E_DTYPE")
     _err(lambda: c.op(E.E_NEG, x, x), "CMD_E_ARG")
     _err(lambda: c.op(99, x, x), "CMD_E_ARG")
     _err(lambda: c.op(E.E_SELECT, x, x), "CMD_E_ARG")                # ternary: cmd_select only
     _err(lambda: c.op(E.E_CMP["lt"], x, x, "f32"), "CMD_E_DTYPE")    # comparisons give int32
     _err(lambda: c.cmp("ltu", x, x), "CMD_E_DTYPE")                  # unsigned needs int32
-    _err(lambda: c.cmp("lt", h, h), "CMD_E_DTYPE")                   # no binary16 comparisons
+    _err(lambda: c.cmp("geu", bh, bh), "CMD_E_DTYPE")                # unsigned needs int32
+    assert c.add(h, h) >= 0 and c.mul(bh, bh) >= 0 and c.cmp("lt", h, h) >= 0   # 16-bit compute types
     _err(lambda: c.min(x, i), "CMD_E_DTYPE")
     _err(lambda: c.select(x, x, x), "CMD_E_DTYPE")                   # condition must be int32
     _err(lambda: c.select(i, x, h), "CMD_E_DTYPE")                   # values of one dtype
@@ -307,6 +309,38 @@ def test_unaligned_views_pick_slower_variants():
 # against the oracle: it catches lowering mistakes (slot reuse, operand order,
 # aliasing) without a GPU.
 
+def _bf_vals(a):
+    """bfloat16 bit patterns (uint16) -> float32 values (exact)."""
+    return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _bf_round(x):
+    """float32 values -> bfloat16 bit patterns, torch's round-to-nearest-even."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _i32_to_bf(a):
+    """int32 -> bfloat16 rounded once from the exact integer (Python integers)."""
+    out = []
+    for i in np.asarray(a, dtype=np.int64).tolist():
+        m = abs(i)
+        if m < (1 << 24):
+            out.append(int(_bf_round(np.array([np.float32(i)]))[0]))
+            continue
+        ulp = 1 << (m.bit_length() - 8)
+        lo = (m // ulp) * ulp
+        up = 2 * (m - lo) > ulp or (2 * (m - lo) == ulp and (lo // ulp) % 2 == 1)
+        v = float(lo + ulp if up else lo) * (1 if i > 0 else -1)
+        out.append(int(_bf_round(np.array([v], dtype=np.float32))[0]))   # exact in binary32
+    return np.array(out, dtype=np.uint16)
+
+
+def _minmax_zero_fix(A, B, r, is_min, zero):
+    z = (A == 0) & (B == 0)
+    neg = np.signbit(A) | np.signbit(B) if is_min else np.signbit(A) & np.signbit(B)
+    return np.where(z, np.where(neg, -zero, zero), r)
+
+
 def _emulate(listing, ins, uni, n):
     regs = {}
     outs = []
@@ -328,9 +362,25 @@ def _emulate(listing, ins, uni, n):
             B = regs[b] if b else None
             C = regs[c] if c else None
             with np.errstate(all="ignore"):
-                if op in ("add.f32", "add.i32"): r = A + B
-                elif op in ("sub.f32", "sub.i32"): r = A - B
-                elif op in ("mul.f32", "mul.i32"): r = A * B
+                if op.endswith(".bf16") and op.split(".")[0] in ("add", "sub", "mul"):
+                    x, y = _bf_vals(A), _bf_vals(B)
+                    # binary32 result rounded to bfloat16 = the exact result rounded once
+                    r = _bf_round({"add": x + y, "sub": x - y, "mul": x * y}[op.split(".")[0]])
+                elif op in ("min.bf16", "max.bf16"):
+                    x, y = _bf_vals(A), _bf_vals(B)
+                    r = _minmax_zero_fix(x, y, (np.fmin if op == "min.bf16" else np.fmax)(x, y),
+                                         op == "min.bf16", np.float32(0.0))
+                    r = _bf_round(r)
+                elif op == "cvt.f16.bf16": r = _bf_round(A.astype(np.float32))
+                elif op == "cvt.bf16.f16": r = _bf_vals(A).astype(f16)
+                elif op == "cvt.bf16.f32": r = _bf_vals(A)
+                elif op == "cvt.f32.bf16": r = _bf_round(A)
+                elif op == "cvt.bf16.i32": r = f2i(_bf_vals(A))
+                elif op == "cvt.i32.bf16": r = _i32_to_bf(A)
+                elif op == "abs.bf16": r = (A & 0x7FFF).astype(np.uint16)
+                elif op in ("add.f32", "add.i32", "add.f16"): r = A + B
+                elif op in ("sub.f32", "sub.i32", "sub.f16"): r = A - B
+                elif op in ("mul.f32", "mul.i32", "mul.f16"): r = A * B
                 elif op.startswith("neg"): r = (A.view(np.uint32 if A.itemsize == 4 else np.uint16) ^ (0x80000000 if A.itemsize == 4 else 0x8000)).view(A.dtype) if op != "neg.i32" else (np.int32(0) - A)
                 elif op == "cvt.f16.f32": r = A.astype(np.float32)
                 elif op == "cvt.f32.f16": r = A.astype(f16)
@@ -339,15 +389,15 @@ def _emulate(listing, ins, uni, n):
                 elif op == "cvt.i32.f16": r = A.astype(np.float64).astype(f16)
                 elif op == "cvt.f16.i32": r = f2i(A.astype(np.float32))
                 elif op.split(".")[0] in ("eq", "ne", "lt", "le", "gt", "ge"):
-                    X, Y = (A.view(np.uint32), B.view(np.uint32)) if op.endswith(".u32") else (A, B)
+                    X, Y = (A.view(np.uint32), B.view(np.uint32)) if op.endswith(".u32") else \
+                        ((_bf_vals(A), _bf_vals(B)) if op.endswith(".bf16") else (A, B))
                     r = getattr(np, {"eq": "equal", "ne": "not_equal", "lt": "less", "le": "less_equal",
                                      "gt": "greater", "ge": "greater_equal"}[op.split(".")[0]])(X, Y).astype(np.int32)
                 elif op in ("min.i32", "max.i32"): r = (np.minimum if op == "min.i32" else np.maximum)(A, B)
-                elif op in ("min.f32", "max.f32"):
-                    r = (np.fmin if op == "min.f32" else np.fmax)(A, B)
-                    z = (A == 0) & (B == 0)                      # order -0 below +0 on ties
-                    neg = np.signbit(A) | np.signbit(B) if op == "min.f32" else np.signbit(A) & np.signbit(B)
-                    r = np.where(z, np.where(neg, np.float32(-0.0), np.float32(0.0)), r)
+                elif op in ("min.f32", "max.f32", "min.f16", "max.f16"):
+                    r = (np.fmin if op.startswith("min") else np.fmax)(A, B)
+                    # order -0 below +0 on ties
+                    r = _minmax_zero_fix(A, B, r, op.startswith("min"), A.dtype.type(0.0))
                 elif op.startswith("abs"):
                     r = (A.view(np.uint32) & 0x7FFFFFFF).view(A.dtype) if op == "abs.f32" else \
                         ((A.view(np.uint16) & 0x7FFF).view(A.dtype) if op == "abs.f16" else np.abs(A))
@@ -390,6 +440,8 @@ def test_lowered_listing_matches_oracle(oracle_mod, seed):
         rb = r.view(np.uint16 if r.itemsize == 2 else np.uint32)
         if r.dtype.kind == "f":
             ok = (gb == rb) | (np.isnan(g) & np.isnan(r))
+        elif r.dtype == np.uint16:          # bfloat16 bit patterns: any NaN equals any NaN
+            ok = (gb == rb) | (np.isnan(_bf_vals(gb)) & np.isnan(_bf_vals(rb)))
         else:
             ok = gb == rb
         assert ok.all(), "seed %d out%d\n%s" % (seed, k, listing)

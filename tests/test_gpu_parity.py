@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import NPD, TD, bits, compare, dev, run_gpu, run_oracle, to_dev
+from gpu_util import NPD, TD, bits, compare, dev, host, run_gpu, run_oracle, to_dev
 from specs import SPECS, arg_dtypes, input_kinds
 import test_oracle_pins as P
 from random_commands import _random_inputs, _random_spec
@@ -50,7 +50,7 @@ def _check_workload(wl, n, generic=False):
             else:
                 os.environ["ECMD_FORCE_GENERIC"] = old
     for k, (g, r) in enumerate(zip(got, ref)):
-        compare(g.cpu().numpy(), r, ULP.get(wl, 0), "%s n=%d out%d %s" % (wl, n, k, plan["kernel"]))
+        compare(host(g), r, ULP.get(wl, 0), "%s n=%d out%d %s" % (wl, n, k, plan["kernel"]))
     return plan
 
 
@@ -65,13 +65,16 @@ def test_hand_worked_on_gpu(n):
         vals = []
         for kind, dt, b in zip(input_kinds(spec), in_dt, ins):
             if kind == "scalar":
-                vals.append(float(np.array(b, dtype=P.NPU[dt]).view(NPD[dt])) if dt != "i32"
-                            else int(np.array(b, dtype=np.uint32).view(np.int32)))
+                if dt == "bf16":
+                    vals.append(np.uint16(b))
+                else:
+                    vals.append(float(np.array(b, dtype=P.NPU[dt]).view(NPD[dt])) if dt != "i32"
+                                else int(np.array(b, dtype=np.uint32).view(np.int32)))
             else:
                 vals.append(to_dev(np.full(n, b, dtype=P.NPU[dt]).view(NPD[dt])))
         _, got = run_gpu(spec, vals, [((n,), d) for d in out_dt])
         for o, e, dt in zip(got, expect, out_dt):
-            ob = bits(o.cpu().numpy())
+            ob = bits(host(o))
             for g in ob:
                 if P.is_nan_bits(e, dt):
                     assert P.is_nan_bits(int(g), dt), "golden line %d: NaN expected, GPU %#x" % (ln, g)
@@ -203,7 +206,7 @@ def test_fill_generic_and_2d(dt):
     torch.cuda.synchronize()
     ref = np.zeros((33, 70), NPD[dt])
     ref[:, 3:67] = np.array(val, dtype=NPD[dt])
-    compare(out.cpu().numpy(), ref, 0, "fill %s" % dt)
+    compare(host(out), ref, 0, "fill %s" % dt)
 
 
 # ---------------------------------------------------------------------------
@@ -232,8 +235,8 @@ def test_unaligned_bases_and_guards(off, n):
     x, y = to_dev(xs)[off:], to_dev(ys)[off:]
     cmd, _ = run_gpu(W.ADD_F32, [x, y], None, outputs=[out])
     assert not cmd.plan(x, y, out)["vector"]
-    compare(out.cpu().numpy(), xs[off:] + ys[off:], 0, "unaligned add")
-    b = buf.cpu().numpy()
+    compare(host(out), xs[off:] + ys[off:], 0, "unaligned add")
+    b = host(buf)
     assert np.all(b[: guard + off] == 7.5) and np.all(b[guard + off + n:] == 7.5)
 
 
@@ -246,9 +249,9 @@ def test_guards_vector_path(n):
     b1 = torch.full((n + 2 * guard,), 3.0, dtype=torch.float32, device=dev())
     outs = [b0[guard:guard + n], b1[guard:guard + n]]
     run_gpu(W.MIXED_TWO_OUT, [to_dev(v) if isinstance(v, np.ndarray) else v for v in vals], None, outputs=outs)
-    compare(outs[0].cpu().numpy(), ref[0], 2, "out0")
-    compare(outs[1].cpu().numpy(), ref[1], 2, "out1")
-    h0, h1 = b0.cpu().numpy(), b1.cpu().numpy()
+    compare(host(outs[0]), ref[0], 2, "out0")
+    compare(host(outs[1]), ref[1], 2, "out1")
+    h0, h1 = host(b0), host(b1)
     assert np.all(h0[:guard] == 1.0) and np.all(h0[guard + n:] == 1.0)
     assert np.all(h1[:guard] == 3.0) and np.all(h1[guard + n:] == 3.0)
 
@@ -259,7 +262,7 @@ def test_in_place_identical_view():
     ref = run_oracle(W.AXPBY_F32, vals)[0]
     x = to_dev(vals[0])
     run_gpu(W.AXPBY_F32, [x, to_dev(vals[1]), vals[2], vals[3]], None, outputs=[x])
-    compare(x.cpu().numpy(), ref, 0, "in place")
+    compare(host(x), ref, 0, "in place")
 
 
 def test_non_default_stream():
@@ -273,7 +276,7 @@ def test_non_default_stream():
     s.synchronize()
     run_gpu(W.INT_FUSED, gv, None, outputs=[out], stream=s)
     s.synchronize()
-    compare(out.cpu().numpy(), ref, 0, "side stream")
+    compare(host(out), ref, 0, "side stream")
 
 
 def test_bound_launch_repeated():
@@ -288,8 +291,8 @@ def test_bound_launch_repeated():
     for _ in range(5):
         bound.launch()
     torch.cuda.synchronize()
-    compare(outs[0].cpu().numpy(), ref[0], 2, "bound out0")
-    compare(outs[1].cpu().numpy(), ref[1], 2, "bound out1")
+    compare(host(outs[0]), ref[0], 2, "bound out0")
+    compare(host(outs[1]), ref[1], 2, "bound out1")
 
 
 def test_rejected_launch_leaves_output():
@@ -323,7 +326,7 @@ def test_transposed_shapes(shape, pad):
     X = to_dev(xs)[:, :C]
     Yt = to_dev(Y).t()
     cmd, (out,) = run_gpu(W.TRANSPOSED_2D, [X, Yt, 2.0], [((R, C), "f32")])
-    compare(out.cpu().numpy(), ref, 0, "transposed %s pad %d %s" % (shape, pad, cmd.plan(X, Yt, 2.0, out)["kernel"]))
+    compare(host(out), ref, 0, "transposed %s pad %d %s" % (shape, pad, cmd.plan(X, Yt, 2.0, out)["kernel"]))
 
 
 def test_transposed_self_is_three_x_on_gpu():
@@ -332,7 +335,7 @@ def test_transposed_self_is_three_x_on_gpu():
     Xd = to_dev(X)
     Y = Xd.t().contiguous()
     _, (out,) = run_gpu(W.TRANSPOSED_2D, [Xd, Y.t(), 2.0], [((320, 192), "f32")])
-    compare(out.cpu().numpy(), np.float32(3) * X, 0, "X + 2 X")
+    compare(host(out), np.float32(3) * X, 0, "X + 2 X")
 
 
 def test_tiled_generic_f16_two_staged():
@@ -354,8 +357,8 @@ def test_tiled_generic_f16_two_staged():
     cmd, got = run_gpu(spec, gv, [((R, C), "f16"), ((R, C), "i32")])
     plan = cmd.plan(*gv, *got)
     assert plan["path"] == "tiled" and not plan["specialised"] and plan["lds_bytes"] == 2 * 64 * 65 * 4, plan
-    compare(got[0].cpu().numpy(), ref[0], 0, "tiled f16 out")
-    compare(got[1].cpu().numpy(), ref[1], 0, "tiled i32 copy")
+    compare(host(got[0]), ref[0], 0, "tiled f16 out")
+    compare(host(got[1]), ref[1], 0, "tiled i32 copy")
 
 
 def test_gather_views():
@@ -375,7 +378,7 @@ def test_gather_views():
     wided = torch.zeros((R, 2 * C), device=dev())
     cmd, _ = run_gpu(spec, [to_dev(x), bd], None, outputs=[wided[:, ::2]])
     assert cmd.plan(to_dev(x), bd, wided[:, ::2])["path"] == "gather"   # the store's inner stride is 2
-    compare(wided.cpu().numpy(), wide, 0, "broadcast row, strided store")
+    compare(host(wided), wide, 0, "broadcast row, strided store")
     # column-major output and a both-strided input -> gather
     xs = rng.random((2 * R, 3 * C), dtype=np.float32)
     xv = xs[::2, ::3]
@@ -385,14 +388,14 @@ def test_gather_views():
     cm = torch.zeros((C, R), device=dev())
     cmd, _ = run_gpu(spec, [xd, bd], None, outputs=[cm.t()])
     assert cmd.plan(xd, bd, cm.t())["path"] == "gather"
-    compare(cm.cpu().numpy(), colmaj, 0, "gather column-major out")
+    compare(host(cm), colmaj, 0, "gather column-major out")
     # rank-1 strided load
     v = rng.random(3000, dtype=np.float32)
     spec1 = [("x", ("load", "f32", 1)), ("n", ("neg", "x")), ("o", ("store", "n", 1))]
     ref = run_oracle(spec1, [v[::3]])[0]
     cmd, (o,) = run_gpu(spec1, [to_dev(v)[::3]], [((1000,), "f32")])
     assert cmd.plan(to_dev(v)[::3], o)["path"] == "gather"
-    compare(o.cpu().numpy(), ref, 0, "rank-1 strided")
+    compare(host(o), ref, 0, "rank-1 strided")
 
 
 # ---------------------------------------------------------------------------
@@ -409,7 +412,8 @@ def test_random_commands(seed):
         ref = run_oracle(spec, vals)
     except Exception as e:   # the oracle front end refuses -> the library must refuse too
         pytest.skip("not a valid Command: %s" % e)
-    gv = [to_dev(v) if isinstance(v, np.ndarray) else (float(v) if v.dtype == np.float32 else int(v)) for v in vals]
+    gv = [to_dev(v) if isinstance(v, np.ndarray) else
+          (v if v.dtype == np.uint16 else float(v) if v.dtype.kind == "f" else int(v)) for v in vals]
     if rank == 2 and seed % 2 == 0:       # transposed views of the loads
         gv = [v.t().contiguous().t() if isinstance(v, torch.Tensor) else v for v in gv]
     _, outs = arg_dtypes(spec)
@@ -420,7 +424,7 @@ def test_random_commands(seed):
         assert e.name == "CMD_E_LIMIT", e          # more live temporaries than registers
         pytest.skip(str(e))
     for k, (g, r) in enumerate(zip(got, ref)):
-        compare(g.cpu().numpy(), r, 0, "random seed %d out%d %s\n%s" % (seed, k, cmd.plan(*gv, *got)["kernel"], cmd.dump()))
+        compare(host(g), r, 0, "random seed %d out%d %s\n%s" % (seed, k, cmd.plan(*gv, *got)["kernel"], cmd.dump()))
 
 
 # ---------------------------------------------------------------------------
@@ -430,7 +434,7 @@ def test_f16_to_f32_all_patterns_gpu():
     from oracle import oracle
     h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     _, (o,) = run_gpu(SPECS["cvt_f16_f32"], [to_dev(h.view(np.float16))], [((65536,), "f32")])
-    compare(o.cpu().numpy(), oracle.f16_to_f32_all().view(np.float32), 0, "f16->f32")
+    compare(host(o), oracle.f16_to_f32_all().view(np.float32), 0, "f16->f32")
 
 
 def test_f32_to_f16_all_2pow32_gpu():
@@ -448,7 +452,7 @@ def test_f32_to_f16_all_2pow32_gpu():
             v = base + first
             x = torch.where(v >= 2**31, v - 2**32, v).to(torch.int32).view(torch.float32)
             run_gpu(SPECS["cvt_f32_f16"], [x], None, outputs=[out])
-            got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+            got = host(out.view(torch.int16)).view(np.uint16)
             ref = np.concatenate(list(ex.map(lambda j: oracle.f32_to_f16_range(first + j * sub, sub), range(chunk // sub))))
             nan_r = ((ref & 0x7C00) == 0x7C00) & ((ref & 0x3FF) != 0)
             nan_g = ((got & 0x7C00) == 0x7C00) & ((got & 0x3FF) != 0)

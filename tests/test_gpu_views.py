@@ -13,7 +13,7 @@ import torch
 from numpy.lib.stride_tricks import as_strided
 
 import workloads as W
-from gpu_util import NPD, compare, dev, run_oracle
+from gpu_util import NPD, compare, dev, host, run_oracle, to_dev
 from random_commands import random_view_case
 from specs import arg_dtypes
 
@@ -29,7 +29,7 @@ def _recut(view, storage, copy):
 
 def _device(view, storage):
     off, strides = W.layout(view, storage)
-    flat = torch.from_numpy(np.ascontiguousarray(storage).reshape(-1)).to(dev())
+    flat = to_dev(np.ascontiguousarray(storage).reshape(-1))
     return flat, flat.as_strided(view.shape, strides, off)
 
 
@@ -64,7 +64,7 @@ def run_views(spec, inputs, outputs, generic=False, what=""):
             else:
                 os.environ["ECMD_FORCE_GENERIC"] = old
     for k, (f, ref) in enumerate(zip(gflat, host_out)):
-        compare(f.cpu().numpy(), ref.reshape(-1), 0, "%s out%d (%s)" % (what, k, plan["kernel"]))
+        compare(host(f), ref.reshape(-1), 0, "%s out%d (%s)" % (what, k, plan["kernel"]))
     return plan
 
 
@@ -127,7 +127,7 @@ def test_full_size_views(wl):
     plan = cmd.plan(*gin, out)
     cmd.launch(*gin, out)
     torch.cuda.synchronize()
-    compare(out.cpu().numpy(), ref[0], 0, "%s full (%s)" % (wl, plan["kernel"]))
+    compare(host(out), ref[0], 0, "%s full (%s)" % (wl, plan["kernel"]))
     assert plan["path"] == {"batched_transpose": "tiled", "bias_nchw": "rows"}[wl]
 
 

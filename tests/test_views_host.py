@@ -4,6 +4,7 @@ dropping size-1 dimensions, ordering by the first output and merging
 contiguous dimensions.  No GPU is used: cmd_plan only reads pointers, sizes and
 strides (the coordinate-transform model of rocRoller "Design Overview",
 section "Kernel Graph": a dimension has a size and a stride)."""
+import numpy as np
 import pytest
 import torch
 
@@ -275,7 +276,8 @@ def test_random_view_cases_reach_every_path():
             if isinstance(x, tuple):
                 view, storage = x
                 off, strides = W.layout(view, storage)
-                dt = {2: torch.float16, 4: torch.float32 if view.dtype.kind == "f" else torch.int32}[view.itemsize]
+                dt = {np.dtype(np.float16): torch.float16, np.dtype(np.uint16): torch.bfloat16,
+                      np.dtype(np.float32): torch.float32, np.dtype(np.int32): torch.int32}[view.dtype]
                 base = T((1,), dtype=dt).data_ptr()
                 vals.append(FakeTensor(view.shape, strides, dt, base + off * view.itemsize))
             else:

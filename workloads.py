@@ -242,6 +242,8 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
     of the rank-3/4 workloads.  ``extra["storage"]`` lists, per input value,
     the contiguous array a view was cut from (the value itself when it is
     contiguous, None for scalars); ``layout`` gives the view inside it.
+    bfloat16 tensors are uint16 arrays of bit patterns, bfloat16 scalars
+    numpy.uint16 bit patterns.
     """
     w = WORKLOADS[workload]
     n = w.get("n") if n is None else n
@@ -355,6 +357,10 @@ def to_torch(vals, extra, device):
             out.append(v)
             continue
         off, strides = layout(v, st)
-        flat = torch.from_numpy(np.ascontiguousarray(st).reshape(-1)).to(device)
+        flat = np.ascontiguousarray(st).reshape(-1)
+        if flat.dtype == np.uint16:          # bfloat16 bit patterns
+            flat = torch.from_numpy(flat.view(np.int16)).to(device).view(torch.bfloat16)
+        else:
+            flat = torch.from_numpy(flat).to(device)
         out.append(flat.as_strided(v.shape, strides, off))
     return out
