@@ -143,23 +143,25 @@ def cpu_baseline(wl, budget_s=20.0):
     shape = {"batched_transpose": (4, 2048, 2048), "bias_nchw": (2, 256, 128, 256)}.get(wl)
     vals, extra = W.make_inputs(wl, n, shape=shape)
     cmd = oracle.from_spec(spec)
-    res = {}
+    # Repeat each thread count for about half the time budget (at least 3
+    # runs, at most 200) and take the median run.
+    res, counts = {}, {}
     for t in (1, threads):
         runs = []
-        for _ in range(3):
+        while len(runs) < 3 or (sum(runs) < budget_s / 2 and len(runs) < 200):
             t0 = time.perf_counter()
             cmd.run(*vals, nthreads=t)
             runs.append(time.perf_counter() - t0)
-            if sum(runs) > budget_s:
-                break
         res[t] = statistics.median(runs)
+        counts[t] = len(runs)
     elems = W.elements(wl, n, shape)
     byts = W.algorithmic_bytes(wl, n, shape)
     best_t = threads
     return {
         "value": round(byts / res[best_t] / 1e9, 3), "unit": "GB/s", "cores": best_t, "kind": "oracle",
-        "sample": "%s, first %d elements (%s of the workload), same seeded inputs; median of up to 3 runs"
-                  % (wl, elems, "all" if elems == W.elements(wl) else "part"),
+        "sample": "%s, first %d elements (%s of the workload), same seeded inputs; median of %d runs "
+                  "(%d on one thread)" % (wl, elems, "all" if elems == W.elements(wl) else "part",
+                                          counts[best_t], counts[1]),
         "gelem_per_s": round(elems / res[best_t] / 1e9, 4),
         "single_thread_gbps": round(byts / res[1] / 1e9, 3),
         "seconds": round(res[best_t], 4),
