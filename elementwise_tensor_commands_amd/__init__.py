@@ -82,6 +82,12 @@ def _load_library():
         "cmd_dump": (ctypes.c_int64, [vp, ctypes.c_char_p, ctypes.c_int64]),
         "cmd_last_error": (ctypes.c_char_p, [vp]),
         "cmd_version": (ctypes.c_int32, []),
+        "cmd_to_yaml": (ctypes.c_int64, [vp, ctypes.c_char_p, ctypes.c_int64]),
+        "cmd_from_yaml": (ctypes.c_int32, [ctypes.c_char_p, ctypes.POINTER(vp)]),
+        "cmd_program_yaml": (ctypes.c_int64, [vp, ctypes.c_char_p, ctypes.c_int64]),
+        "cmd_program_hash": (ctypes.c_int32, [vp, ctypes.POINTER(ctypes.c_uint64)]),
+        "cmd_num_args": (ctypes.c_int32, [vp]),
+        "cmd_arg_info": (ctypes.c_int32, [vp, ctypes.c_int32, i32p, i32p, i32p, i32p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -146,7 +152,6 @@ class Command:
             raise Error(rc, lib.cmd_last_error(None).decode())
         self._h = h
         self.arg_kinds: list[tuple[int, int, int]] = []   # (kind, dtype, rank) per argument
-        self._dtypes: list[int] = []                      # dtype per tag
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -158,26 +163,29 @@ class Command:
         if rc:
             raise Error(rc, lib.cmd_last_error(self._h).decode())
 
+    def _arg_decl(self, index: int) -> tuple[int, int, int]:
+        kind, dt, rank, out = (ctypes.c_int32() for _ in range(4))
+        self._check(lib.cmd_arg_info(self._h, index, ctypes.byref(kind), ctypes.byref(dt), ctypes.byref(rank),
+                                     ctypes.byref(out)))
+        return kind.value, dt.value, rank.value
+
     def load(self, dtype, rank: int = 1) -> int:
         tag, arg = ctypes.c_int32(), ctypes.c_int32()
         self._check(lib.cmd_load(self._h, _dt(dtype), rank, ctypes.byref(tag), ctypes.byref(arg)))
-        self.arg_kinds.append((ARG_TENSOR, _dt(dtype), rank))
-        self._dtypes.append(_dt(dtype))
+        self.arg_kinds.append(self._arg_decl(arg.value))
         return tag.value
 
     def scalar(self, dtype) -> int:
         tag, arg = ctypes.c_int32(), ctypes.c_int32()
         self._check(lib.cmd_scalar(self._h, _dt(dtype), ctypes.byref(tag), ctypes.byref(arg)))
-        self.arg_kinds.append((ARG_SCALAR, _dt(dtype), 0))
-        self._dtypes.append(_dt(dtype))
+        self.arg_kinds.append(self._arg_decl(arg.value))
         return tag.value
 
     def op(self, opcode: int, a: int, b: int = -1, dtype=None) -> int:
-        if dtype is None:
-            dtype = self._dtypes[a] if 0 <= a < len(self._dtypes) else F32
+        """An E_ operation; dtype None is the default result type (int32 for
+        comparisons, the operands' dtype otherwise)."""
         tag = ctypes.c_int32()
-        self._check(lib.cmd_op(self._h, opcode, _dt(dtype), a, b, ctypes.byref(tag)))
-        self._dtypes.append(_dt(dtype))
+        self._check(lib.cmd_op(self._h, opcode, 0 if dtype is None else _dt(dtype), a, b, ctypes.byref(tag)))
         return tag.value
 
     def add(self, a, b): return self.op(E_ADD, a, b)
@@ -197,15 +205,47 @@ class Command:
     def select(self, cond, x, y) -> int:
         tag = ctypes.c_int32()
         self._check(lib.cmd_select(self._h, cond, x, y, ctypes.byref(tag)))
-        self._dtypes.append(self._dtypes[x] if 0 <= x < len(self._dtypes) else 0)
         return tag.value
 
     def store(self, tag: int, rank: int = 1) -> int:
         arg = ctypes.c_int32()
         self._check(lib.cmd_store(self._h, tag, rank, ctypes.byref(arg)))
-        dt = self._dtypes[tag] if 0 <= tag < len(self._dtypes) else 0
-        self.arg_kinds.append((ARG_TENSOR, dt, rank))
+        self.arg_kinds.append(self._arg_decl(arg.value))
         return arg.value
+
+    # -- serialisation ---------------------------------------------------------
+    def _text(self, fn) -> str:
+        n = fn(self._h, None, 0)
+        if n < 0:
+            self._check(int(n))
+        buf = ctypes.create_string_buffer(int(n) + 1)
+        fn(self._h, buf, n + 1)
+        return buf.value.decode()
+
+    def to_yaml(self) -> str:
+        """The Command as a YAML document (cmd_to_yaml)."""
+        return self._text(lib.cmd_to_yaml)
+
+    @classmethod
+    def from_yaml(cls, text: str) -> "Command":
+        """A new Command built from a cmd_to_yaml document (cmd_from_yaml)."""
+        h = ctypes.c_void_p()
+        rc = lib.cmd_from_yaml(text.encode(), ctypes.byref(h))
+        if rc:
+            raise Error(rc, lib.cmd_last_error(None).decode())
+        obj = cls.__new__(cls)
+        obj._h = h
+        obj.arg_kinds = [obj._arg_decl(i) for i in range(lib.cmd_num_args(h))]
+        return obj
+
+    def program_yaml(self) -> str:
+        """The lowered program as YAML (cmd_program_yaml); freezes the Command."""
+        return self._text(lib.cmd_program_yaml)
+
+    def program_hash(self) -> int:
+        x = ctypes.c_uint64()
+        self._check(lib.cmd_program_hash(self._h, ctypes.byref(x)))
+        return x.value
 
     # -- argument marshalling --------------------------------------------------
     def _args(self, values):
@@ -257,12 +297,8 @@ class Command:
                 "dims": info.dims, "size": tuple(info.size), "kernel": info.kernel.decode()}
 
     def dump(self) -> str:
-        n = lib.cmd_dump(self._h, None, 0)
-        if n < 0:
-            self._check(int(n))
-        buf = ctypes.create_string_buffer(int(n) + 1)
-        lib.cmd_dump(self._h, buf, n + 1)
-        return buf.value.decode()
+        """Text listing of the lowered program (cmd_dump); freezes the Command."""
+        return self._text(lib.cmd_dump)
 
 
 class BoundLaunch:

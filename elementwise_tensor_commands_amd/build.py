@@ -27,7 +27,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libecmd.so")
 
-SOURCES = ["ecmd_host.cpp", "kernels_linear.hip", "kernels_tiled.hip", "kernels_rows.hip", "kernels_gather.hip"]
+SOURCES = ["ecmd_host.cpp", "ecmd_serial.cpp", "kernels_linear.hip", "kernels_tiled.hip", "kernels_rows.hip", "kernels_gather.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -24,25 +24,12 @@
 #include <vector>
 
 #include "../../include/ecmd.h"
+#include "ecmd_command.h"
 #include "ecmd_tape.h"
 
 using namespace ecmd;
 
 namespace {
-
-enum NodeKind { N_LOAD = 1, N_SCALAR = 2, N_OP = 3 };
-
-struct Node {
-    int kind, dtype, op, a, b, c, arg;
-};
-
-struct ArgDecl {
-    int kind;       // CMD_ARG_TENSOR or CMD_ARG_SCALAR
-    int dtype;
-    int rank;       // tensors
-    bool output;
-    int tag;        // value produced (load/scalar) or stored (store)
-};
 
 // A bound view over the right-aligned 4-D shape.
 struct View {
@@ -91,19 +78,6 @@ struct Selection {
 };
 
 }  // namespace
-
-struct ecmd_command {
-    std::vector<Node> nodes;
-    std::vector<ArgDecl> args;
-    std::vector<std::pair<int, int>> stores;  // (tag, arg)
-    bool frozen = false;
-    int lower_status = 1;                     // 1 = not lowered yet
-    Program prog{};
-    int in_arg[kMaxIn];                       // CommandArgument index of input k
-    int uni_arg[kMaxUni];
-    int out_arg[kMaxOut];
-    std::string err;
-};
 
 namespace {
 
@@ -822,6 +796,8 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
 
 }  // namespace
 
+void ecmd::set_create_error(const char *msg) { g_create_err = msg; }
+
 // ---------------------------------------------------------------------------
 // The C ABI.
 
@@ -890,9 +866,11 @@ int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, 
     if (h->frozen) return fail(h, CMD_E_STATE, "the Command is frozen");
     const int n = (int)h->nodes.size();
     if (opcode < E_ADD || opcode > E_ABS) return fail(h, CMD_E_ARG, "unknown opcode %d (select: cmd_select)", opcode);
-    if (!valid_dtype(result_dtype)) return fail(h, CMD_E_DTYPE, "unknown dtype %d", result_dtype);
     if (a < 0 || a >= n) return fail(h, CMD_E_TAG, "tag %d does not name an earlier value", a);
     const int da = h->nodes[a].dtype;
+    if (result_dtype == 0 && opcode != E_CVT)        // 0 = the default result type
+        result_dtype = opcode >= E_CMP_EQ && opcode <= E_CMP_GEU ? CMD_I32 : da;
+    if (!valid_dtype(result_dtype)) return fail(h, CMD_E_DTYPE, "unknown dtype %d", result_dtype);
     if (opcode == E_NEG || opcode == E_ABS || opcode == E_CVT) {
         if (b != -1) return fail(h, CMD_E_ARG, "unary operation takes b = -1");
         if (opcode != E_CVT && result_dtype != da)
@@ -1074,6 +1052,97 @@ int64_t cmd_dump(cmd_t h, char *buf, int64_t cap)
         buf[n] = 0;
     }
     return (int64_t)s.size();
+}
+
+// 64-bit FNV-1a over the Program's bytes (all fields are bytes, unused
+// entries zero, so equal Programs hash equally).
+static uint64_t program_hash(const Program &P)
+{
+    const unsigned char *b = reinterpret_cast<const unsigned char *>(&P);
+    uint64_t x = 0xcbf29ce484222325ull;
+    for (size_t i = 0; i < sizeof(Program); ++i) x = (x ^ b[i]) * 0x100000001b3ull;
+    return x;
+}
+
+int32_t cmd_program_hash(cmd_t h, uint64_t *hash)
+{
+    if (!h) return CMD_E_ARG;
+    if (!hash) return fail(h, CMD_E_ARG, "hash is NULL");
+    h->frozen = true;
+    const int rc = lower(h);
+    if (rc) return rc;
+    *hash = program_hash(h->prog);
+    return CMD_OK;
+}
+
+int64_t cmd_program_yaml(cmd_t h, char *buf, int64_t cap)
+{
+    if (!h) return CMD_E_ARG;
+    h->frozen = true;
+    int rc = lower(h);
+    if (rc) return rc;
+    const Program &P = h->prog;
+    auto ref = [](int r) -> std::string {
+        char b[16];
+        if (r == kRefNone) return "none";
+        if (r < kRefSlot) std::snprintf(b, sizeof b, "in%d", r - kRefIn);
+        else if (r < kRefUni) std::snprintf(b, sizeof b, "s%d", r - kRefSlot);
+        else std::snprintf(b, sizeof b, "u%d", r - kRefUni);
+        return b;
+    };
+    char line[200];
+    std::snprintf(line, sizeof line, "ecmd_program: 1\nhash: 0x%016llx\ninputs:\n",
+                  (unsigned long long)program_hash(P));
+    std::string s = line;
+    for (int k = 0; k < P.n_in; ++k) {
+        std::snprintf(line, sizeof line, "  - {ref: in%d, dtype: %s, arg: %d}\n", k, dtype_name(P.in_ty[k]),
+                      h->in_arg[k]);
+        s += line;
+    }
+    s += "uniforms:\n";
+    for (int k = 0; k < P.n_uni; ++k) {
+        std::snprintf(line, sizeof line, "  - {ref: u%d, dtype: %s, arg: %d}\n", k,
+                      dtype_name(h->args[h->uni_arg[k]].dtype), h->uni_arg[k]);
+        s += line;
+    }
+    s += "operations:\n";
+    for (int i = 0; i < P.n_ops; ++i) {
+        const TapeOp &o = P.ops[i];
+        std::snprintf(line, sizeof line, "  - {code: %s, dst: %s, a: %s, b: %s, c: %s}\n", code_name(o.code),
+                      ref(o.dst).c_str(), ref(o.a).c_str(), ref(o.b).c_str(), ref(o.c).c_str());
+        s += line;
+    }
+    s += "outputs:\n";
+    for (int k = 0; k < P.n_out; ++k) {
+        std::snprintf(line, sizeof line, "  - {ref: %s, dtype: %s, arg: %d}\n", ref(P.out_ref[k]).c_str(),
+                      dtype_name(P.out_ty[k]), h->out_arg[k]);
+        s += line;
+    }
+    if (buf && cap > 0) {
+        const int64_t n = std::min<int64_t>(cap - 1, (int64_t)s.size());
+        std::memcpy(buf, s.data(), (size_t)n);
+        buf[n] = 0;
+    }
+    return (int64_t)s.size();
+}
+
+int32_t cmd_num_args(cmd_t h)
+{
+    if (!h) return CMD_E_ARG;
+    return (int32_t)h->args.size();
+}
+
+int32_t cmd_arg_info(cmd_t h, int32_t index, int32_t *kind, int32_t *dtype, int32_t *rank, int32_t *is_output)
+{
+    if (!h) return CMD_E_ARG;
+    if (index < 0 || index >= (int32_t)h->args.size())
+        return fail(h, CMD_E_ARG, "argument %d does not exist", index);
+    const ArgDecl &a = h->args[index];
+    if (kind) *kind = a.kind;
+    if (dtype) *dtype = a.dtype;
+    if (rank) *rank = a.kind == CMD_ARG_TENSOR ? a.rank : 0;
+    if (is_output) *is_output = a.output ? 1 : 0;
+    return CMD_OK;
 }
 
 const char *cmd_last_error(cmd_t h)

@@ -187,6 +187,8 @@ int cmd_scalar(cmd_t h, int32_t dtype, cmd_tag *tag, int32_t *arg_index);
  * and CMD_I32 operands of one dtype; E_CMP_LTU..GEU CMD_I32 only.  E_SELECT
  * is refused here (it has three operands: use cmd_select). */
 int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, cmd_tag *tag);
+/* (result_dtype 0 means the default: int32 for comparisons, the operands'
+ * dtype otherwise; E_CVT needs an explicit target.) */
 
 /* Append a select: cond != 0 ? x : y, per element (a ternary E_ operation of
  * the same T_Execute family).  cond must be CMD_I32; x and y must share a dtype,
@@ -241,9 +243,55 @@ int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info);
  * exceed cap - 1) or a negative status. */
 int64_t cmd_dump(cmd_t h, char *buf, int64_t cap);
 
+/* ------------------------------------------------------------------------ */
+/* Serialisation and introspection.  rocRoller converts Commands, kernel graphs
+ * and operations to and from YAML for debugging and for caching compiled
+ * kernels (rocRoller "Design Overview", section "Serialization"); these calls
+ * do the same for this library's Command and its lowered program, with a
+ * fixed document layout of their own. */
+
+/* Write the Command as a YAML document into buf[cap], NUL-terminated:
+ *   ecmd_command: 1
+ *   arguments:  one {index, kind: tensor|scalar, dtype, rank, role: load|store, tag} per
+ *               CommandArgument, in declaration order
+ *   operations: one {tag, op, dtype, arg} (op: load|scalar) or {tag, op, dtype, a[, b[, c]]}
+ *               (op: add sub mul neg cvt eq ne lt le gt ge ltu leu gtu geu min max abs
+ *               select) per tag, in insertion order
+ *   stores:     one {tag, arg} per store
+ * dtype names: f16 bf16 f32 i32.  Does not freeze the Command.  Returns the
+ * full length (which may exceed cap - 1) or a negative status. */
+int64_t cmd_to_yaml(cmd_t h, char *buf, int64_t cap);
+
+/* Build a new Command from a document in cmd_to_yaml's layout (one flow
+ * mapping per list item; blank lines and # comments allowed).  The document is
+ * replayed through cmd_load / cmd_scalar / cmd_op / cmd_select / cmd_store in
+ * the original call order, so it gets every check those calls make, and the
+ * redundant fields (indexes, tags, the argument list) must agree with what the
+ * calls return.  On failure *out is NULL and cmd_last_error(NULL) names the
+ * line: CMD_E_ARG for a malformed document, else the failing call's status.
+ * The caller destroys *out. */
+int32_t cmd_from_yaml(const char *text, cmd_t *out);
+
+/* Write the lowered program as YAML (ecmd_program: 1, its hash, inputs,
+ * uniforms and outputs with their CommandArgument indexes, operations with
+ * register operands in0..7, s0..7, u0..7).  Freezes and lowers the Command.
+ * Returns the full length or a negative status. */
+int64_t cmd_program_yaml(cmd_t h, char *buf, int64_t cap);
+
+/* 64-bit FNV-1a hash of the lowered program's bytes: equal programs (for
+ * example x+y and y+x) hash equally.  Freezes and lowers the Command. */
+int32_t cmd_program_hash(cmd_t h, uint64_t *hash);
+
+/* Number of CommandArguments declared so far (or a negative status). */
+int32_t cmd_num_args(cmd_t h);
+
+/* Declaration of CommandArgument index: kind (CMD_ARG_*), dtype, rank (0 for
+ * scalars), is_output (1 for stores).  NULL outputs are skipped. */
+int32_t cmd_arg_info(cmd_t h, int32_t index, int32_t *kind, int32_t *dtype, int32_t *rank, int32_t *is_output);
+
 /* Message describing the last failure on this handle ("" if none).  Never
  * NULL; valid until the next call on the handle.  For a NULL handle it
- * describes the last failure of cmd_create on this thread. */
+ * describes the last failure of cmd_create or cmd_from_yaml on this thread. */
 const char *cmd_last_error(cmd_t h);
 
 /* Library version as 10000*major + 100*minor + patch. */
