@@ -27,11 +27,20 @@ PEAK_GBPS = 8000.0        # MI355X HBM3E peak, 8 TB/s
 METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, per Command"
 DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two_out": "f16/f32",
             "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32",
-            "batched_transpose": "f32", "bias_nchw": "f32", "axpby_f16": "f16", "axpby_bf16": "bf16"}
+            "batched_transpose": "f32", "bias_nchw": "f32", "axpby_f16": "f16", "axpby_bf16": "bf16",
+            "bias_relu_f32": "f32"}
 # Measured besides the five configurations: the plain copy (the bandwidth and
 # counter reference), the widened op set, the rank-3/4 views and native 16-bit
-# arithmetic.
-EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "axpby_f16", "axpby_bf16"]
+# arithmetic, and a Command with no ahead-of-time kernel run by the interpreter
+# and by a kernel compiled at run time ("_jit").
+
+
+def split_workload(name):
+    """("bias_relu_f32", True) for "bias_relu_f32_jit": the workload measured
+    with its kernel compiled at run time."""
+    return (name[:-4], True) if name.endswith("_jit") else (name, False)
+EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "axpby_f16", "axpby_bf16",
+         "bias_relu_f32", "bias_relu_f32_jit"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -49,7 +58,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def setup(wl, n=None):
+def setup(wl, n=None, jit=False):
     import numpy as np
     import torch
 
@@ -78,6 +87,8 @@ def setup(wl, n=None):
             out_dt.append(dts[st[1]])
     outs = [torch.empty(shape, dtype=td[d], device=dev) for d in out_dt]
     cmd = ecmd.from_spec(spec)
+    if jit:
+        cmd.jit()
     args = gv + outs
     plan = cmd.plan(*args)
     return cmd, args, plan, vals
@@ -181,14 +192,16 @@ def traffic_from_profiles(wl, kernel_hash):
     return c.get("hbm_bytes_per_launch")
 
 
-def measure(wl, steps, warmup, cold_too=True):
+def measure(wl, steps, warmup, cold_too=True, jit=False):
     """Timed region: steps back-to-back launches between two HIP events on the
     launch stream.  The kernel's average duration is that time / steps (the
     host queues launches faster than they run, so the GPU never waits).
     Separately, per-launch event pairs give median / p10 / p90 and, with a
     cache flush before each launch, the cold rate."""
     import workloads as W
-    cmd, args, plan, _ = setup(wl)
+    cmd, args, plan, _ = setup(wl, jit=jit)
+    if jit:
+        log("%s: run-time compiled kernel from %s" % (wl, {0: "memory", 1: "disk", 2: "compiler"}.get(cmd.prepare(*args))))
     byts = W.algorithmic_bytes(wl)
     elems = W.elements(wl)
     total_ms, wall_ms = time_steps(cmd, args, steps, warmup)
@@ -213,7 +226,7 @@ def measure(wl, steps, warmup, cold_too=True):
 def read_write_bytes(wl):
     """Algorithmic bytes read and written by one launch of the workload."""
     import workloads as W
-    return W.algorithmic_read_write(wl)
+    return W.algorithmic_read_write(split_workload(wl)[0])
 
 
 def _csv_rows(directory, suffix):
@@ -334,8 +347,10 @@ def main():
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     khash = kernel_source_hash()
-    log("workload %s: %s" % (a.workload, W.WORKLOADS[a.workload]["label"]))
-    head = measure(a.workload, a.steps, a.warmup, cold_too=not a.no_cold)
+    base, jit = split_workload(a.workload)
+    label = W.WORKLOADS[base]["label"] + (" (kernel compiled at run time)" if jit else "")
+    log("workload %s: %s" % (a.workload, label))
+    head = measure(base, a.steps, a.warmup, cold_too=not a.no_cold, jit=jit)
     log("headline %s: %.1f GB/s whole-job, kernel avg %.2f us" % (head["kernel"], head["whole_job_gbps"], head["kernel_avg_us"]))
     traffic = traffic_from_profiles(a.workload, khash)
     line = {
@@ -349,9 +364,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": DTYPE_OF[a.workload],
+        "dtype": DTYPE_OF[base],
         "data": "synthetic (seeded NumPy PCG64, seed 1000 + config index), resident in HBM",
-        "config": {"workload": W.WORKLOADS[a.workload]["label"], "elements": head["elements"],
+        "config": {"workload": label, "elements": head["elements"],
                    "algorithmic_bytes_per_step": head["algorithmic_bytes"], "kernel": head["kernel"],
                    "grid": head["grid"], "block": head["block"]},
         "pct_of_peak": round(100 * head["whole_job_gbps"] / PEAK_GBPS, 2),
@@ -373,7 +388,8 @@ def main():
                 r = head
             else:
                 log("measuring %s" % wl)
-                r = measure(wl, min(a.steps, 100), a.warmup)
+                base, jit = split_workload(wl)
+                r = measure(base, min(a.steps, 100), a.warmup, jit=jit)
             line["commands"][wl] = {
                 "kernel": r["kernel"], "gbps": round(r["kernel_gbps"], 1),
                 "pct_of_peak": round(100 * r["kernel_gbps"] / PEAK_GBPS, 2),
@@ -386,7 +402,7 @@ def main():
             log("%s: %s" % (wl, json.dumps(line["commands"][wl])))
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline(a.workload)
+        line["cpu_baseline"] = cpu_baseline(base)
     print(json.dumps(line), flush=True)
 
 

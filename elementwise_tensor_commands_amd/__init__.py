@@ -30,6 +30,7 @@ E_CMP = {"eq": 6, "ne": 7, "lt": 8, "le": 9, "gt": 10, "ge": 11, "ltu": 12, "leu
 E_MIN, E_MAX, E_ABS, E_SELECT = 16, 17, 18, 19
 ARG_TENSOR, ARG_SCALAR = 1, 2
 PATH_NONE, PATH_LINEAR, PATH_TILED, PATH_GATHER, PATH_ROWS = 0, 1, 2, 3, 4
+OPT_JIT = 1
 PATH_NAMES = {0: "none", 1: "linear", 2: "tiled", 3: "gather", 4: "rows"}
 STATUS = {
     0: "CMD_OK", -1: "CMD_E_ARG", -2: "CMD_E_TAG", -3: "CMD_E_DTYPE", -4: "CMD_E_SHAPE",
@@ -59,7 +60,7 @@ class cmd_plan_info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("specialised", ctypes.c_int32), ("vector", ctypes.c_int32),
                 ("elems_per_thread", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("dims", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("size", ctypes.c_int64 * 4), ("kernel", ctypes.c_char * 64)]
+                ("compiled", ctypes.c_int32), ("size", ctypes.c_int64 * 4), ("kernel", ctypes.c_char * 64)]
 
 
 def _load_library():
@@ -87,6 +88,8 @@ def _load_library():
         "cmd_program_yaml": (ctypes.c_int64, [vp, ctypes.c_char_p, ctypes.c_int64]),
         "cmd_program_hash": (ctypes.c_int32, [vp, ctypes.POINTER(ctypes.c_uint64)]),
         "cmd_num_args": (ctypes.c_int32, [vp]),
+        "cmd_set_option": (ctypes.c_int32, [vp, ctypes.c_int32, ctypes.c_int64]),
+        "cmd_prepare": (ctypes.c_int32, [vp, ctypes.POINTER(cmd_arg), ctypes.c_int32, i32p]),
         "cmd_arg_info": (ctypes.c_int32, [vp, ctypes.c_int32, i32p, i32p, i32p, i32p]),
     }
     for name, (res, args) in sig.items():
@@ -213,6 +216,22 @@ class Command:
         self.arg_kinds.append(self._arg_decl(arg.value))
         return arg.value
 
+    # -- run-time compiled kernels ---------------------------------------------
+    def jit(self, enable: bool = True) -> "Command":
+        """Compile a kernel for this Command's program at its first launch when
+        the library has none ahead of time (CMD_OPT_JIT); returns self."""
+        self._check(lib.cmd_set_option(self._h, OPT_JIT, 1 if enable else 0))
+        return self
+
+    def prepare(self, *values) -> int:
+        """Compile (or find) the kernel a launch with these values would use,
+        without touching the GPU: -1 none needed, 0 in memory, 1 from disk,
+        2 compiled now (cmd_prepare)."""
+        arr, n = self._args(values)
+        where = ctypes.c_int32()
+        self._check(lib.cmd_prepare(self._h, arr, n, ctypes.byref(where)))
+        return where.value
+
     # -- serialisation ---------------------------------------------------------
     def _text(self, fn) -> str:
         n = fn(self._h, None, 0)
@@ -294,7 +313,8 @@ class Command:
         return {"path": PATH_NAMES[info.path], "specialised": bool(info.specialised),
                 "vector": bool(info.vector), "elems_per_thread": info.elems_per_thread,
                 "grid": info.grid, "block": info.block, "lds_bytes": info.lds_bytes,
-                "dims": info.dims, "size": tuple(info.size), "kernel": info.kernel.decode()}
+                "dims": info.dims, "size": tuple(info.size), "compiled": bool(info.compiled),
+                "kernel": info.kernel.decode()}
 
     def dump(self) -> str:
         """Text listing of the lowered program (cmd_dump); freezes the Command."""

@@ -41,6 +41,7 @@ struct ecmd_command {
     std::vector<ecmd::ArgDecl> args;
     std::vector<std::pair<int, int>> stores;  // (tag, arg)
     bool frozen = false;
+    bool jit = false;                         // compile kernels for Programs without an ahead-of-time one
     int lower_status = 1;                     // 1 = not lowered yet
     ecmd::Program prog{};
     int in_arg[ecmd::kMaxIn];                 // CommandArgument index of input k

@@ -25,6 +25,7 @@
 
 #include "../../include/ecmd.h"
 #include "ecmd_command.h"
+#include "ecmd_jit.h"
 #include "ecmd_tape.h"
 
 using namespace ecmd;
@@ -59,6 +60,7 @@ struct Canon {
 struct Selection {
     int path = CMD_PATH_NONE;
     int variant = -1;
+    bool jit = false;           // a run-time compiled kernel (variant -1 otherwise means the interpreter)
     bool vec = false;
     LinearShape shape{4, 4, false, true};
     bool xcd_remap = false;
@@ -582,12 +584,13 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         for (int k = 0; k < P.n_in; ++k) S.vec = S.vec && aligned(B.in[k].ptr, 16);
         for (int k = 0; k < P.n_out; ++k) S.vec = S.vec && aligned(B.out[k].ptr, 16);
         S.variant = (S.vec && !force_generic) ? program_match_linear(P) : -1;
+        S.jit = S.vec && !force_generic && S.variant < 0 && h->jit;
         int64_t bytes = 0;
         bool all16 = true;
         for (int k = 0; k < P.n_in; ++k) bytes += numel * esize(B.in[k].dtype), all16 = all16 && esize(B.in[k].dtype) == 2;
         for (int k = 0; k < P.n_out; ++k) bytes += numel * esize(B.out[k].dtype), all16 = all16 && esize(B.out[k].dtype) == 2;
         S.shape = linear_shape(bytes, all16);
-        if (S.variant < 0) S.shape.e = 4, S.shape.g = 4;   // the interpreter has one shape
+        if (S.variant < 0 && !S.jit) S.shape.e = 4, S.shape.g = 4;   // the interpreter has one shape
         S.e = S.shape.e;
         S.block = kLinearBlock;
         // One wavefront per chunk of 64 * E elements (no grid-stride loop)
@@ -600,7 +603,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         S.grid = per_cu > 0 ? std::min(need, std::max<int64_t>(1, per_cu * cu_count)) : need;
         S.grid = std::min<int64_t>(S.grid, kMaxGridItems / kLinearBlock);   // the kernel loops over the rest
         S.xcd_remap = env_flag("ECMD_XCD_REMAP") && S.grid % 8 == 0;
-        S.name = S.vec ? linear_name(S.variant) : "linear_generic_unaligned";
+        S.name = S.jit ? "jit_linear" : S.vec ? linear_name(S.variant) : "linear_generic_unaligned";
         return;
     }
     // Rows: outputs unit-stride along dimension 3, inputs unit-stride or
@@ -625,6 +628,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
             S.path = CMD_PATH_ROWS;
             std::memcpy(S.rowconst, rowconst, sizeof rowconst);
             S.variant = force_generic ? -1 : program_match_linear(P);
+            S.jit = !force_generic && S.variant < 0 && h->jit;
             S.vec = true;
             S.e = 4;
             S.block = kRowsBlock;
@@ -646,7 +650,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
             }
             S.shape = linear_shape(bytes);
             S.shape.nt_store = S.shape.nt_store && lines;
-            S.name = rows_name(S.variant);
+            S.name = S.jit ? "jit_rows" : rows_name(S.variant);
             return;
         }
     }
@@ -810,7 +814,38 @@ int cmd_create(cmd_t *out)
     if (!out) return fail(nullptr, CMD_E_ARG, "out is NULL");
     cmd_t h = new (std::nothrow) ecmd_command();
     if (!h) return fail(nullptr, CMD_E_NOMEM, "out of host memory");
+    h->jit = env_flag("ECMD_JIT");
     *out = h;
+    return CMD_OK;
+}
+
+int32_t cmd_set_option(cmd_t h, int32_t option, int64_t value)
+{
+    if (!h) return CMD_E_ARG;
+    if (option == CMD_OPT_JIT) {
+        if (value != 0 && value != 1) return fail(h, CMD_E_ARG, "CMD_OPT_JIT takes 0 or 1");
+        h->jit = value == 1;
+        return CMD_OK;
+    }
+    return fail(h, CMD_E_ARG, "unknown option %d", option);
+}
+
+int32_t cmd_prepare(cmd_t h, const cmd_arg *args, int32_t nargs, int32_t *from)
+{
+    if (!h) return CMD_E_ARG;
+    Bound B;
+    Selection S;
+    int rc = prepare(h, args, nargs, B, S, cu_count_cached(0));
+    if (rc) return rc;
+    int where = -1;
+    if (S.jit) {
+        std::string err;
+        const JitRequest r{S.path == CMD_PATH_LINEAR ? JIT_LINEAR : JIT_ROWS, S.shape.e, S.shape.g,
+                           S.shape.nt_load, S.shape.nt_store, h->prog};
+        if (jit_prepare(r, &where, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
+    }
+    if (from) *from = where;
+    h->err.clear();
     return CMD_OK;
 }
 
@@ -937,6 +972,8 @@ int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info)
     info->path = S.path;
     info->specialised = S.variant >= 0;
     info->vector = S.path == CMD_PATH_TILED || S.path == CMD_PATH_ROWS ? 1 : S.vec;
+    info->compiled = S.jit ? 1 : 0;
+    if (S.jit) info->specialised = 1;
     info->elems_per_thread = S.e;
     info->grid = S.grid;
     info->block = S.block;
@@ -986,15 +1023,35 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         std::memcpy(A.uni, B.uni, sizeof A.uni);
         A.flags = S.xcd_remap ? kLinearXcdRemap : 0u;
         A.prog = h->prog;
-        herr = launch_linear(S.variant, S.vec, S.shape, A, g, hip_stream);
+        if (S.jit) {
+            hipFunction_t fn;
+            std::string err;
+            const JitRequest r{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, h->prog};
+            if (jit_function(r, &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
+            void *params[] = {&A};
+            herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
+                                              (hipStream_t)hip_stream, params, nullptr);
+        } else {
+            herr = launch_linear(S.variant, S.vec, S.shape, A, g, hip_stream);
+        }
     } else {
         StridedArgs A;
         fill_strided(h, B, S, A);
         const char *ntv = std::getenv("ECMD_TILED_NT");
         const bool nt = !(ntv && std::strcmp(ntv, "0") == 0);
-        herr = S.path == CMD_PATH_TILED  ? launch_tiled(S.variant, nt, S.tile, A, g, hip_stream)
-               : S.path == CMD_PATH_ROWS ? launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream)
-                                         : launch_gather(A, g, hip_stream);
+        if (S.jit) {
+            hipFunction_t fn;
+            std::string err;
+            const JitRequest r{JIT_ROWS, 4, 4, S.shape.nt_load, S.shape.nt_store, h->prog};
+            if (jit_function(r, &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
+            void *params[] = {&A};
+            herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
+                                              (hipStream_t)hip_stream, params, nullptr);
+        } else {
+            herr = S.path == CMD_PATH_TILED  ? launch_tiled(S.variant, nt, S.tile, A, g, hip_stream)
+                   : S.path == CMD_PATH_ROWS ? launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream)
+                                             : launch_gather(A, g, hip_stream);
+        }
     }
     if (herr != 0)
         return fail(h, CMD_E_LAUNCH, "%s launch failed: %s", S.name, hipGetErrorString((hipError_t)herr));

@@ -1,0 +1,41 @@
+// ecmd_jit.h -- run-time compiled kernels for lowered Programs (internal).
+//
+// rocRoller generates the code for a Command when it is built and keeps
+// compiled kernels in a cache (rocRoller "Design Overview", sections "Command
+// Kernel" and "Serialization").  Here the ahead-of-time library holds compiled
+// kernels for a fixed list of Programs and an interpreter for the rest; on
+// request, a Program without an ahead-of-time kernel is compiled at run time:
+// the same device templates (embedded as text) are instantiated for that one
+// Program with hiprtc, and the code object is kept in memory and on disk,
+// keyed by the Program's bytes, the kernel variant and the sources' hash.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <string>
+
+#include "ecmd_tape.h"
+
+namespace ecmd {
+
+enum JitKernel { JIT_LINEAR = 1, JIT_ROWS = 2 };
+
+struct JitRequest {
+    JitKernel kind;
+    int e, g;          // linear: elements per work-item and per vector access
+    bool ntl, nts;     // nontemporal loads / stores
+    Program prog;
+};
+
+// Template instance the request names, e.g.
+// "ecmd::k_linear<ecmd::CtEval<ecmd::kJitProg>, 4, 4, true, true, true>".
+std::string jit_name(const JitRequest &r);
+
+// Make sure the code object exists (memory, else disk, else compile and store
+// it).  Host only: no HIP device call.  *from: 0 memory, 1 disk, 2 compiled.
+int jit_prepare(const JitRequest &r, int *from, std::string &err);
+
+// The loaded kernel for the current device (prepares it first if needed).
+int jit_function(const JitRequest &r, hipFunction_t *fn, std::string &err);
+
+}  // namespace ecmd

@@ -220,7 +220,7 @@ typedef struct {
     int32_t lds_bytes;     /* LDS per work-group                                           */
     int32_t dims;          /* dimensions left after dropping size-1 dimensions and merging */
                            /* the contiguous ones (1..4)                                   */
-    int32_t reserved;
+    int32_t compiled;      /* 1: a kernel compiled at run time for this program (CMD_OPT_JIT) */
     int64_t size[4];       /* those dimensions' sizes, padded on the left with 1s          */
     char kernel[64];       /* kernel name                                                  */
 } cmd_plan_info;
@@ -242,6 +242,30 @@ int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info);
  * and lowers the Command.  Returns the full length of the listing (which may
  * exceed cap - 1) or a negative status. */
 int64_t cmd_dump(cmd_t h, char *buf, int64_t cap);
+
+/* ------------------------------------------------------------------------ */
+/* Run-time compiled kernels.  rocRoller generates a kernel for each Command at
+ * run time and caches compiled kernels (rocRoller "Design Overview", sections
+ * "Command Kernel" and "Serialization").  This library ships compiled kernels
+ * for a fixed list of programs and evaluates any other program with an
+ * interpreter; with CMD_OPT_JIT set, a program without a compiled kernel gets
+ * one compiled at its first launch (hiprtc, the library's own kernel templates
+ * and device flags), kept for the process and stored on disk under
+ * $ECMD_CACHE_DIR (else $XDG_CACHE_HOME/ecmd-amd, else $HOME/.cache/ecmd-amd)
+ * for later processes.  Applies to the linear and rows paths; the tiled and
+ * gather paths always use their ahead-of-time kernels. */
+#define CMD_OPT_JIT 1   /* value 0 (default; the environment variable ECMD_JIT=1 makes it 1) or 1 */
+
+/* Set an option of the handle.  CMD_E_ARG for an unknown option or value. */
+int32_t cmd_set_option(cmd_t h, int32_t option, int64_t value);
+
+/* Validate args as cmd_launch does and make sure the kernel the launch would
+ * use exists: with CMD_OPT_JIT, compile it now (or find it in memory or on
+ * disk) without any GPU call, e.g. to fill the disk cache ahead of time.
+ * *from (may be NULL): -1 no run-time compiled kernel needed, 0 found in
+ * memory, 1 read from disk, 2 compiled now.  A failed compile is CMD_E_LAUNCH
+ * with the compiler's log in cmd_last_error.  Freezes the Command. */
+int32_t cmd_prepare(cmd_t h, const cmd_arg *args, int32_t nargs, int32_t *from);
 
 /* ------------------------------------------------------------------------ */
 /* Serialisation and introspection.  rocRoller converts Commands, kernel graphs

@@ -114,6 +114,19 @@ AXPBY_F16 = [
 ]
 AXPBY_BF16 = [(n, (st[0], "bf16") + st[2:]) if st[0] in ("load", "scalar") else (n, st) for n, st in AXPBY_F16]
 
+# A fused bias + ReLU, out = max(x*s + y, 0): a Command with no ahead-of-time
+# kernel, for the interpreter and the run-time compiled kernel.
+BIAS_RELU_F32 = [
+    ("x", ("load", "f32", 1)),
+    ("y", ("load", "f32", 1)),
+    ("s", ("scalar", "f32")),
+    ("zero", ("scalar", "f32")),
+    ("xs", ("mul", "x", "s")),
+    ("u", ("add", "xs", "y")),
+    ("r", ("max", "u", "zero")),
+    ("out", ("store", "r", 1)),
+]
+
 # Views of rank 3 and 4.  A batch of transposed planes: out[b] = X[b] + alpha * Y[b]^T.
 BATCHED_TRANSPOSE = [
     ("X", ("load", "f32", 3)),
@@ -165,6 +178,9 @@ WORKLOADS = {
                       label="out = alpha*x + beta*y in binary16, n=2^28, alpha=1.5, beta=-0.25"),
     "axpby_bf16": dict(index=11, spec=AXPBY_BF16, n=1 << 28,
                        label="out = alpha*x + beta*y in bfloat16, n=2^28, alpha=1.5, beta=-0.25"),
+    # No ahead-of-time kernel: interpreter, or compiled at run time.
+    "bias_relu_f32": dict(index=12, spec=BIAS_RELU_F32, n=1 << 28,
+                          label="out = max(x*s + y, 0), fp32, n=2^28, s=0.5 (no ahead-of-time kernel)"),
 }
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
@@ -177,6 +193,7 @@ SCALARS = {
     "fill_f32": {"s": np.float32(1.25)},
     "batched_transpose": {"alpha": np.float32(2.0)},
     "axpby_f16": {"alpha": np.float16(1.5), "beta": np.float16(-0.25)},
+    "bias_relu_f32": {"s": np.float32(0.5), "zero": np.float32(0.0)},
     # bfloat16 values are uint16 bit patterns: 1.5 = 0x3fc0, -0.25 = 0xbe80
     "axpby_bf16": {"alpha": np.uint16(0x3FC0), "beta": np.uint16(0xBE80)},
 }
@@ -269,6 +286,9 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
         vals = [(rng.standard_normal(n, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
                 for _ in range(2)]
         vals += [sc["alpha"], sc["beta"]]
+    elif workload == "bias_relu_f32":
+        vals = [rng.standard_normal(n, dtype=np.float32), rng.standard_normal(n, dtype=np.float32)]
+        vals += [sc["s"], sc["zero"]]
     elif workload == "copy_f32":
         vals = [_uniform_pm1_f32(rng, n)]
     elif workload == "classify_u32":
