@@ -730,7 +730,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         S.tiles_r = (T.n[2] + S.tile.tm - 1) / S.tile.tm;
         S.tiles_c = (T.n[3] + S.tile.tn - 1) / S.tile.tn;
         S.grid = S.tiles_r * S.tiles_c * T.n[0] * T.n[1];
-        S.lds = n_staged * S.tile.tn * (S.tile.tm + 1) * 4;
+        S.lds = n_staged * S.tile.tn * S.tile.tm * 4;
         S.name = S.variant == 0 ? "tiled_add_scaled_f32" : "tiled_generic";
         return;
     }

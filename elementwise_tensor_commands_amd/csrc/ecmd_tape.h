@@ -311,11 +311,39 @@ struct LinearShape {
 };
 int launch_linear(int variant, bool vec, LinearShape shape, const LinearArgs &A, LaunchGeometry g,
                   void *stream);
-// Tiled path: output tile of tm x tn elements (64 or 128 each).
+// Tiled path: output tile of tm x tn elements (tm and tn multiples of 32).
 struct TileShape {
     int tm, tn;
     int block;   // work-items per work-group: 256 or 512
 };
+
+// Tiled path: how a tile is split among work-items and laid out in LDS.
+//
+// A tile has tm rows and tn columns.  Work item v of a split takes 4
+// consecutive elements along the "minor" direction at (major, minor..minor+3):
+// output chunks are (row, 4 columns), staging vectors (column, 4 rows).  The
+// split puts each 32 consecutive items (a half-wavefront, the unit in which
+// gfx950 serves a wave64 LDS access over 32 four-byte banks) on 4 consecutive
+// majors 4a..4a+3 by 8 consecutive 4-element groups 8b..8b+7 along the minor
+// direction, so a half-wavefront's global accesses are 4 runs of 32 elements
+// (whole 128-byte lines of binary32).  minor_len is the tile's length in the
+// minor direction (a multiple of 32).
+constexpr void tile_split(int v, int minor_len, int &major, int &minor)
+{
+    const int groups = minor_len / 32;   // 8-vector groups along the minor direction
+    const int g = v >> 5;
+    major = 4 * (g / groups) + ((v >> 3) & 3);
+    minor = 4 * (8 * (g % groups) + (v & 7));
+}
+// LDS word of staged element (column c, row r) of a tile with tm rows: column
+// by column, the row index XOR-ed with the column's low five bits.  The bank
+// (word mod 32) is then (r mod 32) ^ (c mod 32).  A half-wavefront writing
+// element e of its staging vectors touches rows 4i + e (i over 8 consecutive
+// values) of columns 4a + q (q = 0..3): banks 4((i ^ a) mod 8) + (e ^ q), all
+// 32 distinct.  Reading element e of its chunks it touches rows 4a + q of
+// columns 4j + e (j over 8 consecutive values): banks 4((a ^ j) mod 8) +
+// (q ^ e), again all distinct.  No padding is needed: tm * tn words.
+constexpr int tile_word(int tm, int c, int r) { return c * tm + (r ^ (c & 31)); }
 int launch_tiled(int variant, bool nt, TileShape shape, const StridedArgs &A, LaunchGeometry g, void *stream);
 int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
 // Rows path: the linear path's specialised Programs (variant indexes the same

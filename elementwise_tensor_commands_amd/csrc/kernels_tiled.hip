@@ -13,16 +13,19 @@
 // s3 == 0 (broadcast along the columns, e.g. a per-channel bias): one value
 // per row.
 //
-// One work-group (TB = 256 or 512 work-items) owns a TM x TN output tile:
+// One work-group (TB = 256 or 512 work-items) owns a TM x TN output tile
+// (TM and TN multiples of 32):
 //   1. For every staged input it reads the TN tile columns as contiguous runs
-//      of TM elements (16-byte vectors, TM/4 work-items per run) and writes
-//      them into an LDS tile stored column by column with one padding word per
-//      column (pitch TM + 1, odd).  With an odd pitch the transposed read in
-//      step 2 hits 64 distinct banks for a 64 x 64 tile.
+//      of TM elements in 16-byte vectors (each half-wavefront: 4 columns x 32
+//      rows, whole 128-byte lines) and writes them into an LDS tile stored
+//      column by column, the row index XOR-swizzled by the column (tile_word).
 //   2. After one barrier each work-item evaluates TM*TN/(4*TB) chunks of 4
-//      consecutive elements of one row: direct inputs are read with 16-byte
-//      vector loads, staged ones from LDS, and outputs are written with 16-byte
-//      stores, so every global access is a contiguous run of TN elements.
+//      consecutive elements of one row (each half-wavefront: 4 rows x 32
+//      columns): direct inputs are read with 16-byte vector loads, staged ones
+//      from LDS, and outputs are written with 16-byte stores.
+// The swizzle makes both LDS phases free of bank conflicts (the argument is
+// at tile_word; a host test checks it for every instantiated shape), with no
+// padding words.
 // In the specialised kernels the direct inputs' loads are issued before the
 // barrier, together with the staging loads, so that a tile waits for one
 // round trip to memory instead of two.  Full tiles use the nontemporal cache
@@ -36,7 +39,7 @@
 //
 // Staging is a prior-art idea the Silk backend also assumes (its tiled kernels
 // default to a 16 KiB LDS segment, Silk "AMDGPU Backend", section "Code Object
-// Format"): a 64 x 65 binary32 tile is 16,640 bytes.
+// Format"): a 64 x 64 binary32 tile is 16,384 bytes.
 #include <hip/hip_runtime.h>
 
 #include "ecmd_eval.h"
@@ -67,14 +70,12 @@ __device__ __forceinline__ int clamp4(int64_t left) { return left <= 0 ? 0 : (le
 template <class EV, int MASK, bool NT, int TM, int TN, int TB>
 __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
 {
-    constexpr int kPitch = TM + 1;
-    constexpr int kWords = TN * kPitch;
-    constexpr int kRunVec = TM / 4;                     // 4-element vectors per staged column run
+    constexpr int kWords = TN * TM;
     constexpr int kSV = TN * TM / 4 / TB;               // staging vectors per work-item per staged input
-    constexpr int kRowVec = TN / 4;                     // 4-element chunks per output row
     constexpr int kP = TM * TN / 4 / TB;                // chunks per work-item
     constexpr bool kPrefetch = MASK != kMaskRuntime;
     static_assert(kSV >= 1 && kP >= 1, "tile too small for the work-group");
+    static_assert(TM % 32 == 0 && TN % 32 == 0 && TB % 64 == 0, "tile split needs multiples of 32");
     extern __shared__ uint32_t lds[];
 
     // Plane and tile coordinates (all counts fit in 32 bits: the grid is one
@@ -113,13 +114,14 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
     int count[kP];
 #pragma unroll
     for (int p = 0; p < kP; ++p) {
-        const int v = t + TB * p;
-        const int rl = v / kRowVec, cl = 4 * (v % kRowVec);
+        int rl, cl;
+        tile_split(t + TB * p, TN, rl, cl);
         count[p] = full ? 4 : (r0 + rl < rows ? clamp4(cols - (c0 + cl)) : 0);
     }
     auto load_direct = [&](int p) {
-        const int v = t + TB * p;
-        const int64_t r = r0 + v / kRowVec, c = c0 + 4 * (v % kRowVec);
+        int rl, cl;
+        tile_split(t + TB * p, TN, rl, cl);
+        const int64_t r = r0 + rl, c = c0 + cl;
         Regs<4> &Rp = R[kPrefetch ? p : 0];
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
@@ -146,7 +148,8 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
         for (int p = 0; p < kP; ++p) load_direct(p);
     }
 
-    // Stage the column-contiguous inputs: LDS word (cl, rl) at cl * kPitch + rl.
+    // Stage the column-contiguous inputs: element (cl, rl) at LDS word
+    // tile_word(TM, cl, rl).
 #pragma unroll
     for (int k = 0; k < kMaxIn; ++k) {
         if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
@@ -155,8 +158,8 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
             uint32_t sv[kSV][4];
 #pragma unroll
             for (int j = 0; j < kSV; ++j) {
-                const int v = t + TB * j;
-                const int cl = v / kRunVec, rl = 4 * (v % kRunVec);
+                int cl, rl;
+                tile_split(t + TB * j, TM, cl, rl);
                 const int64_t off = in_base(k) + (c0 + cl) * A.in_s[k][3] + (r0 + rl);
                 if (full) {
                     load_group<4, true, NT>(A.in[k], ty, off, 4, sv[j]);
@@ -168,10 +171,10 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
             }
 #pragma unroll
             for (int j = 0; j < kSV; ++j) {
-                const int v = t + TB * j;
-                const int cl = v / kRunVec, rl = 4 * (v % kRunVec);
+                int cl, rl;
+                tile_split(t + TB * j, TM, cl, rl);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[cl * kPitch + rl + e] = sv[j][e];
+                for (int e = 0; e < 4; ++e) dst[tile_word(TM, cl, rl + e)] = sv[j][e];
             }
         }
     }
@@ -180,8 +183,8 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
 #pragma unroll
     for (int p = 0; p < kP; ++p) {
         if (count[p] == 0) continue;
-        const int v = t + TB * p;
-        const int rl = v / kRowVec, cl = 4 * (v % kRowVec);
+        int rl, cl;
+        tile_split(t + TB * p, TN, rl, cl);
         const int64_t r = r0 + rl, c = c0 + cl;
         if constexpr (!kPrefetch) load_direct(p);
         Regs<4> &Rp = R[kPrefetch ? p : 0];
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
             if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
                 const uint32_t *src = lds + stage_pos<MASK>(A, k) * kWords;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Rp.in[k][e] = src[(cl + e) * kPitch + rl];
+                for (int e = 0; e < 4; ++e) Rp.in[k][e] = src[tile_word(TM, cl + e, rl)];
             }
         }
         uint32_t out[kMaxOut][4];
@@ -211,7 +214,7 @@ static int launch_one(const StridedArgs &A, LaunchGeometry g, void *stream, int 
 {
     auto kern = k_tiled<EV, MASK, NT, TM, TN, TB>;
     // Above 64 KiB of dynamic LDS the kernel must be allowed more, once per
-    // process (the largest instantiated tile needs 128 * 129 * 4 bytes per
+    // process (the largest instantiated tile needs 128 * 128 * 4 bytes per
     // staged input, within gfx950's 160 KiB).
     static int lds_allowed = 65536;
     if (lds_bytes > lds_allowed) {
@@ -235,7 +238,7 @@ int launch_tiled(int variant, bool nt, TileShape shape, const StridedArgs &A, La
 {
     int n_staged = 0;
     for (int k = 0; k < A.prog.n_in; ++k) n_staged += A.in_staged[k] != 0;
-    const int lds = n_staged * shape.tn * (shape.tm + 1) * 4;
+    const int lds = n_staged * shape.tn * shape.tm * 4;
     if (variant == 0) {
         // out = X + alpha * Yt with Yt (input 1) staged; the host picks it only
         // for that staging mask.

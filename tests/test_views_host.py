@@ -186,7 +186,7 @@ def test_four_staged_inputs_gather():
             ("u", ("add", "s", "t")), ("out", ("store", "u", 2))]
     tr = lambda: T((64, 64), (1, 64))
     p = E.from_spec(spec).plan(tr(), tr(), tr(), T((64, 64)), T((64, 64)))
-    assert p["path"] == "tiled" and p["lds_bytes"] == 3 * 64 * 65 * 4
+    assert p["path"] == "tiled" and p["lds_bytes"] == 3 * 64 * 64 * 4
     p = E.from_spec(spec).plan(tr(), tr(), tr(), tr(), T((64, 64)))
     assert p["path"] == "gather"
 
