@@ -283,6 +283,23 @@ __device__ __forceinline__ void rt_put(uint8_t dst, Regs<E> &R, const uint32_t (
     }
 }
 
+// Every opcode, for the interpreters' dispatch switches.
+#define ECMD_FOR_EACH_CODE(X)                                                                  \
+    X(C_MOV) X(C_ADD_F32) X(C_SUB_F32) X(C_MUL_F32) X(C_ADD_I32) X(C_SUB_I32) X(C_MUL_I32)      \
+    X(C_NEG_F32) X(C_NEG_I32) X(C_NEG_F16) X(C_CVT_F16_F32) X(C_CVT_F32_F16) X(C_CVT_I32_F32)   \
+    X(C_CVT_F32_I32) X(C_CVT_I32_F16) X(C_CVT_F16_I32)                                         \
+    X(C_EQ_F32) X(C_NE_F32) X(C_LT_F32) X(C_LE_F32) X(C_GT_F32) X(C_GE_F32)                     \
+    X(C_EQ_I32) X(C_NE_I32) X(C_LT_I32) X(C_LE_I32) X(C_GT_I32) X(C_GE_I32)                     \
+    X(C_LT_U32) X(C_LE_U32) X(C_GT_U32) X(C_GE_U32)                                             \
+    X(C_MIN_F32) X(C_MAX_F32) X(C_MIN_I32) X(C_MAX_I32) X(C_ABS_F32) X(C_ABS_I32) X(C_ABS_F16)  \
+    X(C_SELECT) X(C_ADD_F16) X(C_SUB_F16) X(C_MUL_F16) X(C_ADD_BF16) X(C_SUB_BF16) X(C_MUL_BF16) \
+    X(C_NEG_BF16) X(C_ABS_BF16) X(C_CVT_F16_BF16) X(C_CVT_BF16_F16) X(C_CVT_BF16_F32)           \
+    X(C_CVT_F32_BF16) X(C_CVT_BF16_I32) X(C_CVT_I32_BF16)                                       \
+    X(C_EQ_F16) X(C_NE_F16) X(C_LT_F16) X(C_LE_F16) X(C_GT_F16) X(C_GE_F16)                     \
+    X(C_EQ_BF16) X(C_NE_BF16) X(C_LT_BF16) X(C_LE_BF16) X(C_GT_BF16) X(C_GE_BF16)               \
+    X(C_MIN_F16) X(C_MAX_F16) X(C_MIN_BF16) X(C_MAX_BF16)
+static_assert(C_COUNT == 70, "ECMD_FOR_EACH_CODE lists every opcode");
+
 template <int E>
 __device__ __forceinline__ void rt_apply(uint8_t code, const uint32_t (&a)[E], const uint32_t (&b)[E],
                                          const uint32_t (&c)[E], uint32_t (&r)[E])
@@ -292,27 +309,7 @@ __device__ __forceinline__ void rt_apply(uint8_t code, const uint32_t (&a)[E], c
     case k:                                               \
         _Pragma("unroll") for (int e = 0; e < E; ++e) r[e] = apply<k>(a[e], b[e], c[e]); \
         break;
-        ECMD_APPLY(C_MOV) ECMD_APPLY(C_ADD_F32) ECMD_APPLY(C_SUB_F32) ECMD_APPLY(C_MUL_F32)
-        ECMD_APPLY(C_ADD_I32) ECMD_APPLY(C_SUB_I32) ECMD_APPLY(C_MUL_I32)
-        ECMD_APPLY(C_NEG_F32) ECMD_APPLY(C_NEG_I32) ECMD_APPLY(C_NEG_F16)
-        ECMD_APPLY(C_CVT_F16_F32) ECMD_APPLY(C_CVT_F32_F16) ECMD_APPLY(C_CVT_I32_F32)
-        ECMD_APPLY(C_CVT_F32_I32) ECMD_APPLY(C_CVT_I32_F16) ECMD_APPLY(C_CVT_F16_I32)
-        ECMD_APPLY(C_EQ_F32) ECMD_APPLY(C_NE_F32) ECMD_APPLY(C_LT_F32) ECMD_APPLY(C_LE_F32)
-        ECMD_APPLY(C_GT_F32) ECMD_APPLY(C_GE_F32) ECMD_APPLY(C_EQ_I32) ECMD_APPLY(C_NE_I32)
-        ECMD_APPLY(C_LT_I32) ECMD_APPLY(C_LE_I32) ECMD_APPLY(C_GT_I32) ECMD_APPLY(C_GE_I32)
-        ECMD_APPLY(C_LT_U32) ECMD_APPLY(C_LE_U32) ECMD_APPLY(C_GT_U32) ECMD_APPLY(C_GE_U32)
-        ECMD_APPLY(C_MIN_F32) ECMD_APPLY(C_MAX_F32) ECMD_APPLY(C_MIN_I32) ECMD_APPLY(C_MAX_I32)
-        ECMD_APPLY(C_ABS_F32) ECMD_APPLY(C_ABS_I32) ECMD_APPLY(C_ABS_F16) ECMD_APPLY(C_SELECT)
-        ECMD_APPLY(C_ADD_F16) ECMD_APPLY(C_SUB_F16) ECMD_APPLY(C_MUL_F16)
-        ECMD_APPLY(C_ADD_BF16) ECMD_APPLY(C_SUB_BF16) ECMD_APPLY(C_MUL_BF16)
-        ECMD_APPLY(C_NEG_BF16) ECMD_APPLY(C_ABS_BF16)
-        ECMD_APPLY(C_CVT_F16_BF16) ECMD_APPLY(C_CVT_BF16_F16) ECMD_APPLY(C_CVT_BF16_F32)
-        ECMD_APPLY(C_CVT_F32_BF16) ECMD_APPLY(C_CVT_BF16_I32) ECMD_APPLY(C_CVT_I32_BF16)
-        ECMD_APPLY(C_EQ_F16) ECMD_APPLY(C_NE_F16) ECMD_APPLY(C_LT_F16) ECMD_APPLY(C_LE_F16)
-        ECMD_APPLY(C_GT_F16) ECMD_APPLY(C_GE_F16)
-        ECMD_APPLY(C_EQ_BF16) ECMD_APPLY(C_NE_BF16) ECMD_APPLY(C_LT_BF16) ECMD_APPLY(C_LE_BF16)
-        ECMD_APPLY(C_GT_BF16) ECMD_APPLY(C_GE_BF16)
-        ECMD_APPLY(C_MIN_F16) ECMD_APPLY(C_MAX_F16) ECMD_APPLY(C_MIN_BF16) ECMD_APPLY(C_MAX_BF16)
+        ECMD_FOR_EACH_CODE(ECMD_APPLY)
 #undef ECMD_APPLY
     default:
         _Pragma("unroll") for (int e = 0; e < E; ++e) r[e] = 0u;

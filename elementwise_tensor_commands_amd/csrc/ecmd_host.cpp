@@ -61,6 +61,8 @@ struct Selection {
     int path = CMD_PATH_NONE;
     int variant = -1;
     bool jit = false;           // a run-time compiled kernel (variant -1 otherwise means the interpreter)
+    bool interp = false;        // linear path: the LDS-file interpreter (kernels_interp.hip)
+    int k_sub = 0, n_slot = 0;  // its sub-chunks per super-chunk and temporary slots
     bool vec = false;
     LinearShape shape{4, 4, false, true};
     bool xcd_remap = false;
@@ -560,6 +562,11 @@ int cu_count_cached(int dev) { return dev >= 0 && dev < 64 && g_cu_count[dev] > 
 
 // Work-items of one dispatch: its grid size is a 32-bit count.
 constexpr int64_t kMaxGridItems = (int64_t)1 << 31;
+// Linear interpreter: LDS register file budget per work-group for two
+// sub-chunks (at most 24 KiB keeps six or more work-groups on a CU), and the
+// grid cap past which its work-groups stride (4,096 per CU on 256 CUs).
+constexpr int kInterpLdsKiB = 24;
+constexpr int64_t kInterpMaxGrid = (int64_t)1 << 20;
 
 bool aligned(const void *p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes == 0; }
 
@@ -590,7 +597,29 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         for (int k = 0; k < P.n_in; ++k) bytes += numel * esize(B.in[k].dtype), all16 = all16 && esize(B.in[k].dtype) == 2;
         for (int k = 0; k < P.n_out; ++k) bytes += numel * esize(B.out[k].dtype), all16 = all16 && esize(B.out[k].dtype) == 2;
         S.shape = linear_shape(bytes, all16);
-        if (S.variant < 0 && !S.jit) S.shape.e = 4, S.shape.g = 4;   // the interpreter has one shape
+        if (S.vec && S.variant < 0 && !S.jit) {
+            // The interpreter: one wavefront per work-group, one super-chunk of
+            // k_sub x 256 elements each: two sub-chunks (measured fastest for
+            // binary32 and 16-bit data alike), one where the LDS register file
+            // would pass kInterpLdsKiB (fewer work-groups would fit a CU).
+            // ECMD_INTERP_K = 1, 2 or 4 overrides, for A/B runs.
+            int n_slot = 0;
+            for (int i = 0; i < P.n_ops; ++i) n_slot = std::max(n_slot, P.ops[i].dst - (int)kRefSlot + 1);
+            const int entries = P.n_in + n_slot;
+            int k = (int)env_int("ECMD_INTERP_K", 2);
+            if (k != 1 && k != 2 && k != 4) k = 2;
+            while (k > 1 && entries * k + P.n_uni > kInterpLdsKiB) k /= 2;
+            S.interp = true;
+            S.n_slot = n_slot;
+            S.k_sub = k;
+            S.lds = (entries * S.k_sub + P.n_uni) * 1024;
+            S.e = 4 * S.k_sub;
+            S.block = kInterpBlock;
+            S.grid = std::max<int64_t>(1, std::min<int64_t>(numel / (256 * S.k_sub), kInterpMaxGrid));
+            S.name = "linear_generic";
+            return;
+        }
+        if (S.variant < 0 && !S.jit) S.shape.e = 4, S.shape.g = 4;   // the per-element variant has one shape
         S.e = S.shape.e;
         S.block = kLinearBlock;
         // One wavefront per chunk of 64 * E elements (no grid-stride loop)
@@ -753,6 +782,31 @@ int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int
     if (rc) return rc;
     select_path(h, B, cu_count, S);
     return CMD_OK;
+}
+
+// The interpreter's register file in LDS, per work-group: the inputs' entries,
+// then the slots', each k_sub sub-chunks of 1 KiB, then one 1 KiB broadcast
+// entry per uniform value.  Every operand reference becomes `offset | step <<
+// 16` (see InterpTape).
+void resolve_interp_tape(const Program &P, int k_sub, int n_slot, InterpTape &T)
+{
+    std::memset(&T, 0, sizeof T);
+    const uint32_t sub = 1024, entry = sub * (uint32_t)k_sub;
+    T.uni_off = (uint32_t)(P.n_in + n_slot) * entry;
+    auto place = [&](uint8_t ref) -> uint32_t {
+        if (ref < kRefSlot) return (ref - kRefIn) * entry | sub << 16;
+        if (ref < kRefUni) return (uint32_t)(P.n_in + ref - kRefSlot) * entry | sub << 16;
+        return T.uni_off + (ref - kRefUni) * sub;   // step 0
+    };
+    for (int i = 0; i < P.n_ops; ++i) {
+        const TapeOp &o = P.ops[i];
+        const uint32_t a = place(o.a);
+        T.op[i][0] = o.code | ((place(o.dst) & 0xffffu) << 8);   // a slot's offset (its step is 1 KiB)
+        T.op[i][1] = a;
+        T.op[i][2] = o.b == kRefNone ? a : place(o.b);
+        T.op[i][3] = o.c == kRefNone ? a : place(o.c);
+    }
+    for (int k = 0; k < P.n_out; ++k) T.out[k] = place(P.out_ref[k]);
 }
 
 // Multiplier and shifts for dividing 32-bit values by d (1 <= d < 2^31), the
@@ -1031,6 +1085,10 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
             void *params[] = {&A};
             herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
                                               (hipStream_t)hip_stream, params, nullptr);
+        } else if (S.interp) {
+            InterpTape T;
+            resolve_interp_tape(h->prog, S.k_sub, S.n_slot, T);
+            herr = launch_linear_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds, hip_stream);
         } else {
             herr = launch_linear(S.variant, S.vec, S.shape, A, g, hip_stream);
         }

@@ -112,11 +112,18 @@ enum Code : uint8_t {
 };
 
 // Operands a, b, c: b is kRefNone for unary operations and c for every
-// operation except C_SELECT.
-struct TapeOp {
+// operation except C_SELECT.  An operation is 8 bytes (three zero padding
+// bytes) and 4-byte aligned, so that a kernel walking the tape with a
+// run-time index reads each operation with one scalar load from the argument
+// block; a 5-byte operation sits at unaligned offsets, which the scalar unit
+// cannot load, and the compiler falls back to vector loads that wait for all
+// outstanding memory traffic.
+struct alignas(4) TapeOp {
     uint8_t code, dst, a, b;
     uint8_t c = kRefNone;
+    uint8_t pad[3] = {0, 0, 0};
 };
+static_assert(sizeof(TapeOp) == 8, "one operation is two dwords");
 
 // The lowered Command.  Unused entries are zero so that two Programs can be
 // compared byte for byte.
@@ -311,6 +318,21 @@ struct LinearShape {
 };
 int launch_linear(int variant, bool vec, LinearShape shape, const LinearArgs &A, LaunchGeometry g,
                   void *stream);
+// The linear path's interpreter (kernels_interp.hip) keeps its register file
+// in LDS.  The host resolves every operand reference of the Program to a place
+// in that file, so the kernel decodes an operation with one scalar load and no
+// arithmetic: a reference is `offset | step << 16`, the byte offset of its
+// first 1 KiB sub-chunk entry and the step between sub-chunks (0 for a
+// uniform value's single broadcast entry).
+struct InterpTape {
+    uint32_t op[kMaxOps][4];   // code | dst offset << 8; a; b; c (b and c repeat a when unused)
+    uint32_t out[kMaxOut];     // each output's value
+    uint32_t uni_off;          // byte offset of the uniform values' broadcast entries
+};
+// One wavefront per work-group, k_sub (1, 2 or 4) sub-chunks of 256 elements
+// per super-chunk, an LDS register file of lds_bytes.
+int launch_linear_interp(int k_sub, bool nt_load, bool nt_store, const LinearArgs &A, const InterpTape &T,
+                         LaunchGeometry g, int lds_bytes, void *stream);
 // Tiled path: output tile of tm x tn elements (tm and tn multiples of 32).
 struct TileShape {
     int tm, tn;
@@ -351,6 +373,7 @@ int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
 int launch_rows(int variant, bool nt_load, bool nt_store, const StridedArgs &A, LaunchGeometry g, void *stream);
 
 constexpr int kLinearBlock = 256;
+constexpr int kInterpBlock = 64;
 constexpr int kTileBlock = 256;
 constexpr int kGatherE = 4;
 constexpr int kGatherBlock = 256;

@@ -1,0 +1,114 @@
+"""GPU parity of the linear path's interpreter (kernels_interp.hip: the
+register file in LDS, binary32 inputs loaded straight into it) against the
+oracle.
+
+  * random Commands over every operation at lengths around the 256-element
+    sub-chunk and the super-chunk boundaries, with one, two and four
+    sub-chunks per super-chunk (ECMD_INTERP_K);
+  * a large register file (six inputs, six uniform values, eight live
+    temporaries), which the host fits in LDS with one sub-chunk;
+  * Commands without operations (fills of int32 and binary16, a binary16
+    pass-through) and outputs of both widths from one Command.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import compare, dev, host, run_gpu, run_oracle, to_dev
+from random_commands import _random_inputs, _random_spec
+from specs import arg_dtypes
+
+pytestmark = pytest.mark.gpu
+
+LENGTHS = [1, 63, 255, 256, 511, 512, 513, 1023, 1024, 1025, 4096 + 300, 65536 + 77, (1 << 20) + 3]
+
+
+def _gpu_values(vals):
+    return [to_dev(v) if isinstance(v, np.ndarray) else
+            (v if v.dtype == np.uint16 else float(v) if v.dtype.kind == "f" else int(v)) for v in vals]
+
+
+def _run_interp(spec, vals, n, what):
+    import elementwise_tensor_commands_amd as ecmd
+    ref = run_oracle(spec, vals)
+    gv = _gpu_values(vals)
+    _, outs = arg_dtypes(spec)
+    try:
+        cmd, got = run_gpu(spec, gv, [((n,), d) for d in outs])
+    except ecmd.Error as e:
+        assert e.name == "CMD_E_LIMIT", e          # more live temporaries than registers
+        pytest.skip(str(e))
+    plan = cmd.plan(*gv, *got)
+    assert plan["path"] == "linear" and plan["kernel"] == "linear_generic" and plan["block"] == 64, plan
+    for k, (g, r) in enumerate(zip(got, ref)):
+        compare(host(g), r, 0, "%s out%d\n%s" % (what, k, cmd.dump()))
+    return plan
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("seed", range(13))
+def test_random_commands_each_sub_chunk_count(monkeypatch, k, seed):
+    monkeypatch.setenv("ECMD_FORCE_GENERIC", "1")
+    monkeypatch.setenv("ECMD_INTERP_K", str(k))
+    rng = np.random.default_rng(7000 + 31 * seed + k)
+    spec = _random_spec(rng, int(rng.integers(1, 6)), int(rng.integers(1, 14)), 1)
+    n = LENGTHS[seed]
+    vals = _random_inputs(rng, spec, (n,))
+    try:
+        run_oracle(spec, vals)
+    except Exception as e:   # the oracle front end refuses -> not a valid Command
+        pytest.skip("not a valid Command: %s" % e)
+    plan = _run_interp(spec, vals, n, "K=%d seed %d n=%d" % (k, seed, n))
+    # k sub-chunks, or fewer where the LDS register file would run past its budget
+    assert plan["elems_per_thread"] in [4 * j for j in (1, 2, 4) if j <= k], plan
+
+
+def test_large_register_file():
+    """t_i = x_i * s_i for six inputs and six scalars, two more temporaries, all
+    eight live at once, then summed (6 + 6 + 2 = 14 CommandArguments of the 16):
+    14 entries of inputs and slots plus 6 uniform entries, which the host fits
+    in LDS with one sub-chunk (20 KiB)."""
+    spec = [("x%d" % i, ("load", "f32", 1)) for i in range(6)]
+    spec += [("s%d" % i, ("scalar", "f32")) for i in range(6)]
+    spec += [("t%d" % i, ("mul", "x%d" % i, "s%d" % i)) for i in range(6)]
+    spec += [("t6", ("sub", "x0", "x1")), ("t7", ("add", "x2", "x3"))]
+    acc = "t0"
+    for i in range(1, 8):
+        spec.append(("a%d" % i, ("add", acc, "t%d" % i)))
+        acc = "a%d" % i
+    spec += [("o0", ("store", acc, 1)), ("o1", ("store", "t3", 1))]
+    n = (1 << 16) + 1000
+    rng = np.random.default_rng(11)
+    vals = [rng.standard_normal(n).astype(np.float32) for _ in range(6)]
+    vals += [np.float32(rng.standard_normal()) for _ in range(6)]
+    plan = _run_interp(spec, vals, n, "six inputs, six scalars, eight slots")
+    assert plan["elems_per_thread"] == 4 and plan["lds_bytes"] == (14 + 6) * 1024, plan
+
+
+@pytest.mark.parametrize("dt,val", [("i32", -123456789), ("f16", -0.0), ("bf16", np.uint16(0x7F80))])
+@pytest.mark.parametrize("n", [5, 512, 70001])
+def test_fill_without_inputs(dt, val, n):
+    spec = [("s", ("scalar", dt)), ("o", ("store", "s", 1))]
+    import torch
+    from gpu_util import NPD, TD
+    import elementwise_tensor_commands_amd as ecmd
+    out = torch.full((n,), 3, dtype=TD[dt], device=dev())
+    c = ecmd.from_spec(spec)
+    gval = val if dt == "bf16" else (float(val) if dt == "f16" else int(val))
+    c.launch(gval, out)
+    torch.cuda.synchronize()
+    plan = c.plan(gval, out)
+    assert plan["kernel"] == "linear_generic", plan
+    ref = run_oracle(spec, [np.uint16(val) if dt == "bf16" else NPD[dt](val)],
+                     outputs=[np.zeros(n, NPD[dt])])[0]
+    compare(host(out), ref, 0, "fill %s n=%d" % (dt, n))
+
+
+@pytest.mark.parametrize("n", [3, 777, (1 << 18) + 9])
+def test_pass_through_and_mixed_width_outputs(n):
+    """out0 = x (binary16, no operation), out1 = f32(x), out2 = bf16(f32(x) * s)."""
+    spec = [("x", ("load", "f16", 1)), ("s", ("scalar", "f32")), ("w", ("cvt", "x", "f32")),
+            ("p", ("mul", "w", "s")), ("b", ("cvt", "p", "bf16")),
+            ("o0", ("store", "x", 1)), ("o1", ("store", "w", 1)), ("o2", ("store", "b", 1))]
+    rng = np.random.default_rng(n)
+    vals = [(rng.standard_normal(n) * 300).astype(np.float16), np.float32(-0.375)]
+    _run_interp(spec, vals, n, "pass-through n=%d" % n)

@@ -59,8 +59,10 @@ def _release():
 
 @pytest.mark.parametrize("name,specialised", [("add_f32", True), ("add_i32", False)])
 def test_linear_past_the_dispatch_limit(name, specialised):
-    """2^33 + 4099 elements: 2^25 + 16 wavefront chunks of 256 elements, the
-    grid capped at 2^23 work-groups (2^31 work-items), 3 elements of tail."""
+    """2^33 + 4099 elements.  Specialised kernel: 2^25 + 16 wavefront chunks
+    of 256 elements, the grid capped at 2^23 work-groups (2^31 work-items), 3
+    elements of tail.  Interpreter: 2^24 + 8 super-chunks of 512 elements over
+    2^20 work-groups (16 or 17 each), 3 elements of tail."""
     import elementwise_tensor_commands_amd as ecmd
     n = (1 << 33) + 4099
     f32 = name == "add_f32"
@@ -75,7 +77,10 @@ def test_linear_past_the_dispatch_limit(name, specialised):
         cmd = ecmd.from_spec(SPECS[name])
         plan = cmd.plan(x, y, z)
         assert plan["path"] == "linear" and plan["specialised"] == specialised, plan
-        assert plan["grid"] * plan["block"] == 1 << 31, plan
+        if specialised:       # the grid is capped at 2^31 work-items and the kernel loops
+            assert plan["grid"] * plan["block"] == 1 << 31, plan
+        else:                 # the interpreter caps its grid at 2^20 work-groups and strides
+            assert plan["grid"] == 1 << 20 and plan["block"] == 64, plan
         cmd.launch(x, y, z)
         torch.cuda.synchronize()
         idx = _sample(n)

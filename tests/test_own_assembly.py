@@ -8,7 +8,9 @@
     default execution mode the Silk "AMDGPU Backend" page lists under "Code
     Object Format");
   * the linear kernels move data with 128-bit global loads and stores, the
-    tiled kernels go through LDS.
+    tiled kernels go through LDS;
+  * the linear interpreter loads binary32 inputs straight into LDS and waits
+    for those loads (vmcnt 0) before it reads LDS.
 """
 import os
 import re
@@ -18,7 +20,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 BUILD = os.path.join(ROOT, "_build")
-FILES = ["kernels_linear", "kernels_tiled", "kernels_gather"]
+FILES = ["kernels_linear", "kernels_interp", "kernels_rows", "kernels_tiled", "kernels_gather"]
 
 
 def _asm(name):
@@ -105,3 +107,22 @@ def test_tiled_uses_lds():
     ks = _kernels(_asm("kernels_tiled"))
     for name, (body, _) in ks.items():
         assert "ds_write" in body and "ds_read" in body and "s_barrier" in body, name
+
+
+def test_interp_waits_for_lds_dma():
+    """Direct global-to-LDS loads are not ordered before later LDS reads by the
+    compiler: the interpreter waits for them explicitly.  In program order, no
+    ds_read may follow a global_load_lds without an s_waitcnt vmcnt(0) between."""
+    ks = _kernels(_asm("kernels_interp"))
+    assert len(ks) == 12, list(ks)     # K = 1, 2, 4 x nontemporal loads x stores
+    for name, (body, _) in ks.items():
+        assert "global_load_lds_dwordx4" in body and "ds_read_b128" in body, name
+        pending = False
+        for line in body.splitlines():
+            t = line.strip()
+            if t.startswith("global_load_lds"):
+                pending = True
+            elif t.startswith("s_waitcnt") and "vmcnt(0)" in t:
+                pending = False
+            elif t.startswith("ds_read"):
+                assert not pending, "%s: LDS read before the LDS loads were waited for" % name
