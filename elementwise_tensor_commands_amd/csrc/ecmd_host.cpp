@@ -570,6 +570,27 @@ constexpr int64_t kInterpMaxGrid = (int64_t)1 << 20;
 
 bool aligned(const void *p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes == 0; }
 
+// The LDS-file interpreter (linear and rows paths): one wavefront per
+// work-group, one super-chunk of k_sub sub-chunks each: two sub-chunks
+// (measured fastest for binary32 and 16-bit data alike), one where the LDS
+// register file would pass kInterpLdsKiB (fewer work-groups would fit a CU).
+// ECMD_INTERP_K = 1, 2 or 4 overrides, for A/B runs.  The caller sets the grid.
+void size_interp(const Program &P, Selection &S)
+{
+    int n_slot = 0;
+    for (int i = 0; i < P.n_ops; ++i) n_slot = std::max(n_slot, P.ops[i].dst - (int)kRefSlot + 1);
+    const int entries = P.n_in + n_slot;
+    int k = (int)env_int("ECMD_INTERP_K", 2);
+    if (k != 1 && k != 2 && k != 4) k = 2;
+    while (k > 1 && entries * k + P.n_uni > kInterpLdsKiB) k /= 2;
+    S.interp = true;
+    S.n_slot = n_slot;
+    S.k_sub = k;
+    S.lds = (entries * k + P.n_uni) * 1024;
+    S.e = 4 * k;
+    S.block = kInterpBlock;
+}
+
 void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
 {
     const Program &P = h->prog;
@@ -598,23 +619,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         for (int k = 0; k < P.n_out; ++k) bytes += numel * esize(B.out[k].dtype), all16 = all16 && esize(B.out[k].dtype) == 2;
         S.shape = linear_shape(bytes, all16);
         if (S.vec && S.variant < 0 && !S.jit) {
-            // The interpreter: one wavefront per work-group, one super-chunk of
-            // k_sub x 256 elements each: two sub-chunks (measured fastest for
-            // binary32 and 16-bit data alike), one where the LDS register file
-            // would pass kInterpLdsKiB (fewer work-groups would fit a CU).
-            // ECMD_INTERP_K = 1, 2 or 4 overrides, for A/B runs.
-            int n_slot = 0;
-            for (int i = 0; i < P.n_ops; ++i) n_slot = std::max(n_slot, P.ops[i].dst - (int)kRefSlot + 1);
-            const int entries = P.n_in + n_slot;
-            int k = (int)env_int("ECMD_INTERP_K", 2);
-            if (k != 1 && k != 2 && k != 4) k = 2;
-            while (k > 1 && entries * k + P.n_uni > kInterpLdsKiB) k /= 2;
-            S.interp = true;
-            S.n_slot = n_slot;
-            S.k_sub = k;
-            S.lds = (entries * S.k_sub + P.n_uni) * 1024;
-            S.e = 4 * S.k_sub;
-            S.block = kInterpBlock;
+            size_interp(P, S);
             S.grid = std::max<int64_t>(1, std::min<int64_t>(numel / (256 * S.k_sub), kInterpMaxGrid));
             S.name = "linear_generic";
             return;
@@ -680,6 +685,10 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
             S.shape = linear_shape(bytes);
             S.shape.nt_store = S.shape.nt_store && lines;
             S.name = S.jit ? "jit_rows" : rows_name(S.variant);
+            if (S.variant < 0 && !S.jit) {          // the LDS-file interpreter, 64 K vectors per work-group
+                size_interp(P, S);
+                S.grid = std::min<int64_t>((n_vec + 64 * S.k_sub - 1) / (64 * S.k_sub), kInterpMaxGrid);
+            }
             return;
         }
     }
@@ -842,6 +851,8 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
         A.n_vec = S.n_vec;
         A.div_vec = make_fast_div((uint32_t)((C.n[3] + 3) / 4));
         A.wave_in_row = ((C.n[3] + 3) / 4) % 64 == 0 ? 1u : 0u;
+        for (int k = 0; k < h->prog.n_in; ++k)
+            if (S.rowconst[k] && esize(B.in[k].dtype) == 2) A.rowconst16 = 1u;
         A.div_n2 = make_fast_div((uint32_t)C.n[2]);
         A.div_n1 = make_fast_div((uint32_t)C.n[1]);
     }
@@ -1106,9 +1117,14 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
             herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
                                               (hipStream_t)hip_stream, params, nullptr);
         } else {
-            herr = S.path == CMD_PATH_TILED  ? launch_tiled(S.variant, nt, S.tile, A, g, hip_stream)
-                   : S.path == CMD_PATH_ROWS ? launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream)
-                                             : launch_gather(A, g, hip_stream);
+            InterpTape T;
+            if (S.interp) resolve_interp_tape(h->prog, S.k_sub, S.n_slot, T);
+            herr = S.path == CMD_PATH_TILED ? launch_tiled(S.variant, nt, S.tile, A, g, hip_stream)
+                   : S.path == CMD_PATH_ROWS
+                       ? (S.interp ? launch_rows_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds,
+                                                        hip_stream)
+                                   : launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream))
+                       : launch_gather(A, g, hip_stream);
         }
     }
     if (herr != 0)

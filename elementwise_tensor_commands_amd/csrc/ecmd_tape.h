@@ -183,6 +183,7 @@ struct StridedArgs {
     uint8_t in_rowconst[kMaxIn];// tiled and rows paths: 1 = stride 0 along dimension 3 (one value per row)
     int64_t n_vec;              // rows path: vectors in all, ceil(n[3] / 4) per row
     uint32_t wave_in_row;       // rows path: 1 = a multiple of 64 vectors per row (no wavefront spans two rows)
+    uint32_t rowconst16;        // rows path: 1 = some row-constant input is 16-bit
     FastDiv div_vec, div_n2, div_n1;   // rows path: by vectors per row, by n[2], by n[1]
     Program prog;
 };
@@ -333,6 +334,10 @@ struct InterpTape {
 // per super-chunk, an LDS register file of lds_bytes.
 int launch_linear_interp(int k_sub, bool nt_load, bool nt_store, const LinearArgs &A, const InterpTape &T,
                          LaunchGeometry g, int lds_bytes, void *stream);
+// The same interpreter over the rows path's vectors (k_sub x 64 vectors of 4
+// elements per super-chunk).
+int launch_rows_interp(int k_sub, bool nt_load, bool nt_store, const StridedArgs &A, const InterpTape &T,
+                       LaunchGeometry g, int lds_bytes, void *stream);
 // Tiled path: output tile of tm x tn elements (tm and tn multiples of 32).
 struct TileShape {
     int tm, tn;

@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ecmd_kern_linear.h"
+#include "ecmd_kern_rows.h"
 
 namespace ecmd {
 
@@ -45,6 +46,71 @@ typedef __attribute__((address_space(1))) void *global_addr_t;
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kSubBytes = 64 * 16;   // one entry of one sub-chunk: 64 lanes x 16 bytes
 
+// Broadcast entries of the uniform values (after the inputs' and slots').
+__device__ __forceinline__ void interp_uniforms(const Program &P, const uint32_t *uni, const InterpTape &T,
+                                                uint8_t *file, int lane_off)
+{
+#pragma unroll
+    for (int u = 0; u < kMaxUni; ++u) {
+        if (u < P.n_uni) {
+            const uint32_t x = uni[u];
+            *reinterpret_cast<u32x4 *>(file + T.uni_off + u * kSubBytes + lane_off) = u32x4{x, x, x, x};
+        }
+    }
+}
+
+// Walks the tape once over the K sub-chunks of the wavefront's file.
+template <int K>
+__device__ __forceinline__ void interp_tape(const Program &P, const InterpTape &T, uint8_t *file, int lane_off)
+{
+    const int n_ops = P.n_ops;
+    for (int i = 0; i < n_ops; ++i) {
+        const uint32_t w0 = T.op[i][0], wa = T.op[i][1], wb = T.op[i][2], wc = T.op[i][3];
+        const uint8_t *pa = file + (wa & 0xffffu) + lane_off, *pb = file + (wb & 0xffffu) + lane_off;
+        const uint8_t *pc = file + (wc & 0xffffu) + lane_off;
+        const uint32_t as = wa >> 16, bs = wb >> 16, cs = wc >> 16;
+        uint8_t *pd = file + (w0 >> 8) + lane_off;
+        switch (w0 & 0xffu) {
+#define ECMD_INTERP_CASE(C)                                                                        \
+    case C:                                                                                        \
+        _Pragma("unroll") for (int j = 0; j < K; ++j) {                                            \
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(pa + j * as);                         \
+            const u32x4 b = *reinterpret_cast<const u32x4 *>(pb + j * bs);                         \
+            u32x4 cv = {0u, 0u, 0u, 0u};                                                           \
+            if constexpr (C == C_SELECT) cv = *reinterpret_cast<const u32x4 *>(pc + j * cs);       \
+            u32x4 r;                                                                               \
+            r.x = apply<C>(a.x, b.x, cv.x);                                                        \
+            r.y = apply<C>(a.y, b.y, cv.y);                                                        \
+            r.z = apply<C>(a.z, b.z, cv.z);                                                        \
+            r.w = apply<C>(a.w, b.w, cv.w);                                                        \
+            *reinterpret_cast<u32x4 *>(pd + j * kSubBytes) = r;                                    \
+        }                                                                                          \
+        break;
+            ECMD_FOR_EACH_CODE(ECMD_INTERP_CASE)
+#undef ECMD_INTERP_CASE
+        default:
+            break;
+        }
+    }
+}
+
+__device__ __forceinline__ u32x4 widen16(u32x2 d) { return u32x4{d.x & 0xffffu, d.x >> 16, d.y & 0xffffu, d.y >> 16}; }
+
+template <bool NTS>
+__device__ __forceinline__ void store_vec(void *p, uint8_t ty, int64_t off, const u32x4 &o)
+{
+    if (is16(ty)) {
+        const u32x2 d = {(o.x & 0xffffu) | (o.y << 16), (o.z & 0xffffu) | (o.w << 16)};
+        u32x2 *q = reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p) + off);
+        if constexpr (NTS) __builtin_nontemporal_store(d, q);
+        else *q = d;
+    } else {
+        u32x4 *q = reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(p) + off);
+        if constexpr (NTS) __builtin_nontemporal_store(o, q);
+        else *q = o;
+    }
+}
+
 template <int K, bool NTL, bool NTS>
 __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const InterpTape T)
 {
@@ -53,15 +119,7 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
     const Program &P = A.prog;
     const int n_in = P.n_in;
     const int lane_off = lane * 16;
-    // Broadcast entries of the uniform values, after the inputs' and slots'.
-    uint8_t *uni_file = file + T.uni_off;
-#pragma unroll
-    for (int u = 0; u < kMaxUni; ++u) {
-        if (u < P.n_uni) {
-            const uint32_t x = A.uni[u];
-            *reinterpret_cast<u32x4 *>(uni_file + u * kSubBytes + lane_off) = u32x4{x, x, x, x};
-        }
-    }
+    interp_uniforms(P, A.uni, T, file, lane_off);
     constexpr int kSuper = K * 256;
     const int64_t nsup = A.n / kSuper;
     for (int64_t c = blockIdx.x; c < nsup; c += gridDim.x) {
@@ -91,101 +149,236 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
             if (k < n_in && is16(P.in_ty[k])) {
                 uint8_t *dst = file + k * K * kSubBytes + lane_off;
 #pragma unroll
-                for (int j = 0; j < K; ++j) {
-                    const u32x2 d = h16[k][j];
-                    *reinterpret_cast<u32x4 *>(dst + j * kSubBytes) =
-                        u32x4{d.x & 0xffffu, d.x >> 16, d.y & 0xffffu, d.y >> 16};
-                }
+                for (int j = 0; j < K; ++j) *reinterpret_cast<u32x4 *>(dst + j * kSubBytes) = widen16(h16[k][j]);
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         // 2. the tape, once per super-chunk
-        const int n_ops = P.n_ops;
-        for (int i = 0; i < n_ops; ++i) {
-            const uint32_t w0 = T.op[i][0], wa = T.op[i][1], wb = T.op[i][2], wc = T.op[i][3];
-            const uint8_t *pa = file + (wa & 0xffffu) + lane_off, *pb = file + (wb & 0xffffu) + lane_off;
-            const uint8_t *pc = file + (wc & 0xffffu) + lane_off;
-            const uint32_t as = wa >> 16, bs = wb >> 16, cs = wc >> 16;
-            uint8_t *pd = file + (w0 >> 8) + lane_off;
-            switch (w0 & 0xffu) {
-#define ECMD_INTERP_CASE(C)                                                                        \
-    case C:                                                                                        \
-        _Pragma("unroll") for (int j = 0; j < K; ++j) {                                            \
-            const u32x4 a = *reinterpret_cast<const u32x4 *>(pa + j * as);                         \
-            const u32x4 b = *reinterpret_cast<const u32x4 *>(pb + j * bs);                         \
-            u32x4 cv = {0u, 0u, 0u, 0u};                                                           \
-            if constexpr (C == C_SELECT) cv = *reinterpret_cast<const u32x4 *>(pc + j * cs);       \
-            u32x4 r;                                                                               \
-            r.x = apply<C>(a.x, b.x, cv.x);                                                        \
-            r.y = apply<C>(a.y, b.y, cv.y);                                                        \
-            r.z = apply<C>(a.z, b.z, cv.z);                                                        \
-            r.w = apply<C>(a.w, b.w, cv.w);                                                        \
-            *reinterpret_cast<u32x4 *>(pd + j * kSubBytes) = r;                                    \
-        }                                                                                          \
-        break;
-                ECMD_FOR_EACH_CODE(ECMD_INTERP_CASE)
-#undef ECMD_INTERP_CASE
-            default:
-                break;
-            }
-        }
+        interp_tape<K>(P, T, file, lane_off);
         // 3. outputs
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < P.n_out) {
                 const uint32_t wo = T.out[k], os = wo >> 16;
                 const uint8_t *po = file + (wo & 0xffffu) + lane_off;
-                if (is16(P.out_ty[k])) {
-                    uint16_t *dst = static_cast<uint16_t *>(A.out[k]) + base;
 #pragma unroll
-                    for (int j = 0; j < K; ++j) {
-                        const u32x4 o = *reinterpret_cast<const u32x4 *>(po + j * os);
-                        const u32x2 d = {(o.x & 0xffffu) | (o.y << 16), (o.z & 0xffffu) | (o.w << 16)};
-                        u32x2 *q = reinterpret_cast<u32x2 *>(dst + j * 256);
-                        if constexpr (NTS) __builtin_nontemporal_store(d, q);
-                        else *q = d;
-                    }
-                } else {
-                    uint32_t *dst = static_cast<uint32_t *>(A.out[k]) + base;
-#pragma unroll
-                    for (int j = 0; j < K; ++j) {
-                        const u32x4 o = *reinterpret_cast<const u32x4 *>(po + j * os);
-                        u32x4 *q = reinterpret_cast<u32x4 *>(dst + j * 256);
-                        if constexpr (NTS) __builtin_nontemporal_store(o, q);
-                        else *q = o;
-                    }
-                }
+                for (int j = 0; j < K; ++j)
+                    store_vec<NTS>(A.out[k], P.out_ty[k], base + j * 256,
+                                   *reinterpret_cast<const u32x4 *>(po + j * os));
             }
         }
     }
     if (blockIdx.x == gridDim.x - 1) linear_tail<RtEval, 1>(A, nsup * kSuper);
 }
 
-template <int K, bool NTL, bool NTS>
-static int launch_one(const LinearArgs &A, const InterpTape &T, LaunchGeometry g, int lds, void *stream)
+// The rows path's interpreter: the same register file and tape walk over the
+// rows path's vectors (see ecmd_kern_rows.h): sub-chunk j of super-chunk c is
+// the 64 vectors (c K + j) 64 .. + 63, lane l taking one.  Whole vectors of
+// direct binary32 inputs go straight into LDS; row-constant inputs (one value
+// per row) and 16-bit inputs pass through registers; a wavefront holding a
+// partial last vector of a row (n3 not a multiple of 4) or lanes past the
+// last vector loads element by element, and such lanes store the same way or
+// not at all.
+//
+// WROW: every row holds a multiple of 64 vectors, so a sub-chunk (64
+// consecutive vectors from a multiple of 64) lies in one row: the row and
+// every operand's row offset are computed once, in scalar registers, and
+// only the column is per lane.
+template <int K, bool NTL, bool NTS, bool WROW>
+__device__ __forceinline__ void rows_interp_body(const StridedArgs &A, const InterpTape &T, uint8_t *file)
 {
-    hipLaunchKernelGGL((k_linear_interp<K, NTL, NTS>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
-                       (hipStream_t)stream, A, T);
+    const int lane = threadIdx.x;
+    const Program &P = A.prog;
+    const int n_in = P.n_in;
+    const int lane_off = lane * 16;
+    const uint32_t n_vec = (uint32_t)A.n_vec;   // below 2^31 (host)
+    const uint32_t nsup = (n_vec + K * 64 - 1) / (K * 64);
+    for (uint32_t c = blockIdx.x; c < nsup; c += gridDim.x) {
+        // Per sub-chunk: the row (b0, b1, r), this lane's first column and count.
+        uint32_t rb0[K], rb1[K], rr[K], col[K];
+        int count[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const uint32_t v = (c * K + j) * 64 + (WROW ? 0 : lane);   // WROW: the sub-chunk's first vector
+            const uint32_t q = fast_div(A.div_vec, v);
+            col[j] = 4 * (v - q * A.div_vec.d) + (WROW ? 4 * lane : 0);
+            const uint32_t t = fast_div(A.div_n2, q);
+            rr[j] = q - t * A.div_n2.d;
+            rb0[j] = fast_div(A.div_n1, t);
+            rb1[j] = t - rb0[j] * A.div_n1.d;
+            const int64_t left = A.n[3] - (int64_t)col[j];
+            count[j] = v >= n_vec ? 0 : (left >= 4 ? 4 : (int)left);
+        }
+        auto row_of = [&](const int64_t (&s)[4], int j) {
+            return (int64_t)rb0[j] * s[0] + (int64_t)rb1[j] * s[1] + (int64_t)rr[j] * s[2];
+        };
+        // 1. inputs.  When every lane holds whole vectors (the common case,
+        // decided per wavefront) all branches are uniform: direct binary32
+        // inputs go straight into LDS, the others into registers, every load
+        // issued before anything is waited for.  Branches that differ between
+        // lanes would make the compiler wait for each load before the paths
+        // join, one memory round trip per input.
+        bool full = !A.rowconst16;
+#pragma unroll
+        for (int j = 0; j < K; ++j) full = full && count[j] == 4;
+        const bool fast = __all(full);
+        if (fast) {
+            // Every input by direct loads to LDS, so that no load has a vector
+            // register to wait for: whole binary32 vectors into their entries;
+            // a row-constant binary32 value (4 bytes) and the two 4-byte
+            // halves of a binary16 / bfloat16 vector into the first 256 and
+            // 512 bytes of the entry, widened in place after the wait below.
+#pragma unroll
+            for (int k = 0; k < kMaxIn; ++k) {
+                if (k < n_in) {
+                    const bool h16 = is16(P.in_ty[k]);
+                    uint8_t *dst = file + k * K * kSubBytes;
+#pragma unroll
+                    for (int j = 0; j < K; ++j) {
+                        const int64_t row = row_of(A.in_s[k], j);
+                        if (A.in_rowconst[k]) {
+                            __builtin_amdgcn_global_load_lds(
+                                (global_addr_t)(static_cast<const uint32_t *>(A.in[k]) + row),
+                                (lds_addr_t)(dst + j * kSubBytes), 4, 0, 0);
+                        } else if (!h16) {
+                            __builtin_amdgcn_global_load_lds(
+                                (global_addr_t)(static_cast<const uint32_t *>(A.in[k]) + row + col[j]),
+                                (lds_addr_t)(dst + j * kSubBytes), 16, 0, NTL ? 2 : 0);
+                        } else {
+                            const uint16_t *src = static_cast<const uint16_t *>(A.in[k]) + row + col[j];
+                            __builtin_amdgcn_global_load_lds((global_addr_t)src, (lds_addr_t)(dst + j * kSubBytes),
+                                                             4, 0, NTL ? 2 : 0);
+                            __builtin_amdgcn_global_load_lds((global_addr_t)(src + 2),
+                                                             (lds_addr_t)(dst + j * kSubBytes + 256), 4, 0,
+                                                             NTL ? 2 : 0);
+                        }
+                    }
+                }
+            }
+        } else {
+            // Partial vectors or lanes past the end: element by element.
+#pragma unroll
+            for (int k = 0; k < kMaxIn; ++k) {
+                if (k < n_in) {
+                    const uint8_t ty = P.in_ty[k];
+                    uint8_t *dst = file + k * K * kSubBytes + lane_off;
+#pragma unroll
+                    for (int j = 0; j < K; ++j) {
+                        const int64_t row = row_of(A.in_s[k], j);
+                        uint32_t e[4] = {0u, 0u, 0u, 0u};
+                        if (A.in_rowconst[k]) {
+                            uint32_t one[1] = {0u};
+                            if (count[j] > 0) load_elems<1, false>(A.in[k], ty, row, 1, one);
+                            e[0] = e[1] = e[2] = e[3] = one[0];
+                        } else if (count[j] > 0) {
+                            load_elems<4, false>(A.in[k], ty, row + col[j], count[j], e);
+                        }
+                        *reinterpret_cast<u32x4 *>(dst + j * kSubBytes) = u32x4{e[0], e[1], e[2], e[3]};
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if (fast) {
+            // Widen in place: every lane's 4-byte words are read (one LDS
+            // instruction each, executed for the whole wavefront) before any
+            // lane writes its 16-byte entry over them.
+#pragma unroll
+            for (int k = 0; k < kMaxIn; ++k) {
+                if (k < n_in && (A.in_rowconst[k] || is16(P.in_ty[k]))) {
+                    uint8_t *ent = file + k * K * kSubBytes;
+#pragma unroll
+                    for (int j = 0; j < K; ++j) {
+                        uint8_t *e = ent + j * kSubBytes;
+                        const uint32_t lo = *reinterpret_cast<const uint32_t *>(e + lane * 4);
+                        u32x4 v;
+                        if (A.in_rowconst[k]) {
+                            v = u32x4{lo, lo, lo, lo};
+                        } else {
+                            const uint32_t hi = *reinterpret_cast<const uint32_t *>(e + 256 + lane * 4);
+                            v = widen16(u32x2{lo, hi});
+                        }
+                        *reinterpret_cast<u32x4 *>(e + lane_off) = v;
+                    }
+                }
+            }
+        }
+        // 2. the tape
+        interp_tape<K>(P, T, file, lane_off);
+        // 3. outputs
+#pragma unroll
+        for (int k = 0; k < kMaxOut; ++k) {
+            if (k < P.n_out) {
+                const uint8_t ty = P.out_ty[k];
+                const uint32_t wo = T.out[k], os = wo >> 16;
+                const uint8_t *po = file + (wo & 0xffffu) + lane_off;
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    const u32x4 o = *reinterpret_cast<const u32x4 *>(po + j * os);
+                    const int64_t off = row_of(A.out_s[k], j) + col[j];
+                    if (count[j] == 4) {
+                        store_vec<NTS>(A.out[k], ty, off, o);
+                    } else if (count[j] > 0) {
+                        const uint32_t e[4] = {o.x, o.y, o.z, o.w};
+                        store_elems<4, false, false>(A.out[k], ty, off, count[j], e);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int K, bool NTL, bool NTS>
+__global__ __launch_bounds__(64) void k_rows_interp(const StridedArgs A, const InterpTape T)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t file[];
+    interp_uniforms(A.prog, A.uni, T, file, threadIdx.x * 16);
+    if (A.wave_in_row) rows_interp_body<K, NTL, NTS, true>(A, T, file);
+    else rows_interp_body<K, NTL, NTS, false>(A, T, file);
+}
+
+template <int K, bool NTL, bool NTS>
+static int launch_one(bool rows, const void *args, const InterpTape &T, LaunchGeometry g, int lds, void *stream)
+{
+    if (rows)
+        hipLaunchKernelGGL((k_rows_interp<K, NTL, NTS>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
+                           (hipStream_t)stream, *static_cast<const StridedArgs *>(args), T);
+    else
+        hipLaunchKernelGGL((k_linear_interp<K, NTL, NTS>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
+                           (hipStream_t)stream, *static_cast<const LinearArgs *>(args), T);
     return (int)hipGetLastError();
 }
 
 template <int K>
-static int launch_k(bool ntl, bool nts, const LinearArgs &A, const InterpTape &T, LaunchGeometry g, int lds,
+static int launch_k(bool rows, bool ntl, bool nts, const void *args, const InterpTape &T, LaunchGeometry g, int lds,
                     void *stream)
 {
-    if (ntl) return nts ? launch_one<K, true, true>(A, T, g, lds, stream)
-                        : launch_one<K, true, false>(A, T, g, lds, stream);
-    return nts ? launch_one<K, false, true>(A, T, g, lds, stream) : launch_one<K, false, false>(A, T, g, lds, stream);
+    if (ntl) return nts ? launch_one<K, true, true>(rows, args, T, g, lds, stream)
+                        : launch_one<K, true, false>(rows, args, T, g, lds, stream);
+    return nts ? launch_one<K, false, true>(rows, args, T, g, lds, stream)
+               : launch_one<K, false, false>(rows, args, T, g, lds, stream);
+}
+
+static int launch_interp(bool rows, int k_sub, bool nt_load, bool nt_store, const void *args, const InterpTape &T,
+                         LaunchGeometry g, int lds_bytes, void *stream)
+{
+    switch (k_sub) {
+    case 4: return launch_k<4>(rows, nt_load, nt_store, args, T, g, lds_bytes, stream);
+    case 2: return launch_k<2>(rows, nt_load, nt_store, args, T, g, lds_bytes, stream);
+    default: return launch_k<1>(rows, nt_load, nt_store, args, T, g, lds_bytes, stream);
+    }
 }
 
 int launch_linear_interp(int k_sub, bool nt_load, bool nt_store, const LinearArgs &A, const InterpTape &T,
                          LaunchGeometry g, int lds_bytes, void *stream)
 {
-    switch (k_sub) {
-    case 4: return launch_k<4>(nt_load, nt_store, A, T, g, lds_bytes, stream);
-    case 2: return launch_k<2>(nt_load, nt_store, A, T, g, lds_bytes, stream);
-    default: return launch_k<1>(nt_load, nt_store, A, T, g, lds_bytes, stream);
-    }
+    return launch_interp(false, k_sub, nt_load, nt_store, &A, T, g, lds_bytes, stream);
+}
+
+int launch_rows_interp(int k_sub, bool nt_load, bool nt_store, const StridedArgs &A, const InterpTape &T,
+                       LaunchGeometry g, int lds_bytes, void *stream)
+{
+    return launch_interp(true, k_sub, nt_load, nt_store, &A, T, g, lds_bytes, stream);
 }
 
 }  // namespace ecmd
