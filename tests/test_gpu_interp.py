@@ -112,3 +112,52 @@ def test_pass_through_and_mixed_width_outputs(n):
     rng = np.random.default_rng(n)
     vals = [(rng.standard_normal(n) * 300).astype(np.float16), np.float32(-0.375)]
     _run_interp(spec, vals, n, "pass-through n=%d" % n)
+
+
+# ---------------------------------------------------------------------------
+# The rows path's interpreter (k_rows_interp): padded rows, row-constant and
+# column-broadcast inputs, 16-bit inputs and outputs, rows that hold whole
+# wavefronts (n3 a multiple of 256), rows that do not, and partial vectors.
+
+@pytest.mark.parametrize("dx", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("db", ["f32", "f16"])
+@pytest.mark.parametrize("n3", [256, 1024, 100, 253, 7])
+def test_rows_interp_views(dx, db, n3):
+    import torch
+    from gpu_util import NPD
+    rows = 37
+    ld = (n3 + 12 + 3) // 4 * 4          # padded rows whose starts keep 4-element vectors aligned
+    spec = [("x", ("load", dx, 2)), ("b", ("load", db, 2)), ("c", ("load", "f32", 2)),
+            ("xf", ("cvt", "x", "f32")), ("bf", ("cvt", "b", "f32")), ("t", ("mul", "xf", "bf")),
+            ("u", ("add", "t", "c")), ("u16", ("cvt", "u", dx)),
+            ("o0", ("store", "u", 2)), ("o1", ("store", "u16", 2))]
+    rng = np.random.default_rng(n3 * 10 + len(dx) + len(db))
+
+    def draw(dt, shape):
+        f = (rng.standard_normal(shape) * 50).astype(np.float32)
+        if dt == "bf16":
+            return (f.view(np.uint32) >> 16).astype(np.uint16)
+        return f.astype(NPD[dt])
+
+    xs = draw(dx, (rows, ld))
+    bv = draw(db, (rows, 1))
+    cv = draw("f32", (1, n3))
+    x_log = np.ascontiguousarray(xs[:, :n3])
+    ref = run_oracle(spec, [x_log, np.ascontiguousarray(np.broadcast_to(bv, (rows, n3))),
+                            np.ascontiguousarray(np.broadcast_to(cv, (rows, n3)))])
+    xg = to_dev(xs)[:, :n3]
+    bg = to_dev(bv).expand(rows, n3)
+    cg = to_dev(cv).expand(rows, n3)
+    from gpu_util import TD
+    o0s = torch.full((rows, ld), float("nan"), dtype=torch.float32, device=dev())
+    o1s = torch.zeros((rows, ld), dtype=TD[dx], device=dev())
+    o0, o1 = o0s[:, :n3], o1s[:, :n3]
+    import elementwise_tensor_commands_amd as ecmd
+    cmd = ecmd.from_spec(spec)
+    plan = cmd.plan(xg, bg, cg, o0, o1)
+    assert plan["path"] == "rows" and plan["kernel"] == "rows_generic" and plan["block"] == 64, plan
+    cmd.launch(xg, bg, cg, o0, o1)
+    torch.cuda.synchronize()
+    compare(host(o0), ref[0], 0, "rows interp %s/%s n3=%d out0" % (dx, db, n3))
+    compare(host(o1), ref[1], 0, "rows interp %s/%s n3=%d out1" % (dx, db, n3))
+    assert torch.isnan(o0s[:, n3:]).all() and (host(o1s[:, n3:]).view(np.uint16) == 0).all()   # padding untouched
