@@ -388,8 +388,8 @@ def main():
                 r = head
             else:
                 log("measuring %s" % wl)
-                base, jit = split_workload(wl)
-                r = measure(base, min(a.steps, 100), a.warmup, jit=jit)
+                wl_base, wl_jit = split_workload(wl)
+                r = measure(wl_base, min(a.steps, 100), a.warmup, jit=wl_jit)
             line["commands"][wl] = {
                 "kernel": r["kernel"], "gbps": round(r["kernel_gbps"], 1),
                 "pct_of_peak": round(100 * r["kernel_gbps"] / PEAK_GBPS, 2),
