@@ -761,14 +761,33 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         for (int k = 0; k < P.n_in; ++k) any_rowconst = any_rowconst || rowconst[k];
         S.variant = (!force_generic && !any_rowconst && std::memcmp(&P, &kProgAddScaledF32, sizeof(Program)) == 0 &&
                      mask == 0x2) ? 0 : -1;
-        S.tile = S.variant == 0 ? tile_shape() : TileShape{64, 64, 256};   // the interpreter has one shape
+        S.tile = S.variant == 0 ? tile_shape() : TileShape{64, 64, 256};   // RtEval has one shape
+        S.lds = n_staged * S.tile.tn * S.tile.tm * 4;
+        if (S.variant < 0) {
+            // The LDS-file interpreter on its own tile shape, when its staging
+            // tiles and register files fit 64 KiB (two or more work-groups per
+            // CU) and its grid one dispatch; RtEval's 64 x 64 tiles otherwise.
+            constexpr int kSub = kTiledInterpM * kTiledInterpN / 4 / kTiledInterpBlock;
+            int n_slot = 0;
+            for (int i = 0; i < P.n_ops; ++i) n_slot = std::max(n_slot, P.ops[i].dst - (int)kRefSlot + 1);
+            const int per_wave = ((P.n_in + n_slot) * kSub + P.n_uni) * 1024;
+            const int lds = n_staged * kTiledInterpM * kTiledInterpN * 4 + kTiledInterpBlock / 64 * per_wave;
+            const int64_t tiles = ((T.n[2] + kTiledInterpM - 1) / kTiledInterpM) *
+                                  ((T.n[3] + kTiledInterpN - 1) / kTiledInterpN) * T.n[0] * T.n[1];
+            if (lds <= 65536 && tiles * kTiledInterpBlock < kMaxGridItems && !env_flag("ECMD_TILED_RTEVAL")) {
+                S.interp = true;
+                S.k_sub = kSub;
+                S.n_slot = n_slot;
+                S.tile = TileShape{kTiledInterpM, kTiledInterpN, kTiledInterpBlock};
+                S.lds = lds;
+            }
+        }
         S.walk = (int)env_int("ECMD_TILE_WALK", kDefaultTileWalk);
         S.e = 4;
         S.block = S.tile.block;
         S.tiles_r = (T.n[2] + S.tile.tm - 1) / S.tile.tm;
         S.tiles_c = (T.n[3] + S.tile.tn - 1) / S.tile.tn;
         S.grid = S.tiles_r * S.tiles_c * T.n[0] * T.n[1];
-        S.lds = n_staged * S.tile.tn * S.tile.tm * 4;
         S.name = S.variant == 0 ? "tiled_add_scaled_f32" : "tiled_generic";
         return;
     }
@@ -1119,7 +1138,9 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         } else {
             InterpTape T;
             if (S.interp) resolve_interp_tape(h->prog, S.k_sub, S.n_slot, T);
-            herr = S.path == CMD_PATH_TILED ? launch_tiled(S.variant, nt, S.tile, A, g, hip_stream)
+            herr = S.path == CMD_PATH_TILED
+                       ? (S.interp ? launch_tiled_interp(nt, A, T, g, S.lds, hip_stream)
+                                   : launch_tiled(S.variant, nt, S.tile, A, g, hip_stream))
                    : S.path == CMD_PATH_ROWS
                        ? (S.interp ? launch_rows_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds,
                                                         hip_stream)

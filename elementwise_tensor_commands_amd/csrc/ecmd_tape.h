@@ -338,6 +338,13 @@ int launch_linear_interp(int k_sub, bool nt_load, bool nt_store, const LinearArg
 // elements per super-chunk).
 int launch_rows_interp(int k_sub, bool nt_load, bool nt_store, const StridedArgs &A, const InterpTape &T,
                        LaunchGeometry g, int lds_bytes, void *stream);
+// And over the tiled path's tiles: kTiledInterpM x kTiledInterpN tiles,
+// kTiledInterpBlock work-items, so K = M N / (4 block) sub-chunks per
+// wavefront (its register file); lds_bytes covers the staging tiles and the
+// register files of all wavefronts.
+constexpr int kTiledInterpM = 32, kTiledInterpN = 64, kTiledInterpBlock = 256;
+int launch_tiled_interp(bool nt, const StridedArgs &A, const InterpTape &T, LaunchGeometry g, int lds_bytes,
+                        void *stream);
 // Tiled path: output tile of tm x tn elements (tm and tn multiples of 32).
 struct TileShape {
     int tm, tn;

@@ -337,6 +337,202 @@ __global__ __launch_bounds__(64) void k_rows_interp(const StridedArgs A, const I
     else rows_interp_body<K, NTL, NTS, false>(A, T, file);
 }
 
+// The tiled path's interpreter: the tiled kernel's work split and staging
+// (kernels_tiled.hip: column-contiguous "staged" inputs read through a
+// swizzled LDS tile) with the LDS register file and tape walk above.  A
+// work-group owns a TM x TN output tile; chunk p of work-item t is chunk
+// t + TB p of the tile (tile_split), so each wavefront's K = TM TN / (4 TB)
+// chunks are the K sub-chunks of its register file.
+//   1. Full tiles: direct inputs go straight from HBM into their file entries
+//      (binary32: 16 bytes per lane; 16-bit: two 4-byte halves, widened in
+//      step 3).  Staged inputs are read as column runs into the staging tile,
+//      as in the tiled kernel.  Row-constant inputs, and the direct inputs of
+//      edge tiles, are loaded element by element through registers.
+//   2. One wait and one barrier (the staging tile is shared by the
+//      work-group).
+//   3. Staged inputs are copied from the staging tile into their entries
+//      (4 LDS reads per chunk), 16-bit direct inputs widened in place.
+//   4. The tape is walked, and each output is stored from its entry.
+// LDS: the staging tiles (n_staged TM TN words), then one register file per
+// wavefront.
+template <int TM, int TN, int TB, bool NT>
+__global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const InterpTape T)
+{
+    constexpr int K = TM * TN / 4 / TB;
+    static_assert(K >= 1 && TM % 32 == 0 && TN % 32 == 0 && TB % 64 == 0, "tile shape");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const Program &P = A.prog;
+    const int n_in = P.n_in;
+    const int t = threadIdx.x, lane = t & 63;
+    const int lane_off = lane * 16;
+    int n_staged = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) n_staged += (k < n_in && A.in_staged[k]) ? 1 : 0;
+    uint32_t *stage = reinterpret_cast<uint32_t *>(lds);
+    uint8_t *file = lds + n_staged * TM * TN * 4 + (t >> 6) * (T.uni_off + P.n_uni * kSubBytes);
+    interp_uniforms(P, A.uni, T, file, lane_off);
+
+    // Plane and tile coordinates, row by row (as the tiled kernel without a walk).
+    const uint32_t tiles_c = (uint32_t)A.tiles_c, tiles_r = (uint32_t)A.tiles_r;
+    const uint32_t per_plane = tiles_r * tiles_c;
+    const uint32_t plane = blockIdx.x / per_plane;
+    const uint32_t id = blockIdx.x - plane * per_plane;
+    const uint32_t n1 = (uint32_t)A.n[1];
+    const uint32_t b0 = plane / n1, b1 = plane - b0 * n1;
+    const uint32_t tr = id / tiles_c, tc = id - tr * tiles_c;
+    const int64_t rows = A.n[2], cols = A.n[3];
+    const int64_t r0 = (int64_t)tr * TM, c0 = (int64_t)tc * TN;
+    const bool full = (r0 + TM <= rows) && (c0 + TN <= cols);
+    auto in_base = [&](int k) { return (int64_t)b0 * A.in_s[k][0] + (int64_t)b1 * A.in_s[k][1]; };
+    auto out_base = [&](int k) { return (int64_t)b0 * A.out_s[k][0] + (int64_t)b1 * A.out_s[k][1]; };
+    int rl[K], cl[K], count[K];
+#pragma unroll
+    for (int p = 0; p < K; ++p) {
+        tile_split(t + TB * p, TN, rl[p], cl[p]);
+        const int64_t left = cols - (c0 + cl[p]);
+        count[p] = full ? 4 : (r0 + rl[p] < rows ? (left <= 0 ? 0 : (left >= 4 ? 4 : (int)left)) : 0);
+    }
+
+    // 1a. Full tiles: direct inputs straight into their entries.
+    if (full) {
+#pragma unroll
+        for (int k = 0; k < kMaxIn; ++k) {
+            if (k < n_in && !A.in_staged[k] && !A.in_rowconst[k]) {
+                uint8_t *dst = file + k * K * kSubBytes;
+#pragma unroll
+                for (int p = 0; p < K; ++p) {
+                    const int64_t off = in_base(k) + (r0 + rl[p]) * A.in_s[k][2] + c0 + cl[p];
+                    if (!is16(P.in_ty[k])) {
+                        __builtin_amdgcn_global_load_lds((global_addr_t)(static_cast<const uint32_t *>(A.in[k]) + off),
+                                                         (lds_addr_t)(dst + p * kSubBytes), 16, 0, NT ? 2 : 0);
+                    } else {
+                        const uint16_t *src = static_cast<const uint16_t *>(A.in[k]) + off;
+                        __builtin_amdgcn_global_load_lds((global_addr_t)src, (lds_addr_t)(dst + p * kSubBytes), 4,
+                                                         0, NT ? 2 : 0);
+                        __builtin_amdgcn_global_load_lds((global_addr_t)(src + 2),
+                                                         (lds_addr_t)(dst + p * kSubBytes + 256), 4, 0, NT ? 2 : 0);
+                    }
+                }
+            }
+        }
+    }
+    // 1b. Staged inputs into the staging tile: element (c, r) of staged input
+    // s at word s TM TN + tile_word(TM, c, r).
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) {
+        if (k < n_in && A.in_staged[k]) {
+            const uint8_t ty = P.in_ty[k];
+            uint32_t *dst = stage + (A.in_staged[k] - 1) * TM * TN;
+#pragma unroll
+            for (int p = 0; p < K; ++p) {
+                int sc, sr;
+                tile_split(t + TB * p, TM, sc, sr);
+                const int64_t off = in_base(k) + (c0 + sc) * A.in_s[k][3] + (r0 + sr);
+                uint32_t sv[4] = {0u, 0u, 0u, 0u};
+                if (full) {
+                    load_group<4, true, NT>(A.in[k], ty, off, 4, sv);
+                } else {
+                    const int64_t left = rows - (r0 + sr);
+                    const int cnt = c0 + sc < cols ? (left <= 0 ? 0 : (left >= 4 ? 4 : (int)left)) : 0;
+                    if (cnt > 0) load_elems<4, false>(A.in[k], ty, off, cnt, sv);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[tile_word(TM, sc, sr + e)] = sv[e];
+            }
+        }
+    }
+    // 1c. Row-constant inputs, and every direct input of an edge tile.
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) {
+        if (k < n_in && !A.in_staged[k] && (A.in_rowconst[k] || !full)) {
+            const uint8_t ty = P.in_ty[k];
+            uint8_t *dst = file + k * K * kSubBytes + lane_off;
+#pragma unroll
+            for (int p = 0; p < K; ++p) {
+                const int64_t row = in_base(k) + (r0 + rl[p]) * A.in_s[k][2];
+                uint32_t e[4] = {0u, 0u, 0u, 0u};
+                if (A.in_rowconst[k]) {
+                    uint32_t one[1] = {0u};
+                    if (count[p] > 0) load_elems<1, false>(A.in[k], ty, row, 1, one);
+                    e[0] = e[1] = e[2] = e[3] = one[0];
+                } else if (count[p] > 0) {
+                    load_elems<4, false>(A.in[k], ty, row + c0 + cl[p], count[p], e);
+                }
+                *reinterpret_cast<u32x4 *>(dst + p * kSubBytes) = u32x4{e[0], e[1], e[2], e[3]};
+            }
+        }
+    }
+    // 2. The loads to LDS have landed and every wavefront has staged its part.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    // 3. Staged inputs into their entries; 16-bit direct inputs widened.
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) {
+        if (k >= n_in) continue;
+        uint8_t *ent = file + k * K * kSubBytes;
+        if (A.in_staged[k]) {
+            const uint32_t *src = stage + (A.in_staged[k] - 1) * TM * TN;
+#pragma unroll
+            for (int p = 0; p < K; ++p) {
+                u32x4 v;
+                v.x = src[tile_word(TM, cl[p] + 0, rl[p])];
+                v.y = src[tile_word(TM, cl[p] + 1, rl[p])];
+                v.z = src[tile_word(TM, cl[p] + 2, rl[p])];
+                v.w = src[tile_word(TM, cl[p] + 3, rl[p])];
+                *reinterpret_cast<u32x4 *>(ent + p * kSubBytes + lane_off) = v;
+            }
+        } else if (full && !A.in_rowconst[k] && is16(P.in_ty[k])) {
+#pragma unroll
+            for (int p = 0; p < K; ++p) {
+                uint8_t *e = ent + p * kSubBytes;
+                const uint32_t lo = *reinterpret_cast<const uint32_t *>(e + lane * 4);
+                const uint32_t hi = *reinterpret_cast<const uint32_t *>(e + 256 + lane * 4);
+                *reinterpret_cast<u32x4 *>(e + lane_off) = widen16(u32x2{lo, hi});
+            }
+        }
+    }
+    // 4. The tape, and the outputs.
+    interp_tape<K>(P, T, file, lane_off);
+#pragma unroll
+    for (int k = 0; k < kMaxOut; ++k) {
+        if (k < P.n_out) {
+            const uint8_t ty = P.out_ty[k];
+            const uint32_t wo = T.out[k], os = wo >> 16;
+            const uint8_t *po = file + (wo & 0xffffu) + lane_off;
+#pragma unroll
+            for (int p = 0; p < K; ++p) {
+                const u32x4 o = *reinterpret_cast<const u32x4 *>(po + p * os);
+                const int64_t off = out_base(k) + (r0 + rl[p]) * A.out_s[k][2] + c0 + cl[p];
+                if (count[p] == 4) {
+                    store_vec<NT>(A.out[k], ty, off, o);
+                } else if (count[p] > 0) {
+                    const uint32_t e[4] = {o.x, o.y, o.z, o.w};
+                    store_elems<4, false, false>(A.out[k], ty, off, count[p], e);
+                }
+            }
+        }
+    }
+}
+
+int launch_tiled_interp(bool nt, const StridedArgs &A, const InterpTape &T, LaunchGeometry g, int lds_bytes,
+                        void *stream)
+{
+    auto go = [&](auto kern) {
+        static int lds_allowed = 65536;
+        if (lds_bytes > lds_allowed) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+            if (e != hipSuccess) return (int)e;
+            lds_allowed = lds_bytes;
+        }
+        hipLaunchKernelGGL(kern, dim3((unsigned)g.grid), dim3(kTiledInterpBlock), (unsigned)lds_bytes,
+                           (hipStream_t)stream, A, T);
+        return (int)hipGetLastError();
+    };
+    return nt ? go(k_tiled_interp<kTiledInterpM, kTiledInterpN, kTiledInterpBlock, true>)
+              : go(k_tiled_interp<kTiledInterpM, kTiledInterpN, kTiledInterpBlock, false>);
+}
+
 template <int K, bool NTL, bool NTS>
 static int launch_one(bool rows, const void *args, const InterpTape &T, LaunchGeometry g, int lds, void *stream)
 {

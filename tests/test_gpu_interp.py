@@ -161,3 +161,52 @@ def test_rows_interp_views(dx, db, n3):
     compare(host(o0), ref[0], 0, "rows interp %s/%s n3=%d out0" % (dx, db, n3))
     compare(host(o1), ref[1], 0, "rows interp %s/%s n3=%d out1" % (dx, db, n3))
     assert torch.isnan(o0s[:, n3:]).all() and (host(o1s[:, n3:]).view(np.uint16) == 0).all()   # padding untouched
+
+
+# ---------------------------------------------------------------------------
+# The tiled path's interpreter (k_tiled_interp, 32 x 64 tiles) and, for
+# comparison, the tiled kernel with RtEval (ECMD_TILED_RTEVAL=1).
+
+@pytest.mark.parametrize("rteval", [False, True])
+@pytest.mark.parametrize("shape", [(64, 128), (32, 64), (100, 68), (36, 132), (8, 300)])
+def test_tiled_interp_mixed_inputs(monkeypatch, rteval, shape):
+    """A binary16 direct input, a binary32 input read transposed (staged), a
+    per-row constant and a scalar; binary32 and bfloat16 outputs."""
+    import torch
+    from gpu_util import NPD
+    import elementwise_tensor_commands_amd as ecmd
+    if rteval:
+        monkeypatch.setenv("ECMD_TILED_RTEVAL", "1")
+    R, C = shape
+    spec = [("x", ("load", "f16", 2)), ("y", ("load", "f32", 2)), ("b", ("load", "f32", 2)),
+            ("s", ("scalar", "f32")),
+            ("xf", ("cvt", "x", "f32")), ("p", ("mul", "xf", "y")), ("q", ("add", "p", "b")),
+            ("r", ("sub", "q", "s")), ("rb", ("cvt", "r", "bf16")),
+            ("o0", ("store", "r", 2)), ("o1", ("store", "rb", 2))]
+    rng = np.random.default_rng(R * 1000 + C)
+    x = (rng.standard_normal((R, C)) * 30).astype(np.float16)
+    yt = rng.standard_normal((C, R)).astype(np.float32)          # y = yt.T: read transposed
+    b = rng.standard_normal((R, 1)).astype(np.float32)
+    s = np.float32(0.625)
+    ref = run_oracle(spec, [x, np.ascontiguousarray(yt.T), np.ascontiguousarray(np.broadcast_to(b, (R, C))), s])
+    gv = [to_dev(x), to_dev(yt).t(), to_dev(b).expand(R, C), float(s)]
+    o0 = torch.full((R, C), float("nan"), device=dev())
+    o1 = torch.zeros((R, C), dtype=torch.bfloat16, device=dev())
+    cmd = ecmd.from_spec(spec)
+    plan = cmd.plan(*gv, o0, o1)
+    assert plan["path"] == "tiled" and plan["kernel"] == "tiled_generic", plan
+    assert (plan["lds_bytes"] == 64 * 64 * 4) == rteval, plan      # RtEval: one 64 x 64 staging tile
+    cmd.launch(*gv, o0, o1)
+    torch.cuda.synchronize()
+    compare(host(o0), ref[0], 0, "tiled interp %s rteval=%s out0" % (shape, rteval))
+    compare(host(o1), ref[1], 0, "tiled interp %s rteval=%s out1" % (shape, rteval))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_tiled_interp_random_transposed_views(seed):
+    """Random Commands over random transposed rank-2..4 views: most take the
+    tiled path with the interpreter."""
+    from random_commands import random_view_case
+    from test_gpu_views import run_views
+    spec, ins, outs = random_view_case(seed + 500, staged=True)
+    run_views(spec, ins, outs, False, "tiled interp seed %d" % seed)

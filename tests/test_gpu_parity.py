@@ -338,9 +338,13 @@ def test_transposed_self_is_three_x_on_gpu():
     compare(host(out), np.float32(3) * X, 0, "X + 2 X")
 
 
-def test_tiled_generic_f16_two_staged():
+@pytest.mark.parametrize("rteval", [False, True])
+def test_tiled_generic_f16_two_staged(monkeypatch, rteval):
     """Rank 2: a binary16 and an int32 input read transposed (staged through
-    LDS), a row-strided binary32 input, two outputs: the generic tiled kernel."""
+    LDS), a row-strided binary32 input, two outputs: the tiled path's
+    interpreter, and the tiled kernel with RtEval (ECMD_TILED_RTEVAL=1)."""
+    if rteval:
+        monkeypatch.setenv("ECMD_TILED_RTEVAL", "1")
     spec = [("A", ("load", "f16", 2)), ("B", ("load", "f32", 2)), ("C", ("load", "i32", 2)),
             ("s", ("scalar", "f32")),
             ("af", ("cvt", "A", "f32")), ("p", ("mul", "af", "B")), ("q", ("sub", "p", "s")),
@@ -356,7 +360,8 @@ def test_tiled_generic_f16_two_staged():
     gv = [to_dev(A).t(), to_dev(Bs)[:, :C], to_dev(Cs)[:, :R].t(), 0.75]
     cmd, got = run_gpu(spec, gv, [((R, C), "f16"), ((R, C), "i32")])
     plan = cmd.plan(*gv, *got)
-    assert plan["path"] == "tiled" and not plan["specialised"] and plan["lds_bytes"] == 2 * 64 * 64 * 4, plan
+    assert plan["path"] == "tiled" and not plan["specialised"], plan
+    assert (plan["lds_bytes"] == 2 * 64 * 64 * 4) == rteval, plan      # RtEval: two 64 x 64 staging tiles
     compare(host(got[0]), ref[0], 0, "tiled f16 out")
     compare(host(got[1]), ref[1], 0, "tiled i32 copy")
 
