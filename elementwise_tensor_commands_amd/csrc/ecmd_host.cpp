@@ -767,18 +767,29 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
             // The LDS-file interpreter on its own tile shape, when its staging
             // tiles and register files fit 64 KiB (two or more work-groups per
             // CU) and its grid one dispatch; RtEval's 64 x 64 tiles otherwise.
-            constexpr int kSub = kTiledInterpM * kTiledInterpN / 4 / kTiledInterpBlock;
+            // ECMD_TILED_INTERP = "MxNxB" picks another instantiated shape
+            // (then up to 160 KiB of LDS), for A/B runs.
+            TileShape it{kTiledInterpM, kTiledInterpN, kTiledInterpBlock};
+            int lds_cap = 65536;
+            if (const char *v = std::getenv("ECMD_TILED_INTERP")) {
+                int a = 0, b = 0, c = 0;
+                if (std::sscanf(v, "%dx%dx%d", &a, &b, &c) == 3) {
+                    const int key = (a * 1000 + b) * 1000 + c;
+                    if (key == 32064128 || key == 64064256 || key == 32128256 || key == 64064512)
+                        it = TileShape{a, b, c}, lds_cap = 160 * 1024;
+                }
+            }
+            const int k_sub = it.tm * it.tn / 4 / it.block;
             int n_slot = 0;
             for (int i = 0; i < P.n_ops; ++i) n_slot = std::max(n_slot, P.ops[i].dst - (int)kRefSlot + 1);
-            const int per_wave = ((P.n_in + n_slot) * kSub + P.n_uni) * 1024;
-            const int lds = n_staged * kTiledInterpM * kTiledInterpN * 4 + kTiledInterpBlock / 64 * per_wave;
-            const int64_t tiles = ((T.n[2] + kTiledInterpM - 1) / kTiledInterpM) *
-                                  ((T.n[3] + kTiledInterpN - 1) / kTiledInterpN) * T.n[0] * T.n[1];
-            if (lds <= 65536 && tiles * kTiledInterpBlock < kMaxGridItems && !env_flag("ECMD_TILED_RTEVAL")) {
+            const int per_wave = ((P.n_in + n_slot) * k_sub + P.n_uni) * 1024;
+            const int lds = n_staged * it.tm * it.tn * 4 + it.block / 64 * per_wave;
+            const int64_t tiles = ((T.n[2] + it.tm - 1) / it.tm) * ((T.n[3] + it.tn - 1) / it.tn) * T.n[0] * T.n[1];
+            if (lds <= lds_cap && tiles * it.block < kMaxGridItems && !env_flag("ECMD_TILED_RTEVAL")) {
                 S.interp = true;
-                S.k_sub = kSub;
+                S.k_sub = k_sub;
                 S.n_slot = n_slot;
-                S.tile = TileShape{kTiledInterpM, kTiledInterpN, kTiledInterpBlock};
+                S.tile = it;
                 S.lds = lds;
             }
         }
@@ -1139,7 +1150,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
             InterpTape T;
             if (S.interp) resolve_interp_tape(h->prog, S.k_sub, S.n_slot, T);
             herr = S.path == CMD_PATH_TILED
-                       ? (S.interp ? launch_tiled_interp(nt, A, T, g, S.lds, hip_stream)
+                       ? (S.interp ? launch_tiled_interp(S.tile, nt, A, T, g, S.lds, hip_stream)
                                    : launch_tiled(S.variant, nt, S.tile, A, g, hip_stream))
                    : S.path == CMD_PATH_ROWS
                        ? (S.interp ? launch_rows_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds,

@@ -338,13 +338,7 @@ int launch_linear_interp(int k_sub, bool nt_load, bool nt_store, const LinearArg
 // elements per super-chunk).
 int launch_rows_interp(int k_sub, bool nt_load, bool nt_store, const StridedArgs &A, const InterpTape &T,
                        LaunchGeometry g, int lds_bytes, void *stream);
-// And over the tiled path's tiles: kTiledInterpM x kTiledInterpN tiles,
-// kTiledInterpBlock work-items, so K = M N / (4 block) sub-chunks per
-// wavefront (its register file); lds_bytes covers the staging tiles and the
-// register files of all wavefronts.
-constexpr int kTiledInterpM = 32, kTiledInterpN = 64, kTiledInterpBlock = 256;
-int launch_tiled_interp(bool nt, const StridedArgs &A, const InterpTape &T, LaunchGeometry g, int lds_bytes,
-                        void *stream);
+
 // Tiled path: output tile of tm x tn elements (tm and tn multiples of 32).
 struct TileShape {
     int tm, tn;
@@ -379,6 +373,15 @@ constexpr void tile_split(int v, int minor_len, int &major, int &minor)
 // (q ^ e), again all distinct.  No padding is needed: tm * tn words.
 constexpr int tile_word(int tm, int c, int r) { return c * tm + (r ^ (c & 31)); }
 int launch_tiled(int variant, bool nt, TileShape shape, const StridedArgs &A, LaunchGeometry g, void *stream);
+// The LDS-file interpreter (see launch_linear_interp) over the tiled path's
+// tiles: by default kTiledInterpM x kTiledInterpN tiles and kTiledInterpBlock
+// work-items (32 x 64 x 128, 64 x 64 x 256, 32 x 128 x 256 and 64 x 64 x 512
+// are instantiated for A/B runs), so K = M N / (4 block) sub-chunks per
+// wavefront (its register file); lds_bytes covers the staging tiles and the
+// register files of all wavefronts.
+constexpr int kTiledInterpM = 32, kTiledInterpN = 64, kTiledInterpBlock = 256;
+int launch_tiled_interp(TileShape shape, bool nt, const StridedArgs &A, const InterpTape &T, LaunchGeometry g,
+                        int lds_bytes, void *stream);
 int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
 // Rows path: the linear path's specialised Programs (variant indexes the same
 // list); nontemporal loads / stores as the host chooses.

@@ -514,23 +514,38 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
     }
 }
 
-int launch_tiled_interp(bool nt, const StridedArgs &A, const InterpTape &T, LaunchGeometry g, int lds_bytes,
-                        void *stream)
+template <int TM, int TN, int TB, bool NT>
+static int launch_tiled_one(const StridedArgs &A, const InterpTape &T, LaunchGeometry g, int lds_bytes, void *stream)
 {
-    auto go = [&](auto kern) {
-        static int lds_allowed = 65536;
-        if (lds_bytes > lds_allowed) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-            if (e != hipSuccess) return (int)e;
-            lds_allowed = lds_bytes;
-        }
-        hipLaunchKernelGGL(kern, dim3((unsigned)g.grid), dim3(kTiledInterpBlock), (unsigned)lds_bytes,
-                           (hipStream_t)stream, A, T);
-        return (int)hipGetLastError();
-    };
-    return nt ? go(k_tiled_interp<kTiledInterpM, kTiledInterpN, kTiledInterpBlock, true>)
-              : go(k_tiled_interp<kTiledInterpM, kTiledInterpN, kTiledInterpBlock, false>);
+    auto kern = k_tiled_interp<TM, TN, TB, NT>;
+    static int lds_allowed = 65536;   // above 64 KiB a kernel must be allowed more, once
+    if (lds_bytes > lds_allowed) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        if (e != hipSuccess) return (int)e;
+        lds_allowed = lds_bytes;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)g.grid), dim3(TB), (unsigned)lds_bytes, (hipStream_t)stream, A, T);
+    return (int)hipGetLastError();
+}
+
+template <int TM, int TN, int TB>
+static int launch_tiled_nt(bool nt, const StridedArgs &A, const InterpTape &T, LaunchGeometry g, int lds, void *stream)
+{
+    return nt ? launch_tiled_one<TM, TN, TB, true>(A, T, g, lds, stream)
+              : launch_tiled_one<TM, TN, TB, false>(A, T, g, lds, stream);
+}
+
+int launch_tiled_interp(TileShape shape, bool nt, const StridedArgs &A, const InterpTape &T, LaunchGeometry g,
+                        int lds_bytes, void *stream)
+{
+    switch ((shape.tm * 1000 + shape.tn) * 1000 + shape.block) {
+    case 32064128: return launch_tiled_nt<32, 64, 128>(nt, A, T, g, lds_bytes, stream);
+    case 64064256: return launch_tiled_nt<64, 64, 256>(nt, A, T, g, lds_bytes, stream);
+    case 32128256: return launch_tiled_nt<32, 128, 256>(nt, A, T, g, lds_bytes, stream);
+    case 64064512: return launch_tiled_nt<64, 64, 512>(nt, A, T, g, lds_bytes, stream);
+    default: return launch_tiled_nt<kTiledInterpM, kTiledInterpN, kTiledInterpBlock>(nt, A, T, g, lds_bytes, stream);
+    }
 }
 
 template <int K, bool NTL, bool NTS>

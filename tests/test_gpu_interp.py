@@ -167,16 +167,23 @@ def test_rows_interp_views(dx, db, n3):
 # The tiled path's interpreter (k_tiled_interp, 32 x 64 tiles) and, for
 # comparison, the tiled kernel with RtEval (ECMD_TILED_RTEVAL=1).
 
-@pytest.mark.parametrize("rteval", [False, True])
+TILED_INTERP_SHAPES = ["32x64x256", "32x64x128", "64x64x256", "32x128x256", "64x64x512"]
+
+
+@pytest.mark.parametrize("kernel", ["rteval"] + TILED_INTERP_SHAPES)
 @pytest.mark.parametrize("shape", [(64, 128), (32, 64), (100, 68), (36, 132), (8, 300)])
-def test_tiled_interp_mixed_inputs(monkeypatch, rteval, shape):
+def test_tiled_interp_mixed_inputs(monkeypatch, kernel, shape):
     """A binary16 direct input, a binary32 input read transposed (staged), a
-    per-row constant and a scalar; binary32 and bfloat16 outputs."""
+    per-row constant and a scalar; binary32 and bfloat16 outputs.  Every
+    instantiated tile shape of the interpreter (ECMD_TILED_INTERP; the first
+    is the default) and the tiled kernel with RtEval."""
     import torch
-    from gpu_util import NPD
     import elementwise_tensor_commands_amd as ecmd
+    rteval = kernel == "rteval"
     if rteval:
         monkeypatch.setenv("ECMD_TILED_RTEVAL", "1")
+    else:
+        monkeypatch.setenv("ECMD_TILED_INTERP", kernel)
     R, C = shape
     spec = [("x", ("load", "f16", 2)), ("y", ("load", "f32", 2)), ("b", ("load", "f32", 2)),
             ("s", ("scalar", "f32")),
@@ -198,8 +205,8 @@ def test_tiled_interp_mixed_inputs(monkeypatch, rteval, shape):
     assert (plan["lds_bytes"] == 64 * 64 * 4) == rteval, plan      # RtEval: one 64 x 64 staging tile
     cmd.launch(*gv, o0, o1)
     torch.cuda.synchronize()
-    compare(host(o0), ref[0], 0, "tiled interp %s rteval=%s out0" % (shape, rteval))
-    compare(host(o1), ref[1], 0, "tiled interp %s rteval=%s out1" % (shape, rteval))
+    compare(host(o0), ref[0], 0, "tiled interp %s %s out0" % (shape, kernel))
+    compare(host(o1), ref[1], 0, "tiled interp %s %s out1" % (shape, kernel))
 
 
 @pytest.mark.parametrize("seed", range(24))

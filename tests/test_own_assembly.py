@@ -114,7 +114,7 @@ def test_interp_waits_for_lds_dma():
     compiler: the interpreter waits for them explicitly.  In program order, no
     ds_read may follow a global_load_lds without an s_waitcnt vmcnt(0) between."""
     ks = _kernels(_asm("kernels_interp"))
-    assert len(ks) == 26, list(ks)     # linear and rows x K = 1, 2, 4 x nontemporal loads x stores; tiled x 2
+    assert len(ks) == 34, list(ks)     # linear and rows x K = 1, 2, 4 x nontemporal loads x stores; 5 tiled shapes x 2
     for name, (body, _) in ks.items():
         assert "global_load_lds_dwordx4" in body and "ds_read_b128" in body, name
         pending = False
