@@ -339,7 +339,7 @@ int64_t env_int(const char *name, int64_t dflt)
 //   launches anyway.  Smaller working sets use ordinary loads so that repeated
 //   launches can hit in that cache.  ECMD_NT_LOAD=0/1 overrides.
 constexpr int64_t kMallBytes = (int64_t)256 << 20;
-constexpr int kDefaultTileM = 32, kDefaultTileN = 256, kDefaultTileBlock = 512, kDefaultTileWalk = 1;
+constexpr int kDefaultTileM = 32, kDefaultTileN = 256, kDefaultTileBlock = 256, kDefaultTileWalk = 1;
 
 // Linear kernel shape: one 16-byte vector per operand per work-item -- 4
 // elements when any operand is 32-bit (E = 4 measured fastest there), 8 when
