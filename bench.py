@@ -115,6 +115,37 @@ def time_steps(cmd, args, steps, warmup):
     return start.elapsed_time(end), wall_ms
 
 
+def measure_graph(wl, launches=100, replays=20):
+    """Back-to-back launches captured in one HIP graph (torch.cuda.CUDAGraph)
+    and replayed: the rate once the host's per-launch cost is gone (the
+    launch-bound 65,536-element configuration).  Timed by HIP events around
+    the replays."""
+    import torch
+    import workloads as W
+    cmd, args, plan, _ = setup(wl)
+    bound = cmd.bind(*args)
+    bound.launch()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = cmd.bind(*args)              # the capture stream
+        for _ in range(launches):
+            cap.launch()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    per_us = start.elapsed_time(end) * 1e3 / (launches * replays)
+    byts = W.algorithmic_bytes(wl)
+    return {"kernel": plan["kernel"], "launches_per_graph": launches, "replays": replays,
+            "per_launch_us": round(per_us, 3), "gbps": round(byts / (per_us * 1e-6) / 1e9, 1)}
+
+
 def time_each(cmd, args, reps, cold=False):
     """Per-launch HIP event pairs, optionally reading 1 GiB of unrelated data
     before each launch (outside the events) so that none of the Command's data
@@ -400,6 +431,8 @@ def main():
                 "gelem_per_s": round(r["elements"] / (r["kernel_avg_us"] * 1e-6) / 1e9, 2),
             }
             log("%s: %s" % (wl, json.dumps(line["commands"][wl])))
+        line["commands"]["add_f32_graph"] = measure_graph("add_f32")
+        log("add_f32_graph: %s" % json.dumps(line["commands"]["add_f32_graph"]))
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(base)
