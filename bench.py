@@ -28,7 +28,7 @@ METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, per Comm
 DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two_out": "f16/f32",
             "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32",
             "batched_transpose": "f32", "bias_nchw": "f32", "axpby_f16": "f16", "axpby_bf16": "bf16",
-            "bias_relu_f32": "f32"}
+            "bias_relu_f32": "f32", "transposed_relu": "f32"}
 # Measured besides the five configurations: the plain copy (the bandwidth and
 # counter reference), the widened op set, the rank-3/4 views and native 16-bit
 # arithmetic, and a Command with no ahead-of-time kernel run by the interpreter
@@ -40,7 +40,7 @@ def split_workload(name):
     with its kernel compiled at run time."""
     return (name[:-4], True) if name.endswith("_jit") else (name, False)
 EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "axpby_f16", "axpby_bf16",
-         "bias_relu_f32", "bias_relu_f32_jit"]
+         "bias_relu_f32", "bias_relu_f32_jit", "transposed_relu", "transposed_relu_jit"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 

@@ -61,6 +61,7 @@ struct Selection {
     int path = CMD_PATH_NONE;
     int variant = -1;
     bool jit = false;           // a run-time compiled kernel (variant -1 otherwise means the interpreter)
+    int mask = 0;               // tiled path: staged inputs (bit k = input k)
     bool interp = false;        // linear path: the LDS-file interpreter (kernels_interp.hip)
     int k_sub = 0, n_slot = 0;  // its sub-chunks per super-chunk and temporary slots
     bool vec = false;
@@ -763,7 +764,22 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
                      mask == 0x2) ? 0 : -1;
         S.tile = S.variant == 0 ? tile_shape() : TileShape{64, 64, 256};   // RtEval has one shape
         S.lds = n_staged * S.tile.tn * S.tile.tm * 4;
-        if (S.variant < 0) {
+        S.mask = mask;
+        if (S.variant < 0 && !force_generic && h->jit && !any_rowconst) {
+            // A kernel compiled at run time on 32 x 256 tiles with 512
+            // work-items: four chunks per work-item, whose direct inputs it
+            // holds in registers (with 256 work-items, eight: max(X + 2 Y^T, 0)
+            // ran at 5,064 GB/s against 5,770); ECMD_TILE overrides.  Its
+            // staging tiles must fit the 64 KiB a module kernel may use.
+            const TileShape ts = std::getenv("ECMD_TILE") ? tile_shape() : TileShape{32, 256, 512};
+            const int lds = n_staged * ts.tm * ts.tn * 4;
+            if (lds <= 65536) {
+                S.jit = true;
+                S.tile = ts;
+                S.lds = lds;
+            }
+        }
+        if (S.variant < 0 && !S.jit) {
             // The LDS-file interpreter on its own tile shape, when its staging
             // tiles and register files fit 64 KiB (two or more work-groups per
             // CU) and its grid one dispatch; RtEval's 64 x 64 tiles otherwise.
@@ -799,7 +815,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         S.tiles_r = (T.n[2] + S.tile.tm - 1) / S.tile.tm;
         S.tiles_c = (T.n[3] + S.tile.tn - 1) / S.tile.tn;
         S.grid = S.tiles_r * S.tiles_c * T.n[0] * T.n[1];
-        S.name = S.variant == 0 ? "tiled_add_scaled_f32" : "tiled_generic";
+        S.name = S.variant == 0 ? "tiled_add_scaled_f32" : S.jit ? "jit_tiled" : "tiled_generic";
         return;
     }
     S.n_staged = 0;
@@ -810,6 +826,22 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
     const int64_t total = C.n[0] * C.n[1] * C.n[2] * ((C.n[3] + kGatherE - 1) / kGatherE);
     S.grid = std::max<int64_t>(1, std::min<int64_t>((total + kGatherBlock - 1) / kGatherBlock, 8LL * cu_count));
     S.name = "gather_generic";
+}
+
+// Tiled kernels: nontemporal global accesses unless ECMD_TILED_NT=0.
+bool tiled_nt()
+{
+    const char *v = std::getenv("ECMD_TILED_NT");
+    return !(v && std::strcmp(v, "0") == 0);
+}
+
+// The run-time compiled kernel a selection names.
+JitRequest jit_request(const Selection &S, const Program &P)
+{
+    if (S.path == CMD_PATH_LINEAR) return JitRequest{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, P};
+    if (S.path == CMD_PATH_ROWS) return JitRequest{JIT_ROWS, 4, 4, S.shape.nt_load, S.shape.nt_store, P};
+    const bool nt = tiled_nt();
+    return JitRequest{JIT_TILED, 4, 4, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
 }
 
 int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int cu_count)
@@ -935,9 +967,7 @@ int32_t cmd_prepare(cmd_t h, const cmd_arg *args, int32_t nargs, int32_t *from)
     int where = -1;
     if (S.jit) {
         std::string err;
-        const JitRequest r{S.path == CMD_PATH_LINEAR ? JIT_LINEAR : JIT_ROWS, S.shape.e, S.shape.g,
-                           S.shape.nt_load, S.shape.nt_store, h->prog};
-        if (jit_prepare(r, &where, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
+        if (jit_prepare(jit_request(S, h->prog), &where, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
     }
     if (from) *from = where;
     h->err.clear();
@@ -1121,8 +1151,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         if (S.jit) {
             hipFunction_t fn;
             std::string err;
-            const JitRequest r{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, h->prog};
-            if (jit_function(r, &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
+            if (jit_function(jit_request(S, h->prog), &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
             void *params[] = {&A};
             herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
                                               (hipStream_t)hip_stream, params, nullptr);
@@ -1136,15 +1165,14 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
     } else {
         StridedArgs A;
         fill_strided(h, B, S, A);
-        const char *ntv = std::getenv("ECMD_TILED_NT");
-        const bool nt = !(ntv && std::strcmp(ntv, "0") == 0);
+        const bool nt = tiled_nt();
         if (S.jit) {
             hipFunction_t fn;
             std::string err;
-            const JitRequest r{JIT_ROWS, 4, 4, S.shape.nt_load, S.shape.nt_store, h->prog};
-            if (jit_function(r, &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
+            if (jit_function(jit_request(S, h->prog), &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
             void *params[] = {&A};
-            herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
+            herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1,
+                                              S.path == CMD_PATH_TILED ? (unsigned)S.lds : 0u,
                                               (hipStream_t)hip_stream, params, nullptr);
         } else {
             InterpTape T;

@@ -1,12 +1,12 @@
-// ecmd_jit.cpp -- compile the linear or rows kernel for one Program at run
-// time, and cache the code objects in memory and on disk.
+// ecmd_jit.cpp -- compile the linear, rows or tiled kernel for one Program at
+// run time, and cache the code objects in memory and on disk.
 //
 // The translation unit handed to hiprtc is the embedded device headers plus
 //
 //   namespace ecmd { constexpr Program kJitProg = { <the lowered bytes> }; }
 //
-// and the kernel is the template instance CtEval<kJitProg> of the linear or
-// rows kernel -- exactly what an ahead-of-time specialised kernel is, for a
+// and the kernel is the template instance CtEval<kJitProg> of the linear,
+// rows or tiled kernel -- exactly what an ahead-of-time specialised kernel is, for a
 // Program that is not on the ahead-of-time list.  The compile options are the
 // library's own device flags (no contraction, no packed binary32, gfx950).
 //
@@ -169,7 +169,7 @@ void write_file(const std::string &dir, const std::string &key, const JitRequest
 int compile(const JitRequest &r, const std::string &name, Entry &e, std::string &err)
 {
     const std::string src = "#include <hip/hip_runtime.h>\n#include \"ecmd_kern_linear.h\"\n"
-                            "#include \"ecmd_kern_rows.h\"\nnamespace ecmd {\n" +
+                            "#include \"ecmd_kern_rows.h\"\n#include \"ecmd_kern_tiled.h\"\nnamespace ecmd {\n" +
                             program_literal(r.prog) + "}  // namespace ecmd\n";
     std::vector<const char *> names, texts;
     for (int i = 0; i < kJitHeaderCount; ++i) names.push_back(kJitHeaderNames[i]), texts.push_back(kJitHeaderTexts[i]);
@@ -240,6 +240,9 @@ std::string jit_name(const JitRequest &r)
     if (r.kind == JIT_LINEAR)
         std::snprintf(b, sizeof b, "ecmd::k_linear<ecmd::CtEval<ecmd::kJitProg>, %d, %d, true, %s, %s>", r.e, r.g,
                       r.ntl ? "true" : "false", r.nts ? "true" : "false");
+    else if (r.kind == JIT_TILED)
+        std::snprintf(b, sizeof b, "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, %d, %s, %d, %d, %d>", r.mask,
+                      r.ntl ? "true" : "false", r.tm, r.tn, r.tb);
     else
         std::snprintf(b, sizeof b, "ecmd::k_rows<ecmd::CtEval<ecmd::kJitProg>, %s, %s>", r.ntl ? "true" : "false",
                       r.nts ? "true" : "false");

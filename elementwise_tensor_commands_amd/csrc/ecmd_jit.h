@@ -8,6 +8,7 @@
 // the same device templates (embedded as text) are instantiated for that one
 // Program with hiprtc, and the code object is kept in memory and on disk,
 // keyed by the Program's bytes, the kernel variant and the sources' hash.
+// The linear, rows and tiled kernels can be compiled this way.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -18,17 +19,20 @@
 
 namespace ecmd {
 
-enum JitKernel { JIT_LINEAR = 1, JIT_ROWS = 2 };
+enum JitKernel { JIT_LINEAR = 1, JIT_ROWS = 2, JIT_TILED = 3 };
 
 struct JitRequest {
     JitKernel kind;
     int e, g;          // linear: elements per work-item and per vector access
-    bool ntl, nts;     // nontemporal loads / stores
+    bool ntl, nts;     // nontemporal loads / stores (tiled: ntl for both)
     Program prog;
+    int mask = 0;      // tiled: staged inputs (bit k = input k)
+    int tm = 0, tn = 0, tb = 0;   // tiled: tile shape and work-items
 };
 
 // Template instance the request names, e.g.
-// "ecmd::k_linear<ecmd::CtEval<ecmd::kJitProg>, 4, 4, true, true, true>".
+// "ecmd::k_linear<ecmd::CtEval<ecmd::kJitProg>, 4, 4, true, true, true>" or
+// "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, 2, true, 32, 256, 256>".
 std::string jit_name(const JitRequest &r);
 
 // Make sure the code object exists (memory, else disk, else compile and store

@@ -1,0 +1,215 @@
+// ecmd_kern_tiled.h -- the tiled kernel: rank-2 evaluation with transposed
+// operands staged through LDS.  Device templates only: kernels_tiled.hip
+// instantiates them ahead of time, the run-time compiler (ecmd_jit.cpp) for
+// other Programs.
+//
+// Canonical 4-D views (see StridedArgs): dimensions 0 and 1 are batch
+// dimensions, each batch index selects a rows x cols plane (dimensions 2 and
+// 3).  An operand view maps (b0, b1, r, c) to b0*s0 + b1*s1 + r*s2 + c*s3
+// (rocRoller "Design Overview", section "Kernel Graph": each dimension has a
+// size and a stride).  Outputs and "direct" inputs are inner-contiguous
+// (s3 == 1): a row of a tile is one contiguous run.  "Staged" inputs are
+// row-contiguous along the plane's rows instead (s2 == 1, e.g. the transpose
+// of a row-major matrix): a column of a tile is one contiguous run, so reading
+// them along rows would touch one element per run.  "Row-constant" inputs have
+// s3 == 0 (broadcast along the columns, e.g. a per-channel bias): one value
+// per row.
+//
+// One work-group (TB = 256 or 512 work-items) owns a TM x TN output tile
+// (TM and TN multiples of 32):
+//   1. For every staged input it reads the TN tile columns as contiguous runs
+//      of TM elements in 16-byte vectors (each half-wavefront: 4 columns x 32
+//      rows, whole 128-byte lines) and writes them into an LDS tile stored
+//      column by column, the row index XOR-swizzled by the column (tile_word).
+//   2. After one barrier each work-item evaluates TM*TN/(4*TB) chunks of 4
+//      consecutive elements of one row (each half-wavefront: 4 rows x 32
+//      columns): direct inputs are read with 16-byte vector loads, staged ones
+//      from LDS, and outputs are written with 16-byte stores.
+// The swizzle makes both LDS phases free of bank conflicts (the argument is
+// at tile_word; a host test checks it for every instantiated shape), with no
+// padding words.
+// In the specialised kernels the direct inputs' loads are issued before the
+// barrier, together with the staging loads, so that a tile waits for one
+// round trip to memory instead of two.  Full tiles use the nontemporal cache
+// policy (every instruction covers whole cache lines); edge tiles (rows or
+// cols not a multiple of the tile) use per-element masked accesses.
+//
+// Tile order: tile t of the grid is (t / tiles_c, t % tiles_c) when walk <= 1;
+// otherwise tiles go down a band of `walk` tile rows before moving right, so
+// that tiles running at the same time read neighbouring stretches of the
+// staged input's rows (the same DRAM pages) as well as of the direct inputs'.
+//
+// Staging is a prior-art idea the Silk backend also assumes (its tiled kernels
+// default to a 16 KiB LDS segment, Silk "AMDGPU Backend", section "Code Object
+// Format"): a 64 x 64 binary32 tile is 16,384 bytes.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "ecmd_eval.h"
+
+namespace ecmd {
+
+// Staged-input mask: bit k set = input k goes through LDS.  kMaskRuntime reads
+// the mask from the argument block.
+constexpr int kMaskRuntime = -1;
+
+template <int MASK>
+__device__ __forceinline__ bool staged(const StridedArgs &A, int k)
+{
+    if constexpr (MASK == kMaskRuntime) return A.in_staged[k] != 0;
+    else return (MASK >> k) & 1;
+}
+
+// LDS position of staged input k (staged inputs are packed in input order).
+template <int MASK>
+__device__ __forceinline__ int stage_pos(const StridedArgs &A, int k)
+{
+    if constexpr (MASK == kMaskRuntime) return A.in_staged[k] - 1;
+    else return __builtin_popcount(MASK & ((1 << k) - 1));
+}
+
+__device__ __forceinline__ int clamp4(int64_t left) { return left <= 0 ? 0 : (left >= 4 ? 4 : (int)left); }
+
+template <class EV, int MASK, bool NT, int TM, int TN, int TB>
+__global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
+{
+    constexpr int kWords = TN * TM;
+    constexpr int kSV = TN * TM / 4 / TB;               // staging vectors per work-item per staged input
+    constexpr int kP = TM * TN / 4 / TB;                // chunks per work-item
+    constexpr bool kPrefetch = MASK != kMaskRuntime;
+    static_assert(kSV >= 1 && kP >= 1, "tile too small for the work-group");
+    static_assert(TM % 32 == 0 && TN % 32 == 0 && TB % 64 == 0, "tile split needs multiples of 32");
+    extern __shared__ uint32_t lds[];
+
+    // Plane and tile coordinates (all counts fit in 32 bits: the grid is one
+    // dimension).  Each plane (batch index) has tiles_r x tiles_c tiles.
+    const uint32_t tiles_c = (uint32_t)A.tiles_c, tiles_r = (uint32_t)A.tiles_r;
+    const uint32_t per_plane = tiles_r * tiles_c;
+    const uint32_t plane = blockIdx.x / per_plane;
+    const uint32_t id = blockIdx.x - plane * per_plane;
+    const uint32_t n1 = (uint32_t)A.n[1];
+    const uint32_t b0 = plane / n1, b1 = plane - b0 * n1;
+    const uint32_t walk = (uint32_t)A.tile_walk;
+    uint32_t tr, tc;
+    if (walk <= 1) {
+        tr = id / tiles_c;
+        tc = id - tr * tiles_c;
+    } else {
+        const uint32_t band = walk * tiles_c;
+        const uint32_t b = id / band, rem = id - b * band;
+        const uint32_t left = tiles_r - b * walk;
+        const uint32_t h = left < walk ? left : walk;
+        tc = rem / h;
+        tr = b * walk + (rem - tc * h);
+    }
+    const int64_t rows = A.n[2], cols = A.n[3];
+    const int64_t r0 = (int64_t)tr * TM, c0 = (int64_t)tc * TN;
+    const bool full = (r0 + TM <= rows) && (c0 + TN <= cols);
+    const int t = threadIdx.x;
+    // Element offset of this plane in each operand.
+    auto in_base = [&](int k) { return (int64_t)b0 * A.in_s[k][0] + (int64_t)b1 * A.in_s[k][1]; };
+    auto out_base = [&](int k) { return (int64_t)b0 * A.out_s[k][0] + (int64_t)b1 * A.out_s[k][1]; };
+
+    // Direct inputs of every chunk, loaded up front in the specialised kernels
+    // (the interpreter keeps one chunk's registers at a time).
+    constexpr int kRegSets = kPrefetch ? kP : 1;
+    Regs<4> R[kRegSets];
+    int count[kP];
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+        int rl, cl;
+        tile_split(t + TB * p, TN, rl, cl);
+        count[p] = full ? 4 : (r0 + rl < rows ? clamp4(cols - (c0 + cl)) : 0);
+    }
+    auto load_direct = [&](int p) {
+        int rl, cl;
+        tile_split(t + TB * p, TN, rl, cl);
+        const int64_t r = r0 + rl, c = c0 + cl;
+        Regs<4> &Rp = R[kPrefetch ? p : 0];
+#pragma unroll
+        for (int k = 0; k < kMaxIn; ++k) {
+            if (k < EV::n_in(A.prog) && !staged<MASK>(A, k)) {
+                const uint8_t ty = EV::in_ty(A.prog, k);
+                if (MASK == kMaskRuntime && A.in_rowconst[k]) {
+                    // one value per row, the same for the 4 columns
+                    if (count[p] > 0) {
+                        uint32_t one[1];
+                        load_elems<1, false>(A.in[k], ty, in_base(k) + r * A.in_s[k][2], 1, one);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Rp.in[k][e] = one[0];
+                    }
+                    continue;
+                }
+                const int64_t off = in_base(k) + r * A.in_s[k][2] + c;
+                if (full) load_group<4, true, NT>(A.in[k], ty, off, 4, Rp.in[k]);
+                else if (count[p] > 0) load_elems<4, false>(A.in[k], ty, off, count[p], Rp.in[k]);
+            }
+        }
+    };
+    if constexpr (kPrefetch) {
+#pragma unroll
+        for (int p = 0; p < kP; ++p) load_direct(p);
+    }
+
+    // Stage the column-contiguous inputs: element (cl, rl) at LDS word
+    // tile_word(TM, cl, rl).
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) {
+        if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
+            const uint8_t ty = EV::in_ty(A.prog, k);
+            uint32_t *dst = lds + stage_pos<MASK>(A, k) * kWords;
+            uint32_t sv[kSV][4];
+#pragma unroll
+            for (int j = 0; j < kSV; ++j) {
+                int cl, rl;
+                tile_split(t + TB * j, TM, cl, rl);
+                const int64_t off = in_base(k) + (c0 + cl) * A.in_s[k][3] + (r0 + rl);
+                if (full) {
+                    load_group<4, true, NT>(A.in[k], ty, off, 4, sv[j]);
+                } else {
+                    const int cnt = c0 + cl < cols ? clamp4(rows - (r0 + rl)) : 0;
+                    if (cnt > 0) load_elems<4, false>(A.in[k], ty, off, cnt, sv[j]);
+                    else sv[j][0] = sv[j][1] = sv[j][2] = sv[j][3] = 0u;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kSV; ++j) {
+                int cl, rl;
+                tile_split(t + TB * j, TM, cl, rl);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[tile_word(TM, cl, rl + e)] = sv[j][e];
+            }
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+        if (count[p] == 0) continue;
+        int rl, cl;
+        tile_split(t + TB * p, TN, rl, cl);
+        const int64_t r = r0 + rl, c = c0 + cl;
+        if constexpr (!kPrefetch) load_direct(p);
+        Regs<4> &Rp = R[kPrefetch ? p : 0];
+#pragma unroll
+        for (int k = 0; k < kMaxIn; ++k) {
+            if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
+                const uint32_t *src = lds + stage_pos<MASK>(A, k) * kWords;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Rp.in[k][e] = src[tile_word(TM, cl + e, rl)];
+            }
+        }
+        uint32_t out[kMaxOut][4];
+        EV::template run<4>(A.prog, A.uni, Rp, out);
+#pragma unroll
+        for (int k = 0; k < kMaxOut; ++k) {
+            if (k < EV::n_out(A.prog)) {
+                const int64_t off = out_base(k) + r * A.out_s[k][2] + c;
+                if (full) store_group<4, true, NT>(A.out[k], EV::out_ty(A.prog, k), off, 4, out[k]);
+                else store_elems<4, false, false>(A.out[k], EV::out_ty(A.prog, k), off, count[p], out[k]);
+            }
+        }
+    }
+}
+
+}  // namespace ecmd

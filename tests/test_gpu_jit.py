@@ -74,3 +74,32 @@ def test_bias_relu_compiled_and_interpreted(n, monkeypatch):
         cmd.launch(*gv, out)                     # the second launch finds the kernel in memory
         torch.cuda.synchronize()
         compare(host(out), ref, 0, "bias_relu n=%d %s" % (n, plan["kernel"]))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_transposed_views_compiled(seed):
+    """Random Commands over transposed views: the tiled kernel compiled at run
+    time for each (inputs staged through LDS with the compile-time mask)."""
+    spec, ins, outs = random_view_case(seed + 300, staged=True)
+    run_views(spec, ins, outs, False, "compiled tiled seed %d" % seed)
+
+
+@pytest.mark.parametrize("n", [200, 1000, 16384])
+def test_transposed_relu_compiled_and_interpreted(n):
+    """max(X + 2 Y^T, 0) on the transposed configuration's views (row-padded
+    X, Y read transposed), compiled and on the tiled interpreter, up to the
+    full 16384 x 16384."""
+    import elementwise_tensor_commands_amd as ecmd
+    if n == 16384:
+        print("  full size transposed_relu", flush=True)
+    vals, extra = W.make_inputs("transposed_relu", n)
+    ref = run_oracle(W.TRANSPOSED_RELU, vals)[0]
+    gv = W.to_torch(vals, extra, dev())
+    for jit in (True, False):
+        cmd = ecmd.from_spec(W.TRANSPOSED_RELU).jit(jit)
+        out = torch.empty((n, n), device=dev())
+        plan = cmd.plan(*gv, out)
+        assert plan["compiled"] == jit and plan["kernel"] == ("jit_tiled" if jit else "tiled_generic"), plan
+        cmd.launch(*gv, out)
+        torch.cuda.synchronize()
+        compare(host(out), ref, 0, "transposed_relu n=%d %s" % (n, plan["kernel"]))

@@ -1,6 +1,7 @@
 """Run-time compiled kernels on the host: compile without a GPU, the memory
 and disk caches, the plan's report, and our own gfx950 code in the code
-objects (no fused multiply-add, no scratch, 16-byte accesses)."""
+objects (no fused multiply-add, no scratch, 16-byte accesses; LDS staging
+and a barrier in the compiled tiled kernel)."""
 import os
 import subprocess
 import sys
@@ -76,7 +77,22 @@ def test_each_variant_and_program_has_its_own_entry(cache_dir):
     out = torch.zeros(64, 64)
     assert rows.plan(x, bias, 2.0, out)["kernel"] == "jit_rows"
     assert rows.prepare(x, bias, 2.0, out) == 2
-    assert len(os.listdir(cache_dir)) == 2 + compiled
+    tiled = E.from_spec(TILED_SPEC).jit()
+    tv = _tiled_values()
+    p = tiled.plan(*tv)
+    assert p["kernel"] == "jit_tiled" and p["compiled"] and p["block"] == 512 and p["lds_bytes"] == 32 * 256 * 4, p
+    assert tiled.prepare(*tv) == 2
+    assert len(os.listdir(cache_dir)) == 3 + compiled
+
+
+# out = min(X + Y^T, s) - Y^T: a program the tiled path has no ahead-of-time kernel for
+TILED_SPEC = [("X", ("load", "f32", 2)), ("Y", ("load", "f32", 2)), ("s", ("scalar", "f32")),
+              ("a", ("add", "X", "Y")), ("m", ("min", "a", "s")), ("d", ("sub", "m", "Y")),
+              ("o", ("store", "d", 2))]
+
+
+def _tiled_values(R=64, C=512):
+    return [torch.zeros(R, C), torch.zeros(C, R).t(), 1.0, torch.zeros(R, C)]
 
 
 STALE_SPEC = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("p", ("mul", "x", "y")),
@@ -119,7 +135,7 @@ def _code_object(path):
     return data[pos:]
 
 
-@pytest.mark.parametrize("spec_name", ["bias_relu", "mixed16"])
+@pytest.mark.parametrize("spec_name", ["bias_relu", "mixed16", "tiled"])
 def test_compiled_code_is_our_rules(cache_dir, tmp_path, spec_name):
     """Disassemble the run-time compiled code objects (built here): no fused
     multiply-add, no scratch, no packed binary32, 16-byte vector accesses."""
@@ -130,6 +146,10 @@ def test_compiled_code_is_our_rules(cache_dir, tmp_path, spec_name):
         c = E.from_spec(spec).jit()
         n = 1 << 16
         vals = [torch.zeros(n), torch.zeros(n), 0.5, 0.0, torch.zeros(n)]
+    elif spec_name == "tiled":            # max instead of min: a program only this test compiles
+        spec = [st if st[0] != "m" else ("m", ("max", "a", "s")) for st in TILED_SPEC]
+        c = E.from_spec(spec).jit()
+        vals = _tiled_values()
     else:
         spec = [("x", ("load", "f16", 1)), ("y", ("load", "bf16", 1)), ("a", ("cvt", "x", "f32")),
                 ("b", ("cvt", "y", "f32")), ("m", ("mul", "a", "b")), ("s", ("add", "m", "a")),
@@ -143,5 +163,7 @@ def test_compiled_code_is_our_rules(cache_dir, tmp_path, spec_name):
     co.write_bytes(_code_object(f))
     asm = subprocess.run([LLVM_OBJDUMP, "-d", str(co)], capture_output=True, text=True, check=True).stdout
     assert "global_load_dword" in asm and "global_store_dwordx4" in asm
+    if spec_name == "tiled":
+        assert "ds_write" in asm and "ds_read" in asm and "s_barrier" in asm
     for bad in ("v_fma", "v_fmac", "v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32", "scratch_", "v_fma_mix"):
         assert bad not in asm, bad

@@ -127,6 +127,16 @@ BIAS_RELU_F32 = [
     ("out", ("store", "r", 1)),
 ]
 
+# The transposed configuration's views with a Command the tiled path has no
+# ahead-of-time kernel for: out[i,j] = max(X[i,j] + alpha*Y[j,i], 0).
+TRANSPOSED_RELU = TRANSPOSED_2D[:3] + [
+    ("zero", ("scalar", "f32")),
+    ("ay", ("mul", "alpha", "Yt")),
+    ("o", ("add", "X", "ay")),
+    ("r", ("max", "o", "zero")),
+    ("out", ("store", "r", 2)),
+]
+
 # Views of rank 3 and 4.  A batch of transposed planes: out[b] = X[b] + alpha * Y[b]^T.
 BATCHED_TRANSPOSE = [
     ("X", ("load", "f32", 3)),
@@ -181,6 +191,9 @@ WORKLOADS = {
     # No ahead-of-time kernel: interpreter, or compiled at run time.
     "bias_relu_f32": dict(index=12, spec=BIAS_RELU_F32, n=1 << 28,
                           label="out = max(x*s + y, 0), fp32, n=2^28, s=0.5 (no ahead-of-time kernel)"),
+    "transposed_relu": dict(index=13, spec=TRANSPOSED_RELU, n=16384,
+                            label="out[i,j] = max(X[i,j] + alpha*Y[j,i], 0), fp32 16384x16384, X row stride 16448 "
+                                  "(no ahead-of-time kernel)"),
 }
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
@@ -189,6 +202,7 @@ SCALARS = {
     "axpby_f32": {"alpha": np.float32(1.5), "beta": np.float32(-0.25)},
     "mixed_two_out": {"s": np.float32(0.5)},
     "transposed_2d": {"alpha": np.float32(2.0)},
+    "transposed_relu": {"alpha": np.float32(2.0), "zero": np.float32(0.0)},
     "classify_u32": {"t": np.int32(-2**31)},          # 0x80000000 as unsigned
     "fill_f32": {"s": np.float32(1.25)},
     "batched_transpose": {"alpha": np.float32(2.0)},
@@ -206,7 +220,7 @@ def shape_of(workload: str, n: int | None = None, shape=None) -> tuple:
     if "shape" in w:
         return tuple(w["shape"] if shape is None else shape)
     n = w["n"] if n is None else n
-    return (n, n) if workload == "transposed_2d" else (n,)
+    return (n, n) if workload in ("transposed_2d", "transposed_relu") else (n,)
 
 
 def layout(view: np.ndarray, storage: np.ndarray):
@@ -295,13 +309,13 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
         vals = [rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32).view(np.int32), sc["t"]]
     elif workload == "fill_f32":
         vals = [sc["s"]]
-    elif workload == "transposed_2d":
+    elif workload in ("transposed_2d", "transposed_relu"):
         rows = cols = n
         xs = np.full((rows, cols + row_pad), np.nan, dtype=np.float32)
         xs[:, :cols] = _uniform_pm1_f32(rng, (rows, cols))
         y = _uniform_pm1_f32(rng, (cols, rows))
-        extra = {"X_storage": xs, "Y": y, "storage": [xs, y, None]}
-        vals = [xs[:, :cols], y.T, sc["alpha"]]
+        vals = [xs[:, :cols], y.T, sc["alpha"]] + ([sc["zero"]] if workload == "transposed_relu" else [])
+        extra = {"X_storage": xs, "Y": y, "storage": [xs, y] + [None] * (len(vals) - 2)}
         return vals, extra
     elif workload == "batched_transpose":
         b, r, c = shape_of(workload, shape=shape)
