@@ -65,26 +65,20 @@ __device__ __forceinline__ uint32_t f2bf(uint32_t f)
 // int32 -> bfloat16, rounded once from the exact integer (through binary32
 // would round twice: 2^24 + 2^16 + 1 would land on a midpoint).  |a| is
 // shifted to an 8-bit significand; the dropped bits decide the rounding.
+// Selects only (see minmax16).
 __device__ __forceinline__ uint32_t i2bf(uint32_t a)
 {
     const uint32_t sign = (a >> 16) & 0x8000u;
     const uint32_t m = (a & 0x80000000u) ? 0u - a : a;      // |INT_MIN| = 2^31 as unsigned
-    if (m == 0u) return 0u;
-    uint32_t e = 31u - (uint32_t)__builtin_clz(m);           // leading bit position
-    uint32_t q;
-    if (e <= 7u) {
-        q = m << (7u - e);
-    } else {
-        const uint32_t sh = e - 7u;
-        q = m >> sh;
-        const uint32_t rem = m & ((1u << sh) - 1u), half = 1u << (sh - 1u);
-        if (rem > half || (rem == half && (q & 1u))) ++q;
-        if (q == 256u) {                                     // carried into the next binade
-            q = 128u;
-            ++e;
-        }
-    }
-    return sign | ((e + 127u) << 7) | (q & 0x7fu);
+    uint32_t e = 31u - (uint32_t)__builtin_clz(m | 1u);      // leading bit position (m = 0: handled last)
+    const uint32_t sh = e > 7u ? e - 7u : 0u;                // bits dropped below the 8-bit significand
+    uint32_t q = (m >> sh) << (e > 7u ? 0u : 7u - e);
+    const uint32_t rem = m & ((1u << sh) - 1u), half = sh ? 1u << ((sh - 1u) & 31u) : 0u;
+    q += (sh != 0u && (rem > half || (rem == half && (q & 1u)))) ? 1u : 0u;
+    const bool carry = q == 256u;                            // carried into the next binade
+    q = carry ? 128u : q;
+    e += carry ? 1u : 0u;
+    return m == 0u ? 0u : sign | ((e + 127u) << 7) | (q & 0x7fu);
 }
 
 // Value of a binary16 / bfloat16 pattern as binary32 bits (exact).
@@ -92,17 +86,18 @@ template <bool BF>
 __device__ __forceinline__ uint32_t h16f(uint32_t h) { return BF ? bf2f(h) : h2f(h); }
 
 // binary16 / bfloat16 minimum and maximum on the exact values; the result is
-// one operand's 16-bit pattern (NaN operand ignored unless both are, -0 below +0).
+// one operand's 16-bit pattern (NaN operand ignored unless both are, -0 below
+// +0).  Selects only, no early returns: a return per case compiles to branches
+// that differ between lanes (exec-mask juggling for every element).
 template <bool BF, bool MAX>
 __device__ __forceinline__ uint32_t minmax16(uint32_t a, uint32_t b)
 {
     const float x = as_f(h16f<BF>(a)), y = as_f(h16f<BF>(b));
-    if (!(x == x)) return b;
-    if (!(y == y)) return a;
-    if (MAX ? x > y : x < y) return a;
-    if (MAX ? y > x : y < x) return b;
     const bool a_neg = (a & 0x8000u) != 0u;
-    return (MAX ? !a_neg : a_neg) ? a : b;
+    uint32_t r = (MAX ? x > y : x < y) ? a : b;
+    r = (x == y) ? ((MAX ? !a_neg : a_neg) ? a : b) : r;
+    r = (y != y) ? a : r;
+    return (x != x) ? b : r;
 }
 
 // binary16 arithmetic in the format itself (v_add_f16 and friends: one IEEE
@@ -111,36 +106,37 @@ __device__ __forceinline__ _Float16 as_h(uint32_t u) { return __builtin_bit_cast
 __device__ __forceinline__ uint32_t h_bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
 
 // binary32 -> int32: truncate toward zero, saturate, NaN -> 0.  Written out so
-// that no out-of-range conversion (undefined in C++) is ever performed.
+// that no out-of-range conversion (undefined in C++) is ever performed, with
+// selects rather than early returns (see minmax16).
 __device__ __forceinline__ uint32_t f2i_sat(float f)
 {
-    if (!(f == f)) return 0u;
-    if (f >= 2147483648.0f) return 0x7fffffffu;
-    if (f < -2147483648.0f) return 0x80000000u;
-    return (uint32_t)(int32_t)f;
+    const bool hi = f >= 2147483648.0f, lo = f < -2147483648.0f, nan = !(f == f);
+    const float in_range = (hi || lo || nan) ? 0.0f : f;
+    uint32_t r = (uint32_t)(int32_t)in_range;
+    r = hi ? 0x7fffffffu : r;
+    return lo ? 0x80000000u : r;
 }
 
 // binary32 minimum / maximum: a NaN operand is ignored unless both are NaN;
 // -0 is below +0.  Written with comparisons and selects, not v_min/v_max, so
-// that the result does not depend on the hardware's NaN and signed-zero rules.
+// that the result does not depend on the hardware's NaN and signed-zero rules
+// (and with selects only, see minmax16).
 __device__ __forceinline__ uint32_t fmin_bits(uint32_t a, uint32_t b)
 {
     const float x = as_f(a), y = as_f(b);
-    if (!(x == x)) return b;
-    if (!(y == y)) return a;
-    if (x < y) return a;
-    if (y < x) return b;
-    return (a & 0x80000000u) ? a : b;
+    uint32_t r = x < y ? a : b;
+    r = (x == y) ? ((a & 0x80000000u) ? a : b) : r;
+    r = (y != y) ? a : r;
+    return (x != x) ? b : r;
 }
 
 __device__ __forceinline__ uint32_t fmax_bits(uint32_t a, uint32_t b)
 {
     const float x = as_f(a), y = as_f(b);
-    if (!(x == x)) return b;
-    if (!(y == y)) return a;
-    if (x > y) return a;
-    if (y > x) return b;
-    return (a & 0x80000000u) ? b : a;
+    uint32_t r = x > y ? a : b;
+    r = (x == y) ? ((a & 0x80000000u) ? b : a) : r;
+    r = (y != y) ? a : r;
+    return (x != x) ? b : r;
 }
 
 template <int C>
