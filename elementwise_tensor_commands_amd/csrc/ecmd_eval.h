@@ -220,6 +220,13 @@ __device__ __forceinline__ uint32_t apply(uint32_t a, uint32_t b, uint32_t c = 0
     else return 0u;
 }
 
+// n / d for a 32-bit n, by the multiplier and shifts of FastDiv.
+__device__ __forceinline__ uint32_t fast_div(const FastDiv &f, uint32_t n)
+{
+    const uint32_t t = __umulhi(n, f.mul);
+    return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 // ---------------------------------------------------------------------------
 // Generic interpreter.
 

@@ -79,6 +79,8 @@ struct Selection {
     int block = 0;
     int lds = 0;
     int e = 0;
+    int g_mode = 0;             // gather path: 0 per-element kernel, else the interpreter's mode (1 segments, 2 and 3 whole rows)
+    int64_t g_div = 0, g_waves = 0, g_rows_per_wave = 0;
     const char *name = "";
 };
 
@@ -607,11 +609,14 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
     bool all_flat = C.dims == 1;
     for (int k = 0; k < P.n_in && all_flat; ++k) all_flat = C.in_s[k][3] == 1;
     for (int k = 0; k < P.n_out && all_flat; ++k) all_flat = C.out_s[k][3] == 1;
-    if (all_flat) {
+    bool flat_vec = true;
+    for (int k = 0; k < P.n_in; ++k) flat_vec = flat_vec && aligned(B.in[k].ptr, 16);
+    for (int k = 0; k < P.n_out; ++k) flat_vec = flat_vec && aligned(B.out[k].ptr, 16);
+    // Flat views with a base off 16 bytes go to the gather path's segments
+    // (per-element accesses, lane-consecutive) unless 2^31 elements or more.
+    if (all_flat && (flat_vec || numel >= kMaxGridItems || env_int("ECMD_GATHER_MODE", 1) == 0)) {
         S.path = CMD_PATH_LINEAR;
-        S.vec = true;
-        for (int k = 0; k < P.n_in; ++k) S.vec = S.vec && aligned(B.in[k].ptr, 16);
-        for (int k = 0; k < P.n_out; ++k) S.vec = S.vec && aligned(B.out[k].ptr, 16);
+        S.vec = flat_vec;
         S.variant = (S.vec && !force_generic) ? program_match_linear(P) : -1;
         S.jit = S.vec && !force_generic && S.variant < 0 && h->jit;
         int64_t bytes = 0;
@@ -821,8 +826,34 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
     S.n_staged = 0;
     S.path = CMD_PATH_GATHER;
     S.variant = -1;
-    S.e = kGatherE;
+    // The gather interpreter when rows, columns and super-chunks count in 31
+    // bits: segments of 256 K columns of one row for rows longer than half a
+    // super-chunk, else whole rows per super-chunk.  ECMD_GATHER_MODE = 0
+    // forces the per-element kernel (A/B runs).
+    const int64_t rows = C.n[0] * C.n[1] * C.n[2], n3 = C.n[3];
+    const int64_t lim = kMaxGridItems;
+    S.g_mode = 0;
+    if (rows < lim && n3 < lim && env_int("ECMD_GATHER_MODE", 1) != 0) {
+        size_interp(P, S);
+        const int64_t span = 256 * S.k_sub;   // elements per super-chunk
+        if (n3 > span / 2) {
+            const int64_t segs = (n3 + span - 1) / span;
+            if (rows * segs < lim) S.g_mode = 1, S.g_div = segs, S.g_waves = rows * segs;
+        } else {
+            const int64_t m = span / n3;
+            S.g_mode = C.n[0] * C.n[1] == 1 ? 2 : 3;
+            S.g_div = n3, S.g_rows_per_wave = m, S.g_waves = (rows + m - 1) / m;
+        }
+    }
+    if (S.g_mode) {
+        S.grid = std::max<int64_t>(1, std::min<int64_t>(S.g_waves, kInterpMaxGrid));
+        S.name = S.g_mode == 1 ? "gather_segments" : "gather_whole_rows";
+        return;
+    }
+    S.interp = false;
+    S.lds = 0;
     S.block = kGatherBlock;
+    S.e = kGatherE;
     const int64_t total = C.n[0] * C.n[1] * C.n[2] * ((C.n[3] + kGatherE - 1) / kGatherE);
     S.grid = std::max<int64_t>(1, std::min<int64_t>((total + kGatherBlock - 1) / kGatherBlock, 8LL * cu_count));
     S.name = "gather_generic";
@@ -915,6 +946,14 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
         A.wave_in_row = ((C.n[3] + 3) / 4) % 64 == 0 ? 1u : 0u;
         for (int k = 0; k < h->prog.n_in; ++k)
             if (S.rowconst[k] && esize(B.in[k].dtype) == 2) A.rowconst16 = 1u;
+        A.div_n2 = make_fast_div((uint32_t)C.n[2]);
+        A.div_n1 = make_fast_div((uint32_t)C.n[1]);
+    }
+    if (S.path == CMD_PATH_GATHER && S.g_mode) {
+        A.g_waves = (uint32_t)S.g_waves;
+        A.g_rows = (uint32_t)(C.n[0] * C.n[1] * C.n[2]);
+        A.g_rows_per_wave = (uint32_t)S.g_rows_per_wave;
+        A.div_g = make_fast_div((uint32_t)S.g_div);
         A.div_n2 = make_fast_div((uint32_t)C.n[2]);
         A.div_n1 = make_fast_div((uint32_t)C.n[1]);
     }
@@ -1184,7 +1223,8 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
                        ? (S.interp ? launch_rows_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds,
                                                         hip_stream)
                                    : launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream))
-                       : launch_gather(A, g, hip_stream);
+                   : S.interp ? launch_gather_interp(S.g_mode, S.k_sub, A, T, g, S.lds, hip_stream)
+                              : launch_gather(A, g, hip_stream);
         }
     }
     if (herr != 0)

@@ -33,12 +33,6 @@
 namespace ecmd {
 
 
-__device__ __forceinline__ uint32_t fast_div(const FastDiv &f, uint32_t n)
-{
-    const uint32_t t = __umulhi(n, f.mul);
-    return (t + ((n - t) >> f.s1)) >> f.s2;
-}
-
 // WROW: a multiple of 64 vectors per row, so each wavefront lies in one row;
 // the row and the operands' row offsets are then computed once per wavefront
 // from its first lane (the lowest lane is active whenever any is), in scalar

@@ -185,6 +185,10 @@ struct StridedArgs {
     uint32_t wave_in_row;       // rows path: 1 = a multiple of 64 vectors per row (no wavefront spans two rows)
     uint32_t rowconst16;        // rows path: 1 = some row-constant input is 16-bit
     FastDiv div_vec, div_n2, div_n1;   // rows path: by vectors per row, by n[2], by n[1]
+    uint32_t g_waves;           // gather path: super-chunks of work in all
+    uint32_t g_rows;            // gather path: rows n[0] n[1] n[2]
+    uint32_t g_rows_per_wave;   // gather path, whole-row modes: rows per super-chunk
+    FastDiv div_g;              // gather path: by segments per row (segment mode) or by n[3] (whole rows)
     Program prog;
 };
 
@@ -382,7 +386,14 @@ int launch_tiled(int variant, bool nt, TileShape shape, const StridedArgs &A, La
 constexpr int kTiledInterpM = 32, kTiledInterpN = 64, kTiledInterpBlock = 256;
 int launch_tiled_interp(TileShape shape, bool nt, const StridedArgs &A, const InterpTape &T, LaunchGeometry g,
                         int lds_bytes, void *stream);
+// Gather path, any extents: per-element offsets in 64 bits.
 int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
+// The LDS-file interpreter (see launch_linear_interp) over the gather path's
+// positions: mode 1 segments of 256 k_sub columns of one row, mode 2 whole
+// rows of a plane (n[0] = n[1] = 1), mode 3 whole rows over all row
+// dimensions.  Fewer than 2^31 rows, columns and super-chunks (g_waves).
+int launch_gather_interp(int mode, int k_sub, const StridedArgs &A, const InterpTape &T, LaunchGeometry g,
+                         int lds_bytes, void *stream);
 // Rows path: the linear path's specialised Programs (variant indexes the same
 // list); nontemporal loads / stores as the host chooses.
 int launch_rows(int variant, bool nt_load, bool nt_store, const StridedArgs &A, LaunchGeometry g, void *stream);

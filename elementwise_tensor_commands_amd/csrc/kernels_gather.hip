@@ -1,13 +1,13 @@
-// kernels_gather.hip -- evaluation for views no faster path accepts (after
-// canonicalization: an output with no unit-stride dimension, inputs strided in
-// every dimension, broadcasts the tiled path does not take, or bases too
-// misaligned for vector access).
+// kernels_gather.hip -- the gather path's kernel for extents of 2^31 rows,
+// columns or super-chunks and more (the gather interpreter in
+// kernels_interp.hip takes every smaller view: any view no faster path
+// accepts, e.g. an output with no unit-stride dimension, inputs strided in
+// every dimension, or rows too misaligned for vector access).
 //
 // Each work-item takes 4 consecutive elements along the last canonical
 // dimension, computes every operand's element offset i0*s0 + i1*s1 + i2*s2 +
-// i3*s3 (rocRoller "Design Overview", section "Kernel Graph": a view is sizes
-// plus strides) and accesses elements one by one.  It is correct for every accepted view and makes no attempt at
-// coalescing.
+// i3*s3 in 64 bits (rocRoller "Design Overview", section "Kernel Graph": a
+// view is sizes plus strides) and accesses elements one by one.
 #include <hip/hip_runtime.h>
 
 #include "ecmd_eval.h"

@@ -548,6 +548,150 @@ int launch_tiled_interp(TileShape shape, bool nt, const StridedArgs &A, const In
     }
 }
 
+// The gather path's interpreter: the same register file and tape walk over
+// any accepted view, the element positions as in kernels_gather.hip.  Super-
+// chunk w of 256 K elements is either a segment of one row (mode 1: columns
+// 256 K seg ..; the row and every operand's row offset in scalar registers)
+// or whole rows (mode 2: rows w m .. w m + m - 1 of a plane, m = floor(256 K
+// / n3); mode 3 the same over all three row dimensions).  Element p of the
+// super-chunk sits in sub-chunk p / 256 at its own 4-byte word, so access
+// d of sub-chunk j (lane l taking element 256 j + 64 d + l) covers 64
+// consecutive elements of the work and fills 256 consecutive bytes of the
+// entry.  Every input goes straight into LDS: a direct global-to-LDS load of
+// 4 bytes per lane at the lane's own element address, or of 2 bytes for
+// binary16 / bfloat16, which gfx950 writes as one zero-extended word per lane
+// (lane l at M0 + 4 l, checked on the GPU), so 16-bit inputs arrive widened.
+// Lanes past the end of the work load the first element of a row (always in
+// bounds) and store nothing.  The tape then reads the entries 16 bytes per
+// lane as on the linear path (the wavefront's LDS accesses are in program
+// order, no barrier: one wavefront per work-group).
+template <int K, int MODE>
+__global__ __launch_bounds__(64) void k_gather_interp(const StridedArgs A, const InterpTape T)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t file[];
+    const uint32_t lane = threadIdx.x;
+    const Program &P = A.prog;
+    const int n_in = P.n_in;
+    const int lane_off = lane * 16;
+    interp_uniforms(P, A.uni, T, file, lane_off);
+    constexpr int kPos = 4 * K;   // positions per lane: access d of sub-chunk j is position 4 j + d
+    for (uint32_t w = blockIdx.x; w < A.g_waves; w += gridDim.x) {
+        uint32_t col[kPos], rq[MODE == 1 ? 1 : kPos], rb0[MODE == 3 ? kPos : 1], rb1[MODE == 3 ? kPos : 1];
+        bool ok[kPos];
+        uint32_t sb0 = 0u, sb1 = 0u, sr = 0u;
+        if constexpr (MODE == 1) {
+            const uint32_t q = fast_div(A.div_g, w);
+            const uint32_t seg = w - q * A.div_g.d;
+            const uint32_t t = fast_div(A.div_n2, q);
+            sr = q - t * A.div_n2.d;
+            sb0 = fast_div(A.div_n1, t);
+            sb1 = t - sb0 * A.div_n1.d;
+            const uint32_t n3 = (uint32_t)A.n[3];
+#pragma unroll
+            for (int i = 0; i < kPos; ++i) {
+                const uint32_t c = seg * (256u * K) + 64u * i + lane;
+                ok[i] = c < n3;
+                col[i] = ok[i] ? c : 0u;
+            }
+        } else {
+            const uint32_t q0 = w * A.g_rows_per_wave;
+            const uint32_t count = min(A.g_rows_per_wave, A.g_rows - q0) * A.div_g.d;
+#pragma unroll
+            for (int i = 0; i < kPos; ++i) {
+                const uint32_t p0 = 64u * i + lane;
+                ok[i] = p0 < count;
+                const uint32_t p = ok[i] ? p0 : 0u;
+                const uint32_t dq = fast_div(A.div_g, p);
+                col[i] = p - dq * A.div_g.d;
+                const uint32_t q = q0 + dq;
+                if constexpr (MODE == 3) {
+                    const uint32_t t = fast_div(A.div_n2, q);
+                    rq[i] = q - t * A.div_n2.d;
+                    rb0[i] = fast_div(A.div_n1, t);
+                    rb1[i] = t - rb0[i] * A.div_n1.d;
+                } else {
+                    rq[i] = q;
+                }
+            }
+        }
+        // element offset of position i in the view with strides s
+        auto off = [&](const int64_t (&s)[4], int i) -> int64_t {
+            if constexpr (MODE == 1)
+                return (int64_t)sb0 * s[0] + (int64_t)sb1 * s[1] + (int64_t)sr * s[2] + (int64_t)col[i] * s[3];
+            else if constexpr (MODE == 2)
+                return (int64_t)rq[i] * s[2] + (int64_t)col[i] * s[3];
+            else
+                return (int64_t)rb0[i] * s[0] + (int64_t)rb1[i] * s[1] + (int64_t)rq[i] * s[2] +
+                       (int64_t)col[i] * s[3];
+        };
+        // 1. inputs: every load issued before the one wait
+#pragma unroll
+        for (int k = 0; k < kMaxIn; ++k) {
+            if (k < n_in) {
+                uint8_t *dst = file + k * K * kSubBytes;
+                if (is16(P.in_ty[k])) {
+                    const uint16_t *src = static_cast<const uint16_t *>(A.in[k]);
+#pragma unroll
+                    for (int i = 0; i < kPos; ++i)
+                        __builtin_amdgcn_global_load_lds((global_addr_t)(src + off(A.in_s[k], i)),
+                                                         (lds_addr_t)(dst + (i / 4) * kSubBytes + (i % 4) * 256),
+                                                         2, 0, 0);
+                } else {
+                    const uint32_t *src = static_cast<const uint32_t *>(A.in[k]);
+#pragma unroll
+                    for (int i = 0; i < kPos; ++i)
+                        __builtin_amdgcn_global_load_lds((global_addr_t)(src + off(A.in_s[k], i)),
+                                                         (lds_addr_t)(dst + (i / 4) * kSubBytes + (i % 4) * 256),
+                                                         4, 0, 0);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        // 2. the tape
+        interp_tape<K>(P, T, file, lane_off);
+        // 3. outputs, one word per lane and access
+#pragma unroll
+        for (int k = 0; k < kMaxOut; ++k) {
+            if (k < P.n_out) {
+                const uint32_t wo = T.out[k], os = wo >> 16;
+                const uint8_t *po = file + (wo & 0xffffu) + lane * 4;
+                const bool h = is16(P.out_ty[k]);
+#pragma unroll
+                for (int i = 0; i < kPos; ++i) {
+                    const uint32_t v = *reinterpret_cast<const uint32_t *>(po + (i / 4) * os + (i % 4) * 256);
+                    if (ok[i]) {
+                        const int64_t o = off(A.out_s[k], i);
+                        if (h) static_cast<uint16_t *>(A.out[k])[o] = (uint16_t)v;
+                        else static_cast<uint32_t *>(A.out[k])[o] = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int K>
+static int launch_gather_k(int mode, const StridedArgs &A, const InterpTape &T, LaunchGeometry g, int lds,
+                           void *stream)
+{
+    const dim3 grid((unsigned)g.grid), block(64);
+    hipStream_t s = (hipStream_t)stream;
+    if (mode == 1) hipLaunchKernelGGL((k_gather_interp<K, 1>), grid, block, (unsigned)lds, s, A, T);
+    else if (mode == 2) hipLaunchKernelGGL((k_gather_interp<K, 2>), grid, block, (unsigned)lds, s, A, T);
+    else hipLaunchKernelGGL((k_gather_interp<K, 3>), grid, block, (unsigned)lds, s, A, T);
+    return (int)hipGetLastError();
+}
+
+int launch_gather_interp(int mode, int k_sub, const StridedArgs &A, const InterpTape &T, LaunchGeometry g,
+                         int lds_bytes, void *stream)
+{
+    switch (k_sub) {
+    case 4: return launch_gather_k<4>(mode, A, T, g, lds_bytes, stream);
+    case 2: return launch_gather_k<2>(mode, A, T, g, lds_bytes, stream);
+    default: return launch_gather_k<1>(mode, A, T, g, lds_bytes, stream);
+    }
+}
+
 template <int K, bool NTL, bool NTS>
 static int launch_one(bool rows, const void *args, const InterpTape &T, LaunchGeometry g, int lds, void *stream)
 {

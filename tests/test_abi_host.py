@@ -289,7 +289,7 @@ def test_geometry_rules():
         X = _t(R, C)
         Y = _t(C, R)
         p = c2.plan(X, Y.t(), 2.0, _t(R, C))
-        assert p["grid"] >= 1 and p["block"] in (256, 512)
+        assert p["grid"] >= 1 and p["block"] in ((64,) if p["path"] == "gather" else (256, 512)), p
 
 
 def test_unaligned_views_pick_slower_variants():

@@ -1,0 +1,155 @@
+"""GPU parity of the gather path's interpreter (k_gather_interp in
+kernels_interp.hip) against the oracle.
+
+Views no vector path takes: rows whose starts are off 16 bytes, strided
+columns, stride-0 broadcasts along a row, outputs with padded or strided
+rows.  Every mode of the interpreter — segments of one row, whole rows of a
+plane, whole rows over three row dimensions — with one, two and four
+sub-chunks per super-chunk (ECMD_INTERP_K), rows that end inside a segment,
+planes whose last super-chunk holds fewer rows, binary16 and bfloat16 inputs
+(2-byte direct loads to LDS) and outputs of both widths.  Row padding and
+the elements between strided columns of the outputs must stay untouched.
+The per-element kernel (ECMD_GATHER_MODE=0) runs the same cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import NPD, TD, compare, dev, host, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SPEC = [("x", ("load", "f16", 3)), ("y", ("load", "f32", 3)), ("b", ("load", "bf16", 3)),
+        ("i", ("load", "i32", 3)), ("s", ("scalar", "f32")),
+        ("xf", ("cvt", "x", "f32")), ("bf", ("cvt", "b", "f32")), ("p", ("mul", "xf", "y")),
+        ("q", ("add", "p", "bf")), ("r", ("sub", "q", "s")), ("rh", ("cvt", "r", "bf16")),
+        ("ii", ("add", "i", "i")),
+        ("o0", ("store", "r", 3)), ("o1", ("store", "rh", 3)), ("o2", ("store", "ii", 3))]
+
+# (batch, rows, n3): segments (n3 above half a super-chunk of 256 K elements),
+# whole rows of one plane (batch 1), whole rows over a batch.
+SHAPES = [(1, 37, 2100), (1, 5, 1025), (1, 3, 257), (1, 300, 6), (1, 77, 1), (1, 19, 200),
+          (3, 41, 7), (2, 9, 130), (4, 5, 600)]
+
+
+def _draw(rng, dt, shape):
+    f = (rng.standard_normal(shape) * 40).astype(np.float32)
+    if dt == "bf16":
+        return (f.view(np.uint32) >> 16).astype(np.uint16)
+    if dt == "i32":
+        return rng.integers(-(1 << 30), 1 << 30, shape, dtype=np.int32)
+    return f.astype(NPD[dt])
+
+
+def _case(shape, seed):
+    """Inputs and outputs as (host view, device view) over padded storage."""
+    B, R, C = shape
+    rng = np.random.default_rng(seed)
+    xs = _draw(rng, "f16", (B, R, C + 3))            # rows 2 (C + 3) bytes apart: off 16 bytes
+    ys = _draw(rng, "f32", (B, R, 2 * C))             # every other column
+    bs = _draw(rng, "bf16", (B, R, 1))                # one value per row (stride 0 along the row)
+    is_ = _draw(rng, "i32", (B, R + 1, C + 1))        # padded rows and a spare row per batch
+    s = np.float32(0.375)
+    hx, hy = xs[:, :, :C], ys[:, :, ::2]
+    hb = np.ascontiguousarray(np.broadcast_to(bs, (B, R, C)))
+    hi = is_[:, :R, :C]
+    ref = run_oracle(SPEC, [np.ascontiguousarray(hx), np.ascontiguousarray(hy), hb, np.ascontiguousarray(hi), s])
+    gx = to_dev(xs)[:, :, :C]
+    gy = to_dev(ys)[:, :, ::2]
+    gb = to_dev(bs).expand(B, R, C)
+    gi = to_dev(is_)[:, :R, :C]
+    return [gx, gy, gb, gi, float(s)], ref
+
+
+def _outputs(shape):
+    B, R, C = shape
+    o0s = torch.full((B, R, C + 1), float("nan"), dtype=torch.float32, device=dev())   # padded rows
+    o1s = torch.zeros((B, R, 2 * C), dtype=torch.bfloat16, device=dev())              # every other column
+    o2s = torch.full((B, R, C + 5), -7, dtype=torch.int32, device=dev())
+    return (o0s, o1s, o2s), [o0s[:, :, :C], o1s[:, :, ::2], o2s[:, :, :C]]
+
+
+def _check(shape, store, outs, ref, what):
+    B, R, C = shape
+    o0s, o1s, o2s = store
+    compare(host(outs[0]), ref[0], 0, what + " out0")
+    compare(host(outs[1]), ref[1], 0, what + " out1")
+    compare(host(outs[2]), ref[2], 0, what + " out2")
+    assert torch.isnan(o0s[:, :, C:]).all(), what + ": out0 padding written"
+    assert (o1s[:, :, 1::2].view(torch.int16) == 0).all(), what + ": out1 gaps written"
+    assert (o2s[:, :, C:] == -7).all(), what + ": out2 padding written"
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gather_interp_modes(monkeypatch, k, shape):
+    import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_INTERP_K", str(k))
+    vals, ref = _case(shape, 100 * k + sum(shape))
+    store, outs = _outputs(shape)
+    cmd = ecmd.from_spec(SPEC)
+    plan = cmd.plan(*vals, *outs)
+    B, R, C = shape
+    kk = plan["elems_per_thread"] // 4      # K, or fewer where the register file would outgrow LDS
+    want = "gather_segments" if C > 128 * kk else "gather_whole_rows"
+    assert kk <= k and plan["path"] == "gather" and plan["kernel"] == want and plan["block"] == 64, plan
+    print("    gather K=%d %s: %s grid %d" % (k, shape, plan["kernel"], plan["grid"]), flush=True)
+    cmd.launch(*vals, *outs)
+    torch.cuda.synchronize()
+    _check(shape, store, outs, ref, "gather K=%d %s" % (k, shape))
+
+
+@pytest.mark.parametrize("shape", SHAPES[:4] + SHAPES[6:7])
+def test_gather_per_element_kernel(monkeypatch, shape):
+    import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_GATHER_MODE", "0")
+    vals, ref = _case(shape, 7 + sum(shape))
+    store, outs = _outputs(shape)
+    cmd = ecmd.from_spec(SPEC)
+    plan = cmd.plan(*vals, *outs)
+    assert plan["kernel"] == "gather_generic", plan
+    cmd.launch(*vals, *outs)
+    torch.cuda.synchronize()
+    _check(shape, store, outs, ref, "per-element gather %s" % (shape,))
+
+
+@pytest.mark.parametrize("dt,bits", [("i32", 0x89ABCDEF), ("f16", 0xBC00), ("bf16", 0x7F80)])
+@pytest.mark.parametrize("shape", [(1, 50, 1000), (2, 33, 5)])
+def test_gather_fill_strided(dt, bits, shape):
+    """A Command without inputs (a scalar stored) into every other column: the
+    output entry is the uniform value's."""
+    import elementwise_tensor_commands_amd as ecmd
+    B, R, C = shape
+    spec = [("v", ("scalar", dt)), ("o", ("store", "v", 3))]
+    store = torch.zeros((B, R, 2 * C), dtype=TD[dt], device=dev())
+    out = store[:, :, ::2]
+    val = bits if dt == "i32" else -1.0 if dt == "f16" else np.uint16(bits)     # 0xBC00 is binary16 -1.0
+    cmd = ecmd.from_spec(spec)
+    plan = cmd.plan(val, out)
+    assert plan["path"] == "gather", plan
+    cmd.launch(val, out)
+    torch.cuda.synchronize()
+    h = host(store)
+    w = h.view(np.uint32) if dt == "i32" else h.view(np.uint16)
+    assert (w[:, :, ::2] == bits).all() and (w[:, :, 1::2] == 0).all()
+
+
+@pytest.mark.parametrize("n", [1, 255, 256, 257, 511, 512, 513, 100003])
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_gather_rank1_stride(monkeypatch, n, k):
+    """x[::3] - y[::2] over one row: segments with a ragged last one."""
+    import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_INTERP_K", str(k))
+    rng = np.random.default_rng(n + k)
+    xs = rng.standard_normal(3 * n).astype(np.float32)
+    ys = rng.standard_normal(2 * n).astype(np.float32)
+    spec = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("d", ("sub", "x", "y")), ("o", ("store", "d", 1))]
+    ref = run_oracle(spec, [np.ascontiguousarray(xs[::3]), np.ascontiguousarray(ys[::2])])[0]
+    out = torch.full((n,), float("nan"), device=dev())
+    cmd = ecmd.from_spec(spec)
+    gx, gy = to_dev(xs)[::3], to_dev(ys)[::2]
+    plan = cmd.plan(gx, gy, out)
+    assert plan["path"] == ("gather" if n > 1 else "linear"), plan
+    cmd.launch(gx, gy, out)
+    torch.cuda.synchronize()
+    compare(host(out), ref, 0, "rank-1 stride n=%d K=%d" % (n, k))

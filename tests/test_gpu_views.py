@@ -155,7 +155,7 @@ def test_empty_rank4_leaves_outputs_alone():
     run_views(spec, ins, outs, False, "empty")
 
 
-@pytest.mark.parametrize("seed", range(60))
+@pytest.mark.parametrize("seed", range(80))
 def test_random_views(seed):
     spec, ins, outs = random_view_case(seed)
     run_views(spec, ins, outs, False, "seed %d" % seed)

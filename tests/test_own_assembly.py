@@ -9,8 +9,8 @@
     Object Format");
   * the linear kernels move data with 128-bit global loads and stores, the
     tiled kernels go through LDS;
-  * the linear interpreter loads binary32 inputs straight into LDS and waits
-    for those loads (vmcnt 0) before it reads LDS.
+  * the interpreters load inputs straight into LDS and wait for those loads
+    (vmcnt 0) before they read LDS.
 """
 import os
 import re
@@ -109,20 +109,96 @@ def test_tiled_uses_lds():
         assert "ds_write" in body and "ds_read" in body and "s_barrier" in body, name
 
 
+def _blocks(text):
+    """Basic blocks of one kernel's assembly: [(label, lines, successors)]."""
+    blocks, cur, label = [], [], None
+    for line in text.splitlines():
+        t = line.split(";")[0].strip()
+        if not t:
+            continue
+        if t.endswith(":") and not t.startswith("."):
+            continue
+        if t.endswith(":"):
+            blocks.append([label, cur])
+            cur, label = [], t[:-1]
+            continue
+        cur.append(t)
+        if t.startswith(("s_branch", "s_cbranch", "s_endpgm", "s_setpc")):
+            blocks.append([label, cur])
+            cur, label = [], None
+    blocks.append([label, cur])
+    out = []
+    index = {b[0]: i for i, b in enumerate(blocks) if b[0]}
+    for i, (label, lines) in enumerate(blocks):
+        succ = []
+        last = lines[-1] if lines else ""
+        if last.startswith(("s_branch", "s_cbranch")):
+            succ.append(index[last.split()[1]])
+        if not last.startswith(("s_branch", "s_endpgm", "s_setpc")) and i + 1 < len(blocks):
+            succ.append(i + 1)
+        out.append((label, lines, succ))
+    return out
+
+
 def test_interp_waits_for_lds_dma():
     """Direct global-to-LDS loads are not ordered before later LDS reads by the
-    compiler: the interpreter waits for them explicitly.  In program order, no
-    ds_read may follow a global_load_lds without an s_waitcnt vmcnt(0) between."""
-    ks = _kernels(_asm("kernels_interp"))
-    assert len(ks) == 34, list(ks)     # linear and rows x K = 1, 2, 4 x nontemporal loads x stores; 5 tiled shapes x 2
-    for name, (body, _) in ks.items():
-        assert "global_load_lds_dwordx4" in body and "ds_read_b128" in body, name
-        pending = False
-        for line in body.splitlines():
-            t = line.strip()
-            if t.startswith("global_load_lds"):
-                pending = True
-            elif t.startswith("s_waitcnt") and "vmcnt(0)" in t:
-                pending = False
-            elif t.startswith("ds_read"):
-                assert not pending, "%s: LDS read before the LDS loads were waited for" % name
+    compiler: the interpreters wait for them explicitly.  On every path of the
+    control-flow graph, no ds_read follows a global_load_lds without an
+    s_waitcnt vmcnt(0) between."""
+    text = _asm("kernels_interp")
+    ks = _kernels(text)
+    # linear and rows x K = 1, 2, 4 x nontemporal loads x stores; 5 tiled shapes x 2; gather K x 3 modes
+    assert len(ks) == 43, list(ks)
+    for name in ks:
+        start = re.search(r"^%s:.*$" % name, text, re.M).end()
+        blocks = _blocks(text[start: text.find(".Lfunc_end", start)])
+        body = "\n".join("\n".join(b[1]) for b in blocks)
+        if "k_gather_interp" in name:     # one word (binary32) or one 2-byte value per lane into LDS
+            assert "global_load_lds_dword " in body and "global_load_lds_ushort" in body, name
+        else:
+            assert "global_load_lds_dwordx4" in body, name
+        assert "ds_read_b128" in body, name
+        bad = _read_before_wait(blocks)
+        assert bad is None, "%s: LDS read before the LDS loads were waited for: %s" % (name, bad)
+
+
+def _read_before_wait(blocks):
+    """Forward data flow of "a direct load may be outstanding" to a fixed
+    point; the first ds_read reached in that state, or None."""
+    pend_in = [False] * len(blocks)
+    changed = True
+    while changed:
+        changed = False
+        for i, (_, lines, succ) in enumerate(blocks):
+            pending = pend_in[i]
+            for t in lines:
+                if t.startswith("global_load_lds"):
+                    pending = True
+                elif t.startswith("s_waitcnt") and "vmcnt(0)" in t:
+                    pending = False
+                elif t.startswith("ds_read") and pending:
+                    return t
+            for j in succ:
+                if pending and not pend_in[j]:
+                    pend_in[j] = True
+                    changed = True
+    return None
+
+
+def test_wait_check_follows_branches():
+    """The check sees a read reached through a branch taken from a block laid
+    out after it, and accepts the same code with the wait on that path."""
+    bad = """
+\ts_branch .LBB0_2
+.LBB0_1:
+\tds_read_b128 v[0:3], v4
+\ts_endpgm
+.LBB0_2:
+\tglobal_load_lds_dword v[6:7], off
+\ts_cbranch_scc1 .LBB0_1
+\ts_waitcnt vmcnt(0)
+\ts_branch .LBB0_1
+"""
+    assert _read_before_wait(_blocks(bad)) == "ds_read_b128 v[0:3], v4"
+    good = bad.replace("\ts_cbranch_scc1 .LBB0_1\n", "\ts_waitcnt vmcnt(0)\n\ts_cbranch_scc1 .LBB0_1\n")
+    assert _read_before_wait(_blocks(good)) is None

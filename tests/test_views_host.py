@@ -269,7 +269,7 @@ def test_random_view_cases_reach_every_path():
     import workloads as W
     from random_commands import random_view_case
     seen = {}
-    for seed, staged in [(s, False) for s in range(60)] + [(s, True) for s in range(30)]:
+    for seed, staged in [(s, False) for s in range(80)] + [(s, True) for s in range(30)]:
         spec, ins, outs = random_view_case(seed, staged)
         vals = []
         for x in list(ins) + list(outs):
