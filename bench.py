@@ -28,7 +28,7 @@ METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, per Comm
 DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two_out": "f16/f32",
             "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32",
             "batched_transpose": "f32", "bias_nchw": "f32", "axpby_f16": "f16", "axpby_bf16": "bf16",
-            "bias_relu_f32": "f32", "transposed_relu": "f32"}
+            "bias_relu_f32": "f32", "transposed_relu": "f32", "odd_rows_f32": "f32", "narrow_rows_f32": "f32"}
 # Measured besides the five configurations: the plain copy (the bandwidth and
 # counter reference), the widened op set, the rank-3/4 views and native 16-bit
 # arithmetic, and a Command with no ahead-of-time kernel run by the interpreter
@@ -40,7 +40,8 @@ def split_workload(name):
     with its kernel compiled at run time."""
     return (name[:-4], True) if name.endswith("_jit") else (name, False)
 EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "axpby_f16", "axpby_bf16",
-         "bias_relu_f32", "bias_relu_f32_jit", "transposed_relu", "transposed_relu_jit"]
+         "bias_relu_f32", "bias_relu_f32_jit", "transposed_relu", "transposed_relu_jit", "odd_rows_f32",
+         "narrow_rows_f32"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -182,7 +183,8 @@ def cpu_baseline(wl, budget_s=20.0):
     n = full if wl != "transposed_2d" else 2048
     if wl in ("axpby_f32", "mixed_two_out", "axpby_f16", "axpby_bf16"):
         n = 1 << 24
-    shape = {"batched_transpose": (4, 2048, 2048), "bias_nchw": (2, 256, 128, 256)}.get(wl)
+    shape = {"batched_transpose": (4, 2048, 2048), "bias_nchw": (2, 256, 128, 256), "odd_rows_f32": (2048, 8191),
+             "narrow_rows_f32": (1 << 21, 6)}.get(wl)
     vals, extra = W.make_inputs(wl, n, shape=shape)
     cmd = oracle.from_spec(spec)
     # Repeat each thread count for about half the time budget (at least 3

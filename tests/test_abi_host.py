@@ -262,11 +262,14 @@ def test_commutative_operands_canonical():
                                        ("mixed_two_out", "linear_mixed_two_out"),
                                        ("transposed_2d", "tiled_add_scaled_f32"),
                                        ("batched_transpose", "tiled_add_scaled_f32"),
-                                       ("bias_nchw", "rows_affine_f32")])
+                                       ("bias_nchw", "rows_affine_f32"),
+                                       ("odd_rows_f32", "gather_segments"),
+                                       ("narrow_rows_f32", "gather_whole_rows")])
 def test_workloads_select_their_kernels(wl, kernel):
     spec = W.WORKLOADS[wl]["spec"]
     n = 1 << 12 if wl != "transposed_2d" else 256
-    small = {"batched_transpose": (3, 64, 96), "bias_nchw": (2, 8, 4, 16)}
+    small = {"batched_transpose": (3, 64, 96), "bias_nchw": (2, 8, 4, 16), "odd_rows_f32": (33, 1001),
+             "narrow_rows_f32": (1000, 6)}
     vals, extra = W.make_inputs(wl, n, shape=small.get(wl))
     n = None if wl in small else n
     tv = W.to_torch(vals, extra, "cpu")
@@ -274,7 +277,7 @@ def test_workloads_select_their_kernels(wl, kernel):
     shape = W.shape_of(wl, n, small.get(wl))
     o = [torch.empty(shape, dtype={"f16": torch.float16, "f32": torch.float32, "i32": torch.int32}[d]) for d in outs]
     plan = E.from_spec(spec).plan(*tv, *o)
-    assert plan["kernel"] == kernel and plan["specialised"] and plan["vector"]
+    assert plan["kernel"] == kernel and bool(plan["specialised"] and plan["vector"]) == (plan["path"] != "gather")
 
 
 def test_geometry_rules():

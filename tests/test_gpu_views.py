@@ -111,7 +111,7 @@ def test_batched_transpose_tiles(tile):
     assert plan["specialised"] and plan["path"] == "tiled"
 
 
-@pytest.mark.parametrize("wl", ["batched_transpose", "bias_nchw"])
+@pytest.mark.parametrize("wl", ["batched_transpose", "bias_nchw", "odd_rows_f32", "narrow_rows_f32"])
 def test_full_size_views(wl):
     """The full shapes the benchmark times, in its launch configuration,
     compared with the oracle on every element."""
@@ -128,7 +128,9 @@ def test_full_size_views(wl):
     cmd.launch(*gin, out)
     torch.cuda.synchronize()
     compare(host(out), ref[0], 0, "%s full (%s)" % (wl, plan["kernel"]))
-    assert plan["path"] == {"batched_transpose": "tiled", "bias_nchw": "rows"}[wl]
+    assert (plan["path"], plan["kernel"]) == {
+        "batched_transpose": ("tiled", "tiled_add_scaled_f32"), "bias_nchw": ("rows", "rows_affine_f32"),
+        "odd_rows_f32": ("gather", "gather_segments"), "narrow_rows_f32": ("gather", "gather_whole_rows")}[wl]
 
 
 def test_staged_direct_and_row_constant_together():

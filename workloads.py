@@ -158,6 +158,14 @@ BIAS_NCHW = [
     ("out", ("store", "o", 4)),
 ]
 
+# z = x + y over rank-2 views (the gather path's workloads below).
+ADD2_F32 = [
+    ("x", ("load", "f32", 2)),
+    ("y", ("load", "f32", 2)),
+    ("z", ("add", "x", "y")),
+    ("out", ("store", "z", 2)),
+]
+
 WORKLOADS = {
     "add_f32": dict(index=0, spec=ADD_F32, n=65536,
                     label="z = x + y, fp32, n=65536 contiguous"),
@@ -194,6 +202,13 @@ WORKLOADS = {
     "transposed_relu": dict(index=13, spec=TRANSPOSED_RELU, n=16384,
                             label="out[i,j] = max(X[i,j] + alpha*Y[j,i], 0), fp32 16384x16384, X row stride 16448 "
                                   "(no ahead-of-time kernel)"),
+    # Views no vector path takes (the gather path): rows 4 bytes off 16-byte
+    # alignment, and rows shorter than a wavefront's elements.
+    "odd_rows_f32": dict(index=14, spec=ADD2_F32, shape=(8192, 8191),
+                         label="out = x + y, fp32 8192 x 8191, x a column slice of 8192-wide rows, "
+                               "y and out contiguous (rows start 4 bytes off 16-byte alignment)"),
+    "narrow_rows_f32": dict(index=15, spec=ADD2_F32, shape=(1 << 23, 6),
+                            label="out = x + y, fp32 2^23 x 6, x in rows of 8 (row stride 8), y and out contiguous"),
 }
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
@@ -331,6 +346,13 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
         per_channel = lambda v: np.broadcast_to(v.reshape(1, -1, 1, 1), shp)
         extra = {"storage": [x, scale, bias]}
         return [x, per_channel(scale), per_channel(bias)], extra
+    elif workload in ("odd_rows_f32", "narrow_rows_f32"):
+        r, c = shape_of(workload, shape=shape)
+        xs = np.full((r, c + (1 if workload == "odd_rows_f32" else 2)), np.nan, dtype=np.float32)
+        xs[:, :c] = _uniform_pm1_f32(rng, (r, c))
+        y = _uniform_pm1_f32(rng, (r, c))
+        extra = {"storage": [xs, y]}
+        return [xs[:, :c], y], extra
     else:
         raise KeyError(workload)
     extra["storage"] = [v if isinstance(v, np.ndarray) else None for v in vals]
