@@ -63,7 +63,7 @@ struct Selection {
     bool jit = false;           // a run-time compiled kernel (variant -1 otherwise means the interpreter)
     int mask = 0;               // tiled path: staged inputs (bit k = input k)
     bool interp = false;        // linear path: the LDS-file interpreter (kernels_interp.hip)
-    int k_sub = 0, n_slot = 0;  // its sub-chunks per super-chunk and temporary slots
+    int k_sub = 0;              // its sub-chunks per super-chunk
     bool vec = false;
     LinearShape shape{4, 4, false, true};
     bool xcd_remap = false;
@@ -573,6 +573,67 @@ constexpr int64_t kInterpMaxGrid = (int64_t)1 << 20;
 
 bool aligned(const void *p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes == 0; }
 
+// Entries of the interpreters' LDS register file.  Values are the inputs
+// (0 .. n_in - 1, which keep entries 0 .. n_in - 1: the kernels load them
+// there) and the operations' results (n_in + i).  Each result takes the
+// lowest entry free at its operation: an operand's entry when the operation
+// is that operand's last use (every case of the tape walk reads a sub-chunk's
+// operands before it writes the result's sub-chunk, so in place is safe), and
+// a value no later operation or store reads frees its entry.  So the file
+// holds the values live at once, not every input and temporary slot.
+struct EntryPlan {
+    int n = 0;                          // entries in use
+    int8_t entry[kMaxIn + kMaxOps];     // entry of each value
+    int16_t op_val[kMaxOps][3];         // values an operation reads (-1: uniform or none)
+    int16_t out_val[kMaxOut];           // value each store reads (-1: uniform)
+};
+
+EntryPlan plan_entries(const Program &P)
+{
+    EntryPlan E;
+    int slot_val[kMaxSlot], last[kMaxIn + kMaxOps], holder[kMaxIn + kMaxOps];
+    std::fill(std::begin(slot_val), std::end(slot_val), -1);
+    std::fill(std::begin(last), std::end(last), -1);
+    std::fill(std::begin(holder), std::end(holder), -1);
+    std::fill(std::begin(E.entry), std::end(E.entry), (int8_t)-1);
+    auto value = [&](uint8_t r) -> int {
+        if (r == kRefNone || r >= kRefUni) return -1;
+        return r < kRefSlot ? r - kRefIn : slot_val[r - kRefSlot];
+    };
+    for (int i = 0; i < P.n_ops; ++i) {
+        const TapeOp &o = P.ops[i];
+        const uint8_t refs[3] = {o.a, o.b, o.c};
+        for (int j = 0; j < 3; ++j) {
+            const int v = value(refs[j]);
+            E.op_val[i][j] = (int16_t)v;
+            if (v >= 0) last[v] = i;
+        }
+        slot_val[o.dst - kRefSlot] = P.n_in + i;
+    }
+    for (int k = 0; k < P.n_out; ++k) {
+        const int v = value(P.out_ref[k]);
+        E.out_val[k] = (int16_t)v;
+        if (v >= 0) last[v] = P.n_ops;     // read by the stores after the tape
+    }
+    E.n = P.n_in;
+    for (int k = 0; k < P.n_in; ++k) {
+        E.entry[k] = (int8_t)k;
+        if (last[k] >= 0) holder[k] = k;
+    }
+    for (int i = 0; i < P.n_ops; ++i) {
+        for (int j = 0; j < 3; ++j) {
+            const int v = E.op_val[i][j];
+            if (v >= 0 && last[v] == i) holder[E.entry[v]] = -1;
+        }
+        int e = 0;
+        while (e < E.n && holder[e] >= 0) ++e;
+        if (e == E.n) ++E.n;
+        E.entry[P.n_in + i] = (int8_t)e;
+        holder[e] = last[P.n_in + i] >= 0 ? P.n_in + i : -1;
+    }
+    return E;
+}
+
 // The LDS-file interpreter (linear and rows paths): one wavefront per
 // work-group, one super-chunk of k_sub sub-chunks each: two sub-chunks
 // (measured fastest for binary32 and 16-bit data alike), one where the LDS
@@ -580,14 +641,11 @@ bool aligned(const void *p, int64_t bytes) { return reinterpret_cast<uintptr_t>(
 // ECMD_INTERP_K = 1, 2 or 4 overrides, for A/B runs.  The caller sets the grid.
 void size_interp(const Program &P, Selection &S)
 {
-    int n_slot = 0;
-    for (int i = 0; i < P.n_ops; ++i) n_slot = std::max(n_slot, P.ops[i].dst - (int)kRefSlot + 1);
-    const int entries = P.n_in + n_slot;
+    const int entries = plan_entries(P).n;
     int k = (int)env_int("ECMD_INTERP_K", 2);
     if (k != 1 && k != 2 && k != 4) k = 2;
     while (k > 1 && entries * k + P.n_uni > kInterpLdsKiB) k /= 2;
     S.interp = true;
-    S.n_slot = n_slot;
     S.k_sub = k;
     S.lds = (entries * k + P.n_uni) * 1024;
     S.e = 4 * k;
@@ -801,15 +859,12 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
                 }
             }
             const int k_sub = it.tm * it.tn / 4 / it.block;
-            int n_slot = 0;
-            for (int i = 0; i < P.n_ops; ++i) n_slot = std::max(n_slot, P.ops[i].dst - (int)kRefSlot + 1);
-            const int per_wave = ((P.n_in + n_slot) * k_sub + P.n_uni) * 1024;
+            const int per_wave = (plan_entries(P).n * k_sub + P.n_uni) * 1024;
             const int lds = n_staged * it.tm * it.tn * 4 + it.block / 64 * per_wave;
             const int64_t tiles = ((T.n[2] + it.tm - 1) / it.tm) * ((T.n[3] + it.tn - 1) / it.tn) * T.n[0] * T.n[1];
             if (lds <= lds_cap && tiles * it.block < kMaxGridItems && !env_flag("ECMD_TILED_RTEVAL")) {
                 S.interp = true;
                 S.k_sub = k_sub;
-                S.n_slot = n_slot;
                 S.tile = it;
                 S.lds = lds;
             }
@@ -890,25 +945,25 @@ int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int
 // then the slots', each k_sub sub-chunks of 1 KiB, then one 1 KiB broadcast
 // entry per uniform value.  Every operand reference becomes `offset | step <<
 // 16` (see InterpTape).
-void resolve_interp_tape(const Program &P, int k_sub, int n_slot, InterpTape &T)
+void resolve_interp_tape(const Program &P, int k_sub, InterpTape &T)
 {
     std::memset(&T, 0, sizeof T);
+    const EntryPlan E = plan_entries(P);
     const uint32_t sub = 1024, entry = sub * (uint32_t)k_sub;
-    T.uni_off = (uint32_t)(P.n_in + n_slot) * entry;
-    auto place = [&](uint8_t ref) -> uint32_t {
-        if (ref < kRefSlot) return (ref - kRefIn) * entry | sub << 16;
-        if (ref < kRefUni) return (uint32_t)(P.n_in + ref - kRefSlot) * entry | sub << 16;
-        return T.uni_off + (ref - kRefUni) * sub;   // step 0
+    T.uni_off = (uint32_t)E.n * entry;
+    auto place = [&](uint8_t ref, int v) -> uint32_t {
+        if (v >= 0) return (uint32_t)E.entry[v] * entry | sub << 16;
+        return T.uni_off + (ref - kRefUni) * sub;   // a uniform value: step 0
     };
     for (int i = 0; i < P.n_ops; ++i) {
         const TapeOp &o = P.ops[i];
-        const uint32_t a = place(o.a);
-        T.op[i][0] = o.code | ((place(o.dst) & 0xffffu) << 8);   // a slot's offset (its step is 1 KiB)
+        const uint32_t a = place(o.a, E.op_val[i][0]);
+        T.op[i][0] = o.code | (((uint32_t)E.entry[P.n_in + i] * entry) << 8);   // the result's entry (step 1 KiB)
         T.op[i][1] = a;
-        T.op[i][2] = o.b == kRefNone ? a : place(o.b);
-        T.op[i][3] = o.c == kRefNone ? a : place(o.c);
+        T.op[i][2] = o.b == kRefNone ? a : place(o.b, E.op_val[i][1]);
+        T.op[i][3] = o.c == kRefNone ? a : place(o.c, E.op_val[i][2]);
     }
-    for (int k = 0; k < P.n_out; ++k) T.out[k] = place(P.out_ref[k]);
+    for (int k = 0; k < P.n_out; ++k) T.out[k] = place(P.out_ref[k], E.out_val[k]);
 }
 
 // Multiplier and shifts for dividing 32-bit values by d (1 <= d < 2^31), the
@@ -1196,7 +1251,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
                                               (hipStream_t)hip_stream, params, nullptr);
         } else if (S.interp) {
             InterpTape T;
-            resolve_interp_tape(h->prog, S.k_sub, S.n_slot, T);
+            resolve_interp_tape(h->prog, S.k_sub, T);
             herr = launch_linear_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds, hip_stream);
         } else {
             herr = launch_linear(S.variant, S.vec, S.shape, A, g, hip_stream);
@@ -1215,7 +1270,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
                                               (hipStream_t)hip_stream, params, nullptr);
         } else {
             InterpTape T;
-            if (S.interp) resolve_interp_tape(h->prog, S.k_sub, S.n_slot, T);
+            if (S.interp) resolve_interp_tape(h->prog, S.k_sub, T);
             herr = S.path == CMD_PATH_TILED
                        ? (S.interp ? launch_tiled_interp(S.tile, nt, A, T, g, S.lds, hip_stream)
                                    : launch_tiled(S.variant, nt, S.tile, A, g, hip_stream))
@@ -1275,6 +1330,30 @@ int64_t cmd_dump(cmd_t h, char *buf, int64_t cap)
     for (int k = 0; k < P.n_out; ++k) {
         std::snprintf(line, sizeof line, "store.%s arg%d <- %s\n", dtype_name(P.out_ty[k]), h->out_arg[k],
                       refname(P.out_ref[k]).c_str());
+        s += line;
+    }
+    // The same program over the interpreters' LDS register file (entry eN;
+    // input k starts in entry k).
+    const EntryPlan E = plan_entries(P);
+    auto ename = [&](uint8_t ref, int v) -> std::string {
+        char b[16];
+        if (v >= 0) std::snprintf(b, sizeof b, "e%d", E.entry[v]);
+        else return refname(ref);
+        return b;
+    };
+    std::snprintf(line, sizeof line, "lds entries %d\n", E.n);
+    s += line;
+    for (int i = 0; i < P.n_ops; ++i) {
+        const TapeOp &o = P.ops[i];
+        std::string t = "lds e" + std::to_string(E.entry[P.n_in + i]) + " = " + code_name(o.code) + " " +
+                        ename(o.a, E.op_val[i][0]);
+        if (o.b != kRefNone) t += ", " + ename(o.b, E.op_val[i][1]);
+        if (o.c != kRefNone) t += ", " + ename(o.c, E.op_val[i][2]);
+        s += t + "\n";
+    }
+    for (int k = 0; k < P.n_out; ++k) {
+        std::snprintf(line, sizeof line, "lds store.%s arg%d <- %s\n", dtype_name(P.out_ty[k]), h->out_arg[k],
+                      ename(P.out_ref[k], E.out_val[k]).c_str());
         s += line;
     }
     if (buf && cap > 0) {

@@ -344,7 +344,10 @@ def _minmax_zero_fix(A, B, r, is_min, zero):
     return np.where(z, np.where(neg, -zero, zero), r)
 
 
-def _emulate(listing, ins, uni, n):
+def _emulate(listing, ins, uni, n, lds=False):
+    """Runs the listing (or, with lds, its form over the interpreters' LDS
+    entries: input k starts in entry k, results go where the host placed
+    them) with NumPy arithmetic and returns the stored values."""
     regs = {}
     outs = []
     f16 = np.float16
@@ -354,11 +357,14 @@ def _emulate(listing, ins, uni, n):
         r = np.where(np.isnan(a), 0, np.clip(np.trunc(np.nan_to_num(a)), -2**31, 2**31 - 1))
         return r.astype(np.int64).astype(np.int32)
     for k, v in enumerate(ins):
-        regs["in%d" % k] = v
+        regs[("e%d" if lds else "in%d") % k] = v
     for k, v in enumerate(uni):
         regs["u%d" % k] = np.full(n, v)
     for line in listing.splitlines():
-        m = re.match(r"(s\d+) = (\S+) (\S+?)(?:, (\S+?))?(?:, (\S+))?$", line)
+        if line.startswith("lds ") != lds:
+            continue
+        line = line[4:] if lds else line
+        m = re.match(r"([se]\d+) = (\S+) (\S+?)(?:, (\S+?))?(?:, (\S+))?$", line)
         if m:
             dst, op, a, b, c = m.groups()
             A = regs[a]
@@ -436,15 +442,22 @@ def test_lowered_listing_matches_oracle(oracle_mod, seed):
     u_args = [int(a) for a in re.findall(r"u\d+ = scalar\.\S+ arg(\d+)", listing)]
     ins = [vals[a] for a in in_args]
     uni = [vals[a] for a in u_args]
-    got = _emulate(listing, ins, uni, n)
-    for k, (g, r) in enumerate(zip(got, ref)):
-        g = np.asarray(g).astype(r.dtype) if np.asarray(g).dtype != r.dtype else g
-        gb = g.view(np.uint16 if r.itemsize == 2 else np.uint32)
-        rb = r.view(np.uint16 if r.itemsize == 2 else np.uint32)
-        if r.dtype.kind == "f":
-            ok = (gb == rb) | (np.isnan(g) & np.isnan(r))
-        elif r.dtype == np.uint16:          # bfloat16 bit patterns: any NaN equals any NaN
-            ok = (gb == rb) | (np.isnan(_bf_vals(gb)) & np.isnan(_bf_vals(rb)))
-        else:
-            ok = gb == rb
-        assert ok.all(), "seed %d out%d\n%s" % (seed, k, listing)
+    # the listing, then the same program over the interpreters' LDS entries
+    for lds in (False, True):
+        got = _emulate(listing, ins, uni, n, lds)
+        assert len(got) == len(ref)
+        for k, (g, r) in enumerate(zip(got, ref)):
+            g = np.asarray(g).astype(r.dtype) if np.asarray(g).dtype != r.dtype else g
+            gb = g.view(np.uint16 if r.itemsize == 2 else np.uint32)
+            rb = r.view(np.uint16 if r.itemsize == 2 else np.uint32)
+            if r.dtype.kind == "f":
+                ok = (gb == rb) | (np.isnan(g) & np.isnan(r))
+            elif r.dtype == np.uint16:          # bfloat16 bit patterns: any NaN equals any NaN
+                ok = (gb == rb) | (np.isnan(_bf_vals(gb)) & np.isnan(_bf_vals(rb)))
+            else:
+                ok = gb == rb
+            assert ok.all(), "seed %d out%d (lds %s)\n%s" % (seed, k, lds, listing)
+    # entries in use: at most the live values, never more than inputs plus slots
+    n_ent = int(re.search(r"^lds entries (\d+)$", listing, re.M).group(1))
+    n_slot = len({m for m in re.findall(r"^(s\d+) = ", listing, re.M)})
+    assert n_ent <= len(ins) + n_slot, listing
