@@ -64,9 +64,10 @@ def test_random_commands_each_sub_chunk_count(monkeypatch, k, seed):
 
 def test_large_register_file():
     """t_i = x_i * s_i for six inputs and six scalars, two more temporaries, all
-    eight live at once, then summed (6 + 6 + 2 = 14 CommandArguments of the 16):
-    14 entries of inputs and slots plus 6 uniform entries, which the host fits
-    in LDS with one sub-chunk (20 KiB)."""
+    eight live at once, then summed (6 + 6 + 2 = 14 CommandArguments of the 16).
+    At most ten values are live at once (x0..x3 stay live for t6 and t7 while
+    t0..t3 are made; t4, t5 take the entries of x4, x5): ten entries plus six
+    uniform entries, which the host fits in LDS with one sub-chunk (16 KiB)."""
     spec = [("x%d" % i, ("load", "f32", 1)) for i in range(6)]
     spec += [("s%d" % i, ("scalar", "f32")) for i in range(6)]
     spec += [("t%d" % i, ("mul", "x%d" % i, "s%d" % i)) for i in range(6)]
@@ -81,7 +82,7 @@ def test_large_register_file():
     vals = [rng.standard_normal(n).astype(np.float32) for _ in range(6)]
     vals += [np.float32(rng.standard_normal()) for _ in range(6)]
     plan = _run_interp(spec, vals, n, "six inputs, six scalars, eight slots")
-    assert plan["elems_per_thread"] == 4 and plan["lds_bytes"] == (14 + 6) * 1024, plan
+    assert plan["elems_per_thread"] == 4 and plan["lds_bytes"] == (10 + 6) * 1024, plan
 
 
 @pytest.mark.parametrize("dt,val", [("i32", -123456789), ("f16", -0.0), ("bf16", np.uint16(0x7F80))])
