@@ -859,8 +859,8 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
                 }
             }
             const int k_sub = it.tm * it.tn / 4 / it.block;
-            const int per_wave = (plan_entries(P).n * k_sub + P.n_uni) * 1024;
-            const int lds = n_staged * it.tm * it.tn * 4 + it.block / 64 * per_wave;
+            const int lds = n_staged * it.tm * it.tn * 4 + P.n_uni * 1024 +
+                            it.block / 64 * plan_entries(P).n * k_sub * 1024;
             const int64_t tiles = ((T.n[2] + it.tm - 1) / it.tm) * ((T.n[3] + it.tn - 1) / it.tn) * T.n[0] * T.n[1];
             if (lds <= lds_cap && tiles * it.block < kMaxGridItems && !env_flag("ECMD_TILED_RTEVAL")) {
                 S.interp = true;
@@ -953,7 +953,7 @@ void resolve_interp_tape(const Program &P, int k_sub, InterpTape &T)
     T.uni_off = (uint32_t)E.n * entry;
     auto place = [&](uint8_t ref, int v) -> uint32_t {
         if (v >= 0) return (uint32_t)E.entry[v] * entry | sub << 16;
-        return T.uni_off + (ref - kRefUni) * sub;   // a uniform value: step 0
+        return (ref - kRefUni) * sub;   // a uniform value: step 0, from the uniform entries' start
     };
     for (int i = 0; i < P.n_ops; ++i) {
         const TapeOp &o = P.ops[i];

@@ -328,11 +328,14 @@ int launch_linear(int variant, bool vec, LinearShape shape, const LinearArgs &A,
 // in that file, so the kernel decodes an operation with one scalar load and no
 // arithmetic: a reference is `offset | step << 16`, the byte offset of its
 // first 1 KiB sub-chunk entry and the step between sub-chunks (0 for a
-// uniform value's single broadcast entry).
+// uniform value's single broadcast entry).  Offsets of entries count from the
+// wavefront's first entry, offsets of uniform values from the first uniform
+// entry (after the wavefront's entries; on the tiled path shared by the
+// work-group's wavefronts).
 struct InterpTape {
     uint32_t op[kMaxOps][4];   // code | dst offset << 8; a; b; c (b and c repeat a when unused)
     uint32_t out[kMaxOut];     // each output's value
-    uint32_t uni_off;          // byte offset of the uniform values' broadcast entries
+    uint32_t uni_off;          // bytes of a wavefront's entries
 };
 // One wavefront per work-group, k_sub (1, 2 or 4) sub-chunks of 256 elements
 // per super-chunk, an LDS register file of lds_bytes.

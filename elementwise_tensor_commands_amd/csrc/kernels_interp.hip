@@ -46,28 +46,36 @@ typedef __attribute__((address_space(1))) void *global_addr_t;
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kSubBytes = 64 * 16;   // one entry of one sub-chunk: 64 lanes x 16 bytes
 
-// Broadcast entries of the uniform values (after the inputs' and slots').
-__device__ __forceinline__ void interp_uniforms(const Program &P, const uint32_t *uni, const InterpTape &T,
-                                                uint8_t *file, int lane_off)
+// Broadcast entries of the uniform values, from `uni` on (after a wavefront's
+// entries; on the tiled path shared by the work-group's wavefronts).
+__device__ __forceinline__ void interp_uniforms(const Program &P, const uint32_t *vals, uint8_t *uni, int lane_off)
 {
 #pragma unroll
     for (int u = 0; u < kMaxUni; ++u) {
         if (u < P.n_uni) {
-            const uint32_t x = uni[u];
-            *reinterpret_cast<u32x4 *>(file + T.uni_off + u * kSubBytes + lane_off) = u32x4{x, x, x, x};
+            const uint32_t x = vals[u];
+            *reinterpret_cast<u32x4 *>(uni + u * kSubBytes + lane_off) = u32x4{x, x, x, x};
         }
     }
 }
 
+// A value's first sub-chunk in the file: an entry (step 1 KiB) relative to
+// the wavefront's entries, a uniform value (step 0) relative to `uni`.
+__device__ __forceinline__ const uint8_t *interp_at(uint32_t w, const uint8_t *file, const uint8_t *uni, int lane_off)
+{
+    return ((w >> 16) ? file : uni) + (w & 0xffffu) + lane_off;
+}
+
 // Walks the tape once over the K sub-chunks of the wavefront's file.
 template <int K>
-__device__ __forceinline__ void interp_tape(const Program &P, const InterpTape &T, uint8_t *file, int lane_off)
+__device__ __forceinline__ void interp_tape(const Program &P, const InterpTape &T, uint8_t *file, const uint8_t *uni,
+                                            int lane_off)
 {
     const int n_ops = P.n_ops;
     for (int i = 0; i < n_ops; ++i) {
         const uint32_t w0 = T.op[i][0], wa = T.op[i][1], wb = T.op[i][2], wc = T.op[i][3];
-        const uint8_t *pa = file + (wa & 0xffffu) + lane_off, *pb = file + (wb & 0xffffu) + lane_off;
-        const uint8_t *pc = file + (wc & 0xffffu) + lane_off;
+        const uint8_t *pa = interp_at(wa, file, uni, lane_off), *pb = interp_at(wb, file, uni, lane_off);
+        const uint8_t *pc = interp_at(wc, file, uni, lane_off);
         const uint32_t as = wa >> 16, bs = wb >> 16, cs = wc >> 16;
         uint8_t *pd = file + (w0 >> 8) + lane_off;
         switch (w0 & 0xffu) {
@@ -119,7 +127,8 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
     const Program &P = A.prog;
     const int n_in = P.n_in;
     const int lane_off = lane * 16;
-    interp_uniforms(P, A.uni, T, file, lane_off);
+    uint8_t *uni = file + T.uni_off;
+    interp_uniforms(P, A.uni, uni, lane_off);
     constexpr int kSuper = K * 256;
     const int64_t nsup = A.n / kSuper;
     for (int64_t c = blockIdx.x; c < nsup; c += gridDim.x) {
@@ -154,13 +163,13 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         // 2. the tape, once per super-chunk
-        interp_tape<K>(P, T, file, lane_off);
+        interp_tape<K>(P, T, file, uni, lane_off);
         // 3. outputs
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < P.n_out) {
                 const uint32_t wo = T.out[k], os = wo >> 16;
-                const uint8_t *po = file + (wo & 0xffffu) + lane_off;
+                const uint8_t *po = interp_at(wo, file, uni, lane_off);
 #pragma unroll
                 for (int j = 0; j < K; ++j)
                     store_vec<NTS>(A.out[k], P.out_ty[k], base + j * 256,
@@ -304,14 +313,15 @@ __device__ __forceinline__ void rows_interp_body(const StridedArgs &A, const Int
             }
         }
         // 2. the tape
-        interp_tape<K>(P, T, file, lane_off);
+        const uint8_t *uni = file + T.uni_off;
+        interp_tape<K>(P, T, file, uni, lane_off);
         // 3. outputs
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < P.n_out) {
                 const uint8_t ty = P.out_ty[k];
                 const uint32_t wo = T.out[k], os = wo >> 16;
-                const uint8_t *po = file + (wo & 0xffffu) + lane_off;
+                const uint8_t *po = interp_at(wo, file, uni, lane_off);
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
                     const u32x4 o = *reinterpret_cast<const u32x4 *>(po + j * os);
@@ -332,7 +342,7 @@ template <int K, bool NTL, bool NTS>
 __global__ __launch_bounds__(64) void k_rows_interp(const StridedArgs A, const InterpTape T)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t file[];
-    interp_uniforms(A.prog, A.uni, T, file, threadIdx.x * 16);
+    interp_uniforms(A.prog, A.uni, file + T.uni_off, threadIdx.x * 16);
     if (A.wave_in_row) rows_interp_body<K, NTL, NTS, true>(A, T, file);
     else rows_interp_body<K, NTL, NTS, false>(A, T, file);
 }
@@ -369,8 +379,11 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
 #pragma unroll
     for (int k = 0; k < kMaxIn; ++k) n_staged += (k < n_in && A.in_staged[k]) ? 1 : 0;
     uint32_t *stage = reinterpret_cast<uint32_t *>(lds);
-    uint8_t *file = lds + n_staged * TM * TN * 4 + (t >> 6) * (T.uni_off + P.n_uni * kSubBytes);
-    interp_uniforms(P, A.uni, T, file, lane_off);
+    // the staging tiles, the uniform values' entries (shared by the
+    // wavefronts, written by the first), then each wavefront's entries
+    uint8_t *uni = lds + n_staged * TM * TN * 4;
+    uint8_t *file = uni + P.n_uni * kSubBytes + (t >> 6) * T.uni_off;
+    if (t < 64) interp_uniforms(P, A.uni, uni, lane_off);
 
     // Plane and tile coordinates, row by row (as the tiled kernel without a walk).
     const uint32_t tiles_c = (uint32_t)A.tiles_c, tiles_r = (uint32_t)A.tiles_r;
@@ -492,13 +505,13 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
         }
     }
     // 4. The tape, and the outputs.
-    interp_tape<K>(P, T, file, lane_off);
+    interp_tape<K>(P, T, file, uni, lane_off);
 #pragma unroll
     for (int k = 0; k < kMaxOut; ++k) {
         if (k < P.n_out) {
             const uint8_t ty = P.out_ty[k];
             const uint32_t wo = T.out[k], os = wo >> 16;
-            const uint8_t *po = file + (wo & 0xffffu) + lane_off;
+            const uint8_t *po = interp_at(wo, file, uni, lane_off);
 #pragma unroll
             for (int p = 0; p < K; ++p) {
                 const u32x4 o = *reinterpret_cast<const u32x4 *>(po + p * os);
@@ -573,7 +586,8 @@ __global__ __launch_bounds__(64) void k_gather_interp(const StridedArgs A, const
     const Program &P = A.prog;
     const int n_in = P.n_in;
     const int lane_off = lane * 16;
-    interp_uniforms(P, A.uni, T, file, lane_off);
+    uint8_t *uni = file + T.uni_off;
+    interp_uniforms(P, A.uni, uni, lane_off);
     constexpr int kPos = 4 * K;   // positions per lane: access d of sub-chunk j is position 4 j + d
     for (uint32_t w = blockIdx.x; w < A.g_waves; w += gridDim.x) {
         uint32_t col[kPos], rq[MODE == 1 ? 1 : kPos], rb0[MODE == 3 ? kPos : 1], rb1[MODE == 3 ? kPos : 1];
@@ -648,13 +662,13 @@ __global__ __launch_bounds__(64) void k_gather_interp(const StridedArgs A, const
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         // 2. the tape
-        interp_tape<K>(P, T, file, lane_off);
+        interp_tape<K>(P, T, file, uni, lane_off);
         // 3. outputs, one word per lane and access
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < P.n_out) {
                 const uint32_t wo = T.out[k], os = wo >> 16;
-                const uint8_t *po = file + (wo & 0xffffu) + lane * 4;
+                const uint8_t *po = interp_at(wo, file, uni, lane * 4);
                 const bool h = is16(P.out_ty[k]);
 #pragma unroll
                 for (int i = 0; i < kPos; ++i) {
