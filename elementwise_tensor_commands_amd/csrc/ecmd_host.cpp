@@ -858,11 +858,16 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
                         it = TileShape{a, b, c}, lds_cap = 160 * 1024;
                 }
             }
+            // LDS: one region of TM TN 4 bytes per entry (every wavefront's
+            // sub-chunks of it; a staged input is staged in its own entry's
+            // region), then the shared uniform entries.  Entry offsets are
+            // 16-bit, so the regions stay within 64 KiB.
             const int k_sub = it.tm * it.tn / 4 / it.block;
-            const int lds = n_staged * it.tm * it.tn * 4 + P.n_uni * 1024 +
-                            it.block / 64 * plan_entries(P).n * k_sub * 1024;
+            const int regions = plan_entries(P).n * it.tm * it.tn * 4;
+            const int lds = regions + P.n_uni * 1024;
             const int64_t tiles = ((T.n[2] + it.tm - 1) / it.tm) * ((T.n[3] + it.tn - 1) / it.tn) * T.n[0] * T.n[1];
-            if (lds <= lds_cap && tiles * it.block < kMaxGridItems && !env_flag("ECMD_TILED_RTEVAL")) {
+            if (lds <= lds_cap && regions <= 65536 && tiles * it.block < kMaxGridItems &&
+                !env_flag("ECMD_TILED_RTEVAL")) {
                 S.interp = true;
                 S.k_sub = k_sub;
                 S.tile = it;
@@ -945,11 +950,13 @@ int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int
 // then the slots', each k_sub sub-chunks of 1 KiB, then one 1 KiB broadcast
 // entry per uniform value.  Every operand reference becomes `offset | step <<
 // 16` (see InterpTape).
-void resolve_interp_tape(const Program &P, int k_sub, InterpTape &T)
+// entry_bytes: distance between a wavefront's entries (0: K sub-chunks, one
+// wavefront's file; the tiled interpreter passes its entry regions' size).
+void resolve_interp_tape(const Program &P, int k_sub, InterpTape &T, uint32_t entry_bytes = 0)
 {
     std::memset(&T, 0, sizeof T);
     const EntryPlan E = plan_entries(P);
-    const uint32_t sub = 1024, entry = sub * (uint32_t)k_sub;
+    const uint32_t sub = 1024, entry = entry_bytes ? entry_bytes : sub * (uint32_t)k_sub;
     T.uni_off = (uint32_t)E.n * entry;
     auto place = [&](uint8_t ref, int v) -> uint32_t {
         if (v >= 0) return (uint32_t)E.entry[v] * entry | sub << 16;
@@ -1270,7 +1277,9 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
                                               (hipStream_t)hip_stream, params, nullptr);
         } else {
             InterpTape T;
-            if (S.interp) resolve_interp_tape(h->prog, S.k_sub, T);
+            if (S.interp)
+                resolve_interp_tape(h->prog, S.k_sub, T,
+                                    S.path == CMD_PATH_TILED ? (uint32_t)(S.tile.tm * S.tile.tn * 4) : 0u);
             herr = S.path == CMD_PATH_TILED
                        ? (S.interp ? launch_tiled_interp(S.tile, nt, A, T, g, S.lds, hip_stream)
                                    : launch_tiled(S.variant, nt, S.tile, A, g, hip_stream))

@@ -360,11 +360,17 @@ __global__ __launch_bounds__(64) void k_rows_interp(const StridedArgs A, const I
 //      edge tiles, are loaded element by element through registers.
 //   2. One wait and one barrier (the staging tile is shared by the
 //      work-group).
-//   3. Staged inputs are copied from the staging tile into their entries
-//      (4 LDS reads per chunk), 16-bit direct inputs widened in place.
+//   3. Staged inputs are read from the staging tile (4 LDS reads per chunk)
+//      into registers, a second barrier, and written to their entries; 16-bit
+//      direct inputs are widened in place.
 //   4. The tape is walked, and each output is stored from its entry.
-// LDS: the staging tiles (n_staged TM TN words), then one register file per
-// wavefront.
+// LDS, entry by entry: entry e of every wavefront's file forms one region of
+// TB / 64 x K x 1 KiB = TM TN 4 bytes (wavefront w's K sub-chunks at
+// w K KiB), the size of a staging tile; a staged input k is staged in its
+// own entry's region, which its entries then overwrite (hence the second
+// barrier).  The uniform values' broadcast entries follow, shared by the
+// work-group's wavefronts.  The host places entry e at e TM TN 4 bytes from
+// the wavefront's first sub-chunk.
 template <int TM, int TN, int TB, bool NT>
 __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const InterpTape T)
 {
@@ -375,14 +381,9 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
     const int n_in = P.n_in;
     const int t = threadIdx.x, lane = t & 63;
     const int lane_off = lane * 16;
-    int n_staged = 0;
-#pragma unroll
-    for (int k = 0; k < kMaxIn; ++k) n_staged += (k < n_in && A.in_staged[k]) ? 1 : 0;
-    uint32_t *stage = reinterpret_cast<uint32_t *>(lds);
-    // the staging tiles, the uniform values' entries (shared by the
-    // wavefronts, written by the first), then each wavefront's entries
-    uint8_t *uni = lds + n_staged * TM * TN * 4;
-    uint8_t *file = uni + P.n_uni * kSubBytes + (t >> 6) * T.uni_off;
+    constexpr int kRegion = TM * TN * 4;   // one entry of all wavefronts = one staging tile
+    uint8_t *uni = lds + T.uni_off;
+    uint8_t *file = lds + (t >> 6) * K * kSubBytes;
     if (t < 64) interp_uniforms(P, A.uni, uni, lane_off);
 
     // Plane and tile coordinates, row by row (as the tiled kernel without a walk).
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
             if (k < n_in && !A.in_staged[k] && !A.in_rowconst[k]) {
-                uint8_t *dst = file + k * K * kSubBytes;
+                uint8_t *dst = file + k * kRegion;
 #pragma unroll
                 for (int p = 0; p < K; ++p) {
                     const int64_t off = in_base(k) + (r0 + rl[p]) * A.in_s[k][2] + c0 + cl[p];
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
     for (int k = 0; k < kMaxIn; ++k) {
         if (k < n_in && A.in_staged[k]) {
             const uint8_t ty = P.in_ty[k];
-            uint32_t *dst = stage + (A.in_staged[k] - 1) * TM * TN;
+            uint32_t *dst = reinterpret_cast<uint32_t *>(lds + k * kRegion);
 #pragma unroll
             for (int p = 0; p < K; ++p) {
                 int sc, sr;
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
     for (int k = 0; k < kMaxIn; ++k) {
         if (k < n_in && !A.in_staged[k] && (A.in_rowconst[k] || !full)) {
             const uint8_t ty = P.in_ty[k];
-            uint8_t *dst = file + k * K * kSubBytes + lane_off;
+            uint8_t *dst = file + k * kRegion + lane_off;
 #pragma unroll
             for (int p = 0; p < K; ++p) {
                 const int64_t row = in_base(k) + (r0 + rl[p]) * A.in_s[k][2];
@@ -478,23 +479,45 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
     // 2. The loads to LDS have landed and every wavefront has staged its part.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    // 3. Staged inputs into their entries; 16-bit direct inputs widened.
+    // 3. Staged inputs (at most three; ks[s] is the input staged s-th): every
+    // wavefront reads its chunks from the staging tiles, then (all reads
+    // done) writes them into the entries that overlay those tiles; 16-bit
+    // direct inputs widened in place.
+    int ks[3] = {-1, -1, -1};
 #pragma unroll
     for (int k = 0; k < kMaxIn; ++k) {
-        if (k >= n_in) continue;
-        uint8_t *ent = file + k * K * kSubBytes;
-        if (A.in_staged[k]) {
-            const uint32_t *src = stage + (A.in_staged[k] - 1) * TM * TN;
+        const int st = k < n_in ? A.in_staged[k] : 0;
+        ks[0] = st == 1 ? k : ks[0];
+        ks[1] = st == 2 ? k : ks[1];
+        ks[2] = st == 3 ? k : ks[2];
+    }
+    u32x4 sv[3][K];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        if (ks[q] >= 0) {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(lds + ks[q] * kRegion);
 #pragma unroll
             for (int p = 0; p < K; ++p) {
-                u32x4 v;
-                v.x = src[tile_word(TM, cl[p] + 0, rl[p])];
-                v.y = src[tile_word(TM, cl[p] + 1, rl[p])];
-                v.z = src[tile_word(TM, cl[p] + 2, rl[p])];
-                v.w = src[tile_word(TM, cl[p] + 3, rl[p])];
-                *reinterpret_cast<u32x4 *>(ent + p * kSubBytes + lane_off) = v;
+                sv[q][p].x = src[tile_word(TM, cl[p] + 0, rl[p])];
+                sv[q][p].y = src[tile_word(TM, cl[p] + 1, rl[p])];
+                sv[q][p].z = src[tile_word(TM, cl[p] + 2, rl[p])];
+                sv[q][p].w = src[tile_word(TM, cl[p] + 3, rl[p])];
             }
-        } else if (full && !A.in_rowconst[k] && is16(P.in_ty[k])) {
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        if (ks[q] >= 0) {
+            uint8_t *ent = file + ks[q] * kRegion + lane_off;
+#pragma unroll
+            for (int p = 0; p < K; ++p) *reinterpret_cast<u32x4 *>(ent + p * kSubBytes) = sv[q][p];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) {
+        if (k < n_in && !A.in_staged[k] && full && !A.in_rowconst[k] && is16(P.in_ty[k])) {
+            uint8_t *ent = file + k * kRegion;
 #pragma unroll
             for (int p = 0; p < K; ++p) {
                 uint8_t *e = ent + p * kSubBytes;

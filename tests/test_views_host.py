@@ -186,9 +186,10 @@ def test_four_staged_inputs_gather():
             ("u", ("add", "s", "t")), ("out", ("store", "u", 2))]
     tr = lambda: T((64, 64), (1, 64))
     p = E.from_spec(spec).plan(tr(), tr(), tr(), T((64, 64)), T((64, 64)))
-    # the tiled interpreter: three 32 x 64 staging tiles and, per wavefront, four
-    # entries (the four inputs; s, t and u reuse theirs) of two 1 KiB sub-chunks
-    assert p["path"] == "tiled" and p["lds_bytes"] == 3 * 32 * 64 * 4 + 4 * 4 * 2 * 1024, p
+    # the tiled interpreter: four entries (the four inputs; s, t and u reuse
+    # theirs), each a 32 x 64 x 4-byte region holding every wavefront's two
+    # 1 KiB sub-chunks; the three staged inputs are staged in their own regions
+    assert p["path"] == "tiled" and p["lds_bytes"] == 4 * 32 * 64 * 4, p
     p = E.from_spec(spec).plan(tr(), tr(), tr(), tr(), T((64, 64)))
     assert p["path"] == "gather"
 
