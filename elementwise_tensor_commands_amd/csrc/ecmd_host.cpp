@@ -634,16 +634,17 @@ EntryPlan plan_entries(const Program &P)
     return E;
 }
 
-// The LDS-file interpreter (linear and rows paths): one wavefront per
-// work-group, one super-chunk of k_sub sub-chunks each: two sub-chunks
-// (measured fastest for binary32 and 16-bit data alike), one where the LDS
-// register file would pass kInterpLdsKiB (fewer work-groups would fit a CU).
-// ECMD_INTERP_K = 1, 2 or 4 overrides, for A/B runs.  The caller sets the grid.
+// The LDS-file interpreter (linear, rows and gather paths): one wavefront per
+// work-group, one super-chunk of k_sub sub-chunks each: four sub-chunks while
+// the register file fits 12 KiB, two while it fits kInterpLdsKiB, else one
+// (more bytes per wavefront against fewer wavefronts per CU: measured
+// best on every workload tried).  ECMD_INTERP_K = 1, 2 or 4 overrides (within
+// kInterpLdsKiB), for A/B runs.  The caller sets the grid.
 void size_interp(const Program &P, Selection &S)
 {
     const int entries = plan_entries(P).n;
-    int k = (int)env_int("ECMD_INTERP_K", 2);
-    if (k != 1 && k != 2 && k != 4) k = 2;
+    int k = (int)env_int("ECMD_INTERP_K", 0);
+    if (k != 1 && k != 2 && k != 4) k = entries * 4 + P.n_uni <= 12 ? 4 : 2;
     while (k > 1 && entries * k + P.n_uni > kInterpLdsKiB) k /= 2;
     S.interp = true;
     S.k_sub = k;

@@ -58,7 +58,9 @@ def test_flat_views_off_16_bytes_take_gather_segments():
     b = torch.zeros(4097)
     add1 = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("r", ("add", "x", "y")), ("o", ("store", "r", 1))]
     plan = E.from_spec(add1).plan(b[1:], b[:4096], torch.zeros(4096))
-    assert plan["path"] == "gather" and plan["kernel"] == "gather_segments" and plan["grid"] == 8, plan
+    # x, y in two entries of four sub-chunks (K = 4): super-chunks of 1024 elements
+    assert plan["path"] == "gather" and plan["kernel"] == "gather_segments" and plan["grid"] == 4, plan
+    assert plan["elems_per_thread"] == 16 and plan["lds_bytes"] == 2 * 4 * 1024, plan
 
 
 def test_per_element_kernel_on_request(monkeypatch):

@@ -61,8 +61,8 @@ def _release():
 def test_linear_past_the_dispatch_limit(name, specialised):
     """2^33 + 4099 elements.  Specialised kernel: 2^25 + 16 wavefront chunks
     of 256 elements, the grid capped at 2^23 work-groups (2^31 work-items), 3
-    elements of tail.  Interpreter: 2^24 + 8 super-chunks of 512 elements over
-    2^20 work-groups (16 or 17 each), 3 elements of tail."""
+    elements of tail.  Interpreter: 2^23 + 4 super-chunks of 1024 elements
+    (four sub-chunks) over 2^20 work-groups (8 or 9 each), 3 elements of tail."""
     import elementwise_tensor_commands_amd as ecmd
     n = (1 << 33) + 4099
     f32 = name == "add_f32"
