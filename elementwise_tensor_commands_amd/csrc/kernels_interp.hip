@@ -10,11 +10,12 @@
 // uniform value.  Work goes in super-chunks of K x 256 elements per wavefront
 // (lane l holds elements 4l..4l+3 of each 256-element sub-chunk, so every
 // global access of a wavefront is one contiguous 1 KiB run):
-//   1. binary32 / int32 inputs are copied from global memory straight into
-//      their LDS entries by the direct global-to-LDS loads of gfx950 (no
-//      vector registers in between); binary16 / bfloat16 inputs are loaded as
-//      8-byte vectors and widened to 32-bit slots on the way in; all loads of
-//      a super-chunk are issued before the first is waited for;
+//   1. inputs are copied from global memory straight into their LDS entries
+//      by the direct global-to-LDS loads of gfx950 (no vector registers in
+//      between): binary32 / int32 16 bytes per lane, binary16 / bfloat16 2
+//      bytes per lane and access (gfx950 writes one zero-extended word per
+//      lane, so they arrive widened); all loads of a super-chunk are issued
+//      before the first is waited for;
 //   2. one wait for those loads, then the tape is walked once: each operation
 //      is decoded once per super-chunk (one scalar load of its 16 bytes, the
 //      operands already resolved to LDS offsets by the host, see InterpTape;
@@ -133,32 +134,31 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
     const int64_t nsup = A.n / kSuper;
     for (int64_t c = blockIdx.x; c < nsup; c += gridDim.x) {
         const int64_t base = c * kSuper + lane * 4;
-        // 1. inputs into their entries: every load is issued before any is
-        // waited for (16-bit inputs pass through registers to be widened).
-        u32x2 h16[kMaxIn][K];
+        // 1. inputs into their entries, every load issued before the one
+        // wait.  Word q of an entry's sub-chunk holds the sub-chunk's element
+        // q: a binary32 input as 16 bytes per lane (elements 4l .. 4l + 3 at
+        // word 4l), a 16-bit input by four 2-byte loads per sub-chunk (access
+        // d: element 64 d + l, written zero-extended at word 64 d + l).
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
             if (k < n_in) {
+                uint8_t *dst = file + k * K * kSubBytes;
                 if (is16(P.in_ty[k])) {
-                    const uint16_t *src = static_cast<const uint16_t *>(A.in[k]) + base;
+                    const uint16_t *src = static_cast<const uint16_t *>(A.in[k]) + c * kSuper + lane;
 #pragma unroll
-                    for (int j = 0; j < K; ++j) h16[k][j] = ld<NTL>(reinterpret_cast<const u32x2 *>(src + j * 256));
+                    for (int j = 0; j < K; ++j)
+#pragma unroll
+                        for (int d = 0; d < 4; ++d)
+                            __builtin_amdgcn_global_load_lds((global_addr_t)(src + j * 256 + d * 64),
+                                                             (lds_addr_t)(dst + j * kSubBytes + d * 256), 2, 0,
+                                                             NTL ? 2 : 0);
                 } else {
                     const uint32_t *src = static_cast<const uint32_t *>(A.in[k]) + base;
-                    uint8_t *dst = file + k * K * kSubBytes;
 #pragma unroll
                     for (int j = 0; j < K; ++j)
                         __builtin_amdgcn_global_load_lds((global_addr_t)(src + j * 256),
                                                          (lds_addr_t)(dst + j * kSubBytes), 16, 0, NTL ? 2 : 0);
                 }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kMaxIn; ++k) {
-            if (k < n_in && is16(P.in_ty[k])) {
-                uint8_t *dst = file + k * K * kSubBytes + lane_off;
-#pragma unroll
-                for (int j = 0; j < K; ++j) *reinterpret_cast<u32x4 *>(dst + j * kSubBytes) = widen16(h16[k][j]);
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
