@@ -907,7 +907,10 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         }
     }
     if (S.g_mode) {
-        S.grid = std::max<int64_t>(1, std::min<int64_t>(S.g_waves, kInterpMaxGrid));
+        // one work-group per super-chunk; ECMD_GATHER_DISPATCH lowers the
+        // work-groups per dispatch (tests of the split)
+        S.grid = std::max<int64_t>(
+            1, std::min<int64_t>(S.g_waves, std::max<int64_t>(1, env_int("ECMD_GATHER_DISPATCH", kGatherDispatch))));
         S.name = S.g_mode == 1 ? "gather_segments" : "gather_whole_rows";
         return;
     }
@@ -918,6 +921,19 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
     const int64_t total = C.n[0] * C.n[1] * C.n[2] * ((C.n[3] + kGatherE - 1) / kGatherE);
     S.grid = std::max<int64_t>(1, std::min<int64_t>((total + kGatherBlock - 1) / kGatherBlock, 8LL * cu_count));
     S.name = "gather_generic";
+}
+
+// The gather interpreter's work in dispatches of S.grid work-groups, one per
+// super-chunk (the first carried in the argument block).
+int launch_gather_split(const Selection &S, StridedArgs &A, const InterpTape &T, void *stream)
+{
+    for (int64_t first = 0; first < S.g_waves; first += S.grid) {
+        A.g_first = (uint32_t)first;
+        const LaunchGeometry g{std::min<int64_t>(S.grid, S.g_waves - first), 64};
+        const int e = launch_gather_interp(S.g_mode, S.k_sub, A, T, g, S.lds, stream);
+        if (e) return e;
+    }
+    return 0;
 }
 
 // Tiled kernels: nontemporal global accesses unless ECMD_TILED_NT=0.
@@ -1288,7 +1304,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
                        ? (S.interp ? launch_rows_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds,
                                                         hip_stream)
                                    : launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream))
-                   : S.interp ? launch_gather_interp(S.g_mode, S.k_sub, A, T, g, S.lds, hip_stream)
+                   : S.interp ? launch_gather_split(S, A, T, hip_stream)
                               : launch_gather(A, g, hip_stream);
         }
     }

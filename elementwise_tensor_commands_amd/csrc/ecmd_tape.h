@@ -186,6 +186,7 @@ struct StridedArgs {
     uint32_t rowconst16;        // rows path: 1 = some row-constant input is 16-bit
     FastDiv div_vec, div_n2, div_n1;   // rows path: by vectors per row, by n[2], by n[1]
     uint32_t g_waves;           // gather path: super-chunks of work in all
+    uint32_t g_first;           // gather path: super-chunk of this dispatch's first work-group
     uint32_t g_rows;            // gather path: rows n[0] n[1] n[2]
     uint32_t g_rows_per_wave;   // gather path, whole-row modes: rows per super-chunk
     FastDiv div_g;              // gather path: by segments per row (segment mode) or by n[3] (whole rows)
@@ -394,7 +395,9 @@ int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream);
 // The LDS-file interpreter (see launch_linear_interp) over the gather path's
 // positions: mode 1 segments of 256 k_sub columns of one row, mode 2 whole
 // rows of a plane (n[0] = n[1] = 1), mode 3 whole rows over all row
-// dimensions.  Fewer than 2^31 rows, columns and super-chunks (g_waves).
+// dimensions.  Fewer than 2^31 rows, columns and super-chunks (g_waves); one
+// work-group per super-chunk, g_first + blockIdx.x (the host splits the work
+// into dispatches of at most kGatherDispatch work-groups).
 int launch_gather_interp(int mode, int k_sub, const StridedArgs &A, const InterpTape &T, LaunchGeometry g,
                          int lds_bytes, void *stream);
 // Rows path: the linear path's specialised Programs (variant indexes the same
@@ -406,6 +409,7 @@ constexpr int kInterpBlock = 64;
 constexpr int kTileBlock = 256;
 constexpr int kGatherE = 4;
 constexpr int kGatherBlock = 256;
+constexpr int64_t kGatherDispatch = (int64_t)1 << 25;
 constexpr int kRowsBlock = 256;
 
 }  // namespace ecmd

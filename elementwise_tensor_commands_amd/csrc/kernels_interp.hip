@@ -604,6 +604,7 @@ int launch_tiled_interp(TileShape shape, bool nt, const StridedArgs &A, const In
 template <int K, int MODE>
 __global__ __launch_bounds__(64) void k_gather_interp(const StridedArgs A, const InterpTape T)
 {
+    if (A.g_first + blockIdx.x >= A.g_waves) return;
     extern __shared__ __attribute__((aligned(16))) uint8_t file[];
     const uint32_t lane = threadIdx.x;
     const Program &P = A.prog;
@@ -612,7 +613,10 @@ __global__ __launch_bounds__(64) void k_gather_interp(const StridedArgs A, const
     uint8_t *uni = file + T.uni_off;
     interp_uniforms(P, A.uni, uni, lane_off);
     constexpr int kPos = 4 * K;   // positions per lane: access d of sub-chunk j is position 4 j + d
-    for (uint32_t w = blockIdx.x; w < A.g_waves; w += gridDim.x) {
+    // One super-chunk per work-group, no loop: with a loop the compiler keeps
+    // every operand's strides live across it and spills scalar registers.
+    {
+        const uint32_t w = A.g_first + blockIdx.x;
         uint32_t col[kPos], rq[MODE == 1 ? 1 : kPos], rb0[MODE == 3 ? kPos : 1], rb1[MODE == 3 ? kPos : 1];
         bool ok[kPos];
         uint32_t sb0 = 0u, sb1 = 0u, sr = 0u;

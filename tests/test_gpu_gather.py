@@ -153,3 +153,19 @@ def test_gather_rank1_stride(monkeypatch, n, k):
     cmd.launch(gx, gy, out)
     torch.cuda.synchronize()
     compare(host(out), ref, 0, "rank-1 stride n=%d K=%d" % (n, k))
+
+
+@pytest.mark.parametrize("shape", [(1, 37, 2100), (3, 400, 7), (2, 90, 130)])
+def test_gather_split_into_dispatches(monkeypatch, shape):
+    """The work split into dispatches of 7 work-groups (ECMD_GATHER_DISPATCH),
+    each starting at its own super-chunk."""
+    import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_GATHER_DISPATCH", "7")
+    vals, ref = _case(shape, 31 + sum(shape))
+    store, outs = _outputs(shape)
+    cmd = ecmd.from_spec(SPEC)
+    plan = cmd.plan(*vals, *outs)
+    assert plan["path"] == "gather" and plan["grid"] == 7, plan
+    cmd.launch(*vals, *outs)
+    torch.cuda.synchronize()
+    _check(shape, store, outs, ref, "gather in dispatches of 7, %s" % (shape,))
