@@ -752,7 +752,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
             S.name = S.jit ? "jit_rows" : rows_name(S.variant);
             if (S.variant < 0 && !S.jit) {          // the LDS-file interpreter, 64 K vectors per work-group
                 size_interp(P, S);
-                S.grid = std::min<int64_t>((n_vec + 64 * S.k_sub - 1) / (64 * S.k_sub), kInterpMaxGrid);
+                S.grid = (n_vec + 64 * S.k_sub - 1) / (64 * S.k_sub);   // one per super-chunk, below 2^25
             }
             return;
         }

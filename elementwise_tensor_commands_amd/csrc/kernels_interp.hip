@@ -201,8 +201,11 @@ __device__ __forceinline__ void rows_interp_body(const StridedArgs &A, const Int
     const int n_in = P.n_in;
     const int lane_off = lane * 16;
     const uint32_t n_vec = (uint32_t)A.n_vec;   // below 2^31 (host)
-    const uint32_t nsup = (n_vec + K * 64 - 1) / (K * 64);
-    for (uint32_t c = blockIdx.x; c < nsup; c += gridDim.x) {
+    // One super-chunk per work-group (the grid covers them all: fewer than
+    // 2^25), no loop: with a loop the compiler keeps every operand's strides
+    // live across it and spills scalar registers.
+    {
+        const uint32_t c = blockIdx.x;
         // Per sub-chunk: the row (b0, b1, r), this lane's first column and count.
         uint32_t rb0[K], rb1[K], rr[K], col[K];
         int count[K];
