@@ -1022,7 +1022,10 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
     if (S.path == CMD_PATH_ROWS) {
         A.n_vec = S.n_vec;
         A.div_vec = make_fast_div((uint32_t)((C.n[3] + 3) / 4));
-        A.wave_in_row = ((C.n[3] + 3) / 4) % 64 == 0 ? 1u : 0u;
+        // 2: the interpreter's super-chunks (64 K vectors) never span two
+        // rows; 1: no wavefront spans two rows
+        const int64_t per_row = (C.n[3] + 3) / 4;
+        A.wave_in_row = S.interp && per_row % (64 * S.k_sub) == 0 ? 2u : per_row % 64 == 0 ? 1u : 0u;
         for (int k = 0; k < h->prog.n_in; ++k)
             if (S.rowconst[k] && esize(B.in[k].dtype) == 2) A.rowconst16 = 1u;
         A.div_n2 = make_fast_div((uint32_t)C.n[2]);

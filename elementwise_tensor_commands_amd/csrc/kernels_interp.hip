@@ -189,13 +189,18 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
 // last vector loads element by element, and such lanes store the same way or
 // not at all.
 //
-// WROW: every row holds a multiple of 64 vectors, so a sub-chunk (64
-// consecutive vectors from a multiple of 64) lies in one row: the row and
-// every operand's row offset are computed once, in scalar registers, and
-// only the column is per lane.
-template <int K, bool NTL, bool NTS, bool WROW>
+// RM (where a row lies): 1 = every row holds a multiple of 64 vectors, so a
+// sub-chunk (64 consecutive vectors from a multiple of 64) lies in one row:
+// the row and every operand's row offset are computed once per sub-chunk, in
+// scalar registers, and only the column is per lane; 2 = every row holds a
+// multiple of 64 K vectors, so the whole super-chunk lies in one row and the
+// row offsets are computed once (K times fewer scalar values live: with one
+// set per sub-chunk the compiler spills scalar registers to vector lanes);
+// 0 = per lane.
+template <int K, bool NTL, bool NTS, int RM>
 __device__ __forceinline__ void rows_interp_body(const StridedArgs &A, const InterpTape &T, uint8_t *file)
 {
+    constexpr bool WROW = RM != 0;
     const int lane = threadIdx.x;
     const Program &P = A.prog;
     const int n_in = P.n_in;
@@ -207,22 +212,28 @@ __device__ __forceinline__ void rows_interp_body(const StridedArgs &A, const Int
     {
         const uint32_t c = blockIdx.x;
         // Per sub-chunk: the row (b0, b1, r), this lane's first column and count.
-        uint32_t rb0[K], rb1[K], rr[K], col[K];
+        constexpr int NR = RM == 2 ? 1 : K;   // rows computed
+        uint32_t rb0[NR], rb1[NR], rr[NR], col[K];
         int count[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const uint32_t v = (c * K + j) * 64 + (WROW ? 0 : lane);   // WROW: the sub-chunk's first vector
-            const uint32_t q = fast_div(A.div_vec, v);
-            col[j] = 4 * (v - q * A.div_vec.d) + (WROW ? 4 * lane : 0);
-            const uint32_t t = fast_div(A.div_n2, q);
-            rr[j] = q - t * A.div_n2.d;
-            rb0[j] = fast_div(A.div_n1, t);
-            rb1[j] = t - rb0[j] * A.div_n1.d;
+            if (RM != 2 || j == 0) {
+                const uint32_t q = fast_div(A.div_vec, v);
+                col[j] = 4 * (v - q * A.div_vec.d) + (WROW ? 4 * lane : 0);
+                const uint32_t t = fast_div(A.div_n2, q);
+                rr[j] = q - t * A.div_n2.d;
+                rb0[j] = fast_div(A.div_n1, t);
+                rb1[j] = t - rb0[j] * A.div_n1.d;
+            } else {
+                col[j] = col[0] + 256 * j;
+            }
             const int64_t left = A.n[3] - (int64_t)col[j];
             count[j] = v >= n_vec ? 0 : (left >= 4 ? 4 : (int)left);
         }
         auto row_of = [&](const int64_t (&s)[4], int j) {
-            return (int64_t)rb0[j] * s[0] + (int64_t)rb1[j] * s[1] + (int64_t)rr[j] * s[2];
+            const int i = RM == 2 ? 0 : j;
+            return (int64_t)rb0[i] * s[0] + (int64_t)rb1[i] * s[1] + (int64_t)rr[i] * s[2];
         };
         // 1. inputs.  When every lane holds whole vectors (the common case,
         // decided per wavefront) all branches are uniform: direct binary32
@@ -341,13 +352,14 @@ __device__ __forceinline__ void rows_interp_body(const StridedArgs &A, const Int
     }
 }
 
-template <int K, bool NTL, bool NTS>
+// One kernel per row mode RM (A.wave_in_row), so that each gets its own
+// register allocation.
+template <int K, bool NTL, bool NTS, int RM>
 __global__ __launch_bounds__(64) void k_rows_interp(const StridedArgs A, const InterpTape T)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t file[];
     interp_uniforms(A.prog, A.uni, file + T.uni_off, threadIdx.x * 16);
-    if (A.wave_in_row) rows_interp_body<K, NTL, NTS, true>(A, T, file);
-    else rows_interp_body<K, NTL, NTS, false>(A, T, file);
+    rows_interp_body<K, NTL, NTS, RM>(A, T, file);
 }
 
 // The tiled path's interpreter: the tiled kernel's work split and staging
@@ -739,10 +751,18 @@ int launch_gather_interp(int mode, int k_sub, const StridedArgs &A, const Interp
 template <int K, bool NTL, bool NTS>
 static int launch_one(bool rows, const void *args, const InterpTape &T, LaunchGeometry g, int lds, void *stream)
 {
-    if (rows)
-        hipLaunchKernelGGL((k_rows_interp<K, NTL, NTS>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
-                           (hipStream_t)stream, *static_cast<const StridedArgs *>(args), T);
-    else
+    if (rows) {
+        const StridedArgs &A = *static_cast<const StridedArgs *>(args);
+        if (A.wave_in_row == 2)
+            hipLaunchKernelGGL((k_rows_interp<K, NTL, NTS, 2>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
+                               (hipStream_t)stream, A, T);
+        else if (A.wave_in_row)
+            hipLaunchKernelGGL((k_rows_interp<K, NTL, NTS, 1>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
+                               (hipStream_t)stream, A, T);
+        else
+            hipLaunchKernelGGL((k_rows_interp<K, NTL, NTS, 0>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
+                               (hipStream_t)stream, A, T);
+    } else
         hipLaunchKernelGGL((k_linear_interp<K, NTL, NTS>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
                            (hipStream_t)stream, *static_cast<const LinearArgs *>(args), T);
     return (int)hipGetLastError();
