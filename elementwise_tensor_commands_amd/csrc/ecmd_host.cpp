@@ -72,6 +72,7 @@ struct Selection {
     int64_t tiles_r = 0, tiles_c = 0;
     uint8_t rowconst[kMaxIn] = {};
     int64_t n_vec = 0;
+    int64_t n_wg = 0;           // linear interpreter: work-groups in all (split into dispatches of `grid`)
     Canon cn;
     int n_staged = 0;
     uint8_t staged[kMaxIn] = {};
@@ -569,7 +570,6 @@ constexpr int64_t kMaxGridItems = (int64_t)1 << 31;
 // sub-chunks (at most 24 KiB keeps six or more work-groups on a CU), and the
 // grid cap past which its work-groups stride (4,096 per CU on 256 CUs).
 constexpr int kInterpLdsKiB = 24;
-constexpr int64_t kInterpMaxGrid = (int64_t)1 << 20;
 
 bool aligned(const void *p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes == 0; }
 
@@ -685,7 +685,11 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         S.shape = linear_shape(bytes, all16);
         if (S.vec && S.variant < 0 && !S.jit) {
             size_interp(P, S);
-            S.grid = std::max<int64_t>(1, std::min<int64_t>(numel / (256 * S.k_sub), kInterpMaxGrid));
+            // one work-group per super-chunk (at least one: it also takes the
+            // tail), in dispatches of at most kInterpDispatch
+            // (ECMD_INTERP_DISPATCH lowers it, for tests of the split)
+            S.n_wg = std::max<int64_t>(1, numel / (256 * S.k_sub));
+            S.grid = std::min<int64_t>(S.n_wg, std::max<int64_t>(1, env_int("ECMD_INTERP_DISPATCH", kInterpDispatch)));
             S.name = "linear_generic";
             return;
         }
@@ -1279,7 +1283,11 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         } else if (S.interp) {
             InterpTape T;
             resolve_interp_tape(h->prog, S.k_sub, T);
-            herr = launch_linear_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds, hip_stream);
+            for (int64_t first = 0; first < S.n_wg && herr == 0; first += S.grid) {
+                A.first = first;
+                const LaunchGeometry gi{std::min<int64_t>(S.grid, S.n_wg - first), S.block};
+                herr = launch_linear_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, gi, S.lds, hip_stream);
+            }
         } else {
             herr = launch_linear(S.variant, S.vec, S.shape, A, g, hip_stream);
         }

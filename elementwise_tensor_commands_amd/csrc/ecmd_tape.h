@@ -150,6 +150,7 @@ struct LinearArgs {
     int64_t n;
     uint32_t uni[kMaxUni];
     uint32_t flags;           // kLinearXcdRemap
+    int64_t first;            // interpreter: super-chunk of this dispatch's first work-group
     Program prog;
 };
 constexpr uint32_t kLinearXcdRemap = 1;   // give each XCD one contiguous run of blocks
@@ -411,6 +412,7 @@ constexpr int kTileBlock = 256;
 constexpr int kGatherE = 4;
 constexpr int kGatherBlock = 256;
 constexpr int64_t kGatherDispatch = (int64_t)1 << 25;
+constexpr int64_t kInterpDispatch = (int64_t)1 << 25;   // linear interpreter: work-groups per dispatch
 constexpr int kRowsBlock = 256;
 
 }  // namespace ecmd

@@ -26,10 +26,12 @@
 //      16-bit outputs) with the path's cache policy.
 // A lane touches only its own 16 bytes of every entry, so no barrier is
 // needed; the work-group is a single wavefront.  One work-group takes one
-// super-chunk unless the grid is capped (it then strides).  Elements after the
-// last whole super-chunk are done one by one by the last work-group.
+// super-chunk (the host issues dispatches of at most kInterpDispatch
+// work-groups).  Elements after the last whole super-chunk are done one by
+// one by the work-group of the last one.
 //
-// LDS per work-group: (n_in + n_slot) * K KiB + n_uni KiB; the host picks K.
+// LDS per work-group: entries * K KiB + n_uni KiB (the host places values in
+// entries by liveness and picks K).
 #include <hip/hip_runtime.h>
 
 #include "ecmd_kern_linear.h"
@@ -132,7 +134,11 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
     interp_uniforms(P, A.uni, uni, lane_off);
     constexpr int kSuper = K * 256;
     const int64_t nsup = A.n / kSuper;
-    for (int64_t c = blockIdx.x; c < nsup; c += gridDim.x) {
+    // One super-chunk per work-group, no loop (with a loop the compiler keeps
+    // scalar values live across it and spills them); the host splits the
+    // work into dispatches, each starting at super-chunk A.first.
+    const int64_t c = A.first + blockIdx.x;
+    if (c < nsup) {
         const int64_t base = c * kSuper + lane * 4;
         // 1. inputs into their entries, every load issued before the one
         // wait.  Word q of an entry's sub-chunk holds the sub-chunk's element
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
             }
         }
     }
-    if (blockIdx.x == gridDim.x - 1) linear_tail<RtEval, 1>(A, nsup * kSuper);
+    if (c == (nsup > 0 ? nsup - 1 : 0)) linear_tail<RtEval, 1>(A, nsup * kSuper);
 }
 
 // The rows path's interpreter: the same register file and tape walk over the

@@ -255,3 +255,20 @@ def test_rows_interp_row_modes(monkeypatch, k, vec_per_row):
     compare(host(os_[:, :n3]), ref, 0, "rows modes K=%d %d vectors per row (K used %d)" % (
         k, vec_per_row, plan["elems_per_thread"] // 4))
     assert torch.isnan(os_[:, n3:]).all()
+
+
+@pytest.mark.parametrize("n", [13 * 1024 + 77, 1024 * 10, 300])
+def test_linear_interp_split_into_dispatches(monkeypatch, n):
+    """The linear interpreter's work in dispatches of 5 work-groups
+    (ECMD_INTERP_DISPATCH), the tail done by the last super-chunk's work-group
+    (or by the only work-group when there is no whole super-chunk)."""
+    monkeypatch.setenv("ECMD_FORCE_GENERIC", "1")
+    monkeypatch.setenv("ECMD_INTERP_DISPATCH", "5")
+    rng = np.random.default_rng(n)
+    spec = [("x", ("load", "f32", 1)), ("y", ("load", "i32", 1)), ("s", ("scalar", "f32")),
+            ("yf", ("cvt", "y", "f32")), ("t", ("mul", "x", "s")), ("u", ("sub", "t", "yf")),
+            ("o", ("store", "u", 1))]
+    vals = [rng.standard_normal(n).astype(np.float32), rng.integers(-1000, 1000, n, dtype=np.int32),
+            np.float32(1.25)]
+    plan = _run_interp(spec, vals, n, "dispatches of 5, n=%d" % n)
+    assert plan["grid"] == min(5, max(1, n // (64 * plan["elems_per_thread"]))), plan

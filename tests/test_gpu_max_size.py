@@ -62,7 +62,7 @@ def test_linear_past_the_dispatch_limit(name, specialised):
     """2^33 + 4099 elements.  Specialised kernel: 2^25 + 16 wavefront chunks
     of 256 elements, the grid capped at 2^23 work-groups (2^31 work-items), 3
     elements of tail.  Interpreter: 2^23 + 4 super-chunks of 1024 elements
-    (four sub-chunks) over 2^20 work-groups (8 or 9 each), 3 elements of tail."""
+    (four sub-chunks), one work-group each, 3 elements of tail."""
     import elementwise_tensor_commands_amd as ecmd
     n = (1 << 33) + 4099
     f32 = name == "add_f32"
@@ -79,8 +79,8 @@ def test_linear_past_the_dispatch_limit(name, specialised):
         assert plan["path"] == "linear" and plan["specialised"] == specialised, plan
         if specialised:       # the grid is capped at 2^31 work-items and the kernel loops
             assert plan["grid"] * plan["block"] == 1 << 31, plan
-        else:                 # the interpreter caps its grid at 2^20 work-groups and strides
-            assert plan["grid"] == 1 << 20 and plan["block"] == 64, plan
+        else:                 # the interpreter: one work-group per super-chunk
+            assert plan["grid"] == n // (64 * plan["elems_per_thread"]) and plan["block"] == 64, plan
         cmd.launch(x, y, z)
         torch.cuda.synchronize()
         idx = _sample(n)
