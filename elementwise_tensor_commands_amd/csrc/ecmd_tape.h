@@ -340,12 +340,16 @@ struct InterpTape {
     uint32_t out[kMaxOut];     // each output's value
     uint32_t uni_off;          // bytes of a wavefront's entries
 };
-// One wavefront per work-group, k_sub (1, 2 or 4) sub-chunks of 256 elements
-// per super-chunk, an LDS register file of lds_bytes.
+// One wavefront per work-group and one super-chunk of k_sub (1, 2 or 4)
+// sub-chunks of 256 elements per work-group, starting at super-chunk A.first
+// (the caller splits larger grids into several dispatches; the work-group of
+// the last super-chunk also does the elements after it), an LDS register file
+// of lds_bytes.
 int launch_linear_interp(int k_sub, bool nt_load, bool nt_store, const LinearArgs &A, const InterpTape &T,
                          LaunchGeometry g, int lds_bytes, void *stream);
 // The same interpreter over the rows path's vectors (k_sub x 64 vectors of 4
-// elements per super-chunk).
+// elements per super-chunk, one work-group per super-chunk; A.wave_in_row
+// picks the kernel of the row mode).
 int launch_rows_interp(int k_sub, bool nt_load, bool nt_store, const StridedArgs &A, const InterpTape &T,
                        LaunchGeometry g, int lds_bytes, void *stream);
 
