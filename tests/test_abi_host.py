@@ -461,3 +461,56 @@ def test_lowered_listing_matches_oracle(oracle_mod, seed):
     n_ent = int(re.search(r"^lds entries (\d+)$", listing, re.M).group(1))
     n_slot = len({m for m in re.findall(r"^(s\d+) = ", listing, re.M)})
     assert n_ent <= len(ins) + n_slot, listing
+
+
+# Hand-counted LDS entries of the interpreters' register file: (spec, entries).
+# Inputs keep entries 0 .. n_in - 1; a result takes a dying operand's entry
+# (or the lowest free one); values a later operation or a store reads stay.
+_ENTRY_CASES = [
+    # no operations: a uniform value stored (no entry), an input passed through
+    ([("s", ("scalar", "f32")), ("o", ("store", "s", 1))], 0),
+    ([("x", ("load", "f32", 1)), ("o", ("store", "x", 1))], 1),
+    # x + x: x dies at its only use, the sum takes its entry
+    ([("x", ("load", "f32", 1)), ("t", ("add", "x", "x")), ("o", ("store", "t", 1))], 1),
+    # x stored as well as used: it stays live to the end, the sum needs a second entry
+    ([("x", ("load", "f32", 1)), ("t", ("add", "x", "x")), ("o0", ("store", "t", 1)),
+      ("o1", ("store", "x", 1))], 2),
+    # select over three inputs: all die at it
+    ([("c", ("load", "i32", 1)), ("a", ("load", "f32", 1)), ("b", ("load", "f32", 1)),
+      ("r", ("select", "c", "a", "b")), ("o", ("store", "r", 1))], 3),
+    # a chain over one input and a uniform: everything in place
+    ([("x", ("load", "f32", 1)), ("s", ("scalar", "f32")), ("t", ("mul", "x", "s")), ("u", ("add", "t", "s")),
+      ("v", ("max", "u", "s")), ("o", ("store", "v", 1))], 1),
+    # two values kept for two stores while a third is made
+    ([("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("t", ("add", "x", "y")), ("u", ("sub", "x", "y")),
+      ("w", ("mul", "t", "u")), ("o0", ("store", "t", 1)), ("o1", ("store", "w", 1))], 3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(_ENTRY_CASES)))
+def test_interpreter_entries(oracle_mod, case):
+    """The entry count of hand-worked programs, and the entry form of each
+    run with NumPy against the oracle."""
+    spec, want = _ENTRY_CASES[case]
+    c = E.from_spec(spec)
+    listing = c.dump()
+    assert int(re.search(r"^lds entries (\d+)$", listing, re.M).group(1)) == want, listing
+    n = 33
+    rng = np.random.default_rng(case)
+    vals = []
+    for _, st in spec:
+        if st[0] == "load":
+            vals.append(rng.integers(0, 2, n, dtype=np.int32) if st[1] == "i32" else
+                        rng.standard_normal(n).astype(np.float32))
+        elif st[0] == "scalar":
+            vals.append(np.float32(0.75))
+    loads = any(st[0] == "load" for _, st in spec)
+    # without loads the stores give the shape
+    ref = oracle_mod.from_spec(spec).run(*vals, outputs=None if loads else [np.zeros(n, np.float32)])
+    in_args = [int(a) for a in re.findall(r"in\d+ = load\.\S+ arg(\d+)", listing)]
+    u_args = [int(a) for a in re.findall(r"u\d+ = scalar\.\S+ arg(\d+)", listing)]
+    got = _emulate(listing, [vals[a] for a in in_args], [vals[a] for a in u_args], n, lds=True)
+    assert len(got) == len(ref)
+    for g, r in zip(got, ref):
+        g = np.broadcast_to(np.asarray(g, dtype=r.dtype), r.shape)
+        assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), listing
