@@ -272,3 +272,49 @@ def test_linear_interp_split_into_dispatches(monkeypatch, n):
             np.float32(1.25)]
     plan = _run_interp(spec, vals, n, "dispatches of 5, n=%d" % n)
     assert plan["grid"] == min(5, max(1, n // (64 * plan["elems_per_thread"]))), plan
+
+
+@pytest.mark.parametrize("shape", [(64, 128), (100, 68), (36, 300)])
+def test_tiled_interp_three_staged_inputs(shape):
+    """Three inputs read transposed (binary16, bfloat16, binary32), each staged
+    in its own entry's LDS region and overwritten there by its entries, with
+    a direct binary32 input and a per-row constant; full and edge tiles."""
+    import torch
+    import elementwise_tensor_commands_amd as ecmd
+    R, C = shape
+    spec = [("a", ("load", "f16", 2)), ("b", ("load", "bf16", 2)), ("c", ("load", "f32", 2)),
+            ("d", ("load", "f32", 2)), ("r", ("load", "f32", 2)),
+            ("af", ("cvt", "a", "f32")), ("bf", ("cvt", "b", "f32")), ("p", ("mul", "af", "bf")),
+            ("q", ("add", "p", "c")), ("u", ("sub", "q", "d")), ("v", ("mul", "u", "r")),
+            ("o", ("store", "v", 2))]
+    rng = np.random.default_rng(R * 7 + C)
+    at = (rng.standard_normal((C, R)) * 4).astype(np.float16)
+    bt = (rng.standard_normal((C, R)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ct = rng.standard_normal((C, R)).astype(np.float32)
+    d = rng.standard_normal((R, C)).astype(np.float32)
+    r = rng.standard_normal((R, 1)).astype(np.float32)
+    ref = run_oracle(spec, [np.ascontiguousarray(at.T), np.ascontiguousarray(bt.T), np.ascontiguousarray(ct.T), d,
+                            np.ascontiguousarray(np.broadcast_to(r, (R, C)))])[0]
+    gv = [to_dev(at).t(), to_dev(bt).t(), to_dev(ct).t(), to_dev(d), to_dev(r).expand(R, C)]
+    out = torch.full((R, C), float("nan"), device=dev())
+    cmd = ecmd.from_spec(spec)
+    plan = cmd.plan(*gv, out)
+    assert plan["path"] == "tiled" and plan["kernel"] == "tiled_generic", plan
+    cmd.launch(*gv, out)
+    torch.cuda.synchronize()
+    compare(host(out), ref, 0, "three staged inputs %s (lds %d)" % (shape, plan["lds_bytes"]))
+
+
+@pytest.mark.parametrize("n", [9 * 1024 + 5, 700])
+def test_linear_interp_split_16bit(monkeypatch, n):
+    """Dispatches of 3 work-groups with binary16 and bfloat16 inputs (2-byte
+    direct loads) and both output widths."""
+    monkeypatch.setenv("ECMD_INTERP_DISPATCH", "3")
+    rng = np.random.default_rng(n + 1)
+    spec = [("h", ("load", "f16", 1)), ("b", ("load", "bf16", 1)), ("hf", ("cvt", "h", "f32")),
+            ("bf", ("cvt", "b", "f32")), ("t", ("sub", "hf", "bf")), ("m", ("max", "t", "hf")),
+            ("mh", ("cvt", "m", "bf16")), ("o0", ("store", "t", 1)), ("o1", ("store", "mh", 1))]
+    vals = [(rng.standard_normal(n) * 8).astype(np.float16),
+            (rng.standard_normal(n).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)]
+    plan = _run_interp(spec, vals, n, "16-bit dispatches of 3, n=%d" % n)
+    assert plan["grid"] == min(3, max(1, n // (64 * plan["elems_per_thread"]))), plan
