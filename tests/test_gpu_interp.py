@@ -222,24 +222,25 @@ def test_tiled_interp_random_transposed_views(seed):
 
 @pytest.mark.parametrize("k", [1, 2, 4])
 @pytest.mark.parametrize("vec_per_row", [64 * 4 * 3, 64 * 3, 77])
-def test_rows_interp_row_modes(monkeypatch, k, vec_per_row):
+@pytest.mark.parametrize("partial", [False, True])
+def test_rows_interp_row_modes(monkeypatch, k, vec_per_row, partial):
     """Each row mode of the rows interpreter at each sub-chunk count: rows of a
     multiple of 64 K vectors (a super-chunk never spans two rows), of 64
     vectors (a sub-chunk never does), and of neither; a padded binary32
-    input, a binary16 input and a per-row constant, with a partial last
-    vector in every row of the third kind."""
+    input, a binary16 input and a per-row constant; with `partial` the last
+    vector of every row holds fewer than 4 elements."""
     import torch
     import elementwise_tensor_commands_amd as ecmd
     from gpu_util import TD
     monkeypatch.setenv("ECMD_FORCE_GENERIC", "1")
     monkeypatch.setenv("ECMD_INTERP_K", str(k))
     rows = 21
-    n3 = 4 * vec_per_row - (2 if vec_per_row == 77 else 0)
+    n3 = 4 * vec_per_row - (3 if partial else 0)
     ld = (n3 + 8 + 3) // 4 * 4
     spec = [("x", ("load", "f32", 2)), ("h", ("load", "f16", 2)), ("b", ("load", "f32", 2)),
             ("z", ("scalar", "f32")), ("hf", ("cvt", "h", "f32")), ("t", ("add", "x", "b")),
             ("u", ("mul", "t", "hf")), ("r", ("max", "u", "z")), ("o", ("store", "r", 2))]
-    rng = np.random.default_rng(k * 1000 + vec_per_row)
+    rng = np.random.default_rng(k * 1000 + vec_per_row + partial)
     xs = rng.standard_normal((rows, ld)).astype(np.float32)
     hs = (rng.standard_normal((rows, ld)) * 3).astype(np.float16)
     bv = rng.standard_normal((rows, 1)).astype(np.float32)
@@ -252,8 +253,8 @@ def test_rows_interp_row_modes(monkeypatch, k, vec_per_row):
     assert plan["path"] == "rows" and plan["kernel"] == "rows_generic", plan
     cmd.launch(*gv, os_[:, :n3])
     torch.cuda.synchronize()
-    compare(host(os_[:, :n3]), ref, 0, "rows modes K=%d %d vectors per row (K used %d)" % (
-        k, vec_per_row, plan["elems_per_thread"] // 4))
+    compare(host(os_[:, :n3]), ref, 0, "rows modes K=%d %d vectors per row%s (K used %d)" % (
+        k, vec_per_row, ", partial last" if partial else "", plan["elems_per_thread"] // 4))
     assert torch.isnan(os_[:, n3:]).all()
 
 
