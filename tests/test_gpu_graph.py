@@ -103,3 +103,53 @@ def test_graph_of_many_small_launches():
             cmd.launch(x if k % 2 == 0 else y, y, ref)
             torch.cuda.synchronize()
             compare(host(o), host(ref), 0, "replay %d graph launch %d" % (rep, k))
+
+
+def test_graph_of_split_dispatches(monkeypatch):
+    """Launches the host splits into several dispatches (the linear
+    interpreter with ECMD_INTERP_DISPATCH=4, the gather interpreter with
+    ECMD_GATHER_DISPATCH=3) captured in one graph: every replay equals the
+    eager launches bit for bit."""
+    import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_INTERP_DISPATCH", "4")
+    monkeypatch.setenv("ECMD_GATHER_DISPATCH", "3")
+    g = torch.Generator(device=dev()).manual_seed(5)
+    n = 37 * 1024 + 11
+    x = torch.randn(n, device=dev(), generator=g)
+    y = torch.randn(n, device=dev(), generator=g)
+    P = torch.randn(300, 513, device=dev(), generator=g)          # rows 4 bytes off 16-byte alignment
+    Q = torch.randn(300, 512, device=dev(), generator=g)
+    relu = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("z", ("scalar", "f32")),
+            ("u", ("sub", "x", "y")), ("r", ("max", "u", "z")), ("o", ("store", "r", 1))]
+    add2 = [("p", ("load", "f32", 2)), ("q", ("load", "f32", 2)), ("u", ("add", "p", "q")), ("o", ("store", "u", 2))]
+    cases = [(ecmd.from_spec(relu), [x, y, 0.0], (n,), "linear_generic", 4),
+             (ecmd.from_spec(add2), [P[:, 1:], Q], (300, 512), "gather_whole_rows", 3)]
+    outs = [torch.full(shape, float("nan"), device=dev()) for _, _, shape, _, _ in cases]
+    for (cmd, vals, _, kernel, grid), o in zip(cases, outs):
+        plan = cmd.plan(*vals, o)
+        assert plan["kernel"] == kernel and plan["grid"] == grid, plan
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for (cmd, vals, _, _, _), o in zip(cases, outs):
+            cmd.launch(*vals, o)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for (cmd, vals, _, _, _), o in zip(cases, outs):
+            cmd.launch(*vals, o)
+    refs = [torch.empty_like(o) for o in outs]
+    for rep in range(3):
+        for t in (x, y, P, Q):
+            t.mul_(0.875).add_(0.25 * (rep + 1))
+        torch.cuda.synchronize()
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for (cmd, vals, _, _, _), r in zip(cases, refs):
+            cmd.launch(*vals, r)
+        torch.cuda.synchronize()
+        for (_, _, _, kernel, _), o, r in zip(cases, outs, refs):
+            compare(host(o), host(r), 0, "replay %d %s" % (rep, kernel))
