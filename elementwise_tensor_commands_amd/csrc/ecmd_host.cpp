@@ -1010,7 +1010,7 @@ FastDiv make_fast_div(uint32_t d)
 
 void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
 {
-    std::memset(&A, 0, sizeof A);
+    std::memset(static_cast<void *>(&A), 0, sizeof A);   // padding too
     const Canon &C = S.cn;
     for (int k = 0; k < h->prog.n_in; ++k) {
         A.in[k] = B.in[k].ptr;
@@ -1266,7 +1266,7 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
     int herr = 0;
     if (S.path == CMD_PATH_LINEAR) {
         LinearArgs A;
-        std::memset(&A, 0, sizeof A);
+        std::memset(static_cast<void *>(&A), 0, sizeof A);   // padding too
         for (int k = 0; k < h->prog.n_in; ++k) A.in[k] = B.in[k].ptr;
         for (int k = 0; k < h->prog.n_out; ++k) A.out[k] = B.out[k].ptr;
         A.n = B.numel;
