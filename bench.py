@@ -171,7 +171,7 @@ def time_each(cmd, args, reps, cold=False):
 
 
 def cpu_baseline(wl, budget_s=20.0):
-    """The oracle as it stands, on the GPU machine's host cores, over a bounded
+    """The oracle as it stands, on the host's cores, over a bounded
     prefix of the same workload's inputs."""
     import numpy as np
 
@@ -373,7 +373,7 @@ def main():
         summarize_trace(a.summarize_trace[0], a.workload, a.summarize_trace[1], a.command)
         return
     if a.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
