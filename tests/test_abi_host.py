@@ -420,6 +420,37 @@ def _emulate(listing, ins, uni, n, lds=False):
     return outs
 
 
+def _max_live(listing, n_in):
+    """max(n_in, the largest number of values an operation needs at once: the
+    values made earlier and read later, plus its result)."""
+    slot, last, defs, ops = {}, {}, [], []
+    for k in range(n_in):
+        defs.append(("in%d" % k, -1))
+    for line in listing.splitlines():
+        m = re.match(r"(s\d+) = \S+ (.*)$", line)
+        if m:
+            i = len(ops)
+            reads = []
+            for r in m.group(2).split(", "):
+                v = slot.get(r, r) if r.startswith("s") else r
+                if not r.startswith("u"):
+                    reads.append(v)
+                    last[v] = i
+            v = "v%d" % i
+            slot[m.group(1)] = v
+            defs.append((v, i))
+            ops.append(reads)
+        m = re.match(r"store\.\S+ arg\d+ <- (\S+)$", line)
+        if m and not m.group(1).startswith("u"):
+            r = m.group(1)
+            last[slot.get(r, r) if r.startswith("s") else r] = len(ops) + 1   # read after the tape
+    peak = 0
+    for i in range(len(ops)):
+        live = sum(1 for v, d in defs if d < i and last.get(v, -1) > i)
+        peak = max(peak, live + 1)
+    return max(n_in, peak)
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_lowered_listing_matches_oracle(oracle_mod, seed):
     import random_commands as G
@@ -457,10 +488,10 @@ def test_lowered_listing_matches_oracle(oracle_mod, seed):
             else:
                 ok = gb == rb
             assert ok.all(), "seed %d out%d (lds %s)\n%s" % (seed, k, lds, listing)
-    # entries in use: at most the live values, never more than inputs plus slots
+    # entries in use: exactly max(inputs, the most values live at one operation)
+    # -- the optimum for values live over intervals
     n_ent = int(re.search(r"^lds entries (\d+)$", listing, re.M).group(1))
-    n_slot = len({m for m in re.findall(r"^(s\d+) = ", listing, re.M)})
-    assert n_ent <= len(ins) + n_slot, listing
+    assert n_ent == _max_live(listing, len(ins)), listing
 
 
 # Hand-counted LDS entries of the interpreters' register file: (spec, entries).
