@@ -41,7 +41,7 @@ def split_workload(name):
     return (name[:-4], True) if name.endswith("_jit") else (name, False)
 EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "axpby_f16", "axpby_bf16",
          "bias_relu_f32", "bias_relu_f32_jit", "transposed_relu", "transposed_relu_jit", "odd_rows_f32",
-         "narrow_rows_f32"]
+         "odd_rows_f32_jit", "narrow_rows_f32", "narrow_rows_f32_jit"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 

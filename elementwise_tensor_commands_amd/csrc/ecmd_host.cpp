@@ -898,9 +898,13 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
     const int64_t rows = C.n[0] * C.n[1] * C.n[2], n3 = C.n[3];
     const int64_t lim = kMaxGridItems;
     S.g_mode = 0;
+    // On request (CMD_OPT_JIT) a kernel compiled for the Program
+    // (ecmd_kern_gather.h): 64 kGatherCcE elements per wavefront, registers
+    // instead of the LDS file.
+    const bool g_jit = h->jit && !force_generic;
     if (rows < lim && n3 < lim && env_int("ECMD_GATHER_MODE", 1) != 0) {
         size_interp(P, S);
-        const int64_t span = 256 * S.k_sub;   // elements per super-chunk
+        const int64_t span = g_jit ? 64 * kGatherCcE : 256 * S.k_sub;   // elements per super-chunk
         if (n3 > span / 2) {
             const int64_t segs = (n3 + span - 1) / span;
             if (rows * segs < lim) S.g_mode = 1, S.g_div = segs, S.g_waves = rows * segs;
@@ -909,6 +913,17 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
             S.g_mode = C.n[0] * C.n[1] == 1 ? 2 : 3;
             S.g_div = n3, S.g_rows_per_wave = m, S.g_waves = (rows + m - 1) / m;
         }
+    }
+    if (S.g_mode && g_jit) {
+        S.jit = true;
+        S.interp = false;
+        S.lds = 0;
+        S.e = kGatherCcE;
+        S.block = 256;   // four wavefronts, one super-chunk each
+        S.grid = std::max<int64_t>(1, std::min<int64_t>((S.g_waves + 3) / 4, std::max<int64_t>(
+                                                             1, env_int("ECMD_GATHER_DISPATCH", kGatherDispatch))));
+        S.name = "jit_gather";
+        return;
     }
     if (S.g_mode) {
         // one work-group per super-chunk; ECMD_GATHER_DISPATCH lowers the
@@ -952,6 +967,7 @@ JitRequest jit_request(const Selection &S, const Program &P)
 {
     if (S.path == CMD_PATH_LINEAR) return JitRequest{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, P};
     if (S.path == CMD_PATH_ROWS) return JitRequest{JIT_ROWS, 4, 4, S.shape.nt_load, S.shape.nt_store, P};
+    if (S.path == CMD_PATH_GATHER) return JitRequest{JIT_GATHER, S.e, 0, false, false, P, 0, 0, 0, 0, S.g_mode};
     const bool nt = tiled_nt();
     return JitRequest{JIT_TILED, 4, 4, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
 }
@@ -1300,9 +1316,18 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
             std::string err;
             if (jit_function(jit_request(S, h->prog), &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
             void *params[] = {&A};
-            herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1,
-                                              S.path == CMD_PATH_TILED ? (unsigned)S.lds : 0u,
-                                              (hipStream_t)hip_stream, params, nullptr);
+            if (S.path == CMD_PATH_GATHER) {      // dispatches of S.grid work-groups of four wavefronts
+                for (int64_t first = 0; first < S.g_waves && herr == 0; first += 4 * S.grid) {
+                    A.g_first = (uint32_t)first;
+                    const int64_t wg = std::min<int64_t>(S.grid, (S.g_waves - first + 3) / 4);
+                    herr = (int)hipModuleLaunchKernel(fn, (unsigned)wg, 1, 1, (unsigned)g.block, 1, 1, 0u,
+                                                      (hipStream_t)hip_stream, params, nullptr);
+                }
+            } else {
+                herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1,
+                                                  S.path == CMD_PATH_TILED ? (unsigned)S.lds : 0u,
+                                                  (hipStream_t)hip_stream, params, nullptr);
+            }
         } else {
             InterpTape T;
             if (S.interp)

@@ -169,7 +169,8 @@ void write_file(const std::string &dir, const std::string &key, const JitRequest
 int compile(const JitRequest &r, const std::string &name, Entry &e, std::string &err)
 {
     const std::string src = "#include <hip/hip_runtime.h>\n#include \"ecmd_kern_linear.h\"\n"
-                            "#include \"ecmd_kern_rows.h\"\n#include \"ecmd_kern_tiled.h\"\nnamespace ecmd {\n" +
+                            "#include \"ecmd_kern_rows.h\"\n#include \"ecmd_kern_tiled.h\"\n"
+                            "#include \"ecmd_kern_gather.h\"\nnamespace ecmd {\n" +
                             program_literal(r.prog) + "}  // namespace ecmd\n";
     std::vector<const char *> names, texts;
     for (int i = 0; i < kJitHeaderCount; ++i) names.push_back(kJitHeaderNames[i]), texts.push_back(kJitHeaderTexts[i]);
@@ -243,6 +244,8 @@ std::string jit_name(const JitRequest &r)
     else if (r.kind == JIT_TILED)
         std::snprintf(b, sizeof b, "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, %d, %s, %d, %d, %d>", r.mask,
                       r.ntl ? "true" : "false", r.tm, r.tn, r.tb);
+    else if (r.kind == JIT_GATHER)
+        std::snprintf(b, sizeof b, "ecmd::k_gather_cc<ecmd::CtEval<ecmd::kJitProg>, %d, %d>", r.e, r.mode);
     else
         std::snprintf(b, sizeof b, "ecmd::k_rows<ecmd::CtEval<ecmd::kJitProg>, %s, %s>", r.ntl ? "true" : "false",
                       r.nts ? "true" : "false");

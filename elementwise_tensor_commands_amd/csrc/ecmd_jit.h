@@ -8,7 +8,7 @@
 // the same device templates (embedded as text) are instantiated for that one
 // Program with hiprtc, and the code object is kept in memory and on disk,
 // keyed by the Program's bytes, the kernel variant and the sources' hash.
-// The linear, rows and tiled kernels can be compiled this way.
+// The linear, rows, tiled and gather kernels can be compiled this way.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -19,7 +19,7 @@
 
 namespace ecmd {
 
-enum JitKernel { JIT_LINEAR = 1, JIT_ROWS = 2, JIT_TILED = 3 };
+enum JitKernel { JIT_LINEAR = 1, JIT_ROWS = 2, JIT_TILED = 3, JIT_GATHER = 4 };
 
 struct JitRequest {
     JitKernel kind;
@@ -28,6 +28,7 @@ struct JitRequest {
     Program prog;
     int mask = 0;      // tiled: staged inputs (bit k = input k)
     int tm = 0, tn = 0, tb = 0;   // tiled: tile shape and work-items
+    int mode = 0;      // gather: 1 segments, 2 whole rows of a plane, 3 whole rows (e: elements per work-item)
 };
 
 // Template instance the request names, e.g.

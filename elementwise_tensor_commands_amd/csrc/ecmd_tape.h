@@ -416,6 +416,7 @@ constexpr int kTileBlock = 256;
 constexpr int kGatherE = 4;
 constexpr int kGatherBlock = 256;
 constexpr int64_t kGatherDispatch = (int64_t)1 << 25;
+constexpr int kGatherCcE = 8;   // run-time compiled gather kernel: elements per work-item
 constexpr int64_t kInterpDispatch = (int64_t)1 << 25;   // linear interpreter: work-groups per dispatch
 constexpr int kRowsBlock = 256;
 

@@ -169,3 +169,26 @@ def test_gather_split_into_dispatches(monkeypatch, shape):
     cmd.launch(*vals, *outs)
     torch.cuda.synchronize()
     _check(shape, store, outs, ref, "gather in dispatches of 7, %s" % (shape,))
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gather_compiled(monkeypatch, shape):
+    """The gather kernel compiled at run time for the Program (k_gather_cc:
+    the same element placement, the values in registers), every mode, on
+    the same cases as the interpreter; and split into dispatches of 2
+    work-groups."""
+    import elementwise_tensor_commands_amd as ecmd
+    vals, ref = _case(shape, 900 + sum(shape))
+    for dispatch in (None, "2"):
+        if dispatch:
+            monkeypatch.setenv("ECMD_GATHER_DISPATCH", dispatch)
+        store, outs = _outputs(shape)
+        cmd = ecmd.from_spec(SPEC).jit()
+        plan = cmd.plan(*vals, *outs)
+        assert plan["path"] == "gather" and plan["kernel"] == "jit_gather" and plan["block"] == 256, plan
+        if dispatch:
+            assert plan["grid"] <= 2, plan
+        cmd.prepare(*vals, *outs)
+        cmd.launch(*vals, *outs)
+        torch.cuda.synchronize()
+        _check(shape, store, outs, ref, "compiled gather %s dispatch %s" % (shape, dispatch))

@@ -82,7 +82,12 @@ def test_each_variant_and_program_has_its_own_entry(cache_dir):
     p = tiled.plan(*tv)
     assert p["kernel"] == "jit_tiled" and p["compiled"] and p["block"] == 512 and p["lds_bytes"] == 32 * 256 * 4, p
     assert tiled.prepare(*tv) == 2
-    assert len(os.listdir(cache_dir)) == 3 + compiled
+    gather = E.from_spec(GATHER_SPEC).jit()
+    gv = _gather_values()
+    p = gather.plan(*gv)
+    assert p["kernel"] == "jit_gather" and p["compiled"] and p["block"] == 256 and p["lds_bytes"] == 0, p
+    assert gather.prepare(*gv) == 2
+    assert len(os.listdir(cache_dir)) == 4 + compiled
 
 
 # out = min(X + Y^T, s) - Y^T: a program the tiled path has no ahead-of-time kernel for
@@ -93,6 +98,15 @@ TILED_SPEC = [("X", ("load", "f32", 2)), ("Y", ("load", "f32", 2)), ("s", ("scal
 
 def _tiled_values(R=64, C=512):
     return [torch.zeros(R, C), torch.zeros(C, R).t(), 1.0, torch.zeros(R, C)]
+
+
+# out = max(x - y, x * y) over a strided x: a program and views for the gather path
+GATHER_SPEC = [("x", ("load", "f32", 2)), ("y", ("load", "f32", 2)), ("d", ("sub", "x", "y")),
+               ("p", ("mul", "x", "y")), ("m", ("max", "d", "p")), ("o", ("store", "m", 2))]
+
+
+def _gather_values(R=64, C=1000):
+    return [torch.zeros(R, 2 * C)[:, ::2], torch.zeros(R, C), torch.zeros(R, C)]
 
 
 STALE_SPEC = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("p", ("mul", "x", "y")),
@@ -135,7 +149,7 @@ def _code_object(path):
     return data[pos:]
 
 
-@pytest.mark.parametrize("spec_name", ["bias_relu", "mixed16", "tiled"])
+@pytest.mark.parametrize("spec_name", ["bias_relu", "mixed16", "tiled", "gather"])
 def test_compiled_code_is_our_rules(cache_dir, tmp_path, spec_name):
     """Disassemble the run-time compiled code objects (built here): no fused
     multiply-add, no scratch, no packed binary32, 16-byte vector accesses."""
@@ -150,6 +164,10 @@ def test_compiled_code_is_our_rules(cache_dir, tmp_path, spec_name):
         spec = [st if st[0] != "m" else ("m", ("max", "a", "s")) for st in TILED_SPEC]
         c = E.from_spec(spec).jit()
         vals = _tiled_values()
+    elif spec_name == "gather":           # min instead of max: a program only this test compiles
+        spec = [st if st[0] != "m" else ("m", ("min", "d", "p")) for st in GATHER_SPEC]
+        c = E.from_spec(spec).jit()
+        vals = _gather_values()
     else:
         spec = [("x", ("load", "f16", 1)), ("y", ("load", "bf16", 1)), ("a", ("cvt", "x", "f32")),
                 ("b", ("cvt", "y", "f32")), ("m", ("mul", "a", "b")), ("s", ("add", "m", "a")),
@@ -162,7 +180,8 @@ def test_compiled_code_is_our_rules(cache_dir, tmp_path, spec_name):
     co = tmp_path / "k.co"
     co.write_bytes(_code_object(f))
     asm = subprocess.run([LLVM_OBJDUMP, "-d", str(co)], capture_output=True, text=True, check=True).stdout
-    assert "global_load_dword" in asm and "global_store_dwordx4" in asm
+    # the gather kernel accesses elements one by one, the others 16 bytes per lane
+    assert "global_load_dword" in asm and ("global_store_dword" if spec_name == "gather" else "global_store_dwordx4") in asm
     if spec_name == "tiled":
         assert "ds_write" in asm and "ds_read" in asm and "s_barrier" in asm
     for bad in ("v_fma", "v_fmac", "v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32", "scratch_", "v_fma_mix"):
