@@ -902,9 +902,11 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
     // (ecmd_kern_gather.h): 64 kGatherCcE elements per wavefront, registers
     // instead of the LDS file.
     const bool g_jit = h->jit && !force_generic;
+    int gce = (int)env_int("ECMD_GATHER_JIT_E", kGatherCcE);   // A/B runs: 4, 8 or 16
+    if (gce != 4 && gce != 16) gce = kGatherCcE;
     if (rows < lim && n3 < lim && env_int("ECMD_GATHER_MODE", 1) != 0) {
         size_interp(P, S);
-        const int64_t span = g_jit ? 64 * kGatherCcE : 256 * S.k_sub;   // elements per super-chunk
+        const int64_t span = g_jit ? 64 * gce : 256 * S.k_sub;   // elements per super-chunk
         if (n3 > span / 2) {
             const int64_t segs = (n3 + span - 1) / span;
             if (rows * segs < lim) S.g_mode = 1, S.g_div = segs, S.g_waves = rows * segs;
@@ -918,7 +920,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         S.jit = true;
         S.interp = false;
         S.lds = 0;
-        S.e = kGatherCcE;
+        S.e = gce;
         S.block = 256;   // four wavefronts, one super-chunk each
         S.grid = std::max<int64_t>(1, std::min<int64_t>((S.g_waves + 3) / 4, std::max<int64_t>(
                                                              1, env_int("ECMD_GATHER_DISPATCH", kGatherDispatch))));
