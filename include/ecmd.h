@@ -252,8 +252,9 @@ int64_t cmd_dump(cmd_t h, char *buf, int64_t cap);
  * one compiled at its first launch (hiprtc, the library's own kernel templates
  * and device flags), kept for the process and stored on disk under
  * $ECMD_CACHE_DIR (else $XDG_CACHE_HOME/ecmd-amd, else $HOME/.cache/ecmd-amd)
- * for later processes.  Applies to the linear and rows paths; the tiled and
- * gather paths always use their ahead-of-time kernels. */
+ * for later processes.  Applies to every path (linear, rows, tiled, gather);
+ * on the tiled path only where the staging tiles fit 64 KiB and no input is
+ * constant along a row (else the tiled interpreter runs). */
 #define CMD_OPT_JIT 1   /* value 0 (default; the environment variable ECMD_JIT=1 makes it 1) or 1 */
 
 /* Set an option of the handle.  CMD_E_ARG for an unknown option or value. */
