@@ -229,7 +229,7 @@ typedef struct {
 #define CMD_PATH_LINEAR 1  /* every view is flat contiguous (in the library's element order) */
 #define CMD_PATH_TILED 2   /* planes of inner-contiguous, transposed (LDS-staged) and        */
                            /* row-broadcast views, with up to two batch dimensions           */
-#define CMD_PATH_GATHER 3  /* any other strides                                              */
+#define CMD_PATH_GATHER 3  /* any other strides, and flat views off 16-byte alignment        */
 #define CMD_PATH_ROWS 4    /* rows: every view contiguous or constant along its last          */
                            /* dimension (padded rows, batch strides, broadcasts), no transpose */
 
@@ -238,9 +238,10 @@ typedef struct {
 int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info);
 
 /* Write a text listing of the lowered program (inputs, per-element operations
- * with their register slots, stores) into buf[cap], NUL-terminated.  Freezes
- * and lowers the Command.  Returns the full length of the listing (which may
- * exceed cap - 1) or a negative status. */
+ * with their register slots, stores; then the same program over the
+ * interpreters' LDS entries, lines starting "lds ") into buf[cap],
+ * NUL-terminated.  Freezes and lowers the Command.  Returns the full length of
+ * the listing (which may exceed cap - 1) or a negative status. */
 int64_t cmd_dump(cmd_t h, char *buf, int64_t cap);
 
 /* ------------------------------------------------------------------------ */
