@@ -192,3 +192,21 @@ def test_gather_compiled(monkeypatch, shape):
         cmd.launch(*vals, *outs)
         torch.cuda.synchronize()
         _check(shape, store, outs, ref, "compiled gather %s dispatch %s" % (shape, dispatch))
+
+
+@pytest.mark.parametrize("e", [4, 16])
+@pytest.mark.parametrize("shape", [(1, 37, 2100), (3, 41, 7)])
+def test_gather_compiled_other_widths(monkeypatch, e, shape):
+    """The compiled gather kernel at the other elements-per-work-item choices
+    (ECMD_GATHER_JIT_E, for A/B runs)."""
+    import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_GATHER_JIT_E", str(e))
+    vals, ref = _case(shape, 700 + e + sum(shape))
+    store, outs = _outputs(shape)
+    cmd = ecmd.from_spec(SPEC).jit()
+    plan = cmd.plan(*vals, *outs)
+    assert plan["kernel"] == "jit_gather" and plan["elems_per_thread"] == e, plan
+    cmd.prepare(*vals, *outs)
+    cmd.launch(*vals, *outs)
+    torch.cuda.synchronize()
+    _check(shape, store, outs, ref, "compiled gather E=%d %s" % (e, shape))
