@@ -376,9 +376,9 @@ __global__ __launch_bounds__(64) void k_rows_interp(const StridedArgs A, const I
 // chunks are the K sub-chunks of its register file.
 //   1. Full tiles: direct inputs go straight from HBM into their file entries
 //      (binary32: 16 bytes per lane; 16-bit: two 4-byte halves, widened in
-//      step 3).  Staged inputs are read as column runs into the staging tile,
-//      as in the tiled kernel.  Row-constant inputs, and the direct inputs of
-//      edge tiles, are loaded element by element through registers.
+//      step 3), staged inputs straight into the swizzled staging tile (one
+//      element per lane and access).  Row-constant inputs, and the direct and
+//      staged inputs of edge tiles, are loaded through registers.
 //   2. One wait and one barrier (the staging tile is shared by the
 //      work-group).
 //   3. Staged inputs are read from the staging tile (4 LDS reads per chunk)
@@ -452,10 +452,31 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
         }
     }
     // 1b. Staged inputs into the staging tile: element (c, r) of staged input
-    // s at word s TM TN + tile_word(TM, c, r).
+    // k at word tile_word(TM, c, r) of its region.  Full tiles: direct
+    // global-to-LDS loads, one word (2 bytes for 16-bit inputs, written
+    // zero-extended) per lane; access i of wavefront v fills words
+    // 64 (v n + i) .. + 63, so lane l takes the element whose swizzled word
+    // that is (each half-wavefront reads 32 consecutive elements of a column).
+    // Edge tiles: through registers, zeros past the edge.
 #pragma unroll
     for (int k = 0; k < kMaxIn; ++k) {
-        if (k < n_in && A.in_staged[k]) {
+        if (k < n_in && A.in_staged[k] && full) {
+            constexpr int kAcc = TM * TN / TB;   // accesses per wavefront
+            const int v = t >> 6;
+            uint8_t *region = lds + k * kRegion;
+#pragma unroll
+            for (int i = 0; i < kAcc; ++i) {
+                const int w = (v * kAcc + i) * 64 + lane;
+                const int c = w / TM, r = (w % TM) ^ (c & 31);
+                const int64_t off = in_base(k) + (c0 + c) * A.in_s[k][3] + (r0 + r);
+                if (is16(P.in_ty[k]))
+                    __builtin_amdgcn_global_load_lds((global_addr_t)(static_cast<const uint16_t *>(A.in[k]) + off),
+                                                     (lds_addr_t)(region + (v * kAcc + i) * 256), 2, 0, NT ? 2 : 0);
+                else
+                    __builtin_amdgcn_global_load_lds((global_addr_t)(static_cast<const uint32_t *>(A.in[k]) + off),
+                                                     (lds_addr_t)(region + (v * kAcc + i) * 256), 4, 0, NT ? 2 : 0);
+            }
+        } else if (k < n_in && A.in_staged[k]) {
             const uint8_t ty = P.in_ty[k];
             uint32_t *dst = reinterpret_cast<uint32_t *>(lds + k * kRegion);
 #pragma unroll
@@ -464,13 +485,9 @@ __global__ __launch_bounds__(TB) void k_tiled_interp(const StridedArgs A, const 
                 tile_split(t + TB * p, TM, sc, sr);
                 const int64_t off = in_base(k) + (c0 + sc) * A.in_s[k][3] + (r0 + sr);
                 uint32_t sv[4] = {0u, 0u, 0u, 0u};
-                if (full) {
-                    load_group<4, true, NT>(A.in[k], ty, off, 4, sv);
-                } else {
-                    const int64_t left = rows - (r0 + sr);
-                    const int cnt = c0 + sc < cols ? (left <= 0 ? 0 : (left >= 4 ? 4 : (int)left)) : 0;
-                    if (cnt > 0) load_elems<4, false>(A.in[k], ty, off, cnt, sv);
-                }
+                const int64_t left = rows - (r0 + sr);
+                const int cnt = c0 + sc < cols ? (left <= 0 ? 0 : (left >= 4 ? 4 : (int)left)) : 0;
+                if (cnt > 0) load_elems<4, false>(A.in[k], ty, off, cnt, sv);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dst[tile_word(TM, sc, sr + e)] = sv[e];
             }
