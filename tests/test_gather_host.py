@@ -68,3 +68,30 @@ def test_per_element_kernel_on_request(monkeypatch):
     x = torch.zeros(10, 33)[:, :32]
     plan = E.from_spec(ADD2).plan(x, torch.zeros(10, 32), torch.zeros(10, 32))
     assert plan["kernel"] == "gather_generic" and plan["block"] == 256 and plan["lds_bytes"] == 0, plan
+
+
+def test_dispatch_limits_lower_the_planned_grid(monkeypatch):
+    """ECMD_GATHER_DISPATCH / ECMD_INTERP_DISPATCH cap the work-groups of one
+    dispatch; the host issues as many dispatches as the work needs."""
+    x = torch.zeros(100, 1001)[:, :1000]
+    c = E.from_spec(ADD2)
+    whole = c.plan(x, torch.zeros(100, 1000), torch.zeros(100, 1000))["grid"]
+    monkeypatch.setenv("ECMD_GATHER_DISPATCH", "7")
+    assert c.plan(x, torch.zeros(100, 1000), torch.zeros(100, 1000))["grid"] == min(7, whole)
+    add1 = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("m", ("max", "x", "y")), ("o", ("store", "m", 1))]
+    n = 50 * 1024
+    p = E.from_spec(add1).plan(torch.zeros(n), torch.zeros(n), torch.zeros(n))
+    assert p["kernel"] == "linear_generic" and p["grid"] == n // (64 * p["elems_per_thread"]), p
+    monkeypatch.setenv("ECMD_INTERP_DISPATCH", "5")
+    assert E.from_spec(add1).plan(torch.zeros(n), torch.zeros(n), torch.zeros(n))["grid"] == 5
+
+
+def test_compiled_gather_grid():
+    """A compiled gather kernel (Command.jit()): 64 x 8 elements per wavefront,
+    four wavefronts per work-group, no LDS."""
+    rows, n3 = 37, 2100
+    x = torch.zeros(rows, n3 + 1)[:, :n3]
+    p = E.from_spec(ADD2).jit().plan(x, torch.zeros(rows, n3), torch.zeros(rows, n3))
+    segs = -(-n3 // 512)
+    assert p["kernel"] == "jit_gather" and p["compiled"] and p["block"] == 256 and p["lds_bytes"] == 0, p
+    assert p["elems_per_thread"] == 8 and p["grid"] == -(-(rows * segs) // 4), p
