@@ -185,7 +185,7 @@ struct StridedArgs {
     int64_t n_vec;              // rows path: vectors in all, ceil(n[3] / 4) per row
     uint32_t wave_in_row;       // rows path: 1 = a multiple of 64 vectors per row (no wavefront spans two
                                 // rows); 2 = of 64 K vectors (the interpreter: no super-chunk spans two)
-    uint32_t rowconst16;        // rows path: 1 = some row-constant input is 16-bit
+    uint32_t rowconst16;        // rows path: 1 = some row-constant input is 16-bit (informational)
     FastDiv div_vec, div_n2, div_n1;   // rows path: by vectors per row, by n[2], by n[1]
     uint32_t g_waves;           // gather path: super-chunks of work in all
     uint32_t g_first;           // gather path: super-chunk of this dispatch's first work-group

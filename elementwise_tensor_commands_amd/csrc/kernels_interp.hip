@@ -188,12 +188,11 @@ __global__ __launch_bounds__(64) void k_linear_interp(const LinearArgs A, const 
 
 // The rows path's interpreter: the same register file and tape walk over the
 // rows path's vectors (see ecmd_kern_rows.h): sub-chunk j of super-chunk c is
-// the 64 vectors (c K + j) 64 .. + 63, lane l taking one.  Whole vectors of
-// direct binary32 inputs go straight into LDS; row-constant inputs (one value
-// per row) and 16-bit inputs pass through registers; a wavefront holding a
-// partial last vector of a row (n3 not a multiple of 4) or lanes past the
-// last vector loads element by element, and such lanes store the same way or
-// not at all.
+// the 64 vectors (c K + j) 64 .. + 63, lane l taking one.  In a wavefront
+// whose lanes all hold whole vectors every input goes straight into LDS (see
+// the fast path below); a wavefront holding a partial last vector of a row
+// (n3 not a multiple of 4) or lanes past the last vector loads element by
+// element through registers, and such lanes store the same way or not at all.
 //
 // RM (where a row lies): 1 = every row holds a multiple of 64 vectors, so a
 // sub-chunk (64 consecutive vectors from a multiple of 64) lies in one row:
@@ -247,16 +246,17 @@ __device__ __forceinline__ void rows_interp_body(const StridedArgs &A, const Int
         // issued before anything is waited for.  Branches that differ between
         // lanes would make the compiler wait for each load before the paths
         // join, one memory round trip per input.
-        bool full = !A.rowconst16;
+        bool full = true;
 #pragma unroll
         for (int j = 0; j < K; ++j) full = full && count[j] == 4;
         const bool fast = __all(full);
         if (fast) {
             // Every input by direct loads to LDS, so that no load has a vector
             // register to wait for: whole binary32 vectors into their entries;
-            // a row-constant binary32 value (4 bytes) and the two 4-byte
-            // halves of a binary16 / bfloat16 vector into the first 256 and
-            // 512 bytes of the entry, widened in place after the wait below.
+            // a row-constant value (4 bytes, or 2 written zero-extended for
+            // 16-bit inputs) and the two 4-byte halves of a binary16 /
+            // bfloat16 vector into the first 256 and 512 bytes of the entry,
+            // widened in place after the wait below.
 #pragma unroll
             for (int k = 0; k < kMaxIn; ++k) {
                 if (k < n_in) {
@@ -265,7 +265,11 @@ __device__ __forceinline__ void rows_interp_body(const StridedArgs &A, const Int
 #pragma unroll
                     for (int j = 0; j < K; ++j) {
                         const int64_t row = row_of(A.in_s[k], j);
-                        if (A.in_rowconst[k]) {
+                        if (A.in_rowconst[k] && h16) {
+                            __builtin_amdgcn_global_load_lds(
+                                (global_addr_t)(static_cast<const uint16_t *>(A.in[k]) + row),
+                                (lds_addr_t)(dst + j * kSubBytes), 2, 0, 0);
+                        } else if (A.in_rowconst[k]) {
                             __builtin_amdgcn_global_load_lds(
                                 (global_addr_t)(static_cast<const uint32_t *>(A.in[k]) + row),
                                 (lds_addr_t)(dst + j * kSubBytes), 4, 0, 0);
