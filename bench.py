@@ -1,14 +1,26 @@
-"""Benchmark: evaluate one elementwise tensor Command per step on one MI355X.
+"""Benchmark: evaluate elementwise tensor Commands on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-commands]
 
 A step is one launch of the whole Command (load, E_ operations, store) over
-the workload's synthetic tensors, which are resident in HBM before timing
-starts.  The headline is the int32 fused DAG z = (x + y) * w - s on 2^24
-elements.  Prints one JSON line with effective HBM GB/s (algorithmic bytes read
-+ written per second), the roofline of the kernel, and the CPU oracle's rate on
-the same workload as a baseline.
+the workload's synthetic tensors, resident in HBM before timing starts.  The
+headline workload is the largest configuration on the linear path,
+out = 1.5 x - 0.25 y in binary32 over 2^28 elements (3 GiB moved per step),
+timed cold: before every step a 1 GiB read (outside the step's HIP events)
+evicts the Command's data from the 256 MB last-level cache, so each step reads
+its operands from HBM.  `value` is algorithmic bytes x K / the K steps' summed
+kernel time.
+
+The same JSON line carries, under "commands", the five configurations (and a
+plain copy, the reference for "% of copy", plus three programs with no
+ahead-of-time kernel: compiled at run time), each with warm (back-to-back) and
+cold per-launch median / p10 / p90, % of peak and of copy, the host's cost per
+launch and a full-size parity check against the oracle; the roofline of the
+headline kernel; the oracle's own rate on the host's cores; and a snapshot of
+the machine.  Workload names take a suffix: "@noaot" runs a program on the
+ahead-of-time list through a kernel compiled at run time instead,
+"@interp" through the interpreter.
 """
 from __future__ import annotations
 
@@ -16,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import statistics
 import sys
 import time
@@ -25,24 +38,24 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0        # MI355X HBM3E peak, 8 TB/s
 METRIC = "effective HBM GB/s (bytes read+written / time) and % of peak, per Command"
+HEADLINE = "axpby_f32"
 DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two_out": "f16/f32",
             "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32",
             "batched_transpose": "f32", "bias_nchw": "f32", "axpby_f16": "f16", "axpby_bf16": "bf16",
             "bias_relu_f32": "f32", "transposed_relu": "f32", "odd_rows_f32": "f32", "narrow_rows_f32": "f32"}
-# Measured besides the five configurations: the plain copy (the bandwidth and
-# counter reference), the widened op set, the rank-3/4 views and native 16-bit
-# arithmetic, and a Command with no ahead-of-time kernel run by the interpreter
-# and by a kernel compiled at run time ("_jit").
-
-
-def split_workload(name):
-    """("bias_relu_f32", True) for "bias_relu_f32_jit": the workload measured
-    with its kernel compiled at run time."""
-    return (name[:-4], True) if name.endswith("_jit") else (name, False)
-EXTRA = ["copy_f32", "classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "axpby_f16", "axpby_bf16",
-         "bias_relu_f32", "bias_relu_f32_jit", "transposed_relu", "transposed_relu_jit", "odd_rows_f32",
-         "odd_rows_f32_jit", "narrow_rows_f32", "narrow_rows_f32_jit"]
+CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
+# Measured in every run besides the five configurations: the plain copy (the
+# reference for "% of copy") and three programs with no ahead-of-time kernel.
+LINE_EXTRA = ["copy_f32", "bias_relu_f32", "transposed_relu", "mixed_two_out@noaot"]
+# --all adds the widened op set, rank-3/4 views, native 16-bit arithmetic, the
+# gather path and the interpreters.
+ALL_EXTRA = ["classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "axpby_f16", "axpby_bf16",
+             "odd_rows_f32", "narrow_rows_f32", "int_fused_wide", "bias_relu_f32@interp",
+             "transposed_relu@interp", "mixed_two_out@interp", "odd_rows_f32@interp", "narrow_rows_f32@interp"]
 PROFILES = os.path.join(ROOT, "profiles")
+REPS = 50                 # per-launch event pairs, warm and cold
+REPS_SMALL = 200          # the same for the 65,536-element configuration
+BACK_TO_BACK_SMALL = 1000  # its back-to-back launches
 
 
 def log(msg):
@@ -59,20 +72,15 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def setup(wl, n=None, jit=False):
-    import numpy as np
-    import torch
+def split_workload(name):
+    """("bias_relu_f32", "interp") for "bias_relu_f32@interp"; "int_fused_wide"
+    is configuration 1's Command on full-range int32 inputs."""
+    base, _, variant = name.partition("@")
+    return base, variant
 
-    import elementwise_tensor_commands_amd as ecmd
-    import workloads as W
-    spec = W.WORKLOADS[wl]["spec"]
-    vals, extra = W.make_inputs(wl, n)
-    dev = torch.device("cuda:0")
-    gv = W.to_torch(vals, extra, dev)
-    shape = W.shape_of(wl, n)
-    td = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32}
-    out_dt = []
-    dts = {}
+
+def _out_dtypes(spec):
+    dts, outs = {}, []
     for name, st in spec:
         if st[0] in ("load", "scalar"):
             dts[name] = st[1]
@@ -85,24 +93,92 @@ def setup(wl, n=None, jit=False):
         elif st[0] in ("eq", "ne", "lt", "le", "gt", "ge", "ltu", "leu", "gtu", "geu"):
             dts[name] = "i32"
         elif st[0] == "store":
-            out_dt.append(dts[st[1]])
-    outs = [torch.empty(shape, dtype=td[d], device=dev) for d in out_dt]
-    cmd = ecmd.from_spec(spec)
-    if jit:
-        cmd.jit()
-    args = gv + outs
-    plan = cmd.plan(*args)
-    return cmd, args, plan, vals
+            outs.append(dts[st[1]])
+    return outs
 
 
-def time_steps(cmd, args, steps, warmup):
-    """Launch the Command steps times back to back on the current stream, with
-    HIP events at both ends of the timed region.  Returns (total_ms, wall_ms)."""
+def make_host_inputs(name):
+    import numpy as np
+
+    import workloads as W
+    base, _ = split_workload(name)
+    if base == "int_fused_wide":
+        # configuration 1's Command on full-range int32 inputs (wraparound in
+        # nearly every element); seed of configuration 1, plus 100
+        rng = np.random.default_rng(W.seed_of("int_fused") + 100)
+        vals = [rng.integers(-2**31, 2**31, 1 << 24, dtype=np.int64).astype(np.int32) for _ in range(3)]
+        vals.append(W.SCALARS["int_fused"]["s"])
+        return "int_fused", vals, {"storage": [vals[0], vals[1], vals[2], None]}
+    vals, extra = W.make_inputs(base)
+    return base, vals, extra
+
+
+class Setup:
+    """One workload on the GPU: inputs, outputs, the Command and its plan."""
+
+    def __init__(self, name):
+        import torch
+
+        import elementwise_tensor_commands_amd as ecmd
+        import workloads as W
+        self.name = name
+        wl, variant = split_workload(name)
+        self.wl, self.variant = wl, variant
+        spec_wl, vals, extra = make_host_inputs(name)
+        self.spec_wl = spec_wl
+        self.spec = W.WORKLOADS[spec_wl]["spec"]
+        self.vals = vals
+        dev = torch.device("cuda:0")
+        gv = W.to_torch(vals, extra, dev)
+        shape = W.shape_of(spec_wl)
+        td = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32}
+        self.outs = [torch.empty(shape, dtype=td[d], device=dev) for d in _out_dtypes(self.spec)]
+        cmd = ecmd.from_spec(self.spec)
+        if variant == "noaot":
+            cmd.aot(False).jit(ecmd.JIT_SYNC)
+        elif variant == "interp":
+            cmd.aot(False).jit(ecmd.JIT_OFF)
+        elif variant:
+            raise ValueError("unknown variant %r" % variant)
+        self.cmd = cmd
+        self.args = gv + self.outs
+        # Kernels compiled at run time are built (or read from disk) here, off
+        # the clock, as a deployment would with cmd_prepare.
+        self.compiled_from = {-1: None, 0: "memory", 1: "disk", 2: "compiler"}[cmd.prepare(*self.args)]
+        self.plan = cmd.plan(*self.args)
+        self.bytes = W.algorithmic_bytes(spec_wl)
+        self.elements = W.elements(spec_wl)
+        self.read_write = W.algorithmic_read_write(spec_wl)
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(q * len(xs)))]
+
+
+def _stats_us(ms_list):
+    us = [m * 1e3 for m in ms_list]
+    return {"median_us": round(statistics.median(us), 3), "p10_us": round(_pct(us, 0.1), 3),
+            "p90_us": round(_pct(us, 0.9), 3)}
+
+
+class Flusher:
+    """Reads 1 GiB of unrelated data: afterwards none of a Command's data is
+    left in the 256 MB last-level cache (the read leaves no dirty lines)."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+
+    def __call__(self):
+        self.buf.sum()
+
+
+def time_back_to_back(bound, steps):
+    """steps launches back to back between two HIP events on the launch
+    stream: (total ms, host wall ms)."""
     import torch
     stream = torch.cuda.current_stream()
-    bound = cmd.bind(*args, stream=stream)
-    for _ in range(warmup):
-        bound.launch()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -112,24 +188,214 @@ def time_steps(cmd, args, steps, warmup):
         bound.launch()
     end.record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    return start.elapsed_time(end), wall_ms
+    return start.elapsed_time(end), (time.perf_counter() - t0) * 1e3
 
 
-def measure_graph(wl, launches=100, replays=20):
+def time_each(bound, reps, flush=None):
+    """Per-launch HIP event pairs on the launch stream; with flush, the cache
+    is flushed before each launch, outside the pair.  Returns ms per launch."""
+    import torch
+    stream = torch.cuda.current_stream()
+    per = []
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        bound.launch()
+        e.record(stream)
+        e.synchronize()
+        per.append(s.elapsed_time(e))
+    return per
+
+
+def host_launch_us(bound, n=20):
+    """Host wall time per launch call (argument marshalling done once,
+    launches enqueued without waiting), averaged over n calls."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        bound.launch()
+    t = (time.perf_counter() - t0) / n
+    torch.cuda.synchronize()
+    return t * 1e6
+
+
+def ctypes_call_us(n=20000):
+    """Cost of one ctypes call into the library (cmd_version), to separate
+    Python's share of the host launch cost from the library's and HIP's."""
+    import elementwise_tensor_commands_amd as ecmd
+    t0 = time.perf_counter()
+    for _ in range(n):
+        ecmd.cmd_version()
+    return (time.perf_counter() - t0) / n * 1e6
+
+
+def oracle_threads():
+    """Threads for the oracle: the CPUs this process may run on, within the
+    cgroup's CPU quota and OMP_NUM_THREADS (the share of the host the job is
+    given), at least 1."""
+    t = len(os.sched_getaffinity(0))
+    q = cgroup_cpus()
+    if q:
+        t = min(t, max(1, int(q)))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        t = min(t, int(omp))
+    return max(1, t)
+
+
+def cgroup_cpus():
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()
+        return None if quota == "max" else float(quota) / float(period)
+    except (OSError, ValueError):
+        return None
+
+
+def host_snapshot():
+    """CPU model, sockets, cores and SMT from /proc/cpuinfo (read only)."""
+    model, phys, cores, siblings = "", set(), None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and not model:
+                    model = v
+                elif k == "physical id":
+                    phys.add(v)
+                elif k == "cpu cores" and cores is None:
+                    cores = int(v)
+                elif k == "siblings" and siblings is None:
+                    siblings = int(v)
+    except OSError:
+        pass
+    return {"cpu_model": model or platform.processor(), "sockets": len(phys) or None,
+            "cores_per_socket": cores, "threads_per_socket": siblings,
+            "smt": (siblings // cores) if cores and siblings else None,
+            "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cgroup_cpu_quota": cgroup_cpus(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def env_snapshot():
+    """Read-only snapshot of the machine the line was measured on."""
+    import numpy as np
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"gpu": p.name, "gfx": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "hbm_bytes": p.total_memory, "rocm": rocm, "torch_hip": torch.version.hip,
+            "torch": torch.__version__, "numpy": np.__version__, "python": platform.python_version(),
+            "host": host_snapshot()}
+
+
+def ulp_report(got, ref):
+    """Per-element ulp distance in the output's own type (+0 and -0 both 0,
+    NaN against NaN 0): max and histogram {0, 1, 2, >2}."""
+    import numpy as np
+    width = got.itemsize * 8
+    ut = {2: np.uint16, 4: np.uint32}[got.itemsize]
+    gb = np.ascontiguousarray(got).view(ut).ravel().astype(np.int64)
+    rb = np.ascontiguousarray(ref).view(ut).ravel().astype(np.int64)
+    sign = 1 << (width - 1)
+
+    def ordered(b):
+        return np.where(b & sign, -(b & (sign - 1)), b)
+
+    d = np.abs(ordered(gb) - ordered(rb))
+    if got.dtype.kind == "f":
+        ng, nr = np.isnan(got).ravel(), np.isnan(ref).ravel()
+        d = np.where(ng & nr, 0, np.where(ng ^ nr, 1 << 40, d))
+    return {"max_ulp": int(d.max()) if d.size else 0,
+            "hist": {"0": int((d == 0).sum()), "1": int((d == 1).sum()), "2": int((d == 2).sum()),
+                     ">2": int((d > 2).sum())}}
+
+
+def parity(st, threads):
+    """The GPU's outputs of the last launch against the oracle on the same
+    host inputs, every element: mismatches (bitwise; NaN equals NaN), and for
+    outputs of the mixed-precision Command the ulp report."""
+    import numpy as np
+
+    import torch
+    from oracle import oracle
+    t0 = time.perf_counter()
+    ref = oracle.from_spec(st.spec).run(*st.vals, nthreads=threads)
+    oracle_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    res = {"compared": 0, "mismatches": 0, "oracle_threads": threads, "oracle_s": round(oracle_s, 3)}
+    for k, (o, r) in enumerate(zip(st.outs, ref)):
+        g = o.view(torch.int16).cpu().numpy().view(np.uint16) if o.dtype == torch.bfloat16 else o.cpu().numpy()
+        ut = {2: np.uint16, 4: np.uint32}[r.itemsize]
+        gb, rb = g.view(ut).ravel(), np.ascontiguousarray(r).view(ut).ravel()
+        bad = gb != rb
+        if r.dtype.kind == "f":
+            bad &= ~(np.isnan(g).ravel() & np.isnan(r).ravel())
+        res["compared"] += int(gb.size)
+        res["mismatches"] += int(bad.sum())
+        if st.spec_wl == "mixed_two_out":
+            res["out%d_ulp" % k] = ulp_report(g, r)
+    return res, ref, oracle_s
+
+
+def measure(name, steps, warmup, flush, threads, check=True, reps=REPS):
+    """Warm (back-to-back, and per-launch pairs) and cold (flushed before
+    each launch) timings of one workload, its host launch cost and parity."""
+    st = Setup(name)
+    bound = st.cmd.bind(*st.args)
+    small = st.bytes < (64 << 20)
+    for _ in range(warmup):
+        bound.launch()
+    b2b = BACK_TO_BACK_SMALL if small else steps
+    total_ms, wall_ms = time_back_to_back(bound, b2b)
+    reps = max(reps, REPS_SMALL) if small else reps
+    each = time_each(bound, reps)
+    cold = time_each(bound, reps, flush)
+    host_us = host_launch_us(bound)
+    avg_us = total_ms * 1e3 / b2b
+    cold_med = statistics.median(cold) * 1e3
+    r = {
+        "kernel": st.plan["kernel"], "path": st.plan["path"], "grid": st.plan["grid"], "block": st.plan["block"],
+        "elements": st.elements, "algorithmic_bytes": st.bytes,
+        "warm": dict(avg_us=round(avg_us, 3), gbps=round(st.bytes / (avg_us * 1e-6) / 1e9, 1),
+                     launches=b2b, **_stats_us(each)),
+        "cold": dict(gbps=round(st.bytes / (cold_med * 1e-6) / 1e9, 1), launches=reps, **_stats_us(cold)),
+        "gelem_per_s": round(st.elements / (cold_med * 1e-6) / 1e9, 2),
+        "pct_of_peak": round(100 * st.bytes / (cold_med * 1e-6) / 1e9 / PEAK_GBPS, 2),
+        "host_launch_us": round(host_us, 2),
+        "launch_sequence": [warmup, b2b, reps, reps, 20],
+    }
+    if st.compiled_from:
+        r["compiled_from"] = st.compiled_from
+    if small:
+        r["warm"]["host_bound"] = True
+    if check:
+        r["parity"], _, _ = parity(st, threads)
+    return r, st
+
+
+def measure_graph(name, launches=100, replays=20):
     """Back-to-back launches captured in one HIP graph (torch.cuda.CUDAGraph)
     and replayed: the rate once the host's per-launch cost is gone (the
     launch-bound 65,536-element configuration).  Timed by HIP events around
     the replays."""
     import torch
-    import workloads as W
-    cmd, args, plan, _ = setup(wl)
-    bound = cmd.bind(*args)
+    st = Setup(name)
+    bound = st.cmd.bind(*st.args)
     bound.launch()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        cap = cmd.bind(*args)              # the capture stream
+        cap = st.cmd.bind(*st.args)              # the capture stream
         for _ in range(launches):
             cap.launch()
     for _ in range(3):
@@ -142,124 +408,96 @@ def measure_graph(wl, launches=100, replays=20):
     end.record()
     torch.cuda.synchronize()
     per_us = start.elapsed_time(end) * 1e3 / (launches * replays)
-    byts = W.algorithmic_bytes(wl)
-    return {"kernel": plan["kernel"], "launches_per_graph": launches, "replays": replays,
-            "per_launch_us": round(per_us, 3), "gbps": round(byts / (per_us * 1e-6) / 1e9, 1)}
+    return {"kernel": st.plan["kernel"], "launches_per_graph": launches, "replays": replays,
+            "per_launch_us": round(per_us, 3), "gbps": round(st.bytes / (per_us * 1e-6) / 1e9, 1),
+            "launch_sequence": [1, launches * 3 + launches * replays]}
 
 
-def time_each(cmd, args, reps, cold=False):
-    """Per-launch HIP event pairs, optionally reading 1 GiB of unrelated data
-    before each launch (outside the events) so that none of the Command's data
-    is left in the 256 MB last-level cache; reading leaves no dirty lines."""
+def torch_copy_gbps(flush, reps=REPS):
+    """A plain device-to-device copy of 1 GiB (torch's copy_, not this
+    library's code), cold: 2 GiB moved per copy."""
     import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
     stream = torch.cuda.current_stream()
-    bound = cmd.bind(*args, stream=stream)
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0") if cold else None
-    bound.launch()
-    torch.cuda.synchronize()
     per = []
     for _ in range(reps):
-        if cold:
-            flush.sum()
+        flush()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record(stream)
-        bound.launch()
+        dst.copy_(src)
         e.record(stream)
         e.synchronize()
         per.append(s.elapsed_time(e))
-    return per
+    med = statistics.median(per)
+    return {"bytes": 2 << 30, "cold_median_us": round(med * 1e3, 3), "gbps": round((2 << 30) / (med * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(wl, budget_s=20.0):
-    """The oracle as it stands, on the host's cores, over a bounded
-    prefix of the same workload's inputs."""
-    import numpy as np
-
-    import workloads as W
+def cpu_baseline(st, threads, gpu_gbps, budget_s=20.0):
+    """The oracle as it stands, over the headline workload's own inputs (all
+    of them), on `threads` threads and on one: median run of each."""
     from oracle import oracle
-    spec = W.WORKLOADS[wl]["spec"]
-    threads = max(1, min(16, os.cpu_count() or 1))
-    full = W.WORKLOADS[wl].get("n")
-    n = full if wl != "transposed_2d" else 2048
-    if wl in ("axpby_f32", "mixed_two_out", "axpby_f16", "axpby_bf16"):
-        n = 1 << 24
-    shape = {"batched_transpose": (4, 2048, 2048), "bias_nchw": (2, 256, 128, 256), "odd_rows_f32": (2048, 8191),
-             "narrow_rows_f32": (1 << 21, 6)}.get(wl)
-    vals, extra = W.make_inputs(wl, n, shape=shape)
-    cmd = oracle.from_spec(spec)
-    # Repeat each thread count for about half the time budget (at least 3
-    # runs, at most 200) and take the median run.
+    cmd = oracle.from_spec(st.spec)
     res, counts = {}, {}
-    for t in (1, threads):
+    for t in (threads, 1):
         runs = []
-        while len(runs) < 3 or (sum(runs) < budget_s / 2 and len(runs) < 200):
+        while len(runs) < 3 or (sum(runs) < budget_s / 2 and len(runs) < 50):
             t0 = time.perf_counter()
-            cmd.run(*vals, nthreads=t)
+            cmd.run(*st.vals, nthreads=t)
             runs.append(time.perf_counter() - t0)
         res[t] = statistics.median(runs)
         counts[t] = len(runs)
-    elems = W.elements(wl, n, shape)
-    byts = W.algorithmic_bytes(wl, n, shape)
-    best_t = threads
+    byts, elems = st.bytes, st.elements
+    v = byts / res[threads] / 1e9
     return {
-        "value": round(byts / res[best_t] / 1e9, 3), "unit": "GB/s", "cores": best_t, "kind": "oracle",
-        "sample": "%s, first %d elements (%s of the workload), same seeded inputs; median of %d runs "
-                  "(%d on one thread)" % (wl, elems, "all" if elems == W.elements(wl) else "part",
-                                          counts[best_t], counts[1]),
-        "gelem_per_s": round(elems / res[best_t] / 1e9, 4),
-        "single_thread_gbps": round(byts / res[1] / 1e9, 3),
-        "seconds": round(res[best_t], 4),
+        "value": round(v, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": "%s, all %d elements, the same seeded inputs; median of %d runs on %d threads, %d on one"
+                  % (st.name, elems, counts[threads], threads, counts[1]),
+        "seconds": round(res[threads], 4), "gelem_per_s": round(elems / res[threads] / 1e9, 4),
+        "single_thread": {"gbps": round(byts / res[1] / 1e9, 3), "seconds": round(res[1], 3)},
+        "gpu_over_oracle": round(gpu_gbps / v, 1),
+        "gpu_over_oracle_single_thread": round(gpu_gbps / (byts / res[1] / 1e9), 1),
+        "threads_rule": "CPUs in this process's affinity mask, within the cgroup CPU quota and OMP_NUM_THREADS",
+        "host": host_snapshot(),
     }
 
 
-def traffic_from_profiles(wl, kernel_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    the kernels have not changed since it was taken (else None)."""
-    path = os.path.join(ROOT, "profiles", "counters_%s.json" % wl)
+def counters_record(wl, kernel_hash):
+    """The committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary for the
+    workload, if the kernels have not changed since it was taken (else None)."""
+    path = os.path.join(PROFILES, "counters_%s.json" % wl.replace("@", "_"))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         c = json.load(f)
-    if c.get("kernel_source_hash") != kernel_hash:
-        return None
-    return c.get("hbm_bytes_per_launch")
+    return c if c.get("kernel_source_hash") == kernel_hash else None
 
 
-def measure(wl, steps, warmup, cold_too=True, jit=False):
-    """Timed region: steps back-to-back launches between two HIP events on the
-    launch stream.  The kernel's average duration is that time / steps (the
-    host queues launches faster than they run, so the GPU never waits).
-    Separately, per-launch event pairs give median / p10 / p90 and, with a
-    cache flush before each launch, the cold rate."""
-    import workloads as W
-    cmd, args, plan, _ = setup(wl, jit=jit)
-    if jit:
-        log("%s: run-time compiled kernel from %s" % (wl, {0: "memory", 1: "disk", 2: "compiler"}.get(cmd.prepare(*args))))
-    byts = W.algorithmic_bytes(wl)
-    elems = W.elements(wl)
-    total_ms, wall_ms = time_steps(cmd, args, steps, warmup)
-    avg_ms = total_ms / steps
-    per = sorted(time_each(cmd, args, min(steps, 50)))
-    r = {
-        "kernel": plan["kernel"], "grid": plan["grid"], "block": plan["block"],
-        "algorithmic_bytes": byts, "elements": elems,
-        "whole_job_gbps": byts * steps / (total_ms * 1e-3) / 1e9,
-        "kernel_avg_us": avg_ms * 1e3, "kernel_median_us": statistics.median(per) * 1e3,
-        "kernel_p10_us": per[len(per) // 10] * 1e3, "kernel_p90_us": per[(9 * len(per)) // 10] * 1e3,
-        "total_ms": total_ms, "wall_ms": wall_ms,
-    }
-    r["kernel_gbps"] = byts / (avg_ms * 1e-3) / 1e9
-    if cold_too:
-        per_c = time_each(cmd, args, 20, cold=True)
-        r["cold_median_us"] = statistics.median(per_c) * 1e3
-        r["cold_gbps"] = byts / (statistics.median(per_c) * 1e-3) / 1e9
-    return r
+def headline(a, flush, threads, khash):
+    """The contract's K steps of the headline workload, cold: the timed
+    region is K steps, each a flush (outside the events) and one launch
+    between two HIP events; barrier-free (one process), synchronised on both
+    sides."""
+    import torch
+    st = Setup(a.workload)
+    bound = st.cmd.bind(*st.args)
+    for _ in range(a.warmup):
+        bound.launch()
+    torch.cuda.synchronize()
+    per = time_each(bound, a.steps, flush)
+    torch.cuda.synchronize()
+    kernel_ms = sum(per)
+    mean_us = kernel_ms * 1e3 / a.steps
+    gbps = st.bytes * a.steps / (kernel_ms * 1e-3) / 1e9
+    return st, per, mean_us, gbps
 
 
-def read_write_bytes(wl):
-    """Algorithmic bytes read and written by one launch of the workload."""
-    import workloads as W
-    return W.algorithmic_read_write(split_workload(wl)[0])
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries for profiles/.  A profiled run of this script launches
+# the ecmd kernels in the order its JSON line's launch_sequence lists (per
+# workload: warm-up, back-to-back, warm per-launch, cold per-launch, host-cost
+# launches); the summaries split the profiler's ecmd dispatches by that order.
 
 
 def _csv_rows(directory, suffix):
@@ -272,172 +510,277 @@ def _csv_rows(directory, suffix):
     return rows
 
 
-def summarize_counters(root, command):
-    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (root/fetch_<wl>,
-    root/write_<wl>, one per workload plus copy_f32) into profiles/.  Each
-    counter is scaled by what it reads for the plain copy of known size (1 GiB
-    read + 1 GiB written)."""
+def _bench_line(path):
+    with open(path) as f:
+        return json.loads([l for l in f.read().splitlines() if l.startswith("{")][-1])
+
+
+def _split(rows, sequence):
+    """rows: the ecmd dispatches in launch order; sequence: [[workload, [count
+    per phase]], ...].  Returns {workload: [rows of each phase]} for the
+    workloads fully covered."""
+    out, i = {}, 0
+    for name, counts in sequence:
+        if i + sum(counts) > len(rows):
+            break
+        phases = []
+        for c in counts:
+            phases.append(rows[i:i + c])
+            i += c
+        out[name] = phases
+    return out
+
+
+def _order(r):
+    return (int(r.get("Dispatch_Id") or 0), int(r.get("Start_Timestamp") or 0))
+
+
+def summarize_trace(directory, bench_json, command):
+    """profiles/kernel_trace_<workload>.txt and kernel_trace_summary.md from a
+    rocprofv3 --kernel-trace --stats run of this script and the JSON line that
+    run printed: per workload, the kernel's own durations per phase beside the
+    HIP-event figures of the line."""
+    line = _bench_line(bench_json)
+    khash = line["kernel_source_hash"]
+    disp = sorted((r for r in _csv_rows(directory, "kernel_trace.csv") if "ecmd::" in r["Kernel_Name"]), key=_order)
+    stats = {r["Name"]: r for r in _csv_rows(directory, "kernel_stats.csv")}
+    split = _split(disp, line["launch_sequence"])
+    table = ["# Kernel durations: rocprofv3 kernel trace against bench.py's HIP events", "",
+             "Command:", "", "    " + command, "",
+             "kernel source hash: %s" % khash, "",
+             "| workload | kernel | trace cold median us | bench cold median us | diff | trace back-to-back "
+             "mean us | bench back-to-back us | diff |", "|---|---|---|---|---|---|---|---|"]
+
+    def dur_us(rs):
+        return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+
+    for name, phases in split.items():
+        names = sorted({r["Kernel_Name"] for ph in phases for r in ph})
+        text = ["kernel trace: %s" % name, "", "command:", "    " + command, "", "kernels: " + "; ".join(names), ""]
+        if name.startswith("headline:"):
+            steps = dur_us(phases[1])
+            tr, be = statistics.mean(steps), line["roofline"]["kernel_avg_us"]
+            text += ["headline: %d cold steps" % len(steps),
+                     "    trace mean kernel duration: %.3f us" % tr,
+                     "    bench.py HIP-event mean over the same steps: %.3f us" % be,
+                     "    difference: %.2f %%" % (100 * (tr - be) / be),
+                     "    value %s GB/s = %.1f %% of 8 TB/s" % (line["value"], 100 * line["roofline"]["frac"])]
+            table.append("| %s (headline, %d cold steps) | `%s` | %.3f | %.3f | %.2f %% | - | - | - |" % (
+                name, len(steps), names[0][:60], statistics.median(steps), be, 100 * (statistics.median(steps) - be) / be))
+        else:
+            c = line.get("commands", {}).get(name)
+            if not c or "cold" not in c:
+                continue
+            b2b, each, cold = dur_us(phases[1]), dur_us(phases[2]), dur_us(phases[3])
+            rows = [("back-to-back mean", statistics.mean(b2b), c["warm"]["avg_us"]),
+                    ("warm per-launch median", statistics.median(each), c["warm"]["median_us"]),
+                    ("cold per-launch median", statistics.median(cold), c["cold"]["median_us"])]
+            for what, tr, be in rows:
+                text.append("%-24s trace %10.3f us   bench %10.3f us   difference %6.2f %%" % (
+                    what, tr, be, 100 * (tr - be) / be))
+            table.append("| %s | `%s` | %.3f | %.3f | %.2f %% | %.3f | %.3f | %.2f %% |" % (
+                name, names[0][:60], rows[2][1], rows[2][2], 100 * (rows[2][1] - rows[2][2]) / rows[2][2],
+                rows[0][1], rows[0][2], 100 * (rows[0][1] - rows[0][2]) / rows[0][2]))
+        for n in names:
+            if n in stats:
+                text += ["", "rocprofv3 kernel stats row (all dispatches of this kernel name in the run):"]
+                text += ["    %s: %s" % (k, v) for k, v in stats[n].items()]
+        text.append("kernel source hash: %s" % khash)
+        fname = name.replace("headline:", "headline_").replace("@", "_")
+        with open(os.path.join(PROFILES, "kernel_trace_%s.txt" % fname), "w") as out:
+            out.write("\n".join(text) + "\n")
+    with open(os.path.join(PROFILES, "kernel_trace_summary.md"), "w") as out:
+        out.write("\n".join(table) + "\n")
+    print("\n".join(table))
+
+
+def summarize_counters(fetch_dir, fetch_json, write_dir, write_json, command):
+    """profiles/counters_<workload>.json and counters_summary.md from two
+    rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) and the JSON lines they printed.  Each counter is scaled by what
+    it reads for the plain copy copy_f32 (1 GiB read, 1 GiB written); as an
+    independent check of the FETCH_SIZE scale, the cache flush (torch's sum
+    over 1 GiB, a read of known size by code outside this library) is scaled
+    the same way."""
     import workloads as W
-
-    def per_dispatch(kind, wl):
-        rows = [r for r in _csv_rows(os.path.join(root, "%s_%s" % (kind, wl)), "counter_collection.csv")
-                if "ecmd::k_" in r["Kernel_Name"]]
-        assert rows, "no ecmd kernel rows for %s %s" % (kind, wl)
-        names = sorted({r["Kernel_Name"] for r in rows})
-        assert len(names) == 1, names
-        vals = [float(r["Counter_Value"]) for r in rows]
-        return names[0], statistics.mean(vals), len(vals)
-
     khash = kernel_source_hash()
-    cr, cw = read_write_bytes("copy_f32")
-    _, f_copy, _ = per_dispatch("fetch", "copy_f32")
-    _, w_copy, _ = per_dispatch("write", "copy_f32")
-    cal_f, cal_w = cr / (f_copy * 1024), cw / (w_copy * 1024)
-    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
-             "Command (one counter per run, one run per workload):", "", "    " + command, "",
+
+    def per_workload(directory, bench_json):
+        rows = [r for r in _csv_rows(directory, "counter_collection.csv")]
+        ecmd_rows = sorted((r for r in rows if "ecmd::" in r["Kernel_Name"]), key=_order)
+        flush = [float(r["Counter_Value"]) for r in rows
+                 if "ecmd::" not in r["Kernel_Name"] and float(r["Counter_Value"]) > 256 * 1024]
+        line = _bench_line(bench_json)
+        split = _split(ecmd_rows, line["launch_sequence"])
+        res = {}
+        for name, phases in split.items():
+            rs = [r for ph in phases for r in ph]
+            res[name] = (sorted({r["Kernel_Name"] for r in rs}), statistics.mean(float(r["Counter_Value"]) for r in rs),
+                         len(rs))
+        return res, flush
+
+    fetch, flush_f = per_workload(fetch_dir, fetch_json)
+    write, _ = per_workload(write_dir, write_json)
+    assert "copy_f32" in fetch and "copy_f32" in write, "the copy must be measured for the calibration"
+    cr, cw = W.algorithmic_read_write("copy_f32")
+    cal_f, cal_w = cr / (fetch["copy_f32"][1] * 1024), cw / (write["copy_f32"][1] * 1024)
+    flush_kib = statistics.median(flush_f) if flush_f else None
+    lines = ["# L2-to-fabric traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands (one counter per run):", "", "    " + command, "",
+             "These counters count the bytes the L2 caches move to and from the fabric (the last-level "
+             "cache and HBM behind it); they do not tell last-level cache hits from HBM accesses.", "",
              "Calibration: the plain copy `copy_f32` (2^28 fp32: 1 GiB read, 1 GiB written) reads "
              "FETCH_SIZE = %.0f KiB and WRITE_SIZE = %.0f KiB per dispatch, so FETCH_SIZE is scaled by "
-             "%.4f and WRITE_SIZE by %.4f." % (f_copy, w_copy, cal_f, cal_w), "",
-             "kernel source hash: %s" % khash, "",
-             "| workload | kernel | dispatches | FETCH KiB | WRITE KiB | read B (scaled) | algorithmic read B | "
-             "ratio | written B (scaled) | algorithmic write B | ratio |",
-             "|---|---|---|---|---|---|---|---|---|---|---|"]
-    for wl in W.CONFIGS + EXTRA:
-        if not os.path.isdir(os.path.join(root, "fetch_" + wl)):
+             "%.4f and WRITE_SIZE by %.4f." % (fetch["copy_f32"][1], write["copy_f32"][1], cal_f, cal_w), ""]
+    if flush_kib:
+        lines += ["Independent check of the FETCH_SIZE scale: the cache flush (torch's sum over 2^28 fp32, "
+                  "1 GiB read) reads FETCH_SIZE = %.0f KiB per dispatch: scale %.4f from it alone." % (
+                      flush_kib, (1 << 30) / (flush_kib * 1024)), ""]
+    lines += ["kernel source hash: %s" % khash, "",
+              "| workload | kernel | dispatches | FETCH KiB | WRITE KiB | read B (scaled) | algorithmic read B | "
+              "ratio | written B (scaled) | algorithmic write B | ratio |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name in fetch:
+        if name not in write:
             continue
-        name, f, nf = per_dispatch("fetch", wl)
-        _, w, _ = per_dispatch("write", wl)
-        rd, wr = read_write_bytes(wl)
+        base = split_workload(name)[0]
+        spec_wl = "int_fused" if base == "int_fused_wide" else base
+        names, f, nf = fetch[name]
+        _, w, _ = write[name]
+        rd, wr = W.algorithmic_read_write(spec_wl)
         fb, wb = f * 1024 * cal_f, w * 1024 * cal_w
-        rec = {"workload": wl, "kernel": name, "dispatches": nf, "fetch_kib_per_dispatch": f,
+        rec = {"workload": name, "kernel": names, "dispatches": nf, "fetch_kib_per_dispatch": f,
                "write_kib_per_dispatch": w, "fetch_scale": cal_f, "write_scale": cal_w,
+               "fetch_scale_from_flush": (1 << 30) / (flush_kib * 1024) if flush_kib else None,
                "read_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                "hbm_bytes_per_launch": fb + wb, "algorithmic_read_bytes": rd,
                "algorithmic_write_bytes": wr, "read_ratio": fb / rd if rd else None,
-               "write_ratio": wb / wr,
-               "kernel_source_hash": khash, "command": command}
-        with open(os.path.join(PROFILES, "counters_%s.json" % wl), "w") as out:
+               "write_ratio": wb / wr, "kernel_source_hash": khash, "command": command}
+        with open(os.path.join(PROFILES, "counters_%s.json" % name.replace("@", "_")), "w") as out:
             json.dump(rec, out, indent=1)
         lines.append("| %s | `%s` | %d | %.0f | %.0f | %.0f | %d | %s | %.0f | %d | %.4f |" % (
-            wl, name[:70], nf, f, w, fb, rd, "%.4f" % (fb / rd) if rd else "-", wb, wr, wb / wr))
+            name, names[0][:70], nf, f, w, fb, rd, "%.4f" % (fb / rd) if rd else "-", wb, wr, wb / wr))
     with open(os.path.join(PROFILES, "counters_summary.md"), "w") as out:
         out.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def summarize_trace(directory, wl, bench_json, command):
-    """profiles/kernel_trace_<wl>.txt from a rocprofv3 --kernel-trace --stats
-    run of bench.py and the JSON line that same run printed."""
-    rows = [r for r in _csv_rows(directory, "kernel_stats.csv") if "ecmd::k_" in r["Name"]]
-    assert len(rows) == 1, [r["Name"] for r in rows]
-    r = rows[0]
-    with open(bench_json) as f:
-        line = json.loads([l for l in f.read().splitlines() if l.startswith("{")][-1])
-    prof_us = float(r["AverageNs"]) / 1e3
-    bench_us = line["roofline"]["kernel_avg_us"]
-    text = ["kernel trace: %s" % wl, "", "command:", "    " + command, "",
-            "rocprofv3 kernel stats (ecmd kernel row):"]
-    text += ["    %s: %s" % (k, v) for k, v in r.items()]
-    text += ["", "bench.py HIP-event average over the same run's timed launches: %.3f us" % bench_us,
-             "rocprofv3 average over all dispatches (warm-up + timed): %.3f us" % prof_us,
-             "difference: %.2f %%" % (100 * (prof_us - bench_us) / bench_us),
-             "bench value: %s %s; roofline achieved %s GB/s = %.1f %% of %s GB/s" % (
-                 line["value"], line["unit"], line["roofline"]["achieved"], 100 * line["roofline"]["frac"],
-                 line["roofline"]["peak"]),
-             "kernel source hash: %s" % kernel_source_hash()]
-    with open(os.path.join(PROFILES, "kernel_trace_%s.txt" % wl), "w") as out:
-        out.write("\n".join(text) + "\n")
-    print("\n".join(text))
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="int_fused")
-    ap.add_argument("--all", action="store_true", help="also measure every other workload")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--all", action="store_true", help="also measure the further workloads")
+    ap.add_argument("--only", default="", help="comma-separated workloads to measure under commands "
+                                               "(instead of the default set)")
+    ap.add_argument("--no-commands", action="store_true", help="the headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold (cache-flushed) launches, e.g. under a kernel-trace profiler")
-    ap.add_argument("--summarize-counters", metavar="DIR",
-                    help="write profiles/ counter summaries from rocprofv3 --pmc output in DIR and exit")
+    ap.add_argument("--no-parity", action="store_true", help="skip the full-size oracle comparisons")
+    ap.add_argument("--reps", type=int, default=REPS, help="per-launch event pairs per workload, warm and cold")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "FETCH_JSON", "WRITE_DIR", "WRITE_JSON"),
+                    help="write profiles/ counter summaries from two rocprofv3 --pmc runs of this script and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "BENCH_JSON"),
-                    help="write profiles/kernel_trace_<workload>.txt from a kernel-trace run and exit")
+                    help="write profiles/kernel_trace_*.txt from a kernel-trace run of this script and exit")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     a = ap.parse_args()
     if a.summarize_counters:
-        summarize_counters(a.summarize_counters, a.command)
+        summarize_counters(*a.summarize_counters, a.command)
         return
     if a.summarize_trace:
-        summarize_trace(a.summarize_trace[0], a.workload, a.summarize_trace[1], a.command)
+        summarize_trace(*a.summarize_trace, a.command)
         return
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
+
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     khash = kernel_source_hash()
-    base, jit = split_workload(a.workload)
-    label = W.WORKLOADS[base]["label"] + (" (kernel compiled at run time)" if jit else "")
-    log("workload %s: %s" % (a.workload, label))
-    head = measure(base, a.steps, a.warmup, cold_too=not a.no_cold, jit=jit)
-    log("headline %s: %.1f GB/s whole-job, kernel avg %.2f us" % (head["kernel"], head["whole_job_gbps"], head["kernel_avg_us"]))
-    traffic = traffic_from_profiles(a.workload, khash)
+    threads = oracle_threads()
+    flush = Flusher()
+    base, variant = split_workload(a.workload)
+    label = W.WORKLOADS[base]["label"] + (" (%s)" % variant if variant else "")
+    log("headline %s: %s, %d cold steps" % (a.workload, label, a.steps))
+    st, per, mean_us, gbps = headline(a, flush, threads, khash)
+    log("headline %s: %.1f GB/s cold, kernel mean %.2f us" % (st.plan["kernel"], gbps, mean_us))
+    cnt = counters_record(a.workload, khash)
     line = {
         "metric": METRIC,
-        "value": round(head["whole_job_gbps"], 2),
+        "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(head["total_ms"] / a.steps, 6),
+        "ms_per_step": round(mean_us / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_OF[base],
-        "data": "synthetic (seeded NumPy PCG64, seed 1000 + config index), resident in HBM",
-        "config": {"workload": label, "elements": head["elements"],
-                   "algorithmic_bytes_per_step": head["algorithmic_bytes"], "kernel": head["kernel"],
-                   "grid": head["grid"], "block": head["block"]},
-        "pct_of_peak": round(100 * head["whole_job_gbps"] / PEAK_GBPS, 2),
-        "gelem_per_s": round(head["elements"] * a.steps / (head["total_ms"] * 1e-3) / 1e9, 3),
-        "cold": ({"median_us": round(head["cold_median_us"], 3), "gbps": round(head["cold_gbps"], 2)}
-                 if "cold_median_us" in head else None),
+        "data": "synthetic (seeded NumPy PCG64, seed 1000 + config index), resident in HBM; "
+                "each step cold (last-level cache flushed before it, outside its HIP events)",
+        "config": {"workload": label, "elements": st.elements,
+                   "algorithmic_bytes_per_step": st.bytes, "kernel": st.plan["kernel"],
+                   "grid": st.plan["grid"], "block": st.plan["block"]},
+        "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "gelem_per_s": round(st.elements * a.steps / (sum(per) * 1e-3) / 1e9, 3),
+        "step_us": _stats_us(per),
         "roofline": {
-            "bound": "hbm", "achieved": round(head["kernel_gbps"], 2), "peak": PEAK_GBPS, "unit": "GB/s",
-            "frac": round(head["kernel_gbps"] / PEAK_GBPS, 4),
-            "traffic": traffic,
-            "kernel_avg_us": round(head["kernel_avg_us"], 3),
+            "bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_GBPS, 4),
+            "traffic": cnt["hbm_bytes_per_launch"] if cnt else None,
+            "kernel_avg_us": round(mean_us, 3),
         },
         "kernel_source_hash": khash,
     }
-    if a.all:
+    if cnt:
+        line["roofline"]["traffic_counters"] = {
+            "what": "L2-to-fabric bytes per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE), scaled by the plain "
+                    "copy's reading; MALL hits are not told apart from HBM",
+            "fetch_kib_raw": cnt["fetch_kib_per_dispatch"], "write_kib_raw": cnt["write_kib_per_dispatch"],
+            "fetch_scale": cnt["fetch_scale"], "write_scale": cnt["write_scale"],
+            "read_ratio": cnt["read_ratio"], "write_ratio": cnt["write_ratio"]}
+    if not a.no_parity:
+        log("oracle on %d threads: full-size parity of the headline" % threads)
+        line["parity"], _, _ = parity(st, threads)
+        log("headline parity: %s" % json.dumps(line["parity"]))
+    line["launch_sequence"] = [["headline:" + a.workload, [a.warmup, a.steps]]]
+    if not a.no_commands:
+        names = a.only.split(",") if a.only else CONFIGS + LINE_EXTRA + (ALL_EXTRA if a.all else [])
         line["commands"] = {}
-        for wl in W.CONFIGS + EXTRA:
-            if wl == a.workload:
-                r = head
-            else:
-                log("measuring %s" % wl)
-                wl_base, wl_jit = split_workload(wl)
-                r = measure(wl_base, min(a.steps, 100), a.warmup, jit=wl_jit)
-            line["commands"][wl] = {
-                "kernel": r["kernel"], "gbps": round(r["kernel_gbps"], 1),
-                "pct_of_peak": round(100 * r["kernel_gbps"] / PEAK_GBPS, 2),
-                "avg_us": round(r["kernel_avg_us"], 3),
-                "median_us": round(r["kernel_median_us"], 3), "p10_us": round(r["kernel_p10_us"], 3),
-                "p90_us": round(r["kernel_p90_us"], 3), "cold_median_us": round(r["cold_median_us"], 3),
-                "cold_gbps": round(r["cold_gbps"], 1), "whole_job_gbps": round(r["whole_job_gbps"], 1),
-                "gelem_per_s": round(r["elements"] / (r["kernel_avg_us"] * 1e-6) / 1e9, 2),
-            }
-            log("%s: %s" % (wl, json.dumps(line["commands"][wl])))
-        line["commands"]["add_f32_graph"] = measure_graph("add_f32")
-        log("add_f32_graph: %s" % json.dumps(line["commands"]["add_f32_graph"]))
+        for name in names:
+            log("measuring %s" % name)
+            r, s2 = measure(name, max(a.steps, 50), a.warmup, flush, threads, check=not a.no_parity, reps=a.reps)
+            line["launch_sequence"].append([name, r.pop("launch_sequence")])
+            line["commands"][name] = r
+            del s2
+            torch.cuda.empty_cache()
+            log("%s: %s" % (name, json.dumps(r)))
+        if "add_f32" in names:
+            g = measure_graph("add_f32")
+            line["launch_sequence"].append(["add_f32@graph", g.pop("launch_sequence")])
+            line["commands"]["add_f32@graph"] = g
+            log("add_f32@graph: %s" % json.dumps(g))
+        copies = {}
+        if "copy_f32" in line["commands"]:
+            copies["copy_f32"] = line["commands"]["copy_f32"]["cold"]["gbps"]
+        tc = torch_copy_gbps(flush)
+        line["torch_copy"] = tc
+        copies["torch_copy"] = tc["gbps"]
+        ref_name = max(copies, key=copies.get)
+        line["copy_reference"] = {"workload": ref_name, "cold_gbps": copies[ref_name],
+                                  "rule": "the faster plain 1 GiB copy of this run, cold"}
+        for name, r in line["commands"].items():
+            if "cold" in r:
+                r["pct_of_copy"] = round(100 * r["cold"]["gbps"] / copies[ref_name], 2)
+        line["pct_of_copy"] = round(100 * gbps / copies[ref_name], 2)
+        line["ctypes_call_us"] = round(ctypes_call_us(), 3)
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline(base)
+        line["cpu_baseline"] = cpu_baseline(st, threads, gbps)
+    line["env"] = env_snapshot()
     print(json.dumps(line), flush=True)
 
 

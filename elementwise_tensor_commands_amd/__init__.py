@@ -30,7 +30,8 @@ E_CMP = {"eq": 6, "ne": 7, "lt": 8, "le": 9, "gt": 10, "ge": 11, "ltu": 12, "leu
 E_MIN, E_MAX, E_ABS, E_SELECT = 16, 17, 18, 19
 ARG_TENSOR, ARG_SCALAR = 1, 2
 PATH_NONE, PATH_LINEAR, PATH_TILED, PATH_GATHER, PATH_ROWS = 0, 1, 2, 3, 4
-OPT_JIT = 1
+OPT_JIT, OPT_AOT = 1, 2
+JIT_OFF, JIT_SYNC, JIT_BACKGROUND = 0, 1, 2
 PATH_NAMES = {0: "none", 1: "linear", 2: "tiled", 3: "gather", 4: "rows"}
 STATUS = {
     0: "CMD_OK", -1: "CMD_E_ARG", -2: "CMD_E_TAG", -3: "CMD_E_DTYPE", -4: "CMD_E_SHAPE",
@@ -217,10 +218,20 @@ class Command:
         return arg.value
 
     # -- run-time compiled kernels ---------------------------------------------
-    def jit(self, enable: bool = True) -> "Command":
-        """Compile a kernel for this Command's program at its first launch when
-        the library has none ahead of time (CMD_OPT_JIT); returns self."""
-        self._check(lib.cmd_set_option(self._h, OPT_JIT, 1 if enable else 0))
+    def jit(self, mode=JIT_SYNC) -> "Command":
+        """How a program with no ahead-of-time kernel runs (CMD_OPT_JIT):
+        JIT_SYNC (or True) compiles its kernel at the first launch, JIT_BACKGROUND
+        (the default) compiles it in a background thread and runs the
+        interpreter meanwhile, JIT_OFF (or False) always interprets; returns self."""
+        mode = JIT_SYNC if mode is True else JIT_OFF if mode is False else int(mode)
+        self._check(lib.cmd_set_option(self._h, OPT_JIT, mode))
+        return self
+
+    def aot(self, enable: bool = True) -> "Command":
+        """Whether a program on the ahead-of-time list runs its specialised
+        kernel (CMD_OPT_AOT); off, it is compiled at run time or interpreted
+        like any other program (for comparisons); returns self."""
+        self._check(lib.cmd_set_option(self._h, OPT_AOT, 1 if enable else 0))
         return self
 
     def prepare(self, *values) -> int:

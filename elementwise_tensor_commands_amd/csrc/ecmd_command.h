@@ -7,6 +7,7 @@
 // launch (or plan, dump, program query) it is frozen and lowered to a Program.
 #pragma once
 
+#include <memory>
 #include <string>
 #include <utility>
 #include <vector>
@@ -34,6 +35,15 @@ struct ArgDecl {
 // Set the message cmd_last_error(NULL) returns (failures without a handle).
 void set_create_error(const char *msg);
 
+// What the last launch on a handle prepared (defined by the launch code), kept
+// so that a launch with the same argument values skips validation and packing.
+struct LaunchCacheBase {
+    virtual ~LaunchCacheBase() = default;
+};
+
+// Run-time compilation modes (CMD_OPT_JIT values).
+enum { JIT_OFF = 0, JIT_SYNC = 1, JIT_BACKGROUND = 2 };
+
 }  // namespace ecmd
 
 struct ecmd_command {
@@ -41,11 +51,13 @@ struct ecmd_command {
     std::vector<ecmd::ArgDecl> args;
     std::vector<std::pair<int, int>> stores;  // (tag, arg)
     bool frozen = false;
-    bool jit = false;                         // compile kernels for Programs without an ahead-of-time one
+    int jit = ecmd::JIT_BACKGROUND;           // kernels for Programs without an ahead-of-time one (JIT_*)
+    bool aot = true;                          // use the ahead-of-time specialised kernels
     int lower_status = 1;                     // 1 = not lowered yet
     ecmd::Program prog{};
     int in_arg[ecmd::kMaxIn];                 // CommandArgument index of input k
     int uni_arg[ecmd::kMaxUni];
     int out_arg[ecmd::kMaxOut];
     std::string err;
+    std::unique_ptr<ecmd::LaunchCacheBase> launch_cache;
 };

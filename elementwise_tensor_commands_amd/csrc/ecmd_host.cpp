@@ -338,10 +338,11 @@ int64_t env_int(const char *name, int64_t dflt)
 //   Stores are nontemporal by default (ECMD_NT_STORE=0 turns it off): with G = 4
 //   every store instruction covers whole cache lines, and streaming them past
 //   the caches raised every workload's rate.
-//   Loads are nontemporal when the launch moves more than kMallBytes (the
+//   Loads are nontemporal when the launch moves at least kMallBytes (the
 //   256 MB last-level Infinity Cache): such data cannot stay cached between
-//   launches anyway.  Smaller working sets use ordinary loads so that repeated
-//   launches can hit in that cache.  ECMD_NT_LOAD=0/1 overrides.
+//   launches anyway, and streaming past the caches is the faster way to read
+//   it from HBM.  Smaller working sets use ordinary loads so that data a
+//   previous kernel left in that cache can hit.  ECMD_NT_LOAD=0/1 overrides.
 constexpr int64_t kMallBytes = (int64_t)256 << 20;
 constexpr int kDefaultTileM = 32, kDefaultTileN = 256, kDefaultTileBlock = 256, kDefaultTileWalk = 1;
 
@@ -351,7 +352,7 @@ constexpr int kDefaultTileM = 32, kDefaultTileN = 256, kDefaultTileBlock = 256, 
 // 5.1 against 6.5 TB/s for the 16-bit axpby).
 LinearShape linear_shape(int64_t bytes, bool all16 = false)
 {
-    LinearShape s{all16 ? 8 : 4, all16 ? 8 : 4, bytes > kMallBytes, true};
+    LinearShape s{all16 ? 8 : 4, all16 ? 8 : 4, bytes >= kMallBytes, true};
     const char *v = std::getenv("ECMD_LINEAR_SHAPE");
     if (v && std::strcmp(v, "8x8") == 0) s.e = 8, s.g = 8;
     if (v && std::strcmp(v, "8x4") == 0) s.e = 8, s.g = 4;
@@ -653,7 +654,9 @@ void size_interp(const Program &P, Selection &S)
     S.block = kInterpBlock;
 }
 
-void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
+// allow_jit: a Program without an ahead-of-time kernel may take a run-time
+// compiled one (else the path's interpreter).
+void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow_jit)
 {
     const Program &P = h->prog;
     const int64_t numel = B.numel;
@@ -662,7 +665,11 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         S.name = "none";
         return;
     }
+    // ECMD_FORCE_GENERIC: the interpreters only (A/B runs and tests);
+    // CMD_OPT_AOT 0: no ahead-of-time kernel (run-time compiled or interpreted).
     const bool force_generic = env_flag("ECMD_FORCE_GENERIC");
+    const bool no_aot = force_generic || !h->aot;
+    allow_jit = allow_jit && !force_generic;
     S.cn = canonicalize(P, B);
     const Canon &C = S.cn;
     bool all_flat = C.dims == 1;
@@ -676,8 +683,8 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
     if (all_flat && (flat_vec || numel >= kMaxGridItems || env_int("ECMD_GATHER_MODE", 1) == 0)) {
         S.path = CMD_PATH_LINEAR;
         S.vec = flat_vec;
-        S.variant = (S.vec && !force_generic) ? program_match_linear(P) : -1;
-        S.jit = S.vec && !force_generic && S.variant < 0 && h->jit;
+        S.variant = (S.vec && !no_aot) ? program_match_linear(P) : -1;
+        S.jit = S.vec && S.variant < 0 && allow_jit;
         int64_t bytes = 0;
         bool all16 = true;
         for (int k = 0; k < P.n_in; ++k) bytes += numel * esize(B.in[k].dtype), all16 = all16 && esize(B.in[k].dtype) == 2;
@@ -730,8 +737,8 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         if (rows && n_vec < kMaxGridItems && per_row < kMaxGridItems) {
             S.path = CMD_PATH_ROWS;
             std::memcpy(S.rowconst, rowconst, sizeof rowconst);
-            S.variant = force_generic ? -1 : program_match_linear(P);
-            S.jit = !force_generic && S.variant < 0 && h->jit;
+            S.variant = no_aot ? -1 : program_match_linear(P);
+            S.jit = S.variant < 0 && allow_jit;
             S.vec = true;
             S.e = 4;
             S.block = kRowsBlock;
@@ -828,12 +835,12 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
         std::memcpy(S.rowconst, rowconst, sizeof rowconst);
         bool any_rowconst = false;
         for (int k = 0; k < P.n_in; ++k) any_rowconst = any_rowconst || rowconst[k];
-        S.variant = (!force_generic && !any_rowconst && std::memcmp(&P, &kProgAddScaledF32, sizeof(Program)) == 0 &&
+        S.variant = (!no_aot && !any_rowconst && std::memcmp(&P, &kProgAddScaledF32, sizeof(Program)) == 0 &&
                      mask == 0x2) ? 0 : -1;
         S.tile = S.variant == 0 ? tile_shape() : TileShape{64, 64, 256};   // RtEval has one shape
         S.lds = n_staged * S.tile.tn * S.tile.tm * 4;
         S.mask = mask;
-        if (S.variant < 0 && !force_generic && h->jit && !any_rowconst) {
+        if (S.variant < 0 && allow_jit && !any_rowconst) {
             // A kernel compiled at run time on 32 x 256 tiles with 512
             // work-items: four chunks per work-item, whose direct inputs it
             // holds in registers (with 256 work-items, eight: max(X + 2 Y^T, 0)
@@ -901,7 +908,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S)
     // On request (CMD_OPT_JIT) a kernel compiled for the Program
     // (ecmd_kern_gather.h): 64 kGatherCcE elements per wavefront, registers
     // instead of the LDS file.
-    const bool g_jit = h->jit && !force_generic;
+    const bool g_jit = allow_jit;
     int gce = (int)env_int("ECMD_GATHER_JIT_E", kGatherCcE);   // A/B runs: 4, 8 or 16
     if (gce != 4 && gce != 16) gce = kGatherCcE;
     if (rows < lim && n3 < lim && env_int("ECMD_GATHER_MODE", 1) != 0) {
@@ -974,14 +981,14 @@ JitRequest jit_request(const Selection &S, const Program &P)
     return JitRequest{JIT_TILED, 4, 4, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
 }
 
-int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int cu_count)
+int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int cu_count, bool allow_jit)
 {
     h->frozen = true;
     int rc = lower(h);
     if (rc) return rc;
     rc = bind(h, args, nargs, B);
     if (rc) return rc;
-    select_path(h, B, cu_count, S);
+    select_path(h, B, cu_count, S, allow_jit);
     return CMD_OK;
 }
 
@@ -1068,6 +1075,133 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
     A.prog = h->prog;
 }
 
+// A launch ready to enqueue: the argument values it was made for, the bound
+// views, the selection and its packed argument blocks.  Kept per handle, so a
+// launch with the same values (byte for byte) and device reuses it; the
+// environment's A/B knobs are read when a plan is made.
+struct LaunchPlan : ecmd::LaunchCacheBase {
+    int dev = -1;
+    std::vector<cmd_arg> args;
+    Bound B;
+    Selection S;
+    LinearArgs LA;
+    StridedArgs SA;
+    InterpTape T;
+    bool tiled_nt = true;         // tiled kernels: nontemporal global accesses
+    hipFunction_t fn = nullptr;   // S.jit: the loaded run-time compiled kernel
+    bool pending = false;         // S is the interpreter while S_jit's kernel compiles
+    Selection S_jit;
+};
+
+bool capturing(void *stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+}
+
+// The argument blocks of L.S.
+void pack(cmd_t h, LaunchPlan &L)
+{
+    const Selection &S = L.S;
+    const Bound &B = L.B;
+    if (S.path == CMD_PATH_LINEAR) {
+        LinearArgs &A = L.LA;
+        std::memset(static_cast<void *>(&A), 0, sizeof A);   // padding too
+        for (int k = 0; k < h->prog.n_in; ++k) A.in[k] = B.in[k].ptr;
+        for (int k = 0; k < h->prog.n_out; ++k) A.out[k] = B.out[k].ptr;
+        A.n = B.numel;
+        std::memcpy(A.uni, B.uni, sizeof A.uni);
+        A.flags = S.xcd_remap ? kLinearXcdRemap : 0u;
+        A.prog = h->prog;
+    } else {
+        fill_strided(h, B, S, L.SA);
+        L.tiled_nt = tiled_nt();
+    }
+    if (S.interp)
+        resolve_interp_tape(h->prog, S.k_sub, L.T,
+                            S.path == CMD_PATH_TILED ? (uint32_t)(S.tile.tm * S.tile.tn * 4) : 0u);
+}
+
+// A plan running the interpreter while its compiled kernel is built: switch
+// to the kernel once it is ready (its module is loaded outside stream
+// capture only); stop asking if the compile failed.
+void upgrade_plan(cmd_t h, LaunchPlan &L, void *stream)
+{
+    std::string err;
+    const JitRequest req = jit_request(L.S_jit, h->prog);
+    const int st = jit_poll(req, false, err);
+    if (st == JIT_COMPILING) return;
+    if (st != JIT_READY) {          // failed: the interpreter stays
+        L.pending = false;
+        return;
+    }
+    if (capturing(stream)) return;
+    hipFunction_t fn;
+    if (jit_loaded_function(req, &fn, err) != 0) {
+        L.pending = false;
+        return;
+    }
+    if (env_flag("ECMD_DUMP_TAPE"))
+        std::fprintf(stderr, "[ecmd] compiled kernel ready: %s replaces %s\n", L.S_jit.name, L.S.name);
+    L.S = L.S_jit;
+    L.fn = fn;
+    L.pending = false;
+    pack(h, L);
+}
+
+// Enqueue the plan's kernel(s) on stream; returns a hipError_t.
+int enqueue(cmd_t h, LaunchPlan &L, void *hip_stream)
+{
+    const Selection &S = L.S;
+    const LaunchGeometry g{S.grid, S.block};
+    int herr = 0;
+    if (S.path == CMD_PATH_LINEAR) {
+        LinearArgs &A = L.LA;
+        if (S.jit) {
+            void *params[] = {&A};
+            herr = (int)hipModuleLaunchKernel(L.fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
+                                              (hipStream_t)hip_stream, params, nullptr);
+        } else if (S.interp) {
+            for (int64_t first = 0; first < S.n_wg && herr == 0; first += S.grid) {
+                A.first = first;
+                const LaunchGeometry gi{std::min<int64_t>(S.grid, S.n_wg - first), S.block};
+                herr = launch_linear_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, L.T, gi, S.lds, hip_stream);
+            }
+        } else {
+            herr = launch_linear(S.variant, S.vec, S.shape, A, g, hip_stream);
+        }
+        return herr;
+    }
+    StridedArgs &A = L.SA;
+    const bool nt = L.tiled_nt;
+    if (S.jit) {
+        void *params[] = {&A};
+        if (S.path == CMD_PATH_GATHER) {      // dispatches of S.grid work-groups of four wavefronts
+            for (int64_t first = 0; first < S.g_waves && herr == 0; first += 4 * S.grid) {
+                A.g_first = (uint32_t)first;
+                const int64_t wg = std::min<int64_t>(S.grid, (S.g_waves - first + 3) / 4);
+                herr = (int)hipModuleLaunchKernel(L.fn, (unsigned)wg, 1, 1, (unsigned)g.block, 1, 1, 0u,
+                                                  (hipStream_t)hip_stream, params, nullptr);
+            }
+        } else {
+            herr = (int)hipModuleLaunchKernel(L.fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1,
+                                              S.path == CMD_PATH_TILED ? (unsigned)S.lds : 0u,
+                                              (hipStream_t)hip_stream, params, nullptr);
+        }
+        return herr;
+    }
+    (void)h;
+    return S.path == CMD_PATH_TILED
+               ? (S.interp ? launch_tiled_interp(S.tile, nt, A, L.T, g, S.lds, hip_stream)
+                           : launch_tiled(S.variant, nt, S.tile, A, g, hip_stream))
+           : S.path == CMD_PATH_ROWS
+               ? (S.interp ? launch_rows_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, L.T, g, S.lds,
+                                                hip_stream)
+                           : launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream))
+           : S.interp ? launch_gather_split(S, A, L.T, hip_stream)
+                      : launch_gather(A, g, hip_stream);
+}
+
 }  // namespace
 
 void ecmd::set_create_error(const char *msg) { g_create_err = msg; }
@@ -1084,7 +1218,9 @@ int cmd_create(cmd_t *out)
     if (!out) return fail(nullptr, CMD_E_ARG, "out is NULL");
     cmd_t h = new (std::nothrow) ecmd_command();
     if (!h) return fail(nullptr, CMD_E_NOMEM, "out of host memory");
-    h->jit = env_flag("ECMD_JIT");
+    // ECMD_JIT = 0, 1 or 2 sets CMD_OPT_JIT's starting value (else 2)
+    const int64_t jit = env_int("ECMD_JIT", JIT_BACKGROUND);
+    h->jit = jit >= JIT_OFF && jit <= JIT_BACKGROUND ? (int)jit : JIT_BACKGROUND;
     *out = h;
     return CMD_OK;
 }
@@ -1093,8 +1229,15 @@ int32_t cmd_set_option(cmd_t h, int32_t option, int64_t value)
 {
     if (!h) return CMD_E_ARG;
     if (option == CMD_OPT_JIT) {
-        if (value != 0 && value != 1) return fail(h, CMD_E_ARG, "CMD_OPT_JIT takes 0 or 1");
-        h->jit = value == 1;
+        if (value < JIT_OFF || value > JIT_BACKGROUND) return fail(h, CMD_E_ARG, "CMD_OPT_JIT takes 0, 1 or 2");
+        h->jit = (int)value;
+        h->launch_cache.reset();
+        return CMD_OK;
+    }
+    if (option == CMD_OPT_AOT) {
+        if (value != 0 && value != 1) return fail(h, CMD_E_ARG, "CMD_OPT_AOT takes 0 or 1");
+        h->aot = value == 1;
+        h->launch_cache.reset();
         return CMD_OK;
     }
     return fail(h, CMD_E_ARG, "unknown option %d", option);
@@ -1105,7 +1248,7 @@ int32_t cmd_prepare(cmd_t h, const cmd_arg *args, int32_t nargs, int32_t *from)
     if (!h) return CMD_E_ARG;
     Bound B;
     Selection S;
-    int rc = prepare(h, args, nargs, B, S, cu_count_cached(0));
+    int rc = prepare(h, args, nargs, B, S, cu_count_cached(0), h->jit != JIT_OFF);
     if (rc) return rc;
     int where = -1;
     if (S.jit) {
@@ -1234,8 +1377,14 @@ int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info)
     Bound B;
     Selection S;
     int dev = 0;
-    int rc = prepare(h, args, nargs, B, S, cu_count_cached(dev));
+    int rc = prepare(h, args, nargs, B, S, cu_count_cached(dev), h->jit != JIT_OFF);
     if (rc) return rc;
+    if (S.jit && h->jit == JIT_BACKGROUND) {
+        // what a launch would run now: the compiled kernel once it is ready
+        // (in memory or on disk), else the interpreter; starts no compile
+        std::string err;
+        if (jit_poll(jit_request(S, h->prog), false, err) != JIT_READY) select_path(h, B, cu_count_cached(dev), S, false);
+    }
     std::memset(info, 0, sizeof *info);
     info->path = S.path;
     info->specialised = S.variant >= 0;
@@ -1256,15 +1405,31 @@ int cmd_plan(cmd_t h, const cmd_arg *args, int32_t nargs, cmd_plan_info *info)
 int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
 {
     if (!h) return CMD_E_ARG;
+    LaunchPlan *L = static_cast<LaunchPlan *>(h->launch_cache.get());
+    int dev = 0;
+    // The same argument values as the last launch on this handle: checked and
+    // packed then, so the launch goes straight to the kernel.
+    if (L && nargs == (int)L->args.size() && nargs > 0 && args &&
+        std::memcmp(args, L->args.data(), sizeof(cmd_arg) * (size_t)nargs) == 0) {
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(h, CMD_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+        if (dev == L->dev) {
+            if (L->pending) upgrade_plan(h, *L, hip_stream);
+            const int herr = enqueue(h, *L, hip_stream);
+            if (herr != 0)
+                return fail(h, CMD_E_LAUNCH, "%s launch failed: %s", L->S.name, hipGetErrorString((hipError_t)herr));
+            h->err.clear();
+            return CMD_OK;
+        }
+    }
     h->frozen = true;
     int rc = lower(h);
     if (rc) return rc;
-    Bound B;
-    rc = bind(h, args, nargs, B);
+    auto plan = std::make_unique<LaunchPlan>();
+    rc = bind(h, args, nargs, plan->B);
     if (rc) return rc;
-    if (B.numel == 0) return CMD_OK;
+    if (plan->B.numel == 0) return CMD_OK;
     // All checks passed; from here on HIP is called.
-    int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(h, CMD_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
     if (dev >= 0 && dev < 64 && g_cu_count[dev] == 0) {
@@ -1273,81 +1438,40 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
         if (e != hipSuccess) return fail(h, CMD_E_LAUNCH, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
         g_cu_count[dev] = cus > 0 ? cus : 256;
     }
-    Selection S;
-    select_path(h, B, cu_count_cached(dev), S);
+    plan->dev = dev;
+    plan->args.assign(args, args + nargs);
+    Selection &S = plan->S;
+    select_path(h, plan->B, cu_count_cached(dev), S, h->jit != JIT_OFF);
+    if (S.jit) {
+        std::string err;
+        const JitRequest req = jit_request(S, h->prog);
+        if (h->jit == JIT_SYNC) {
+            if (jit_function(req, &plan->fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
+        } else {
+            // Background: the compiled kernel if it is ready and its module can
+            // be loaded now (not while the stream is being captured), else the
+            // interpreter until a later launch finds it ready.
+            const int st = jit_poll(req, true, err);
+            if (st == JIT_READY && !capturing(hip_stream) && jit_loaded_function(req, &plan->fn, err) == 0) {
+                // ready: S stays the compiled kernel
+            } else {
+                plan->pending = st == JIT_READY || st == JIT_COMPILING;
+                plan->S_jit = S;
+                S = Selection{};
+                select_path(h, plan->B, cu_count_cached(dev), S, false);
+            }
+        }
+    }
     if (env_flag("ECMD_DUMP_TAPE")) {
         char buf[4096];
         cmd_dump(h, buf, sizeof buf);
         std::fprintf(stderr, "[ecmd] %s grid=%lld block=%d\n%s", S.name, (long long)S.grid, S.block, buf);
     }
-    const LaunchGeometry g{S.grid, S.block};
-    int herr = 0;
-    if (S.path == CMD_PATH_LINEAR) {
-        LinearArgs A;
-        std::memset(static_cast<void *>(&A), 0, sizeof A);   // padding too
-        for (int k = 0; k < h->prog.n_in; ++k) A.in[k] = B.in[k].ptr;
-        for (int k = 0; k < h->prog.n_out; ++k) A.out[k] = B.out[k].ptr;
-        A.n = B.numel;
-        std::memcpy(A.uni, B.uni, sizeof A.uni);
-        A.flags = S.xcd_remap ? kLinearXcdRemap : 0u;
-        A.prog = h->prog;
-        if (S.jit) {
-            hipFunction_t fn;
-            std::string err;
-            if (jit_function(jit_request(S, h->prog), &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
-            void *params[] = {&A};
-            herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
-                                              (hipStream_t)hip_stream, params, nullptr);
-        } else if (S.interp) {
-            InterpTape T;
-            resolve_interp_tape(h->prog, S.k_sub, T);
-            for (int64_t first = 0; first < S.n_wg && herr == 0; first += S.grid) {
-                A.first = first;
-                const LaunchGeometry gi{std::min<int64_t>(S.grid, S.n_wg - first), S.block};
-                herr = launch_linear_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, gi, S.lds, hip_stream);
-            }
-        } else {
-            herr = launch_linear(S.variant, S.vec, S.shape, A, g, hip_stream);
-        }
-    } else {
-        StridedArgs A;
-        fill_strided(h, B, S, A);
-        const bool nt = tiled_nt();
-        if (S.jit) {
-            hipFunction_t fn;
-            std::string err;
-            if (jit_function(jit_request(S, h->prog), &fn, err)) return fail(h, CMD_E_LAUNCH, "%s", err.c_str());
-            void *params[] = {&A};
-            if (S.path == CMD_PATH_GATHER) {      // dispatches of S.grid work-groups of four wavefronts
-                for (int64_t first = 0; first < S.g_waves && herr == 0; first += 4 * S.grid) {
-                    A.g_first = (uint32_t)first;
-                    const int64_t wg = std::min<int64_t>(S.grid, (S.g_waves - first + 3) / 4);
-                    herr = (int)hipModuleLaunchKernel(fn, (unsigned)wg, 1, 1, (unsigned)g.block, 1, 1, 0u,
-                                                      (hipStream_t)hip_stream, params, nullptr);
-                }
-            } else {
-                herr = (int)hipModuleLaunchKernel(fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1,
-                                                  S.path == CMD_PATH_TILED ? (unsigned)S.lds : 0u,
-                                                  (hipStream_t)hip_stream, params, nullptr);
-            }
-        } else {
-            InterpTape T;
-            if (S.interp)
-                resolve_interp_tape(h->prog, S.k_sub, T,
-                                    S.path == CMD_PATH_TILED ? (uint32_t)(S.tile.tm * S.tile.tn * 4) : 0u);
-            herr = S.path == CMD_PATH_TILED
-                       ? (S.interp ? launch_tiled_interp(S.tile, nt, A, T, g, S.lds, hip_stream)
-                                   : launch_tiled(S.variant, nt, S.tile, A, g, hip_stream))
-                   : S.path == CMD_PATH_ROWS
-                       ? (S.interp ? launch_rows_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, T, g, S.lds,
-                                                        hip_stream)
-                                   : launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream))
-                   : S.interp ? launch_gather_split(S, A, T, hip_stream)
-                              : launch_gather(A, g, hip_stream);
-        }
-    }
-    if (herr != 0)
-        return fail(h, CMD_E_LAUNCH, "%s launch failed: %s", S.name, hipGetErrorString((hipError_t)herr));
+    pack(h, *plan);
+    L = plan.get();
+    h->launch_cache = std::move(plan);
+    const int herr = enqueue(h, *L, hip_stream);
+    if (herr != 0) return fail(h, CMD_E_LAUNCH, "%s launch failed: %s", L->S.name, hipGetErrorString((hipError_t)herr));
     h->err.clear();
     return CMD_OK;
 }

@@ -17,6 +17,14 @@
 // the code object.  <dir> is $ECMD_CACHE_DIR, else $XDG_CACHE_HOME/ecmd-amd,
 // else $HOME/.cache/ecmd-amd; files are written to a temporary name and
 // renamed, so concurrent processes never read half a file.
+//
+// Background compiles: jit_poll never waits for the compiler.  A code object
+// that is in memory or on disk is ready at once; otherwise the request goes to
+// one worker thread, which compiles queued requests in order and publishes
+// each code object (or its compile error) under g_mu.  The caller meanwhile
+// runs the interpreter.  The compiler runs outside g_mu, so launches and
+// polls never wait for a compile.  At library unload the worker finishes the
+// compile in progress, drops the rest of the queue and is joined.
 #include "ecmd_jit.h"
 
 #include <hip/hiprtc.h>
@@ -24,12 +32,15 @@
 #include <unistd.h>
 
 #include <cerrno>
+#include <condition_variable>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <deque>
 #include <map>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 namespace ecmd {
@@ -209,27 +220,126 @@ int compile(const JitRequest &r, const std::string &name, Entry &e, std::string 
     return 0;
 }
 
-// With g_mu held: the entry for the request, from memory, disk or the compiler.
+// A code object for the request from disk or the compiler (no lock held).
+int build_entry(const JitRequest &r, const std::string &name, const std::string &key, Entry &e, int *from,
+                std::string &err)
+{
+    const std::string dir = cache_dir();
+    if (!dir.empty() && read_file(dir + "/" + key + ".ecmdjit", r, name, e)) {
+        if (from) *from = 1;
+        return 0;
+    }
+    if (compile(r, name, e, err)) return -1;
+    write_file(dir, key, r, name, e);
+    if (from) *from = 2;
+    return 0;
+}
+
+// Compile state of requests handed to the worker.
+enum { JIT_QUEUED = 1, JIT_FAILED = 2 };
+struct Pending {
+    int state = JIT_QUEUED;
+    std::string err;
+};
+std::map<std::string, Pending> g_pending;     // under g_mu
+
+struct Worker {
+    std::mutex mu;
+    std::condition_variable cv;
+    std::deque<std::pair<std::string, JitRequest>> queue;
+    bool stop = false;
+    std::thread thread;
+
+    void run()
+    {
+        for (;;) {
+            std::pair<std::string, JitRequest> job;
+            {
+                std::unique_lock<std::mutex> lock(mu);
+                cv.wait(lock, [&] { return stop || !queue.empty(); });
+                if (stop) return;
+                job = queue.front();
+                queue.pop_front();
+            }
+            Entry e;
+            std::string err;
+            const int rc = build_entry(job.second, jit_name(job.second), job.first, e, nullptr, err);
+            std::lock_guard<std::mutex> lock(g_mu);
+            if (rc == 0) {
+                g_cache.emplace(job.first, std::move(e));
+                g_pending.erase(job.first);
+            } else {
+                Pending &p = g_pending[job.first];
+                p.state = JIT_FAILED;
+                p.err = err;
+            }
+        }
+    }
+    void submit(const std::string &key, const JitRequest &r)
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (!thread.joinable()) thread = std::thread([this] { run(); });
+        queue.emplace_back(key, r);
+        cv.notify_one();
+    }
+    ~Worker()
+    {
+        {
+            std::lock_guard<std::mutex> lock(mu);
+            stop = true;
+        }
+        cv.notify_all();
+        if (thread.joinable()) thread.join();
+    }
+};
+Worker g_worker;
+
+// The entry for the request, from memory, disk or the compiler.  g_mu is held
+// only to look up and publish, never across a compile.
 int find_or_build(const JitRequest &r, Entry *&out, int *from, std::string &err)
 {
     const std::string name = jit_name(r);
     const std::string key = key_of(r, name);
-    auto it = g_cache.find(key);
-    if (it != g_cache.end()) {
-        out = &it->second;
-        if (from) *from = 0;
-        return 0;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_cache.find(key);
+        if (it != g_cache.end()) {
+            out = &it->second;
+            if (from) *from = 0;
+            return 0;
+        }
     }
     Entry e;
-    const std::string dir = cache_dir();
-    if (!dir.empty() && read_file(dir + "/" + key + ".ecmdjit", r, name, e)) {
-        if (from) *from = 1;
-    } else {
-        if (compile(r, name, e, err)) return -1;
-        write_file(dir, key, r, name, e);
-        if (from) *from = 2;
-    }
+    if (build_entry(r, name, key, e, from, err)) return -1;
+    std::lock_guard<std::mutex> lock(g_mu);
+    // (std::map never moves its elements, so the pointer stays valid)
     out = &g_cache.emplace(key, std::move(e)).first->second;
+    g_pending.erase(key);
+    return 0;
+}
+
+// The loaded function of an entry for device dev (g_mu held).
+int load_function(Entry &e, int dev, hipFunction_t *fn, std::string &err)
+{
+    auto f = e.fn.find(dev);
+    if (f != e.fn.end()) {
+        *fn = f->second;
+        return 0;
+    }
+    hipModule_t mod;
+    hipError_t he = hipModuleLoadData(&mod, e.code.data());
+    if (he != hipSuccess) {
+        err = std::string("hipModuleLoadData: ") + hipGetErrorString(he);
+        return -1;
+    }
+    hipFunction_t k;
+    he = hipModuleGetFunction(&k, mod, e.lowered.c_str());
+    if (he != hipSuccess) {
+        err = std::string("hipModuleGetFunction: ") + hipGetErrorString(he);
+        return -1;
+    }
+    e.fn[dev] = k;         // the module stays loaded for the life of the process
+    *fn = k;
     return 0;
 }
 
@@ -254,7 +364,6 @@ std::string jit_name(const JitRequest &r)
 
 int jit_prepare(const JitRequest &r, int *from, std::string &err)
 {
-    std::lock_guard<std::mutex> lock(g_mu);
     Entry *e = nullptr;
     return find_or_build(r, e, from, err);
 }
@@ -267,29 +376,63 @@ int jit_function(const JitRequest &r, hipFunction_t *fn, std::string &err)
         err = std::string("hipGetDevice: ") + hipGetErrorString(he);
         return -1;
     }
-    std::lock_guard<std::mutex> lock(g_mu);
     Entry *e = nullptr;
     if (find_or_build(r, e, nullptr, err)) return -1;
-    auto f = e->fn.find(dev);
-    if (f != e->fn.end()) {
-        *fn = f->second;
-        return 0;
+    std::lock_guard<std::mutex> lock(g_mu);
+    return load_function(*e, dev, fn, err);
+}
+
+int jit_poll(const JitRequest &r, bool submit, std::string &err)
+{
+    const std::string name = jit_name(r);
+    const std::string key = key_of(r, name);
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (g_cache.count(key)) return JIT_READY;
+        auto p = g_pending.find(key);
+        if (p != g_pending.end()) {
+            if (p->second.state == JIT_FAILED) {
+                err = p->second.err;
+                return JIT_ERROR;
+            }
+            return JIT_COMPILING;
+        }
     }
-    hipModule_t mod;
-    he = hipModuleLoadData(&mod, e->code.data());
+    // A file from an earlier process is read at once (no compiler involved).
+    Entry e;
+    const std::string dir = cache_dir();
+    if (!dir.empty() && read_file(dir + "/" + key + ".ecmdjit", r, name, e)) {
+        std::lock_guard<std::mutex> lock(g_mu);
+        g_cache.emplace(key, std::move(e));
+        return JIT_READY;
+    }
+    if (!submit) return JIT_ABSENT;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (g_cache.count(key)) return JIT_READY;
+        if (g_pending.count(key)) return JIT_COMPILING;
+        g_pending[key] = Pending{};
+    }
+    g_worker.submit(key, r);
+    return JIT_COMPILING;
+}
+
+int jit_loaded_function(const JitRequest &r, hipFunction_t *fn, std::string &err)
+{
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
     if (he != hipSuccess) {
-        err = std::string("hipModuleLoadData: ") + hipGetErrorString(he);
+        err = std::string("hipGetDevice: ") + hipGetErrorString(he);
         return -1;
     }
-    hipFunction_t k;
-    he = hipModuleGetFunction(&k, mod, e->lowered.c_str());
-    if (he != hipSuccess) {
-        err = std::string("hipModuleGetFunction: ") + hipGetErrorString(he);
+    const std::string key = key_of(r, jit_name(r));
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_cache.find(key);
+    if (it == g_cache.end()) {
+        err = "the run-time compiled kernel is not ready";
         return -1;
     }
-    e->fn[dev] = k;         // the module stays loaded for the life of the process
-    *fn = k;
-    return 0;
+    return load_function(it->second, dev, fn, err);
 }
 
 }  // namespace ecmd

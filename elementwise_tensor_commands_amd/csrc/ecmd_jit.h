@@ -43,4 +43,16 @@ int jit_prepare(const JitRequest &r, int *from, std::string &err);
 // The loaded kernel for the current device (prepares it first if needed).
 int jit_function(const JitRequest &r, hipFunction_t *fn, std::string &err);
 
+// Non-blocking state of the request's code object: ready in memory (a file
+// on disk is read into memory first), being compiled by the background
+// worker, failed to compile (err holds the log), or absent.  With submit, an
+// absent request is handed to the worker (and JIT_COMPILING returned).  Host
+// only: no HIP call.
+enum { JIT_READY = 0, JIT_COMPILING = 1, JIT_ERROR = 2, JIT_ABSENT = 3 };
+int jit_poll(const JitRequest &r, bool submit, std::string &err);
+
+// The loaded kernel for the current device when the code object is in memory
+// (loads its module on first use); never compiles.
+int jit_loaded_function(const JitRequest &r, hipFunction_t *fn, std::string &err);
+
 }  // namespace ecmd

@@ -256,7 +256,17 @@ int64_t cmd_dump(cmd_t h, char *buf, int64_t cap);
  * for later processes.  Applies to every path (linear, rows, tiled, gather);
  * on the tiled path only where the staging tiles fit 64 KiB and no input is
  * constant along a row (else the tiled interpreter runs). */
-#define CMD_OPT_JIT 1   /* value 0 (default; the environment variable ECMD_JIT=1 makes it 1) or 1 */
+#define CMD_OPT_JIT 1   /* 0: off (the interpreters run such programs);                           */
+                        /* 1: compile at the first launch that needs the kernel, which waits for  */
+                        /*    the compiler (about half a second for a kernel not on disk);        */
+                        /* 2 (default): compile in a background thread; launches run the          */
+                        /*    interpreter until the kernel is ready, then switch to it (a module  */
+                        /*    is loaded outside stream capture only).  A failed background        */
+                        /*    compile leaves the interpreter in place.                            */
+                        /* The environment variable ECMD_JIT=0, 1 or 2 sets the starting value.   */
+#define CMD_OPT_AOT 2   /* 1 (default): programs on the ahead-of-time list run their specialised */
+                        /* kernel; 0: they are treated like any other program (compiled at run     */
+                        /* time per CMD_OPT_JIT, else interpreted) -- for comparisons.              */
 
 /* Set an option of the handle.  CMD_E_ARG for an unknown option or value. */
 int32_t cmd_set_option(cmd_t h, int32_t option, int64_t value);

@@ -103,3 +103,88 @@ def test_transposed_relu_compiled_and_interpreted(n):
         cmd.launch(*gv, out)
         torch.cuda.synchronize()
         compare(host(out), ref, 0, "transposed_relu n=%d %s" % (n, plan["kernel"]))
+
+
+def _unique_spec(k):
+    """A program no other test compiles (compiled kernels stay in the
+    process's memory): out = min(x * s - y, t) + k-th constant chain."""
+    spec = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("s", ("scalar", "f32")),
+            ("t", ("scalar", "f32")), ("p", ("mul", "x", "s")), ("q", ("sub", "p", "y"))]
+    last = "q"
+    for j in range(k):
+        spec.append(("a%d" % j, ("abs", last)))
+        last = "a%d" % j
+    spec += [("r", ("min", last, "t")), ("o", ("store", "r", 1))]
+    return spec
+
+
+def _background_case(tmp_path, monkeypatch, k, n):
+    import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_CACHE_DIR", str(tmp_path / "bg-cache"))
+    monkeypatch.setenv("ECMD_JIT", "2")
+    spec = _unique_spec(k)
+    rng = np.random.default_rng(500 + k)
+    x, y = rng.standard_normal(n, dtype=np.float32), rng.standard_normal(n, dtype=np.float32)
+    ref = run_oracle(spec, [x, y, np.float32(0.75), np.float32(0.5)])[0]
+    out = torch.empty(n, device=dev())
+    args = [to_dev(x), to_dev(y), 0.75, 0.5, out]
+    cmd = ecmd.from_spec(spec)
+    assert cmd.plan(*args)["kernel"] == "linear_generic"
+    return cmd, args, out, ref
+
+
+def _wait_compiled(cmd, args, limit_s=120):
+    import time
+    t0 = time.time()
+    while not cmd.plan(*args)["compiled"]:
+        assert time.time() - t0 < limit_s, "the background compile did not finish in %d s" % limit_s
+        time.sleep(0.05)
+
+
+def test_background_compile_switches_kernels(tmp_path, monkeypatch, capfd):
+    """Default mode: the first launch of a program with no ahead-of-time
+    kernel runs the interpreter while a worker thread compiles; once the
+    compile is done, the next launch with the same argument values switches
+    to the compiled kernel.  Both results equal the oracle."""
+    n = (1 << 20) + 7
+    cmd, args, out, ref = _background_case(tmp_path, monkeypatch, 1, n)
+    monkeypatch.setenv("ECMD_DUMP_TAPE", "1")
+    bound = cmd.bind(*args)
+    bound.launch()
+    torch.cuda.synchronize()
+    compare(host(out), ref, 0, "interpreter while compiling")
+    _wait_compiled(cmd, args)
+    out.zero_()
+    bound.launch()
+    torch.cuda.synchronize()
+    compare(host(out), ref, 0, "compiled after the switch")
+    err = capfd.readouterr().err
+    assert "linear_generic" in err and "compiled kernel ready: jit_linear replaces linear_generic" in err, err
+
+
+def test_background_compile_and_graph_capture(tmp_path, monkeypatch):
+    """A launch captured while its kernel compiles records the interpreter
+    (no module is loaded during capture); replays stay correct after the
+    compile ends, and eager launches then use the compiled kernel."""
+    n = (1 << 18) + 3
+    cmd, args, out, ref = _background_case(tmp_path, monkeypatch, 2, n)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        cmd.bind(*args).launch()
+    for _ in range(2):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        compare(host(out), ref, 0, "replay while compiling")
+    _wait_compiled(cmd, args)
+    for _ in range(2):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        compare(host(out), ref, 0, "replay after the compile")
+    out.zero_()
+    cmd.launch(*args)
+    torch.cuda.synchronize()
+    compare(host(out), ref, 0, "eager, compiled")
+    assert cmd.plan(*args)["kernel"] == "jit_linear"

@@ -413,16 +413,20 @@ def test_random_commands(seed):
     spec = _random_spec(rng, int(rng.integers(1, 5)), int(rng.integers(1, 12)), rank)
     shape = (int(rng.integers(1, 90)), int(rng.integers(1, 90))) if rank == 2 else (int(rng.integers(1, 5000)),)
     vals = _random_inputs(rng, spec, shape)
-    try:
-        ref = run_oracle(spec, vals)
-    except Exception as e:   # the oracle front end refuses -> the library must refuse too
-        pytest.skip("not a valid Command: %s" % e)
+    from oracle.oracle import OracleError
+    import elementwise_tensor_commands_amd as ecmd
     gv = [to_dev(v) if isinstance(v, np.ndarray) else
           (v if v.dtype == np.uint16 else float(v) if v.dtype.kind == "f" else int(v)) for v in vals]
     if rank == 2 and seed % 2 == 0:       # transposed views of the loads
         gv = [v.t().contiguous().t() if isinstance(v, torch.Tensor) else v for v in gv]
     _, outs = arg_dtypes(spec)
-    import elementwise_tensor_commands_amd as ecmd
+    try:
+        ref = run_oracle(spec, vals)
+    except OracleError as e:   # the oracle refuses the Command: the library must refuse it too
+        with pytest.raises(ecmd.Error) as le:
+            run_gpu(spec, gv, [(shape, d) for d in outs])
+        assert le.value.name != "CMD_E_LAUNCH", le.value
+        return
     try:
         cmd, got = run_gpu(spec, gv, [(shape, d) for d in outs])
     except ecmd.Error as e:

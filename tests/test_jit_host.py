@@ -186,3 +186,41 @@ def test_compiled_code_is_our_rules(cache_dir, tmp_path, spec_name):
         assert "ds_write" in asm and "ds_read" in asm and "s_barrier" in asm
     for bad in ("v_fma", "v_fmac", "v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32", "scratch_", "v_fma_mix"):
         assert bad not in asm, bad
+
+
+def test_options_pick_the_kernel_kind(cache_dir, monkeypatch):
+    """CMD_OPT_AOT 0 sends an ahead-of-time program to the interpreter or to
+    run-time compilation; CMD_OPT_JIT 0 / 1 / 2 (off, at first launch, in the
+    background); bad values are refused."""
+    n = 4096
+    vals = [torch.zeros(n), torch.zeros(n), 1.5, -0.25, torch.zeros(n)]
+    assert E.from_spec(W.AXPBY_F32).plan(*vals)["kernel"] == "linear_axpby_f32"
+    assert E.from_spec(W.AXPBY_F32).aot(False).jit(E.JIT_OFF).plan(*vals)["kernel"] == "linear_generic"
+    c = E.from_spec(W.AXPBY_F32).aot(False).jit(E.JIT_SYNC)
+    assert c.plan(*vals)["kernel"] == "jit_linear"
+    # background mode: the plan names the interpreter until the kernel exists
+    b = E.from_spec(W.AXPBY_F32).aot(False).jit(E.JIT_BACKGROUND)
+    assert b.plan(*vals)["kernel"] == "linear_generic"
+    assert b.prepare(*vals) == 2
+    assert b.plan(*vals)["kernel"] == "jit_linear"
+    for opt, bad in ((E.OPT_JIT, 3), (E.OPT_JIT, -1), (E.OPT_AOT, 2), (99, 0)):
+        rc = E.lib.cmd_set_option(c._h, opt, bad)
+        assert rc == -1 and E.lib.cmd_last_error(c._h)
+
+
+def test_environment_sets_the_starting_mode(cache_dir, monkeypatch):
+    n = 4096
+    vals = [torch.zeros(n), torch.zeros(n), 0.5, 0.0, torch.zeros(n)]
+    monkeypatch.setenv("ECMD_JIT", "1")
+    assert E.from_spec(W.BIAS_RELU_F32).plan(*vals)["kernel"] == "jit_linear"
+    monkeypatch.setenv("ECMD_JIT", "0")
+    assert E.from_spec(W.BIAS_RELU_F32).plan(*vals)["kernel"] == "linear_generic"
+    monkeypatch.delenv("ECMD_JIT")                    # default: background compile
+    # a program no other test compiles (the process keeps compiled kernels in memory)
+    spec = [("x", ("load", "f32", 1)), ("y", ("load", "f32", 1)), ("s", ("scalar", "f32")),
+            ("t", ("scalar", "f32")), ("p", ("mul", "x", "s")), ("q", ("sub", "p", "y")),
+            ("r", ("min", "q", "t")), ("o", ("store", "r", 1))]
+    c = E.from_spec(spec)
+    assert c.plan(*vals)["kernel"] == "linear_generic"  # not compiled yet (fresh cache directory)
+    assert c.prepare(*vals) == 2
+    assert c.plan(*vals)["kernel"] == "jit_linear"
