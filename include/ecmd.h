@@ -66,8 +66,10 @@
  * of the stream, separately from the launch status.
  *
  * Ownership: the caller owns the cmd_t handle (cmd_create / cmd_destroy), every
- * device buffer and the stream.  The library never allocates device memory and
- * keeps no argument pointer after cmd_launch returns.  A handle is not
+ * device buffer and the stream.  The library never allocates device memory.
+ * A handle keeps a copy of its last launch's argument values only to
+ * recognise a repeat (the values are compared, never dereferenced on the
+ * host, and no GPU work refers to them after the call).  A handle is not
  * thread-safe; separate handles are independent.
  */
 #ifndef ECMD_H
@@ -95,8 +97,8 @@ typedef int32_t cmd_tag;
 #define E_NEG 4
 #define E_CVT 5
 /* Comparisons: int32 result 1 (true) or 0 (false).  EQ..GE compare int32 as
- * signed and binary32 as IEEE values; LTU..GEU compare int32 bit patterns as
- * unsigned. */
+ * signed and binary32, binary16 and bfloat16 as IEEE values; LTU..GEU compare
+ * int32 bit patterns as unsigned. */
 #define E_CMP_EQ 6
 #define E_CMP_NE 7
 #define E_CMP_LT 8
@@ -183,9 +185,10 @@ int cmd_scalar(cmd_t h, int32_t dtype, cmd_tag *tag, int32_t *arg_index);
  * T_Execute holds E_ operations on vectors or scalars).  a and b are earlier
  * tags; b must be -1 for E_NEG, E_ABS and E_CVT.  result_dtype must equal the
  * operands' dtype except for E_CVT (the target dtype) and the comparisons
- * (CMD_I32).  E_ADD, E_SUB, E_MUL, E_MIN, E_MAX and E_CMP_EQ..GE accept CMD_F32
- * and CMD_I32 operands of one dtype; E_CMP_LTU..GEU CMD_I32 only.  E_SELECT
- * is refused here (it has three operands: use cmd_select). */
+ * (CMD_I32).  E_ADD, E_SUB, E_MUL, E_MIN, E_MAX, E_NEG, E_ABS and
+ * E_CMP_EQ..GE accept operands of any one of the four dtypes (both operands
+ * the same); E_CMP_LTU..GEU CMD_I32 only.  E_SELECT is refused here (it has
+ * three operands: use cmd_select). */
 int cmd_op(cmd_t h, int32_t opcode, int32_t result_dtype, cmd_tag a, cmd_tag b, cmd_tag *tag);
 /* (result_dtype 0 means the default: int32 for comparisons, the operands'
  * dtype otherwise; E_CVT needs an explicit target.) */
@@ -206,7 +209,12 @@ int cmd_store(cmd_t h, cmd_tag value, int32_t rank, int32_t *arg_index);
  * CommandArgument.  The first call freezes and lowers the Command.  The work
  * is enqueued on hip_stream (a hipStream_t; NULL means the null stream) of the
  * current HIP device and the call returns without waiting.  A shape with no
- * elements succeeds without launching anything. */
+ * elements succeeds without launching anything.  A launch whose argument
+ * values equal the previous launch's on this handle byte for byte, on the
+ * same device, reuses that launch's checks, kernel choice and packed
+ * argument block and goes straight to the kernel; the environment's A/B
+ * variables (ECMD_*) are read when a launch is prepared, not on such a
+ * repeat. */
 int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream);
 
 /* Description of what cmd_launch would do with these arguments. */
