@@ -641,7 +641,7 @@ def summarize_counters(fetch_dir, fetch_json, write_dir, write_json, command):
               "ratio | written B (scaled) | algorithmic write B | ratio |",
               "|---|---|---|---|---|---|---|---|---|---|---|"]
     for name in fetch:
-        if name not in write:
+        if name not in write or name.startswith("headline:") or name.endswith("@graph"):
             continue
         base = split_workload(name)[0]
         spec_wl = "int_fused" if base == "int_fused_wide" else base

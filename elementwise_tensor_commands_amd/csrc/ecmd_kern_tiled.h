@@ -70,16 +70,21 @@ __device__ __forceinline__ int stage_pos(const StridedArgs &A, int k)
 
 __device__ __forceinline__ int clamp4(int64_t left) { return left <= 0 ? 0 : (left >= 4 ? 4 : (int)left); }
 
-template <class EV, int MASK, bool NT, int TM, int TN, int TB>
+// Whether the tile body's tile is full: decided at run time, or known at
+// compile time to be full or to be an edge tile.
+enum TileKind { kTileAny = 0, kTileFull = 1, kTileEdge = 2 };
+
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND>
+__device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, uint32_t b0, uint32_t b1, int64_t r0,
+                                          int64_t c0);
+
+// SPLIT: full and edge tiles run two separate instances of the tile body (see
+// below); otherwise one body tests `full` at each access.
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, bool SPLIT>
 __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
 {
-    constexpr int kWords = TN * TM;
-    constexpr int kSV = TN * TM / 4 / TB;               // staging vectors per work-item per staged input
-    constexpr int kP = TM * TN / 4 / TB;                // chunks per work-item
-    constexpr bool kPrefetch = MASK != kMaskRuntime;
-    static_assert(kSV >= 1 && kP >= 1, "tile too small for the work-group");
+    static_assert(TN * TM / 4 / TB >= 1, "tile too small for the work-group");
     static_assert(TM % 32 == 0 && TN % 32 == 0 && TB % 64 == 0, "tile split needs multiples of 32");
-    extern __shared__ uint32_t lds[];
 
     // Plane and tile coordinates (all counts fit in 32 bits: the grid is one
     // dimension).  Each plane (batch index) has tiles_r x tiles_c tiles.
@@ -104,7 +109,30 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
     }
     const int64_t rows = A.n[2], cols = A.n[3];
     const int64_t r0 = (int64_t)tr * TM, c0 = (int64_t)tc * TN;
-    const bool full = (r0 + TM <= rows) && (c0 + TN <= cols);
+    const bool full = r0 + TM <= rows && c0 + TN <= cols;   // uniform over the work-group
+    if constexpr (SPLIT) {
+        // Two instances of the body: the full tiles' code then holds no masked
+        // per-element path whose registers the compiler could merge with the
+        // vector loads' (hiprtc's build of the one-body form did that, making
+        // every staging load wait for all loads before it).
+        if (full) tile_body<EV, MASK, NT, TM, TN, TB, kTileFull>(A, true, b0, b1, r0, c0);
+        else tile_body<EV, MASK, NT, TM, TN, TB, kTileEdge>(A, false, b0, b1, r0, c0);
+    } else {
+        tile_body<EV, MASK, NT, TM, TN, TB, kTileAny>(A, full, b0, b1, r0, c0);
+    }
+}
+
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND>
+__device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, uint32_t b0, uint32_t b1, int64_t r0,
+                                          int64_t c0)
+{
+    const bool full = KIND == kTileAny ? full_tile : KIND == kTileFull;
+    constexpr int kWords = TN * TM;
+    constexpr int kSV = TN * TM / 4 / TB;               // staging vectors per work-item per staged input
+    constexpr int kP = TM * TN / 4 / TB;                // chunks per work-item
+    constexpr bool kPrefetch = MASK != kMaskRuntime;
+    extern __shared__ uint32_t lds[];
+    const int64_t rows = A.n[2], cols = A.n[3];
     const int t = threadIdx.x;
     // Element offset of this plane in each operand.
     auto in_base = [&](int k) { return (int64_t)b0 * A.in_s[k][0] + (int64_t)b1 * A.in_s[k][1]; };
