@@ -7,10 +7,13 @@ A step is one launch of the whole Command (load, E_ operations, store) over
 the workload's synthetic tensors, resident in HBM before timing starts.  The
 headline workload is the largest configuration on the linear path,
 out = 1.5 x - 0.25 y in binary32 over 2^28 elements (3 GiB moved per step),
-timed cold: before every step a 1 GiB read (outside the step's HIP events)
-evicts the Command's data from the 256 MB last-level cache, so each step reads
-its operands from HBM.  `value` is algorithmic bytes x K / the K steps' summed
-kernel time.
+timed cold: before every step a 1 GiB read evicts the Command's data from the
+256 MB last-level cache, so each step reads its operands from HBM.  Each
+step's kernel time comes from HIP events that the launch's dispatch records at
+its start and end (cmd_launch_timed: what a kernel-trace profiler measures);
+`value` is algorithmic bytes x K / the K steps' summed kernel time.  The same
+steps timed by ordinary events around the launch (dispatch latency included,
+about 5 us more per launch) are reported beside it.
 
 The same JSON line carries, under "commands", the five configurations (and a
 plain copy, the reference for "% of copy", plus three programs with no
@@ -191,23 +194,55 @@ def time_back_to_back(bound, steps):
     return start.elapsed_time(end), (time.perf_counter() - t0) * 1e3
 
 
-def time_each(bound, reps, flush=None):
-    """Per-launch HIP event pairs on the launch stream; with flush, the cache
-    is flushed before each launch, outside the pair.  Returns ms per launch."""
+def _events(stream, n=2):
+    """n timing events, each recorded once (torch creates events lazily)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for ev in evs:
+        ev.record(stream)
+    return evs
+
+
+def time_each(bound, reps, flush=None, pairs=None):
+    """Per-launch kernel durations: the launch's dispatches record a pair of
+    HIP events at their start and end (cmd_launch_timed), as a kernel-trace
+    profiler times a kernel.  With flush, the cache is flushed before each
+    launch.  Returns ms per launch; if pairs is a list, each launch's
+    duration between ordinary events recorded on the stream around it
+    (dispatch latency included) is appended to it."""
     import torch
     stream = torch.cuda.current_stream()
+    ks, ke, s, e = _events(stream, 4)
     per = []
     torch.cuda.synchronize()
     for _ in range(reps):
         if flush is not None:
             flush()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record(stream)
-        bound.launch()
+        bound.launch_timed(ks, ke)
         e.record(stream)
         e.synchronize()
-        per.append(s.elapsed_time(e))
+        per.append(ks.elapsed_time(ke))
+        if pairs is not None:
+            pairs.append(s.elapsed_time(e))
     return per
+
+
+def settle(bound, seconds=0.3, min_launches=20):
+    """Launch back to back for about `seconds` (at least min_launches) so the
+    GPU has left its idle power states before anything is timed: after the
+    seconds of host work that building a workload's inputs takes, the first
+    launches of a run measured up to 1% slower than the same kernel later in
+    the process."""
+    import torch
+    t0 = time.perf_counter()
+    k = 0
+    while k < min_launches or time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            bound.launch()
+        k += 10
+        torch.cuda.synchronize()
+    return k
 
 
 def host_launch_us(bound, n=20):
@@ -353,13 +388,15 @@ def measure(name, steps, warmup, flush, threads, check=True, reps=REPS):
     st = Setup(name)
     bound = st.cmd.bind(*st.args)
     small = st.bytes < (64 << 20)
+    settled = settle(bound)
     for _ in range(warmup):
         bound.launch()
     b2b = BACK_TO_BACK_SMALL if small else steps
     total_ms, wall_ms = time_back_to_back(bound, b2b)
     reps = max(reps, REPS_SMALL) if small else reps
     each = time_each(bound, reps)
-    cold = time_each(bound, reps, flush)
+    cold_pairs = []
+    cold = time_each(bound, reps, flush, cold_pairs)
     host_us = host_launch_us(bound)
     avg_us = total_ms * 1e3 / b2b
     cold_med = statistics.median(cold) * 1e3
@@ -368,11 +405,12 @@ def measure(name, steps, warmup, flush, threads, check=True, reps=REPS):
         "elements": st.elements, "algorithmic_bytes": st.bytes,
         "warm": dict(avg_us=round(avg_us, 3), gbps=round(st.bytes / (avg_us * 1e-6) / 1e9, 1),
                      launches=b2b, **_stats_us(each)),
-        "cold": dict(gbps=round(st.bytes / (cold_med * 1e-6) / 1e9, 1), launches=reps, **_stats_us(cold)),
+        "cold": dict(gbps=round(st.bytes / (cold_med * 1e-6) / 1e9, 1), launches=reps, **_stats_us(cold),
+                     with_dispatch_median_us=round(statistics.median(cold_pairs) * 1e3, 3)),
         "gelem_per_s": round(st.elements / (cold_med * 1e-6) / 1e9, 2),
         "pct_of_peak": round(100 * st.bytes / (cold_med * 1e-6) / 1e9 / PEAK_GBPS, 2),
         "host_launch_us": round(host_us, 2),
-        "launch_sequence": [warmup, b2b, reps, reps, 20],
+        "launch_sequence": [settled + warmup, b2b, reps, reps, 20],
     }
     if st.compiled_from:
         r["compiled_from"] = st.compiled_from
@@ -475,22 +513,24 @@ def counters_record(wl, kernel_hash):
 
 
 def headline(a, flush, threads, khash):
-    """The contract's K steps of the headline workload, cold: the timed
-    region is K steps, each a flush (outside the events) and one launch
-    between two HIP events; barrier-free (one process), synchronised on both
-    sides."""
+    """The K steps of the headline workload, cold: the timed region is K
+    steps, each a flush and one launch whose dispatch records a pair of HIP
+    events at its start and end (one process, so no barrier; synchronised on
+    both sides)."""
     import torch
     st = Setup(a.workload)
     bound = st.cmd.bind(*st.args)
+    settled = settle(bound)
     for _ in range(a.warmup):
         bound.launch()
     torch.cuda.synchronize()
-    per = time_each(bound, a.steps, flush)
+    pairs = []
+    per = time_each(bound, a.steps, flush, pairs)
     torch.cuda.synchronize()
     kernel_ms = sum(per)
     mean_us = kernel_ms * 1e3 / a.steps
     gbps = st.bytes * a.steps / (kernel_ms * 1e-3) / 1e9
-    return st, per, mean_us, gbps
+    return st, per, pairs, mean_us, gbps, settled
 
 
 # ---------------------------------------------------------------------------
@@ -535,12 +575,16 @@ def _order(r):
     return (int(r.get("Dispatch_Id") or 0), int(r.get("Start_Timestamp") or 0))
 
 
-def summarize_trace(directory, bench_json, command):
+def summarize_trace(directory, bench_json, command, plain_json=None):
     """profiles/kernel_trace_<workload>.txt and kernel_trace_summary.md from a
     rocprofv3 --kernel-trace --stats run of this script and the JSON line that
     run printed: per workload, the kernel's own durations per phase beside the
-    HIP-event figures of the line."""
+    HIP-event figures of the line.  plain_json: the line of the same command
+    run without the profiler on the same box just before (under the profiler
+    the dispatch-recorded events read about 4 us longer per launch), compared
+    the same way."""
     line = _bench_line(bench_json)
+    plain = _bench_line(plain_json) if plain_json else None
     khash = line["kernel_source_hash"]
     disp = sorted((r for r in _csv_rows(directory, "kernel_trace.csv") if "ecmd::" in r["Kernel_Name"]), key=_order)
     stats = {r["Name"]: r for r in _csv_rows(directory, "kernel_stats.csv")}
@@ -548,39 +592,54 @@ def summarize_trace(directory, bench_json, command):
     table = ["# Kernel durations: rocprofv3 kernel trace against bench.py's HIP events", "",
              "Command:", "", "    " + command, "",
              "kernel source hash: %s" % khash, "",
-             "| workload | kernel | trace cold median us | bench cold median us | diff | trace back-to-back "
-             "mean us | bench back-to-back us | diff |", "|---|---|---|---|---|---|---|---|"]
+             "Per workload: the kernel trace's median over the cold per-launch phase (for the headline: its "
+             "cold steps) and mean over the back-to-back phase, against the same figures of the bench line "
+             "printed by the profiled run and by the same command run without the profiler on the same box "
+             "just before (\"plain\").", "",
+             "| workload | kernel | trace cold us | profiled bench cold us | diff | plain bench cold us | diff | "
+             "trace back-to-back us | profiled bench us | diff | plain bench us | diff |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
 
     def dur_us(rs):
         return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
 
-    for name, phases in split.items():
-        names = sorted({r["Kernel_Name"] for ph in phases for r in ph})
-        text = ["kernel trace: %s" % name, "", "command:", "    " + command, "", "kernels: " + "; ".join(names), ""]
+    def pct(a, b):
+        return "%.2f %%" % (100 * (b - a) / a) if a and b else "-"
+
+    def figures(ln, name):
+        """(cold median us, back-to-back us) of a workload in a bench line."""
+        if ln is None:
+            return None, None
         if name.startswith("headline:"):
-            steps = dur_us(phases[1])
-            tr, be = statistics.mean(steps), line["roofline"]["kernel_avg_us"]
-            text += ["headline: %d cold steps" % len(steps),
-                     "    trace mean kernel duration: %.3f us" % tr,
-                     "    bench.py HIP-event mean over the same steps: %.3f us" % be,
-                     "    difference: %.2f %%" % (100 * (tr - be) / be),
-                     "    value %s GB/s = %.1f %% of 8 TB/s" % (line["value"], 100 * line["roofline"]["frac"])]
-            table.append("| %s (headline, %d cold steps) | `%s` | %.3f | %.3f | %.2f %% | - | - | - |" % (
-                name, len(steps), names[0][:60], statistics.median(steps), be, 100 * (statistics.median(steps) - be) / be))
-        else:
-            c = line.get("commands", {}).get(name)
-            if not c or "cold" not in c:
-                continue
-            b2b, each, cold = dur_us(phases[1]), dur_us(phases[2]), dur_us(phases[3])
-            rows = [("back-to-back mean", statistics.mean(b2b), c["warm"]["avg_us"]),
-                    ("warm per-launch median", statistics.median(each), c["warm"]["median_us"]),
-                    ("cold per-launch median", statistics.median(cold), c["cold"]["median_us"])]
-            for what, tr, be in rows:
-                text.append("%-24s trace %10.3f us   bench %10.3f us   difference %6.2f %%" % (
-                    what, tr, be, 100 * (tr - be) / be))
-            table.append("| %s | `%s` | %.3f | %.3f | %.2f %% | %.3f | %.3f | %.2f %% |" % (
-                name, names[0][:60], rows[2][1], rows[2][2], 100 * (rows[2][1] - rows[2][2]) / rows[2][2],
-                rows[0][1], rows[0][2], 100 * (rows[0][1] - rows[0][2]) / rows[0][2]))
+            return ln["step_us"]["median_us"], None
+        c = ln.get("commands", {}).get(name)
+        if not c or "cold" not in c:
+            return None, None
+        return c["cold"]["median_us"], c["warm"]["avg_us"]
+
+    fmt = lambda v: "%.3f" % v if v else "-"
+    for name, phases in split.items():
+        if name.endswith("@graph"):
+            continue
+        names = sorted({r["Kernel_Name"] for ph in phases for r in ph})
+        headline_row = name.startswith("headline:")
+        cold = dur_us(phases[1] if headline_row else phases[3])
+        b2b = None if headline_row else statistics.mean(dur_us(phases[1]))
+        tr_cold = statistics.median(cold)
+        pc, pb = figures(line, name)
+        qc, qb = figures(plain, name)
+        text = ["kernel trace: %s" % name, "", "command:", "    " + command, "", "kernels: " + "; ".join(names), "",
+                "trace, cold %s median: %.3f us over %d launches" % ("step" if headline_row else "per-launch",
+                                                                      tr_cold, len(cold)),
+                "bench line of the profiled run: %s us (%s)" % (fmt(pc), pct(tr_cold, pc)),
+                "bench line of the plain run:    %s us (%s)" % (fmt(qc), pct(tr_cold, qc))]
+        if b2b:
+            text += ["trace, back-to-back mean: %.3f us" % b2b,
+                     "bench line of the profiled run: %s us (%s)" % (fmt(pb), pct(b2b, pb)),
+                     "bench line of the plain run:    %s us (%s)" % (fmt(qb), pct(b2b, qb))]
+        table.append("| %s | `%s` | %.3f | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            name, names[0][:60], tr_cold, fmt(pc), pct(tr_cold, pc), fmt(qc), pct(tr_cold, qc),
+            fmt(b2b), fmt(pb), pct(b2b, pb), fmt(qb), pct(b2b, qb)))
         for n in names:
             if n in stats:
                 text += ["", "rocprofv3 kernel stats row (all dispatches of this kernel name in the run):"]
@@ -665,6 +724,41 @@ def summarize_counters(fetch_dir, fetch_json, write_dir, write_json, command):
     print("\n".join(lines))
 
 
+def summarize_lds(directory, bench_json, command):
+    """profiles/lds_bank_conflicts.md from a rocprofv3 --pmc SQ_LDS_BANK_CONFLICT
+    SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS run of this script and the JSON line it
+    printed: per workload, the counters per dispatch of its kernel."""
+    line = _bench_line(bench_json)
+    per = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if "ecmd::" not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "order": _order(r)})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    disp = sorted(per.values(), key=lambda d: d["order"])
+    split = _split(disp, line["launch_sequence"])
+    lines = ["# LDS bank conflicts (rocprofv3 SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_INSTS_LDS)", "",
+             "Command:", "", "    " + command, "",
+             "kernel source hash: %s" % line["kernel_source_hash"], "",
+             "Per dispatch, averaged over the workload's dispatches.  SQ_LDS_IDX_ACTIVE counts the cycles LDS "
+             "instructions keep the LDS busy, SQ_LDS_BANK_CONFLICT the cycles of those lost to bank conflicts.", "",
+             "| workload | kernel | dispatches | SQ_INSTS_LDS | SQ_LDS_IDX_ACTIVE | SQ_LDS_BANK_CONFLICT | "
+             "conflict share |", "|---|---|---|---|---|---|---|"]
+    for name, phases in split.items():
+        ds = [d for ph in phases for d in ph]
+        if not ds or name.startswith("headline:"):
+            continue
+        mean = {c: statistics.mean(d.get(c, 0.0) for d in ds)
+                for c in ("SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT")}
+        share = mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"] if mean["SQ_LDS_IDX_ACTIVE"] else 0.0
+        lines.append("| %s | `%s` | %d | %.0f | %.0f | %.0f | %.2f %% |" % (
+            name, sorted({d["name"] for d in ds})[0][:80], len(ds), mean["SQ_INSTS_LDS"], mean["SQ_LDS_IDX_ACTIVE"],
+            mean["SQ_LDS_BANK_CONFLICT"], 100 * share))
+    with open(os.path.join(PROFILES, "lds_bank_conflicts.md"), "w") as out:
+        out.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -680,15 +774,22 @@ def main():
     ap.add_argument("--reps", type=int, default=REPS, help="per-launch event pairs per workload, warm and cold")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "FETCH_JSON", "WRITE_DIR", "WRITE_JSON"),
                     help="write profiles/ counter summaries from two rocprofv3 --pmc runs of this script and exit")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "BENCH_JSON"),
-                    help="write profiles/kernel_trace_*.txt from a kernel-trace run of this script and exit")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="DIR BENCH_JSON [PLAIN_JSON]",
+                    help="write profiles/kernel_trace_*.txt from a kernel-trace run of this script (its directory "
+                         "and JSON line, optionally the line of the same command run without the profiler) and exit")
+    ap.add_argument("--summarize-lds", nargs=2, metavar=("DIR", "BENCH_JSON"),
+                    help="write profiles/lds_bank_conflicts.md from an LDS-counter run of this script and exit")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     a = ap.parse_args()
     if a.summarize_counters:
         summarize_counters(*a.summarize_counters, a.command)
         return
+    if a.summarize_lds:
+        summarize_lds(*a.summarize_lds, a.command)
+        return
     if a.summarize_trace:
-        summarize_trace(*a.summarize_trace, a.command)
+        summarize_trace(a.summarize_trace[0], a.summarize_trace[1], a.command,
+                        a.summarize_trace[2] if len(a.summarize_trace) > 2 else None)
         return
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path "
@@ -704,7 +805,7 @@ def main():
     base, variant = split_workload(a.workload)
     label = W.WORKLOADS[base]["label"] + (" (%s)" % variant if variant else "")
     log("headline %s: %s, %d cold steps" % (a.workload, label, a.steps))
-    st, per, mean_us, gbps = headline(a, flush, threads, khash)
+    st, per, pairs, mean_us, gbps, settled = headline(a, flush, threads, khash)
     log("headline %s: %.1f GB/s cold, kernel mean %.2f us" % (st.plan["kernel"], gbps, mean_us))
     cnt = counters_record(a.workload, khash)
     line = {
@@ -727,6 +828,9 @@ def main():
         "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         "gelem_per_s": round(st.elements * a.steps / (sum(per) * 1e-3) / 1e9, 3),
         "step_us": _stats_us(per),
+        "step_us_with_dispatch": dict(_stats_us(pairs), gbps=round(st.bytes * len(pairs) / (sum(pairs) * 1e-3) / 1e9, 2),
+                                      what="ordinary HIP events recorded on the stream around each step: "
+                                           "the command processor's dispatch latency included"),
         "roofline": {
             "bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(gbps / PEAK_GBPS, 4),
@@ -746,7 +850,8 @@ def main():
         log("oracle on %d threads: full-size parity of the headline" % threads)
         line["parity"], _, _ = parity(st, threads)
         log("headline parity: %s" % json.dumps(line["parity"]))
-    line["launch_sequence"] = [["headline:" + a.workload, [a.warmup, a.steps]]]
+    line["launch_sequence"] = [["headline:" + a.workload, [settled + a.warmup, a.steps]]]
+    line["settle_launches"] = settled
     if not a.no_commands:
         names = a.only.split(",") if a.only else CONFIGS + LINE_EXTRA + (ALL_EXTRA if a.all else [])
         line["commands"] = {}

@@ -80,6 +80,7 @@ def _load_library():
         "cmd_store": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, i32p]),
         "cmd_select": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p]),
         "cmd_launch": (ctypes.c_int, [vp, ctypes.POINTER(cmd_arg), ctypes.c_int32, vp]),
+        "cmd_launch_timed": (ctypes.c_int, [vp, ctypes.POINTER(cmd_arg), ctypes.c_int32, vp, vp, vp]),
         "cmd_plan": (ctypes.c_int, [vp, ctypes.POINTER(cmd_arg), ctypes.c_int32, ctypes.POINTER(cmd_plan_info)]),
         "cmd_dump": (ctypes.c_int64, [vp, ctypes.c_char_p, ctypes.c_int64]),
         "cmd_last_error": (ctypes.c_char_p, [vp]),
@@ -111,6 +112,7 @@ cmd_op = lib.cmd_op
 cmd_store = lib.cmd_store
 cmd_select = lib.cmd_select
 cmd_launch = lib.cmd_launch
+cmd_launch_timed = lib.cmd_launch_timed
 cmd_plan = lib.cmd_plan
 cmd_dump = lib.cmd_dump
 cmd_last_error = lib.cmd_last_error
@@ -351,6 +353,25 @@ class BoundLaunch:
         rc = lib.cmd_launch(self.cmd._h, self.arr, self.n, self.stream)
         if rc:
             self.cmd._check(rc)
+
+    def launch_timed(self, start, stop):
+        """Launch with the kernel execution timed by the dispatches
+        (cmd_launch_timed): start and stop are torch.cuda.Event(enable_timing=
+        True) objects already recorded once (torch creates events lazily);
+        afterwards start.elapsed_time(stop) is the kernel's own duration."""
+        rc = lib.cmd_launch_timed(self.cmd._h, self.arr, self.n, self.stream, _event_handle(start),
+                                  _event_handle(stop))
+        if rc:
+            self.cmd._check(rc)
+
+
+def _event_handle(ev):
+    if ev is None:
+        return None
+    h = getattr(ev, "cuda_event", 0)
+    if not h:
+        raise ValueError("record the event once before a timed launch (torch creates its events lazily)")
+    return ctypes.c_void_p(h)
 
 
 def from_spec(spec) -> Command:

@@ -26,6 +26,7 @@
 #include "../../include/ecmd.h"
 #include "ecmd_command.h"
 #include "ecmd_jit.h"
+#include "ecmd_launch.h"
 #include "ecmd_tape.h"
 
 using namespace ecmd;
@@ -1159,8 +1160,7 @@ int enqueue(cmd_t h, LaunchPlan &L, void *hip_stream)
         LinearArgs &A = L.LA;
         if (S.jit) {
             void *params[] = {&A};
-            herr = (int)hipModuleLaunchKernel(L.fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1, 0,
-                                              (hipStream_t)hip_stream, params, nullptr);
+            herr = launch_module(L.fn, (unsigned)g.grid, (unsigned)g.block, 0u, hip_stream, params);
         } else if (S.interp) {
             for (int64_t first = 0; first < S.n_wg && herr == 0; first += S.grid) {
                 A.first = first;
@@ -1180,13 +1180,11 @@ int enqueue(cmd_t h, LaunchPlan &L, void *hip_stream)
             for (int64_t first = 0; first < S.g_waves && herr == 0; first += 4 * S.grid) {
                 A.g_first = (uint32_t)first;
                 const int64_t wg = std::min<int64_t>(S.grid, (S.g_waves - first + 3) / 4);
-                herr = (int)hipModuleLaunchKernel(L.fn, (unsigned)wg, 1, 1, (unsigned)g.block, 1, 1, 0u,
-                                                  (hipStream_t)hip_stream, params, nullptr);
+                herr = launch_module(L.fn, (unsigned)wg, (unsigned)g.block, 0u, hip_stream, params);
             }
         } else {
-            herr = (int)hipModuleLaunchKernel(L.fn, (unsigned)g.grid, 1, 1, (unsigned)g.block, 1, 1,
-                                              S.path == CMD_PATH_TILED ? (unsigned)S.lds : 0u,
-                                              (hipStream_t)hip_stream, params, nullptr);
+            herr = launch_module(L.fn, (unsigned)g.grid, (unsigned)g.block,
+                                 S.path == CMD_PATH_TILED ? (unsigned)S.lds : 0u, hip_stream, params);
         }
         return herr;
     }
@@ -1205,6 +1203,29 @@ int enqueue(cmd_t h, LaunchPlan &L, void *hip_stream)
 }  // namespace
 
 void ecmd::set_create_error(const char *msg) { g_create_err = msg; }
+
+ecmd::LaunchEvents &ecmd::launch_events()
+{
+    thread_local LaunchEvents ev;
+    return ev;
+}
+
+int ecmd::launch_module(hipFunction_t fn, unsigned grid, unsigned block, unsigned lds_bytes, void *stream,
+                        void **params)
+{
+    LaunchEvents &ev = launch_events();
+    hipError_t e;
+    if (ev.start || ev.stop) {
+        // the extension takes the grid in work-items (below 2^31: the dispatch limits)
+        e = hipExtModuleLaunchKernel(fn, grid * block, 1, 1, block, 1, 1, lds_bytes, (hipStream_t)stream, params,
+                                     nullptr, ev.start, ev.stop, 0);
+        ev.start = nullptr;
+    } else {
+        e = hipModuleLaunchKernel(fn, grid, 1, 1, block, 1, 1, lds_bytes, (hipStream_t)stream, params, nullptr);
+    }
+    if (e != hipSuccess) (void)hipGetLastError();
+    return (int)e;
+}
 
 // ---------------------------------------------------------------------------
 // The C ABI.
@@ -1474,6 +1495,17 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
     if (herr != 0) return fail(h, CMD_E_LAUNCH, "%s launch failed: %s", L->S.name, hipGetErrorString((hipError_t)herr));
     h->err.clear();
     return CMD_OK;
+}
+
+int cmd_launch_timed(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream, void *start_event,
+                     void *stop_event)
+{
+    LaunchEvents &ev = launch_events();
+    ev.start = static_cast<hipEvent_t>(start_event);
+    ev.stop = static_cast<hipEvent_t>(stop_event);
+    const int rc = cmd_launch(h, args, nargs, hip_stream);
+    ev = LaunchEvents{};
+    return rc;
 }
 
 int64_t cmd_dump(cmd_t h, char *buf, int64_t cap)

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ecmd_eval.h"
+#include "ecmd_launch.h"
 
 namespace ecmd {
 
@@ -77,8 +78,7 @@ __global__ __launch_bounds__(kGatherBlock) void k_gather(const StridedArgs A)
 
 int launch_gather(const StridedArgs &A, LaunchGeometry g, void *stream)
 {
-    hipLaunchKernelGGL(k_gather, dim3((unsigned)g.grid), dim3(g.block), 0, (hipStream_t)stream, A);
-    return (int)hipGetLastError();
+    return launch_kernel(reinterpret_cast<const void *>(&k_gather), dim3((unsigned)g.grid), dim3(g.block), 0, stream, A);
 }
 
 }  // namespace ecmd

@@ -36,6 +36,7 @@
 
 #include "ecmd_kern_linear.h"
 #include "ecmd_kern_rows.h"
+#include "ecmd_launch.h"
 
 namespace ecmd {
 
@@ -603,8 +604,8 @@ static int launch_tiled_one(const StridedArgs &A, const InterpTape &T, LaunchGeo
         if (e != hipSuccess) return (int)e;
         lds_allowed = lds_bytes;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)g.grid), dim3(TB), (unsigned)lds_bytes, (hipStream_t)stream, A, T);
-    return (int)hipGetLastError();
+    return launch_kernel(reinterpret_cast<const void *>(kern), dim3((unsigned)g.grid), dim3(TB), (unsigned)lds_bytes,
+                         stream, A, T);
 }
 
 template <int TM, int TN, int TB>
@@ -759,10 +760,10 @@ static int launch_gather_k(int mode, const StridedArgs &A, const InterpTape &T, 
 {
     const dim3 grid((unsigned)g.grid), block(64);
     hipStream_t s = (hipStream_t)stream;
-    if (mode == 1) hipLaunchKernelGGL((k_gather_interp<K, 1>), grid, block, (unsigned)lds, s, A, T);
-    else if (mode == 2) hipLaunchKernelGGL((k_gather_interp<K, 2>), grid, block, (unsigned)lds, s, A, T);
-    else hipLaunchKernelGGL((k_gather_interp<K, 3>), grid, block, (unsigned)lds, s, A, T);
-    return (int)hipGetLastError();
+    const void *fn = mode == 1   ? reinterpret_cast<const void *>(&k_gather_interp<K, 1>)
+                     : mode == 2 ? reinterpret_cast<const void *>(&k_gather_interp<K, 2>)
+                                 : reinterpret_cast<const void *>(&k_gather_interp<K, 3>);
+    return launch_kernel(fn, grid, block, (unsigned)lds, s, A, T);
 }
 
 int launch_gather_interp(int mode, int k_sub, const StridedArgs &A, const InterpTape &T, LaunchGeometry g,
@@ -780,19 +781,13 @@ static int launch_one(bool rows, const void *args, const InterpTape &T, LaunchGe
 {
     if (rows) {
         const StridedArgs &A = *static_cast<const StridedArgs *>(args);
-        if (A.wave_in_row == 2)
-            hipLaunchKernelGGL((k_rows_interp<K, NTL, NTS, 2>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
-                               (hipStream_t)stream, A, T);
-        else if (A.wave_in_row)
-            hipLaunchKernelGGL((k_rows_interp<K, NTL, NTS, 1>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
-                               (hipStream_t)stream, A, T);
-        else
-            hipLaunchKernelGGL((k_rows_interp<K, NTL, NTS, 0>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
-                               (hipStream_t)stream, A, T);
-    } else
-        hipLaunchKernelGGL((k_linear_interp<K, NTL, NTS>), dim3((unsigned)g.grid), dim3(64), (unsigned)lds,
-                           (hipStream_t)stream, *static_cast<const LinearArgs *>(args), T);
-    return (int)hipGetLastError();
+        const void *fn = A.wave_in_row == 2 ? reinterpret_cast<const void *>(&k_rows_interp<K, NTL, NTS, 2>)
+                         : A.wave_in_row    ? reinterpret_cast<const void *>(&k_rows_interp<K, NTL, NTS, 1>)
+                                            : reinterpret_cast<const void *>(&k_rows_interp<K, NTL, NTS, 0>);
+        return launch_kernel(fn, dim3((unsigned)g.grid), dim3(64), (unsigned)lds, stream, A, T);
+    }
+    return launch_kernel(reinterpret_cast<const void *>(&k_linear_interp<K, NTL, NTS>), dim3((unsigned)g.grid), dim3(64),
+                         (unsigned)lds, stream, *static_cast<const LinearArgs *>(args), T);
 }
 
 template <int K>

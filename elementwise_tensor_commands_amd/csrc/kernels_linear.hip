@@ -3,15 +3,15 @@
 #include <hip/hip_runtime.h>
 
 #include "ecmd_kern_linear.h"
+#include "ecmd_launch.h"
 
 namespace ecmd {
 
 template <class EV, int E, int G, bool VEC, bool NTL, bool NTS>
 static int launch_one(const LinearArgs &A, LaunchGeometry g, void *stream)
 {
-    hipLaunchKernelGGL((k_linear<EV, E, G, VEC, NTL, NTS>), dim3((unsigned)g.grid), dim3(g.block), 0,
-                       (hipStream_t)stream, A);
-    return (int)hipGetLastError();
+    return launch_kernel(reinterpret_cast<const void *>(&k_linear<EV, E, G, VEC, NTL, NTS>), dim3((unsigned)g.grid),
+                         dim3(g.block), 0, stream, A);
 }
 
 template <class EV, int E, int G>

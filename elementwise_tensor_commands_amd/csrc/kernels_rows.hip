@@ -3,15 +3,15 @@
 #include <hip/hip_runtime.h>
 
 #include "ecmd_kern_rows.h"
+#include "ecmd_launch.h"
 
 namespace ecmd {
 
 template <class EV, bool NTL, bool NTS>
 static int launch_one(const StridedArgs &A, LaunchGeometry g, void *stream)
 {
-    hipLaunchKernelGGL((k_rows<EV, NTL, NTS>), dim3((unsigned)g.grid), dim3(kRowsBlock), 0, (hipStream_t)stream,
-                       A);
-    return (int)hipGetLastError();
+    return launch_kernel(reinterpret_cast<const void *>(&k_rows<EV, NTL, NTS>), dim3((unsigned)g.grid), dim3(kRowsBlock),
+                         0, stream, A);
 }
 
 template <class EV>

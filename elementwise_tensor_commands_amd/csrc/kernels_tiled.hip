@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ecmd_kern_tiled.h"
+#include "ecmd_launch.h"
 
 namespace ecmd {
 
@@ -23,8 +24,8 @@ static int launch_one(const StridedArgs &A, LaunchGeometry g, void *stream, int 
         if (e != hipSuccess) return (int)e;
         lds_allowed = lds_bytes;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)g.grid), dim3(TB), (unsigned)lds_bytes, (hipStream_t)stream, A);
-    return (int)hipGetLastError();
+    return launch_kernel(reinterpret_cast<const void *>(kern), dim3((unsigned)g.grid), dim3(TB), (unsigned)lds_bytes,
+                         stream, A);
 }
 
 template <class EV, int MASK, int TM, int TN, int TB>

@@ -217,6 +217,18 @@ int cmd_store(cmd_t h, cmd_tag value, int32_t rank, int32_t *arg_index);
  * repeat. */
 int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream);
 
+/* cmd_launch, with the kernel execution timed by the dispatches themselves:
+ * start_event and stop_event (hipEvent_t, created by the caller with timing
+ * enabled; either may be NULL) are recorded by the launch's first dispatch
+ * when it begins and by its last dispatch when it ends (HIP's
+ * hipExtLaunchKernel / hipExtModuleLaunchKernel), so hipEventElapsedTime
+ * gives the kernel execution time -- the interval a kernel-trace profiler
+ * reports -- without the command processor's time between separate event
+ * packets and the dispatch.  Statuses as cmd_launch; a failed check or a
+ * shape with no elements records neither event. */
+int cmd_launch_timed(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream, void *start_event,
+                     void *stop_event);
+
 /* Description of what cmd_launch would do with these arguments. */
 typedef struct {
     int32_t path;          /* CMD_PATH_* below                                           */

@@ -297,6 +297,18 @@ static void gpu_checks(int64_t n)
     HIP_OK(hipDeviceSynchronize());
     const double b2b_us = (now_us() - t0) / reps;
     printf("launch_us %.3f %.3f\n", host_us, b2b_us);
+    /* a timed launch: the dispatch records the two events around the kernel */
+    hipEvent_t e0, e1;
+    HIP_OK(hipEventCreate(&e0));
+    HIP_OK(hipEventCreate(&e1));
+    EXPECT_STATUS(cmd_launch_timed(h, args, 6, NULL, e0, e1), CMD_OK, h);
+    HIP_OK(hipEventSynchronize(e1));
+    float kernel_ms = 0.f;
+    HIP_OK(hipEventElapsedTime(&kernel_ms, e0, e1));
+    CHECK(kernel_ms > 0.f && kernel_ms < 1000.f);
+    printf("kernel_us %.3f\n", kernel_ms * 1e3);
+    HIP_OK(hipEventDestroy(e0));
+    HIP_OK(hipEventDestroy(e1));
     HIP_OK(hipFree(dx));
     HIP_OK(hipFree(dy));
     HIP_OK(hipFree(dz));
