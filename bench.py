@@ -11,9 +11,10 @@ timed cold: before every step a 1 GiB read evicts the Command's data from the
 256 MB last-level cache, so each step reads its operands from HBM.  Each
 step's kernel time comes from HIP events that the launch's dispatch records at
 its start and end (cmd_launch_timed: what a kernel-trace profiler measures);
-`value` is algorithmic bytes x K / the K steps' summed kernel time.  The same
-steps timed by ordinary events around the launch (dispatch latency included,
-about 5 us more per launch) are reported beside it.
+`value` is algorithmic bytes x K / the K steps' summed kernel time.  After the
+timed region the same cold steps are timed again by ordinary events recorded on
+the stream around each launch (the command processor's dispatch latency
+included, a few microseconds per launch) and reported beside it.
 
 The same JSON line carries, under "commands", the five configurations (and a
 plain copy, the reference for "% of copy", plus three programs with no
@@ -203,28 +204,29 @@ def _events(stream, n=2):
     return evs
 
 
-def time_each(bound, reps, flush=None, pairs=None):
+def time_each(bound, reps, flush=None, dispatch=False):
     """Per-launch kernel durations: the launch's dispatches record a pair of
     HIP events at their start and end (cmd_launch_timed), as a kernel-trace
     profiler times a kernel.  With flush, the cache is flushed before each
-    launch.  Returns ms per launch; if pairs is a list, each launch's
-    duration between ordinary events recorded on the stream around it
-    (dispatch latency included) is appended to it."""
+    launch.  With dispatch, ordinary events recorded on the stream around an
+    ordinary launch instead (the command processor's dispatch latency
+    included).  Returns ms per launch."""
     import torch
     stream = torch.cuda.current_stream()
-    ks, ke, s, e = _events(stream, 4)
+    s, e = _events(stream, 2)
     per = []
     torch.cuda.synchronize()
     for _ in range(reps):
         if flush is not None:
             flush()
-        s.record(stream)
-        bound.launch_timed(ks, ke)
-        e.record(stream)
+        if dispatch:
+            s.record(stream)
+            bound.launch()
+            e.record(stream)
+        else:
+            bound.launch_timed(s, e)
         e.synchronize()
-        per.append(ks.elapsed_time(ke))
-        if pairs is not None:
-            pairs.append(s.elapsed_time(e))
+        per.append(s.elapsed_time(e))
     return per
 
 
@@ -395,8 +397,7 @@ def measure(name, steps, warmup, flush, threads, check=True, reps=REPS):
     total_ms, wall_ms = time_back_to_back(bound, b2b)
     reps = max(reps, REPS_SMALL) if small else reps
     each = time_each(bound, reps)
-    cold_pairs = []
-    cold = time_each(bound, reps, flush, cold_pairs)
+    cold = time_each(bound, reps, flush)
     host_us = host_launch_us(bound)
     avg_us = total_ms * 1e3 / b2b
     cold_med = statistics.median(cold) * 1e3
@@ -405,8 +406,7 @@ def measure(name, steps, warmup, flush, threads, check=True, reps=REPS):
         "elements": st.elements, "algorithmic_bytes": st.bytes,
         "warm": dict(avg_us=round(avg_us, 3), gbps=round(st.bytes / (avg_us * 1e-6) / 1e9, 1),
                      launches=b2b, **_stats_us(each)),
-        "cold": dict(gbps=round(st.bytes / (cold_med * 1e-6) / 1e9, 1), launches=reps, **_stats_us(cold),
-                     with_dispatch_median_us=round(statistics.median(cold_pairs) * 1e3, 3)),
+        "cold": dict(gbps=round(st.bytes / (cold_med * 1e-6) / 1e9, 1), launches=reps, **_stats_us(cold)),
         "gelem_per_s": round(st.elements / (cold_med * 1e-6) / 1e9, 2),
         "pct_of_peak": round(100 * st.bytes / (cold_med * 1e-6) / 1e9 / PEAK_GBPS, 2),
         "host_launch_us": round(host_us, 2),
@@ -524,12 +524,13 @@ def headline(a, flush, threads, khash):
     for _ in range(a.warmup):
         bound.launch()
     torch.cuda.synchronize()
-    pairs = []
-    per = time_each(bound, a.steps, flush, pairs)
+    per = time_each(bound, a.steps, flush)
     torch.cuda.synchronize()
     kernel_ms = sum(per)
     mean_us = kernel_ms * 1e3 / a.steps
     gbps = st.bytes * a.steps / (kernel_ms * 1e-3) / 1e9
+    # after the timed region: the same cold steps between ordinary events
+    pairs = time_each(bound, a.steps, flush, dispatch=True)
     return st, per, pairs, mean_us, gbps, settled
 
 
@@ -829,7 +830,8 @@ def main():
         "gelem_per_s": round(st.elements * a.steps / (sum(per) * 1e-3) / 1e9, 3),
         "step_us": _stats_us(per),
         "step_us_with_dispatch": dict(_stats_us(pairs), gbps=round(st.bytes * len(pairs) / (sum(pairs) * 1e-3) / 1e9, 2),
-                                      what="ordinary HIP events recorded on the stream around each step: "
+                                      what="the same K cold steps again after the timed region, between "
+                                           "ordinary HIP events recorded on the stream around each launch: "
                                            "the command processor's dispatch latency included"),
         "roofline": {
             "bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS, "unit": "GB/s",
@@ -850,7 +852,7 @@ def main():
         log("oracle on %d threads: full-size parity of the headline" % threads)
         line["parity"], _, _ = parity(st, threads)
         log("headline parity: %s" % json.dumps(line["parity"]))
-    line["launch_sequence"] = [["headline:" + a.workload, [settled + a.warmup, a.steps]]]
+    line["launch_sequence"] = [["headline:" + a.workload, [settled + a.warmup, a.steps, a.steps]]]
     line["settle_launches"] = settled
     if not a.no_commands:
         names = a.only.split(",") if a.only else CONFIGS + LINE_EXTRA + (ALL_EXTRA if a.all else [])
