@@ -24,10 +24,12 @@
 // each code object (or its compile error) under g_mu.  The caller meanwhile
 // runs the interpreter.  The compiler runs outside g_mu, so launches and
 // polls never wait for a compile.  At library unload the worker finishes the
-// compile in progress, drops the rest of the queue and is joined.
+// compile in progress, drops the rest of the queue and is joined.  A child
+// process made by fork() starts a worker of its own when it needs one.
 #include "ecmd_jit.h"
 
 #include <hip/hiprtc.h>
+#include <pthread.h>
 #include <sys/stat.h>
 #include <unistd.h>
 
@@ -37,6 +39,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <deque>
+#include <iterator>
 #include <map>
 #include <mutex>
 #include <string>
@@ -248,7 +251,7 @@ struct Worker {
     std::condition_variable cv;
     std::deque<std::pair<std::string, JitRequest>> queue;
     bool stop = false;
-    std::thread thread;
+    std::thread *thread = nullptr;   // started by the first submit
 
     void run()
     {
@@ -275,13 +278,7 @@ struct Worker {
             }
         }
     }
-    void submit(const std::string &key, const JitRequest &r)
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        if (!thread.joinable()) thread = std::thread([this] { run(); });
-        queue.emplace_back(key, r);
-        cv.notify_one();
-    }
+    void submit(const std::string &key, const JitRequest &r);
     ~Worker()
     {
         {
@@ -289,10 +286,48 @@ struct Worker {
             stop = true;
         }
         cv.notify_all();
-        if (thread.joinable()) thread.join();
+        if (thread) {
+            thread->join();
+            delete thread;
+        }
     }
 };
 Worker g_worker;
+
+// fork(): the child has only the thread that forked, so the worker and any
+// compile in progress do not exist there.  The handlers hold both locks
+// across the fork (no other thread can own them in the child), and the child
+// forgets the parent's worker thread (never joined there), its queue and the
+// requests in flight, so that its own first compile starts a new worker.
+void fork_prepare()
+{
+    g_mu.lock();
+    g_worker.mu.lock();
+}
+void fork_parent()
+{
+    g_worker.mu.unlock();
+    g_mu.unlock();
+}
+void fork_child()
+{
+    g_worker.thread = nullptr;   // the copied object names no thread in this process
+    g_worker.queue.clear();
+    for (auto it = g_pending.begin(); it != g_pending.end();)
+        it = it->second.state == JIT_QUEUED ? g_pending.erase(it) : std::next(it);
+    g_worker.mu.unlock();
+    g_mu.unlock();
+}
+
+void Worker::submit(const std::string &key, const JitRequest &r)
+{
+    static std::once_flag registered;
+    std::call_once(registered, [] { pthread_atfork(fork_prepare, fork_parent, fork_child); });
+    std::lock_guard<std::mutex> lock(mu);
+    if (!thread) thread = new std::thread([this] { run(); });
+    queue.emplace_back(key, r);
+    cv.notify_one();
+}
 
 // The entry for the request, from memory, disk or the compiler.  g_mu is held
 // only to look up and publish, never across a compile.
