@@ -409,6 +409,10 @@ def measure(name, steps, warmup, flush, threads, check=True, reps=REPS):
         "cold": dict(gbps=round(st.bytes / (cold_med * 1e-6) / 1e9, 1), launches=reps, **_stats_us(cold)),
         "gelem_per_s": round(st.elements / (cold_med * 1e-6) / 1e9, 2),
         "pct_of_peak": round(100 * st.bytes / (cold_med * 1e-6) / 1e9 / PEAK_GBPS, 2),
+        # the slower of the cold rate and the back-to-back one: a kernel whose
+        # stores stay in the caches leaves their write-back to the cache flush
+        # of a cold launch, and pays it in back-to-back launches instead
+        "sustained_gbps": round(min(st.bytes / (cold_med * 1e-6), st.bytes / (avg_us * 1e-6)) / 1e9, 1),
         "host_launch_us": round(host_us, 2),
         "launch_sequence": [settled + warmup, b2b, reps, reps, 20],
     }

@@ -1065,6 +1065,17 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
         A.g_waves = (uint32_t)S.g_waves;
         A.g_rows = (uint32_t)(C.n[0] * C.n[1] * C.n[2]);
         A.g_rows_per_wave = (uint32_t)S.g_rows_per_wave;
+        // 32-bit outputs whose elements of one super-chunk are one contiguous
+        // run: a unit-stride row (segments), or whole rows of an output that
+        // is contiguous across its rows (whole-row modes)
+        for (int k = 0; k < h->prog.n_out; ++k) {
+            const int64_t *st = C.out_s[k];
+            bool run = esize(B.out[k].dtype) == 4 && st[3] == 1;
+            if (S.g_mode != 1)
+                run = run && (C.n[2] == 1 || st[2] == C.n[3]) && (C.n[1] == 1 || st[1] == C.n[2] * C.n[3]) &&
+                      (C.n[0] == 1 || st[0] == C.n[1] * C.n[2] * C.n[3]);
+            if (run) A.g_out_run |= 1u << k;
+        }
         A.div_g = make_fast_div((uint32_t)S.g_div);
         A.div_n2 = make_fast_div((uint32_t)C.n[2]);
         A.div_n1 = make_fast_div((uint32_t)C.n[1]);

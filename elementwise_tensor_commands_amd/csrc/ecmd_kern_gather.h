@@ -15,6 +15,18 @@
 // element of a row (always in bounds) and store nothing.  Four wavefronts
 // per work-group; the host splits the work into dispatches (A.g_first: the
 // first wavefront of the dispatch).
+//
+// An output whose elements of the wavefront form one contiguous run (a
+// segment of a unit-stride row, or whole rows of a contiguous output;
+// A.g_out_run) is not stored element by element: its 64 E results go to a
+// wavefront-private LDS buffer, and are read back four consecutive elements
+// per lane, in runs that start on a 128-byte line, so that the run's
+// interior is written by 16-byte nontemporal stores that cover whole lines
+// (a run off line alignment written one element per lane touches three lines
+// per instruction, and ordinary stores leave the write-back to later work).
+// Only the partial lines at the run's two ends are written element by
+// element.  A wavefront's LDS instructions execute in order, so the buffer
+// needs no barrier, only a compiler fence.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -95,8 +107,53 @@ __global__ __launch_bounds__(kGatherCcBlock) void k_gather_cc(const StridedArgs 
     }
     uint32_t out[kMaxOut][E];
     EV::template run<E>(A.prog, A.uni, R, out);
+    __shared__ uint32_t stage[kWaves][64 * E];
+    uint32_t *buf = stage[threadIdx.x >> 6];
 #pragma unroll
     for (int k = 0; k < kMaxOut; ++k) {
+        if (k < EV::n_out(A.prog) && !is16(EV::out_ty(A.prog, k)) && ((A.g_out_run >> k) & 1u)) {
+            // this wavefront's run: its first element and length
+            int64_t start;
+            uint32_t count;
+            if constexpr (MODE == 1) {
+                const uint32_t seg_c0 = (w - fast_div(A.div_g, w) * A.div_g.d) * (64u * E);
+                start = (int64_t)sb0 * A.out_s[k][0] + (int64_t)sb1 * A.out_s[k][1] + (int64_t)sr * A.out_s[k][2] +
+                        seg_c0;
+                count = min(64u * E, (uint32_t)A.n[3] - seg_c0);
+            } else {
+                const uint32_t q0 = w * A.g_rows_per_wave;
+                start = (int64_t)q0 * A.n[3];
+                count = min(A.g_rows_per_wave, A.g_rows - q0) * A.div_g.d;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (ok[e]) buf[64 * e + lane] = out[k][e];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint32_t *p = static_cast<uint32_t *>(A.out[k]);
+            // elements of the run's first 128-byte line that lie before it
+            const int m = (int)((reinterpret_cast<uintptr_t>(p + start) >> 2) & 31u);
+            const int total = (int)count + m;
+            for (int c = 0; c * 256 < total; ++c) {
+                const int j0 = c * 256 + 4 * (int)lane - m;       // run index of this lane's first element
+                uint32_t v[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = (j0 + t >= 0 && j0 + t < (int)count) ? buf[j0 + t] : 0u;
+                if (j0 >= 0 && j0 + 3 < (int)count) {
+                    store_group<4, true, true>(p, TY_F32, start + j0, 4, v);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (j0 + t >= 0 && j0 + t < (int)count) p[start + j0 + t] = v[t];
+                }
+            }
+            // the buffer is reused by the next staged output
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            continue;
+        }
         if (k < EV::n_out(A.prog)) {
             if (is16(EV::out_ty(A.prog, k))) {
                 uint16_t *p = static_cast<uint16_t *>(A.out[k]);

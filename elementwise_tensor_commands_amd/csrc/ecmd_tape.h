@@ -191,6 +191,9 @@ struct StridedArgs {
     uint32_t g_first;           // gather path: super-chunk of this dispatch's first work-group
     uint32_t g_rows;            // gather path: rows n[0] n[1] n[2]
     uint32_t g_rows_per_wave;   // gather path, whole-row modes: rows per super-chunk
+    uint32_t g_out_run;         // gather path, compiled kernel: bit k = output k is 32-bit and the elements
+                                // of each super-chunk are one contiguous run of it (stored through LDS
+                                // as whole 128-byte lines)
     FastDiv div_g;              // gather path: by segments per row (segment mode) or by n[3] (whole rows)
     Program prog;
 };

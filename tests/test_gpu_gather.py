@@ -210,3 +210,48 @@ def test_gather_compiled_other_widths(monkeypatch, e, shape):
     cmd.launch(*vals, *outs)
     torch.cuda.synchronize()
     _check(shape, store, outs, ref, "compiled gather E=%d %s" % (e, shape))
+
+
+CONTIG_SPEC = [("x", ("load", "f32", 3)), ("i", ("load", "i32", 3)), ("s", ("scalar", "f32")),
+               ("p", ("mul", "x", "s")), ("ii", ("sub", "i", "i")), ("j", ("add", "ii", "i")),
+               ("h", ("cvt", "p", "f16")),
+               ("o0", ("store", "p", 3)), ("o1", ("store", "j", 3)), ("o2", ("store", "h", 3))]
+
+
+@pytest.mark.parametrize("shape", [(1, 37, 2100), (1, 5, 1025), (1, 300, 6), (1, 77, 1), (1, 19, 200),
+                                   (3, 41, 7), (2, 9, 130)])
+@pytest.mark.parametrize("off", [0, 1, 5, 31])
+def test_gather_compiled_contiguous_outputs(shape, off):
+    """Outputs whose super-chunks are contiguous runs (every mode: unit-stride
+    rows for segments, outputs contiguous across rows for whole rows) go
+    through the compiled kernel's LDS buffer as 128-byte-line stores: two
+    32-bit outputs share the buffer, a binary16 output is stored element by
+    element; each output starts `off` elements into a guard-banded buffer, so
+    runs start at every position in a line.  The guards must stay untouched."""
+    import elementwise_tensor_commands_amd as ecmd
+    B, R, C = shape
+    rng = np.random.default_rng(40 + off + sum(shape))
+    xs = (rng.standard_normal((B, R, C + 1)) * 10).astype(np.float32)     # rows 4 bytes off: the gather path
+    ins = rng.integers(-(1 << 30), 1 << 30, (B, R, C), dtype=np.int32)
+    hx = np.ascontiguousarray(xs[:, :, :C])
+    ref = run_oracle(CONTIG_SPEC, [hx, ins, np.float32(0.75)])
+    n, guard = B * R * C, 64
+    bufs = [torch.full((n + off + 2 * guard,), v, dtype=d, device=dev())
+            for v, d in ((float("nan"), torch.float32), (-7, torch.int32), (float("nan"), torch.float16))]
+    outs = [b[guard + off:guard + off + n].view(B, R, C) for b in bufs]
+    vals = [to_dev(xs)[:, :, :C], to_dev(ins), 0.75]
+    cmd = ecmd.from_spec(CONTIG_SPEC).jit()
+    plan = cmd.plan(*vals, *outs)
+    assert plan["path"] == "gather" and plan["kernel"] == "jit_gather", plan
+    cmd.prepare(*vals, *outs)
+    cmd.launch(*vals, *outs)
+    torch.cuda.synchronize()
+    for k, (o, r) in enumerate(zip(outs, ref)):
+        compare(host(o), r, 0, "contiguous outputs %s off %d out%d" % (shape, off, k))
+    for k, b in enumerate(bufs):
+        hb = host(b)
+        for part in (hb[:guard + off], hb[guard + off + n:]):
+            if k == 1:
+                assert (part == -7).all(), "out%d guard written (%s, off %d)" % (k, shape, off)
+            else:
+                assert np.isnan(part.astype(np.float32)).all(), "out%d guard written (%s, off %d)" % (k, shape, off)
