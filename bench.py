@@ -78,7 +78,7 @@ def kernel_source_hash():
 
 def split_workload(name):
     """("bias_relu_f32", "interp") for "bias_relu_f32@interp"; "int_fused_wide"
-    is configuration 1's Command on full-range int32 inputs."""
+    is the int32 fused Command (int_fused) on full-range int32 inputs."""
     base, _, variant = name.partition("@")
     return base, variant
 
@@ -107,8 +107,8 @@ def make_host_inputs(name):
     import workloads as W
     base, _ = split_workload(name)
     if base == "int_fused_wide":
-        # configuration 1's Command on full-range int32 inputs (wraparound in
-        # nearly every element); seed of configuration 1, plus 100
+        # the int32 fused Command on full-range int32 inputs (wraparound in
+        # nearly every element); int_fused's seed plus 100
         rng = np.random.default_rng(W.seed_of("int_fused") + 100)
         vals = [rng.integers(-2**31, 2**31, 1 << 24, dtype=np.int64).astype(np.int32) for _ in range(3)]
         vals.append(W.SCALARS["int_fused"]["s"])

@@ -31,7 +31,7 @@ F32_SPECIAL = [
 # int32 bit patterns: zero, +-1, the range's ends and their neighbours, the
 # 16-bit boundaries, 2^24 and its neighbours (exactness of int32 -> binary32),
 # binary16's largest finite and overflow threshold as integers, alternating
-# bits, and configuration 1's scalar.
+# bits, and the int32 fused Command's scalar 12345.
 I32_SPECIAL = [
     0x00000000, 0x00000001, 0xFFFFFFFF, 0x00000002, 0xFFFFFFFE, 0x00000003,
     0x7FFFFFFF, 0x80000000, 0x80000001, 0x7FFFFFFE,

@@ -7,9 +7,10 @@ reaches the ahead-of-time kernels' vector bodies, the interpreters' tape walks
 only their per-element tails; each element is compared with its case's
 hand-worked result.  Then every pair of binary32 / int32 edge values plus 2^20
 random pairs runs through each operation on the linear path's three kernel
-kinds, against the oracle; configuration 1's Command on full-range int32
+kinds, against the oracle; the int32 fused Command on full-range int32
 inputs (wraparound in nearly every element) at full size on its ahead-of-time
-kernel; and configuration 3 at full size with its per-element ulp report.
+kernel; and the mixed-precision two-output Command at full size with its
+per-element ulp report.
 """
 import os
 from collections import defaultdict
