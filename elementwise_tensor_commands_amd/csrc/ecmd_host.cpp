@@ -20,6 +20,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <numeric>
 #include <string>
 #include <vector>
 
@@ -83,6 +84,7 @@ struct Selection {
     int e = 0;
     int g_mode = 0;             // gather path: 0 per-element kernel, else the interpreter's mode (1 segments, 2 and 3 whole rows)
     int64_t g_div = 0, g_waves = 0, g_rows_per_wave = 0;
+    int g_align = 0;            // gather path, compiled kernel, segments: 1 + the output they are laid from (0: none)
     const char *name = "";
 };
 
@@ -575,6 +577,18 @@ constexpr int kInterpLdsKiB = 24;
 
 bool aligned(const void *p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes == 0; }
 
+// Gather path: are an operand's elements of one super-chunk (strides st) one
+// contiguous run?  Segments (mode 1): a unit-stride row; whole rows (modes 2
+// and 3): an operand contiguous across its rows.
+bool gather_run(const Canon &C, int g_mode, const int64_t *st)
+{
+    bool run = st[3] == 1;
+    if (g_mode != 1)
+        run = run && (C.n[2] == 1 || st[2] == C.n[3]) && (C.n[1] == 1 || st[1] == C.n[2] * C.n[3]) &&
+              (C.n[0] == 1 || st[0] == C.n[1] * C.n[2] * C.n[3]);
+    return run;
+}
+
 // Entries of the interpreters' LDS register file.  Values are the inputs
 // (0 .. n_in - 1, which keep entries 0 .. n_in - 1: the kernels load them
 // there) and the operations' results (n_in + i).  Each result takes the
@@ -906,20 +920,45 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
     const int64_t rows = C.n[0] * C.n[1] * C.n[2], n3 = C.n[3];
     const int64_t lim = kMaxGridItems;
     S.g_mode = 0;
-    // On request (CMD_OPT_JIT) a kernel compiled for the Program
-    // (ecmd_kern_gather.h): 64 kGatherCcE elements per wavefront, registers
-    // instead of the LDS file.
+    // With compilation at run time allowed (CMD_OPT_JIT), a kernel compiled
+    // for the Program (ecmd_kern_gather.h): 64 kGatherCcE elements per
+    // wavefront, registers instead of the LDS file.
     const bool g_jit = allow_jit;
     int gce = (int)env_int("ECMD_GATHER_JIT_E", kGatherCcE);   // A/B runs: 4, 8 or 16
     if (gce != 4 && gce != 16) gce = kGatherCcE;
+    // The compiled kernel lays its super-chunks on the 128-byte lines of a
+    // 32-bit output, so that no line inside a row (segments) or inside the
+    // output (whole rows) is written in parts by two wavefronts: partial line
+    // writes cost about 7% of the rate on MI355X (a misaligned 8192 x 8191
+    // add: 5.6 TB/s, the same add over whole-line rows: 6.0 TB/s).
+    //   segments: laid from the first 32-bit output with unit stride
+    //     (segment s of a row starts at its line-aligned column s * span - r,
+    //     r < 32 the row start's place in its line), so a row takes one more
+    //     segment when r pushes its end past the last;
+    //   whole rows: rows per super-chunk a multiple of those that fill whole
+    //     lines of a 32-bit output contiguous across its rows.
+    int line_out = -1;
+    bool rows_out = false;
+    for (int k = 0; k < P.n_out; ++k) {
+        if (esize(B.out[k].dtype) != 4) continue;
+        const int64_t *st = C.out_s[k];
+        if (st[3] == 1 && line_out < 0) line_out = k;
+        rows_out = rows_out || gather_run(C, 2, st);
+    }
     if (rows < lim && n3 < lim && env_int("ECMD_GATHER_MODE", 1) != 0) {
         size_interp(P, S);
         const int64_t span = g_jit ? 64 * gce : 256 * S.k_sub;   // elements per super-chunk
         if (n3 > span / 2) {
-            const int64_t segs = (n3 + span - 1) / span;
-            if (rows * segs < lim) S.g_mode = 1, S.g_div = segs, S.g_waves = rows * segs;
+            const bool lay = g_jit && line_out >= 0;
+            const int64_t segs = (n3 + (lay ? 31 : 0) + span - 1) / span;
+            if (rows * segs < lim)
+                S.g_mode = 1, S.g_div = segs, S.g_waves = rows * segs, S.g_align = lay ? line_out + 1 : 0;
         } else {
-            const int64_t m = span / n3;
+            int64_t m = span / n3;
+            if (g_jit && rows_out) {
+                const int64_t unit = 32 / std::gcd<int64_t>(n3, 32);
+                if (m >= unit) m -= m % unit;
+            }
             S.g_mode = C.n[0] * C.n[1] == 1 ? 2 : 3;
             S.g_div = n3, S.g_rows_per_wave = m, S.g_waves = (rows + m - 1) / m;
         }
@@ -929,6 +968,12 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
         S.interp = false;
         S.lds = 0;
         S.e = gce;
+        // the linear kernel's load policy: nontemporal from the last-level
+        // cache's size up (ECMD_NT_LOAD overrides)
+        int64_t bytes = 0;
+        for (int k = 0; k < P.n_in; ++k) bytes += numel * esize(B.in[k].dtype);
+        for (int k = 0; k < P.n_out; ++k) bytes += numel * esize(B.out[k].dtype);
+        S.shape = linear_shape(bytes);
         S.block = 256;   // four wavefronts, one super-chunk each
         S.grid = std::max<int64_t>(1, std::min<int64_t>((S.g_waves + 3) / 4, std::max<int64_t>(
                                                              1, env_int("ECMD_GATHER_DISPATCH", kGatherDispatch))));
@@ -977,7 +1022,8 @@ JitRequest jit_request(const Selection &S, const Program &P)
 {
     if (S.path == CMD_PATH_LINEAR) return JitRequest{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, P};
     if (S.path == CMD_PATH_ROWS) return JitRequest{JIT_ROWS, 4, 4, S.shape.nt_load, S.shape.nt_store, P};
-    if (S.path == CMD_PATH_GATHER) return JitRequest{JIT_GATHER, S.e, 0, false, false, P, 0, 0, 0, 0, S.g_mode};
+    if (S.path == CMD_PATH_GATHER)
+        return JitRequest{JIT_GATHER, S.e, 0, S.shape.nt_load, false, P, 0, 0, 0, 0, S.g_mode};
     const bool nt = tiled_nt();
     return JitRequest{JIT_TILED, 4, 4, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
 }
@@ -1065,17 +1111,13 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
         A.g_waves = (uint32_t)S.g_waves;
         A.g_rows = (uint32_t)(C.n[0] * C.n[1] * C.n[2]);
         A.g_rows_per_wave = (uint32_t)S.g_rows_per_wave;
-        // 32-bit outputs whose elements of one super-chunk are one contiguous
-        // run: a unit-stride row (segments), or whole rows of an output that
-        // is contiguous across its rows (whole-row modes)
-        for (int k = 0; k < h->prog.n_out; ++k) {
-            const int64_t *st = C.out_s[k];
-            bool run = esize(B.out[k].dtype) == 4 && st[3] == 1;
-            if (S.g_mode != 1)
-                run = run && (C.n[2] == 1 || st[2] == C.n[3]) && (C.n[1] == 1 || st[1] == C.n[2] * C.n[3]) &&
-                      (C.n[0] == 1 || st[0] == C.n[1] * C.n[2] * C.n[3]);
-            if (run) A.g_out_run |= 1u << k;
-        }
+        // 32-bit operands whose elements of one super-chunk are one
+        // contiguous run
+        for (int k = 0; k < h->prog.n_out; ++k)
+            if (esize(B.out[k].dtype) == 4 && gather_run(C, S.g_mode, C.out_s[k])) A.g_out_run |= 1u << k;
+        for (int k = 0; k < h->prog.n_in; ++k)
+            if (esize(B.in[k].dtype) == 4 && gather_run(C, S.g_mode, C.in_s[k])) A.g_in_run |= 1u << k;
+        A.g_align = (uint32_t)S.g_align;
         A.div_g = make_fast_div((uint32_t)S.g_div);
         A.div_n2 = make_fast_div((uint32_t)C.n[2]);
         A.div_n1 = make_fast_div((uint32_t)C.n[1]);

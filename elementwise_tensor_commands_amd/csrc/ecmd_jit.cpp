@@ -390,7 +390,8 @@ std::string jit_name(const JitRequest &r)
         std::snprintf(b, sizeof b, "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, %d, %s, %d, %d, %d, true>", r.mask,
                       r.ntl ? "true" : "false", r.tm, r.tn, r.tb);
     else if (r.kind == JIT_GATHER)
-        std::snprintf(b, sizeof b, "ecmd::k_gather_cc<ecmd::CtEval<ecmd::kJitProg>, %d, %d>", r.e, r.mode);
+        std::snprintf(b, sizeof b, "ecmd::k_gather_cc<ecmd::CtEval<ecmd::kJitProg>, %d, %d, %s>", r.e, r.mode,
+                      r.ntl ? "true" : "false");
     else
         std::snprintf(b, sizeof b, "ecmd::k_rows<ecmd::CtEval<ecmd::kJitProg>, %s, %s>", r.ntl ? "true" : "false",
                       r.nts ? "true" : "false");

@@ -194,6 +194,10 @@ struct StridedArgs {
     uint32_t g_out_run;         // gather path, compiled kernel: bit k = output k is 32-bit and the elements
                                 // of each super-chunk are one contiguous run of it (stored through LDS
                                 // as whole 128-byte lines)
+    uint32_t g_in_run;          // the same for input k (loaded as 16-byte vectors through LDS)
+    uint32_t g_align;           // gather path, compiled kernel, segments: 1 + the output whose 128-byte lines
+                                // the segments are laid from (segment s of a row starts at column
+                                // s * 64 E - r, r the row start's place in its line); 0: from column 0
     FastDiv div_g;              // gather path: by segments per row (segment mode) or by n[3] (whole rows)
     Program prog;
 };

@@ -218,8 +218,8 @@ CONTIG_SPEC = [("x", ("load", "f32", 3)), ("i", ("load", "i32", 3)), ("s", ("sca
                ("o0", ("store", "p", 3)), ("o1", ("store", "j", 3)), ("o2", ("store", "h", 3))]
 
 
-@pytest.mark.parametrize("shape", [(1, 37, 2100), (1, 5, 1025), (1, 300, 6), (1, 77, 1), (1, 19, 200),
-                                   (3, 41, 7), (2, 9, 130)])
+@pytest.mark.parametrize("shape", [(1, 37, 2100), (1, 5, 1025), (1, 37, 1000), (1, 300, 6), (1, 77, 1),
+                                   (1, 19, 200), (3, 41, 7), (2, 9, 130)])
 @pytest.mark.parametrize("off", [0, 1, 5, 31])
 def test_gather_compiled_contiguous_outputs(shape, off):
     """Outputs whose super-chunks are contiguous runs (every mode: unit-stride
@@ -227,7 +227,9 @@ def test_gather_compiled_contiguous_outputs(shape, off):
     through the compiled kernel's LDS buffer as 128-byte-line stores: two
     32-bit outputs share the buffer, a binary16 output is stored element by
     element; each output starts `off` elements into a guard-banded buffer, so
-    runs start at every position in a line.  The guards must stay untouched."""
+    runs start at every position in a line.  Segments are laid from out0's
+    lines, so a row's first segment starts before the row and 1000-column
+    rows end with an empty segment.  The guards must stay untouched."""
     import elementwise_tensor_commands_amd as ecmd
     B, R, C = shape
     rng = np.random.default_rng(40 + off + sum(shape))
@@ -255,3 +257,52 @@ def test_gather_compiled_contiguous_outputs(shape, off):
                 assert (part == -7).all(), "out%d guard written (%s, off %d)" % (k, shape, off)
             else:
                 assert np.isnan(part.astype(np.float32)).all(), "out%d guard written (%s, off %d)" % (k, shape, off)
+
+
+RUNS_SPEC = [("x", ("load", "f32", 3)), ("y", ("load", "i32", 3)), ("h", ("load", "f16", 3)),
+             ("b", ("load", "f32", 3)), ("s", ("scalar", "f32")),
+             ("xs", ("mul", "x", "s")), ("t", ("add", "xs", "b")), ("hf", ("cvt", "h", "f32")),
+             ("u", ("sub", "t", "hf")), ("yy", ("add", "y", "y")),
+             ("o0", ("store", "u", 3)), ("o1", ("store", "yy", 3))]
+
+
+@pytest.mark.parametrize("shape", [(1, 37, 2100), (1, 5, 1025), (1, 3, 4097), (1, 37, 1000), (1, 300, 6),
+                                   (1, 77, 1), (1, 19, 200), (3, 41, 7), (2, 9, 130)])
+@pytest.mark.parametrize("off", [0, 1, 5, 31])
+@pytest.mark.parametrize("pad", [0, 3])
+def test_gather_compiled_contiguous_inputs(shape, off, pad):
+    """32-bit inputs whose super-chunks are contiguous runs are read as
+    line-aligned 16-byte vectors through the compiled kernel's LDS buffer:
+    each run input starts `off` elements into its storage (runs start at every
+    place in a 128-byte line), x's rows are padded by `pad` elements (a run per
+    segment, but not across whole rows), beside a binary16 input (rows padded,
+    a spare row per batch, 2 bytes off alignment: no vector path takes the
+    views, and batches do not merge into one plane) and a per-row
+    constant (stride 0 along the row) that are read element by element."""
+    import elementwise_tensor_commands_amd as ecmd
+    B, R, C = shape
+    rng = np.random.default_rng(90 + off + 7 * pad + sum(shape))
+    cp = C + pad
+    xs = np.full(off + B * R * cp, np.nan, dtype=np.float32)
+    xs[off:] = (rng.standard_normal(B * R * cp) * 10).astype(np.float32)
+    ys = np.zeros(off + B * R * C, dtype=np.int32)
+    ys[off:] = rng.integers(-(1 << 31), 1 << 31, B * R * C, dtype=np.int64).astype(np.int32)
+    hs = (rng.standard_normal(1 + B * (R + 1) * (C + 3)) * 4).astype(np.float16)
+    bb = (rng.standard_normal((B, R, 1)) * 3).astype(np.float32)
+    hx = xs[off:].reshape(B, R, cp)[:, :, :C]
+    hy = ys[off:].reshape(B, R, C)
+    hh = hs[1:].reshape(B, R + 1, C + 3)[:, :R, :C]
+    ref = run_oracle(RUNS_SPEC, [hx, hy, hh, np.broadcast_to(bb, (B, R, C)), np.float32(-1.25)])
+    dx, dy = to_dev(xs), to_dev(ys)
+    vals = [dx[off:].view(B, R, cp)[:, :, :C], dy[off:].view(B, R, C), to_dev(hs)[1:].view(B, R + 1, C + 3)[:, :R, :C],
+            to_dev(bb).expand(B, R, C), -1.25]
+    outs = [torch.empty((B, R, C), dtype=torch.float32, device=dev()),
+            torch.empty((B, R, C), dtype=torch.int32, device=dev())]
+    cmd = ecmd.from_spec(RUNS_SPEC).jit()
+    plan = cmd.plan(*vals, *outs)
+    assert plan["path"] == "gather" and plan["kernel"] == "jit_gather", plan
+    cmd.prepare(*vals, *outs)
+    cmd.launch(*vals, *outs)
+    torch.cuda.synchronize()
+    for k, (o, r) in enumerate(zip(outs, ref)):
+        compare(host(o), r, 0, "contiguous inputs %s off %d pad %d out%d" % (shape, off, pad, k))
