@@ -558,6 +558,63 @@ __device__ __forceinline__ void load_group(const void *p, uint8_t ty, int64_t i,
     }
 }
 
+// load_group split in two, for code that picks between access forms at run
+// time: load_raw issues the vector access of G elements at element index i
+// and keeps the words as loaded (32-bit: G elements; 16-bit: G / 2 words of
+// two elements), unpack_raw makes elements of them.  A use of a load's result
+// inside the branch that issued it makes the wavefront wait for that load
+// before it issues the next operand's; with the unpacking after every
+// operand's loads, all of them are in flight together.
+template <int G, bool NTL>
+__device__ __forceinline__ void load_raw(const void *p, uint8_t ty, int64_t i, uint32_t (&raw)[G])
+{
+    static_assert(G == 4 || G == 8, "group of 4 or 8");
+    if (is16(ty)) {
+        const uint16_t *q = static_cast<const uint16_t *>(p) + i;
+        if constexpr (G == 8) {
+            const u32x4 d = ld<NTL>(reinterpret_cast<const u32x4 *>(q));
+            raw[0] = d.x, raw[1] = d.y, raw[2] = d.z, raw[3] = d.w;
+        } else {
+            const u32x2 d = ld<NTL>(reinterpret_cast<const u32x2 *>(q));
+            raw[0] = d.x, raw[1] = d.y;
+        }
+    } else {
+        const uint32_t *q = static_cast<const uint32_t *>(p) + i;
+#pragma unroll
+        for (int w = 0; w < G / 4; ++w) {
+            const u32x4 d = ld<NTL>(reinterpret_cast<const u32x4 *>(q) + w);
+            raw[4 * w + 0] = d.x, raw[4 * w + 1] = d.y, raw[4 * w + 2] = d.z, raw[4 * w + 3] = d.w;
+        }
+    }
+}
+
+// The first count (< G) elements at element index i, one by one, laid out as
+// load_raw lays out a whole vector (the rest zero).  Packing 16-bit elements
+// waits for their loads, but only where some work-item takes this branch.
+template <int G>
+__device__ __forceinline__ void load_raw_elems(const void *p, uint8_t ty, int64_t i, int count, uint32_t (&raw)[G])
+{
+    if (is16(ty)) {
+        const uint16_t *q = static_cast<const uint16_t *>(p) + i;
+        uint32_t h[G];
+#pragma unroll
+        for (int e = 0; e < G; ++e) h[e] = e < count ? (uint32_t)q[e] : 0u;
+#pragma unroll
+        for (int w = 0; w < G / 2; ++w) raw[w] = h[2 * w] | (h[2 * w + 1] << 16);
+    } else {
+        const uint32_t *q = static_cast<const uint32_t *>(p) + i;
+#pragma unroll
+        for (int e = 0; e < G; ++e) raw[e] = e < count ? q[e] : 0u;
+    }
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t unpack_raw(uint8_t ty, const uint32_t (&raw)[G], int e)
+{
+    if (is16(ty)) return (e & 1) ? raw[e >> 1] >> 16 : raw[e >> 1] & 0xffffu;
+    return raw[e];
+}
+
 template <int G, bool VEC, bool NT>
 __device__ __forceinline__ void store_group(void *p, uint8_t ty, int64_t i, int count, const uint32_t (&v)[G])
 {

@@ -85,6 +85,7 @@ struct Selection {
     int g_mode = 0;             // gather path: 0 per-element kernel, else the interpreter's mode (1 segments, 2 and 3 whole rows)
     int64_t g_div = 0, g_waves = 0, g_rows_per_wave = 0;
     int g_align = 0;            // gather path, compiled kernel, segments: 1 + the output they are laid from (0: none)
+    int rows_v = 4;             // rows path, compiled kernels: elements per vector (8: every operand 16-bit)
     const char *name = "";
 };
 
@@ -734,28 +735,45 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
     // Rows: outputs unit-stride along dimension 3, inputs unit-stride or
     // constant along it, vectors aligned in every row.
     {
-        auto row_aligned = [&](const View &v, const int64_t (&st)[4]) {
-            bool ok = aligned(v.ptr, 4 * esize(v.dtype));
+        // every row of every direct operand starts on a whole vector of
+        // `unit` elements
+        auto row_aligned = [&](const View &v, const int64_t (&st)[4], int unit) {
+            bool ok = aligned(v.ptr, unit * esize(v.dtype));
             for (int d = 0; d < 3 && ok; ++d)
-                if (C.n[d] > 1) ok = st[d] % 4 == 0;
+                if (C.n[d] > 1) ok = st[d] % unit == 0;
             return ok;
         };
-        bool rows = true;
+        bool rows = true, rows8 = true;
         uint8_t rowconst[kMaxIn] = {};
-        for (int k = 0; k < P.n_out && rows; ++k) rows = C.out_s[k][3] == 1 && row_aligned(B.out[k], C.out_s[k]);
-        for (int k = 0; k < P.n_in && rows; ++k) {
-            if (C.in_s[k][3] == 0) rowconst[k] = 1;
-            else rows = C.in_s[k][3] == 1 && row_aligned(B.in[k], C.in_s[k]);
+        for (int k = 0; k < P.n_out && rows; ++k) {
+            rows = C.out_s[k][3] == 1 && row_aligned(B.out[k], C.out_s[k], 4);
+            rows8 = rows8 && esize(B.out[k].dtype) == 2 && row_aligned(B.out[k], C.out_s[k], 8);
         }
-        const int64_t per_row = (C.n[3] + 3) / 4;
-        const int64_t n_vec = C.n[0] * C.n[1] * C.n[2] * per_row;
-        if (rows && n_vec < kMaxGridItems && per_row < kMaxGridItems) {
+        for (int k = 0; k < P.n_in && rows; ++k) {
+            rows8 = rows8 && esize(B.in[k].dtype) == 2;
+            if (C.in_s[k][3] == 0) {
+                rowconst[k] = 1;
+            } else {
+                rows = C.in_s[k][3] == 1 && row_aligned(B.in[k], C.in_s[k], 4);
+                rows8 = rows8 && row_aligned(B.in[k], C.in_s[k], 8);
+            }
+        }
+        const int64_t per_row4 = (C.n[3] + 3) / 4;
+        if (rows && C.n[0] * C.n[1] * C.n[2] * per_row4 < kMaxGridItems && per_row4 < kMaxGridItems) {
             S.path = CMD_PATH_ROWS;
             std::memcpy(S.rowconst, rowconst, sizeof rowconst);
             S.variant = no_aot ? -1 : program_match_linear(P);
             S.jit = S.variant < 0 && allow_jit;
             S.vec = true;
-            S.e = 4;
+            // Vectors of 4 elements (16 bytes of a 32-bit operand); of 8 when
+            // every operand is 16-bit and every row starts on 16 bytes, so
+            // that 16-bit accesses are 16 bytes wide too, as on the linear
+            // path (ECMD_ROWS_V=4 keeps 4; the interpreter always takes 4).
+            const bool interp = S.variant < 0 && !S.jit;
+            S.rows_v = !interp && rows8 && env_int("ECMD_ROWS_V", 8) != 4 ? 8 : 4;
+            const int64_t per_row = (C.n[3] + S.rows_v - 1) / S.rows_v;
+            const int64_t n_vec = C.n[0] * C.n[1] * C.n[2] * per_row;
+            S.e = S.rows_v;
             S.block = kRowsBlock;
             S.grid = (n_vec + kRowsBlock - 1) / kRowsBlock;
             S.n_vec = n_vec;
@@ -776,7 +794,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
             S.shape = linear_shape(bytes);
             S.shape.nt_store = S.shape.nt_store && lines;
             S.name = S.jit ? "jit_rows" : rows_name(S.variant);
-            if (S.variant < 0 && !S.jit) {          // the LDS-file interpreter, 64 K vectors per work-group
+            if (interp) {                           // the LDS-file interpreter, 64 K vectors per work-group
                 size_interp(P, S);
                 S.grid = (n_vec + 64 * S.k_sub - 1) / (64 * S.k_sub);   // one per super-chunk, below 2^25
             }
@@ -1021,7 +1039,7 @@ bool tiled_nt()
 JitRequest jit_request(const Selection &S, const Program &P)
 {
     if (S.path == CMD_PATH_LINEAR) return JitRequest{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, P};
-    if (S.path == CMD_PATH_ROWS) return JitRequest{JIT_ROWS, 4, 4, S.shape.nt_load, S.shape.nt_store, P};
+    if (S.path == CMD_PATH_ROWS) return JitRequest{JIT_ROWS, S.rows_v, S.rows_v, S.shape.nt_load, S.shape.nt_store, P};
     if (S.path == CMD_PATH_GATHER)
         return JitRequest{JIT_GATHER, S.e, 0, S.shape.nt_load, false, P, 0, 0, 0, 0, S.g_mode};
     const bool nt = tiled_nt();
@@ -1097,10 +1115,10 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
     std::memcpy(A.n, C.n, sizeof A.n);
     if (S.path == CMD_PATH_ROWS) {
         A.n_vec = S.n_vec;
-        A.div_vec = make_fast_div((uint32_t)((C.n[3] + 3) / 4));
+        const int64_t per_row = (C.n[3] + S.rows_v - 1) / S.rows_v;
+        A.div_vec = make_fast_div((uint32_t)per_row);
         // 2: the interpreter's super-chunks (64 K vectors) never span two
         // rows; 1: no wavefront spans two rows
-        const int64_t per_row = (C.n[3] + 3) / 4;
         A.wave_in_row = S.interp && per_row % (64 * S.k_sub) == 0 ? 2u : per_row % 64 == 0 ? 1u : 0u;
         for (int k = 0; k < h->prog.n_in; ++k)
             if (S.rowconst[k] && esize(B.in[k].dtype) == 2) A.rowconst16 = 1u;
@@ -1248,7 +1266,7 @@ int enqueue(cmd_t h, LaunchPlan &L, void *hip_stream)
            : S.path == CMD_PATH_ROWS
                ? (S.interp ? launch_rows_interp(S.k_sub, S.shape.nt_load, S.shape.nt_store, A, L.T, g, S.lds,
                                                 hip_stream)
-                           : launch_rows(S.variant, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream))
+                           : launch_rows(S.variant, S.rows_v, S.shape.nt_load, S.shape.nt_store, A, g, hip_stream))
            : S.interp ? launch_gather_split(S, A, L.T, hip_stream)
                       : launch_gather(A, g, hip_stream);
 }

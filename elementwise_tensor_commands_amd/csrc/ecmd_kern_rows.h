@@ -13,7 +13,8 @@
 // dimensions 0..2 are all just row offsets here.
 //
 // Work decomposition: the rows are numbered q = (b0 * n1 + b1) * n2 + r and
-// each is cut into ceil(n3 / 4) vectors of 4 elements; work-item v of the
+// each is cut into ceil(n3 / V) vectors of V elements (V = 4, or 8 when every
+// operand is 16-bit: a 16-byte access either way); work-item v of the
 // one-dimensional grid takes vector v.  Consecutive work-items of a wavefront
 // therefore take consecutive 16-byte pieces of one row (of two rows at a row
 // boundary), so every access instruction of a direct operand is one
@@ -23,7 +24,7 @@
 // that is done once per wavefront.  A row-constant input is one
 // 4-byte load per work-item, the same address for all work-items of a row,
 // which the memory pipeline serves once per wavefront.  The last vector of a
-// row is partial when n3 is not a multiple of 4; its work-items access their
+// row is partial when n3 is not a multiple of V; its work-items access their
 // elements one by one.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -37,19 +38,21 @@ namespace ecmd {
 // the row and the operands' row offsets are then computed once per wavefront
 // from its first lane (the lowest lane is active whenever any is), in scalar
 // registers.
-template <class EV, bool NTL, bool NTS, bool WROW>
+template <class EV, bool NTL, bool NTS, bool WROW, int V>
 __device__ __forceinline__ void rows_body(const StridedArgs &A, uint32_t v)
 {
     const uint32_t q = fast_div(A.div_vec, WROW ? __builtin_amdgcn_readfirstlane(v) : v);
-    const uint32_t c = 4 * (v - q * A.div_vec.d);
+    const uint32_t c = V * (v - q * A.div_vec.d);
     const uint32_t t = fast_div(A.div_n2, q);
     const uint32_t r = q - t * A.div_n2.d;
     const uint32_t b0 = fast_div(A.div_n1, t);
     const uint32_t b1 = t - b0 * A.div_n1.d;
     const int64_t left = A.n[3] - (int64_t)c;
-    const int count = left >= 4 ? 4 : (int)left;
+    const int count = left >= V ? V : (int)left;
 
-    Regs<4> R;
+    // Every load is issued before any loaded value is used (load_raw): a
+    // full or partial vector's words, a row constant.
+    uint32_t raw[kMaxIn][V];
 #pragma unroll
     for (int k = 0; k < kMaxIn; ++k) {
         if (k < EV::n_in(A.prog)) {
@@ -58,37 +61,50 @@ __device__ __forceinline__ void rows_body(const StridedArgs &A, uint32_t v)
             if (A.in_rowconst[k]) {
                 uint32_t one[1];
                 load_elems<1, false>(A.in[k], ty, row, 1, one);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) R.in[k][e] = one[0];
-            } else if (count == 4) {
-                load_group<4, true, NTL>(A.in[k], ty, row + c, 4, R.in[k]);
+                raw[k][0] = one[0];
+            } else if (count == V) {
+                load_raw<V, NTL>(A.in[k], ty, row + c, raw[k]);
             } else {
-                load_elems<4, false>(A.in[k], ty, row + c, count, R.in[k]);
+                load_raw_elems<V>(A.in[k], ty, row + c, count, raw[k]);
             }
         }
     }
-    uint32_t out[kMaxOut][4];
-    EV::template run<4>(A.prog, A.uni, R, out);
+    Regs<V> R;
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) {
+        if (k < EV::n_in(A.prog)) {
+            const uint8_t ty = EV::in_ty(A.prog, k);
+            if (A.in_rowconst[k]) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) R.in[k][e] = raw[k][0];
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) R.in[k][e] = unpack_raw<V>(ty, raw[k], e);
+            }
+        }
+    }
+    uint32_t out[kMaxOut][V];
+    EV::template run<V>(A.prog, A.uni, R, out);
 #pragma unroll
     for (int k = 0; k < kMaxOut; ++k) {
         if (k < EV::n_out(A.prog)) {
             const uint8_t ty = EV::out_ty(A.prog, k);
             const int64_t off =
                 (int64_t)b0 * A.out_s[k][0] + (int64_t)b1 * A.out_s[k][1] + (int64_t)r * A.out_s[k][2] + c;
-            if (count == 4) store_group<4, true, NTS>(A.out[k], ty, off, 4, out[k]);
-            else store_elems<4, false, false>(A.out[k], ty, off, count, out[k]);
+            if (count == V) store_group<V, true, NTS>(A.out[k], ty, off, V, out[k]);
+            else store_elems<V, false, false>(A.out[k], ty, off, count, out[k]);
         }
     }
 }
 
-template <class EV, bool NTL, bool NTS>
+template <class EV, bool NTL, bool NTS, int V = 4>
 __global__ __launch_bounds__(kRowsBlock) void k_rows(const StridedArgs A)
 {
     // The host keeps n_vec below 2^31, so vector and row indexes are 32-bit.
     const uint32_t v = blockIdx.x * (uint32_t)kRowsBlock + threadIdx.x;
     if (v >= (uint32_t)A.n_vec) return;
-    if (A.wave_in_row) rows_body<EV, NTL, NTS, true>(A, v);
-    else rows_body<EV, NTL, NTS, false>(A, v);
+    if (A.wave_in_row) rows_body<EV, NTL, NTS, true, V>(A, v);
+    else rows_body<EV, NTL, NTS, false, V>(A, v);
 }
 
 }  // namespace ecmd

@@ -415,7 +415,8 @@ int launch_gather_interp(int mode, int k_sub, const StridedArgs &A, const Interp
                          int lds_bytes, void *stream);
 // Rows path: the linear path's specialised Programs (variant indexes the same
 // list); nontemporal loads / stores as the host chooses.
-int launch_rows(int variant, bool nt_load, bool nt_store, const StridedArgs &A, LaunchGeometry g, void *stream);
+// v: elements per vector, 4 or 8 (8 only for Programs whose operands are all 16-bit)
+int launch_rows(int variant, int v, bool nt_load, bool nt_store, const StridedArgs &A, LaunchGeometry g, void *stream);
 
 constexpr int kLinearBlock = 256;
 constexpr int kInterpBlock = 64;

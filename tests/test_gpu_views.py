@@ -33,9 +33,10 @@ def _device(view, storage):
     return flat, flat.as_strided(view.shape, strides, off)
 
 
-def run_views(spec, inputs, outputs, generic=False, what=""):
+def run_views(spec, inputs, outputs, generic=False, what="", jit=False):
     """inputs: (view, storage) pairs for loads, plain values for scalars, in
-    declaration order; outputs: (view, storage) pairs in store order.
+    declaration order; outputs: (view, storage) pairs in store order; jit: a
+    kernel compiled at run time where no ahead-of-time one fits.
     Returns the plan the GPU launch used."""
     import elementwise_tensor_commands_amd as ecmd
     host_out = [st.copy() for _, st in outputs]
@@ -49,6 +50,8 @@ def run_views(spec, inputs, outputs, generic=False, what=""):
         gflat.append(f)
         gout.append(g)
     cmd = ecmd.from_spec(spec)
+    if jit:
+        cmd.jit(ecmd.JIT_SYNC)
     old = os.environ.get("ECMD_FORCE_GENERIC")
     if generic:
         os.environ["ECMD_FORCE_GENERIC"] = "1"
@@ -86,7 +89,8 @@ def _workload_case(wl, shape):
     ("batched_transpose", (3, 200, 300)), ("batched_transpose", (2, 64, 64)), ("batched_transpose", (5, 33, 517)),
     ("batched_transpose", (1, 1, 1)), ("batched_transpose", (4, 1, 260)), ("batched_transpose", (7, 260, 4)),
     ("bias_nchw", (3, 37, 5, 67)), ("bias_nchw", (2, 8, 1, 1)), ("bias_nchw", (1, 1, 1, 1)),
-    ("bias_nchw", (2, 3, 16, 16)), ("bias_nchw", (2, 70, 9, 12))])
+    ("bias_nchw", (2, 3, 16, 16)), ("bias_nchw", (2, 70, 9, 12)),
+    ("bias_nchw_f16", (2, 8, 4, 16)), ("bias_nchw_f16", (3, 37, 5, 24)), ("bias_nchw_f16", (2, 70, 9, 12))])
 def test_workload_shapes(wl, shape, generic):
     spec, ins, outs = _workload_case(wl, shape)
     plan = run_views(spec, ins, outs, generic, "%s %s" % (wl, shape))
@@ -111,10 +115,11 @@ def test_batched_transpose_tiles(tile):
     assert plan["specialised"] and plan["path"] == "tiled"
 
 
-@pytest.mark.parametrize("wl", ["batched_transpose", "bias_nchw", "odd_rows_f32", "narrow_rows_f32"])
+@pytest.mark.parametrize("wl", ["batched_transpose", "bias_nchw", "bias_nchw_f16", "odd_rows_f32", "narrow_rows_f32"])
 def test_full_size_views(wl):
-    """The full shapes the benchmark times, in its launch configuration,
-    compared with the oracle on every element."""
+    """The full shapes the benchmark times, in its launch configuration
+    (binary16 NCHW: compiled at run time), compared with the oracle on every
+    element."""
     shape = W.WORKLOADS[wl]["shape"]
     print("  full size %s %s" % (wl, shape), flush=True)
     spec = W.WORKLOADS[wl]["spec"]
@@ -123,14 +128,19 @@ def test_full_size_views(wl):
     gin = W.to_torch(vals, extra, dev())
     import elementwise_tensor_commands_amd as ecmd
     cmd = ecmd.from_spec(spec)
-    out = torch.empty(shape, dtype=torch.float32, device=dev())
+    if wl == "bias_nchw_f16":
+        cmd.jit(ecmd.JIT_SYNC)
+    out = torch.empty(shape, dtype=torch.float16 if wl.endswith("f16") else torch.float32, device=dev())
     plan = cmd.plan(*gin, out)
     cmd.launch(*gin, out)
     torch.cuda.synchronize()
     compare(host(out), ref[0], 0, "%s full (%s)" % (wl, plan["kernel"]))
     assert (plan["path"], plan["kernel"]) == {
         "batched_transpose": ("tiled", "tiled_add_scaled_f32"), "bias_nchw": ("rows", "rows_affine_f32"),
+        "bias_nchw_f16": ("rows", "jit_rows"),
         "odd_rows_f32": ("gather", "gather_segments"), "narrow_rows_f32": ("gather", "gather_whole_rows")}[wl]
+    if wl == "bias_nchw_f16":
+        assert plan["elems_per_thread"] == 8, plan
 
 
 def test_staged_direct_and_row_constant_together():
@@ -204,3 +214,44 @@ def test_rows_path_shapes(shape):
         assert plan["path"] == "linear", plan
     elif last > 1:                     # rows of one element are a strided vector: gathered
         assert plan["path"] == "rows", plan
+
+
+AXPBY16 = {dt: [("x", ("load", dt, 3)), ("y", ("load", dt, 3)), ("a", ("scalar", dt)), ("b", ("scalar", dt)),
+                ("ax", ("mul", "a", "x")), ("by", ("mul", "b", "y")), ("s", ("add", "ax", "by")),
+                ("o", ("store", "s", 3))] for dt in ("f16", "bf16")}
+
+
+@pytest.mark.parametrize("which", ["f16", "bf16", "jit"])
+@pytest.mark.parametrize("n3,stride", [(8, 8), (64, 72), (67, 72), (1000, 1008), (1003, 1016), (4101, 4104),
+                                       (64, 68), (1001, 1004)])
+def test_rows_16bit_vectors(which, n3, stride):
+    """Programs whose operands are all 16-bit take 16-byte vectors of 8
+    elements on the rows path when every row starts on 16 bytes (row stride a
+    multiple of 8), else 8-byte vectors of 4: the binary16 / bfloat16 axpby
+    (ahead-of-time kernels) and a per-row affine map compiled at run time, over
+    padded rows, a partial last vector and a batch of planes; the padding of
+    the output rows must stay untouched."""
+    B, R = 3, 37
+    rng = np.random.default_rng(n3 + stride + len(which))
+    dt = "f16" if which == "jit" else which
+
+    def draw(shape):
+        f = (rng.standard_normal(shape) * 8).astype(np.float32)
+        return (f.view(np.uint32) >> 16).astype(np.uint16) if dt == "bf16" else f.astype(np.float16)
+
+    xs, ys = draw((B, R, stride)), draw((B, R + 1, stride))
+    os_ = draw((B, R, stride))
+    x, y, o = xs[:, :, :n3], ys[:, 1:, :n3], os_[:, :, :n3]
+    if which == "jit":
+        cs = draw((B, R, 1))
+        c = as_strided(cs, shape=(B, R, n3), strides=(cs.strides[0], cs.strides[1], 0), writeable=False)
+        spec = [("x", ("load", "f16", 3)), ("y", ("load", "f16", 3)), ("c", ("load", "f16", 3)),
+                ("p", ("mul", "x", "c")), ("q", ("sub", "p", "y")), ("m", ("max", "q", "x")), ("o", ("store", "m", 3))]
+        ins = [(x, xs), (y, ys), (c, cs)]
+    else:
+        spec = AXPBY16[dt]
+        a, b = (np.float16(1.5), np.float16(-0.25)) if dt == "f16" else (np.uint16(0x3FC0), np.uint16(0xBE80))
+        ins = [(x, xs), (y, ys), a, b]
+    plan = run_views(spec, ins, [(o, os_)], False, "rows16 %s %d/%d" % (which, n3, stride), jit=which == "jit")
+    assert plan["path"] == "rows" and plan["elems_per_thread"] == (8 if stride % 8 == 0 else 4), plan
+    assert plan["kernel"] == ("jit_rows" if which == "jit" else "rows_axpby_" + dt), plan

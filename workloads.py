@@ -158,6 +158,17 @@ BIAS_NCHW = [
     ("out", ("store", "o", 4)),
 ]
 
+# The same map in binary16 (scale and bias binary16 too; every operation
+# rounds to binary16).
+BIAS_NCHW_F16 = [
+    ("x", ("load", "f16", 4)),
+    ("scale", ("load", "f16", 4)),
+    ("bias", ("load", "f16", 4)),
+    ("xs", ("mul", "x", "scale")),
+    ("o", ("add", "xs", "bias")),
+    ("out", ("store", "o", 4)),
+]
+
 # z = x + y over rank-2 views (the gather path's workloads below).
 ADD2_F32 = [
     ("x", ("load", "f32", 2)),
@@ -209,6 +220,8 @@ WORKLOADS = {
                                "y and out contiguous (rows start 4 bytes off 16-byte alignment)"),
     "narrow_rows_f32": dict(index=15, spec=ADD2_F32, shape=(1 << 23, 6),
                             label="out = x + y, fp32 2^23 x 6, x in rows of 8 (row stride 8), y and out contiguous"),
+    "bias_nchw_f16": dict(index=16, spec=BIAS_NCHW_F16, shape=(32, 256, 128, 256), varies={"scale": (1,), "bias": (1,)},
+                          label="out = x*scale[c] + bias[c], binary16 NCHW 32 x 256 x 128 x 256, per-channel broadcast"),
 }
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
@@ -338,11 +351,13 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
         y = _uniform_pm1_f32(rng, (b, c, r))
         extra = {"storage": [x, y, None]}
         return [x, y.transpose(0, 2, 1), sc["alpha"]], extra
-    elif workload == "bias_nchw":
+    elif workload in ("bias_nchw", "bias_nchw_f16"):
         shp = shape_of(workload, shape=shape)
         x = _uniform_pm1_f32(rng, shp)
         scale = rng.standard_normal(shp[1], dtype=np.float32)
         bias = rng.standard_normal(shp[1], dtype=np.float32)
+        if workload == "bias_nchw_f16":
+            x, scale, bias = x.astype(np.float16), scale.astype(np.float16), bias.astype(np.float16)
         per_channel = lambda v: np.broadcast_to(v.reshape(1, -1, 1, 1), shp)
         extra = {"storage": [x, scale, bias]}
         return [x, per_channel(scale), per_channel(bias)], extra
