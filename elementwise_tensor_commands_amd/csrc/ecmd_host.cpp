@@ -1039,7 +1039,22 @@ bool tiled_nt()
 JitRequest jit_request(const Selection &S, const Program &P)
 {
     if (S.path == CMD_PATH_LINEAR) return JitRequest{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, P};
-    if (S.path == CMD_PATH_ROWS) return JitRequest{JIT_ROWS, S.rows_v, S.rows_v, S.shape.nt_load, S.shape.nt_store, P};
+    if (S.path == CMD_PATH_ROWS) {
+        // Which inputs are row-constant: fixed in the kernel when one of them
+        // is 16-bit, else read from the argument block as the ahead-of-time
+        // kernels do.  With the flag read at run time, every 16-bit input
+        // carries code for both forms (a broadcast value, a vector to
+        // unpack): a binary16 per-channel affine map ran 5-9% slower; for
+        // 32-bit row constants, fixed in the kernel they become scalar loads
+        // and a per-channel scale ran 2.6% slower.  ECMD_ROWS_RC = 0 / 1
+        // forces either form (A/B runs).
+        bool rc16 = false;
+        for (int k = 0; k < P.n_in; ++k) rc16 = rc16 || (S.rowconst[k] && is16(P.in_ty[k]));
+        int rc = env_int("ECMD_ROWS_RC", rc16 ? 1 : 0) != 0 ? 0 : -1;
+        for (int k = 0; k < P.n_in && rc >= 0; ++k)
+            if (S.rowconst[k]) rc |= 1 << k;
+        return JitRequest{JIT_ROWS, S.rows_v, S.rows_v, S.shape.nt_load, S.shape.nt_store, P, rc};
+    }
     if (S.path == CMD_PATH_GATHER)
         return JitRequest{JIT_GATHER, S.e, 0, S.shape.nt_load, false, P, 0, 0, 0, 0, S.g_mode};
     const bool nt = tiled_nt();

@@ -393,8 +393,8 @@ std::string jit_name(const JitRequest &r)
         std::snprintf(b, sizeof b, "ecmd::k_gather_cc<ecmd::CtEval<ecmd::kJitProg>, %d, %d, %s>", r.e, r.mode,
                       r.ntl ? "true" : "false");
     else
-        std::snprintf(b, sizeof b, "ecmd::k_rows<ecmd::CtEval<ecmd::kJitProg>, %s, %s, %d>", r.ntl ? "true" : "false",
-                      r.nts ? "true" : "false", r.e);
+        std::snprintf(b, sizeof b, "ecmd::k_rows<ecmd::CtEval<ecmd::kJitProg>, %s, %s, %d, %d>",
+                      r.ntl ? "true" : "false", r.nts ? "true" : "false", r.e, r.mask);
     return b;
 }
 

@@ -26,7 +26,7 @@ struct JitRequest {
     int e, g;          // linear: elements per work-item and per vector access
     bool ntl, nts;     // nontemporal loads / stores (tiled: ntl for both)
     Program prog;
-    int mask = 0;      // tiled: staged inputs (bit k = input k)
+    int mask = 0;      // tiled: staged inputs; rows: row-constant inputs (bit k = input k)
     int tm = 0, tn = 0, tb = 0;   // tiled: tile shape and work-items
     int mode = 0;      // gather: 1 segments, 2 whole rows of a plane, 3 whole rows (e: elements per work-item)
 };

@@ -38,7 +38,9 @@ namespace ecmd {
 // the row and the operands' row offsets are then computed once per wavefront
 // from its first lane (the lowest lane is active whenever any is), in scalar
 // registers.
-template <class EV, bool NTL, bool NTS, bool WROW, int V>
+// RC: bit k = input k is row-constant, fixed at compile time (kernels
+// compiled for one launch's views); -1: read from A.in_rowconst.
+template <class EV, bool NTL, bool NTS, bool WROW, int V, int RC>
 __device__ __forceinline__ void rows_body(const StridedArgs &A, uint32_t v)
 {
     const uint32_t q = fast_div(A.div_vec, WROW ? __builtin_amdgcn_readfirstlane(v) : v);
@@ -58,7 +60,7 @@ __device__ __forceinline__ void rows_body(const StridedArgs &A, uint32_t v)
         if (k < EV::n_in(A.prog)) {
             const uint8_t ty = EV::in_ty(A.prog, k);
             const int64_t row = (int64_t)b0 * A.in_s[k][0] + (int64_t)b1 * A.in_s[k][1] + (int64_t)r * A.in_s[k][2];
-            if (A.in_rowconst[k]) {
+            if (RC >= 0 ? ((RC >> k) & 1) != 0 : A.in_rowconst[k] != 0) {
                 uint32_t one[1];
                 load_elems<1, false>(A.in[k], ty, row, 1, one);
                 raw[k][0] = one[0];
@@ -74,7 +76,7 @@ __device__ __forceinline__ void rows_body(const StridedArgs &A, uint32_t v)
     for (int k = 0; k < kMaxIn; ++k) {
         if (k < EV::n_in(A.prog)) {
             const uint8_t ty = EV::in_ty(A.prog, k);
-            if (A.in_rowconst[k]) {
+            if (RC >= 0 ? ((RC >> k) & 1) != 0 : A.in_rowconst[k] != 0) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) R.in[k][e] = raw[k][0];
             } else {
@@ -97,14 +99,14 @@ __device__ __forceinline__ void rows_body(const StridedArgs &A, uint32_t v)
     }
 }
 
-template <class EV, bool NTL, bool NTS, int V = 4>
+template <class EV, bool NTL, bool NTS, int V = 4, int RC = -1>
 __global__ __launch_bounds__(kRowsBlock) void k_rows(const StridedArgs A)
 {
     // The host keeps n_vec below 2^31, so vector and row indexes are 32-bit.
     const uint32_t v = blockIdx.x * (uint32_t)kRowsBlock + threadIdx.x;
     if (v >= (uint32_t)A.n_vec) return;
-    if (A.wave_in_row) rows_body<EV, NTL, NTS, true, V>(A, v);
-    else rows_body<EV, NTL, NTS, false, V>(A, v);
+    if (A.wave_in_row) rows_body<EV, NTL, NTS, true, V, RC>(A, v);
+    else rows_body<EV, NTL, NTS, false, V, RC>(A, v);
 }
 
 }  // namespace ecmd

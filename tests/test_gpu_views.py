@@ -255,3 +255,35 @@ def test_rows_16bit_vectors(which, n3, stride):
     plan = run_views(spec, ins, [(o, os_)], False, "rows16 %s %d/%d" % (which, n3, stride), jit=which == "jit")
     assert plan["path"] == "rows" and plan["elems_per_thread"] == (8 if stride % 8 == 0 else 4), plan
     assert plan["kernel"] == ("jit_rows" if which == "jit" else "rows_axpby_" + dt), plan
+
+
+@pytest.mark.parametrize("rc", ["0", "1"])
+@pytest.mark.parametrize("dt", ["f16", "f32", "bf16"])
+def test_rows_row_constant_forms(monkeypatch, rc, dt):
+    """A kernel compiled at run time for the rows path, with its row-constant
+    inputs read from the argument block (ECMD_ROWS_RC=0) or fixed in the
+    kernel (1), over per-channel views of several batches, including rows
+    with a partial last vector."""
+    monkeypatch.setenv("ECMD_ROWS_RC", rc)
+    rng = np.random.default_rng(600 + int(rc) + len(dt))
+    N, C, L = 3, 11, 1003
+
+    def draw(shape):
+        f = (rng.standard_normal(shape) * 8).astype(np.float32)
+        if dt == "bf16":
+            return (f.view(np.uint32) >> 16).astype(np.uint16)
+        return f.astype(np.float16) if dt == "f16" else f
+
+    xs = draw((N, C, L + 5))                     # rows of L + 5: 16-byte aligned only for f32
+    if dt != "f32":
+        xs = draw((N, C, L + 13))                # L + 13 = 1016: a multiple of 8
+    x = xs[:, :, :L]
+    cs, bs = draw((C, 1)), draw((N, C, 1))
+    c = as_strided(cs, shape=(N, C, L), strides=(0, cs.strides[0], 0), writeable=False)
+    b = as_strided(bs, shape=(N, C, L), strides=(bs.strides[0], bs.strides[1], 0), writeable=False)
+    spec = [("x", ("load", dt, 3)), ("c", ("load", dt, 3)), ("b", ("load", dt, 3)), ("m", ("mul", "x", "c")),
+            ("a", ("sub", "m", "b")), ("o", ("store", "a", 3))]
+    os_ = draw((N, C, xs.shape[2]))
+    o = os_[:, :, :L]
+    plan = run_views(spec, [(x, xs), (c, cs), (b, bs)], [(o, os_)], False, "rows rc=%s %s" % (rc, dt), jit=True)
+    assert plan["path"] == "rows" and plan["kernel"] == "jit_rows", plan
