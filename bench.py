@@ -47,14 +47,15 @@ DTYPE_OF = {"add_f32": "f32", "int_fused": "i32", "axpby_f32": "f32", "mixed_two
             "transposed_2d": "f32", "copy_f32": "f32", "classify_u32": "i32", "fill_f32": "f32",
             "batched_transpose": "f32", "bias_nchw": "f32", "axpby_f16": "f16", "axpby_bf16": "bf16",
             "bias_relu_f32": "f32", "transposed_relu": "f32", "odd_rows_f32": "f32", "narrow_rows_f32": "f32",
-            "bias_nchw_f16": "f16"}
+            "bias_nchw_f16": "f16", "transposed_2d_f16": "f16"}
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 # Measured in every run besides the five configurations: the plain copy (the
 # reference for "% of copy") and three programs with no ahead-of-time kernel.
 LINE_EXTRA = ["copy_f32", "bias_relu_f32", "transposed_relu", "mixed_two_out@noaot"]
 # --all adds the widened op set, rank-3/4 views, native 16-bit arithmetic, the
 # gather path and the interpreters.
-ALL_EXTRA = ["classify_u32", "fill_f32", "batched_transpose", "bias_nchw", "bias_nchw_f16", "axpby_f16", "axpby_bf16",
+ALL_EXTRA = ["classify_u32", "fill_f32", "batched_transpose", "transposed_2d_f16", "bias_nchw", "bias_nchw_f16",
+             "axpby_f16", "axpby_bf16",
              "odd_rows_f32", "narrow_rows_f32", "int_fused_wide", "bias_relu_f32@interp",
              "transposed_relu@interp", "mixed_two_out@interp", "odd_rows_f32@interp", "narrow_rows_f32@interp"]
 PROFILES = os.path.join(ROOT, "profiles")

@@ -86,6 +86,7 @@ struct Selection {
     int64_t g_div = 0, g_waves = 0, g_rows_per_wave = 0;
     int g_align = 0;            // gather path, compiled kernel, segments: 1 + the output they are laid from (0: none)
     int rows_v = 4;             // rows path, compiled kernels: elements per vector (8: every operand 16-bit)
+    int tiled_v = 4;            // tiled path, compiled kernels: the same
     const char *name = "";
 };
 
@@ -829,24 +830,32 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
         for (int k = 0; k < P.n_in; ++k) move(T.in_s[k]);
         for (int k = 0; k < P.n_out; ++k) move(T.out_s[k]);
     }
-    // Full tiles access 4-element vectors that start at a multiple of 4 along
-    // the view's unit-stride dimension `unit`: the base and every other stride
-    // must keep them 4-element aligned.
-    auto plane_aligned = [&](const View &v, const int64_t (&st)[4], int unit) {
-        bool ok = aligned(v.ptr, 4 * esize(v.dtype));
+    // Full tiles access vectors of `vec` elements that start at a multiple of
+    // vec along the view's unit-stride dimension `unit`: the base and every
+    // other stride must keep them vec-element aligned.  tiled8: 8-element
+    // vectors would do too, and every operand is 16-bit (16-byte vectors).
+    auto plane_aligned = [&](const View &v, const int64_t (&st)[4], int unit, int vec) {
+        bool ok = aligned(v.ptr, vec * esize(v.dtype));
         for (int d = 0; d < 4 && ok; ++d)
-            if (d != unit && T.n[d] > 1) ok = st[d] % 4 == 0;
+            if (d != unit && T.n[d] > 1) ok = st[d] % vec == 0;
         return ok;
     };
     uint8_t staged[kMaxIn] = {}, rowconst[kMaxIn] = {};
-    for (int k = 0; k < P.n_out && tiled; ++k) tiled = plane_aligned(B.out[k], T.out_s[k], 3);
+    bool tiled8 = true;
+    for (int k = 0; k < P.n_out && tiled; ++k) {
+        tiled = plane_aligned(B.out[k], T.out_s[k], 3, 4);
+        tiled8 = tiled8 && esize(B.out[k].dtype) == 2 && plane_aligned(B.out[k], T.out_s[k], 3, 8);
+    }
     for (int k = 0; k < P.n_in && tiled; ++k) {
+        tiled8 = tiled8 && esize(B.in[k].dtype) == 2;
         if (T.in_s[k][3] == 0) {
             rowconst[k] = 1;
         } else if (T.in_s[k][3] == 1) {
-            tiled = plane_aligned(B.in[k], T.in_s[k], 3);
+            tiled = plane_aligned(B.in[k], T.in_s[k], 3, 4);
+            tiled8 = tiled8 && plane_aligned(B.in[k], T.in_s[k], 3, 8);
         } else {
-            tiled = plane_aligned(B.in[k], T.in_s[k], 2);
+            tiled = plane_aligned(B.in[k], T.in_s[k], 2, 4);
+            tiled8 = tiled8 && plane_aligned(B.in[k], T.in_s[k], 2, 8);
             staged[k] = (uint8_t)(++n_staged);
             mask |= 1 << k;
         }
@@ -879,12 +888,34 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
             // holds in registers (with 256 work-items, eight: max(X + 2 Y^T, 0)
             // ran at 5,064 GB/s against 5,770); ECMD_TILE overrides.  Its
             // staging tiles must fit the 64 KiB a module kernel may use.
-            const TileShape ts = std::getenv("ECMD_TILE") ? tile_shape() : TileShape{32, 256, 512};
-            const int lds = n_staged * ts.tm * ts.tn * 4;
+            //   Programs whose operands are all 16-bit take vectors of 8
+            // elements (16 bytes; with 4, every access is 8 bytes and a
+            // half-wavefront covers half lines) on 64 x 256 tiles with 512
+            // work-items, again four chunks per work-item (a binary16
+            // X + 2 Y^T at 16384^2: 5,850-5,920 GB/s; 64 x 128 tiles 5,290,
+            // vectors of 4 on 32 x 256 tiles 5,245); ECMD_TILE may name a
+            // shape whose sides are multiples of 64, ECMD_TILED_V=4 keeps
+            // vectors of 4.
+            // With more staged inputs than that LDS holds, the same split on
+            // narrower tiles.
+            const bool v8 = tiled8 && env_int("ECMD_TILED_V", 8) != 4;
+            const int unit = v8 ? 64 : 32;   // tile sides: multiples of 8 vectors
+            TileShape ts = v8 ? TileShape{64, 256, 512} : TileShape{32, 256, 512};
+            if (const char *v = std::getenv("ECMD_TILE")) {
+                int a = 0, b = 0, c = 256;
+                if (std::sscanf(v, "%dx%dx%d", &a, &b, &c) >= 2 && a > 0 && b > 0 && a % unit == 0 &&
+                    b % unit == 0 && (c == 256 || c == 512) && a * b / ((v8 ? 8 : 4) * c) >= 1 && a * b <= 65536)
+                    ts = TileShape{a, b, c};
+            }
+            const int word_elems = v8 ? 2 : 1;   // 16-bit tiles keep two elements per LDS word
+            if (n_staged * ts.tm * ts.tn * 4 / word_elems > 65536) ts = TileShape{ts.tm, 128, 256};
+            if (n_staged * ts.tm * ts.tn * 4 / word_elems > 65536) ts = TileShape{ts.tm, 64, 256};
+            const int lds = n_staged * ts.tm * ts.tn * 4 / word_elems;
             if (lds <= 65536) {
                 S.jit = true;
                 S.tile = ts;
                 S.lds = lds;
+                S.tiled_v = v8 ? 8 : 4;
             }
         }
         if (S.variant < 0 && !S.jit) {
@@ -920,7 +951,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
             }
         }
         S.walk = (int)env_int("ECMD_TILE_WALK", kDefaultTileWalk);
-        S.e = 4;
+        S.e = S.tiled_v;
         S.block = S.tile.block;
         S.tiles_r = (T.n[2] + S.tile.tm - 1) / S.tile.tm;
         S.tiles_c = (T.n[3] + S.tile.tn - 1) / S.tile.tn;
@@ -1058,7 +1089,7 @@ JitRequest jit_request(const Selection &S, const Program &P)
     if (S.path == CMD_PATH_GATHER)
         return JitRequest{JIT_GATHER, S.e, 0, S.shape.nt_load, false, P, 0, 0, 0, 0, S.g_mode};
     const bool nt = tiled_nt();
-    return JitRequest{JIT_TILED, 4, 4, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
+    return JitRequest{JIT_TILED, S.tiled_v, S.tiled_v, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
 }
 
 int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int cu_count, bool allow_jit)

@@ -33,7 +33,7 @@ struct JitRequest {
 
 // Template instance the request names, e.g.
 // "ecmd::k_linear<ecmd::CtEval<ecmd::kJitProg>, 4, 4, true, true, true>" or
-// "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, 2, true, 32, 256, 512, true>".
+// "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, 2, true, 32, 256, 512, true, 4>".
 std::string jit_name(const JitRequest &r);
 
 // Make sure the code object exists (memory, else disk, else compile and store

@@ -28,6 +28,12 @@
 // The swizzle makes both LDS phases free of bank conflicts (the argument is
 // at tile_word; a host test checks it for every instantiated shape), with no
 // padding words.
+// When every operand is 16-bit, the kernels compiled at run time take vectors
+// of V = 8 elements instead (16-byte accesses; each half-wavefront 4 x 64
+// elements, whole lines again), with tile_split8 and tile sides that are
+// multiples of 64, and keep two elements per LDS word (tile_pair_word: the
+// staging loads' words are written as loaded), so that a 64 x 256 tile takes
+// 32 KiB.
 // In the specialised kernels the direct inputs' loads are issued before the
 // barrier, together with the staging loads, so that a tile waits for one
 // round trip to memory instead of two.  Full tiles use the nontemporal cache
@@ -68,23 +74,36 @@ __device__ __forceinline__ int stage_pos(const StridedArgs &A, int k)
     else return __builtin_popcount(MASK & ((1 << k) - 1));
 }
 
-__device__ __forceinline__ int clamp4(int64_t left) { return left <= 0 ? 0 : (left >= 4 ? 4 : (int)left); }
+template <int V>
+__device__ __forceinline__ int clampv(int64_t left) { return left <= 0 ? 0 : (left >= V ? V : (int)left); }
+
+// Vectors of V elements: 4 (tile_split), or 8 for tiles whose operands are
+// all 16-bit (tile_split8), so that every access is 16 bytes wide and a
+// half-wavefront's access covers whole 128-byte lines.
+template <int V>
+__device__ __forceinline__ void vsplit(int v, int minor_len, int &major, int &minor)
+{
+    if constexpr (V == 4) tile_split(v, minor_len, major, minor);
+    else tile_split8(v, minor_len, major, minor);
+}
 
 // Whether the tile body's tile is full: decided at run time, or known at
 // compile time to be full or to be an edge tile.
 enum TileKind { kTileAny = 0, kTileFull = 1, kTileEdge = 2 };
 
-template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND>
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND, int V>
 __device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, uint32_t b0, uint32_t b1, int64_t r0,
                                           int64_t c0);
 
 // SPLIT: full and edge tiles run two separate instances of the tile body (see
-// below); otherwise one body tests `full` at each access.
-template <class EV, int MASK, bool NT, int TM, int TN, int TB, bool SPLIT>
+// below); otherwise one body tests `full` at each access.  V: elements per
+// vector (4, or 8 when every operand is 16-bit).
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, bool SPLIT, int V = 4>
 __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
 {
-    static_assert(TN * TM / 4 / TB >= 1, "tile too small for the work-group");
-    static_assert(TM % 32 == 0 && TN % 32 == 0 && TB % 64 == 0, "tile split needs multiples of 32");
+    static_assert(V == 4 || V == 8, "vectors of 4 or 8 elements");
+    static_assert(TN * TM / V / TB >= 1, "tile too small for the work-group");
+    static_assert(TM % (8 * V) == 0 && TN % (8 * V) == 0 && TB % 64 == 0, "tile split needs multiples of 8 V");
 
     // Plane and tile coordinates (all counts fit in 32 bits: the grid is one
     // dimension).  Each plane (batch index) has tiles_r x tiles_c tiles.
@@ -115,21 +134,21 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
         // per-element path whose registers the compiler could merge with the
         // vector loads' (hiprtc's build of the one-body form did that, making
         // every staging load wait for all loads before it).
-        if (full) tile_body<EV, MASK, NT, TM, TN, TB, kTileFull>(A, true, b0, b1, r0, c0);
-        else tile_body<EV, MASK, NT, TM, TN, TB, kTileEdge>(A, false, b0, b1, r0, c0);
+        if (full) tile_body<EV, MASK, NT, TM, TN, TB, kTileFull, V>(A, true, b0, b1, r0, c0);
+        else tile_body<EV, MASK, NT, TM, TN, TB, kTileEdge, V>(A, false, b0, b1, r0, c0);
     } else {
-        tile_body<EV, MASK, NT, TM, TN, TB, kTileAny>(A, full, b0, b1, r0, c0);
+        tile_body<EV, MASK, NT, TM, TN, TB, kTileAny, V>(A, full, b0, b1, r0, c0);
     }
 }
 
-template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND>
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND, int V>
 __device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, uint32_t b0, uint32_t b1, int64_t r0,
                                           int64_t c0)
 {
     const bool full = KIND == kTileAny ? full_tile : KIND == kTileFull;
-    constexpr int kWords = TN * TM;
-    constexpr int kSV = TN * TM / 4 / TB;               // staging vectors per work-item per staged input
-    constexpr int kP = TM * TN / 4 / TB;                // chunks per work-item
+    constexpr int kWords = V == 8 ? TN * TM / 2 : TN * TM;   // LDS words per staged input
+    constexpr int kSV = TN * TM / V / TB;               // staging vectors per work-item per staged input
+    constexpr int kP = TM * TN / V / TB;                // chunks per work-item
     constexpr bool kPrefetch = MASK != kMaskRuntime;
     extern __shared__ uint32_t lds[];
     const int64_t rows = A.n[2], cols = A.n[3];
@@ -141,36 +160,36 @@ __device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, 
     // Direct inputs of every chunk, loaded up front in the specialised kernels
     // (the interpreter keeps one chunk's registers at a time).
     constexpr int kRegSets = kPrefetch ? kP : 1;
-    Regs<4> R[kRegSets];
+    Regs<V> R[kRegSets];
     int count[kP];
 #pragma unroll
     for (int p = 0; p < kP; ++p) {
         int rl, cl;
-        tile_split(t + TB * p, TN, rl, cl);
-        count[p] = full ? 4 : (r0 + rl < rows ? clamp4(cols - (c0 + cl)) : 0);
+        vsplit<V>(t + TB * p, TN, rl, cl);
+        count[p] = full ? V : (r0 + rl < rows ? clampv<V>(cols - (c0 + cl)) : 0);
     }
     auto load_direct = [&](int p) {
         int rl, cl;
-        tile_split(t + TB * p, TN, rl, cl);
+        vsplit<V>(t + TB * p, TN, rl, cl);
         const int64_t r = r0 + rl, c = c0 + cl;
-        Regs<4> &Rp = R[kPrefetch ? p : 0];
+        Regs<V> &Rp = R[kPrefetch ? p : 0];
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
             if (k < EV::n_in(A.prog) && !staged<MASK>(A, k)) {
                 const uint8_t ty = EV::in_ty(A.prog, k);
                 if (MASK == kMaskRuntime && A.in_rowconst[k]) {
-                    // one value per row, the same for the 4 columns
+                    // one value per row, the same for the V columns
                     if (count[p] > 0) {
                         uint32_t one[1];
                         load_elems<1, false>(A.in[k], ty, in_base(k) + r * A.in_s[k][2], 1, one);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) Rp.in[k][e] = one[0];
+                        for (int e = 0; e < V; ++e) Rp.in[k][e] = one[0];
                     }
                     continue;
                 }
                 const int64_t off = in_base(k) + r * A.in_s[k][2] + c;
-                if (full) load_group<4, true, NT>(A.in[k], ty, off, 4, Rp.in[k]);
-                else if (count[p] > 0) load_elems<4, false>(A.in[k], ty, off, count[p], Rp.in[k]);
+                if (full) load_group<V, true, NT>(A.in[k], ty, off, V, Rp.in[k]);
+                else if (count[p] > 0) load_elems<V, false>(A.in[k], ty, off, count[p], Rp.in[k]);
             }
         }
     };
@@ -186,26 +205,46 @@ __device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, 
         if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
             const uint8_t ty = EV::in_ty(A.prog, k);
             uint32_t *dst = lds + stage_pos<MASK>(A, k) * kWords;
+            // V = 4: one element per word (the staging vector's 4 words);
+            // V = 8: 16-bit pairs of rows, the 4 words as loaded (load_raw)
             uint32_t sv[kSV][4];
 #pragma unroll
             for (int j = 0; j < kSV; ++j) {
                 int cl, rl;
-                tile_split(t + TB * j, TM, cl, rl);
+                vsplit<V>(t + TB * j, TM, cl, rl);
                 const int64_t off = in_base(k) + (c0 + cl) * A.in_s[k][3] + (r0 + rl);
                 if (full) {
-                    load_group<4, true, NT>(A.in[k], ty, off, 4, sv[j]);
+                    if constexpr (V == 8) {
+                        uint32_t w[8];
+                        load_raw<8, NT>(A.in[k], ty, off, w);   // 16-bit: words 0..3
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sv[j][e] = w[e];
+                    } else {
+                        load_group<4, true, NT>(A.in[k], ty, off, 4, sv[j]);
+                    }
                 } else {
-                    const int cnt = c0 + cl < cols ? clamp4(rows - (r0 + rl)) : 0;
-                    if (cnt > 0) load_elems<4, false>(A.in[k], ty, off, cnt, sv[j]);
-                    else sv[j][0] = sv[j][1] = sv[j][2] = sv[j][3] = 0u;
+                    const int cnt = c0 + cl < cols ? clampv<V>(rows - (r0 + rl)) : 0;
+                    if (cnt > 0) {
+                        uint32_t w[V];
+                        if constexpr (V == 8) load_raw_elems<8>(A.in[k], ty, off, cnt, w);
+                        else load_elems<4, false>(A.in[k], ty, off, cnt, w);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sv[j][e] = w[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sv[j][e] = 0u;
+                    }
                 }
             }
 #pragma unroll
             for (int j = 0; j < kSV; ++j) {
                 int cl, rl;
-                tile_split(t + TB * j, TM, cl, rl);
+                vsplit<V>(t + TB * j, TM, cl, rl);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[tile_word(TM, cl, rl + e)] = sv[j][e];
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (V == 8) dst[tile_pair_word(TM, cl, (rl >> 1) + e)] = sv[j][e];
+                    else dst[tile_word(TM, cl, rl + e)] = sv[j][e];
+                }
             }
         }
     }
@@ -215,26 +254,29 @@ __device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, 
     for (int p = 0; p < kP; ++p) {
         if (count[p] == 0) continue;
         int rl, cl;
-        tile_split(t + TB * p, TN, rl, cl);
+        vsplit<V>(t + TB * p, TN, rl, cl);
         const int64_t r = r0 + rl, c = c0 + cl;
         if constexpr (!kPrefetch) load_direct(p);
-        Regs<4> &Rp = R[kPrefetch ? p : 0];
+        Regs<V> &Rp = R[kPrefetch ? p : 0];
 #pragma unroll
         for (int k = 0; k < kMaxIn; ++k) {
             if (k < EV::n_in(A.prog) && staged<MASK>(A, k)) {
                 const uint32_t *src = lds + stage_pos<MASK>(A, k) * kWords;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Rp.in[k][e] = src[tile_word(TM, cl + e, rl)];
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (V == 8) Rp.in[k][e] = (src[tile_pair_word(TM, cl + e, rl >> 1)] >> (16 * (rl & 1))) & 0xffffu;
+                    else Rp.in[k][e] = src[tile_word(TM, cl + e, rl)];
+                }
             }
         }
-        uint32_t out[kMaxOut][4];
-        EV::template run<4>(A.prog, A.uni, Rp, out);
+        uint32_t out[kMaxOut][V];
+        EV::template run<V>(A.prog, A.uni, Rp, out);
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < EV::n_out(A.prog)) {
                 const int64_t off = out_base(k) + r * A.out_s[k][2] + c;
-                if (full) store_group<4, true, NT>(A.out[k], EV::out_ty(A.prog, k), off, 4, out[k]);
-                else store_elems<4, false, false>(A.out[k], EV::out_ty(A.prog, k), off, count[p], out[k]);
+                if (full) store_group<V, true, NT>(A.out[k], EV::out_ty(A.prog, k), off, V, out[k]);
+                else store_elems<V, false, false>(A.out[k], EV::out_ty(A.prog, k), off, count[p], out[k]);
             }
         }
     }

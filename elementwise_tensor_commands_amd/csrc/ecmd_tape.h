@@ -393,6 +393,32 @@ constexpr void tile_split(int v, int minor_len, int &major, int &minor)
 // columns 4j + e (j over 8 consecutive values): banks 4((a ^ j) mod 8) +
 // (q ^ e), again all distinct.  No padding is needed: tm * tn words.
 constexpr int tile_word(int tm, int c, int r) { return c * tm + (r ^ (c & 31)); }
+
+// The same for tiles whose operands are all 16-bit, in 16-byte vectors of 8
+// elements: item v takes (major, minor..minor+7); each half-wavefront covers
+// 4 consecutive majors by 8 consecutive 8-element groups, 4 runs of 64
+// elements (whole 128-byte lines of binary16); minor_len is a multiple of 64.
+constexpr void tile_split8(int v, int minor_len, int &major, int &minor)
+{
+    const int groups = minor_len / 64;
+    const int g = v >> 5;
+    major = 4 * (g / groups) + ((v >> 3) & 3);
+    minor = 8 * (8 * (g % groups) + (v & 7));
+}
+// LDS word of the staged 16-bit pair (column c, rows 2 p and 2 p + 1), two
+// elements per word (row 2 p in the low half), tm / 2 words per column: the
+// pair index XOR-ed with the column's low five bits and, in bit 1, with bit 5
+// of the column.  A half-wavefront writing word w of its staging vectors (the
+// pair of rows 8i + 2w, 8i + 2w + 1, as loaded) touches pairs 4i + w of
+// columns 4a + q (i = 0..7, q = 0..3): bits 0-1 of the bank vary with q,
+// bits 2-4 with i.  Reading element e of its chunks it touches the pairs of
+// rows 4a + q (two lanes per word: a broadcast) of columns 8j + e
+// (j = 0..7): bit 0 varies with q >> 1, bit 1 with j >> 2 (bit 5 of the
+// column), bits 3-4 with j & 3: 16 words on 16 banks.  tm a multiple of 64.
+constexpr int tile_pair_word(int tm, int c, int p)
+{
+    return c * (tm / 2) + (p ^ (c & 31) ^ (((c >> 5) & 1) << 1));
+}
 int launch_tiled(int variant, bool nt, TileShape shape, const StridedArgs &A, LaunchGeometry g, void *stream);
 // The LDS-file interpreter (see launch_linear_interp) over the tiled path's
 // tiles: by default kTiledInterpM x kTiledInterpN tiles and kTiledInterpBlock

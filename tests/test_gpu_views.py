@@ -115,12 +115,13 @@ def test_batched_transpose_tiles(tile):
     assert plan["specialised"] and plan["path"] == "tiled"
 
 
-@pytest.mark.parametrize("wl", ["batched_transpose", "bias_nchw", "bias_nchw_f16", "odd_rows_f32", "narrow_rows_f32"])
+@pytest.mark.parametrize("wl", ["batched_transpose", "bias_nchw", "bias_nchw_f16", "transposed_2d_f16", "odd_rows_f32",
+                                "narrow_rows_f32"])
 def test_full_size_views(wl):
     """The full shapes the benchmark times, in its launch configuration
-    (binary16 NCHW: compiled at run time), compared with the oracle on every
-    element."""
-    shape = W.WORKLOADS[wl]["shape"]
+    (the binary16 workloads: compiled at run time), compared with the oracle
+    on every element."""
+    shape = W.shape_of(wl)
     print("  full size %s %s" % (wl, shape), flush=True)
     spec = W.WORKLOADS[wl]["spec"]
     vals, extra = W.make_inputs(wl)
@@ -128,7 +129,7 @@ def test_full_size_views(wl):
     gin = W.to_torch(vals, extra, dev())
     import elementwise_tensor_commands_amd as ecmd
     cmd = ecmd.from_spec(spec)
-    if wl == "bias_nchw_f16":
+    if wl.endswith("_f16"):
         cmd.jit(ecmd.JIT_SYNC)
     out = torch.empty(shape, dtype=torch.float16 if wl.endswith("f16") else torch.float32, device=dev())
     plan = cmd.plan(*gin, out)
@@ -137,9 +138,9 @@ def test_full_size_views(wl):
     compare(host(out), ref[0], 0, "%s full (%s)" % (wl, plan["kernel"]))
     assert (plan["path"], plan["kernel"]) == {
         "batched_transpose": ("tiled", "tiled_add_scaled_f32"), "bias_nchw": ("rows", "rows_affine_f32"),
-        "bias_nchw_f16": ("rows", "jit_rows"),
+        "bias_nchw_f16": ("rows", "jit_rows"), "transposed_2d_f16": ("tiled", "jit_tiled"),
         "odd_rows_f32": ("gather", "gather_segments"), "narrow_rows_f32": ("gather", "gather_whole_rows")}[wl]
-    if wl == "bias_nchw_f16":
+    if wl.endswith("_f16"):
         assert plan["elems_per_thread"] == 8, plan
 
 
@@ -287,3 +288,64 @@ def test_rows_row_constant_forms(monkeypatch, rc, dt):
     o = os_[:, :, :L]
     plan = run_views(spec, [(x, xs), (c, cs), (b, bs)], [(o, os_)], False, "rows rc=%s %s" % (rc, dt), jit=True)
     assert plan["path"] == "rows" and plan["kernel"] == "jit_rows", plan
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape,xpad,ypad", [((2, 200, 300), 4, 4), ((1, 64, 128), 0, 0), ((3, 77, 1000), 8, 3),
+                                             ((1, 1000, 72), 24, 0), ((2, 130, 66), 6, 6), ((1, 96, 200), 4, 4),
+                                             ((2, 70, 130), 6, 2)])
+def test_tiled_16bit_vectors(dt, shape, xpad, ypad):
+    """Transposed 16-bit operands on the tiled path, compiled at run time:
+    vectors of 8 elements (64 x 256 tiles) when every plane's rows (X, the
+    outputs: C + xpad) and staged columns (Y: R + ypad) start on 16 bytes,
+    else of 4, with edge tiles on both sides, several planes, padded rows and
+    two outputs; the padding must stay untouched."""
+    B, R, C = shape
+    pad = xpad
+    rng = np.random.default_rng(sum(shape) + xpad + 3 * ypad + len(dt))
+
+    def draw(shp):
+        f = (rng.standard_normal(shp) * 8).astype(np.float32)
+        return (f.view(np.uint32) >> 16).astype(np.uint16) if dt == "bf16" else f.astype(np.float16)
+
+    xs = draw((B, R, C + pad))
+    ys = draw((B, C, R + ypad))
+    x, yt = xs[:, :, :C], ys[:, :, :R].transpose(0, 2, 1)
+    o0s, o1s = draw((B, R, C + pad)), draw((B, R, C + pad))
+    spec = [("X", ("load", dt, 3)), ("Yt", ("load", dt, 3)), ("a", ("scalar", dt)), ("ay", ("mul", "a", "Yt")),
+            ("s", ("add", "X", "ay")), ("m", ("min", "s", "X")), ("n", ("neg", "m")),
+            ("o0", ("store", "s", 3)), ("o1", ("store", "n", 3))]
+    a = np.float16(-1.5) if dt == "f16" else np.uint16(0xBFC0)
+    plan = run_views(spec, [(x, xs), (yt, ys), a], [(o0s[:, :, :C], o0s), (o1s[:, :, :C], o1s)], False,
+                     "tiled16 %s %s pad %d/%d" % (dt, shape, xpad, ypad), jit=True)
+    v = 8 if (C + xpad) % 8 == 0 and (R + ypad) % 8 == 0 else 4
+    assert plan["path"] == "tiled" and plan["kernel"] == "jit_tiled" and plan["elems_per_thread"] == v, plan
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+@pytest.mark.parametrize("n_staged", [1, 2, 3])
+def test_tiled_compiled_staged_counts(dt, n_staged):
+    """One to three transposed inputs on the tiled path, compiled at run
+    time: the staging tiles of all of them fit the 64 KiB of LDS (narrower
+    tiles for more inputs), over a batch of planes with edge tiles."""
+    B, R, C = 2, 200, 264
+    rng = np.random.default_rng(70 + n_staged + len(dt))
+
+    def draw(shp):
+        return (rng.standard_normal(shp) * 4).astype(np.float16 if dt == "f16" else np.float32)
+
+    xs = draw((B, R, C + 8))
+    ins = [(xs[:, :, :C], xs)]
+    spec = [("X", ("load", dt, 3))]
+    acc = "X"
+    for k in range(n_staged):
+        ys = draw((B, C, R + 8))
+        ins.append((ys[:, :, :R].transpose(0, 2, 1), ys))
+        spec.append(("Y%d" % k, ("load", dt, 3)))
+        spec.append(("s%d" % k, ("add", acc, "Y%d" % k)))
+        acc = "s%d" % k
+    spec.append(("o", ("store", acc, 3)))
+    os_ = draw((B, R, C + 8))
+    plan = run_views(spec, ins, [(os_[:, :, :C], os_)], False, "staged x%d %s" % (n_staged, dt), jit=True)
+    assert plan["path"] == "tiled" and plan["kernel"] == "jit_tiled", plan
+    assert plan["lds_bytes"] <= 65536 and plan["elems_per_thread"] == (8 if dt == "f16" else 4), plan

@@ -603,6 +603,28 @@ def test_bias_nchw_workload_matches_numpy(oracle_mod, shape):
     assert np.array_equal(o.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("shape", [(2, 5, 3, 7), (1, 1, 1, 1), (3, 16, 1, 9)])
+def test_bias_nchw_f16_workload_matches_numpy(oracle_mod, shape):
+    """The binary16 per-channel map: each operation rounds to binary16, as
+    NumPy's float16 multiply and add do (binary32 arithmetic, exact for one
+    product or sum of two binary16 values, then one rounding)."""
+    vals, extra = W.make_inputs("bias_nchw_f16", shape=shape)
+    assert vals[0].dtype == np.float16 and vals[1].strides[0] == 0
+    (o,) = oracle_mod.from_spec(W.BIAS_NCHW_F16).run(*vals)
+    _, scale, bias = extra["storage"]
+    ref = (vals[0] * scale.reshape(1, -1, 1, 1)).astype(np.float16) + bias.reshape(1, -1, 1, 1)
+    assert ref.dtype == np.float16
+    assert np.array_equal(o.view(np.uint16), ref.view(np.uint16))
+
+
+def test_transposed_f16_workload_matches_numpy(oracle_mod):
+    vals, extra = W.make_inputs("transposed_2d_f16", 96)
+    (o,) = oracle_mod.from_spec(W.TRANSPOSED_2D_F16).run(*vals)
+    ref = vals[0] + (np.float16(2) * extra["Y"].T).astype(np.float16)
+    assert ref.dtype == np.float16
+    assert np.array_equal(o.view(np.uint16), ref.view(np.uint16))
+
+
 # ---------------------------------------------------------------------------
 # Native binary16 / bfloat16 arithmetic and bfloat16 conversions.
 #

@@ -1,9 +1,12 @@
 // Host check of the tiled kernel's work split and LDS layout (tile_split and
-// tile_word in ecmd_tape.h), for the tile shapes given on the command line as
-// TM TN TB triples.  For each shape it checks:
+// tile_word in ecmd_tape.h; for 16-bit tiles tile_split8 and tile_pair_word,
+// two elements per word), for the tile shapes given on the command line as
+// TM TN TB triples (after "-8": shapes of 8-element vectors).  For each shape
+// it checks:
 //   * the output-chunk split and the staging split each cover every 4-element
-//     group of the tile exactly once and stay inside the tile;
-//   * tile_word maps the tile's TM x TN elements one to one onto TM * TN words;
+//     (8-element) group of the tile exactly once and stay inside the tile;
+//   * the layout maps the tile's TM x TN elements (TM x TN / 2 pairs) one to
+//     one onto TM * TN (TM * TN / 2) words;
 //   * under gfx950's LDS model for wave64 four-byte accesses (32 banks, each
 //     half-wavefront served on its own, bank = word mod 32) no half-wavefront
 //     of the staging writes or of the chunk reads has two lanes on one bank
@@ -11,9 +14,27 @@
 // Prints one line per shape and exits non-zero on the first failure.
 #include <cstdio>
 #include <cstdlib>
+#include <string>
 #include <vector>
 
 #include "ecmd_tape.h"
+
+// The split and layout for vectors of V elements.
+template <int V>
+static void split(int v, int minor_len, int &major, int &minor)
+{
+    if constexpr (V == 4) ecmd::tile_split(v, minor_len, major, minor);
+    else ecmd::tile_split8(v, minor_len, major, minor);
+}
+
+// The LDS word holding element (column c, row r), for the element layout
+// (V = 4) or the pair layout (V = 8).
+template <int V>
+static int word(int tm, int c, int r)
+{
+    if constexpr (V == 4) return ecmd::tile_word(tm, c, r);
+    else return ecmd::tile_pair_word(tm, c, r >> 1);
+}
 
 using ecmd::tile_split;
 using ecmd::tile_word;
@@ -46,50 +67,59 @@ static int worst_conflict(const std::vector<int> &words)
     return worst;
 }
 
+template <int V>
 static int check(int tm, int tn, int tb)
 {
-    const int vecs = tm * tn / 4;
-    if (tm % 32 || tn % 32 || tb % 64 || vecs % tb) return fail(tm, tn, tb, "shape not supported by the split");
-    // Splits: (row, 4 columns) chunks and (column, 4 rows) staging vectors.
-    std::vector<int> seen_chunk(vecs, 0), seen_stage(vecs, 0), seen_word(tm * tn, 0);
+    const int vecs = tm * tn / V;
+    const int unit = 8 * V;      // minor extent of a half-wavefront
+    if (tm % unit || tn % unit || tb % 64 || vecs % tb) return fail(tm, tn, tb, "shape not supported by the split");
+    // Splits: (row, V columns) chunks and (column, V rows) staging vectors.
+    const int per_word = V == 8 ? 2 : 1, words = tm * tn / per_word;
+    std::vector<int> seen_chunk(vecs, 0), seen_stage(vecs, 0), seen_word(words, 0);
     for (int v = 0; v < vecs; ++v) {
         int r, c;
-        tile_split(v, tn, r, c);
-        if (r < 0 || r >= tm || c < 0 || c + 3 >= tn || c % 4) return fail(tm, tn, tb, "chunk outside the tile");
-        ++seen_chunk[r * (tn / 4) + c / 4];
+        split<V>(v, tn, r, c);
+        if (r < 0 || r >= tm || c < 0 || c + V - 1 >= tn || c % V) return fail(tm, tn, tb, "chunk outside the tile");
+        ++seen_chunk[r * (tn / V) + c / V];
         int sc, sr;
-        tile_split(v, tm, sc, sr);
-        if (sc < 0 || sc >= tn || sr < 0 || sr + 3 >= tm || sr % 4) return fail(tm, tn, tb, "staging vector outside the tile");
-        ++seen_stage[sc * (tm / 4) + sr / 4];
+        split<V>(v, tm, sc, sr);
+        if (sc < 0 || sc >= tn || sr < 0 || sr + V - 1 >= tm || sr % V)
+            return fail(tm, tn, tb, "staging vector outside the tile");
+        ++seen_stage[sc * (tm / V) + sr / V];
     }
     for (int k = 0; k < vecs; ++k)
         if (seen_chunk[k] != 1 || seen_stage[k] != 1) return fail(tm, tn, tb, "split not one to one");
     for (int c = 0; c < tn; ++c)
-        for (int r = 0; r < tm; ++r) {
-            const int w = tile_word(tm, c, r);
-            if (w < 0 || w >= tm * tn) return fail(tm, tn, tb, "LDS word out of range");
+        for (int r = 0; r < tm; r += per_word) {
+            const int w = word<V>(tm, c, r);
+            if (w < 0 || w >= words) return fail(tm, tn, tb, "LDS word out of range");
+            if (per_word == 2 && word<V>(tm, c, r + 1) != w) return fail(tm, tn, tb, "a pair split over two words");
             ++seen_word[w];
         }
-    for (int w = 0; w < tm * tn; ++w)
+    for (int w = 0; w < words; ++w)
         if (seen_word[w] != 1) return fail(tm, tn, tb, "LDS layout not one to one");
     // Bank conflicts.  Item order: work-item t of pass j is item t + TB * j;
     // a pass is one instruction of every wavefront, so half-wavefronts are
     // 32-aligned runs of items.
+    // Staging writes: one word per element (V = 4) or per pair of rows (V = 8:
+    // word e holds rows 2e, 2e + 1 of the vector); chunk reads: one word per
+    // element either way.
     int worst_w = 0, worst_r = 0;
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < V; ++e) {
         std::vector<int> wr(vecs), rd(vecs);
         for (int v = 0; v < vecs; ++v) {
             int sc, sr, r, c;
-            tile_split(v, tm, sc, sr);
-            wr[v] = tile_word(tm, sc, sr + e);
-            tile_split(v, tn, r, c);
-            rd[v] = tile_word(tm, c + e, r);
+            split<V>(v, tm, sc, sr);
+            wr[v] = word<V>(tm, sc, sr + (V == 8 ? 2 * (e % 4) : e));
+            split<V>(v, tn, r, c);
+            rd[v] = word<V>(tm, c + e, r);
         }
         const int a = worst_conflict(wr), b = worst_conflict(rd);
         worst_w = a > worst_w ? a : worst_w;
         worst_r = b > worst_r ? b : worst_r;
     }
-    std::printf("%dx%dx%d: staging writes %d-way, chunk reads %d-way\n", tm, tn, tb, worst_w, worst_r);
+    std::printf("%s%dx%dx%d: staging writes %d-way, chunk reads %d-way\n", V == 8 ? "8-element " : "", tm, tn, tb,
+                worst_w, worst_r);
     if (worst_w != 1 || worst_r != 1) return fail(tm, tn, tb, "bank conflict");
     return 0;
 }
@@ -128,11 +158,23 @@ static int check_model()
 int main(int argc, char **argv)
 {
     if (check_model()) return 1;
-    if (argc < 4 || (argc - 1) % 3) {
-        std::fprintf(stderr, "usage: %s TM TN TB [TM TN TB ...]\n", argv[0]);
+    bool eight = false;
+    int shapes = 0;
+    for (int i = 1; i < argc;) {
+        if (std::string(argv[i]) == "-8") {
+            eight = true;
+            ++i;
+            continue;
+        }
+        if (i + 2 >= argc) break;
+        const int tm = std::atoi(argv[i]), tn = std::atoi(argv[i + 1]), tb = std::atoi(argv[i + 2]);
+        if (eight ? check<8>(tm, tn, tb) : check<4>(tm, tn, tb)) return 1;
+        ++shapes;
+        i += 3;
+    }
+    if (shapes == 0) {
+        std::fprintf(stderr, "usage: %s TM TN TB [TM TN TB ...] [-8 TM TN TB ...]\n", argv[0]);
         return 2;
     }
-    for (int i = 1; i < argc; i += 3)
-        if (check(std::atoi(argv[i]), std::atoi(argv[i + 1]), std::atoi(argv[i + 2]))) return 1;
     return 0;
 }

@@ -169,6 +169,16 @@ BIAS_NCHW_F16 = [
     ("out", ("store", "o", 4)),
 ]
 
+# The transposed add in binary16 (every operation rounds to binary16).
+TRANSPOSED_2D_F16 = [
+    ("X", ("load", "f16", 2)),
+    ("Yt", ("load", "f16", 2)),
+    ("alpha", ("scalar", "f16")),
+    ("ay", ("mul", "alpha", "Yt")),
+    ("o", ("add", "X", "ay")),
+    ("out", ("store", "o", 2)),
+]
+
 # z = x + y over rank-2 views (the gather path's workloads below).
 ADD2_F32 = [
     ("x", ("load", "f32", 2)),
@@ -222,6 +232,9 @@ WORKLOADS = {
                             label="out = x + y, fp32 2^23 x 6, x in rows of 8 (row stride 8), y and out contiguous"),
     "bias_nchw_f16": dict(index=16, spec=BIAS_NCHW_F16, shape=(32, 256, 128, 256), varies={"scale": (1,), "bias": (1,)},
                           label="out = x*scale[c] + bias[c], binary16 NCHW 32 x 256 x 128 x 256, per-channel broadcast"),
+    "transposed_2d_f16": dict(index=17, spec=TRANSPOSED_2D_F16, n=16384,
+                              label="out[i,j] = X[i,j] + alpha*Y[j,i], binary16 16384x16384, X row stride 16448, "
+                                    "alpha=2"),
 }
 CONFIGS = ["add_f32", "int_fused", "axpby_f32", "mixed_two_out", "transposed_2d"]
 
@@ -230,6 +243,7 @@ SCALARS = {
     "axpby_f32": {"alpha": np.float32(1.5), "beta": np.float32(-0.25)},
     "mixed_two_out": {"s": np.float32(0.5)},
     "transposed_2d": {"alpha": np.float32(2.0)},
+    "transposed_2d_f16": {"alpha": np.float16(2.0)},
     "transposed_relu": {"alpha": np.float32(2.0), "zero": np.float32(0.0)},
     "classify_u32": {"t": np.int32(-2**31)},          # 0x80000000 as unsigned
     "fill_f32": {"s": np.float32(1.25)},
@@ -248,7 +262,7 @@ def shape_of(workload: str, n: int | None = None, shape=None) -> tuple:
     if "shape" in w:
         return tuple(w["shape"] if shape is None else shape)
     n = w["n"] if n is None else n
-    return (n, n) if workload in ("transposed_2d", "transposed_relu") else (n,)
+    return (n, n) if workload in ("transposed_2d", "transposed_relu", "transposed_2d_f16") else (n,)
 
 
 def layout(view: np.ndarray, storage: np.ndarray):
@@ -337,11 +351,13 @@ def make_inputs(workload: str, n: int | None = None, seed: int | None = None,
         vals = [rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32).view(np.int32), sc["t"]]
     elif workload == "fill_f32":
         vals = [sc["s"]]
-    elif workload in ("transposed_2d", "transposed_relu"):
+    elif workload in ("transposed_2d", "transposed_relu", "transposed_2d_f16"):
         rows = cols = n
         xs = np.full((rows, cols + row_pad), np.nan, dtype=np.float32)
         xs[:, :cols] = _uniform_pm1_f32(rng, (rows, cols))
         y = _uniform_pm1_f32(rng, (cols, rows))
+        if workload == "transposed_2d_f16":
+            xs, y = xs.astype(np.float16), y.astype(np.float16)
         vals = [xs[:, :cols], y.T, sc["alpha"]] + ([sc["zero"]] if workload == "transposed_relu" else [])
         extra = {"X_storage": xs, "Y": y, "storage": [xs, y] + [None] * (len(vals) - 2)}
         return vals, extra
