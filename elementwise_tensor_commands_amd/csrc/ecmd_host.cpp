@@ -882,7 +882,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
         S.tile = S.variant == 0 ? tile_shape() : TileShape{64, 64, 256};   // RtEval has one shape
         S.lds = n_staged * S.tile.tn * S.tile.tm * 4;
         S.mask = mask;
-        if (S.variant < 0 && allow_jit && !any_rowconst) {
+        if (S.variant < 0 && allow_jit) {
             // A kernel compiled at run time on 32 x 256 tiles with 512
             // work-items: four chunks per work-item, whose direct inputs it
             // holds in registers (with 256 work-items, eight: max(X + 2 Y^T, 0)
@@ -1089,7 +1089,10 @@ JitRequest jit_request(const Selection &S, const Program &P)
     if (S.path == CMD_PATH_GATHER)
         return JitRequest{JIT_GATHER, S.e, 0, S.shape.nt_load, false, P, 0, 0, 0, 0, S.g_mode};
     const bool nt = tiled_nt();
-    return JitRequest{JIT_TILED, S.tiled_v, S.tiled_v, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
+    JitRequest r{JIT_TILED, S.tiled_v, S.tiled_v, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
+    for (int k = 0; k < P.n_in; ++k)
+        if (S.rowconst[k]) r.rc |= 1 << k;
+    return r;
 }
 
 int prepare(cmd_t h, const cmd_arg *args, int nargs, Bound &B, Selection &S, int cu_count, bool allow_jit)

@@ -387,8 +387,8 @@ std::string jit_name(const JitRequest &r)
         std::snprintf(b, sizeof b, "ecmd::k_linear<ecmd::CtEval<ecmd::kJitProg>, %d, %d, true, %s, %s>", r.e, r.g,
                       r.ntl ? "true" : "false", r.nts ? "true" : "false");
     else if (r.kind == JIT_TILED)
-        std::snprintf(b, sizeof b, "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, %d, %s, %d, %d, %d, true, %d>", r.mask,
-                      r.ntl ? "true" : "false", r.tm, r.tn, r.tb, r.e);
+        std::snprintf(b, sizeof b, "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, %d, %s, %d, %d, %d, true, %d, %d>",
+                      r.mask, r.ntl ? "true" : "false", r.tm, r.tn, r.tb, r.e, r.rc);
     else if (r.kind == JIT_GATHER)
         std::snprintf(b, sizeof b, "ecmd::k_gather_cc<ecmd::CtEval<ecmd::kJitProg>, %d, %d, %s>", r.e, r.mode,
                       r.ntl ? "true" : "false");

@@ -29,11 +29,12 @@ struct JitRequest {
     int mask = 0;      // tiled: staged inputs; rows: row-constant inputs (bit k = input k)
     int tm = 0, tn = 0, tb = 0;   // tiled: tile shape and work-items
     int mode = 0;      // gather: 1 segments, 2 whole rows of a plane, 3 whole rows (e: elements per work-item)
+    int rc = 0;        // tiled: row-constant inputs (bit k = input k)
 };
 
 // Template instance the request names, e.g.
 // "ecmd::k_linear<ecmd::CtEval<ecmd::kJitProg>, 4, 4, true, true, true>" or
-// "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, 2, true, 32, 256, 512, true, 4>".
+// "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, 2, true, 32, 256, 512, true, 4, 0>".
 std::string jit_name(const JitRequest &r);
 
 // Make sure the code object exists (memory, else disk, else compile and store

@@ -91,14 +91,16 @@ __device__ __forceinline__ void vsplit(int v, int minor_len, int &major, int &mi
 // compile time to be full or to be an edge tile.
 enum TileKind { kTileAny = 0, kTileFull = 1, kTileEdge = 2 };
 
-template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND, int V>
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND, int V, int RC>
 __device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, uint32_t b0, uint32_t b1, int64_t r0,
                                           int64_t c0);
 
 // SPLIT: full and edge tiles run two separate instances of the tile body (see
 // below); otherwise one body tests `full` at each access.  V: elements per
-// vector (4, or 8 when every operand is 16-bit).
-template <class EV, int MASK, bool NT, int TM, int TN, int TB, bool SPLIT, int V = 4>
+// vector (4, or 8 when every operand is 16-bit).  RC: row-constant inputs
+// (bit k = input k) when MASK is fixed at compile time; with kMaskRuntime
+// they are read from A.in_rowconst.
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, bool SPLIT, int V = 4, int RC = 0>
 __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
 {
     static_assert(V == 4 || V == 8, "vectors of 4 or 8 elements");
@@ -134,14 +136,14 @@ __global__ __launch_bounds__(TB) void k_tiled(const StridedArgs A)
         // per-element path whose registers the compiler could merge with the
         // vector loads' (hiprtc's build of the one-body form did that, making
         // every staging load wait for all loads before it).
-        if (full) tile_body<EV, MASK, NT, TM, TN, TB, kTileFull, V>(A, true, b0, b1, r0, c0);
-        else tile_body<EV, MASK, NT, TM, TN, TB, kTileEdge, V>(A, false, b0, b1, r0, c0);
+        if (full) tile_body<EV, MASK, NT, TM, TN, TB, kTileFull, V, RC>(A, true, b0, b1, r0, c0);
+        else tile_body<EV, MASK, NT, TM, TN, TB, kTileEdge, V, RC>(A, false, b0, b1, r0, c0);
     } else {
-        tile_body<EV, MASK, NT, TM, TN, TB, kTileAny, V>(A, full, b0, b1, r0, c0);
+        tile_body<EV, MASK, NT, TM, TN, TB, kTileAny, V, RC>(A, full, b0, b1, r0, c0);
     }
 }
 
-template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND, int V>
+template <class EV, int MASK, bool NT, int TM, int TN, int TB, int KIND, int V, int RC>
 __device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, uint32_t b0, uint32_t b1, int64_t r0,
                                           int64_t c0)
 {
@@ -177,7 +179,7 @@ __device__ __forceinline__ void tile_body(const StridedArgs &A, bool full_tile, 
         for (int k = 0; k < kMaxIn; ++k) {
             if (k < EV::n_in(A.prog) && !staged<MASK>(A, k)) {
                 const uint8_t ty = EV::in_ty(A.prog, k);
-                if (MASK == kMaskRuntime && A.in_rowconst[k]) {
+                if (MASK == kMaskRuntime ? A.in_rowconst[k] != 0 : ((RC >> k) & 1) != 0) {
                     // one value per row, the same for the V columns
                     if (count[p] > 0) {
                         uint32_t one[1];

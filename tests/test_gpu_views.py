@@ -349,3 +349,27 @@ def test_tiled_compiled_staged_counts(dt, n_staged):
     plan = run_views(spec, ins, [(os_[:, :, :C], os_)], False, "staged x%d %s" % (n_staged, dt), jit=True)
     assert plan["path"] == "tiled" and plan["kernel"] == "jit_tiled", plan
     assert plan["lds_bytes"] <= 65536 and plan["elems_per_thread"] == (8 if dt == "f16" else 4), plan
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("shape", [(2, 200, 264), (1, 64, 256), (3, 72, 136)])
+def test_tiled_compiled_row_constants(dt, shape):
+    """A transposed input with per-row and per-column constants (stride 0
+    along the columns, stride 0 along the rows) on the tiled path, compiled
+    at run time with the row-constant inputs fixed in the kernel."""
+    B, R, C = shape
+    rng = np.random.default_rng(80 + sum(shape) + len(dt))
+
+    def draw(shp):
+        return (rng.standard_normal(shp) * 4).astype(np.float16 if dt == "f16" else np.float32)
+
+    xs, ys = draw((B, R, C + 8)), draw((B, C, R + 8))
+    rs, cs = draw((B, R, 1)), draw((1, 1, C))
+    rv = as_strided(rs, shape=(B, R, C), strides=(rs.strides[0], rs.strides[1], 0), writeable=False)
+    cv = as_strided(cs, shape=(B, R, C), strides=(0, 0, cs.strides[2]), writeable=False)
+    spec = [("X", ("load", dt, 3)), ("Yt", ("load", dt, 3)), ("r", ("load", dt, 3)), ("c", ("load", dt, 3)),
+            ("yr", ("mul", "Yt", "r")), ("s", ("add", "X", "yr")), ("t", ("sub", "s", "c")), ("o", ("store", "t", 3))]
+    os_ = draw((B, R, C + 8))
+    plan = run_views(spec, [(xs[:, :, :C], xs), (ys[:, :, :R].transpose(0, 2, 1), ys), (rv, rs), (cv, cs)],
+                     [(os_[:, :, :C], os_)], False, "tiled row constants %s %s" % (dt, shape), jit=True)
+    assert plan["path"] == "tiled" and plan["kernel"] == "jit_tiled", plan
