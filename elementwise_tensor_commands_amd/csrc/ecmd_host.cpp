@@ -15,6 +15,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -566,9 +567,15 @@ Canon canonicalize(const Program &P, const Bound &B)
 // ---------------------------------------------------------------------------
 // Path and geometry.
 
-int g_cu_count[64];   // per device ordinal, 0 = not queried yet
+// Per device ordinal, 0 = not queried yet.  Launches on separate handles may
+// run on several threads: each fills in the same value, atomically.
+std::atomic<int> g_cu_count[64];
 
-int cu_count_cached(int dev) { return dev >= 0 && dev < 64 && g_cu_count[dev] > 0 ? g_cu_count[dev] : 256; }
+int cu_count_cached(int dev)
+{
+    const int n = dev >= 0 && dev < 64 ? g_cu_count[dev].load(std::memory_order_relaxed) : 0;
+    return n > 0 ? n : 256;
+}
 
 // Work-items of one dispatch: its grid size is a 32-bit count.
 constexpr int64_t kMaxGridItems = (int64_t)1 << 31;
@@ -1573,11 +1580,11 @@ int cmd_launch(cmd_t h, const cmd_arg *args, int32_t nargs, void *hip_stream)
     // All checks passed; from here on HIP is called.
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(h, CMD_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
-    if (dev >= 0 && dev < 64 && g_cu_count[dev] == 0) {
+    if (dev >= 0 && dev < 64 && g_cu_count[dev].load(std::memory_order_relaxed) == 0) {
         int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return fail(h, CMD_E_LAUNCH, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
-        g_cu_count[dev] = cus > 0 ? cus : 256;
+        g_cu_count[dev].store(cus > 0 ? cus : 256, std::memory_order_relaxed);
     }
     plan->dev = dev;
     plan->args.assign(args, args + nargs);
