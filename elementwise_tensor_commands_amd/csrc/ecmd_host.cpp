@@ -86,6 +86,7 @@ struct Selection {
     int g_mode = 0;             // gather path: 0 per-element kernel, else the interpreter's mode (1 segments, 2 and 3 whole rows)
     int64_t g_div = 0, g_waves = 0, g_rows_per_wave = 0;
     int g_align = 0;            // gather path, compiled kernel, segments: 1 + the output they are laid from (0: none)
+    bool g_s32 = false;         // gather path, compiled kernel: every operand's offsets below 2^32 elements
     int rows_v = 4;             // rows path, compiled kernels: elements per vector (8: every operand 16-bit)
     int tiled_v = 4;            // tiled path, compiled kernels: the same
     const char *name = "";
@@ -982,39 +983,40 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
     const bool g_jit = allow_jit;
     int gce = (int)env_int("ECMD_GATHER_JIT_E", kGatherCcE);   // A/B runs: 4, 8 or 16
     if (gce != 4 && gce != 16) gce = kGatherCcE;
-    // The compiled kernel lays its super-chunks on the 128-byte lines of a
-    // 32-bit output, so that no line inside a row (segments) or inside the
-    // output (whole rows) is written in parts by two wavefronts: partial line
+    // The compiled kernel lays its super-chunks on the 128-byte lines of an
+    // output, so that no line inside a row (segments) or inside the output
+    // (whole rows) is written in parts by two wavefronts: partial line
     // writes cost about 7% of the rate on MI355X (a misaligned 8192 x 8191
     // add: 5.6 TB/s, the same add over whole-line rows: 6.0 TB/s).
-    //   segments: laid from the first 32-bit output with unit stride
-    //     (segment s of a row starts at its line-aligned column s * span - r,
-    //     r < 32 the row start's place in its line), so a row takes one more
-    //     segment when r pushes its end past the last;
+    //   segments: laid from the first 32-bit output with unit stride, else
+    //     the first 16-bit one (segment s of a row starts at its line-aligned
+    //     column s * span - r, r the row start's place in its line of 32 or
+    //     64 elements), so a row takes one more segment when r pushes its end
+    //     past the last;
     //   whole rows: rows per super-chunk a multiple of those that fill whole
-    //     lines of a 32-bit output contiguous across its rows.
-    int line_out = -1;
-    bool rows_out = false;
+    //     lines of every output contiguous across its rows.
+    int line_out = -1, line_elems = 32;
+    int64_t rows_unit = 1;
+    for (int w : {4, 2}) {
+        for (int k = 0; k < P.n_out && line_out < 0; ++k)
+            if (esize(B.out[k].dtype) == w && C.out_s[k][3] == 1) line_out = k, line_elems = w == 4 ? 32 : 64;
+    }
     for (int k = 0; k < P.n_out; ++k) {
-        if (esize(B.out[k].dtype) != 4) continue;
-        const int64_t *st = C.out_s[k];
-        if (st[3] == 1 && line_out < 0) line_out = k;
-        rows_out = rows_out || gather_run(C, 2, st);
+        if (!gather_run(C, 2, C.out_s[k])) continue;
+        const int64_t per_line = esize(B.out[k].dtype) == 4 ? 32 : 64;
+        rows_unit = std::lcm<int64_t>(rows_unit, per_line / std::gcd<int64_t>(C.n[3], per_line));
     }
     if (rows < lim && n3 < lim && env_int("ECMD_GATHER_MODE", 1) != 0) {
         size_interp(P, S);
         const int64_t span = g_jit ? 64 * gce : 256 * S.k_sub;   // elements per super-chunk
         if (n3 > span / 2) {
             const bool lay = g_jit && line_out >= 0;
-            const int64_t segs = (n3 + (lay ? 31 : 0) + span - 1) / span;
+            const int64_t segs = (n3 + (lay ? line_elems - 1 : 0) + span - 1) / span;
             if (rows * segs < lim)
                 S.g_mode = 1, S.g_div = segs, S.g_waves = rows * segs, S.g_align = lay ? line_out + 1 : 0;
         } else {
             int64_t m = span / n3;
-            if (g_jit && rows_out) {
-                const int64_t unit = 32 / std::gcd<int64_t>(n3, 32);
-                if (m >= unit) m -= m % unit;
-            }
+            if (g_jit && m >= rows_unit) m -= m % rows_unit;
             S.g_mode = C.n[0] * C.n[1] == 1 ? 2 : 3;
             S.g_div = n3, S.g_rows_per_wave = m, S.g_waves = (rows + m - 1) / m;
         }
@@ -1030,6 +1032,17 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
         for (int k = 0; k < P.n_in; ++k) bytes += numel * esize(B.in[k].dtype);
         for (int k = 0; k < P.n_out; ++k) bytes += numel * esize(B.out[k].dtype);
         S.shape = linear_shape(bytes);
+        // Ordinary stores, one element per lane (ECMD_NT_STORE=1: nontemporal;
+        // the 8192 x 8191 binary32 add 121-122 us against 128-129, binary16
+        // 65 against 66).
+        const char *nts = std::getenv("ECMD_NT_STORE");
+        S.shape.nt_store = nts && *nts && std::strcmp(nts, "0") != 0;
+        // 32-bit element offsets when every operand's view spans fewer than
+        // 2^32 elements (ECMD_GATHER_S32=0: 64-bit, A/B runs; the binary16
+        // add 65-66 us against 76-77, binary32 unchanged)
+        S.g_s32 = env_int("ECMD_GATHER_S32", 1) != 0;
+        for (int k = 0; k < P.n_in; ++k) S.g_s32 = S.g_s32 && max_offset(C.n, C.in_s[k]) < ((__int128)1 << 32);
+        for (int k = 0; k < P.n_out; ++k) S.g_s32 = S.g_s32 && max_offset(C.n, C.out_s[k]) < ((__int128)1 << 32);
         S.block = 256;   // four wavefronts, one super-chunk each
         S.grid = std::max<int64_t>(1, std::min<int64_t>((S.g_waves + 3) / 4, std::max<int64_t>(
                                                              1, env_int("ECMD_GATHER_DISPATCH", kGatherDispatch))));
@@ -1093,8 +1106,8 @@ JitRequest jit_request(const Selection &S, const Program &P)
             if (S.rowconst[k]) rc |= 1 << k;
         return JitRequest{JIT_ROWS, S.rows_v, S.rows_v, S.shape.nt_load, S.shape.nt_store, P, rc};
     }
-    if (S.path == CMD_PATH_GATHER)
-        return JitRequest{JIT_GATHER, S.e, 0, S.shape.nt_load, false, P, 0, 0, 0, 0, S.g_mode};
+    if (S.path == CMD_PATH_GATHER)   // g: 1 = 32-bit element offsets
+        return JitRequest{JIT_GATHER, S.e, S.g_s32 ? 1 : 0, S.shape.nt_load, S.shape.nt_store, P, 0, 0, 0, 0, S.g_mode};
     const bool nt = tiled_nt();
     JitRequest r{JIT_TILED, S.tiled_v, S.tiled_v, nt, nt, P, S.mask, S.tile.tm, S.tile.tn, S.tile.block};
     for (int k = 0; k < P.n_in; ++k)
@@ -1185,12 +1198,6 @@ void fill_strided(cmd_t h, const Bound &B, const Selection &S, StridedArgs &A)
         A.g_waves = (uint32_t)S.g_waves;
         A.g_rows = (uint32_t)(C.n[0] * C.n[1] * C.n[2]);
         A.g_rows_per_wave = (uint32_t)S.g_rows_per_wave;
-        // 32-bit operands whose elements of one super-chunk are one
-        // contiguous run
-        for (int k = 0; k < h->prog.n_out; ++k)
-            if (esize(B.out[k].dtype) == 4 && gather_run(C, S.g_mode, C.out_s[k])) A.g_out_run |= 1u << k;
-        for (int k = 0; k < h->prog.n_in; ++k)
-            if (esize(B.in[k].dtype) == 4 && gather_run(C, S.g_mode, C.in_s[k])) A.g_in_run |= 1u << k;
         A.g_align = (uint32_t)S.g_align;
         A.div_g = make_fast_div((uint32_t)S.g_div);
         A.div_n2 = make_fast_div((uint32_t)C.n[2]);

@@ -390,8 +390,8 @@ std::string jit_name(const JitRequest &r)
         std::snprintf(b, sizeof b, "ecmd::k_tiled<ecmd::CtEval<ecmd::kJitProg>, %d, %s, %d, %d, %d, true, %d, %d>",
                       r.mask, r.ntl ? "true" : "false", r.tm, r.tn, r.tb, r.e, r.rc);
     else if (r.kind == JIT_GATHER)
-        std::snprintf(b, sizeof b, "ecmd::k_gather_cc<ecmd::CtEval<ecmd::kJitProg>, %d, %d, %s>", r.e, r.mode,
-                      r.ntl ? "true" : "false");
+        std::snprintf(b, sizeof b, "ecmd::k_gather_cc<ecmd::CtEval<ecmd::kJitProg>, %d, %d, %s, %s, %s>", r.e, r.mode,
+                      r.ntl ? "true" : "false", r.nts ? "true" : "false", r.g ? "true" : "false");
     else
         std::snprintf(b, sizeof b, "ecmd::k_rows<ecmd::CtEval<ecmd::kJitProg>, %s, %s, %d, %d>",
                       r.ntl ? "true" : "false", r.nts ? "true" : "false", r.e, r.mask);

@@ -23,7 +23,8 @@ enum JitKernel { JIT_LINEAR = 1, JIT_ROWS = 2, JIT_TILED = 3, JIT_GATHER = 4 };
 
 struct JitRequest {
     JitKernel kind;
-    int e, g;          // linear: elements per work-item and per vector access
+    int e, g;          // linear: elements per work-item and per vector access; gather: g = 1 for 32-bit
+                       // element offsets
     bool ntl, nts;     // nontemporal loads / stores (tiled: ntl for both)
     Program prog;
     int mask = 0;      // tiled: staged inputs; rows: row-constant inputs (bit k = input k)

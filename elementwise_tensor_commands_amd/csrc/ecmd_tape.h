@@ -191,13 +191,10 @@ struct StridedArgs {
     uint32_t g_first;           // gather path: super-chunk of this dispatch's first work-group
     uint32_t g_rows;            // gather path: rows n[0] n[1] n[2]
     uint32_t g_rows_per_wave;   // gather path, whole-row modes: rows per super-chunk
-    uint32_t g_out_run;         // gather path, compiled kernel: bit k = output k is 32-bit and the elements
-                                // of each super-chunk are one contiguous run of it (stored through LDS
-                                // as whole 128-byte lines)
-    uint32_t g_in_run;          // the same for input k (loaded as 16-byte vectors through LDS)
     uint32_t g_align;           // gather path, compiled kernel, segments: 1 + the output whose 128-byte lines
                                 // the segments are laid from (segment s of a row starts at column
-                                // s * 64 E - r, r the row start's place in its line); 0: from column 0
+                                // s * 64 E - r, r the row start's place in its line of 32 or 64
+                                // elements); 0: from column 0
     FastDiv div_g;              // gather path: by segments per row (segment mode) or by n[3] (whole rows)
     Program prog;
 };

@@ -212,6 +212,23 @@ def test_gather_compiled_other_widths(monkeypatch, e, shape):
     _check(shape, store, outs, ref, "compiled gather E=%d %s" % (e, shape))
 
 
+@pytest.mark.parametrize("shape", [(1, 37, 2100), (3, 41, 7), (2, 9, 130)])
+def test_gather_compiled_64bit_offsets(monkeypatch, shape):
+    """The compiled gather kernel's 64-bit offset arithmetic (taken by views
+    spanning 2^32 elements and more; ECMD_GATHER_S32=0 forces it here)."""
+    import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_GATHER_S32", "0")
+    vals, ref = _case(shape, 900 + sum(shape))
+    store, outs = _outputs(shape)
+    cmd = ecmd.from_spec(SPEC).jit()
+    plan = cmd.plan(*vals, *outs)
+    assert plan["kernel"] == "jit_gather", plan
+    cmd.prepare(*vals, *outs)
+    cmd.launch(*vals, *outs)
+    torch.cuda.synchronize()
+    _check(shape, store, outs, ref, "compiled gather, 64-bit offsets %s" % (shape,))
+
+
 CONTIG_SPEC = [("x", ("load", "f32", 3)), ("i", ("load", "i32", 3)), ("s", ("scalar", "f32")),
                ("p", ("mul", "x", "s")), ("ii", ("sub", "i", "i")), ("j", ("add", "ii", "i")),
                ("h", ("cvt", "p", "f16")),
@@ -222,14 +239,13 @@ CONTIG_SPEC = [("x", ("load", "f32", 3)), ("i", ("load", "i32", 3)), ("s", ("sca
                                    (1, 19, 200), (3, 41, 7), (2, 9, 130)])
 @pytest.mark.parametrize("off", [0, 1, 5, 31])
 def test_gather_compiled_contiguous_outputs(shape, off):
-    """Outputs whose super-chunks are contiguous runs (every mode: unit-stride
-    rows for segments, outputs contiguous across rows for whole rows) go
-    through the compiled kernel's LDS buffer as 128-byte-line stores: two
-    32-bit outputs share the buffer, a binary16 output is stored element by
-    element; each output starts `off` elements into a guard-banded buffer, so
-    runs start at every position in a line.  Segments are laid from out0's
-    lines, so a row's first segment starts before the row and 1000-column
-    rows end with an empty segment.  The guards must stay untouched."""
+    """Contiguous outputs of the compiled gather kernel (every mode: unit-stride
+    rows for segments, outputs contiguous across rows for whole rows): two
+    32-bit outputs and a binary16 one, each starting `off` elements into a
+    guard-banded buffer, so rows start at every place in a line.  Segments
+    are laid from out0's lines, so a row's first segment starts before the
+    row and 1000-column rows end with an empty segment; whole-row chunks end
+    on out0's lines.  The guards must stay untouched."""
     import elementwise_tensor_commands_amd as ecmd
     B, R, C = shape
     rng = np.random.default_rng(40 + off + sum(shape))
@@ -271,14 +287,13 @@ RUNS_SPEC = [("x", ("load", "f32", 3)), ("y", ("load", "i32", 3)), ("h", ("load"
 @pytest.mark.parametrize("off", [0, 1, 5, 31])
 @pytest.mark.parametrize("pad", [0, 3])
 def test_gather_compiled_contiguous_inputs(shape, off, pad):
-    """32-bit inputs whose super-chunks are contiguous runs are read as
-    line-aligned 16-byte vectors through the compiled kernel's LDS buffer:
-    each run input starts `off` elements into its storage (runs start at every
-    place in a 128-byte line), x's rows are padded by `pad` elements (a run per
-    segment, but not across whole rows), beside a binary16 input (rows padded,
-    a spare row per batch, 2 bytes off alignment: no vector path takes the
-    views, and batches do not merge into one plane) and a per-row
-    constant (stride 0 along the row) that are read element by element."""
+    """Inputs of the compiled gather kernel in every layout next to line-laid
+    segments: contiguous inputs starting `off` elements into their storage
+    (at every place in a 128-byte line), x with rows padded by `pad` elements
+    (contiguous per segment, not across whole rows), a binary16 input (rows
+    padded, a spare row per batch, 2 bytes off alignment: no vector path
+    takes the views, and batches do not merge into one plane) and a per-row
+    constant (stride 0 along the row)."""
     import elementwise_tensor_commands_amd as ecmd
     B, R, C = shape
     rng = np.random.default_rng(90 + off + 7 * pad + sum(shape))
@@ -306,3 +321,55 @@ def test_gather_compiled_contiguous_inputs(shape, off, pad):
     torch.cuda.synchronize()
     for k, (o, r) in enumerate(zip(outs, ref)):
         compare(host(o), r, 0, "contiguous inputs %s off %d pad %d out%d" % (shape, off, pad, k))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 37, 2100), (1, 5, 1025), (1, 37, 960), (1, 300, 6), (1, 19, 200),
+                                   (3, 41, 7), (2, 9, 130)])
+@pytest.mark.parametrize("off", [0, 1, 7, 63])
+@pytest.mark.parametrize("wide", [False, True])
+def test_gather_compiled_16bit_runs(dt, shape, off, wide):
+    """16-bit operands on the compiled gather kernel: segments are laid from
+    the 16-bit output's lines of 64 elements when no 32-bit output has unit
+    stride (wide: a binary32 output too, which then sets the lines); whole
+    rows per chunk fill the lines of both.  y and the outputs start `off`
+    elements into guard-banded storage; x's rows are padded by one element."""
+    import elementwise_tensor_commands_amd as ecmd
+    B, R, C = shape
+    rng = np.random.default_rng(300 + off + sum(shape) + 5 * wide + len(dt))
+
+    def draw(n):
+        f = (rng.standard_normal(n) * 6).astype(np.float32)
+        return (f.view(np.uint32) >> 16).astype(np.uint16) if dt == "bf16" else f.astype(np.float16)
+
+    xs = draw(B * R * (C + 1)).reshape(B, R, C + 1)
+    ys = draw(off + B * R * C)
+    hx, hy = xs[:, :, :C], ys[off:].reshape(B, R, C)
+    spec = [("x", ("load", dt, 3)), ("y", ("load", dt, 3)), ("p", ("mul", "x", "y")), ("q", ("sub", "p", "x")),
+            ("o0", ("store", "q", 3))]
+    if wide:
+        spec += [("w", ("cvt", "q", "f32")), ("o1", ("store", "w", 3))]
+    ref = run_oracle(spec, [hx, hy])
+    n, guard = B * R * C, 64
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    bufs = [torch.full((n + off + 2 * guard,), -3.0, dtype=tdt, device=dev())]
+    if wide:
+        bufs.append(torch.full((n + off + 2 * guard,), float("nan"), dtype=torch.float32, device=dev()))
+    outs = [b[guard + off:guard + off + n].view(B, R, C) for b in bufs]
+    vals = [to_dev(xs)[:, :, :C], to_dev(ys)[off:].view(B, R, C)]
+    cmd = ecmd.from_spec(spec).jit()
+    plan = cmd.plan(*vals, *outs)
+    assert plan["path"] == "gather" and plan["kernel"] == "jit_gather", plan
+    cmd.prepare(*vals, *outs)
+    cmd.launch(*vals, *outs)
+    torch.cuda.synchronize()
+    for k, (o, r) in enumerate(zip(outs, ref)):
+        compare(host(o), r, 0, "16-bit runs %s %s off %d out%d" % (dt, shape, off, k))
+    for k, b in enumerate(bufs):
+        hb = host(b).astype(np.float32) if k == 0 and dt == "f16" else host(b)
+        for part in (hb[:guard + off], hb[guard + off + n:]):
+            if k == 0:
+                want = np.uint16(0xC040) if dt == "bf16" else np.float32(-3.0)
+                assert (part == want).all(), "out0 guard written (%s, off %d)" % (shape, off)
+            else:
+                assert np.isnan(part).all(), "out1 guard written (%s, off %d)" % (shape, off)

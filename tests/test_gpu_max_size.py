@@ -125,11 +125,14 @@ def test_padded_rows_past_the_rows_limit():
     compare(zv, ref, 0, "padded rows (%s), %d sampled elements" % (plan["kernel"], idx.size))
 
 
-def test_gather_past_2pow32_elements():
+@pytest.mark.parametrize("compiled", [False, True])
+def test_gather_past_2pow32_elements(compiled, tmp_path, monkeypatch):
     """(2^20 + 1, 4099) int32 add whose rows start every 4101 elements (not a
     multiple of 4: no vector path applies), 2^32 + 3,149,827 elements, so the
-    gather kernel's element index and every offset pass 2^32."""
+    gather kernel's element index and every offset pass 2^32: the gather
+    interpreter, and the kernel compiled at run time (its 64-bit offsets)."""
     import elementwise_tensor_commands_amd as ecmd
+    monkeypatch.setenv("ECMD_CACHE_DIR", str(tmp_path))
     rows, cols, ld = (1 << 20) + 1, 4099, 4101
     total = rows * cols
     print("  max size gather %dx%d ld=%d (%d elements)" % (rows, cols, ld, total), flush=True)
@@ -142,8 +145,10 @@ def test_gather_past_2pow32_elements():
         _fill_hash(yb, 0x85EBCA77, 2, False)
         x, y, z = xb[:, :cols], yb[:, :cols], zb[:, :cols]
         cmd = ecmd.from_spec(_add2("i32"))
+        if compiled:
+            cmd.jit(ecmd.JIT_SYNC)
         plan = cmd.plan(x, y, z)
-        assert plan["path"] == "gather", plan
+        assert plan["path"] == "gather" and (plan["kernel"] == "jit_gather") == compiled, plan
         cmd.launch(x, y, z)
         torch.cuda.synchronize()
         idx = _sample(total, extra=(total - (1 << 20),))
