@@ -367,8 +367,14 @@ def parity(st, threads):
 
     import torch
     from oracle import oracle
+    # A Command without tensor inputs (the fill) takes its shape from the
+    # outputs: the oracle writes into host arrays of the outputs' shape.
+    outs = None
+    if not any(isinstance(v, np.ndarray) for v in st.vals):
+        npd = {torch.float32: np.float32, torch.float16: np.float16, torch.int32: np.int32, torch.bfloat16: np.uint16}
+        outs = [np.empty(tuple(o.shape), dtype=npd[o.dtype]) for o in st.outs]
     t0 = time.perf_counter()
-    ref = oracle.from_spec(st.spec).run(*st.vals, nthreads=threads)
+    ref = oracle.from_spec(st.spec).run(*st.vals, outputs=outs, nthreads=threads)
     oracle_s = time.perf_counter() - t0
     torch.cuda.synchronize()
     res = {"compared": 0, "mismatches": 0, "oracle_threads": threads, "oracle_s": round(oracle_s, 3)}

@@ -77,12 +77,20 @@ __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
 #pragma unroll
         for (int k = 0; k < kMaxOut; ++k) {
             if (k < EV::n_out(A.prog)) {
+                const uint8_t ty = EV::out_ty(A.prog, k);
+                const int es = is16(ty) ? 2 : 4;
 #pragma unroll
                 for (int w = 0; w < E / G; ++w) {
                     uint32_t v[G];
 #pragma unroll
                     for (int j = 0; j < G; ++j) v[j] = out[k][w * G + j];
-                    store_group<G, VEC, NTS>(A.out[k], EV::out_ty(A.prog, k), base + (int64_t)(w * 64 + lane) * G, G, v);
+                    if (VEC && NTS && (A.flags & kLinearStreamStore)) {
+                        // the chunk as one streaming buffer, based at its first element
+                        void *cb = uniform_ptr(static_cast<char *>(A.out[k]) + base * es);
+                        store_stream<G>(cb, (uint32_t)(kChunk * es), (uint32_t)((w * 64 + lane) * G * es), ty, v);
+                    } else {
+                        store_group<G, VEC, NTS>(A.out[k], ty, base + (int64_t)(w * 64 + lane) * G, G, v);
+                    }
                 }
             }
         }

@@ -91,10 +91,23 @@ __device__ __forceinline__ void rows_body(const StridedArgs &A, uint32_t v)
     for (int k = 0; k < kMaxOut; ++k) {
         if (k < EV::n_out(A.prog)) {
             const uint8_t ty = EV::out_ty(A.prog, k);
-            const int64_t off =
-                (int64_t)b0 * A.out_s[k][0] + (int64_t)b1 * A.out_s[k][1] + (int64_t)r * A.out_s[k][2] + c;
-            if (count == V) store_group<V, true, NTS>(A.out[k], ty, off, V, out[k]);
-            else store_elems<V, false, false>(A.out[k], ty, off, count, out[k]);
+            const int64_t row = (int64_t)b0 * A.out_s[k][0] + (int64_t)b1 * A.out_s[k][1] + (int64_t)r * A.out_s[k][2];
+            const int64_t off = row + c;
+            if (count == V) {
+                if (WROW && NTS && A.rows_stream) {
+                    // the wavefront's 64 vectors of one row as one streaming
+                    // buffer, based at the first lane's vector
+                    const int es = is16(ty) ? 2 : 4;
+                    const uint32_t v0 = __builtin_amdgcn_readfirstlane(v);
+                    const int64_t c0 = (int64_t)V * (v0 - q * A.div_vec.d);
+                    void *wb = uniform_ptr(static_cast<char *>(A.out[k]) + (row + c0) * es);
+                    store_stream<V>(wb, (uint32_t)(64 * V * es), (uint32_t)((v - v0) * V * es), ty, out[k]);
+                } else {
+                    store_group<V, true, NTS>(A.out[k], ty, off, V, out[k]);
+                }
+            } else {
+                store_elems<V, false, false>(A.out[k], ty, off, count, out[k]);
+            }
         }
     }
 }

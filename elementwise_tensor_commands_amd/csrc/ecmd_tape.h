@@ -149,11 +149,12 @@ struct LinearArgs {
     void *out[kMaxOut];
     int64_t n;
     uint32_t uni[kMaxUni];
-    uint32_t flags;           // kLinearXcdRemap
+    uint32_t flags;           // kLinearXcdRemap, kLinearStreamStore
     int64_t first;            // interpreter: super-chunk of this dispatch's first work-group
     Program prog;
 };
 constexpr uint32_t kLinearXcdRemap = 1;   // give each XCD one contiguous run of blocks
+constexpr uint32_t kLinearStreamStore = 2;   // nontemporal stores as streaming buffer stores (nt sc1)
 
 // Unsigned 32-bit division by a divisor d fixed at launch, as a multiply-high,
 // a subtraction and two shifts (Granlund and Montgomery, "Division by
@@ -186,6 +187,8 @@ struct StridedArgs {
     uint32_t wave_in_row;       // rows path: 1 = a multiple of 64 vectors per row (no wavefront spans two
                                 // rows); 2 = of 64 K vectors (the interpreter: no super-chunk spans two)
     uint32_t rowconst16;        // rows path: 1 = some row-constant input is 16-bit (informational)
+    uint32_t rows_stream;       // rows path, no wavefront across two rows: nontemporal stores as
+                                // streaming buffer stores (nt sc1)
     FastDiv div_vec, div_n2, div_n1;   // rows path: by vectors per row, by n[2], by n[1]
     uint32_t g_waves;           // gather path: super-chunks of work in all
     uint32_t g_first;           // gather path: super-chunk of this dispatch's first work-group

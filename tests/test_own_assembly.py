@@ -90,17 +90,20 @@ def test_denormals_kept(kernels):
 
 def test_linear_uses_128bit_accesses():
     ks = _kernels(_asm("kernels_linear"))
-    vec = [n for n in ks if "Lb1E" in n]      # VEC = true instantiations
+    vec = [n for n in ks if re.findall(r"Lb([01])E", n)[:1] == ["1"]]      # VEC = true instantiations
     assert vec
     for name in vec:
         body = ks[name][0]
+        nts = re.findall(r"Lb([01])E", name)[2] == "1"        # template flags VEC, NTL, NTS
         # every vector-path kernel moves data in 64- or 128-bit accesses (binary16
-        # groups of 4 elements are 8 bytes); all-32-bit Programs use 128-bit only
+        # groups of 4 elements are 8 bytes); all-32-bit Programs use 128-bit only.
+        # Streaming stores go through buffer stores with the nt and sc1 bits.
+        store = r"buffer_store_dwordx([24]) v\[\d+:\d+\], v\d+, s\[\d+:\d+\], 0 offen nt sc1" if nts else \
+            r"global_store_dwordx([24])"
         has_loads = "kProgFill" not in name                    # a fill only stores
-        assert (not has_loads or re.search(r"global_load_dwordx[24]", body)) and \
-            re.search(r"global_store_dwordx[24]", body), name
+        assert (not has_loads or re.search(r"global_load_dwordx[24]", body)) and re.search(store, body), name
         if any(p in name for p in ("kProgAddF32", "kProgIntFused", "kProgAxpbyF32", "kProgCopyF32")):
-            assert "global_load_dwordx4" in body and "global_store_dwordx4" in body, name
+            assert "global_load_dwordx4" in body and "4" in re.search(store, body).group(1), name
 
 
 def test_tiled_uses_lds():
