@@ -89,6 +89,7 @@ struct Selection {
     int g_align = 0;            // gather path, compiled kernel, segments: 1 + the output they are laid from (0: none)
     bool g_s32 = false;         // gather path, compiled kernel: every operand's offsets below 2^32 elements
     int rows_v = 4;             // rows path, compiled kernels: elements per vector (8: every operand 16-bit)
+    uint32_t occ_lds = 0;       // linear and rows vector kernels: LDS bytes per work-group that only bound occupancy
     int tiled_v = 4;            // tiled path, compiled kernels: the same
     const char *name = "";
 };
@@ -352,6 +353,16 @@ int64_t env_int(const char *name, int64_t dflt)
 //   it from HBM.  Smaller working sets use ordinary loads so that data a
 //   previous kernel left in that cache can hit.  ECMD_NT_LOAD=0/1 overrides.
 constexpr int64_t kMallBytes = (int64_t)256 << 20;
+
+// LDS requested per work-group by the linear and rows vector kernels, which
+// use none, only to bound the work-groups resident on a CU (a CU has 160 KiB
+// of LDS; ECMD_OCC_LDS sets the bytes, 0 none).
+uint32_t occupancy_lds(bool vec_kernel)
+{
+    if (!vec_kernel) return 0;
+    const int64_t b = env_int("ECMD_OCC_LDS", 0);
+    return b > 0 && b <= 65536 ? (uint32_t)b : 0u;
+}
 constexpr int kDefaultTileM = 32, kDefaultTileN = 256, kDefaultTileBlock = 256, kDefaultTileWalk = 1;
 
 // Linear kernel shape: one 16-byte vector per operand per work-item -- 4
@@ -754,6 +765,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
             for (int k = 0; k < P.n_in; ++k) read += numel * esize(B.in[k].dtype);
             S.stream_store = env_int("ECMD_STREAM_STORE", written > kMallBytes && written >= read ? 1 : 0) != 0;
         }
+        S.occ_lds = occupancy_lds(S.vec);
         S.name = S.jit ? "jit_linear" : S.vec ? linear_name(S.variant) : "linear_generic_unaligned";
         return;
     }
@@ -827,6 +839,7 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
                                  env_int("ECMD_STREAM_STORE", written > kMallBytes && 2 * written >= bytes ? 1 : 0) != 0;
             }
             S.name = S.jit ? "jit_rows" : rows_name(S.variant);
+            S.occ_lds = occupancy_lds(!interp);
             if (interp) {                           // the LDS-file interpreter, 64 K vectors per work-group
                 size_interp(P, S);
                 S.grid = (n_vec + 64 * S.k_sub - 1) / (64 * S.k_sub);   // one per super-chunk, below 2^25
@@ -1313,13 +1326,13 @@ void upgrade_plan(cmd_t h, LaunchPlan &L, void *stream)
 int enqueue(cmd_t h, LaunchPlan &L, void *hip_stream)
 {
     const Selection &S = L.S;
-    const LaunchGeometry g{S.grid, S.block};
+    const LaunchGeometry g{S.grid, S.block, S.occ_lds};
     int herr = 0;
     if (S.path == CMD_PATH_LINEAR) {
         LinearArgs &A = L.LA;
         if (S.jit) {
             void *params[] = {&A};
-            herr = launch_module(L.fn, (unsigned)g.grid, (unsigned)g.block, 0u, hip_stream, params);
+            herr = launch_module(L.fn, (unsigned)g.grid, (unsigned)g.block, g.occ_lds, hip_stream, params);
         } else if (S.interp) {
             for (int64_t first = 0; first < S.n_wg && herr == 0; first += S.grid) {
                 A.first = first;
@@ -1343,7 +1356,7 @@ int enqueue(cmd_t h, LaunchPlan &L, void *hip_stream)
             }
         } else {
             herr = launch_module(L.fn, (unsigned)g.grid, (unsigned)g.block,
-                                 S.path == CMD_PATH_TILED ? (unsigned)S.lds : 0u, hip_stream, params);
+                                 S.path == CMD_PATH_TILED ? (unsigned)S.lds : g.occ_lds, hip_stream, params);
         }
         return herr;
     }

@@ -48,15 +48,31 @@ __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
     constexpr int kChunk = 64 * E;
     constexpr int kWaves = kLinearBlock / 64;
     const int lane = threadIdx.x & 63;
-    uint32_t bid = blockIdx.x;
-    if (A.flags & kLinearXcdRemap) {
-        // Work-groups are handed to the 8 XCDs in turn; renumber them so that
-        // XCD x works through the x-th eighth of the array in order.
-        const uint32_t per = gridDim.x >> 3;
-        bid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    // The arguments the first loads need -- the flags, the length, the grid
+    // size and, for a compile-time Program, every operand's address -- are
+    // read before anything depends on one of them, so that their scalar
+    // loads share one round trip to the argument segment (a branch on the
+    // flags and the loop guard would otherwise put three round trips before
+    // the first global load of every wavefront that starts on a CU).
+    const uint32_t flags = A.flags;
+    const uint32_t n_wg = gridDim.x;
+    const int64_t n = A.n;
+    asm volatile("" ::"s"(flags), "s"(n_wg), "s"(n));
+    if constexpr (EV::kSpecialised) {
+#pragma unroll
+        for (int k = 0; k < kMaxIn; ++k)
+            if (k < EV::n_in(A.prog)) asm volatile("" ::"s"(A.in[k]));
+#pragma unroll
+        for (int k = 0; k < kMaxOut; ++k)
+            if (k < EV::n_out(A.prog)) asm volatile("" ::"s"(A.out[k]));
     }
-    const int64_t nchunks = A.n / kChunk;
-    const int64_t stride = (int64_t)gridDim.x * kWaves;
+    // Work-groups are handed to the 8 XCDs in turn; with kLinearXcdRemap they
+    // are renumbered so that XCD x works through the x-th eighth of the array
+    // in order.
+    const uint32_t remapped = (blockIdx.x & 7) * (n_wg >> 3) + (blockIdx.x >> 3);
+    const uint32_t bid = (flags & kLinearXcdRemap) ? remapped : blockIdx.x;
+    const int64_t nchunks = n / kChunk;
+    const int64_t stride = (int64_t)n_wg * kWaves;
     for (int64_t c = (int64_t)bid * kWaves + (threadIdx.x >> 6); c < nchunks; c += stride) {
         const int64_t base = c * kChunk;
         Regs<E> R;
@@ -84,7 +100,7 @@ __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
                     uint32_t v[G];
 #pragma unroll
                     for (int j = 0; j < G; ++j) v[j] = out[k][w * G + j];
-                    if (VEC && NTS && (A.flags & kLinearStreamStore)) {
+                    if (VEC && NTS && (flags & kLinearStreamStore)) {
                         // the chunk as one streaming buffer, based at its first element
                         void *cb = uniform_ptr(static_cast<char *>(A.out[k]) + base * es);
                         store_stream<G>(cb, (uint32_t)(kChunk * es), (uint32_t)((w * 64 + lane) * G * es), ty, v);
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
             }
         }
     }
-    if (blockIdx.x == gridDim.x - 1) linear_tail<EV, E>(A, nchunks * kChunk);
+    if (blockIdx.x == n_wg - 1) linear_tail<EV, E>(A, nchunks * kChunk);
 }
 
 }  // namespace ecmd

@@ -324,6 +324,9 @@ namespace ecmd {
 struct LaunchGeometry {
     int64_t grid;
     int32_t block;
+    // Kernels that use no LDS: bytes of LDS requested per work-group only to
+    // bound how many work-groups a CU holds at once (0: no bound).
+    uint32_t occ_lds = 0;
 };
 // Linear kernel shapes: E elements per work-item per step, moved in groups of
 // G consecutive elements per vector access.

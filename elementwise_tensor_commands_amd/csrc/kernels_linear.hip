@@ -11,7 +11,7 @@ template <class EV, int E, int G, bool VEC, bool NTL, bool NTS>
 static int launch_one(const LinearArgs &A, LaunchGeometry g, void *stream)
 {
     return launch_kernel(reinterpret_cast<const void *>(&k_linear<EV, E, G, VEC, NTL, NTS>), dim3((unsigned)g.grid),
-                         dim3(g.block), 0, stream, A);
+                         dim3(g.block), g.occ_lds, stream, A);
 }
 
 template <class EV, int E, int G>

@@ -22,7 +22,7 @@ template <class EV, bool NTL, bool NTS, int V>
 static int launch_one(const StridedArgs &A, LaunchGeometry g, void *stream)
 {
     return launch_kernel(reinterpret_cast<const void *>(&k_rows<EV, NTL, NTS, V>), dim3((unsigned)g.grid),
-                         dim3(kRowsBlock), 0, stream, A);
+                         dim3(kRowsBlock), g.occ_lds, stream, A);
 }
 
 template <class EV, int V>
