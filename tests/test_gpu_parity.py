@@ -94,11 +94,13 @@ def test_linear_small(wl, n):
 
 @pytest.mark.parametrize("wl", LINEAR)
 @pytest.mark.parametrize("shape", ["8x4", "8x8", "4x4", "8x4/ld0", "8x4/st0", "8x8/ld0st0", "4x4/ld0st0",
-                                   "8x4/xcd", "8x4/cap"])
+                                   "8x4/xcd", "8x4/cap", "4x4/stream", "8x8/stream", "4x4/occ"])
 def test_linear_shapes(wl, shape):
     """Every linear kernel instantiation (group size, nontemporal loads and
-    stores on or off, XCD renumbering, capped grid with a grid-stride loop)
-    against the oracle, at a size with several chunks and a ragged tail."""
+    stores on or off, XCD renumbering, capped grid with a grid-stride loop,
+    streaming stores forced below the size that selects them, occupancy
+    bounded through LDS) against the oracle, at a size with several chunks and
+    a ragged tail."""
     g, _, opt = shape.partition("/")
     env = {"ECMD_LINEAR_SHAPE": g, "ECMD_NT_LOAD": "0" if "ld0" in opt else "1",
            "ECMD_NT_STORE": "0" if "st0" in opt else "1"}
@@ -106,6 +108,9 @@ def test_linear_shapes(wl, shape):
         env["ECMD_XCD_REMAP"] = "1"
     if opt == "cap":
         env["ECMD_BLOCKS_PER_CU"] = "1"
+    env["ECMD_STREAM_STORE"] = "1" if opt == "stream" else "0"
+    if opt == "occ":
+        env["ECMD_OCC_LDS"] = "24576"
     old = {k: os.environ.get(k) for k in env}
     os.environ.update(env)
     try:

@@ -290,6 +290,38 @@ def test_rows_row_constant_forms(monkeypatch, rc, dt):
     assert plan["path"] == "rows" and plan["kernel"] == "jit_rows", plan
 
 
+@pytest.mark.parametrize("knob", ["ECMD_STREAM_STORE=1", "ECMD_OCC_LDS=24576"])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("L,pad", [(512, 0), (1024, 0), (1003, 5)])
+def test_rows_store_switches(monkeypatch, knob, dt, L, pad):
+    """The rows kernels with streaming stores forced below the size that
+    selects them (rows of whole 128-byte lines and of a multiple of 64
+    vectors: each wavefront stores its 64 vectors of one row as one buffer;
+    other rows keep ordinary stores) and with occupancy bounded through LDS,
+    over a per-channel affine map on several planes; padding stays untouched."""
+    name, value = knob.split("=")
+    monkeypatch.setenv(name, value)
+    rng = np.random.default_rng(L + pad + len(dt) + len(knob))
+    N, C = 3, 11
+
+    def draw(shape):
+        f = (rng.standard_normal(shape) * 8).astype(np.float32)
+        return f.astype(np.float16) if dt == "f16" else f
+
+    xs = draw((N, C, L + pad))
+    x = xs[:, :, :L]
+    cs, bs = draw((C, 1)), draw((N, C, 1))
+    c = as_strided(cs, shape=(N, C, L), strides=(0, cs.strides[0], 0), writeable=False)
+    b = as_strided(bs, shape=(N, C, L), strides=(bs.strides[0], bs.strides[1], 0), writeable=False)
+    spec = [("x", ("load", dt, 3)), ("c", ("load", dt, 3)), ("b", ("load", dt, 3)), ("m", ("mul", "x", "c")),
+            ("a", ("sub", "m", "b")), ("o", ("store", "a", 3))]
+    os_ = draw((N, C, L + pad))
+    o = os_[:, :, :L]
+    plan = run_views(spec, [(x, xs), (c, cs), (b, bs)], [(o, os_)], False,
+                     "rows %s %s L=%d+%d" % (knob, dt, L, pad), jit=True)
+    assert plan["path"] == "rows", plan
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape,xpad,ypad", [((2, 200, 300), 4, 4), ((1, 64, 128), 0, 0), ((3, 77, 1000), 8, 3),
                                              ((1, 1000, 72), 24, 0), ((2, 130, 66), 6, 6), ((1, 96, 200), 4, 4),
