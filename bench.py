@@ -14,7 +14,10 @@ its start and end (cmd_launch_timed: what a kernel-trace profiler measures);
 `value` is algorithmic bytes x K / the K steps' summed kernel time.  After the
 timed region the same cold steps are timed again by ordinary events recorded on
 the stream around each launch (the command processor's dispatch latency
-included, a few microseconds per launch) and reported beside it.
+included, a few microseconds per launch) and reported beside it.  Then the
+same K steps run once more over copies of the operands placed 4 KiB apart
+modulo 32 KiB (ecmd.empty_staggered) instead of where torch's allocator puts
+them; that rate goes to "placement", beside the value, not into it.
 
 The same JSON line carries, under "commands", the five configurations (and a
 plain copy, the reference for "% of copy", plus three programs with no
@@ -546,6 +549,50 @@ def headline(a, flush, threads, khash):
     return st, per, pairs, mean_us, gbps, settled
 
 
+def headline_staggered(a, st, flush):
+    """The headline's K cold steps again over copies of its operands placed
+    by ecmd.empty_staggered (operand k starting k * 4 KiB past a 32 KiB
+    boundary) instead of torch's 2 MiB-aligned tensors: the same kernel, bytes
+    and values, another placement in HBM.  Reported beside the headline, not
+    as its value; the outputs must equal the headline's bit for bit."""
+    import torch
+
+    import elementwise_tensor_commands_amd as ecmd
+    tensors = [v for v in st.args if isinstance(v, torch.Tensor)]
+    if not all(t.is_contiguous() for t in tensors):
+        # a copy would change the views' layout, hence the path and the kernel
+        return {"skipped": "the headline's operands are not all contiguous"}, None
+    placed = iter(ecmd.empty_staggered([(t.shape, t.dtype) for t in tensors]))
+    args = []
+    for v in st.args:
+        if isinstance(v, torch.Tensor):
+            t = next(placed)
+            t.copy_(v)
+            args.append(t)
+        else:
+            args.append(v)
+    n_out = len(st.outs)
+    for t in args[-n_out:]:
+        t.zero_()
+    ptrs = [t.data_ptr() for t in args if isinstance(t, torch.Tensor)]
+    bound = st.cmd.bind(*args)
+    settled = settle(bound)
+    for _ in range(a.warmup):
+        bound.launch()
+    torch.cuda.synchronize()
+    per = time_each(bound, a.steps, flush)
+    torch.cuda.synchronize()
+    same = all(bool(torch.equal(x.view(torch.uint8), y.view(torch.uint8)))
+               for x, y in zip(args[-n_out:], st.outs))
+    gbps = st.bytes * a.steps / (sum(per) * 1e-3) / 1e9
+    r = {"what": "the headline's kernel over the same values in operands placed 4 KiB apart modulo 32 KiB "
+                 "(ecmd.empty_staggered) instead of torch's 2 MiB-aligned tensors; not the headline value",
+         "offsets_mod_32k": [(p - ptrs[0]) % ecmd.STAGGER_PERIOD for p in ptrs],
+         "step_us": _stats_us(per), "gbps": round(gbps, 2), "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+         "outputs_equal_headline": same}
+    return r, [settled + a.warmup, a.steps]
+
+
 # ---------------------------------------------------------------------------
 # rocprofv3 summaries for profiles/.  A profiled run of this script launches
 # the ecmd kernels in the order its JSON line's launch_sequence lists (per
@@ -624,7 +671,8 @@ def summarize_trace(directory, bench_json, command, plain_json=None):
         if ln is None:
             return None, None
         if name.startswith("headline:"):
-            return ln["step_us"]["median_us"], None
+            src = ln.get("placement", {}) if name.endswith("@staggered") else ln
+            return (src["step_us"]["median_us"], None) if "step_us" in src else (None, None)
         c = ln.get("commands", {}).get(name)
         if not c or "cold" not in c:
             return None, None
@@ -820,6 +868,10 @@ def main():
     log("headline %s: %s, %d cold steps" % (a.workload, label, a.steps))
     st, per, pairs, mean_us, gbps, settled = headline(a, flush, threads, khash)
     log("headline %s: %.1f GB/s cold, kernel mean %.2f us" % (st.plan["kernel"], gbps, mean_us))
+    placement, placement_seq = headline_staggered(a, st, flush)
+    log("headline, staggered operands: %s" % json.dumps(placement))
+    if placement_seq and not placement["outputs_equal_headline"]:
+        raise SystemExit("the headline over staggered operands gave other outputs")
     cnt = counters_record(a.workload, khash)
     line = {
         "metric": METRIC,
@@ -864,7 +916,10 @@ def main():
         log("oracle on %d threads: full-size parity of the headline" % threads)
         line["parity"], _, _ = parity(st, threads)
         log("headline parity: %s" % json.dumps(line["parity"]))
+    line["placement"] = placement
     line["launch_sequence"] = [["headline:" + a.workload, [settled + a.warmup, a.steps, a.steps]]]
+    if placement_seq:
+        line["launch_sequence"].append(["headline:" + a.workload + "@staggered", placement_seq])
     line["settle_launches"] = settled
     if not a.no_commands:
         names = a.only.split(",") if a.only else CONFIGS + LINE_EXTRA + (ALL_EXTRA if a.all else [])

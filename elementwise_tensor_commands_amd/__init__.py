@@ -412,3 +412,44 @@ def from_spec(spec) -> Command:
         else:
             raise ValueError("unknown step %r" % (k,))
     return c
+
+
+# Placement of the operands of one launch.  On MI355X a streaming Command whose
+# operands start at addresses that agree modulo 32 KiB -- as large tensors from
+# torch's caching allocator do: it aligns them to 2 MiB -- reads measurably
+# slower than the same Command over operands whose starts differ by a few KiB
+# modulo 32 KiB (binary32 x, y and output at 0, 4 and 8 KiB: 2.4% faster;
+# binary16: 6%).  The kernels cannot undo it (element i of every operand is
+# needed together), so the helper below leaves it to the caller's allocation.
+STAGGER_PERIOD = 32768
+
+
+def empty_staggered(specs, device="cuda", step=4096):
+    """Uninitialised contiguous tensors for the operands of one launch, cut
+    from one allocation so that their start addresses differ modulo 32 KiB:
+    tensor k starts ``(k * step) % 32768`` bytes past a 32 KiB boundary.
+
+    specs: ``(shape, torch dtype)`` pairs; step: a positive multiple of 256
+    bytes.  The tensors share one storage, which lives as long as any of them;
+    they never overlap.  Plumbing only: no kernel runs."""
+    import torch
+    step = int(step)
+    if step <= 0 or step % 256:
+        raise ValueError("step must be a positive multiple of 256 bytes, got %d" % step)
+    sizes = []
+    for shape, dt in specs:
+        n = 1
+        for d in shape:
+            if int(d) < 0:
+                raise ValueError("negative dimension in %r" % (shape,))
+            n *= int(d)
+        sizes.append(n * torch.empty((), dtype=dt).element_size())
+    offsets, end = [], 0
+    for k, nbytes in enumerate(sizes):
+        start = -(-end // STAGGER_PERIOD) * STAGGER_PERIOD + (k * step) % STAGGER_PERIOD
+        offsets.append(start)
+        end = start + nbytes
+    buf = torch.empty(end + STAGGER_PERIOD, dtype=torch.uint8, device=device)
+    base = (-buf.data_ptr()) % STAGGER_PERIOD
+    return [buf[base + o:base + o + nbytes].view(dt).view(tuple(int(d) for d in shape))
+            for (shape, dt), o, nbytes in zip(specs, offsets, sizes)]
