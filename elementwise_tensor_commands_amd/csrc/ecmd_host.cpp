@@ -354,15 +354,6 @@ int64_t env_int(const char *name, int64_t dflt)
 //   previous kernel left in that cache can hit.  ECMD_NT_LOAD=0/1 overrides.
 constexpr int64_t kMallBytes = (int64_t)256 << 20;
 
-// LDS requested per work-group by the linear and rows vector kernels, which
-// use none, only to bound the work-groups resident on a CU (a CU has 160 KiB
-// of LDS; ECMD_OCC_LDS sets the bytes, 0 none).
-uint32_t occupancy_lds(bool vec_kernel)
-{
-    if (!vec_kernel) return 0;
-    const int64_t b = env_int("ECMD_OCC_LDS", 0);
-    return b > 0 && b <= 65536 ? (uint32_t)b : 0u;
-}
 constexpr int kDefaultTileM = 32, kDefaultTileN = 256, kDefaultTileBlock = 256, kDefaultTileWalk = 1;
 
 // Linear kernel shape: one 16-byte vector per operand per work-item -- 4
@@ -380,6 +371,18 @@ LinearShape linear_shape(int64_t bytes, bool all16 = false)
     const char *st = std::getenv("ECMD_NT_STORE");
     if (st && *st) s.nt_store = std::strcmp(st, "0") != 0;
     return s;
+}
+
+// LDS requested per work-group by the linear and rows vector kernels, which
+// use none, only to bound the work-groups resident on a CU (a CU has 160 KiB
+// of LDS): ECMD_OCC_LDS sets the bytes (up to 64 KiB), for A/B runs.  None by
+// default: 22-30 KiB (7 to 5 work-groups per CU) measured equal or slower on
+// every linear and rows workload.
+uint32_t occupancy_lds(bool vec_kernel)
+{
+    if (!vec_kernel) return 0;
+    const int64_t b = env_int("ECMD_OCC_LDS", 0);
+    return b > 0 && b <= 65536 ? (uint32_t)b : 0u;
 }
 
 // Tiled kernel: ECMD_TILE = "TMxTN" or "TMxTNxTB" picks the specialised
