@@ -300,6 +300,50 @@ def test_bound_launch_repeated():
     compare(host(outs[1]), ref[1], 2, "bound out1")
 
 
+@pytest.mark.parametrize("wl", ["axpby_f32", "mixed_two_out", "axpby_f16"])
+def test_staggered_operands(wl):
+    """Operands cut by ecmd.empty_staggered from one allocation (starts 4 KiB
+    apart modulo 32 KiB) through the linear kernels, against the oracle, at a
+    size with a ragged tail; the bytes between the operands stay untouched."""
+    import elementwise_tensor_commands_amd as ecmd
+    n = (1 << 20) + 9
+    spec = W.WORKLOADS[wl]["spec"]
+    vals, _ = W.make_inputs(wl, n)
+    ref = run_oracle(spec, vals)
+    ins, outs = arg_dtypes(spec)
+    specs = [((n,), TD[d]) for d, v in zip(ins, vals) if isinstance(v, np.ndarray)]
+    specs += [((n,), TD[d]) for d in outs]
+    placed = ecmd.empty_staggered(specs)
+    storage = torch.empty(0, dtype=torch.uint8, device=dev()).set_(placed[0].untyped_storage())
+    storage.fill_(0xA5)
+    it = iter(placed)
+    gv = []
+    for v in vals:
+        if isinstance(v, np.ndarray):
+            t = next(it)
+            t.copy_(to_dev(v))
+            gv.append(t)
+        else:
+            gv.append(v)
+    got = list(it)
+    p0 = placed[0].data_ptr()
+    assert [(t.data_ptr() - p0) % ecmd.STAGGER_PERIOD for t in placed] == [
+        (4096 * k) % ecmd.STAGGER_PERIOD for k in range(len(placed))]
+    plan = ecmd.from_spec(spec).plan(*gv, *got)
+    assert plan["path"] == "linear" and plan["vector"], plan
+    ecmd.from_spec(spec).launch(*gv, *got)
+    torch.cuda.synchronize()
+    for k, (g, r) in enumerate(zip(got, ref)):
+        compare(host(g), r, 0, "%s staggered out%d" % (wl, k))
+    # every byte outside the operands keeps the fill
+    mask = torch.ones(storage.numel(), dtype=torch.bool, device=dev())
+    s0 = storage.data_ptr()
+    for t in placed:
+        a = t.data_ptr() - s0
+        mask[a:a + t.numel() * t.element_size()] = False
+    assert bool((storage[mask] == 0xA5).all())
+
+
 def test_rejected_launch_leaves_output():
     """Failed checks submit nothing: the output keeps its contents."""
     import elementwise_tensor_commands_amd as ecmd
