@@ -753,6 +753,11 @@ void select_path(cmd_t h, const Bound &B, int cu_count, Selection &S, bool allow
         S.grid = per_cu > 0 ? std::min(need, std::max<int64_t>(1, per_cu * cu_count)) : need;
         S.grid = std::min<int64_t>(S.grid, kMaxGridItems / kLinearBlock);   // the kernel loops over the rest
         S.xcd_remap = env_flag("ECMD_XCD_REMAP") && S.grid % 8 == 0;
+        // The lean kernel (one wavefront per chunk, no loop) wherever the grid
+        // is exactly that, with vector accesses, the default shapes and
+        // nontemporal stores (ECMD_LINEAR_LEAN=0: the general kernel).
+        S.shape.lean = S.vec && S.shape.e == S.shape.g && S.shape.nt_store && S.grid == need && !S.xcd_remap &&
+                       chunks < ((int64_t)1 << 32) && env_int("ECMD_LINEAR_LEAN", 1) != 0;
         // Nontemporal stores as streaming buffer stores (nt sc1) when the
         // launch writes at least as many bytes as it reads, and more than
         // the last-level cache holds; otherwise the plain nt stores
@@ -1129,7 +1134,15 @@ bool tiled_nt()
 // The run-time compiled kernel a selection names.
 JitRequest jit_request(const Selection &S, const Program &P)
 {
-    if (S.path == CMD_PATH_LINEAR) return JitRequest{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, P};
+    if (S.path == CMD_PATH_LINEAR) {
+        JitRequest r{JIT_LINEAR, S.shape.e, S.shape.g, S.shape.nt_load, S.shape.nt_store, P};
+        r.lean = S.shape.lean;
+        // ECMD_LINEAR_ORDER = 0 / 1 / 2 picks the order of the input loads
+        // (together, one after the other, the first alone), for A/B runs
+        const int64_t order = env_int("ECMD_LINEAR_ORDER", -1);
+        r.order = r.lean && order >= 0 && order <= 2 ? (int)order : -1;
+        return r;
+    }
     if (S.path == CMD_PATH_ROWS) {
         // Which inputs are row-constant: fixed in the kernel when one of them
         // is 16-bit, else read from the argument block as the ahead-of-time
@@ -1288,6 +1301,7 @@ void pack(cmd_t h, LaunchPlan &L)
         A.n = B.numel;
         std::memcpy(A.uni, B.uni, sizeof A.uni);
         A.flags = (S.xcd_remap ? kLinearXcdRemap : 0u) | (S.stream_store ? kLinearStreamStore : 0u);
+        A.nchunks = S.shape.lean ? (uint32_t)(B.numel / (64 * S.shape.e)) : 0u;
         A.prog = h->prog;
     } else {
         fill_strided(h, B, S, L.SA);

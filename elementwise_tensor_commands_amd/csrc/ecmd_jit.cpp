@@ -383,7 +383,13 @@ int load_function(Entry &e, int dev, hipFunction_t *fn, std::string &err)
 std::string jit_name(const JitRequest &r)
 {
     char b[160];
-    if (r.kind == JIT_LINEAR)
+    if (r.kind == JIT_LINEAR && r.lean && r.order >= 0)
+        std::snprintf(b, sizeof b, "ecmd::k_linear1<ecmd::CtEval<ecmd::kJitProg>, %d, %d, %s, %s, %d>", r.e, r.g,
+                      r.ntl ? "true" : "false", r.nts ? "true" : "false", r.order);
+    else if (r.kind == JIT_LINEAR && r.lean)
+        std::snprintf(b, sizeof b, "ecmd::k_linear1<ecmd::CtEval<ecmd::kJitProg>, %d, %d, %s, %s>", r.e, r.g,
+                      r.ntl ? "true" : "false", r.nts ? "true" : "false");
+    else if (r.kind == JIT_LINEAR)
         std::snprintf(b, sizeof b, "ecmd::k_linear<ecmd::CtEval<ecmd::kJitProg>, %d, %d, true, %s, %s>", r.e, r.g,
                       r.ntl ? "true" : "false", r.nts ? "true" : "false");
     else if (r.kind == JIT_TILED)

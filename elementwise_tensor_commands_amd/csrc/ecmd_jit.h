@@ -31,6 +31,8 @@ struct JitRequest {
     int tm = 0, tn = 0, tb = 0;   // tiled: tile shape and work-items
     int mode = 0;      // gather: 1 segments, 2 whole rows of a plane, 3 whole rows (e: elements per work-item)
     int rc = 0;        // tiled: row-constant inputs (bit k = input k)
+    bool lean = false; // linear: k_linear1 (one wavefront per chunk) instead of k_linear
+    int order = -1;    // linear, lean: order of the input loads (kSer*; -1 the default)
 };
 
 // Template instance the request names, e.g.

@@ -42,6 +42,90 @@ __device__ __forceinline__ void linear_tail(const LinearArgs &A, int64_t first)
     }
 }
 
+// Order of a wavefront's input loads (linear_chunk's SER): 0 every input's
+// loads issued together; 1 each input's once the previous input's have
+// returned; 2 the first input's alone, then the others together.
+constexpr int kSerTogether = 0, kSerEach = 1, kSerFirst = 2;
+
+// The order the kernels take by default: the first input's loads alone, then
+// the others'.  Element i of every operand sits at the same offset from
+// its base, and issued together a wavefront's loads of x[i] and y[i] reach
+// the memory at the same moment; on MI355X that measured slower than one
+// after the other although each wavefront then keeps fewer loads in flight.
+// Same box, cold, kernels compiled at run time (together / each input alone
+// / the first alone): the 3 GiB axpby 503.6 / 497.3 / 497.6 us, its binary16
+// form 263.1 / 248.4 / 248.3, bias + ReLU 495.7 / 492.3 / 492.1, the int32
+// Command 47.6 / 45.2 / 46.1, the mixed-precision Command (three inputs)
+// 247.0 / 250.7 / 246.1.  With two inputs the last two orders are one.
+constexpr int kSerDefault = kSerFirst;
+
+// One chunk of 64 * E elements starting at element `base`, by one wavefront:
+// every load, the Program in registers, every store.  SER orders the input
+// loads (kSer*); a wait is an asm statement that needs the loaded values and
+// keeps every later memory access behind it.
+template <class EV, int E, int G, bool VEC, bool NTL, bool NTS, int SER = kSerTogether>
+__device__ __forceinline__ void linear_chunk(const LinearArgs &A, uint32_t flags, int64_t base, int lane)
+{
+    constexpr int kChunk = 64 * E;
+    Regs<E> R;
+#pragma unroll
+    for (int k = 0; k < kMaxIn; ++k) {
+        if (k < EV::n_in(A.prog)) {
+#pragma unroll
+            for (int w = 0; w < E / G; ++w) {
+                uint32_t v[G];
+                load_group<G, VEC, NTL>(A.in[k], EV::in_ty(A.prog, k), base + (int64_t)(w * 64 + lane) * G, G, v);
+#pragma unroll
+                for (int j = 0; j < G; ++j) R.in[k][w * G + j] = v[j];
+            }
+            if ((SER == kSerEach || (SER == kSerFirst && k == 0)) && k + 1 < EV::n_in(A.prog)) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) asm volatile("" : "+v"(R.in[k][e])::"memory");
+            }
+        }
+    }
+    uint32_t out[kMaxOut][E];
+    EV::template run<E>(A.prog, A.uni, R, out);
+#pragma unroll
+    for (int k = 0; k < kMaxOut; ++k) {
+        if (k < EV::n_out(A.prog)) {
+            const uint8_t ty = EV::out_ty(A.prog, k);
+            const int es = is16(ty) ? 2 : 4;
+#pragma unroll
+            for (int w = 0; w < E / G; ++w) {
+                uint32_t v[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) v[j] = out[k][w * G + j];
+                if (VEC && NTS && (flags & kLinearStreamStore)) {
+                    // the chunk as one streaming buffer, based at its first element
+                    void *cb = uniform_ptr(static_cast<char *>(A.out[k]) + base * es);
+                    store_stream<G>(cb, (uint32_t)(kChunk * es), (uint32_t)((w * 64 + lane) * G * es), ty, v);
+                } else {
+                    store_group<G, VEC, NTS>(A.out[k], ty, base + (int64_t)(w * 64 + lane) * G, G, v);
+                }
+            }
+        }
+    }
+}
+
+// For a compile-time Program: every operand's address is read with the other
+// kernel arguments, before anything depends on one of them, so that all of
+// them share one round trip to the argument segment.
+template <class EV>
+__device__ __forceinline__ void pin_operand_addresses(const LinearArgs &A)
+{
+    if constexpr (EV::kSpecialised) {
+#pragma unroll
+        for (int k = 0; k < kMaxIn; ++k)
+            if (k < EV::n_in(A.prog)) asm volatile("" ::"s"(A.in[k]));
+#pragma unroll
+        for (int k = 0; k < kMaxOut; ++k)
+            if (k < EV::n_out(A.prog)) asm volatile("" ::"s"(A.out[k]));
+    }
+}
+
+// The general form: any grid (a grid-stride loop over the chunks), XCD
+// renumbering on request.
 template <class EV, int E, int G, bool VEC, bool NTL, bool NTS>
 __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
 {
@@ -58,14 +142,7 @@ __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
     const uint32_t n_wg = gridDim.x;
     const int64_t n = A.n;
     asm volatile("" ::"s"(flags), "s"(n_wg), "s"(n));
-    if constexpr (EV::kSpecialised) {
-#pragma unroll
-        for (int k = 0; k < kMaxIn; ++k)
-            if (k < EV::n_in(A.prog)) asm volatile("" ::"s"(A.in[k]));
-#pragma unroll
-        for (int k = 0; k < kMaxOut; ++k)
-            if (k < EV::n_out(A.prog)) asm volatile("" ::"s"(A.out[k]));
-    }
+    pin_operand_addresses<EV>(A);
     // Work-groups are handed to the 8 XCDs in turn; with kLinearXcdRemap they
     // are renumbered so that XCD x works through the x-th eighth of the array
     // in order.
@@ -73,45 +150,34 @@ __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
     const uint32_t bid = (flags & kLinearXcdRemap) ? remapped : blockIdx.x;
     const int64_t nchunks = n / kChunk;
     const int64_t stride = (int64_t)n_wg * kWaves;
-    for (int64_t c = (int64_t)bid * kWaves + (threadIdx.x >> 6); c < nchunks; c += stride) {
-        const int64_t base = c * kChunk;
-        Regs<E> R;
-#pragma unroll
-        for (int k = 0; k < kMaxIn; ++k) {
-            if (k < EV::n_in(A.prog)) {
-#pragma unroll
-                for (int w = 0; w < E / G; ++w) {
-                    uint32_t v[G];
-                    load_group<G, VEC, NTL>(A.in[k], EV::in_ty(A.prog, k), base + (int64_t)(w * 64 + lane) * G, G, v);
-#pragma unroll
-                    for (int j = 0; j < G; ++j) R.in[k][w * G + j] = v[j];
-                }
-            }
-        }
-        uint32_t out[kMaxOut][E];
-        EV::template run<E>(A.prog, A.uni, R, out);
-#pragma unroll
-        for (int k = 0; k < kMaxOut; ++k) {
-            if (k < EV::n_out(A.prog)) {
-                const uint8_t ty = EV::out_ty(A.prog, k);
-                const int es = is16(ty) ? 2 : 4;
-#pragma unroll
-                for (int w = 0; w < E / G; ++w) {
-                    uint32_t v[G];
-#pragma unroll
-                    for (int j = 0; j < G; ++j) v[j] = out[k][w * G + j];
-                    if (VEC && NTS && (flags & kLinearStreamStore)) {
-                        // the chunk as one streaming buffer, based at its first element
-                        void *cb = uniform_ptr(static_cast<char *>(A.out[k]) + base * es);
-                        store_stream<G>(cb, (uint32_t)(kChunk * es), (uint32_t)((w * 64 + lane) * G * es), ty, v);
-                    } else {
-                        store_group<G, VEC, NTS>(A.out[k], ty, base + (int64_t)(w * 64 + lane) * G, G, v);
-                    }
-                }
-            }
-        }
-    }
+    for (int64_t c = (int64_t)bid * kWaves + (threadIdx.x >> 6); c < nchunks; c += stride)
+        linear_chunk<EV, E, G, VEC, NTL, NTS, kSerDefault>(A, flags, c * kChunk, lane);
     if (blockIdx.x == n_wg - 1) linear_tail<EV, E>(A, nchunks * kChunk);
+}
+
+// The lean form, for a grid of exactly one wavefront per chunk (the last
+// work-group's spare wavefronts idle) with vector accesses: the chunk index
+// and its test are scalar, from a chunk count the host computed, so a
+// wavefront issues its first load a few instructions after its argument
+// loads return.  Every instruction before the first load and after the last
+// store is time in which the wavefront's slot holds no memory request; the
+// general form's 64-bit loop bookkeeping made the 3 GiB axpby 2-3% slower
+// than a bare kernel on the same buffers.
+// SER < 0: the default order (kSerDefault).
+template <class EV, int E, int G, bool NTL, bool NTS, int SER = -1>
+__global__ __launch_bounds__(kLinearBlock) void k_linear1(const LinearArgs A)
+{
+    constexpr int kOrder = SER >= 0 ? SER : kSerDefault;
+    constexpr int kChunk = 64 * E;
+    constexpr int kWaves = kLinearBlock / 64;
+    const uint32_t flags = A.flags;
+    const uint32_t nchunks = A.nchunks;
+    const uint32_t n_wg = gridDim.x;
+    asm volatile("" ::"s"(flags), "s"(nchunks), "s"(n_wg));
+    pin_operand_addresses<EV>(A);
+    const uint32_t c = blockIdx.x * (uint32_t)kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (c < nchunks) linear_chunk<EV, E, G, true, NTL, NTS, kOrder>(A, flags, (int64_t)c * kChunk, threadIdx.x & 63);
+    if (blockIdx.x == n_wg - 1) linear_tail<EV, E>(A, (int64_t)nchunks * kChunk);
 }
 
 }  // namespace ecmd

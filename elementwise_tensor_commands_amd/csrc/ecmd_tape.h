@@ -150,6 +150,7 @@ struct LinearArgs {
     int64_t n;
     uint32_t uni[kMaxUni];
     uint32_t flags;           // kLinearXcdRemap, kLinearStreamStore
+    uint32_t nchunks;         // k_linear1: chunks of 64 * E elements (n / (64 * E), below 2^32)
     int64_t first;            // interpreter: super-chunk of this dispatch's first work-group
     Program prog;
 };
@@ -333,6 +334,7 @@ struct LaunchGeometry {
 struct LinearShape {
     int e, g;
     bool nt_load, nt_store;   // nontemporal ("nt") cache policy on loads / stores
+    bool lean = false;        // k_linear1: one wavefront per chunk, scalar chunk index (E == G, nt stores)
 };
 int launch_linear(int variant, bool vec, LinearShape shape, const LinearArgs &A, LaunchGeometry g,
                   void *stream);

@@ -8,19 +8,22 @@
 namespace ecmd {
 
 template <class EV, int E, int G, bool VEC, bool NTL, bool NTS>
-static int launch_one(const LinearArgs &A, LaunchGeometry g, void *stream)
+static int launch_one(bool lean, const LinearArgs &A, LaunchGeometry g, void *stream)
 {
-    return launch_kernel(reinterpret_cast<const void *>(&k_linear<EV, E, G, VEC, NTL, NTS>), dim3((unsigned)g.grid),
-                         dim3(g.block), g.occ_lds, stream, A);
+    const void *fn = reinterpret_cast<const void *>(&k_linear<EV, E, G, VEC, NTL, NTS>);
+    // the lean form exists for the default shapes and store policy only
+    if constexpr (VEC && E == G && NTS)
+        if (lean) fn = reinterpret_cast<const void *>(&k_linear1<EV, E, G, NTL, NTS>);
+    return launch_kernel(fn, dim3((unsigned)g.grid), dim3(g.block), g.occ_lds, stream, A);
 }
 
 template <class EV, int E, int G>
 static int launch_policy(LinearShape s, const LinearArgs &A, LaunchGeometry g, void *stream)
 {
-    if (s.nt_load) return s.nt_store ? launch_one<EV, E, G, true, true, true>(A, g, stream)
-                                     : launch_one<EV, E, G, true, true, false>(A, g, stream);
-    return s.nt_store ? launch_one<EV, E, G, true, false, true>(A, g, stream)
-                      : launch_one<EV, E, G, true, false, false>(A, g, stream);
+    if (s.nt_load) return s.nt_store ? launch_one<EV, E, G, true, true, true>(s.lean, A, g, stream)
+                                     : launch_one<EV, E, G, true, true, false>(s.lean, A, g, stream);
+    return s.nt_store ? launch_one<EV, E, G, true, false, true>(s.lean, A, g, stream)
+                      : launch_one<EV, E, G, true, false, false>(s.lean, A, g, stream);
 }
 
 template <class EV>
@@ -32,7 +35,7 @@ static int launch_shape(LinearShape s, const LinearArgs &A, LaunchGeometry g, vo
 
 int launch_linear(int variant, bool vec, LinearShape shape, const LinearArgs &A, LaunchGeometry g, void *stream)
 {
-    if (!vec) return launch_one<RtEval, 4, 4, false, false, false>(A, g, stream);
+    if (!vec) return launch_one<RtEval, 4, 4, false, false, false>(false, A, g, stream);
     int k = 0;
 #define ECMD_DISPATCH(name, prog)                                          \
     if (variant == k) return launch_shape<CtEval<prog>>(shape, A, g, stream); \

@@ -90,11 +90,18 @@ def test_denormals_kept(kernels):
 
 def test_linear_uses_128bit_accesses():
     ks = _kernels(_asm("kernels_linear"))
-    vec = [n for n in ks if re.findall(r"Lb([01])E", n)[:1] == ["1"]]      # VEC = true instantiations
-    assert vec
+
+    def flags(name):
+        """(VEC, NTL, NTS) of an instance: k_linear<EV, E, G, VEC, NTL, NTS> or the
+        lean k_linear1<EV, E, G, NTL, NTS> (vector accesses only)."""
+        f = [b == "1" for b in re.findall(r"Lb([01])E", name)]
+        return (True, *f) if "k_linear1I" in name else tuple(f)
+
+    vec = [n for n in ks if flags(n)[0]]                       # VEC = true instantiations
+    assert vec and any("k_linear1I" in n for n in vec)
     for name in vec:
         body = ks[name][0]
-        nts = re.findall(r"Lb([01])E", name)[2] == "1"        # template flags VEC, NTL, NTS
+        nts = flags(name)[2]
         # every vector-path kernel moves data in 64- or 128-bit accesses (binary16
         # groups of 4 elements are 8 bytes); all-32-bit Programs use 128-bit only.
         # Streaming stores go through buffer stores with the nt and sc1 bits.
