@@ -353,6 +353,7 @@ struct RtEval {
 template <const Program &P>
 struct CtEval {
     static constexpr bool kSpecialised = true;
+    static constexpr const Program &kProg = P;
     __device__ static constexpr int n_in(const Program &) { return P.n_in; }
     __device__ static constexpr int n_out(const Program &) { return P.n_out; }
     __device__ static constexpr uint8_t in_ty(const Program &, int k) { return P.in_ty[k]; }

@@ -47,17 +47,28 @@ __device__ __forceinline__ void linear_tail(const LinearArgs &A, int64_t first)
 // returned; 2 the first input's alone, then the others together.
 constexpr int kSerTogether = 0, kSerEach = 1, kSerFirst = 2;
 
-// The order the kernels take by default: the first input's loads alone, then
-// the others'.  Element i of every operand sits at the same offset from
-// its base, and issued together a wavefront's loads of x[i] and y[i] reach
-// the memory at the same moment; on MI355X that measured slower than one
-// after the other although each wavefront then keeps fewer loads in flight.
-// Same box, cold, kernels compiled at run time (together / each input alone
-// / the first alone): the 3 GiB axpby 503.6 / 497.3 / 497.6 us, its binary16
-// form 263.1 / 248.4 / 248.3, bias + ReLU 495.7 / 492.3 / 492.1, the int32
-// Command 47.6 / 45.2 / 46.1, the mixed-precision Command (three inputs)
-// 247.0 / 250.7 / 246.1.  With two inputs the last two orders are one.
-constexpr int kSerDefault = kSerFirst;
+// The order the kernels take by default.  Element i of every operand sits
+// at the same offset from its base, and issued together a wavefront's loads
+// of x[i] and y[i] reach the memory at the same moment; on MI355X that
+// measured slower than one after the other although each wavefront then
+// keeps fewer loads in flight.  Same box, cold, kernels compiled at run time
+// (together / each input alone / the first alone): the 3 GiB axpby 503.6 /
+// 497.3 / 497.6 us, its binary16 form 263.1 / 248.4 / 248.3, bias + ReLU
+// 495.7 / 492.3 / 492.1, the int32 Command (three inputs) 47.6 / 45.2 /
+// 46.1, the mixed-precision Command (three binary16 inputs read 8 bytes a
+// work-item) 247.0 / 250.7 / 246.1.  So: each input alone where every input
+// access is 16 bytes, the first alone otherwise (with two inputs the two
+// are one).
+template <class EV, int G>
+constexpr int default_order()
+{
+    if constexpr (EV::kSpecialised) {
+        for (int k = 0; k < EV::kProg.n_in; ++k)
+            if (G * ty_size(EV::kProg.in_ty[k]) != 16) return kSerFirst;
+        return kSerEach;
+    }
+    return kSerFirst;
+}
 
 // One chunk of 64 * E elements starting at element `base`, by one wavefront:
 // every load, the Program in registers, every store.  SER orders the input
@@ -151,7 +162,7 @@ __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
     const int64_t nchunks = n / kChunk;
     const int64_t stride = (int64_t)n_wg * kWaves;
     for (int64_t c = (int64_t)bid * kWaves + (threadIdx.x >> 6); c < nchunks; c += stride)
-        linear_chunk<EV, E, G, VEC, NTL, NTS, kSerDefault>(A, flags, c * kChunk, lane);
+        linear_chunk<EV, E, G, VEC, NTL, NTS, default_order<EV, G>()>(A, flags, c * kChunk, lane);
     if (blockIdx.x == n_wg - 1) linear_tail<EV, E>(A, nchunks * kChunk);
 }
 
@@ -163,11 +174,11 @@ __global__ __launch_bounds__(kLinearBlock) void k_linear(const LinearArgs A)
 // store is time in which the wavefront's slot holds no memory request; the
 // general form's 64-bit loop bookkeeping made the 3 GiB axpby 2-3% slower
 // than a bare kernel on the same buffers.
-// SER < 0: the default order (kSerDefault).
+// SER < 0: the default order (default_order).
 template <class EV, int E, int G, bool NTL, bool NTS, int SER = -1>
 __global__ __launch_bounds__(kLinearBlock) void k_linear1(const LinearArgs A)
 {
-    constexpr int kOrder = SER >= 0 ? SER : kSerDefault;
+    constexpr int kOrder = SER >= 0 ? SER : default_order<EV, G>();
     constexpr int kChunk = 64 * E;
     constexpr int kWaves = kLinearBlock / 64;
     const uint32_t flags = A.flags;
