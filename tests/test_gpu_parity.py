@@ -124,6 +124,35 @@ def test_linear_shapes(wl, shape):
                 os.environ[k] = v
 
 
+@pytest.mark.parametrize("wl", ["int_fused", "mixed_two_out", "axpby_f32", "add_f32"])
+@pytest.mark.parametrize("order", ["0", "1", "2", "lean0"])
+def test_linear_load_orders(monkeypatch, wl, order):
+    """The lean linear kernel compiled at run time with every order of the
+    input loads (together, each input alone, the first alone) and the general
+    kernel compiled at run time, against the oracle, at a size with several
+    chunks and a ragged tail."""
+    import elementwise_tensor_commands_amd as ecmd
+    if order == "lean0":
+        monkeypatch.setenv("ECMD_LINEAR_LEAN", "0")
+    else:
+        monkeypatch.setenv("ECMD_LINEAR_ORDER", order)
+    n = (1 << 19) + 333
+    spec = W.WORKLOADS[wl]["spec"]
+    vals, extra = W.make_inputs(wl, n)
+    ref = run_oracle(spec, vals)
+    _, outs = arg_dtypes(spec)
+    gv = W.to_torch(vals, extra, dev())
+    got = [torch.empty(n, dtype=TD[d], device=dev()) for d in outs]
+    cmd = ecmd.from_spec(spec).aot(False).jit(ecmd.JIT_SYNC)
+    assert cmd.prepare(*gv, *got) in (0, 1, 2)
+    plan = cmd.plan(*gv, *got)
+    assert plan["path"] == "linear" and plan["kernel"] == "jit_linear", plan
+    cmd.launch(*gv, *got)
+    torch.cuda.synchronize()
+    for k, (g, r) in enumerate(zip(got, ref)):
+        compare(host(g), r, 0, "%s order %s out%d" % (wl, order, k))
+
+
 @pytest.mark.parametrize("wl", LINEAR + ["transposed_2d"])
 def test_generic_interpreter(wl):
     n = 257 if wl == "transposed_2d" else (1 << 18) + 5
