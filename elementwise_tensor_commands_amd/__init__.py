@@ -416,14 +416,16 @@ def from_spec(spec) -> Command:
 
 # Placement of the operands of one launch.  On MI355X a streaming Command whose
 # operands start at addresses that agree modulo 32 KiB -- as large tensors from
-# torch's caching allocator do: it aligns them to 2 MiB -- runs measurably
-# slower than the same Command over operands whose starts are 4 KiB apart
-# modulo 32 KiB: the axpby 2.4-2.8% (binary16: 6%), bias + ReLU 1.7%, the int32
-# fused Command 1.5%, a copy or the classifier 0.7-0.9%; the mixed-precision
-# Command (binary16 inputs, binary16 and binary32 outputs) within +-1.3% either
-# way.  Steps of 8 KiB were slower on some machines, so the step stays 4 KiB.
-# The kernels cannot undo it (element i of every operand is needed together),
-# so the helper below leaves it to the caller's allocation.
+# torch's caching allocator do: it aligns them to 2 MiB -- ran measurably
+# slower, with every input's loads issued at once, than the same Command over
+# operands whose starts are 4 KiB apart modulo 32 KiB: the axpby 2.4-2.8%
+# (binary16: 6%), bias + ReLU 1.7%, the int32 fused Command 1.5%, a copy or the
+# classifier 0.7-0.9%; the mixed-precision Command within +-1.3% either way;
+# steps of 8 KiB were slower on some machines.  The linear kernel now issues an
+# input's loads after the previous input's have returned, which avoids most of
+# that collision in time (the axpby: 497.8 us as torch places it, 496.5
+# staggered); the helper below remains for callers that allocate their own
+# operands.
 STAGGER_PERIOD = 32768
 
 
