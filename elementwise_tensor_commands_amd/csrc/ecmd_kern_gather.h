@@ -135,6 +135,12 @@ __global__ __launch_bounds__(kGatherCcBlock) void k_gather_cc(const StridedArgs 
 #pragma unroll
                 for (int e = 0; e < E; ++e) R.in[k][e] = ld<NTL>(p + off(A.in_s[k], e));
             }
+            // the first input's loads alone, then the others' (as on the
+            // linear path: 121.6 -> 121.0 us for the odd rows)
+            if (k == 0 && EV::n_in(A.prog) > 1) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) asm volatile("" : "+v"(R.in[0][e])::"memory");
+            }
         }
     }
     uint32_t out[kMaxOut][E];
