@@ -422,10 +422,10 @@ def from_spec(spec) -> Command:
 # (binary16: 6%), bias + ReLU 1.7%, the int32 fused Command 1.5%, a copy or the
 # classifier 0.7-0.9%; the mixed-precision Command within +-1.3% either way;
 # steps of 8 KiB were slower on some machines.  The linear kernel now issues an
-# input's loads after the previous input's have returned, which avoids most of
-# that collision in time (the axpby: 497.8 us as torch places it, 496.5
-# staggered); the helper below remains for callers that allocate their own
-# operands.
+# input's loads after the previous input's have returned, which avoids that
+# collision in time (the axpby: 497.2 us as torch places it, 498.3 staggered);
+# the helper below remains for callers that allocate their own operands and
+# for kernels that read their inputs together.
 STAGGER_PERIOD = 32768
 
 
