@@ -86,10 +86,22 @@ def test_hand_worked_on_gpu(n):
 # The workloads: small sizes spanning several steps and ragged tails, then full size.
 
 @pytest.mark.parametrize("wl", LINEAR)
-@pytest.mark.parametrize("n", [1, 7, 8, 9, 255, 2048 * 8 + 5, 65536, (1 << 20) + 3])
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 255, 2048 * 8 + 5, 65536, (1 << 20) + 3,
+                               256 * 2, 256 * 5 + 3, 256 * 31 + 17, 256 * 4099 + 255])
 def test_linear_small(wl, n):
+    """Small sizes through the ahead-of-time linear kernels: tails only, whole
+    chunks only, and a last work-group whose spare wavefronts idle (chunk
+    counts not a multiple of 4) beside the tail."""
     plan = _check_workload(wl, n)
     assert plan["path"] == "linear" and plan["specialised"]
+
+
+@pytest.mark.parametrize("wl", ["axpby_f16", "axpby_bf16"])
+@pytest.mark.parametrize("n", [511, 512 * 3, 512 * 5 + 3, 512 * 31 + 509, (1 << 20) + 7])
+def test_linear_small_16bit(wl, n):
+    """The same for the 16-bit kernels (chunks of 512 elements)."""
+    plan = _check_workload(wl, n)
+    assert plan["path"] == "linear" and plan["specialised"] and plan["elems_per_thread"] == 8, plan
 
 
 @pytest.mark.parametrize("wl", LINEAR)
