@@ -136,9 +136,10 @@ def test_linear_shapes(wl, shape):
                 os.environ[k] = v
 
 
-@pytest.mark.parametrize("wl", ["int_fused", "mixed_two_out", "axpby_f32", "add_f32"])
+@pytest.mark.parametrize("wl", ["int_fused", "mixed_two_out", "axpby_f32", "add_f32", "axpby_f16"])
 @pytest.mark.parametrize("order", ["0", "1", "2", "lean0"])
-def test_linear_load_orders(monkeypatch, wl, order):
+@pytest.mark.parametrize("n", [(1 << 19) + 333, 256 * 31 + 17])
+def test_linear_load_orders(monkeypatch, wl, order, n):
     """The lean linear kernel compiled at run time with every order of the
     input loads (together, each input alone, the first alone) and the general
     kernel compiled at run time, against the oracle, at a size with several
@@ -148,7 +149,6 @@ def test_linear_load_orders(monkeypatch, wl, order):
         monkeypatch.setenv("ECMD_LINEAR_LEAN", "0")
     else:
         monkeypatch.setenv("ECMD_LINEAR_ORDER", order)
-    n = (1 << 19) + 333
     spec = W.WORKLOADS[wl]["spec"]
     vals, extra = W.make_inputs(wl, n)
     ref = run_oracle(spec, vals)
@@ -162,7 +162,7 @@ def test_linear_load_orders(monkeypatch, wl, order):
     cmd.launch(*gv, *got)
     torch.cuda.synchronize()
     for k, (g, r) in enumerate(zip(got, ref)):
-        compare(host(g), r, 0, "%s order %s out%d" % (wl, order, k))
+        compare(host(g), r, 0, "%s order %s n=%d out%d" % (wl, order, n, k))
 
 
 @pytest.mark.parametrize("wl", LINEAR + ["transposed_2d"])
