@@ -213,3 +213,23 @@ def test_wait_check_follows_branches():
     assert _read_before_wait(_blocks(bad)) == "ds_read_b128 v[0:3], v4"
     good = bad.replace("\ts_cbranch_scc1 .LBB0_1\n", "\ts_waitcnt vmcnt(0)\n\ts_cbranch_scc1 .LBB0_1\n")
     assert _read_before_wait(_blocks(good)) is None
+
+
+def test_linear_input_loads_ordered():
+    """The lean linear kernels issue an input's loads only once the previous
+    input's have returned where every input access is 16 bytes (the axpby, the
+    int32 Command), and the first input's alone otherwise (the mixed-precision
+    Command, binary16 inputs read 8 bytes a work-item): in the assembly, a
+    vmcnt(0) wait between the loads as the order asks."""
+    ks = _kernels(_asm("kernels_linear"))
+    for prog, expect in (("kProgAxpbyF32", "LWL"), ("kProgIntFused", "LWLWL"), ("kProgMixedTwoOut", "LWLL")):
+        names = [n for n in ks if "k_linear1I" in n and prog + "E" in n and "Li4ELi4ELb1ELb1ELin1E" in n]
+        assert len(names) == 1, (prog, names)
+        seq = ""
+        for line in ks[names[0]][0].splitlines():
+            op = line.strip()
+            if re.match(r"global_load_dwordx[24]\b", op):
+                seq += "L"
+            elif re.match(r"s_waitcnt vmcnt\(0\)", op):
+                seq += "W"
+        assert seq.startswith(expect), (prog, seq)
