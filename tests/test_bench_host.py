@@ -136,3 +136,26 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_summarize_lds(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(bench.PROFILES)
+    seq = [["headline:transposed_2d", [1, 2, 2]], ["transposed_2d", [1, 2, 2, 2, 1]]]
+    rows, did = [], 0
+    for name, counts in seq:
+        for cnt in counts:
+            for _ in range(cnt):
+                did += 1
+                for c, v in (("SQ_INSTS_LDS", 64.0), ("SQ_LDS_IDX_ACTIVE", 200.0),
+                             ("SQ_LDS_BANK_CONFLICT", 10.0 if name == "transposed_2d" else 0.0)):
+                    rows.append({"Kernel_Name": "void ecmd::k_tiled<%s>" % name, "Dispatch_Id": did,
+                                 "Start_Timestamp": did * 10, "Counter_Name": c, "Counter_Value": v})
+    _write_csv(str(tmp_path / "lds" / "p_counter_collection.csv"), rows)
+    bj = tmp_path / "lds.json"
+    bj.write_text(json.dumps({"kernel_source_hash": "abc", "launch_sequence": seq}) + "\n")
+    bench.summarize_lds(str(tmp_path / "lds"), str(bj), "the command")
+    text = open(os.path.join(bench.PROFILES, "lds_bank_conflicts.md")).read()
+    row = [r for r in text.splitlines() if r.startswith("| transposed_2d |")]
+    assert len(row) == 1 and "| 8 | 64 | 200 | 10 | 5.00 % |" in row[0], row
+    assert "headline:" not in text and "the command" in text
