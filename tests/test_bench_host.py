@@ -6,7 +6,6 @@ source hash, and the multi-GPU refusal."""
 import csv
 import json
 import os
-import statistics
 import subprocess
 import sys
 
