@@ -25,8 +25,10 @@ FILES = ["kernels_linear", "kernels_interp", "kernels_rows", "kernels_tiled", "k
 
 def _asm(name):
     path = os.path.join(BUILD, name + ".s")
-    src = os.path.join(ROOT, "elementwise_tensor_commands_amd", "csrc", name + ".hip")
-    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
+    csrc = os.path.join(ROOT, "elementwise_tensor_commands_amd", "csrc")
+    src = os.path.join(csrc, name + ".hip")
+    newest = max(os.path.getmtime(os.path.join(csrc, f)) for f in os.listdir(csrc) if f.endswith(".h"))
+    if not os.path.exists(path) or os.path.getmtime(path) < max(os.path.getmtime(src), newest):
         import importlib.util
         spec = importlib.util.spec_from_file_location(
             "ecmd_build", os.path.join(ROOT, "elementwise_tensor_commands_amd", "build.py"))
