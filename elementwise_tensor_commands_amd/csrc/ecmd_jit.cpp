@@ -23,8 +23,9 @@
 // one worker thread, which compiles queued requests in order and publishes
 // each code object (or its compile error) under g_mu.  The caller meanwhile
 // runs the interpreter.  The compiler runs outside g_mu, so launches and
-// polls never wait for a compile.  At library unload the worker finishes the
-// compile in progress, drops the rest of the queue and is joined.  A child
+// polls never wait for a compile.  At process exit (or library unload) the
+// worker finishes the compile in progress, drops the rest of the queue and is
+// joined, before the compiler's own static objects are destroyed.  A child
 // process made by fork() starts a worker of its own when it needs one.
 #include "ecmd_jit.h"
 
@@ -267,6 +268,7 @@ struct Worker {
             Entry e;
             std::string err;
             const int rc = build_entry(job.second, jit_name(job.second), job.first, e, nullptr, err);
+            exit_guard();
             std::lock_guard<std::mutex> lock(g_mu);
             if (rc == 0) {
                 g_cache.emplace(job.first, std::move(e));
@@ -279,7 +281,8 @@ struct Worker {
         }
     }
     void submit(const std::string &key, const JitRequest &r);
-    ~Worker()
+    // Finish the compile in progress, drop the queue, join the thread.
+    void shutdown()
     {
         {
             std::lock_guard<std::mutex> lock(mu);
@@ -289,10 +292,32 @@ struct Worker {
         if (thread) {
             thread->join();
             delete thread;
+            thread = nullptr;
         }
     }
+    ~Worker() { shutdown(); }
+    // Process exit while the worker compiles.  The compiler's libraries make
+    // some of their static objects during a compile, after this library's
+    // g_worker, so exit() destroys those first; a compile still running then
+    // (every queued request a process leaves behind) used destroyed state and
+    // crashed or hung the exit.  A function-local static made right after a
+    // compile returns is destroyed before every object that compile made: its
+    // destructor stops the worker and waits for the compile in progress before
+    // any of them goes.  (Objects first made during the first compile itself
+    // are not covered if the process exits while that compile runs.)
+    struct ExitGuard;
+    static void exit_guard();
 };
 Worker g_worker;
+
+struct Worker::ExitGuard {
+    ~ExitGuard() { g_worker.shutdown(); }
+};
+void Worker::exit_guard()
+{
+    static ExitGuard guard;
+    (void)guard;
+}
 
 // fork(): the child has only the thread that forked, so the worker and any
 // compile in progress do not exist there.  The handlers hold both locks
